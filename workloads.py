@@ -1,0 +1,138 @@
+"""Seeded synthetic inputs for the W4A4 microscaling linear layer.
+
+This module is shared by the tests, the smoke check and the benchmark.  It
+draws random bf16 tensors and holds the workload shapes; it contains none of
+the quantization or GEMM arithmetic.
+
+Recipe (the model-card pages publish no tensors, so these stand in for the
+layers they describe: the MLP and lm_head projections of the 27B-class models
+and the attention projections of the AutoRound card):
+
+* draws come from ``numpy.random.default_rng(seed)`` (PCG64) as float32 and
+  are rounded once to bf16 (round to nearest even, via torch);
+* activations A ~ N(0, 1) with seed 0; weights W ~ N(0, 0.02) with seed 1;
+* "entry outliers": exactly round(0.01 * M * K) entries of A, picked with
+  seed 2 without replacement, are multiplied by 20 before the bf16 rounding;
+* "channel outliers": round(0.005 * K) whole columns (input channels) of A,
+  picked with seed 2, are multiplied by 30;
+* heavy-tailed weights: Student-t with 4 degrees of freedom scaled to a
+  standard deviation of 0.02 (t4 has variance 2, so the factor is 0.02/sqrt 2);
+* NVFP4 calibration batches b = 1..8 use seeds 100 + b, each N(0, 1) of the
+  evaluated activation's shape.
+
+Large tensors are drawn in row chunks from one stream, which gives the same
+numbers as a single draw.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+SEED_A, SEED_W, SEED_OUTLIER = 0, 1, 2
+_CHUNK = 1 << 24  # elements per draw
+
+
+def _to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x32, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _draw(shape, seed: int, kind: str = "normal", std: float = 1.0, dof: float = 4.0) -> np.ndarray:
+    """float32 draws of the given shape, chunked along the flat index."""
+    rng = np.random.default_rng(seed)
+    total = int(np.prod(shape))
+    out = np.empty(total, np.float32)
+    pos = 0
+    while pos < total:
+        cnt = min(_CHUNK, total - pos)
+        if kind == "normal":
+            out[pos:pos + cnt] = rng.standard_normal(cnt, dtype=np.float32)
+        elif kind == "t":
+            out[pos:pos + cnt] = rng.standard_t(dof, cnt).astype(np.float32)
+        else:
+            raise ValueError(kind)
+        pos += cnt
+    out *= np.float32(std)
+    return out.reshape(shape)
+
+
+def normal_bf16(rows: int, cols: int, std: float = 1.0, seed: int = SEED_A) -> np.ndarray:
+    return _to_bf16_bits(_draw((rows, cols), seed, "normal", std))
+
+
+def student_t_bf16(rows: int, cols: int, std: float = 0.02, dof: float = 4.0,
+                   seed: int = SEED_W) -> np.ndarray:
+    # Var(t_nu) = nu / (nu - 2); scale so the standard deviation is `std`
+    scale = std / math.sqrt(dof / (dof - 2.0))
+    return _to_bf16_bits(_draw((rows, cols), seed, "t", scale, dof))
+
+
+def activations_entry_outliers(m: int, k: int, frac: float = 0.01, factor: float = 20.0,
+                               seed: int = SEED_A, outlier_seed: int = SEED_OUTLIER) -> np.ndarray:
+    x = _draw((m, k), seed, "normal", 1.0)
+    count = int(round(frac * m * k))
+    idx = np.random.default_rng(outlier_seed).choice(m * k, size=count, replace=False)
+    x.reshape(-1)[idx] *= np.float32(factor)
+    return _to_bf16_bits(x)
+
+
+def activations_channel_outliers(m: int, k: int, frac: float = 0.005, factor: float = 30.0,
+                                 seed: int = SEED_A, outlier_seed: int = SEED_OUTLIER) -> np.ndarray:
+    x = _draw((m, k), seed, "normal", 1.0)
+    count = int(round(frac * k))
+    cols = np.random.default_rng(outlier_seed).choice(k, size=count, replace=False)
+    x[:, cols] *= np.float32(factor)
+    return _to_bf16_bits(x)
+
+
+# --------------------------------------------------------------------------- workloads
+@dataclass
+class Gemm:
+    """One linear layer Y[M, N] = A[M, K] W[N, K]^T and how its inputs are drawn."""
+    name: str
+    m: int
+    k: int
+    n: int
+    a_fmt: str = "mxfp4"          # mxfp4 | mxfp8 | nvfp4
+    w_fmt: str = "mxfp4"
+    a_dist: str = "entry_outliers"  # entry_outliers | channel_outliers | normal
+    w_dist: str = "normal"          # normal | student_t
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.m * self.n * self.k
+
+    def activations(self, m: int | None = None) -> np.ndarray:
+        m = self.m if m is None else m
+        if self.a_dist == "entry_outliers":
+            return activations_entry_outliers(m, self.k)
+        if self.a_dist == "channel_outliers":
+            return activations_channel_outliers(m, self.k)
+        return normal_bf16(m, self.k, 1.0, SEED_A)
+
+    def weights(self, n: int | None = None) -> np.ndarray:
+        n = self.n if n is None else n
+        if self.w_dist == "student_t":
+            return student_t_bf16(n, self.k, 0.02, 4.0, SEED_W)
+        return normal_bf16(n, self.k, 0.02, SEED_W)
+
+    def calibration_batches(self):
+        """NVFP4 activation calibration: 8 batches, seeds 101..108."""
+        for b in range(1, 9):
+            yield normal_bf16(self.m, self.k, 1.0, 100 + b)
+
+
+SMALL = Gemm("mxfp4_small_16x256x256", 16, 256, 256)
+DECODE = [Gemm(f"mxfp4_decode_m{m}_k5120_n17408", m, 5120, 17408, a_dist="channel_outliers",
+               w_dist="student_t") for m in (1, 8, 32)]
+PREFILL_UP = Gemm("mxfp4_prefill_up_8192x5120x17408", 8192, 5120, 17408)
+PREFILL_DOWN = Gemm("mxfp4_prefill_down_8192x17408x5120", 8192, 17408, 5120)
+NVFP4 = Gemm("nvfp4_4096x5120x5120", 4096, 5120, 5120, "nvfp4", "nvfp4", a_dist="normal")
+MXFP8_ATTN = Gemm("mxfp8_attn_4096x5120x6144", 4096, 5120, 6144, "mxfp8", "mxfp8")
+MXFP4_VOCAB = Gemm("mxfp4_vocab_4096x5120x151936", 4096, 5120, 151936)
+
+ALL = [SMALL, *DECODE, PREFILL_UP, PREFILL_DOWN, NVFP4, MXFP8_ATTN, MXFP4_VOCAB]
