@@ -1,0 +1,319 @@
+"""Benchmark of the W4A4 microscaling linear layer on one MI355X.
+
+Headline (the JSON line's `value`): MXFP4 W4A4 GEMM throughput in TFLOP/s at
+M = 8192 on the MLP prefill pair -- up projection K=5120 -> N=17408 and down
+projection K=17408 -> N=5120.  One step is one pass of the serving hot path
+over one batch for both projections: per-token CEIL activation quantization
+(mx_quantize_act) followed by the block-scaled FP4 GEMM (mx_gemm).  Weights
+are packed once beforehand (mx_pack_weights, EVEN rule): packing is the
+offline exporter step, and its own time is reported under `rows`.
+
+Also reported under `rows`: the fused-quantization GEMM, decode-shaped GEMMs
+(M = 1, 8, 32) in GB/s with weight copies rotated so the 256 MB last-level
+cache cannot serve them, the standalone quantizer in GB/s, NVFP4, MXFP8 and
+the vocab-sized projection.
+
+`roofline` covers the dominant kernel (mx_gemm) with HIP-event durations of
+its launches inside the timed steps; `cpu_baseline` is the CPU oracle timed
+on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP4 W4A4 GEMM TFLOP/s (M=8192) + GB/s (M<=32) and % of MI355X roofline"
+PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "f16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--quick", action="store_true", help="headline only (skip the other rows)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the hot path is data-parallel "
+                          "over tokens with no communication, and multi-GPU runs are not part of it; "
+                          "run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import fp8_quantized_linear_amd as mxl
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # ------------------------------------------------------------ headline inputs
+    t0 = time.time()
+    up, down = W.PREFILL_UP, W.PREFILL_DOWN
+    a_up, w_up = to_dev(up.activations()), to_dev(up.weights())
+    a_dn, w_dn = to_dev(down.activations()), to_dev(down.weights())
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+
+    # offline weight packing (timed separately)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    wq_up, ws_up = mxl.mx_pack_weights(w_up, "mxfp4", "even")
+    wq_dn, ws_dn = mxl.mx_pack_weights(w_dn, "mxfp4", "even")
+    e1.record()
+    torch.cuda.synchronize()
+    pack_ms = e0.elapsed_time(e1)
+
+    aq_up = torch.empty((up.m, up.k // 2), dtype=torch.uint8, device=dev)
+    as_up = torch.empty((up.m, up.k // 32), dtype=torch.uint8, device=dev)
+    aq_dn = torch.empty((down.m, down.k // 2), dtype=torch.uint8, device=dev)
+    as_dn = torch.empty((down.m, down.k // 32), dtype=torch.uint8, device=dev)
+    y_up = torch.empty((up.m, up.n), dtype=torch.bfloat16, device=dev)
+    y_dn = torch.empty((down.m, down.n), dtype=torch.bfloat16, device=dev)
+
+    def step(events=None):
+        mxl.mx_quantize_act(a_up, "mxfp4", "ceil", out=(aq_up, as_up))
+        if events is not None:
+            events[0].record()
+        mxl.mx_gemm(aq_up, as_up, wq_up, ws_up, up.k, y=y_up)
+        if events is not None:
+            events[1].record()
+        mxl.mx_quantize_act(a_dn, "mxfp4", "ceil", out=(aq_dn, as_dn))
+        if events is not None:
+            events[2].record()
+        mxl.mx_gemm(aq_dn, as_dn, wq_dn, ws_dn, down.k, y=y_dn)
+        if events is not None:
+            events[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+    step_flops = up.flops + down.flops
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    gemm_up_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_dn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    achieved = step_flops / ((gemm_up_ms + gemm_dn_ms) * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms -> {value:.1f} TFLOP/s; gemm up {gemm_up_ms * 1e3:.1f} us, "
+        f"down {gemm_dn_ms * 1e3:.1f} us")
+
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS["fp4"],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp4"], 4),
+                "traffic": traffic_from_profiles(),
+                "kernel": mxl.mx_gemm_plan("mxfp4", "mxfp4", up.m, up.n, up.k),
+                "per_launch_us": {"up": round(gemm_up_ms * 1e3, 2), "down": round(gemm_dn_ms * 1e3, 2)},
+                "algorithmic_flop_per_launch": up.flops}
+
+    rows = {"pack_weights_ms": round(pack_ms, 3)}
+    if not args.quick:
+        rows.update(extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_dn))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(up, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4",
+        "data": "synthetic (seeded N(0,1) activations with 1% x20 outliers, N(0,0.02) weights)",
+        "config": {"workload": "mxfp4 MLP prefill pair: up 8192x5120x17408 + down 8192x17408x5120, "
+                               "per-token CEIL quantize + block-scaled FP4 GEMM, bf16 out",
+                   "m": up.m, "k_up": up.k, "n_up": up.n, "k_down": down.k, "n_down": down.n,
+                   "step_flop": step_flops},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out))
+
+
+def traffic_from_profiles():
+    """HBM bytes per mx_gemm launch from the committed rocprofv3 PMC summary, if
+    it was taken on the current kernel source (else null)."""
+    path = os.path.join(ROOT, "profiles", "mx_gemm_prefill_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("mx_device.h", "gemm_mx.hip"):
+        h.update(open(os.path.join(ROOT, "fp8_quantized_linear_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def _median_ms(torch, fn, iters, warmup=3):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
+def extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_dn):
+    rows = {}
+    up, down = W.PREFILL_UP, W.PREFILL_DOWN
+    # fused quantization prologue vs standalone
+    y = torch.empty((up.m, up.n), dtype=torch.bfloat16, device=dev)
+    med, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm_fused(a_up, wq_up, ws_up, y=y), 10)
+    y2 = torch.empty((down.m, down.n), dtype=torch.bfloat16, device=dev)
+    med2, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm_fused(a_dn, wq_dn, ws_dn, y=y2), 10)
+    rows["fused_prefill"] = {"up_us": round(med * 1e3, 1), "down_us": round(med2 * 1e3, 1),
+                             "tflops": round((up.flops + down.flops) / ((med + med2) * 1e-3) / 1e12, 1)}
+    log(f"fused: up {med * 1e3:.1f} us down {med2 * 1e3:.1f} us")
+
+    # standalone quantizer GB/s (inputs rotated through 4 copies: > 256 MB)
+    for name, cfg, a in (("up", up, a_up), ("down", down, a_dn)):
+        copies = [a] + [a.clone() for _ in range(3)]
+        q = torch.empty((cfg.m, cfg.k // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((cfg.m, cfg.k // 32), dtype=torch.uint8, device=dev)
+        med, p10, p90 = _median_ms(torch, lambda i: mxl.mx_quantize_act(copies[i % 4], out=(q, s)), 20)
+        nbytes = cfg.m * cfg.k * 2 + cfg.m * cfg.k // 2 + cfg.m * cfg.k // 32
+        rows[f"quantizer_{name}"] = {"us": round(med * 1e3, 2), "GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
+                                     "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                                     "bytes": nbytes}
+        del copies
+
+    # decode-shaped GEMMs, weights rotated through 11 copies (> 512 MB)
+    dec = W.DECODE[0]
+    w_bits = to_dev(dec.weights())
+    wq0, ws0 = mxl.mx_pack_weights(w_bits, "mxfp4", "even")
+    del w_bits
+    wcopies = [(wq0, ws0)] + [(wq0.clone(), ws0.clone()) for _ in range(10)]
+    for cfg in W.DECODE:
+        a = to_dev(cfg.activations())
+        aq, as_ = mxl.mx_quantize_act(a)
+        yd = torch.empty((cfg.m, cfg.n), dtype=torch.bfloat16, device=dev)
+        med, p10, p90 = _median_ms(
+            torch, lambda i: mxl.mx_gemm(aq, as_, wcopies[i % 11][0], wcopies[i % 11][1], cfg.k, y=yd), 50)
+        nbytes = (cfg.m + cfg.n) * (cfg.k // 2 + cfg.k // 32) + cfg.m * cfg.n * 2
+        gbs = nbytes / (med * 1e-3) / 1e9
+        rows[f"decode_m{cfg.m}"] = {"us": round(med * 1e3, 2), "p10_us": round(p10 * 1e3, 2),
+                                    "p90_us": round(p90 * 1e3, 2), "GBps": round(gbs, 1),
+                                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 3), "bytes": nbytes,
+                                    "kernel": mxl.mx_gemm_plan("mxfp4", "mxfp4", cfg.m, cfg.n, cfg.k)}
+        log(f"decode m={cfg.m}: {med * 1e3:.2f} us {gbs:.0f} GB/s")
+    del wcopies
+
+    # NVFP4 W4A4
+    nv = W.NVFP4
+    run = 0.0
+    for b in nv.calibration_batches():
+        run = max(run, float(mxl.mx_tensor_amax(to_dev(b)).item()))
+    g_a = mxl.mx_nv_global_scale(run)
+    a = to_dev(nv.activations())
+    w = to_dev(nv.weights())
+    g_w = mxl.mx_nv_global_scale(float(mxl.mx_tensor_amax(w).item()))
+    wq, ws = mxl.mx_pack_weights(w, "nvfp4", global_scale=g_w)
+    aq, as_ = mxl.mx_quantize_act(a, "nvfp4", global_scale=g_a)
+    alpha = float(np.float32(1.0) / (np.float32(g_a) * np.float32(g_w)))
+    yn = torch.empty((nv.m, nv.n), dtype=torch.bfloat16, device=dev)
+    med, _, _ = _median_ms(torch, lambda i: mxl.nv_gemm(aq, as_, wq, ws, nv.k, alpha, y=yn), 20)
+    tf = nv.flops / (med * 1e-3) / 1e12
+    rows["nvfp4"] = {"us": round(med * 1e3, 1), "tflops": round(tf, 1),
+                     "frac_f16_peak": round(tf / PEAK_TFLOPS["f16"], 3),
+                     "frac_fp4_peak": round(tf / PEAK_TFLOPS["fp4"], 4)}
+    log(f"nvfp4: {med * 1e3:.1f} us {tf:.0f} TFLOP/s")
+    del a, w, wq, ws, aq, as_, yn
+
+    # MXFP8 attention projection and the vocab-sized MXFP4 projection on the same A
+    c8, cv = W.MXFP8_ATTN, W.MXFP4_VOCAB
+    a = to_dev(c8.activations())
+    w8 = to_dev(c8.weights())
+    wq8, ws8 = mxl.mx_pack_weights(w8, "mxfp8", "floor")
+    del w8
+    aq8, as8 = mxl.mx_quantize_act(a, "mxfp8", "ceil")
+    y8 = torch.empty((c8.m, c8.n), dtype=torch.bfloat16, device=dev)
+    med, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm(aq8, as8, wq8, ws8, c8.k, "mxfp8", "mxfp8", y=y8), 20)
+    tf8 = c8.flops / (med * 1e-3) / 1e12
+    rows["mxfp8_attn"] = {"us": round(med * 1e3, 1), "tflops": round(tf8, 1),
+                          "frac_fp8_peak": round(tf8 / PEAK_TFLOPS["fp8"], 3)}
+    log(f"mxfp8: {med * 1e3:.1f} us {tf8:.0f} TFLOP/s")
+    del wq8, ws8, y8, aq8, as8
+    wv = to_dev(cv.weights())
+    wqv, wsv = mxl.mx_pack_weights(wv, "mxfp4", "even")
+    del wv
+    aqv, asv = mxl.mx_quantize_act(a)
+    yv = torch.empty((cv.m, cv.n), dtype=torch.bfloat16, device=dev)
+    med, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm(aqv, asv, wqv, wsv, cv.k, y=yv), 10, warmup=2)
+    tfv = cv.flops / (med * 1e-3) / 1e12
+    rows["mxfp4_vocab"] = {"us": round(med * 1e3, 1), "tflops": round(tfv, 1),
+                           "frac_fp4_peak": round(tfv / PEAK_TFLOPS["fp4"], 3)}
+    log(f"vocab: {med * 1e3:.1f} us {tfv:.0f} TFLOP/s")
+    return rows
+
+
+def cpu_baseline(cfg, target_s):
+    """The CPU oracle on a contiguous sample of activation rows of the up
+    projection: CEIL quantization of those rows plus their full output rows
+    from codes (weights packed by the oracle beforehand, untimed like the
+    GPU's packing).  Rows are doubled until the run takes ~target_s."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    a_bits = cfg.activations(m=512)
+    w_bits = cfg.weights()
+    wq, ws = oracle.mx_quantize("e2m1", "even", w_bits, nthreads=threads)
+    rows, took = 2, 0.0
+    while True:
+        t = time.perf_counter()
+        aq, as_ = oracle.mx_quantize("e2m1", "ceil", np.ascontiguousarray(a_bits[:rows]), nthreads=threads)
+        oracle.mx_gemm("e2m1", aq, as_, "e2m1", wq, ws, rows, cfg.n, cfg.k, nthreads=threads)
+        took = time.perf_counter() - t
+        if took >= target_s / 2 or rows >= 512:
+            break
+        rows *= 2
+    flops = 2 * rows * cfg.n * cfg.k
+    return {"value": round(flops / took / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of 8192 activation rows of the up projection (K=5120, N=17408): oracle CEIL "
+                      f"quantization + fp64 GEMM from codes, {took:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+"""fp8_quantized_linear_amd -- Python binding of libmxlinear.so, the gfx950
+(MI355X) library for the W4A4 microscaling linear layer.
+
+The binding only marshals arguments: it checks tensor dtypes, shapes and
+devices, allocates outputs with torch (device memory is torch's job here) and
+passes raw pointers plus the current HIP stream to the C ABI declared in
+``include/mxlinear.h``.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback path.  If the library is missing, importing
+this package raises.
+
+Entry points (same names as the C ABI):
+    mx_pack_weights, mx_quantize_act, mx_gemm, mx_gemm_fused, nv_gemm,
+    mx_tensor_amax, mx_nv_global_scale, mx_gemm_plan
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmxlinear.so")
+
+FORMATS = {"mxfp4": 0, "mxfp8": 1, "nvfp4": 2}
+RULES = {"floor": 0, "ceil": 1, "even": 2}
+MX_OUT_F32 = 0x1
+STATUS = {0: "MX_OK", 1: "MX_ERR_INVALID_ARG", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN",
+          4: "MX_ERR_WORKSPACE", 5: "MX_ERR_UNSUPPORTED", 6: "MX_ERR_HIP"}
+
+
+class MXError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({message})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
+            "or python fp8_quantized_linear_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, u32, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint,
+                                 ctypes.c_float, ctypes.c_size_t)
+    L.mx_abi_version.restype, L.mx_abi_version.argtypes = i32, []
+    L.mx_status_string.restype, L.mx_status_string.argtypes = ctypes.c_char_p, [i32]
+    for f in (L.mx_quantize_act, L.mx_pack_weights):
+        f.restype, f.argtypes = i32, [i32, i32, P, i64, i64, f32, P, P, P]
+    L.mx_gemm.restype = i32
+    L.mx_gemm.argtypes = [i32, i32, P, P, P, P, i64, i64, i64, P, u32, P, sz, P]
+    L.mx_gemm_fused.restype = i32
+    L.mx_gemm_fused.argtypes = [i32, i32, P, i32, P, P, i64, i64, i64, P, u32, P, sz, P]
+    L.nv_gemm.restype = i32
+    L.nv_gemm.argtypes = [P, P, P, P, i64, i64, i64, f32, P, u32, P, sz, P]
+    L.mx_tensor_amax.restype, L.mx_tensor_amax.argtypes = i32, [P, i64, P, P]
+    L.mx_nv_global_scale.restype, L.mx_nv_global_scale.argtypes = f32, [f32]
+    L.mx_gemm_plan.restype = i32
+    L.mx_gemm_plan.argtypes = [i32, i32, i64, i64, i64, i32, ctypes.c_char_p, sz]
+    return L
+
+
+lib = _load()
+ABI_VERSION = lib.mx_abi_version()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MXError(status, where, lib.mx_status_string(status).decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _fmt(f):
+    return FORMATS[f] if isinstance(f, str) else int(f)
+
+
+def _rule(r):
+    return RULES[r] if isinstance(r, str) else int(r)
+
+
+def codes_per_row(fmt: str, k: int) -> int:
+    """Bytes of codes per row of k elements."""
+    return k if fmt == "mxfp8" else k // 2
+
+
+def scales_per_row(fmt: str, k: int) -> int:
+    return k // 16 if fmt == "nvfp4" else k // 32
+
+
+def _quantize(entry, x: torch.Tensor, fmt: str, rule: str, global_scale: float, out=None):
+    _need(x, torch.bfloat16, "input")
+    if x.dim() != 2:
+        raise ValueError("input must be [rows, k]")
+    rows, k = x.shape
+    if out is None:
+        q = torch.empty((rows, codes_per_row(fmt, k)), dtype=torch.uint8, device=x.device)
+        s = torch.empty((rows, scales_per_row(fmt, k)), dtype=torch.uint8, device=x.device)
+    else:
+        q, s = out
+    st = entry(_fmt(fmt), _rule(rule), _ptr(x), rows, k, float(global_scale), _ptr(q), _ptr(s),
+               _stream(x))
+    _check(st, entry.__name__)
+    return q, s
+
+
+def mx_quantize_act(a: torch.Tensor, fmt: str = "mxfp4", rule: str = "ceil",
+                    global_scale: float = 1.0, out=None):
+    """Dynamic per-token activation quantization of bf16 a[m, k] -> (codes, scales)."""
+    return _quantize(lib.mx_quantize_act, a, fmt, rule, global_scale, out)
+
+
+def mx_pack_weights(w: torch.Tensor, fmt: str = "mxfp4", rule: str = "even",
+                    global_scale: float = 1.0, out=None):
+    """Round-to-nearest packing of bf16 w[n, k] -> (codes, scales)."""
+    return _quantize(lib.mx_pack_weights, w, fmt, rule, global_scale, out)
+
+
+def _gemm_out(m, n, device, out_f32, y):
+    if y is not None:
+        return y
+    return torch.empty((m, n), dtype=torch.float32 if out_f32 else torch.bfloat16, device=device)
+
+
+def mx_gemm(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str = "mxfp4",
+            out_f32: bool = False, y=None):
+    """Y[m, n] = A W^T on MX codes/scales (bf16 out, or fp32 with out_f32)."""
+    for t, nm in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
+        _need(t, torch.uint8, nm)
+    m, n = a_q.shape[0], w_q.shape[0]
+    if a_q.shape[1] != codes_per_row(a_fmt, k) or w_q.shape[1] != codes_per_row(w_fmt, k):
+        raise ValueError("code tensors do not match k")
+    if a_s.shape != (m, k // 32) or w_s.shape != (n, k // 32):
+        raise ValueError("scale tensors do not match k")
+    y = _gemm_out(m, n, a_q.device, out_f32, y)
+    st = lib.mx_gemm(_fmt(a_fmt), _fmt(w_fmt), _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, n, k,
+                     _ptr(y), MX_OUT_F32 if out_f32 else 0, None, 0, _stream(a_q))
+    _check(st, "mx_gemm")
+    return y
+
+
+def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str = "ceil",
+                  w_fmt: str = "mxfp4", out_f32: bool = False, y=None):
+    """mx_gemm with the activation quantization done inside the GEMM from bf16 a[m, k]."""
+    _need(a, torch.bfloat16, "a")
+    _need(w_q, torch.uint8, "w_q")
+    _need(w_s, torch.uint8, "w_s")
+    m, k = a.shape
+    n = w_q.shape[0]
+    if w_q.shape[1] != codes_per_row(w_fmt, k) or w_s.shape != (n, k // 32):
+        raise ValueError("weight tensors do not match k")
+    y = _gemm_out(m, n, a.device, out_f32, y)
+    st = lib.mx_gemm_fused(_fmt(a_fmt), _rule(a_rule), _ptr(a), _fmt(w_fmt), _ptr(w_q), _ptr(w_s),
+                           m, n, k, _ptr(y), MX_OUT_F32 if out_f32 else 0, None, 0, _stream(a))
+    _check(st, "mx_gemm_fused")
+    return y
+
+
+def nv_gemm(a_q, a_s, w_q, w_s, k: int, alpha: float, out_f32: bool = False, y=None):
+    """NVFP4 GEMM: Y = alpha * sum_k dq(A) dq(W) with E4M3 block-16 scales."""
+    for t, nm in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
+        _need(t, torch.uint8, nm)
+    m, n = a_q.shape[0], w_q.shape[0]
+    if a_q.shape[1] != k // 2 or w_q.shape[1] != k // 2 or a_s.shape != (m, k // 16) \
+            or w_s.shape != (n, k // 16):
+        raise ValueError("NVFP4 tensors do not match k")
+    y = _gemm_out(m, n, a_q.device, out_f32, y)
+    st = lib.nv_gemm(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, n, k, float(alpha), _ptr(y),
+                     MX_OUT_F32 if out_f32 else 0, None, 0, _stream(a_q))
+    _check(st, "nv_gemm")
+    return y
+
+
+def mx_tensor_amax(x: torch.Tensor) -> torch.Tensor:
+    """Largest |x| of a bf16 tensor, as a 1-element fp32 GPU tensor."""
+    _need(x, torch.bfloat16, "x")
+    out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib.mx_tensor_amax(_ptr(x), x.numel(), _ptr(out), _stream(x)), "mx_tensor_amax")
+    return out
+
+
+def mx_nv_global_scale(amax: float) -> float:
+    """g = RNE_fp32(448 * 6 / amax) (host helper)."""
+    return float(lib.mx_nv_global_scale(float(amax)))
+
+
+def mx_gemm_plan(a_fmt: str, w_fmt: str, m: int, n: int, k: int, fused: bool = False) -> str:
+    """Name of the kernel/tile configuration the GEMM would launch for this shape."""
+    buf = ctypes.create_string_buffer(256)
+    _check(lib.mx_gemm_plan(_fmt(a_fmt), _fmt(w_fmt), m, n, k, int(fused), buf, 256), "mx_gemm_plan")
+    return buf.value.decode()

@@ -1,0 +1,257 @@
+// abi.cpp -- the C ABI of libmxlinear.so (declared in include/mxlinear.h):
+// argument validation (done before any HIP call), device check, dispatch to
+// the gfx950 kernel launchers, status strings and host helpers.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cfloat>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "mxlinear.h"
+
+extern "C" {
+hipError_t mxl_launch_mx_quantize(int elem, int rule, const void* x, int64_t total, void* q, void* s,
+                                  hipStream_t stream);
+hipError_t mxl_launch_nv_quantize(const void* x, int64_t total, float g, void* q, void* s,
+                                  hipStream_t stream);
+hipError_t mxl_launch_amax(const void* x, int64_t count, float* out, hipStream_t stream);
+hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq, const void* as, const void* wq,
+                              const void* ws, int64_t m, int64_t n, int64_t k, void* y, int out_f32,
+                              hipStream_t stream);
+hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, int w_bits,
+                                    const void* wq, const void* ws, int64_t m, int64_t n, int64_t k,
+                                    void* y, int out_f32, hipStream_t stream);
+hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const void* wq, const void* ws, int64_t m,
+                              int64_t n, int64_t k, float alpha, void* y, int out_f32,
+                              hipStream_t stream);
+const char* mxl_mx_gemm_config_name(void);
+const char* mxl_nv_gemm_config_name(void);
+}
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // kernels index rows/columns with 32-bit ints
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_fmt(int f) { return f == MX_FMT_MXFP4 || f == MX_FMT_MXFP8 || f == MX_FMT_NVFP4; }
+bool valid_rule(int r) { return r == MX_RULE_FLOOR || r == MX_RULE_CEIL || r == MX_RULE_EVEN; }
+
+bool log_enabled()
+{
+    static int v = -1;
+    if (v < 0) {
+        const char* e = std::getenv("MXL_LOG");
+        v = (e && e[0] && e[0] != '0') ? 1 : 0;
+    }
+    return v == 1;
+}
+
+// gfx950 check, cached per device ordinal.
+std::atomic<int> g_dev_ok[64];
+
+mx_status check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MX_ERR_HIP;
+    if (dev < 0 || dev >= 64) return MX_ERR_UNSUPPORTED;
+    int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MX_ERR_HIP;
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? MX_OK : MX_ERR_UNSUPPORTED;
+}
+
+mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+mx_status check_quant_args(mx_format fmt, mx_scale_rule rule, const void* x, int64_t rows, int64_t k,
+                           float gscale, const void* q, const void* s)
+{
+    if (!valid_fmt(fmt) || (fmt != MX_FMT_NVFP4 && !valid_rule(rule))) return MX_ERR_INVALID_ARG;
+    if (!x || !q || !s) return MX_ERR_INVALID_ARG;
+    if (rows < 1 || k < 1 || rows > kMaxDim || k > kMaxDim) return MX_ERR_SHAPE;
+    if (k % (fmt == MX_FMT_NVFP4 ? 16 : 32) != 0) return MX_ERR_SHAPE;
+    if (fmt == MX_FMT_NVFP4 && !(std::isfinite(gscale) && gscale > 0.0f)) return MX_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return MX_ERR_ALIGN;
+    return MX_OK;
+}
+
+mx_status quantize(mx_format fmt, mx_scale_rule rule, const void* x, int64_t rows, int64_t k, float g,
+                   void* q, void* s, mx_stream_t stream)
+{
+    mx_status st = check_quant_args(fmt, rule, x, rows, k, g, q, s);
+    if (st != MX_OK) return st;
+    if ((st = check_device()) != MX_OK) return st;
+    const int64_t total = rows * k;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (fmt == MX_FMT_NVFP4) return from_hip(mxl_launch_nv_quantize(x, total, g, q, s, hs));
+    return from_hip(mxl_launch_mx_quantize(fmt == MX_FMT_MXFP4 ? 0 : 1, (int)rule, x, total, q, s, hs));
+}
+
+mx_status check_gemm_shape(int64_t m, int64_t n, int64_t k, int block)
+{
+    if (m < 1 || n < 1 || k < 1 || m > kMaxDim || n > kMaxDim || k > kMaxDim) return MX_ERR_SHAPE;
+    if (k % block != 0) return MX_ERR_SHAPE;
+    return MX_OK;
+}
+
+int bits_of(mx_format f) { return f == MX_FMT_MXFP8 ? 8 : 4; }
+
+} // namespace
+
+extern "C" {
+
+int mx_abi_version(void) { return MXLINEAR_ABI_VERSION; }
+
+const char* mx_status_string(mx_status s)
+{
+    switch (s) {
+    case MX_OK: return "ok";
+    case MX_ERR_INVALID_ARG: return "invalid argument (null pointer, unknown enum or bad format/rule pair)";
+    case MX_ERR_SHAPE: return "invalid shape (m, n, k must be >= 1 and k a multiple of the block size)";
+    case MX_ERR_ALIGN: return "misaligned pointer (all tensors must be 16-byte aligned)";
+    case MX_ERR_WORKSPACE: return "workspace too small";
+    case MX_ERR_UNSUPPORTED: return "unsupported (device is not gfx950, or format pair not implemented)";
+    case MX_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+mx_status mx_quantize_act(mx_format fmt, mx_scale_rule rule, const void* a_bf16, int64_t m, int64_t k,
+                          float global_scale, void* a_q, void* a_s, mx_stream_t stream)
+{
+    return quantize(fmt, rule, a_bf16, m, k, global_scale, a_q, a_s, stream);
+}
+
+mx_status mx_pack_weights(mx_format fmt, mx_scale_rule rule, const void* w_bf16, int64_t n, int64_t k,
+                          float global_scale, void* w_q, void* w_s, mx_stream_t stream)
+{
+    return quantize(fmt, rule, w_bf16, n, k, global_scale, w_q, w_s, stream);
+}
+
+mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void* a_s, const void* w_q,
+                  const void* w_s, int64_t m, int64_t n, int64_t k, void* y, unsigned flags,
+                  void* workspace, size_t ws_bytes, mx_stream_t stream)
+{
+    (void)workspace;
+    (void)ws_bytes;
+    if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || a_fmt == MX_FMT_NVFP4 || w_fmt == MX_FMT_NVFP4)
+        return MX_ERR_INVALID_ARG;
+    if (!a_q || !a_s || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
+    if (flags & ~MX_OUT_F32) return MX_ERR_INVALID_ARG;
+    mx_status st = check_gemm_shape(m, n, k, 32);
+    if (st != MX_OK) return st;
+    if (a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y))
+        return MX_ERR_ALIGN;
+    if ((st = check_device()) != MX_OK) return st;
+    if (log_enabled())
+        std::fprintf(stderr, "[mxlinear] mx_gemm m=%lld n=%lld k=%lld -> %s\n", (long long)m, (long long)n,
+                     (long long)k, mxl_mx_gemm_config_name());
+    return from_hip(mxl_launch_mx_gemm(bits_of(a_fmt), bits_of(w_fmt), a_q, a_s, w_q, w_s, m, n, k, y,
+                                       (flags & MX_OUT_F32) ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf16, mx_format w_fmt,
+                        const void* w_q, const void* w_s, int64_t m, int64_t n, int64_t k, void* y,
+                        unsigned flags, void* workspace, size_t ws_bytes, mx_stream_t stream)
+{
+    (void)workspace;
+    (void)ws_bytes;
+    if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || a_fmt == MX_FMT_NVFP4 || w_fmt == MX_FMT_NVFP4 ||
+        !valid_rule(a_rule))
+        return MX_ERR_INVALID_ARG;
+    if (!a_bf16 || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
+    if (flags & ~MX_OUT_F32) return MX_ERR_INVALID_ARG;
+    mx_status st = check_gemm_shape(m, n, k, 32);
+    if (st != MX_OK) return st;
+    if (a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
+    if (!aligned16(a_bf16) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y)) return MX_ERR_ALIGN;
+    if ((st = check_device()) != MX_OK) return st;
+    return from_hip(mxl_launch_mx_gemm_fused(bits_of(a_fmt), (int)a_rule, a_bf16, bits_of(w_fmt), w_q, w_s,
+                                             m, n, k, y, (flags & MX_OUT_F32) ? 1 : 0,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t m, int64_t n,
+                  int64_t k, float alpha, void* y, unsigned flags, void* workspace, size_t ws_bytes,
+                  mx_stream_t stream)
+{
+    (void)workspace;
+    (void)ws_bytes;
+    if (!a_q || !a_s || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
+    if (flags & ~MX_OUT_F32) return MX_ERR_INVALID_ARG;
+    if (!std::isfinite(alpha)) return MX_ERR_INVALID_ARG;
+    mx_status st = check_gemm_shape(m, n, k, 16);
+    if (st != MX_OK) return st;
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y))
+        return MX_ERR_ALIGN;
+    if ((st = check_device()) != MX_OK) return st;
+    return from_hip(mxl_launch_nv_gemm(a_q, a_s, w_q, w_s, m, n, k, alpha, y, (flags & MX_OUT_F32) ? 1 : 0,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_tensor_amax(const void* x_bf16, int64_t count, float* amax_dev, mx_stream_t stream)
+{
+    if (!x_bf16 || !amax_dev) return MX_ERR_INVALID_ARG;
+    if (count < 1) return MX_ERR_SHAPE;
+    if (!aligned16(x_bf16) || (reinterpret_cast<uintptr_t>(amax_dev) & 3u)) return MX_ERR_ALIGN;
+    mx_status st = check_device();
+    if (st != MX_OK) return st;
+    return from_hip(mxl_launch_amax(x_bf16, count, amax_dev, static_cast<hipStream_t>(stream)));
+}
+
+// g = RNE_fp32(2688 / amax).  The double quotient is within one fp32 ulp of
+// the exact one; the float candidates around it are compared by their exact
+// distance |c * amax - 2688| (c * amax is exact in a double), ties to the
+// even significand.
+float mx_nv_global_scale(float amax)
+{
+    if (!(amax > 0.0f) || !std::isfinite(amax)) return 1.0f;
+    const double a = (double)amax;
+    const double q = 2688.0 / a;
+    if (q > (double)FLT_MAX) return FLT_MAX;
+    float c = (float)q;
+    float best = c;
+    double bestd = std::fabs((double)c * a - 2688.0);
+    float lo = c, hi = c;
+    for (int i = 0; i < 2; ++i) {
+        lo = std::nextafter(lo, 0.0f);
+        hi = std::nextafter(hi, FLT_MAX);
+        const float cand[2] = {lo, hi};
+        for (float v : cand) {
+            const double d = std::fabs((double)v * a - 2688.0);
+            uint32_t vb, bb;
+            std::memcpy(&vb, &v, 4);
+            std::memcpy(&bb, &best, 4);
+            if (d < bestd || (d == bestd && (vb & 1u) == 0 && (bb & 1u) == 1)) {
+                best = v;
+                bestd = d;
+            }
+        }
+    }
+    return best;
+}
+
+mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k, int fused,
+                       char* name, size_t len)
+{
+    if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || !name || len == 0) return MX_ERR_INVALID_ARG;
+    const bool nv = a_fmt == MX_FMT_NVFP4;
+    if (nv != (w_fmt == MX_FMT_NVFP4)) return MX_ERR_INVALID_ARG;
+    mx_status st = check_gemm_shape(m, n, k, nv ? 16 : 32);
+    if (st != MX_OK) return st;
+    if (!nv && a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
+    const char* fmt = nv ? "nvfp4" : (a_fmt == MX_FMT_MXFP4 ? "mxfp4" : "mxfp8");
+    const char* cfg = nv ? mxl_nv_gemm_config_name() : mxl_mx_gemm_config_name();
+    std::snprintf(name, len, "%s%s %s", fused && !nv ? "fused-quant " : "", fmt, cfg);
+    return MX_OK;
+}
+
+} // extern "C"

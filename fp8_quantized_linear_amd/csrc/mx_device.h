@@ -1,0 +1,192 @@
+// mx_device.h -- device-side building blocks shared by the gfx950 kernels of
+// libmxlinear: bf16 bit handling, wave-level reductions, the block-scale
+// rules on bf16 bit patterns, and the element encoders.
+//
+// Formats (OCP Microscaling v1.0, which the AutoRound card
+// Qwen3.8-27B-MXFP8Attn-MXFP4MLP-lmheadMXFP4 names in section 7):
+//   E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0; magnitudes
+//         0, .5, 1, 1.5, 2, 3, 4, 6.
+//   E4M3: sign bit 7, exponent bits 6..3 (bias 7), mantissa 2..0; max 448,
+//         S.1111.111 is NaN.
+//   E8M0: biased exponent, value 2^(c - 127).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxl {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short short2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef int int8_t_ __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+enum : int { ELEM_E2M1 = 0, ELEM_E4M3 = 1 };
+enum : int { RULE_FLOOR = 0, RULE_CEIL = 1, RULE_EVEN = 2 };
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Max over the 4 lanes of a lane quad (lanes 4q .. 4q+3) via DPP quad permutes.
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v)
+{
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); // [1,0,3,2]
+    v = v > o ? v : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);          // [2,3,0,1]
+    return v > o ? v : o;
+}
+// Max over lane pairs (2p, 2p+1).
+__device__ __forceinline__ uint32_t pair_max_u32(uint32_t v)
+{
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+    return v > o ? v : o;
+}
+
+// Largest |x| of 8 bf16 values packed in a uint4, as a 15-bit magnitude
+// pattern.  Non-negative floats order like their bit patterns, so the
+// maximum is an integer maximum of the sign-cleared halves.
+__device__ __forceinline__ uint32_t amax_bits8(uint4 v)
+{
+    uint32_t m = 0;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+        m = m > lo ? m : lo;
+        m = m > hi ? m : hi;
+    }
+    return m;
+}
+
+// Scale exponent e (scale 2^e) of a block from its amax bf16 magnitude bits.
+// amax = M * 2^E with M in [1, 2):
+//   FLOOR e = E - emax
+//   CEIL  e = E - emax + [M > max_elem / 2^emax]   (1.5 for E2M1, 1.75 for E4M3)
+//   EVEN  e = E - emax + [M >= 2 - 2^-(mbits+1)]   (1.75 for E2M1, 1.9375 for E4M3)
+// clamped to [-127, 127].  A zero or subnormal bf16 amax always lands on the
+// lower clamp (E <= -127), so only the normal encoding is decoded here.
+template <int ELEM, int RULE>
+__device__ __forceinline__ int scale_exponent(uint32_t amax16)
+{
+    const int ef = (int)(amax16 >> 7);       // bf16 exponent field
+    const uint32_t mb = amax16 & 0x7Fu;      // 7 mantissa bits
+    if (ef == 0) return -127;
+    const int emax = ELEM == ELEM_E2M1 ? 2 : 8;
+    int bump = 0;
+    if (RULE == RULE_CEIL) bump = ELEM == ELEM_E2M1 ? (mb > 0x40u) : (mb > 0x60u);
+    if (RULE == RULE_EVEN) bump = ELEM == ELEM_E2M1 ? (mb >= 0x60u) : (mb >= 0x78u);
+    int e = ef - 127 - emax + bump;
+    e = e < -127 ? -127 : e;
+    return e > 127 ? 127 : e;
+}
+
+// 2^e as an fp32 for e in [-126, 127].
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// Encode 8 bf16 values (a uint4) as E2M1 codes of x / 2^e, 4 bytes, element
+// 2j in the low nibble of byte j.  The gfx950 conversion rounds to nearest
+// even, saturates at 6 and keeps the sign; its scale operand contributes
+// only its exponent, so it is passed as the fp32 2^e.  e = -127 has no normal
+// fp32, so that (rare) case pre-multiplies by 2^126 and divides by 2^-1.
+__device__ __forceinline__ uint32_t encode8_e2m1(uint4 v, int e)
+{
+    uint32_t r = 0;
+    if (e > -127) {
+        const float s = pow2f(e);
+        bf16x2_t p0, p1, p2, p3;
+        __builtin_memcpy(&p0, &v.x, 4);
+        __builtin_memcpy(&p1, &v.y, 4);
+        __builtin_memcpy(&p2, &v.z, 4);
+        __builtin_memcpy(&p3, &v.w, 4);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, p0, s, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, p1, s, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, p2, s, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, p3, s, 3);
+    } else {
+        const float up = 0x1p126f, s = 0.5f;
+#define MXL_LO(w) (bf16_bits_to_float((w) & 0xFFFFu) * up)
+#define MXL_HI(w) (bf16_bits_to_float((w) >> 16) * up)
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, MXL_LO(v.x), MXL_HI(v.x), s, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, MXL_LO(v.y), MXL_HI(v.y), s, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, MXL_LO(v.z), MXL_HI(v.z), s, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, MXL_LO(v.w), MXL_HI(v.w), s, 3);
+#undef MXL_LO
+#undef MXL_HI
+    }
+    return r;
+}
+
+// Encode 8 bf16 values as E4M3 codes of x / 2^e (8 bytes).  The gfx950
+// conversion rounds to nearest even but turns values beyond 464 into NaN, so
+// inputs are clamped to +-448 * 2^e first (exact), giving the saturating
+// behaviour of the format definition.
+__device__ __forceinline__ uint2 encode8_e4m3(uint4 v, int e)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float up = 1.0f, s;
+    if (e > -127) {
+        s = pow2f(e);
+    } else {
+        up = 0x1p126f;
+        s = 0.5f;
+    }
+    const float lim = 448.0f * s;
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __builtin_amdgcn_fmed3f(bf16_bits_to_float(w[i] & 0xFFFFu) * up, -lim, lim);
+        f[2 * i + 1] = __builtin_amdgcn_fmed3f(bf16_bits_to_float(w[i] >> 16) * up, -lim, lim);
+    }
+    short2_t lo = {0, 0}, hi = {0, 0};
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, f[0], f[1], s, false);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, f[2], f[3], s, true);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, f[4], f[5], s, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, f[6], f[7], s, true);
+    uint32_t out[2];
+    __builtin_memcpy(&out[0], &lo, 4);
+    __builtin_memcpy(&out[1], &hi, 4);
+    return make_uint2(out[0], out[1]);
+}
+
+// ---------------------------------------------------------------- NVFP4 helpers
+// E4M3 value of a code (non-NaN codes), as a double.
+__device__ __forceinline__ double e4m3_value_f64(uint32_t c)
+{
+    const uint32_t ef = (c >> 3) & 15u, m = c & 7u;
+    double mag = ef == 0 ? (double)m * 0x1p-9 : (1.0 + (double)m * 0.125) * __builtin_ldexp(1.0, (int)ef - 7);
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// RNE_E4M3 of a non-negative double v (saturating at 448): v >= 448 -> 0x7E;
+// below 2^-6 the subnormal step 2^-9 applies; otherwise the double is rounded
+// to 3 mantissa bits (ties to even) on its bit pattern.
+__device__ __forceinline__ uint32_t e4m3_rne_f64(double v)
+{
+    if (v >= 448.0) return 0x7Eu;
+    if (v < 0x1p-6) return (uint32_t)__builtin_rint(v * 512.0); // 0..8; 8 is 2^-6 (code 0x08)
+    uint64_t b = (uint64_t)__double_as_longlong(v);
+    b += ((uint64_t)1 << 48) - 1 + ((b >> 49) & 1);              // RNE at mantissa bit 49
+    const uint32_t top = (uint32_t)(b >> 49);                    // exponent(11) | mantissa(3)
+    return top - ((1023u - 7u) << 3);
+}
+
+// RNE_E2M1 of the exact real num/den (num >= 0, den > 0), by comparisons
+// num <=> t * den against the 7 rounding thresholds (exact in fp64 here:
+// num has at most 32 significant bits, t * den at most 7).
+__device__ __forceinline__ uint32_t e2m1_rne_ratio(double num, double den)
+{
+    uint32_t c = 0;
+    c += num > 0.25 * den;
+    c += num >= 0.75 * den;
+    c += num > 1.25 * den;
+    c += num >= 1.75 * den;
+    c += num > 2.5 * den;
+    c += num >= 3.5 * den;
+    c += num > 5.0 * den;
+    return c;
+}
+
+} // namespace mxl

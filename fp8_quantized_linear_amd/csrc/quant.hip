@@ -1,0 +1,182 @@
+// quant.hip -- block quantizers for gfx950: MX (E2M1 / E4M3 elements with an
+// E8M0 scale per 32) and NVFP4 (E2M1 with an E4M3 scale per 16 and an fp32
+// per-tensor global scale), plus the tensor amax used for NVFP4 global scales.
+//
+// Operations (model-card pages):
+//  - Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode": per-token block-32
+//    E2M1 activations with CEIL-rule UE8M0 scales, computed at run time.
+//  - Qwen3.5-27B-MXFP4-QAD-W4A4-LR1e-5-s1000, "How this checkpoint was
+//    produced": block-32 E2M1 weights with EVEN-rule E8M0 scales, rounded to
+//    nearest (Qwen3.5-27B-NVFP4-RTN-weight-only: "rounded to the lattice").
+//  - Qwen3.8-27B-MXFP8Attn-MXFP4MLP-lmheadMXFP4, introduction and section 2:
+//    MXFP8 = E4M3 elements with an E8M0 scale per group of 32.
+//  - Qwen3.5-27B-NVFP4-RTN-weight-only / Qwen3.5-27B-NVFP4-GPTQ, introductions:
+//    NVFP4 with per-tensor global scales.
+//
+// Layout: since k is a multiple of the block, block b of a [rows, k] tensor
+// is elements [B*b, B*b + B) of the flat array and its scale is byte b of the
+// flat scale plane.  The kernels therefore run over the flat arrays: rows
+// never appear.
+//
+// Work mapping (MX): a wave covers 2048 consecutive elements (4 KiB of bf16)
+// with 4 loads of 16 B per lane; load j of lane i reads the 8-element group
+// 64*j + i, so every load instruction is one contiguous 1 KiB read.  The 32
+// elements of a block sit in a lane quad; its amax is a quad reduction over
+// DPP.  Codes go out as one contiguous 256 B (E2M1) or 512 B (E4M3) store per
+// load; scales as 16 consecutive bytes per load.
+#include "mx_device.h"
+
+namespace mxl {
+
+constexpr int QUANT_THREADS = 256;
+constexpr int ELEMS_PER_WAVE = 2048;
+constexpr int ELEMS_PER_BLOCK = ELEMS_PER_WAVE * (QUANT_THREADS / 64);
+
+template <int ELEM, int RULE>
+__global__ __launch_bounds__(QUANT_THREADS) void mx_quantize_kernel(const uint4* __restrict__ x,
+                                                                     int64_t total,
+                                                                     uint8_t* __restrict__ q,
+                                                                     uint8_t* __restrict__ s)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_base = ((int64_t)blockIdx.x * (QUANT_THREADS / 64) + (threadIdx.x >> 6)) * ELEMS_PER_WAVE;
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t g = wave_base / 8 + 64 * j + lane;  // 8-element group index
+        if (g * 8 < total) v[j] = x[g];
+        else v[j] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t g = wave_base / 8 + 64 * j + lane;
+        const uint32_t amax = quad_max_u32(amax_bits8(v[j]));
+        const int e = scale_exponent<ELEM, RULE>(amax);
+        if (g * 8 < total) {
+            if (ELEM == ELEM_E2M1) {
+                reinterpret_cast<uint32_t*>(q)[g] = encode8_e2m1(v[j], e);
+            } else {
+                reinterpret_cast<uint2*>(q)[g] = encode8_e4m3(v[j], e);
+            }
+            if ((lane & 3) == 0) s[g >> 2] = (uint8_t)(e + 127);
+        }
+    }
+}
+
+// NVFP4: a block of 16 is a lane pair.  The block scale and the element codes
+// are roundings of exact reals (amax * g / 6 and x * g / s): x * g is exact in
+// fp64 (8 + 24 significant bits), and the element thresholds are compared as
+// x * g <=> t * s, exact as well.  The scale's quotient by 6 is evaluated in
+// fp64; it can only meet an E4M3 rounding midpoint when the quotient is
+// exactly that midpoint, which fp64 then represents exactly.
+__global__ __launch_bounds__(QUANT_THREADS) void nv_quantize_kernel(const uint4* __restrict__ x,
+                                                                     int64_t total, float gscale,
+                                                                     uint8_t* __restrict__ q,
+                                                                     uint8_t* __restrict__ s)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_base = ((int64_t)blockIdx.x * (QUANT_THREADS / 64) + (threadIdx.x >> 6)) * ELEMS_PER_WAVE;
+    const double g = (double)gscale;
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t gi = wave_base / 8 + 64 * j + lane;
+        v[j] = (gi * 8 < total) ? x[gi] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t gi = wave_base / 8 + 64 * j + lane;
+        const uint32_t amax = pair_max_u32(amax_bits8(v[j]));
+        const double ag = (double)bf16_bits_to_float(amax) * g;   // exact
+        const uint32_t sc = e4m3_rne_f64(ag / 6.0);
+        const double sv = e4m3_value_f64(sc);
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        uint32_t codes = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t b = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+            const double xg = (double)bf16_bits_to_float(b & 0x7FFFu) * g; // exact
+            const uint32_t mag = sv == 0.0 ? 0u : e2m1_rne_ratio(xg, sv);
+            codes |= (mag | ((b >> 15) << 3)) << (4 * i);
+        }
+        if (gi * 8 < total) {
+            reinterpret_cast<uint32_t*>(q)[gi] = codes;
+            if ((lane & 1) == 0) s[gi >> 1] = (uint8_t)sc;
+        }
+    }
+}
+
+// amax of a bf16 tensor into *out (fp32 bits; non-negative floats order like
+// unsigned integers, so an integer atomic max is a float max).
+__global__ void amax_init_kernel(uint32_t* out) { *out = 0u; }
+
+__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t count,
+                                                   uint32_t* __restrict__ out)
+{
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t nvec = count / 8;
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
+        uint32_t a = amax_bits8(xv[i]);
+        m = m > a ? m : a;
+    }
+    for (int64_t i = nvec * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        uint32_t a = x[i] & 0x7FFFu;
+        m = m > a ? m : a;
+    }
+    // wave reduction, then one atomic per wave
+    for (int off = 32; off > 0; off >>= 1) {
+        uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
+        m = m > o ? m : o;
+    }
+    if ((threadIdx.x & 63) == 0) atomicMax(out, m << 16);
+}
+
+} // namespace mxl
+
+// ---------------------------------------------------------------- launchers
+using namespace mxl;
+
+extern "C" hipError_t mxl_launch_mx_quantize(int elem, int rule, const void* x, int64_t total,
+                                             void* q, void* s, hipStream_t stream)
+{
+    const int64_t blocks = (total + ELEMS_PER_BLOCK - 1) / ELEMS_PER_BLOCK;
+    dim3 grid((unsigned)blocks), block(QUANT_THREADS);
+    const uint4* xv = static_cast<const uint4*>(x);
+    uint8_t* qb = static_cast<uint8_t*>(q);
+    uint8_t* sb = static_cast<uint8_t*>(s);
+#define MXL_Q(E, R) hipLaunchKernelGGL((mx_quantize_kernel<E, R>), grid, block, 0, stream, xv, total, qb, sb)
+    if (elem == ELEM_E2M1) {
+        if (rule == RULE_FLOOR) MXL_Q(ELEM_E2M1, RULE_FLOOR);
+        else if (rule == RULE_CEIL) MXL_Q(ELEM_E2M1, RULE_CEIL);
+        else MXL_Q(ELEM_E2M1, RULE_EVEN);
+    } else {
+        if (rule == RULE_FLOOR) MXL_Q(ELEM_E4M3, RULE_FLOOR);
+        else if (rule == RULE_CEIL) MXL_Q(ELEM_E4M3, RULE_CEIL);
+        else MXL_Q(ELEM_E4M3, RULE_EVEN);
+    }
+#undef MXL_Q
+    return hipGetLastError();
+}
+
+extern "C" hipError_t mxl_launch_nv_quantize(const void* x, int64_t total, float g, void* q, void* s,
+                                             hipStream_t stream)
+{
+    const int64_t blocks = (total + ELEMS_PER_BLOCK - 1) / ELEMS_PER_BLOCK;
+    hipLaunchKernelGGL(nv_quantize_kernel, dim3((unsigned)blocks), dim3(QUANT_THREADS), 0, stream,
+                       static_cast<const uint4*>(x), total, g, static_cast<uint8_t*>(q),
+                       static_cast<uint8_t*>(s));
+    return hipGetLastError();
+}
+
+extern "C" hipError_t mxl_launch_amax(const void* x, int64_t count, float* out, hipStream_t stream)
+{
+    hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, stream, reinterpret_cast<uint32_t*>(out));
+    int64_t blocks = (count / 8 + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), count, reinterpret_cast<uint32_t*>(out));
+    return hipGetLastError();
+}

@@ -1,0 +1,183 @@
+/*
+ * mxlinear.h -- C ABI of libmxlinear.so, the MI355X (gfx950) library for the
+ * W4A4 microscaling linear layer:
+ *
+ *   (a) round-to-nearest weight packing to MXFP4 (E2M1 elements, one E8M0
+ *       scale per 32 elements, EVEN scale rule),
+ *   (b) dynamic per-token activation quantization to MXFP4 (CEIL rule),
+ *   (c) the block-scaled FP4 x FP4 GEMM with fp32 accumulation and a bf16
+ *       output,
+ * and the same path for MXFP8 (E4M3 elements, E8M0 per 32) and NVFP4 (E2M1
+ * elements, an E4M3 scale per 16, a per-tensor fp32 global scale).
+ *
+ * Passages defining the operations (model-card pages):
+ *  - Qwen3.5-27B-MXFP4-QAD-W4A4-LR1e-5-s1000, "How this checkpoint was
+ *    produced": MXFP4 weights are E2M1 in blocks of 32 with EVEN-rule E8M0
+ *    scales; activations are quantized dynamically.
+ *  - Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode": activations are
+ *    quantized per token in blocks of 32 to E2M1 with CEIL-rule UE8M0 scales,
+ *    a rule distinct from the weights' EVEN rule; "Serving": the packed format
+ *    (E2M1 weights, block-32 E8M0 scales) and the W4A4 FP4 GEMM with
+ *    activations quantized per token at run time.
+ *  - Qwen3.5-27B-NVFP4-RTN-weight-only (introduction, "How this checkpoint was
+ *    produced") and Qwen3.5-27B-NVFP4-GPTQ (introduction): NVFP4 weights
+ *    rounded to the lattice, per-tensor input global scales.
+ *  - Qwen3.8-27B-MXFP8Attn-MXFP4MLP-lmheadMXFP4, introduction and sections 1,
+ *    2 and 7: MXFP8 = E4M3 + E8M0 per group of 32, MXFP4 = E2M1 + E8M0,
+ *    symmetric, dynamic activations, OCP Microscaling formats; the prior FP8
+ *    kernel rejected N < 128, which this library does not.
+ *
+ * Conventions for every entry point:
+ *  - All tensors are dense, row-major, contiguous device buffers owned by the
+ *    caller.  The library never allocates, frees or keeps a pointer after the
+ *    call returns, and keeps no per-call state.
+ *  - bf16 tensors are arrays of uint16_t bit patterns.
+ *  - Block layout: a block is 32 (MX) or 16 (NVFP4) consecutive elements
+ *    along K of one row.  E2M1 codes are packed two per byte, element 2j in
+ *    the low nibble of byte j: a [rows, K] tensor occupies rows * K/2 bytes.
+ *    E4M3 codes take one byte each.  Scales form a [rows, K/32] (E8M0) or
+ *    [rows, K/16] (E4M3) byte plane.
+ *  - GEMM orientation: Y[M, N] = A[M, K] * W[N, K]^T (W as nn.Linear stores
+ *    it), fp32 accumulation, Y written as bf16 (or fp32 with MX_OUT_F32).
+ *  - Every call only enqueues work on `stream` (0 = the null stream) and never
+ *    synchronizes the host.
+ *  - Arguments are validated before any HIP call.  On an error nothing is
+ *    enqueued and a status code comes back.  Kernels never trap; non-finite
+ *    inputs are outside the contract (unspecified output, no crash).
+ *  - Functions are thread-safe.
+ */
+#ifndef MXLINEAR_H
+#define MXLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A HIP stream handle (hipStream_t); declared opaque so that callers need no
+ * HIP headers. */
+typedef void* mx_stream_t;
+
+typedef enum {
+    MX_OK = 0,
+    MX_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, bad format/rule pair */
+    MX_ERR_SHAPE = 2,       /* m, n or k < 1; k not a multiple of the block */
+    MX_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+    MX_ERR_WORKSPACE = 4,   /* reserved: workspace too small */
+    MX_ERR_UNSUPPORTED = 5, /* current device is not gfx950 */
+    MX_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+} mx_status;
+
+typedef enum {
+    MX_FMT_MXFP4 = 0, /* E2M1 elements, E8M0 scale per 32 */
+    MX_FMT_MXFP8 = 1, /* E4M3 elements, E8M0 scale per 32 */
+    MX_FMT_NVFP4 = 2  /* E2M1 elements, E4M3 scale per 16, fp32 global scale */
+} mx_format;
+
+typedef enum {
+    MX_RULE_FLOOR = 0, /* e = floor(log2 amax) - emax (OCP MX v1.0) */
+    MX_RULE_CEIL = 1,  /* smallest e with amax <= max_elem * 2^e (activations) */
+    MX_RULE_EVEN = 2   /* amax rounded to the element's mantissa width, then FLOOR (weights) */
+} mx_scale_rule;
+
+/* GEMM flags */
+#define MX_OUT_F32 0x1u /* write Y as fp32 instead of bf16 */
+
+/* ABI version of this header (bumped on any signature change). */
+#define MXLINEAR_ABI_VERSION 1
+int mx_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* mx_status_string(mx_status status);
+
+/*
+ * mx_quantize_act -- dynamic per-token activation quantization.
+ * a_bf16: [m, k] bf16.  Outputs a_q and a_s in the block layout above.
+ *  fmt MXFP4 or MXFP8: one E8M0 scale per 32 along k, chosen by `rule`
+ *    (CEIL is the activation rule); element = RNE(x * 2^-e), ties to the even
+ *    code, saturating at the largest magnitude (6 or 448); the sign bit copies
+ *    the input's sign; an all-zero block gets scale byte 0.
+ *  fmt NVFP4: `global_scale` g is the tensor's encode scale (see
+ *    mx_nv_global_scale); per 16 along k: s = RNE_E4M3(amax * g / 6),
+ *    element = RNE_E2M1(x * g / s), both of the exact real values; `rule` is
+ *    ignored.
+ * Requires k % 32 == 0 (MX) or k % 16 == 0 (NVFP4); a_q/a_s 16-byte aligned
+ * when the row size in bytes allows it is not required: only a_bf16 must be
+ * 16-byte aligned.
+ */
+mx_status mx_quantize_act(mx_format fmt, mx_scale_rule rule, const void* a_bf16, int64_t m,
+                          int64_t k, float global_scale, void* a_q, void* a_s,
+                          mx_stream_t stream);
+
+/*
+ * mx_pack_weights -- round-to-nearest weight packing, once per weight tensor
+ * (the exporter step).  Same kernel and layouts as mx_quantize_act with the
+ * [n, k] weight matrix; EVEN is the MXFP4 weight rule.
+ */
+mx_status mx_pack_weights(mx_format fmt, mx_scale_rule rule, const void* w_bf16, int64_t n,
+                          int64_t k, float global_scale, void* w_q, void* w_s,
+                          mx_stream_t stream);
+
+/*
+ * mx_gemm -- block-scaled GEMM on MX operands.
+ * a_fmt, w_fmt in {MXFP4, MXFP8} (mixed pairs allowed).  a_q/a_s are [m, k]
+ * codes and [m, k/32] scales, w_q/w_s are [n, k] codes and [n, k/32] scales.
+ * y is [m, n] bf16 (RNE of the fp32 accumulator) or fp32 with MX_OUT_F32.
+ * Requires k % 32 == 0; any m, n >= 1.  workspace/ws_bytes are reserved and
+ * may be NULL/0.  Operand pointers must be 16-byte aligned.
+ */
+mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void* a_s,
+                  const void* w_q, const void* w_s, int64_t m, int64_t n, int64_t k, void* y,
+                  unsigned flags, void* workspace, size_t ws_bytes, mx_stream_t stream);
+
+/*
+ * mx_gemm_fused -- mx_gemm with the activation quantization computed inside
+ * the GEMM from bf16 A ([m, k]), with scale rule a_rule.  The result equals
+ * mx_quantize_act followed by mx_gemm.
+ */
+mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf16,
+                        mx_format w_fmt, const void* w_q, const void* w_s, int64_t m, int64_t n,
+                        int64_t k, void* y, unsigned flags, void* workspace, size_t ws_bytes,
+                        mx_stream_t stream);
+
+/*
+ * nv_gemm -- NVFP4 x NVFP4 GEMM.  a_q [m, k/2] E2M1, a_s [m, k/16] E4M3,
+ * w_q [n, k/2], w_s [n, k/16].  Y = alpha * sum_k (e2m1_a * s_a) *
+ * (e2m1_w * s_w), with alpha = 1 / (g_a * g_w) supplied by the caller.
+ * Requires k % 16 == 0.  The block products are exact in f16, so the
+ * contraction runs on f16 matrix cores with fp32 accumulation.
+ */
+mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t m,
+                  int64_t n, int64_t k, float alpha, void* y, unsigned flags, void* workspace,
+                  size_t ws_bytes, mx_stream_t stream);
+
+/*
+ * mx_tensor_amax -- largest |x| of a bf16 tensor of `count` elements, written
+ * as fp32 to *amax_dev (device memory).  The NVFP4 global scales come from it
+ * (activations: the running maximum over calibration batches).
+ */
+mx_status mx_tensor_amax(const void* x_bf16, int64_t count, float* amax_dev, mx_stream_t stream);
+
+/*
+ * mx_nv_global_scale -- host helper: g = RNE_fp32(448 * 6 / amax), correctly
+ * rounded; 1 when amax <= 0; the largest finite fp32 when the quotient
+ * leaves the fp32 range.
+ */
+float mx_nv_global_scale(float amax);
+
+/*
+ * mx_gemm_plan -- writes into `name` (capacity `len`) the kernel and tile
+ * configuration that mx_gemm (fused != 0: mx_gemm_fused; a_fmt == NVFP4:
+ * nv_gemm) would launch for this shape, so callers can confirm which path
+ * runs.  Pure host logic; makes no HIP call.
+ */
+mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k,
+                       int fused, char* name, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXLINEAR_H */

@@ -1,0 +1,77 @@
+"""Shared helpers for the GPU parity tests: moving seeded inputs to the GPU,
+running the oracle on sampled rows, and the GEMM acceptance bound.
+
+Acceptance bound (per output element), from the per-element error bound
+|err| <= 1e-4 * sum_k |a_k w_k| that the GEMM must meet: with an fp32 output
+the bound applies as is; with a bf16 output the final rounding of Y to bf16
+adds at most half a bf16 ulp of the larger of |y_ref| and |y_gpu|.  If the
+absolute sum S is 0 the output must be exactly 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+
+def cuda_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
+    a = np.abs(v)
+    out = np.zeros_like(a)
+    nz = a > 0
+    e = np.floor(np.log2(a[nz]))
+    e = np.maximum(e, -126)  # subnormal spacing below the normal range
+    out[nz] = np.ldexp(1.0, (e - 8).astype(np.int64))
+    return out
+
+
+def check_gemm(y_gpu: np.ndarray, y_ref: np.ndarray, s_abs: np.ndarray, bf16_out: bool, what: str):
+    y_gpu = y_gpu.astype(np.float64)
+    err = np.abs(y_gpu - y_ref)
+    bound = 1e-4 * s_abs
+    if bf16_out:
+        bound = bound + half_ulp_bf16(np.maximum(np.abs(y_ref), np.abs(y_gpu)))
+    bad = ~(err <= bound)
+    zero_s = s_abs == 0
+    bad |= zero_s & (y_gpu != 0)
+    nbad = int(bad.sum())
+    if nbad:
+        i = np.argwhere(bad)[0]
+        i = tuple(i)
+        raise AssertionError(f"{what}: {nbad}/{bad.size} outside bound; first at {i}: gpu={y_gpu[i]!r} "
+                             f"ref={y_ref[i]!r} S={s_abs[i]!r} bound={bound[i]!r}")
+    rel = float((err / np.where(s_abs > 0, s_abs, 1)).max()) if err.size else 0.0
+    return rel
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def sample_pairs(m: int, n: int, count: int, seed: int = 0, tile: int = 128):
+    """Random (row, col) pairs plus rows/cols at tile edges and the last ones."""
+    rng = np.random.default_rng(seed)
+    mi = list(rng.integers(0, m, count))
+    ni = list(rng.integers(0, n, count))
+    edge_m = sorted({0, m - 1, *[min(m - 1, t) for t in range(tile - 1, m, tile)][:16],
+                     *[min(m - 1, t) for t in range(tile, m, tile)][:16]})
+    edge_n = sorted({0, n - 1, *[min(n - 1, t) for t in range(tile - 1, n, tile)][:16],
+                     *[min(n - 1, t) for t in range(tile, n, tile)][:16]})
+    for a in edge_m:
+        for b in edge_n[:8]:
+            mi.append(a)
+            ni.append(b)
+    return np.array(mi, np.int64), np.array(ni, np.int64)
+
+
+def oracle_rows_mx(elem, rule, bits: np.ndarray, rows: np.ndarray):
+    """Oracle quantization of selected rows (row-local, so a sample suffices)."""
+    return oracle.mx_quantize(elem, rule, np.ascontiguousarray(bits[rows]))

@@ -1,0 +1,136 @@
+"""Host-side checks of libmxlinear.so that need no GPU: the library loads,
+exports every entry point that include/mxlinear.h declares, validates its
+arguments before touching the HIP runtime, and its host helpers agree with
+the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxlinear.h")
+
+mxl = pytest.importorskip("fp8_quantized_linear_amd")
+L = mxl.lib
+
+OK, INVALID, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED, HIPERR = range(7)
+P = ctypes.c_void_p
+GOOD = P(0x10000)      # 16-byte aligned, never dereferenced by validation failures
+BAD_ALIGN = P(0x10008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("mx_pack_weights", "mx_quantize_act", "mx_gemm", "mx_gemm_fused", "nv_gemm",
+              "mx_tensor_amax", "mx_nv_global_scale", "mx_gemm_plan", "mx_status_string",
+              "mx_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} declared in mxlinear.h but not exported"
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define MXLINEAR_ABI_VERSION (\d+)", open(HEADER).read())
+    assert L.mx_abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    for s in range(7):
+        assert L.mx_status_string(s)
+    assert b"unknown" in L.mx_status_string(99)
+
+
+def q(fn, fmt=0, rule=1, x=GOOD, rows=4, k=64, g=1.0, qp=GOOD, sp=GOOD):
+    return fn(fmt, rule, x, rows, k, g, qp, sp, None)
+
+
+@pytest.mark.parametrize("fn", [L.mx_quantize_act, L.mx_pack_weights])
+def test_quantize_validation(fn):
+    assert q(fn, fmt=7) == INVALID
+    assert q(fn, rule=9) == INVALID
+    assert q(fn, fmt=2, rule=9, g=0.5) != INVALID  # NVFP4 ignores the rule
+    assert q(fn, x=None) == INVALID
+    assert q(fn, qp=None) == INVALID
+    assert q(fn, sp=None) == INVALID
+    assert q(fn, rows=0) == SHAPE
+    assert q(fn, k=0) == SHAPE
+    assert q(fn, k=48) == SHAPE              # MX needs k % 32
+    assert q(fn, fmt=2, k=40, g=1.0) == SHAPE  # NVFP4 needs k % 16
+    assert q(fn, fmt=2, k=48, g=0.0) == INVALID  # global scale must be > 0
+    assert q(fn, fmt=2, k=48, g=float("nan")) == INVALID
+    assert q(fn, x=BAD_ALIGN) == ALIGN
+    # valid arguments reach the device check: without a GPU that is a HIP error
+    st = q(fn)
+    assert st in (OK, UNSUPPORTED, HIPERR)
+
+
+def g(**kw):
+    a = dict(a_fmt=0, w_fmt=0, aq=GOOD, as_=GOOD, wq=GOOD, ws=GOOD, m=16, n=16, k=64, y=GOOD,
+             flags=0)
+    a.update(kw)
+    return L.mx_gemm(a["a_fmt"], a["w_fmt"], a["aq"], a["as_"], a["wq"], a["ws"], a["m"], a["n"],
+                     a["k"], a["y"], a["flags"], None, 0, None)
+
+
+def test_gemm_validation():
+    assert g(a_fmt=2) == INVALID          # NVFP4 goes through nv_gemm
+    assert g(w_fmt=5) == INVALID
+    assert g(aq=None) == INVALID
+    assert g(y=None) == INVALID
+    assert g(flags=0x80) == INVALID
+    assert g(m=0) == SHAPE
+    assert g(n=0) == SHAPE
+    assert g(k=48) == SHAPE
+    assert g(k=1 << 31) == SHAPE
+    assert g(a_fmt=0, w_fmt=1) == UNSUPPORTED  # mixed element types
+    assert g(ws=BAD_ALIGN) == ALIGN
+    assert g(n=96) in (OK, UNSUPPORTED, HIPERR)  # N < 128 is accepted (validation passes)
+    assert g(n=1, m=1, k=32) in (OK, UNSUPPORTED, HIPERR)
+
+
+def test_fused_and_nv_validation():
+    f = L.mx_gemm_fused
+    assert f(0, 9, GOOD, 0, GOOD, GOOD, 4, 4, 64, GOOD, 0, None, 0, None) == INVALID
+    assert f(0, 1, None, 0, GOOD, GOOD, 4, 4, 64, GOOD, 0, None, 0, None) == INVALID
+    assert f(0, 1, GOOD, 0, GOOD, GOOD, 4, 4, 40, GOOD, 0, None, 0, None) == SHAPE
+    assert f(1, 1, GOOD, 0, GOOD, GOOD, 4, 4, 64, GOOD, 0, None, 0, None) == UNSUPPORTED
+    nv = L.nv_gemm
+    assert nv(GOOD, GOOD, GOOD, GOOD, 4, 4, 40, 1.0, GOOD, 0, None, 0, None) == SHAPE
+    assert nv(GOOD, GOOD, GOOD, GOOD, 4, 4, 48, float("inf"), GOOD, 0, None, 0, None) == INVALID
+    assert nv(None, GOOD, GOOD, GOOD, 4, 4, 48, 1.0, GOOD, 0, None, 0, None) == INVALID
+    assert L.mx_tensor_amax(None, 10, GOOD, None) == INVALID
+    assert L.mx_tensor_amax(GOOD, 0, GOOD, None) == SHAPE
+    assert L.mx_tensor_amax(GOOD, 10, P(0x10002), None) == ALIGN
+
+
+def test_plan_names_the_kernel():
+    s = mxl.mx_gemm_plan("mxfp4", "mxfp4", 8192, 17408, 5120)
+    assert "mfma" in s and "mxfp4" in s
+    assert "f16 mfma" in mxl.mx_gemm_plan("nvfp4", "nvfp4", 4096, 5120, 5120)
+    assert "fused" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 64, 64, 64, fused=True)
+    assert mxl.mx_gemm_plan("mxfp8", "mxfp8", 16, 96, 5120)  # N = 96 is a valid plan
+    with pytest.raises(mxl.MXError):
+        mxl.mx_gemm_plan("mxfp4", "mxfp4", 16, 16, 40)
+
+
+def test_global_scale_helper_matches_oracle():
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([np.ldexp(rng.random(3000) + 0.5, rng.integers(-100, 100, 3000)),
+                           [1.0, 3.0, 7.0, 2688.0, 6.0, 448.0, 1e-38, 3e38]]).astype(np.float32)
+    for v in vals:
+        assert np.float32(L.mx_nv_global_scale(float(v))) == oracle.nv_global_scale(float(v)), v
+    assert L.mx_nv_global_scale(0.0) == 1.0

@@ -1,0 +1,201 @@
+"""GPU parity of the GEMMs (mx_gemm, mx_gemm_fused, nv_gemm) against the CPU
+oracle's fp64 product of the dequantized operands.
+
+Bound per element (stated in helpers.check_gemm): |y - y_ref| <= 1e-4 *
+sum_k |a_k w_k|, plus half a bf16 ulp when Y is written as bf16.  Full-size
+configurations are checked on sampled outputs (random pairs plus tile-edge
+rows and columns), computed one by one by the oracle from the quantized rows;
+smaller shapes that still span several tiles and a ragged tail are checked in
+full."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import check_gemm, cuda_bf16, host, sample_pairs
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import fp8_quantized_linear_amd as mxl  # noqa: E402
+
+ELEM = {"mxfp4": "e2m1", "mxfp8": "e4m3"}
+W_RULE = {"mxfp4": "even", "mxfp8": "floor"}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_mx(a_bits, w_bits, fmt="mxfp4", out_f32=False, fused=False):
+    a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
+    k = a_bits.shape[1]
+    wq, ws = mxl.mx_pack_weights(w, fmt=fmt, rule=W_RULE[fmt])
+    aq, as_ = mxl.mx_quantize_act(a, fmt=fmt, rule="ceil")
+    y = mxl.mx_gemm(aq, as_, wq, ws, k, fmt, fmt, out_f32=out_f32)
+    yf = mxl.mx_gemm_fused(a, wq, ws, fmt, "ceil", fmt, out_f32=out_f32) if fused else None
+    torch.cuda.synchronize()
+    return y, yf, (aq, as_), (wq, ws)
+
+
+def oracle_full(a_bits, w_bits, fmt):
+    m, k = a_bits.shape
+    n = w_bits.shape[0]
+    aq, as_ = oracle.mx_quantize(ELEM[fmt], "ceil", a_bits)
+    wq, ws = oracle.mx_quantize(ELEM[fmt], W_RULE[fmt], w_bits)
+    ad = oracle.mx_dequantize(ELEM[fmt], aq, as_, m, k)
+    wd = oracle.mx_dequantize(ELEM[fmt], wq, ws, n, k)
+    y, s = oracle.gemm_dq(ad, wd)
+    return y, s, (aq, as_), (wq, ws)
+
+
+def y_host(y):
+    return host(y.float()) if y.dtype == torch.bfloat16 else host(y)
+
+
+SHAPES = [(16, 256, 256), (200, 416, 300), (1, 32, 1), (129, 160, 257), (33, 5120, 96),
+          (64, 1056, 130), (260, 384, 520)]
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("m,k,n", SHAPES)
+def test_gemm_full_small_shapes(fmt, m, k, n):
+    say(f"gemm {fmt} m={m} k={k} n={n}")
+    a_bits = W.activations_entry_outliers(m, k)
+    w_bits = W.normal_bf16(n, k, 0.02, 1)
+    y_ref, s, (raq, ras), (rwq, rws) = oracle_full(a_bits, w_bits, fmt)
+    for out_f32 in (False, True):
+        y, yf, (aq, as_), (wq, ws) = run_mx(a_bits, w_bits, fmt, out_f32=out_f32, fused=True)
+        assert np.array_equal(host(aq), raq) and np.array_equal(host(as_), ras)
+        assert np.array_equal(host(wq), rwq) and np.array_equal(host(ws), rws)
+        check_gemm(y_host(y), y_ref, s, not out_f32, f"{fmt} {m}x{k}x{n} f32={out_f32}")
+        # the fused prologue quantizes exactly like the standalone quantizer
+        # and feeds the same matrix-core sequence: bitwise equal outputs
+        assert torch.equal(y, yf), "fused != standalone"
+
+
+def test_integer_exact_tiny():
+    # lattice-valued operands with unit scales: every partial sum is an exact
+    # binary fraction, so the fp32 result must equal the oracle exactly
+    rng = np.random.default_rng(8)
+    lat = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    for (m, k, n) in [(16, 128, 16), (32, 64, 48), (5, 96, 7)]:
+        a = (lat[rng.integers(0, 8, (m, k))] * rng.choice([-1, 1], (m, k))).astype(np.float32)
+        w = (lat[rng.integers(0, 8, (n, k))] * rng.choice([-1, 1], (n, k))).astype(np.float32)
+        # each block holds a 4, so its max is 4 or 6 and every rule picks
+        # scale 2^0: the codes are the lattice values themselves
+        a[:, ::32] = 4.0
+        w[:, ::32] = 4.0
+        ab, wb = W._to_bf16_bits(a), W._to_bf16_bits(w)
+        y_ref, s, _, _ = oracle_full(ab, wb, "mxfp4")
+        y, _, _, _ = run_mx(ab, wb, "mxfp4", out_f32=True)
+        assert np.array_equal(y_host(y), y_ref.astype(np.float32)), (m, k, n)
+
+
+def test_decode_shapes_full():
+    for cfg in W.DECODE:
+        say(f"decode {cfg.name}")
+        a_bits, w_bits = cfg.activations(), cfg.weights()
+        y_ref, s, _, _ = oracle_full(a_bits, w_bits, "mxfp4")
+        y, yf, _, _ = run_mx(a_bits, w_bits, "mxfp4", fused=True)
+        check_gemm(y_host(y), y_ref, s, True, cfg.name)
+        assert torch.equal(y, yf)
+
+
+def sampled_check(cfg, fmt, fused=True, count=4096):
+    a_bits, w_bits = cfg.activations(), cfg.weights()
+    say(f"sampled {cfg.name}: generated inputs")
+    y, yf, (aq, as_), (wq, ws) = run_mx(a_bits, w_bits, fmt, fused=fused)
+    mi, ni = sample_pairs(cfg.m, cfg.n, count)
+    ur, ir = np.unique(mi, return_inverse=True)
+    uc, ic = np.unique(ni, return_inverse=True)
+    raq, ras = oracle.mx_quantize(ELEM[fmt], "ceil", np.ascontiguousarray(a_bits[ur]))
+    rwq, rws = oracle.mx_quantize(ELEM[fmt], W_RULE[fmt], np.ascontiguousarray(w_bits[uc]))
+    assert np.array_equal(host(aq)[ur], raq) and np.array_equal(host(as_)[ur], ras)
+    assert np.array_equal(host(wq)[uc], rwq) and np.array_equal(host(ws)[uc], rws)
+    ad = oracle.mx_dequantize(ELEM[fmt], raq, ras, len(ur), cfg.k)
+    wd = oracle.mx_dequantize(ELEM[fmt], rwq, rws, len(uc), cfg.k)
+    y_ref, s = oracle.gemm_dq_pairs(ad, wd, ir, ic)
+    yv = y[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()]
+    check_gemm(y_host(yv), y_ref, s, True, cfg.name)
+    if fused:
+        assert torch.equal(y, yf), f"{cfg.name}: fused != standalone"
+    return y
+
+
+def test_prefill_up_sampled():
+    sampled_check(W.PREFILL_UP, "mxfp4")
+
+
+def test_prefill_down_sampled():
+    sampled_check(W.PREFILL_DOWN, "mxfp4")
+
+
+def test_mxfp8_attention_sampled():
+    sampled_check(W.MXFP8_ATTN, "mxfp8")
+
+
+def test_vocab_projection_sampled():
+    sampled_check(W.MXFP4_VOCAB, "mxfp4", fused=False)
+
+
+def test_deterministic():
+    a_bits = W.activations_entry_outliers(300, 1024)
+    w_bits = W.normal_bf16(700, 1024, 0.02, 1)
+    y1, _, _, _ = run_mx(a_bits, w_bits)
+    y2, _, _, _ = run_mx(a_bits, w_bits)
+    assert torch.equal(y1, y2)
+
+
+# ---------------------------------------------------------------- NVFP4
+def nv_case(a_bits, w_bits, g_a, g_w, out_f32=False):
+    a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
+    k = a_bits.shape[1]
+    aq, as_ = mxl.mx_quantize_act(a, fmt="nvfp4", global_scale=g_a)
+    wq, ws = mxl.mx_pack_weights(w, fmt="nvfp4", global_scale=g_w)
+    alpha = float(np.float32(1.0) / (np.float32(g_a) * np.float32(g_w)))
+    y = mxl.nv_gemm(aq, as_, wq, ws, k, alpha, out_f32=out_f32)
+    torch.cuda.synchronize()
+    return y, (aq, as_), (wq, ws)
+
+
+@pytest.mark.parametrize("m,k,n", [(16, 256, 256), (200, 400, 300), (1, 16, 1), (130, 5120, 96)])
+def test_nvfp4_full_small(m, k, n):
+    a_bits = W.normal_bf16(m, k, 1.0, 0)
+    w_bits = W.normal_bf16(n, k, 0.02, 1)
+    g_a = oracle.nv_global_scale(oracle.bf16_amax(a_bits))
+    g_w = oracle.nv_global_scale(oracle.bf16_amax(w_bits))
+    aq, as_ = oracle.nv_quantize(a_bits, g_a)
+    wq, ws = oracle.nv_quantize(w_bits, g_w)
+    y_ref, s = oracle.gemm_dq(oracle.nv_dequantize(aq, as_, m, k, g_a),
+                              oracle.nv_dequantize(wq, ws, n, k, g_w))
+    for out_f32 in (False, True):
+        y, (gaq, gas), (gwq, gws) = nv_case(a_bits, w_bits, g_a, g_w, out_f32)
+        assert np.array_equal(host(gaq), aq) and np.array_equal(host(gas), as_)
+        assert np.array_equal(host(gwq), wq) and np.array_equal(host(gws), ws)
+        check_gemm(y_host(y), y_ref, s, not out_f32, f"nvfp4 {m}x{k}x{n}")
+
+
+def test_nvfp4_config_sampled():
+    cfg = W.NVFP4
+    run = max(oracle.bf16_amax(b) for b in cfg.calibration_batches())
+    g_a = oracle.nv_global_scale(run)
+    a_bits, w_bits = cfg.activations(), cfg.weights()
+    g_w = oracle.nv_global_scale(oracle.bf16_amax(w_bits))
+    say(f"nvfp4 config g_a={g_a} g_w={g_w}")
+    y, _, _ = nv_case(a_bits, w_bits, g_a, g_w)
+    mi, ni = sample_pairs(cfg.m, cfg.n, 4096)
+    ur, ir = np.unique(mi, return_inverse=True)
+    uc, ic = np.unique(ni, return_inverse=True)
+    aq, as_ = oracle.nv_quantize(np.ascontiguousarray(a_bits[ur]), g_a)
+    wq, ws = oracle.nv_quantize(np.ascontiguousarray(w_bits[uc]), g_w)
+    y_ref, s = oracle.gemm_dq_pairs(oracle.nv_dequantize(aq, as_, len(ur), cfg.k, g_a),
+                                    oracle.nv_dequantize(wq, ws, len(uc), cfg.k, g_w), ir, ic)
+    yv = y[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()]
+    check_gemm(y_host(yv), y_ref, s, True, cfg.name)

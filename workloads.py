@@ -136,3 +136,76 @@ MXFP8_ATTN = Gemm("mxfp8_attn_4096x5120x6144", 4096, 5120, 6144, "mxfp8", "mxfp8
 MXFP4_VOCAB = Gemm("mxfp4_vocab_4096x5120x151936", 4096, 5120, 151936)
 
 ALL = [SMALL, *DECODE, PREFILL_UP, PREFILL_DOWN, NVFP4, MXFP8_ATTN, MXFP4_VOCAB]
+
+
+# --------------------------------------------------------------------------- fuzz corpus
+_E2M1_POINTS = np.array([0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0],
+                        np.float64)  # lattice points and the midpoints between them
+
+
+def _e4m3_points():
+    mags = []
+    for ef in range(16):
+        for m in range(8):
+            if ef == 15 and m == 7:
+                continue
+            mags.append(m * 2.0 ** -9 if ef == 0 else (1 + m / 8) * 2.0 ** (ef - 7))
+    mags = np.array(mags)
+    return np.concatenate([mags, (mags[:-1] + mags[1:]) / 2])
+
+
+_AMAX_MANTISSAS = np.array([1.0, 1.0078125, 1.4921875, 1.5, 1.5078125, 1.7421875, 1.75, 1.7578125,
+                            1.9296875, 1.9375, 1.9453125, 1.9921875])
+
+
+def fuzz_bf16(rows: int, k: int, seed: int = 7) -> np.ndarray:
+    """Adversarial bf16 blocks (32 along k) for quantizer fuzzing.
+
+    Every block draws a binade E in [-135, 120] and one of six shapes:
+    random normals; E2M1 rounding ties (the block max is 2^(E+2), so every
+    scale rule picks exponent E, and the other elements sit on lattice points,
+    midpoints, or one bf16 step either side of them); E4M3 ties (max
+    2^(E+8)); a block max with a mantissa at a rule threshold; all-zero or
+    negative-zero blocks; mixed huge and tiny values.  Values are built
+    exactly in bf16, so the final rounding changes nothing.
+    """
+    rng = np.random.default_rng(seed)
+    nblk = rows * k // 32
+    out = np.zeros((nblk, 32), np.float64)
+    kind = rng.integers(0, 6, nblk)
+    E = rng.integers(-135, 121, nblk)
+    p2 = np.ldexp(1.0, E)[:, None]
+    sign = np.where(rng.random((nblk, 32)) < 0.5, -1.0, 1.0)
+    # 0: normals
+    out[kind == 0] = (rng.standard_normal((nblk, 32)) * p2)[kind == 0]
+    # 1: E2M1 ties
+    t = _E2M1_POINTS[rng.integers(0, len(_E2M1_POINTS), (nblk, 32))] * p2 * sign
+    t[:, 0] = np.ldexp(1.0, E + 2)
+    out[kind == 1] = t[kind == 1]
+    # 2: E4M3 ties
+    pts = _e4m3_points()
+    t8 = pts[rng.integers(0, len(pts), (nblk, 32))] * p2 * sign
+    t8[:, 0] = np.ldexp(1.0, E + 8)
+    out[kind == 2] = t8[kind == 2]
+    # 3: block max on a threshold mantissa
+    tm = rng.standard_normal((nblk, 32)) * p2 * 0.3
+    tm[:, 5] = _AMAX_MANTISSAS[rng.integers(0, len(_AMAX_MANTISSAS), nblk)] * p2[:, 0] * sign[:, 5]
+    out[kind == 3] = tm[kind == 3]
+    # 4: zeros, some negative
+    z = np.where(rng.random((nblk, 32)) < 0.5, -0.0, 0.0)
+    out[kind == 4] = z[kind == 4]
+    # 5: mixed magnitudes
+    mix = rng.standard_normal((nblk, 32)) * np.ldexp(1.0, rng.integers(-60, 60, (nblk, 32)))
+    out[kind == 5] = mix[kind == 5]
+    # keep everything finite in bf16 and round to bf16 exactly once
+    out = np.clip(out, -3.0e38, 3.0e38).astype(np.float32)
+    bits = _to_bf16_bits(out.reshape(rows, k))
+    # one bf16 step either side of a tie for a quarter of the tie blocks
+    bump = (rng.random((nblk, 32)) < 0.25) & ((kind == 1) | (kind == 2))[:, None]
+    bump[:, 0] = False
+    step = np.where(rng.random((nblk, 32)) < 0.5, 1, -1).astype(np.int32)
+    b = bits.reshape(nblk, 32).astype(np.int32)
+    mag = b & 0x7FFF
+    newmag = np.clip(mag + step, 0, 0x7F7F)
+    b = np.where(bump & (mag != 0), (b & 0x8000) | newmag, b)
+    return b.astype(np.uint16).reshape(rows, k)
