@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libmxlinear.so")
 FORMATS = {"mxfp4": 0, "mxfp8": 1, "nvfp4": 2}
 RULES = {"floor": 0, "ceil": 1, "even": 2}
 MX_OUT_F32 = 0x1
+MX_FP8_FAST = 0x2
 STATUS = {0: "MX_OK", 1: "MX_ERR_INVALID_ARG", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN",
           4: "MX_ERR_WORKSPACE", 5: "MX_ERR_UNSUPPORTED", 6: "MX_ERR_HIP"}
 
@@ -56,7 +57,7 @@ def _load():
     L.mx_tensor_amax.restype, L.mx_tensor_amax.argtypes = i32, [P, i64, P, P]
     L.mx_nv_global_scale.restype, L.mx_nv_global_scale.argtypes = f32, [f32]
     L.mx_gemm_plan.restype = i32
-    L.mx_gemm_plan.argtypes = [i32, i32, i64, i64, i64, i32, ctypes.c_char_p, sz]
+    L.mx_gemm_plan.argtypes = [i32, i32, i64, i64, i64, i32, u32, ctypes.c_char_p, sz]
     return L
 
 
@@ -139,9 +140,14 @@ def _gemm_out(m, n, device, out_f32, y):
     return torch.empty((m, n), dtype=torch.float32 if out_f32 else torch.bfloat16, device=device)
 
 
+def _flags(out_f32, fp8_fast):
+    return (MX_OUT_F32 if out_f32 else 0) | (MX_FP8_FAST if fp8_fast else 0)
+
+
 def mx_gemm(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str = "mxfp4",
-            out_f32: bool = False, y=None):
-    """Y[m, n] = A W^T on MX codes/scales (bf16 out, or fp32 with out_f32)."""
+            out_f32: bool = False, y=None, fp8_fast: bool = False):
+    """Y[m, n] = A W^T on MX codes/scales (bf16 out, or fp32 with out_f32).
+    fp8_fast selects the FP8 matrix cores for MXFP8 (inexact accumulation)."""
     for t, nm in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
         _need(t, torch.uint8, nm)
     m, n = a_q.shape[0], w_q.shape[0]
@@ -151,13 +157,13 @@ def mx_gemm(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str = "mxfp
         raise ValueError("scale tensors do not match k")
     y = _gemm_out(m, n, a_q.device, out_f32, y)
     st = lib.mx_gemm(_fmt(a_fmt), _fmt(w_fmt), _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, n, k,
-                     _ptr(y), MX_OUT_F32 if out_f32 else 0, None, 0, _stream(a_q))
+                     _ptr(y), _flags(out_f32, fp8_fast), None, 0, _stream(a_q))
     _check(st, "mx_gemm")
     return y
 
 
 def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str = "ceil",
-                  w_fmt: str = "mxfp4", out_f32: bool = False, y=None):
+                  w_fmt: str = "mxfp4", out_f32: bool = False, y=None, fp8_fast: bool = False):
     """mx_gemm with the activation quantization done inside the GEMM from bf16 a[m, k]."""
     _need(a, torch.bfloat16, "a")
     _need(w_q, torch.uint8, "w_q")
@@ -168,7 +174,7 @@ def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str =
         raise ValueError("weight tensors do not match k")
     y = _gemm_out(m, n, a.device, out_f32, y)
     st = lib.mx_gemm_fused(_fmt(a_fmt), _rule(a_rule), _ptr(a), _fmt(w_fmt), _ptr(w_q), _ptr(w_s),
-                           m, n, k, _ptr(y), MX_OUT_F32 if out_f32 else 0, None, 0, _stream(a))
+                           m, n, k, _ptr(y), _flags(out_f32, fp8_fast), None, 0, _stream(a))
     _check(st, "mx_gemm_fused")
     return y
 
@@ -201,8 +207,10 @@ def mx_nv_global_scale(amax: float) -> float:
     return float(lib.mx_nv_global_scale(float(amax)))
 
 
-def mx_gemm_plan(a_fmt: str, w_fmt: str, m: int, n: int, k: int, fused: bool = False) -> str:
+def mx_gemm_plan(a_fmt: str, w_fmt: str, m: int, n: int, k: int, fused: bool = False,
+                 fp8_fast: bool = False) -> str:
     """Name of the kernel/tile configuration the GEMM would launch for this shape."""
     buf = ctypes.create_string_buffer(256)
-    _check(lib.mx_gemm_plan(_fmt(a_fmt), _fmt(w_fmt), m, n, k, int(fused), buf, 256), "mx_gemm_plan")
+    _check(lib.mx_gemm_plan(_fmt(a_fmt), _fmt(w_fmt), m, n, k, int(fused), _flags(False, fp8_fast),
+                            buf, 256), "mx_gemm_plan")
     return buf.value.decode()

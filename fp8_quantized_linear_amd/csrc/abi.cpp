@@ -27,8 +27,15 @@ hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, 
 hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const void* wq, const void* ws, int64_t m,
                               int64_t n, int64_t k, float alpha, void* y, int out_f32,
                               hipStream_t stream);
+hipError_t mxl_launch_mxfp8_exact_gemm(const void* aq, const void* as, const void* wq, const void* ws,
+                                       int64_t m, int64_t n, int64_t k, void* y, int out_f32,
+                                       hipStream_t stream);
+hipError_t mxl_launch_mxfp8_exact_gemm_fused(int a_rule, const void* a_bf16, const void* wq, const void* ws,
+                                             int64_t m, int64_t n, int64_t k, void* y, int out_f32,
+                                             hipStream_t stream);
 const char* mxl_mx_gemm_config_name(void);
 const char* mxl_nv_gemm_config_name(void);
+const char* mxl_mxfp8_exact_config_name(void);
 }
 
 namespace {
@@ -144,18 +151,21 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
     if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || a_fmt == MX_FMT_NVFP4 || w_fmt == MX_FMT_NVFP4)
         return MX_ERR_INVALID_ARG;
     if (!a_q || !a_s || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
-    if (flags & ~MX_OUT_F32) return MX_ERR_INVALID_ARG;
+    if (flags & ~(MX_OUT_F32 | MX_FP8_FAST)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, 32);
     if (st != MX_OK) return st;
     if (a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
     if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y))
         return MX_ERR_ALIGN;
     if ((st = check_device()) != MX_OK) return st;
+    const int f32 = (flags & MX_OUT_F32) ? 1 : 0;
+    const bool exact8 = a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST);
     if (log_enabled())
         std::fprintf(stderr, "[mxlinear] mx_gemm m=%lld n=%lld k=%lld -> %s\n", (long long)m, (long long)n,
-                     (long long)k, mxl_mx_gemm_config_name());
-    return from_hip(mxl_launch_mx_gemm(bits_of(a_fmt), bits_of(w_fmt), a_q, a_s, w_q, w_s, m, n, k, y,
-                                       (flags & MX_OUT_F32) ? 1 : 0, static_cast<hipStream_t>(stream)));
+                     (long long)k, exact8 ? mxl_mxfp8_exact_config_name() : mxl_mx_gemm_config_name());
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (exact8) return from_hip(mxl_launch_mxfp8_exact_gemm(a_q, a_s, w_q, w_s, m, n, k, y, f32, hs));
+    return from_hip(mxl_launch_mx_gemm(bits_of(a_fmt), bits_of(w_fmt), a_q, a_s, w_q, w_s, m, n, k, y, f32, hs));
 }
 
 mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf16, mx_format w_fmt,
@@ -168,15 +178,18 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf1
         !valid_rule(a_rule))
         return MX_ERR_INVALID_ARG;
     if (!a_bf16 || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
-    if (flags & ~MX_OUT_F32) return MX_ERR_INVALID_ARG;
+    if (flags & ~(MX_OUT_F32 | MX_FP8_FAST)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, 32);
     if (st != MX_OK) return st;
     if (a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
     if (!aligned16(a_bf16) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y)) return MX_ERR_ALIGN;
     if ((st = check_device()) != MX_OK) return st;
+    const int f32 = (flags & MX_OUT_F32) ? 1 : 0;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST))
+        return from_hip(mxl_launch_mxfp8_exact_gemm_fused((int)a_rule, a_bf16, w_q, w_s, m, n, k, y, f32, hs));
     return from_hip(mxl_launch_mx_gemm_fused(bits_of(a_fmt), (int)a_rule, a_bf16, bits_of(w_fmt), w_q, w_s,
-                                             m, n, k, y, (flags & MX_OUT_F32) ? 1 : 0,
-                                             static_cast<hipStream_t>(stream)));
+                                             m, n, k, y, f32, hs));
 }
 
 mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t m, int64_t n,
@@ -240,7 +253,7 @@ float mx_nv_global_scale(float amax)
 }
 
 mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k, int fused,
-                       char* name, size_t len)
+                       unsigned flags, char* name, size_t len)
 {
     if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || !name || len == 0) return MX_ERR_INVALID_ARG;
     const bool nv = a_fmt == MX_FMT_NVFP4;
@@ -249,7 +262,9 @@ mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, i
     if (st != MX_OK) return st;
     if (!nv && a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
     const char* fmt = nv ? "nvfp4" : (a_fmt == MX_FMT_MXFP4 ? "mxfp4" : "mxfp8");
-    const char* cfg = nv ? mxl_nv_gemm_config_name() : mxl_mx_gemm_config_name();
+    const bool exact8 = a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST);
+    const char* cfg = nv ? mxl_nv_gemm_config_name()
+                         : (exact8 ? mxl_mxfp8_exact_config_name() : mxl_mx_gemm_config_name());
     std::snprintf(name, len, "%s%s %s", fused && !nv ? "fused-quant " : "", fmt, cfg);
     return MX_OK;
 }

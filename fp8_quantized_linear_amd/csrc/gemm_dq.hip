@@ -1,0 +1,385 @@
+// gemm_dq.hip -- GEMMs that dequantize their operands exactly into 16-bit
+// floats while staging them into LDS and contract them on f16/bf16 matrix
+// cores with fp32 accumulation:
+//
+//   NVFP4: Y = alpha * sum_k (e2m1_a * s_a) * (e2m1_w * s_w), E4M3 scale per 16,
+//          alpha = 1 / (g_a * g_w)                                   -> f16
+//   MXFP8: Y = sum_k (e4m3_a * 2^ea) * (e4m3_w * 2^ew), E8M0 scale per 32 -> bf16
+//
+// Operations: the NVFP4 W4A4 path of Qwen3.5-27B-NVFP4-GPTQ and
+// Qwen3.5-27B-NVFP4-RTN-weight-only (introductions: FP4 elements, per-block
+// scales, per-tensor global scales), and the MXFP8 W8A8 attention projections
+// of Qwen3.8-27B-MXFP8Attn-MXFP4MLP-lmheadMXFP4 (introduction, section 2).
+//
+// Why these do not use the block-scaled FP4/FP8 matrix cores:
+//  - NVFP4 scales are E4M3 per 16 elements; the scaled instructions accept
+//    only power-of-two scales per 32.  e2m1 (2 significant bits) times an
+//    E4M3 scale (4 bits, 2^-9 .. 448) is exact in f16.
+//  - The FP8 matrix-core instructions of gfx950 do not accumulate exactly:
+//    measured on hardware, their error reaches about 1.7e-4 (scaled 32x32x64)
+//    to 3.9e-4 (unscaled 32x32x16) of sum|a*b| on operands with a wide
+//    exponent spread, beyond the 1e-4 bound.  The f16/bf16 instructions stay at
+//    fp32 rounding level.  An E4M3 value times its power-of-two block scale is
+//    exact in bf16 (8-bit significand, fp32 exponent range) for every block
+//    whose scale exponent is at least -117; below that, dequantized values
+//    under 2^-126 are flushed (only blocks with amax below ~2^-110 have them).
+//
+// 16-bit matrix-core layout (32x32x16): lane l = r + 32 g holds row/column r
+// and the 8 consecutive K elements [8g, 8g + 8) of the 16-wide step.
+#include "mx_device.h"
+
+namespace mxl {
+
+enum : int { DQ_NVFP4 = 0, DQ_MXFP8 = 1 };
+
+constexpr int DQ_BK = 64;                 // K elements per LDS stage
+constexpr int DQ_ROW_BYTES = DQ_BK * 2;   // 16-bit bytes per LDS row per stage (8 chunks)
+
+__device__ __forceinline__ int dq_swz(int row) { return row & 7; }
+
+template <int KIND>
+struct DqTraits {
+    // global bytes of one row per stage, 16-byte chunks per row per stage
+    static constexpr int SRC_ROW_BYTES = KIND == DQ_NVFP4 ? DQ_BK / 2 : DQ_BK;
+    static constexpr int CHUNKS = SRC_ROW_BYTES / 16;
+    static constexpr int ELEMS_PER_CHUNK = KIND == DQ_NVFP4 ? 32 : 16;
+    static constexpr int SCALE_BLOCK = KIND == DQ_NVFP4 ? 16 : 32;
+};
+
+typedef __bf16 bf16x2_t_ __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// E4M3 code -> f16 (exact; NaN codes never occur in valid scales).
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t c)
+{
+    const uint32_t ef = (c >> 3) & 15u, m = c & 7u;
+    float v = ef == 0 ? (float)m * 0x1p-9f : __uint_as_float(((ef + 120u) << 23) | (m << 20));
+    return (_Float16)((c & 0x80u) ? -v : v);
+}
+
+// 8 E2M1 codes (one dword, element 2j in the low nibble of byte j) times an
+// E4M3 scale, as 8 f16 values.
+__device__ __forceinline__ uint4 dequant8_nvfp4(uint32_t codes, _Float16 s)
+{
+    const half2_t s2 = {s, s};
+    half2_t h[4];
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;  // exact products
+    h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s2;
+    h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s2;
+    h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s2;
+    uint4 out;
+    __builtin_memcpy(&out, h, 16);
+    return out;
+}
+
+// Halve bf16 pairs by exponent decrement; values that would leave the normal
+// range are flushed to signed zero.
+__device__ __forceinline__ uint32_t bf16x2_halve(uint32_t v)
+{
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        uint32_t h = (v >> (16 * i)) & 0xFFFFu;
+        h = ((h >> 7) & 0xFFu) >= 2u ? h - 0x80u : (h & 0x8000u);
+        out |= h << (16 * i);
+    }
+    return out;
+}
+
+// 8 E4M3 codes (uint2) times 2^e, as 8 bf16 values: the conversion multiplies
+// by the power of two of its fp32 scale operand, which must be a normal fp32,
+// so e = -127 converts with 2^-126 and halves afterwards.
+__device__ __forceinline__ uint4 dequant8_mxfp8(uint2 codes, int e)
+{
+    const float s = pow2f(e < -126 ? -126 : e);
+    bf16x2_t_ h[4];
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, s, false);
+    h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, s, true);
+    h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, s, false);
+    h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, s, true);
+    uint4 out;
+    __builtin_memcpy(&out, h, 16);
+    if (e < -126) {
+        out.x = bf16x2_halve(out.x);
+        out.y = bf16x2_halve(out.y);
+        out.z = bf16x2_halve(out.z);
+        out.w = bf16x2_halve(out.w);
+    }
+    return out;
+}
+
+struct DqArgs {
+    const uint8_t* a_q; const uint8_t* a_s;
+    const uint8_t* w_q; const uint8_t* w_s;
+    void* y;
+    int M, N, K;
+    float alpha;
+};
+
+// FUSED_A (MXFP8 only): A arrives as bf16 [M, K]; each 8-element chunk is
+// quantized in registers (block-32 scale by A_RULE over a lane quad, E4M3
+// codes) and dequantized back exactly, as mx_quantize_act would have done.
+template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL>
+__global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
+{
+    using T = DqTraits<KIND>;
+    static_assert(!FUSED_A || KIND == DQ_MXFP8, "fused quantization is for MXFP8");
+    constexpr int NT = WM * WN * 64;
+    constexpr int A_TILE = BM * DQ_ROW_BYTES, W_TILE = BN * DQ_ROW_BYTES;
+    constexpr int STAGE = A_TILE + W_TILE;
+    constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
+    constexpr int A_CPR = FUSED_A ? DQ_BK * 2 / 16 : T::CHUNKS;   // A chunks per row per stage
+    constexpr int A_CH = BM * A_CPR, W_CH = BN * T::CHUNKS;
+    static_assert(!FUSED_A || (A_CH % NT == 0 && NT % A_CPR == 0), "fused tile mapping");
+    constexpr int A_PER_T = (A_CH + NT - 1) / NT, W_PER_T = (W_CH + NT - 1) / NT;
+
+    extern __shared__ __align__(16) uint8_t smem[];
+
+    const int tiles_n = (p.N + BN - 1) / BN;
+    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int K = p.K, KS = K / T::SCALE_BLOCK;
+    const int row_bytes = KIND == DQ_NVFP4 ? K / 2 : K;
+    const int nk = (K + DQ_BK - 1) / DQ_BK;
+
+    uint4 ra[A_PER_T], rw[W_PER_T];
+    uint32_t sa[A_PER_T], sw[W_PER_T];  // scale bytes of the chunk (NVFP4: two, MXFP8: one)
+
+    auto load_one = [&](const uint8_t* q, const uint8_t* s, int rows_lim, int r0, int qi, int kt,
+                        uint4& v, uint32_t& sc) {
+        const int row = qi / T::CHUNKS, c = qi % T::CHUNKS;
+        const int gr = r0 + row;
+        const int kb = kt * T::SRC_ROW_BYTES + c * 16;
+        v = make_uint4(0, 0, 0, 0);
+        sc = KIND == DQ_NVFP4 ? 0u : 127u;
+        if (gr < rows_lim && kb < row_bytes) {
+            const uint8_t* src = q + (size_t)gr * row_bytes + kb;
+            if ((row_bytes & 15) == 0) {
+                v = *reinterpret_cast<const uint4*>(src);
+            } else {
+                // NVFP4 with k % 32 == 16: rows are 8-byte aligned and the last
+                // chunk of a row holds a single block of 16 elements
+                const uint2 lo = *reinterpret_cast<const uint2*>(src);
+                const uint2 hi = kb + 8 < row_bytes ? *reinterpret_cast<const uint2*>(src + 8) : make_uint2(0, 0);
+                v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+            if (KIND == DQ_NVFP4) {
+                const int blk = kt * (DQ_BK / 16) + c * 2;
+                sc = (uint32_t)s[(size_t)gr * KS + blk];
+                if (blk + 1 < KS) sc |= (uint32_t)s[(size_t)gr * KS + blk + 1] << 8;
+            } else {
+                sc = (uint32_t)s[(size_t)gr * KS + (kt * DQ_BK + c * 16) / 32];
+            }
+        }
+    };
+    auto load_stage = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i) {
+            const int qi = tid + i * NT;
+            if (FUSED_A) {
+                const int row = qi / A_CPR, c = qi % A_CPR, gm = m0 + row;
+                const int kb = kt * DQ_BK * 2 + c * 16;
+                ra[i] = make_uint4(0, 0, 0, 0);
+                if (gm < p.M && kb < K * 2)
+                    ra[i] = *reinterpret_cast<const uint4*>(p.a_q + (size_t)gm * K * 2 + kb);
+            } else if (qi < A_CH) {
+                load_one(p.a_q, p.a_s, p.M, m0, qi, kt, ra[i], sa[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < W_PER_T; ++i) {
+            const int qi = tid + i * NT;
+            if (qi < W_CH) load_one(p.w_q, p.w_s, p.N, n0, qi, kt, rw[i], sw[i]);
+        }
+    };
+    auto store_one = [&](uint8_t* tile, int qi, const uint4& v, uint32_t sc) {
+        const int row = qi / T::CHUNKS, c = qi % T::CHUNKS;
+        if (KIND == DQ_NVFP4) {
+            const _Float16 s0 = e4m3_to_f16(sc & 0xFFu), s1 = e4m3_to_f16((sc >> 8) & 0xFFu);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {   // 8 elements per dword -> one 16-B chunk of f16
+                const uint4 d = dequant8_nvfp4(w[h], h < 2 ? s0 : s1);
+                const int chunk = (c * 4 + h) ^ dq_swz(row);
+                *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + chunk * 16) = d;
+            }
+        } else {
+            const int e = (int)sc - 127;
+            const uint4 d0 = dequant8_mxfp8(make_uint2(v.x, v.y), e);
+            const uint4 d1 = dequant8_mxfp8(make_uint2(v.z, v.w), e);
+            *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + (((2 * c) ^ dq_swz(row)) * 16)) = d0;
+            *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + (((2 * c + 1) ^ dq_swz(row)) * 16)) = d1;
+        }
+    };
+    auto store_stage = [&](int buf) {
+        uint8_t* a_t = smem + buf * STAGE;
+        uint8_t* w_t = a_t + A_TILE;
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i) {
+            const int qi = tid + i * NT;
+            if (FUSED_A) {
+                // 8 bf16 per lane; a lane quad holds one block of 32
+                const int row = qi / A_CPR, c = qi % A_CPR;
+                const uint32_t amax = quad_max_u32(amax_bits8(ra[i]));
+                const int e = scale_exponent<ELEM_E4M3, A_RULE>(amax);
+                const uint4 d = dequant8_mxfp8(encode8_e4m3(ra[i], e), e);
+                *reinterpret_cast<uint4*>(a_t + row * DQ_ROW_BYTES + ((c ^ dq_swz(row)) * 16)) = d;
+            } else if (qi < A_CH) {
+                store_one(a_t, qi, ra[i], sa[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < W_PER_T; ++i) {
+            const int qi = tid + i * NT;
+            if (qi < W_CH) store_one(w_t, qi, rw[i], sw[i]);
+        }
+    };
+
+    float16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int r32 = lane & 31, g = lane >> 5;
+    auto compute_stage = [&](int buf) {
+        const uint8_t* a_t = smem + buf * STAGE;
+        const uint8_t* w_t = a_t + A_TILE;
+#pragma unroll
+        for (int kk = 0; kk < DQ_BK / 16; ++kk) {
+            uint4 fa[FM], fw[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = wm * WTM + i * 32 + r32;
+                fa[i] = *reinterpret_cast<const uint4*>(a_t + row * DQ_ROW_BYTES + (((2 * kk + g) ^ dq_swz(row)) * 16));
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int row = wn * WTN + j * 32 + r32;
+                fw[j] = *reinterpret_cast<const uint4*>(w_t + row * DQ_ROW_BYTES + (((2 * kk + g) ^ dq_swz(row)) * 16));
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    if (KIND == DQ_NVFP4) {
+                        half8_t a8, b8;
+                        __builtin_memcpy(&a8, &fa[i], 16);
+                        __builtin_memcpy(&b8, &fw[j], 16);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, b8, acc[i][j], 0, 0, 0);
+                    } else {
+                        bf16x8_t a8, b8;
+                        __builtin_memcpy(&a8, &fa[i], 16);
+                        __builtin_memcpy(&b8, &fw[j], 16);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, acc[i][j], 0, 0, 0);
+                    }
+                }
+        }
+    };
+
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool more = kt + 1 < nk;
+        if (more) load_stage(kt + 1);
+        compute_stage(kt & 1);
+        if (more) store_stage((kt + 1) & 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * WTN + j * 32 + r32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * WTM + i * 32 + (r / 4) * 8 + g * 4 + (r % 4);
+                if (m < p.M && n < p.N) {
+                    const float v = KIND == DQ_NVFP4 ? acc[i][j][r] * p.alpha : acc[i][j][r];
+                    if (OUT_F32) {
+                        reinterpret_cast<float*>(p.y)[(size_t)m * p.N + n] = v;
+                    } else {
+                        uint32_t u = __float_as_uint(v);
+                        u += 0x7FFFu + ((u >> 16) & 1u);
+                        reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + n] = (uint16_t)(u >> 16);
+                    }
+                }
+            }
+        }
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL>
+hipError_t launch_dq(const DqArgs& a, hipStream_t stream)
+{
+    constexpr int LDS = 2 * (BM + BN) * DQ_ROW_BYTES;
+    auto kern = dq_gemm_kernel<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    hipLaunchKernelGGL(kern, dim3(tiles), dim3(WM * WN * 64), LDS, stream, a);
+    return hipGetLastError();
+}
+
+} // namespace mxl
+
+using namespace mxl;
+
+extern "C" hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const void* wq, const void* ws,
+                                         int64_t m, int64_t n, int64_t k, float alpha, void* y,
+                                         int out_f32, hipStream_t stream)
+{
+    DqArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
+             static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
+             (int)m, (int)n, (int)k, alpha};
+    if (out_f32) return launch_dq<DQ_NVFP4, 128, 128, 2, 2, true>(a, stream);
+    return launch_dq<DQ_NVFP4, 128, 128, 2, 2, false>(a, stream);
+}
+
+extern "C" hipError_t mxl_launch_mxfp8_exact_gemm(const void* aq, const void* as, const void* wq,
+                                                  const void* ws, int64_t m, int64_t n, int64_t k, void* y,
+                                                  int out_f32, hipStream_t stream)
+{
+    DqArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
+             static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
+             (int)m, (int)n, (int)k, 1.0f};
+    if (out_f32) return launch_dq<DQ_MXFP8, 128, 128, 2, 2, true>(a, stream);
+    return launch_dq<DQ_MXFP8, 128, 128, 2, 2, false>(a, stream);
+}
+
+template <int RULE>
+static hipError_t fused8(const DqArgs& a, int out_f32, hipStream_t stream)
+{
+    if (out_f32) return launch_dq<DQ_MXFP8, 128, 128, 2, 2, true, true, RULE>(a, stream);
+    return launch_dq<DQ_MXFP8, 128, 128, 2, 2, false, true, RULE>(a, stream);
+}
+
+extern "C" hipError_t mxl_launch_mxfp8_exact_gemm_fused(int a_rule, const void* a_bf16, const void* wq,
+                                                        const void* ws, int64_t m, int64_t n, int64_t k,
+                                                        void* y, int out_f32, hipStream_t stream)
+{
+    DqArgs a{static_cast<const uint8_t*>(a_bf16), nullptr, static_cast<const uint8_t*>(wq),
+             static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, 1.0f};
+    if (a_rule == RULE_CEIL) return fused8<RULE_CEIL>(a, out_f32, stream);
+    if (a_rule == RULE_FLOOR) return fused8<RULE_FLOOR>(a, out_f32, stream);
+    return fused8<RULE_EVEN>(a, out_f32, stream);
+}
+
+extern "C" const char* mxl_nv_gemm_config_name(void)
+{
+    return "dq_gemm_kernel<nvfp4 -> exact f16, tile 128x128x64, 2x2 waves of 64x64, f16 mfma 32x32x16>";
+}
+
+extern "C" const char* mxl_mxfp8_exact_config_name(void)
+{
+    return "dq_gemm_kernel<mxfp8 -> exact bf16, tile 128x128x64, 2x2 waves of 64x64, bf16 mfma 32x32x16>";
+}

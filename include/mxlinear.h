@@ -83,10 +83,14 @@ typedef enum {
 } mx_scale_rule;
 
 /* GEMM flags */
-#define MX_OUT_F32 0x1u /* write Y as fp32 instead of bf16 */
+#define MX_OUT_F32 0x1u  /* write Y as fp32 instead of bf16 */
+#define MX_FP8_FAST 0x2u /* MXFP8 only: contract on the FP8 matrix cores (about 2x the
+                          * throughput); their internal accumulation is inexact, with
+                          * errors measured up to ~2e-4 * sum|a*b|, so this opts out of
+                          * the 1e-4 bound that the default path meets */
 
 /* ABI version of this header (bumped on any signature change). */
-#define MXLINEAR_ABI_VERSION 1
+#define MXLINEAR_ABI_VERSION 2
 int mx_abi_version(void);
 
 /* Static text for a status code; never NULL. */
@@ -103,9 +107,9 @@ const char* mx_status_string(mx_status status);
  *    mx_nv_global_scale); per 16 along k: s = RNE_E4M3(amax * g / 6),
  *    element = RNE_E2M1(x * g / s), both of the exact real values; `rule` is
  *    ignored.
- * Requires k % 32 == 0 (MX) or k % 16 == 0 (NVFP4); a_q/a_s 16-byte aligned
- * when the row size in bytes allows it is not required: only a_bf16 must be
- * 16-byte aligned.
+ * Requires k % 32 == 0 (MX) or k % 16 == 0 (NVFP4) and 16-byte aligned
+ * pointers.  Each block is quantized independently, so the result does not
+ * depend on how rows are batched.
  */
 mx_status mx_quantize_act(mx_format fmt, mx_scale_rule rule, const void* a_bf16, int64_t m,
                           int64_t k, float global_scale, void* a_q, void* a_s,
@@ -122,11 +126,17 @@ mx_status mx_pack_weights(mx_format fmt, mx_scale_rule rule, const void* w_bf16,
 
 /*
  * mx_gemm -- block-scaled GEMM on MX operands.
- * a_fmt, w_fmt in {MXFP4, MXFP8} (mixed pairs allowed).  a_q/a_s are [m, k]
- * codes and [m, k/32] scales, w_q/w_s are [n, k] codes and [n, k/32] scales.
- * y is [m, n] bf16 (RNE of the fp32 accumulator) or fp32 with MX_OUT_F32.
- * Requires k % 32 == 0; any m, n >= 1.  workspace/ws_bytes are reserved and
- * may be NULL/0.  Operand pointers must be 16-byte aligned.
+ * a_fmt == w_fmt in {MXFP4, MXFP8} (a mixed pair returns MX_ERR_UNSUPPORTED).
+ * a_q/a_s are [m, k] codes and [m, k/32] scales, w_q/w_s are [n, k] codes and
+ * [n, k/32] scales.  y is [m, n] bf16 (RNE of the fp32 accumulator) or fp32
+ * with MX_OUT_F32.  Requires k % 32 == 0; any m, n >= 1 (no lower limit on n).
+ * MXFP4 runs on the block-scaled FP4 matrix cores, whose block sums are exact.
+ * MXFP8 by default dequantizes each operand exactly to bf16 (element times
+ * its power-of-two block scale) and runs on bf16 matrix cores; MX_FP8_FAST
+ * selects the FP8 matrix cores instead.  Result: fp32 accumulation within
+ * 1e-4 * sum_k |a_k w_k| of the exact product (plus the bf16 output rounding).
+ * workspace/ws_bytes are reserved and may be NULL/0.  All pointers must be
+ * 16-byte aligned.
  */
 mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void* a_s,
                   const void* w_q, const void* w_s, int64_t m, int64_t n, int64_t k, void* y,
@@ -169,12 +179,12 @@ float mx_nv_global_scale(float amax);
 
 /*
  * mx_gemm_plan -- writes into `name` (capacity `len`) the kernel and tile
- * configuration that mx_gemm (fused != 0: mx_gemm_fused; a_fmt == NVFP4:
- * nv_gemm) would launch for this shape, so callers can confirm which path
- * runs.  Pure host logic; makes no HIP call.
+ * configuration that mx_gemm with these flags (fused != 0: mx_gemm_fused;
+ * a_fmt == NVFP4: nv_gemm) would launch for this shape, so callers can
+ * confirm which path runs.  Pure host logic; makes no HIP call.
  */
 mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k,
-                       int fused, char* name, size_t len);
+                       int fused, unsigned flags, char* name, size_t len);
 
 #ifdef __cplusplus
 }
