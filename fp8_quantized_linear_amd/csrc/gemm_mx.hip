@@ -81,19 +81,28 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
-// Tile-ordering: consecutive workgroups walk down M within a column group of
-// GROUP_N tiles so that tiles sharing W rows run close together in time.
-template <int BM, int BN>
+// Tile ordering.  Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup i runs on XCD i % 8), and each XCD has its own L2.  So the
+// workgroup id is first remapped so that each XCD receives one contiguous
+// range of the tile order, and the tile order itself walks groups of GROUP_N
+// tile columns down M (N fastest inside a group): the tiles an XCD runs at
+// the same time share a few A row panels and W column panels in its L2.
+constexpr int NUM_XCD = 8;
+
+template <int BM, int BN, int GROUP_N>
 __device__ __forceinline__ void tile_coords(int M, int N, int& tm, int& tn)
 {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int total = tiles_m * tiles_n;
     const int id = blockIdx.x;
-    constexpr int GROUP = 8;
-    const int group_size = GROUP * tiles_m;
-    const int gidx = id / group_size;
-    const int first_n = gidx * GROUP;
-    const int gn = (tiles_n - first_n) < GROUP ? (tiles_n - first_n) : GROUP;
-    const int in = id % group_size;
+    const int xcd = id % NUM_XCD, j = id / NUM_XCD;
+    const int q = total / NUM_XCD, r = total % NUM_XCD;
+    const int t = xcd * q + (xcd < r ? xcd : r) + j;   // bijection onto [0, total)
+    const int group_size = GROUP_N * tiles_m;
+    const int gidx = t / group_size;
+    const int first_n = gidx * GROUP_N;
+    const int gn = (tiles_n - first_n) < GROUP_N ? (tiles_n - first_n) : GROUP_N;
+    const int in = t % group_size;
     tm = in / gn;
     tn = first_n + in % gn;
 }
@@ -120,7 +129,7 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
     extern __shared__ __align__(16) uint8_t smem[];
 
     int tm, tn;
-    tile_coords<BM, BN>(p.M, p.N, tm, tn);
+    tile_coords<BM, BN, 4>(p.M, p.N, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -164,10 +173,15 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
                 const int lim = is_a ? p.M : p.N;
                 const uint8_t* sp = is_a ? p.a_s : p.w_s;
                 if (grow < lim) {
+                    if ((KB & 3) == 0) {
+                        // the stage's 4 scale bytes are one aligned dword
+                        v = *reinterpret_cast<const uint32_t*>(sp + (size_t)grow * KB + kt * 4);
+                    } else {
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const int blk = kt * 4 + b;
-                        if (blk < KB) v |= (uint32_t)sp[(size_t)grow * KB + blk] << (8 * b);
+                        for (int b = 0; b < 4; ++b) {
+                            const int blk = kt * 4 + b;
+                            if (blk < KB) v |= (uint32_t)sp[(size_t)grow * KB + blk] << (8 * b);
+                        }
                     }
                 }
             }
@@ -314,21 +328,127 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
+
+
+// ---------------------------------------------------------------- decode (M <= 32)
+// Weight streaming for a handful of tokens.  A workgroup owns 16 W rows and
+// its 8 waves split the K steps (128 elements each) between them; every wave
+// multiplies its K range on the 16x16x128 scaled matrix core (tokens padded
+// to 16 rows, MT fragments for up to 16*MT tokens) and the 8 partial tiles
+// are summed through LDS.  The W bytes are read exactly once, 64 contiguous
+// bytes per row per step; A (at most 32 rows) stays in L2.
+//   16x16x128 layout: lane l = r + 16 g holds row/column r and K block g of
+//   the step (16 bytes of E2M1); the output register i of lane l is
+//   C[(l/16)*4 + i][l%16].
+typedef float float4_t_ __attribute__((ext_vector_type(4)));
+
+template <int MT, bool OUT_F32>
+__global__ __launch_bounds__(512) void mx_decode_kernel(GemmArgs p)
+{
+    constexpr int WAVES = 8, UNROLL = 4;
+    __shared__ float red[WAVES][MT][64][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16, n = n0 + r;
+    const int K = p.K, KB = K / 32, row_bytes = K / 2;
+    const int steps = (K + 127) / 128;
+    const int s0 = wave * steps / WAVES, s1 = (wave + 1) * steps / WAVES;
+
+    float4_t_ acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = float4_t_{0.f, 0.f, 0.f, 0.f};
+
+    for (int sb = s0; sb < s1; sb += UNROLL) {
+        int4_t wf[UNROLL], af[UNROLL][MT];
+        int ws[UNROLL], as[UNROLL][MT];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int blk = 4 * (sb + u) + g;
+            const bool ok = sb + u < s1 && blk < KB;
+            wf[u] = int4_t{0, 0, 0, 0};
+            ws[u] = 0;
+            if (ok && n < p.N) {
+                wf[u] = *reinterpret_cast<const int4_t*>(p.w_q + (size_t)n * row_bytes + blk * 16);
+                ws[u] = p.w_s[(size_t)n * KB + blk];
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const int m = t * 16 + r;
+                af[u][t] = int4_t{0, 0, 0, 0};
+                as[u][t] = 0;
+                if (ok && m < p.M) {
+                    af[u][t] = *reinterpret_cast<const int4_t*>(p.a_q + (size_t)m * row_bytes + blk * 16);
+                    as[u][t] = p.a_s[(size_t)m * KB + blk];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int8_t_ b8 = int8_t_{wf[u][0], wf[u][1], wf[u][2], wf[u][3], 0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const int8_t_ a8 = int8_t_{af[u][t][0], af[u][t][1], af[u][t][2], af[u][t][3], 0, 0, 0, 0};
+                acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 4, 4, 0, as[u][t], 0, ws[u]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][t][lane][i] = acc[t][i];
+    __syncthreads();
+    // one output element per thread: (t, lane, i) -> m = 16 t + (lane/16)*4 + i, n = n0 + lane%16
+    for (int e = tid; e < MT * 64 * 4; e += WAVES * 64) {
+        const int t = e / 256, l = (e / 4) % 64, i = e % 4;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) v += red[w][t][l][i];
+        const int m = t * 16 + (l / 16) * 4 + i, nn = n0 + l % 16;
+        if (m < p.M && nn < p.N) {
+            if (OUT_F32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + nn] = v;
+            else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + nn] = f32_to_bf16_rne(v);
+        }
+    }
+}
+
+template <int MT, bool OUT_F32>
+hipError_t launch_decode(const GemmArgs& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((mx_decode_kernel<MT, OUT_F32>), dim3((a.N + 15) / 16), dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
 } // namespace mxl
 
 using namespace mxl;
 
-// Tile configuration used for every shape in this version.
-#define MXL_BM 128
-#define MXL_BN 128
-#define MXL_WM 2
-#define MXL_WN 2
+// ---------------------------------------------------------------- dispatch
+// Shape classes (MXFP4 and fast-path MXFP8):
+//   decode  : M <= 32 (MXFP4)                     -> mx_decode_kernel
+//   large   : MXFP4, M >= 1024 and N >= 1024       -> 256x256 tiles, 2x2 waves of 128x128
+//             (the E4M3 fragments are twice as wide and would spill there)
+//   default : everything else                      -> 128x128 tiles, 2x2 waves of 64x64
+enum ShapeClass { SC_DECODE, SC_LARGE, SC_DEFAULT };
+
+static ShapeClass classify(int a_bits, int64_t m, int64_t n, bool fused)
+{
+    if (!fused && a_bits == 4 && m <= 32) return SC_DECODE;
+    if (a_bits == 4 && m >= 1024 && n >= 1024) return SC_LARGE;
+    return SC_DEFAULT;
+}
+
+template <int AB, int WB, bool FUSED, int RULE, bool F32>
+static hipError_t dispatch_tile(const GemmArgs& a, ShapeClass sc, hipStream_t s)
+{
+    if (AB == 4 && sc == SC_LARGE) return launch_tile<AB, WB, 256, 256, 2, 2, FUSED, RULE, F32>(a, s);
+    return launch_tile<AB, WB, 128, 128, 2, 2, FUSED, RULE, F32>(a, s);
+}
 
 template <int AB, int WB, bool FUSED, int RULE>
-static hipError_t dispatch_out(const GemmArgs& a, bool f32, hipStream_t s)
+static hipError_t dispatch_out(const GemmArgs& a, ShapeClass sc, bool f32, hipStream_t s)
 {
-    if (f32) return launch_tile<AB, WB, MXL_BM, MXL_BN, MXL_WM, MXL_WN, FUSED, RULE, true>(a, s);
-    return launch_tile<AB, WB, MXL_BM, MXL_BN, MXL_WM, MXL_WN, FUSED, RULE, false>(a, s);
+    if (f32) return dispatch_tile<AB, WB, FUSED, RULE, true>(a, sc, s);
+    return dispatch_tile<AB, WB, FUSED, RULE, false>(a, sc, s);
 }
 
 extern "C" hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq, const void* as,
@@ -337,8 +457,13 @@ extern "C" hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq,
 {
     GemmArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
                static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k};
-    if (a_bits == 4 && w_bits == 4) return dispatch_out<4, 4, false, RULE_CEIL>(a, out_f32, stream);
-    if (a_bits == 8 && w_bits == 8) return dispatch_out<8, 8, false, RULE_CEIL>(a, out_f32, stream);
+    const ShapeClass sc = classify(a_bits, m, n, false);
+    if (sc == SC_DECODE) {
+        if (m <= 16) return out_f32 ? launch_decode<1, true>(a, stream) : launch_decode<1, false>(a, stream);
+        return out_f32 ? launch_decode<2, true>(a, stream) : launch_decode<2, false>(a, stream);
+    }
+    if (a_bits == 4 && w_bits == 4) return dispatch_out<4, 4, false, RULE_CEIL>(a, sc, out_f32, stream);
+    if (a_bits == 8 && w_bits == 8) return dispatch_out<8, 8, false, RULE_CEIL>(a, sc, out_f32, stream);
     return hipErrorInvalidValue;
 }
 
@@ -348,20 +473,28 @@ extern "C" hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const voi
 {
     GemmArgs a{static_cast<const uint8_t*>(a_bf16), nullptr, static_cast<const uint8_t*>(wq),
                static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k};
+    const ShapeClass sc = classify(a_bits, m, n, true);
     if (a_bits == 4 && w_bits == 4) {
-        if (a_rule == RULE_CEIL) return dispatch_out<4, 4, true, RULE_CEIL>(a, out_f32, stream);
-        if (a_rule == RULE_FLOOR) return dispatch_out<4, 4, true, RULE_FLOOR>(a, out_f32, stream);
-        return dispatch_out<4, 4, true, RULE_EVEN>(a, out_f32, stream);
+        if (a_rule == RULE_CEIL) return dispatch_out<4, 4, true, RULE_CEIL>(a, sc, out_f32, stream);
+        if (a_rule == RULE_FLOOR) return dispatch_out<4, 4, true, RULE_FLOOR>(a, sc, out_f32, stream);
+        return dispatch_out<4, 4, true, RULE_EVEN>(a, sc, out_f32, stream);
     }
     if (a_bits == 8 && w_bits == 8) {
-        if (a_rule == RULE_CEIL) return dispatch_out<8, 8, true, RULE_CEIL>(a, out_f32, stream);
-        if (a_rule == RULE_FLOOR) return dispatch_out<8, 8, true, RULE_FLOOR>(a, out_f32, stream);
-        return dispatch_out<8, 8, true, RULE_EVEN>(a, out_f32, stream);
+        if (a_rule == RULE_CEIL) return dispatch_out<8, 8, true, RULE_CEIL>(a, sc, out_f32, stream);
+        if (a_rule == RULE_FLOOR) return dispatch_out<8, 8, true, RULE_FLOOR>(a, sc, out_f32, stream);
+        return dispatch_out<8, 8, true, RULE_EVEN>(a, sc, out_f32, stream);
     }
     return hipErrorInvalidValue;
 }
 
-extern "C" const char* mxl_mx_gemm_config_name(void)
+extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n, int fused)
 {
-    return "mx_gemm_kernel<tile 128x128x128, 2x2 waves of 64x64, scaled mfma 32x32x64>";
+    switch (classify(a_bits, m, n, fused != 0)) {
+    case SC_DECODE:
+        return "mx_decode_kernel<16 W rows per workgroup, 8-wave split-K, scaled mfma 16x16x128>";
+    case SC_LARGE:
+        return "mx_gemm_kernel<tile 256x256x128, 2x2 waves of 128x128, scaled mfma 32x32x64>";
+    default:
+        return "mx_gemm_kernel<tile 128x128x128, 2x2 waves of 64x64, scaled mfma 32x32x64>";
+    }
 }
