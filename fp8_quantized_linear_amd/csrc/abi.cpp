@@ -33,7 +33,7 @@ hipError_t mxl_launch_mxfp8_exact_gemm(const void* aq, const void* as, const voi
 hipError_t mxl_launch_mxfp8_exact_gemm_fused(int a_rule, const void* a_bf16, const void* wq, const void* ws,
                                              int64_t m, int64_t n, int64_t k, void* y, int out_f32,
                                              hipStream_t stream);
-const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n, int fused);
+const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n, int64_t k, int fused);
 const char* mxl_nv_gemm_config_name(void);
 const char* mxl_mxfp8_exact_config_name(void);
 }
@@ -163,7 +163,7 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
     if (log_enabled())
         std::fprintf(stderr, "[mxlinear] mx_gemm m=%lld n=%lld k=%lld -> %s\n", (long long)m, (long long)n,
                      (long long)k,
-                     exact8 ? mxl_mxfp8_exact_config_name() : mxl_mx_gemm_config_name(bits_of(a_fmt), m, n, 0));
+                     exact8 ? mxl_mxfp8_exact_config_name() : mxl_mx_gemm_config_name(bits_of(a_fmt), m, n, k, 0));
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (exact8) return from_hip(mxl_launch_mxfp8_exact_gemm(a_q, a_s, w_q, w_s, m, n, k, y, f32, hs));
     return from_hip(mxl_launch_mx_gemm(bits_of(a_fmt), bits_of(w_fmt), a_q, a_s, w_q, w_s, m, n, k, y, f32, hs));
@@ -266,7 +266,7 @@ mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, i
     const bool exact8 = a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST);
     const char* cfg = nv ? mxl_nv_gemm_config_name()
                          : (exact8 ? mxl_mxfp8_exact_config_name()
-                                   : mxl_mx_gemm_config_name(bits_of(a_fmt), m, n, fused));
+                                   : mxl_mx_gemm_config_name(bits_of(a_fmt), m, n, k, fused));
     std::snprintf(name, len, "%s%s %s", fused && !nv ? "fused-quant " : "", fmt, cfg);
     return MX_OK;
 }

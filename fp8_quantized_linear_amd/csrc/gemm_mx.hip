@@ -16,7 +16,8 @@
 //   E2M1: its 16 bytes are K elements [32g, 32g + 32) of the 64-wide step.
 //   E4M3: bytes 0..15 are K [16g, 16g + 16), bytes 16..31 are K [32 + 16g, ..).
 //   Either way lane group g supplies the E8M0 scale of K block g (of 2).
-//   Accumulator register i of lane l is C[(i/4)*8 + (l/32)*4 + i%4][l%32].
+//   Accumulator register i of lane l is C[(i/4)*8 + (l/32)*4 + i%4][l%32]
+//   (C = first operand x second operand^T; the tile kernel passes W first).
 //
 // Tiling: a workgroup of WM x WN waves computes a BM x BN tile of Y; each wave
 // a (BM/WM) x (BN/WN) sub-tile of 32x32 matrix-core tiles.  K advances in
@@ -25,6 +26,8 @@
 // 16-byte chunks of each LDS row are XOR-swizzled by row so that the 32 lanes
 // reading the same chunk of 32 consecutive rows hit distinct banks.
 #include "mx_device.h"
+
+#include <type_traits>
 
 namespace mxl {
 
@@ -41,6 +44,41 @@ template <int OPSEL_A, int OPSEL_B, int CBSZ, int BLGP>
 __device__ __forceinline__ void mfma_scaled(float16_t& acc, const int8_t_& a, const int8_t_& b, int sa, int sb)
 {
     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, CBSZ, BLGP, OPSEL_A, sa, OPSEL_B, sb);
+}
+
+// Scaled MFMA with byte selectors chosen at run time; after unrolling the
+// selectors are constants and the branches fold away.
+template <int CBSZ, int BLGP>
+__device__ __forceinline__ void mfma_scaled_sel(float16_t& acc, const int8_t_& a, const int8_t_& b, int sa,
+                                                int sb, int pa, int pb)
+{
+#define MXL_MF(OA, OB) acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, CBSZ, BLGP, OA, sa, OB, sb)
+#define MXL_ROW(OA)                  \
+    if (pb == 0) MXL_MF(OA, 0);      \
+    else if (pb == 1) MXL_MF(OA, 1); \
+    else if (pb == 2) MXL_MF(OA, 2); \
+    else MXL_MF(OA, 3);
+    if (pa == 0) { MXL_ROW(0) }
+    else if (pa == 1) { MXL_ROW(1) }
+    else if (pa == 2) { MXL_ROW(2) }
+    else { MXL_ROW(3) }
+#undef MXL_ROW
+#undef MXL_MF
+}
+
+// LDS layout of a stage's E8M0 scales.  Lane (r, g) of a wave needs, for
+// fragment i of its wave tile and K step kk, the byte of K block 2*kk + g of
+// its row.  Each tile row therefore stores two 16-bit entries,
+//   entry g = byte g | byte (g + 2) << 8,
+// placed so that one lane's entries for its F = WT/32 fragments are adjacent:
+// entry index ((wave_row_group * 32 + r) * 2 + g) * F + i.  One 4-byte (F = 2)
+// or 8-byte (F = 4) LDS read then gives a lane all its scales for the stage,
+// and the scale operand's byte selector picks 2 * (i % 2) + kk.
+template <int WT>
+__device__ __forceinline__ int scale_entry(int r, int g)
+{
+    constexpr int F = WT / 32;
+    return (((r / WT) * 32 + (r % 32)) * 2 + g) * F + (r % WT) / 32;
 }
 
 // Load one 32-row matrix-core fragment for K step kk (0 or 1) of the stage
@@ -74,40 +112,12 @@ struct GemmArgs {
     int M, N, K;
 };
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
 
-// Tile ordering.  Workgroups are dispatched round-robin over the 8 XCDs
-// (workgroup i runs on XCD i % 8), and each XCD has its own L2.  So the
-// workgroup id is first remapped so that each XCD receives one contiguous
-// range of the tile order, and the tile order itself walks groups of GROUP_N
-// tile columns down M (N fastest inside a group): the tiles an XCD runs at
-// the same time share a few A row panels and W column panels in its L2.
-constexpr int NUM_XCD = 8;
-
-template <int BM, int BN, int GROUP_N>
-__device__ __forceinline__ void tile_coords(int M, int N, int& tm, int& tn)
-{
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const int total = tiles_m * tiles_n;
-    const int id = blockIdx.x;
-    const int xcd = id % NUM_XCD, j = id / NUM_XCD;
-    const int q = total / NUM_XCD, r = total % NUM_XCD;
-    const int t = xcd * q + (xcd < r ? xcd : r) + j;   // bijection onto [0, total)
-    const int group_size = GROUP_N * tiles_m;
-    const int gidx = t / group_size;
-    const int first_n = gidx * GROUP_N;
-    const int gn = (tiles_n - first_n) < GROUP_N ? (tiles_n - first_n) : GROUP_N;
-    const int in = t % group_size;
-    tm = in / gn;
-    tn = first_n + in % gn;
-}
-
-template <int ABITS, int WBITS, int BM, int BN, int WM, int WN, bool FUSED, int A_RULE, bool OUT_F32>
+// PREFETCH = 2 keeps two K stages in flight in registers (the loop is
+// unrolled by two so that the register sets swap roles statically and the
+// compiler waits only for the stage being written to LDS); 1 keeps one.
+template <int ABITS, int WBITS, int BM, int BN, int WM, int WN, bool FUSED, int A_RULE, bool OUT_F32,
+          int PREFETCH = 1, bool SCALE_DWORD = false>
 __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
 {
     using TA = OpTraits<ABITS>;
@@ -122,8 +132,6 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
     constexpr int A_CHUNKS = FUSED ? BM * (BK * 2 / 16) : BM * TA::CHUNKS;  // fused: bf16 chunks of 8
     constexpr int W_CHUNKS = BN * TW::CHUNKS;
     constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT, W_PER_T = (W_CHUNKS + NT - 1) / NT;
-    constexpr int S_ROWS = (FUSED ? 0 : BM) + BN;
-    constexpr int S_PER_T = (S_ROWS + NT - 1) / NT;
     static_assert(!FUSED || (A_CHUNKS % NT == 0 && NT % 16 == 0), "fused tile mapping");
 
     extern __shared__ __align__(16) uint8_t smem[];
@@ -138,71 +146,90 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
     const int w_row_bytes = K * WBITS / 8;
     const int nk = (K + BK - 1) / BK;
 
-    uint4 ra[A_PER_T], rw[W_PER_T];
-    uint32_t rs[S_PER_T];
+    constexpr int SA_PER_T = FUSED ? 1 : (BM + NT - 1) / NT;   // A scale rows per thread
+    constexpr int SW_PER_T = (BN + NT - 1) / NT;                 // W scale rows per thread
+    struct Stage {
+        uint4 ra[A_PER_T], rw[W_PER_T];
+        uint32_t rsa[SA_PER_T], rsw[SW_PER_T];
+    };
 
-    auto load_stage = [&](int kt) {
+    // Buffer resources: 32-bit per-lane offsets, the stage offset in a scalar
+    // register, and rows past the end of a tensor read as zero in hardware.
+    // (The host splits launches so that every tensor stays below 2 GiB.)
+    const __amdgpu_buffer_rsrc_t rsrc_a =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.a_q, (short)0, p.M * a_row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsrc_w =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.w_q, (short)0, p.N * w_row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsrc_as =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.a_s, (short)0, FUSED ? 0 : p.M * KB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsrc_ws =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.w_s, (short)0, p.N * KB, 0x00020000);
+    constexpr int A_CPR = FUSED ? 16 : TA::CHUNKS;          // 16-byte chunks per row per stage
+    constexpr int A_STAGE_BYTES = FUSED ? BK * 2 : TA::ROW_BYTES;
+    const int a_c = tid % A_CPR, w_c = tid % TW::CHUNKS;      // chunk column: same for all i
+    const int a_voff0 = (m0 + tid / A_CPR) * a_row_bytes + a_c * 16;
+    const int w_voff0 = (n0 + tid / TW::CHUNKS) * w_row_bytes + w_c * 16;
+    static_assert(NT % A_CPR == 0 && NT % TW::CHUNKS == 0, "chunk column must be loop invariant");
+
+    static_assert(A_CHUNKS % NT == 0 && W_CHUNKS % NT == 0, "even work split");
+
+    // Branch-free stage loads with uniform buffer descriptors.  Rows past the
+    // end of a tensor read as zero (buffer range check).  When K is a multiple
+    // of the stage (SCALE_DWORD), no stage has a K tail; otherwise the tail
+    // chunks are zeroed by a select.
+    auto scale_dword = [&](const __amdgpu_buffer_rsrc_t& rs, const uint8_t* sp, int grow, int lim, int kt) -> uint32_t {
+        if (SCALE_DWORD) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, grow * KB, kt * 4, 0);
+        uint32_t v = 0;
+        if (grow < lim) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int blk = kt * 4 + b;
+                if (blk < KB) v |= (uint32_t)sp[(size_t)grow * KB + blk] << (8 * b);
+            }
+        }
+        return v;
+    };
+    auto load_stage = [&](int kt, Stage& st) {
+        const bool a_in_k = SCALE_DWORD || kt * A_STAGE_BYTES + a_c * 16 < a_row_bytes;
+        const bool w_in_k = SCALE_DWORD || kt * TW::ROW_BYTES + w_c * 16 < w_row_bytes;
 #pragma unroll
         for (int i = 0; i < A_PER_T; ++i) {
-            const int q = tid + i * NT;
-            const int cpr = FUSED ? 16 : TA::CHUNKS;
-            const int row = q / cpr, c = q % cpr;
-            const int gm = m0 + row;
-            const int kb = kt * (FUSED ? BK * 2 : TA::ROW_BYTES) + c * 16;  // byte offset in the row
-            ra[i] = make_uint4(0, 0, 0, 0);
-            if (q < A_CHUNKS && gm < p.M && kb < a_row_bytes)
-                ra[i] = *reinterpret_cast<const uint4*>(p.a_q + (size_t)gm * a_row_bytes + kb);
+            const int voff = a_voff0 + i * (NT / A_CPR) * a_row_bytes;
+            const int4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff, kt * A_STAGE_BYTES, 0);
+            st.ra[i] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+            if (!a_in_k) st.ra[i] = make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < W_PER_T; ++i) {
-            const int q = tid + i * NT;
-            const int row = q / TW::CHUNKS, c = q % TW::CHUNKS;
-            const int gn = n0 + row;
-            const int kb = kt * TW::ROW_BYTES + c * 16;
-            rw[i] = make_uint4(0, 0, 0, 0);
-            if (q < W_CHUNKS && gn < p.N && kb < w_row_bytes)
-                rw[i] = *reinterpret_cast<const uint4*>(p.w_q + (size_t)gn * w_row_bytes + kb);
+            const int voff = w_voff0 + i * (NT / TW::CHUNKS) * w_row_bytes;
+            const int4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc_w, voff, kt * TW::ROW_BYTES, 0);
+            st.rw[i] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+            if (!w_in_k) st.rw[i] = make_uint4(0, 0, 0, 0);
+        }
+        // scale rows: threads beyond the tile's rows load a neighbouring row
+        // (or zero) and never store it
+        if (!FUSED) {
+#pragma unroll
+            for (int i = 0; i < SA_PER_T; ++i) st.rsa[i] = scale_dword(rsrc_as, p.a_s, m0 + tid + i * NT, p.M, kt);
         }
 #pragma unroll
-        for (int i = 0; i < S_PER_T; ++i) {
-            const int r = tid + i * NT;
-            uint32_t v = 0;
-            if (r < S_ROWS) {
-                const bool is_a = !FUSED && r < BM;
-                const int grow = is_a ? m0 + r : n0 + (r - (FUSED ? 0 : BM));
-                const int lim = is_a ? p.M : p.N;
-                const uint8_t* sp = is_a ? p.a_s : p.w_s;
-                if (grow < lim) {
-                    if ((KB & 3) == 0) {
-                        // the stage's 4 scale bytes are one aligned dword
-                        v = *reinterpret_cast<const uint32_t*>(sp + (size_t)grow * KB + kt * 4);
-                    } else {
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) {
-                            const int blk = kt * 4 + b;
-                            if (blk < KB) v |= (uint32_t)sp[(size_t)grow * KB + blk] << (8 * b);
-                        }
-                    }
-                }
-            }
-            rs[i] = v;
-        }
+        for (int i = 0; i < SW_PER_T; ++i) st.rsw[i] = scale_dword(rsrc_ws, p.w_s, n0 + tid + i * NT, p.N, kt);
     };
 
-    auto store_stage = [&](int buf) {
+    auto store_stage = [&](const Stage& sg, int buf) {
+        const uint4* ra = sg.ra;
+        const uint4* rw = sg.rw;
         uint8_t* st = smem + buf * STAGE;
         uint8_t* a_t = st;
         uint8_t* w_t = st + A_TILE;
-        uint32_t* sa_t = reinterpret_cast<uint32_t*>(st + A_TILE + W_TILE);
-        uint32_t* sw_t = sa_t + BM;
+        uint16_t* sa16 = reinterpret_cast<uint16_t*>(st + A_TILE + W_TILE);
+        uint16_t* sw16 = sa16 + 2 * BM;
         if (!FUSED) {
 #pragma unroll
             for (int i = 0; i < A_PER_T; ++i) {
                 const int q = tid + i * NT;
-                if (q < A_CHUNKS) {
-                    const int row = q / TA::CHUNKS, c = q % TA::CHUNKS;
-                    *reinterpret_cast<uint4*>(a_t + row * TA::ROW_BYTES + ((c ^ TA::swz(row)) * 16)) = ra[i];
-                }
+                const int row = q / TA::CHUNKS, c = q % TA::CHUNKS;
+                *reinterpret_cast<uint4*>(a_t + row * TA::ROW_BYTES + ((c ^ TA::swz(row)) * 16)) = ra[i];
             }
         } else {
             // quantize 8 bf16 per lane; 16 consecutive lanes hold one row's
@@ -222,25 +249,31 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
                     const int chunk = (2 * blk + part / 2) ^ TA::swz(row);
                     *reinterpret_cast<uint2*>(a_t + row * TA::ROW_BYTES + chunk * 16 + (part % 2) * 8) = codes;
                 }
-                if (part == 0) (reinterpret_cast<uint8_t*>(sa_t + row))[blk] = (uint8_t)(e + 127);
+                if (part == 0)
+                    reinterpret_cast<uint8_t*>(sa16)[scale_entry<WTM>(row, blk % 2) * 2 + blk / 2] = (uint8_t)(e + 127);
             }
         }
 #pragma unroll
         for (int i = 0; i < W_PER_T; ++i) {
             const int q = tid + i * NT;
-            if (q < W_CHUNKS) {
-                const int row = q / TW::CHUNKS, c = q % TW::CHUNKS;
-                *reinterpret_cast<uint4*>(w_t + row * TW::ROW_BYTES + ((c ^ TW::swz(row)) * 16)) = rw[i];
-            }
+            const int row = q / TW::CHUNKS, c = q % TW::CHUNKS;
+            *reinterpret_cast<uint4*>(w_t + row * TW::ROW_BYTES + ((c ^ TW::swz(row)) * 16)) = rw[i];
+        }
+        auto put_scales = [&](uint16_t* base, int r, uint32_t v, auto wt) {
+            constexpr int WT = decltype(wt)::value;
+            base[scale_entry<WT>(r, 0)] = (uint16_t)((v & 0xFFu) | ((v >> 8) & 0xFF00u));
+            base[scale_entry<WT>(r, 1)] = (uint16_t)(((v >> 8) & 0xFFu) | ((v >> 16) & 0xFF00u));
+        };
+        if (!FUSED) {
+#pragma unroll
+            for (int i = 0; i < SA_PER_T; ++i)
+                if (BM % NT == 0 || tid + i * NT < BM)
+                    put_scales(sa16, tid + i * NT, sg.rsa[i], std::integral_constant<int, WTM>{});
         }
 #pragma unroll
-        for (int i = 0; i < S_PER_T; ++i) {
-            const int r = tid + i * NT;
-            if (r < S_ROWS) {
-                if (!FUSED && r < BM) sa_t[r] = rs[i];
-                else sw_t[r - (FUSED ? 0 : BM)] = rs[i];
-            }
-        }
+        for (int i = 0; i < SW_PER_T; ++i)
+            if (BN % NT == 0 || tid + i * NT < BN)
+                put_scales(sw16, tid + i * NT, sg.rsw[i], std::integral_constant<int, WTN>{});
     };
 
     float16_t acc[FM][FN];
@@ -257,13 +290,18 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
         const uint8_t* st = smem + buf * STAGE;
         const uint8_t* a_t = st;
         const uint8_t* w_t = st + A_TILE;
-        const uint32_t* sa_t = reinterpret_cast<const uint32_t*>(st + A_TILE + W_TILE);
-        const uint32_t* sw_t = sa_t + BM;
-        int sa[FM], sw[FN];
+        const uint16_t* sa16 = reinterpret_cast<const uint16_t*>(st + A_TILE + W_TILE);
+        const uint16_t* sw16 = sa16 + 2 * BM;
+        static_assert(FM % 2 == 0 && FN % 2 == 0, "scale entries come in pairs");
+        int sa[FM / 2], sw[FN / 2];
+        {
+            const uint32_t* pa = reinterpret_cast<const uint32_t*>(sa16 + scale_entry<WTM>(wm * WTM + r32, g));
+            const uint32_t* pw = reinterpret_cast<const uint32_t*>(sw16 + scale_entry<WTN>(wn * WTN + r32, g));
 #pragma unroll
-        for (int i = 0; i < FM; ++i) sa[i] = (int)(sa_t[wm * WTM + i * 32 + r32] >> (8 * g));
+            for (int i = 0; i < FM / 2; ++i) sa[i] = (int)pa[i];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) sw[j] = (int)(sw_t[wn * WTN + j * 32 + r32] >> (8 * g));
+            for (int j = 0; j < FN / 2; ++j) sw[j] = (int)pw[j];
+        }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             int8_t_ fa[FM], fw[FN];
@@ -275,48 +313,114 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    if (kk == 0) mfma_scaled<0, 0, CBSZ, BLGP>(acc[i][j], fa[i], fw[j], sa[i], sw[j]);
-                    else mfma_scaled<2, 2, CBSZ, BLGP>(acc[i][j], fa[i], fw[j], sa[i], sw[j]);
+                    // W is the matrix core's A operand and A its B operand, so the
+                    // accumulator holds Y^T: each lane ends up with 4 consecutive
+                    // output columns (see the epilogue)
+                    mfma_scaled_sel<BLGP, CBSZ>(acc[i][j], fw[j], fa[i], sw[j / 2], sa[i / 2],
+                                                 2 * (j % 2) + kk, 2 * (i % 2) + kk);
                 }
         }
     };
 
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        if (more) load_stage(kt + 1);
-        compute_stage(kt & 1);
-        if (more) store_stage((kt + 1) & 1);
-        __syncthreads();
+    Stage s0, s1;
+    load_stage(0, s0);
+    if (PREFETCH >= 2 && nk > 1) load_stage(1, s1);
+    store_stage(s0, 0);
+    lds_barrier();
+    if (PREFETCH == 3) {
+        // As PREFETCH == 2, but each half first writes the stage that has been
+        // in flight for a whole compute period to the free LDS buffer, and only
+        // then issues the next stage's loads (a scheduling fence keeps that
+        // order), so no wait ever covers the loads just issued.
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            store_stage(s1, 1);                      // stage kt + 1 -> buffer 1
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 2 < nk) load_stage(kt + 2, s0);
+            compute_stage(0);                        // stage kt from buffer 0
+            lds_barrier();
+            if (kt + 2 < nk) store_stage(s0, 0);     // stage kt + 2 -> buffer 0
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 3 < nk) load_stage(kt + 3, s1);
+            compute_stage(1);                        // stage kt + 1 from buffer 1
+            lds_barrier();
+        }
+        if (kt < nk) compute_stage(0);
+    } else if (PREFETCH == 2) {
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            // LDS buffer 0 holds stage kt; s1 holds stage kt + 1 (in flight)
+            if (kt + 2 < nk) load_stage(kt + 2, s0);
+            compute_stage(0);
+            store_stage(s1, 1);
+            lds_barrier();
+            // LDS buffer 1 holds stage kt + 1; s0 holds stage kt + 2 (in flight)
+            if (kt + 3 < nk) load_stage(kt + 3, s1);
+            compute_stage(1);
+            if (kt + 2 < nk) store_stage(s0, 0);
+            lds_barrier();
+        }
+        if (kt < nk) compute_stage(0);  // odd stage count: the last stage is in buffer 0
+    } else {
+        for (int kt = 0; kt < nk; ++kt) {
+            const bool more = kt + 1 < nk;
+            if (more) load_stage(kt + 1, s1);
+            compute_stage(kt & 1);
+            if (more) store_stage(s1, (kt + 1) & 1);
+            lds_barrier();
+        }
     }
 
-    // epilogue: accumulator (i, j, r) -> Y[m, n]
+    // epilogue: accumulator (i, j) register r holds Y[m][n] with
+    //   m = tile row of fragment i + lane % 32,
+    //   n = tile column of fragment j + (r / 4) * 8 + (lane / 32) * 4 + r % 4,
+    // so registers 4q .. 4q+3 are 4 consecutive columns of one row: one 8-byte
+    // (bf16) or 16-byte (fp32) store when the row is aligned and in range.
+    const bool vec_ok = (p.N & 3) == 0;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WTM + i * 32 + r32;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int n = n0 + wn * WTN + j * 32 + r32;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * WTM + i * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-                if (m < p.M && n < p.N) {
-                    if (OUT_F32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + n] = acc[i][j][r];
-                    else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + n] = f32_to_bf16_rne(acc[i][j][r]);
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * WTN + j * 32 + q * 8 + g * 4;
+                const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+                if (m < p.M && vec_ok && n + 3 < p.N) {
+                    if (OUT_F32) {
+                        *reinterpret_cast<float4_t*>(reinterpret_cast<float*>(p.y) + (size_t)m * p.N + n) =
+                            float4_t{v0, v1, v2, v3};
+                    } else {
+                        const uint32_t lo = (uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16);
+                        const uint32_t hi = (uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16);
+                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + (size_t)m * p.N + n) =
+                            make_uint2(lo, hi);
+                    }
+                } else if (m < p.M) {
+                    const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        if (n + t < p.N) {
+                            if (OUT_F32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + n + t] = vv[t];
+                            else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + n + t] = f32_to_bf16_rne(vv[t]);
+                        }
+                    }
                 }
             }
         }
+    }
 }
 
-template <int ABITS, int WBITS, int BM, int BN, int WM, int WN, bool FUSED, int A_RULE, bool OUT_F32>
+template <int ABITS, int WBITS, int BM, int BN, int WM, int WN, bool FUSED, int A_RULE, bool OUT_F32,
+          int PREFETCH = 1, bool SCALE_DWORD = false>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t stream)
 {
     using TA = OpTraits<ABITS>;
     using TW = OpTraits<WBITS>;
     constexpr int STAGE = BM * TA::ROW_BYTES + BN * TW::ROW_BYTES + 4 * (BM + BN);
     constexpr int LDS = 2 * STAGE;
-    auto kern = mx_gemm_kernel<ABITS, WBITS, BM, BN, WM, WN, FUSED, A_RULE, OUT_F32>;
+    auto kern = mx_gemm_kernel<ABITS, WBITS, BM, BN, WM, WN, FUSED, A_RULE, OUT_F32, PREFETCH, SCALE_DWORD>;
     static bool attr_set = false;  // benign race: setting the same value twice is harmless
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
@@ -425,22 +529,23 @@ using namespace mxl;
 // ---------------------------------------------------------------- dispatch
 // Shape classes (MXFP4 and fast-path MXFP8):
 //   decode  : M <= 32 (MXFP4)                     -> mx_decode_kernel
-//   large   : MXFP4, M >= 1024 and N >= 1024       -> 256x256 tiles, 2x2 waves of 128x128
+//   large   : MXFP4, M, N >= 1024, K % 128 == 0    -> 256x256 tiles, 2x2 waves of 128x128
 //             (the E4M3 fragments are twice as wide and would spill there)
 //   default : everything else                      -> 128x128 tiles, 2x2 waves of 64x64
 enum ShapeClass { SC_DECODE, SC_LARGE, SC_DEFAULT };
 
-static ShapeClass classify(int a_bits, int64_t m, int64_t n, bool fused)
+static ShapeClass classify(int a_bits, int64_t m, int64_t n, int64_t k, bool fused)
 {
     if (!fused && a_bits == 4 && m <= 32) return SC_DECODE;
-    if (a_bits == 4 && m >= 1024 && n >= 1024) return SC_LARGE;
+    if (a_bits == 4 && m >= 1024 && n >= 1024 && k % 128 == 0) return SC_LARGE;
     return SC_DEFAULT;
 }
 
 template <int AB, int WB, bool FUSED, int RULE, bool F32>
 static hipError_t dispatch_tile(const GemmArgs& a, ShapeClass sc, hipStream_t s)
 {
-    if (AB == 4 && sc == SC_LARGE) return launch_tile<AB, WB, 256, 256, 2, 2, FUSED, RULE, F32>(a, s);
+    if constexpr (AB == 4) if (sc == SC_LARGE)
+        return launch_tile<AB, WB, 256, 256, 2, 2, FUSED, RULE, F32, FUSED ? 1 : 3, true>(a, s);
     return launch_tile<AB, WB, 128, 128, 2, 2, FUSED, RULE, F32>(a, s);
 }
 
@@ -451,13 +556,20 @@ static hipError_t dispatch_out(const GemmArgs& a, ShapeClass sc, bool f32, hipSt
     return dispatch_tile<AB, WB, FUSED, RULE, false>(a, sc, s);
 }
 
+extern "C" int mxl_prefill_ok(int64_t m, int64_t n, int64_t k);
+extern "C" hipError_t mxl_launch_mx_prefill(const void* aq, const void* as, const void* wq, const void* ws,
+                                            int64_t m, int64_t n, int64_t k, void* y, int out_f32,
+                                            hipStream_t stream);
+
 extern "C" hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq, const void* as,
                                          const void* wq, const void* ws, int64_t m, int64_t n,
                                          int64_t k, void* y, int out_f32, hipStream_t stream)
 {
     GemmArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
                static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k};
-    const ShapeClass sc = classify(a_bits, m, n, false);
+    const ShapeClass sc = classify(a_bits, m, n, k, false);
+    if (sc == SC_LARGE && mxl_prefill_ok(m, n, k))
+        return mxl_launch_mx_prefill(aq, as, wq, ws, m, n, k, y, out_f32, stream);
     if (sc == SC_DECODE) {
         if (m <= 16) return out_f32 ? launch_decode<1, true>(a, stream) : launch_decode<1, false>(a, stream);
         return out_f32 ? launch_decode<2, true>(a, stream) : launch_decode<2, false>(a, stream);
@@ -473,7 +585,7 @@ extern "C" hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const voi
 {
     GemmArgs a{static_cast<const uint8_t*>(a_bf16), nullptr, static_cast<const uint8_t*>(wq),
                static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k};
-    const ShapeClass sc = classify(a_bits, m, n, true);
+    const ShapeClass sc = classify(a_bits, m, n, k, true);
     if (a_bits == 4 && w_bits == 4) {
         if (a_rule == RULE_CEIL) return dispatch_out<4, 4, true, RULE_CEIL>(a, sc, out_f32, stream);
         if (a_rule == RULE_FLOOR) return dispatch_out<4, 4, true, RULE_FLOOR>(a, sc, out_f32, stream);
@@ -487,12 +599,15 @@ extern "C" hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const voi
     return hipErrorInvalidValue;
 }
 
-extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n, int fused)
+extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n, int64_t k, int fused)
 {
-    switch (classify(a_bits, m, n, fused != 0)) {
+    switch (classify(a_bits, m, n, k, fused != 0)) {
     case SC_DECODE:
         return "mx_decode_kernel<16 W rows per workgroup, 8-wave split-K, scaled mfma 16x16x128>";
     case SC_LARGE:
+        if (!fused && mxl_prefill_ok(m, n, k))
+            return "mx_gemm_prefill_kernel<tile 256x256x128, 2x2 waves of 128x128, 4-slot LDS ring fed by "
+                   "buffer-to-LDS copies, scaled mfma 32x32x64>";
         return "mx_gemm_kernel<tile 256x256x128, 2x2 waves of 128x128, scaled mfma 32x32x64>";
     default:
         return "mx_gemm_kernel<tile 128x128x128, 2x2 waves of 64x64, scaled mfma 32x32x64>";

@@ -30,6 +30,21 @@ enum : int { RULE_FLOOR = 0, RULE_CEIL = 1, RULE_EVEN = 2 };
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also fences
+// global memory, which makes every wave wait for all of its outstanding
+// global loads (vmcnt(0)) at each barrier and defeats register prefetching.
+// Here each wave waits only for its own LDS operations (lgkmcnt(0)) before the
+// hardware barrier; the empty asm statements keep the compiler from moving
+// memory accesses across it.  Global loads into registers are still waited for
+// precisely by the compiler where their registers are used.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Max over the 4 lanes of a lane quad (lanes 4q .. 4q+3) via DPP quad permutes.
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v)
 {
@@ -187,6 +202,40 @@ __device__ __forceinline__ uint32_t e2m1_rne_ratio(double num, double den)
     c += num >= 3.5 * den;
     c += num > 5.0 * den;
     return c;
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Tile ordering.  Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup i runs on XCD i % 8), and each XCD has its own L2.  So the
+// workgroup id is first remapped so that each XCD receives one contiguous
+// range of the tile order, and the tile order itself walks groups of GROUP_N
+// tile columns down M (N fastest inside a group): the tiles an XCD runs at
+// the same time share a few A row panels and W column panels in its L2.
+constexpr int NUM_XCD = 8;
+
+template <int BM, int BN, int GROUP_N>
+__device__ __forceinline__ void tile_coords(int M, int N, int& tm, int& tn)
+{
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int total = tiles_m * tiles_n;
+    const int id = blockIdx.x;
+    const int xcd = id % NUM_XCD, j = id / NUM_XCD;
+    const int q = total / NUM_XCD, r = total % NUM_XCD;
+    const int t = xcd * q + (xcd < r ? xcd : r) + j;   // bijection onto [0, total)
+    const int group_size = GROUP_N * tiles_m;
+    const int gidx = t / group_size;
+    const int first_n = gidx * GROUP_N;
+    const int gn = (tiles_n - first_n) < GROUP_N ? (tiles_n - first_n) : GROUP_N;
+    const int in = t % group_size;
+    tm = in / gn;
+    tn = first_n + in % gn;
 }
 
 } // namespace mxl
