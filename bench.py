@@ -48,7 +48,27 @@ def parse():
     p.add_argument("--quick", action="store_true", help="headline only (skip the other rows)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain elementwise copy of known size (the reference point that "
+                        "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes) and exit")
     return p.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(torch):
+    """Three launches of torch's elementwise negate over a 1 GiB fp32 tensor:
+    each reads exactly COPY_BYTES and writes exactly COPY_BYTES."""
+    dev = torch.device("cuda:0")
+    src = torch.randn(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"read_bytes": COPY_BYTES, "write_bytes": COPY_BYTES,
+                                           "launches": 3}}))
 
 
 def main():
@@ -60,6 +80,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     import fp8_quantized_linear_amd as mxl
     import workloads as W
@@ -178,7 +202,7 @@ def traffic_from_profiles():
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("mx_device.h", "gemm_mx.hip"):
+    for f in ("mx_device.h", "gemm_mx.hip", "gemm_prefill.hip"):
         h.update(open(os.path.join(ROOT, "fp8_quantized_linear_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
