@@ -606,8 +606,8 @@ extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n,
         return "mx_decode_kernel<16 W rows per workgroup, 8-wave split-K, scaled mfma 16x16x128>";
     case SC_LARGE:
         if (!fused && mxl_prefill_ok(m, n, k))
-            return "mx_gemm_prefill_kernel<tile 256x256x128, 2x2 waves of 128x128, 4-slot LDS ring fed by "
-                   "buffer-to-LDS copies, scaled mfma 32x32x64>";
+            return "mx_gemm_prefill_kernel<tile 256x256x128, 2x2 waves of 128x128, 3-slot code ring + "
+                   "8-stage scale windows fed by buffer-to-LDS copies, stage-ahead fragments, scaled mfma 32x32x64>";
         return "mx_gemm_kernel<tile 256x256x128, 2x2 waves of 128x128, scaled mfma 32x32x64>";
     default:
         return "mx_gemm_kernel<tile 128x128x128, 2x2 waves of 64x64, scaled mfma 32x32x64>";

@@ -7,20 +7,31 @@
 //
 // Design (one 256x256 output tile per workgroup of 4 waves, each wave a
 // 128x128 sub-tile of 4x4 matrix-core fragments held in 256 AGPRs):
-//  * K advances in stages of 128 elements.  A stage is 16 KiB of A codes,
-//    16 KiB of W codes and 2 x 1 KiB of scales, and lives in one slot of a
-//    4-slot LDS ring (136 KiB), three stages ahead of the one being computed.
-//  * Stages are copied global -> LDS by the buffer-load-to-LDS path (each
-//    instruction writes 64 lanes x 16 B contiguously at the address in M0).
-//    No registers are spent on staging and no LDS write instructions are
-//    issued.  The swizzled LDS layout is obtained by choosing, per lane, which
-//    global 16-byte chunk lands at that lane's LDS position.  Rows past the
-//    end of A or W read as zero (buffer range check).
-//  * These copies are issued from inline assembly, so the compiler does not
-//    track them; every wave waits for its own copies of stage kt with an
-//    explicit vmcnt before the workgroup barrier that publishes the stage.
-//    Each wave issues exactly 10 copies per stage, so the count of copies
-//    still allowed in flight is 10 per later stage.
+//  * K advances in stages of 128 elements.  A stage's codes (16 KiB of A, 16
+//    KiB of W) live in one slot of a 3-slot LDS ring.  The E8M0 scales travel
+//    separately, in windows of 8 stages (32 bytes per row per operand, 16 KiB
+//    per window) held in a 3-window LDS ring: fetching 4 scale bytes per row
+//    per stage would cost one 64-row gather per 256 bytes, which measured as
+//    the dominant cost of the loop; a window fetch moves 32 contiguous bytes
+//    per row.
+//  * Everything is copied global -> LDS by the buffer-load-to-LDS path (each
+//    instruction writes 64 lanes x its width contiguously at the address in
+//    M0), so no registers are spent on staging.  The swizzled code layout is
+//    obtained by choosing, per lane, which global 16-byte chunk lands at that
+//    lane's LDS position.  Rows past the end of A or W read as zero (buffer
+//    range check); copies past the last stage use a zero-sized buffer and
+//    fill a free slot with zeros, which keeps the loop free of branches and
+//    the outstanding-copy count the same every stage.
+//  * Each wave issues 10 copies per stage: 2 scale pieces (8 rows x 32 B each)
+//    of the window after next, then 8 code copies (16 rows x 64 B each) of
+//    the stage three ahead.  A wave waits for its own copies with an explicit
+//    vmcnt (the copies come from inline assembly the compiler does not
+//    track), then a workgroup barrier publishes them.
+//  * The fragments of stage s+1 (16 code reads, 8 scale reads per lane) are
+//    read from LDS while the 32 matrix-core instructions of stage s run, into
+//    a second register set, so no LDS latency is exposed; the loop is
+//    unrolled by two to alternate the sets without copies.  Reads, copies and
+//    matrix-core instructions are pinned in place with scheduling barriers.
 //  * W is the matrix core's first operand, A the second, so each lane's
 //    accumulator holds 4 consecutive output columns; the epilogue stages each
 //    32-row band of a wave's tile through LDS and writes whole 256-byte row
@@ -30,18 +41,23 @@
 //    group g supplies the E8M0 scale of K block g.  Accumulator register i of
 //    lane l is C[(i/4)*8 + g*4 + i%4][r] with C = W_frag x A_frag^T.
 //  * Tile order: XCD-aware grouped order (tile_coords in mx_device.h).
-// Requires K % 128 == 0 (whole stages, aligned scale dwords); other shapes
-// use the general tile kernel.
+// Requires K % 128 == 0 (whole stages); other shapes use the general tile
+// kernel.
 #include "mx_device.h"
 
 namespace mxl {
 
-constexpr int PF_BM = 256, PF_BN = 256, PF_BK = 128, PF_NS = 4;
+constexpr int PF_BM = 256, PF_BN = 256, PF_BK = 128;
 constexpr int PF_ROWB = PF_BK / 2;                 // E2M1 bytes of a row per stage
 constexpr int PF_TILE = PF_BM * PF_ROWB;           // 16 KiB per operand per stage
-constexpr int PF_SCALE = PF_BM * 4;                // 1 KiB of scales per operand per stage
-constexpr int PF_SLOT = 2 * PF_TILE + 2 * PF_SCALE;
-constexpr int PF_LDS = PF_NS * PF_SLOT;            // 139264 bytes
+constexpr int PF_NS = 3;                           // code slots; copies run PF_NS stages ahead
+constexpr int PF_SLOT = 2 * PF_TILE;               // A codes, then W codes
+constexpr int PF_SWS = 8;                          // stages per scale window
+constexpr int PF_SWB = PF_SWS * 4;                 // scale bytes per row per window
+constexpr int PF_WIN = 2 * PF_BM * PF_SWB;         // A scales [256][32 B], then W scales
+constexpr int PF_NWIN = 3;
+constexpr int PF_SC0 = PF_NS * PF_SLOT;            // the scale windows follow the code ring
+constexpr int PF_LDS = PF_SC0 + PF_NWIN * PF_WIN;  // 147456 bytes
 constexpr int PF_COPIES = 10;                      // copies per wave per stage
 
 struct PrefillArgs {
@@ -72,18 +88,26 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
+// Raw buffer descriptor (stride 0) over `bytes` bytes at `base`, built as
+// four uniform dwords so it lives in SGPRs: base address (48 bits),
+// num_records, and the dword-format word that raw buffer loads use.
 __device__ __forceinline__ int4_t make_rsrc(const void* base, uint32_t bytes)
 {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+    const uint64_t a = (uint64_t)(uintptr_t)base;
     int4_t v;
-    __builtin_memcpy(&v, &r, 16);
-    // uniform by construction; make that explicit so it lives in SGPRs
-    v[0] = __builtin_amdgcn_readfirstlane(v[0]);
-    v[1] = __builtin_amdgcn_readfirstlane(v[1]);
-    v[2] = __builtin_amdgcn_readfirstlane(v[2]);
-    v[3] = __builtin_amdgcn_readfirstlane(v[3]);
+    v[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    v[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    v[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    v[3] = 0x00020000;
     return v;
 }
+
+// one stage's operands in registers: code fragments per 64-wide step kk, and
+// the raw scale dwords (4 blocks of the stage) of this lane's fragment rows
+struct PfFrags {
+    int4_t a[2][4], w[2][4];
+    int sa[4], sw[4];
+};
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
@@ -106,12 +130,10 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     const int4_t rsrc_ws = make_rsrc(p.w_s, (uint32_t)p.N * KB);
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
-    // Per-lane source offsets.  Wave w copies code segments 4w .. 4w+3 of each
-    // operand (a segment is 16 rows x 64 B = 1 KiB of LDS); LDS position L of
-    // a segment is row 16*seg + L/4, physical chunk L%4, which holds logical
-    // chunk (L%4) ^ swz(row).  Scale segment w holds dwords 64w .. 64w+63 of
-    // the stage's scale area, ordered (row group of 128, r, fragment i): dword
-    // p is tile row (p/128)*128 + (p%4)*32 + (p/4)%32.
+    // Code copies: wave w copies segments 4w .. 4w+3 (16 rows x 64 B = 1 KiB
+    // of LDS each) of each operand.  LDS position L of a segment is row
+    // 16*seg + L/4, physical chunk L%4, which holds logical chunk
+    // (L%4) ^ swz(row).
     int a_voff[4], w_voff[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -120,23 +142,65 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
         a_voff[s] = (m0 + row) * row_bytes + c * 16;
         w_voff[s] = (n0 + row) * row_bytes + c * 16;
     }
-    int as_voff, ws_voff;
-    {
-        const int pidx = 64 * wave + lane;
-        const int row = (pidx / 128) * 128 + (pidx % 4) * 32 + (pidx / 4) % 32;
-        as_voff = (m0 + row) * KB;
-        ws_voff = (n0 + row) * KB;
-    }
+    // Scale pieces: piece j (0..7) of a window is copy t = 4 j + wave of each
+    // operand, rows 8t .. 8t+7 of the tile, 32 bytes each ([row][32 B] in LDS).
+    // The window offset is part of the per-lane offset so that the buffer
+    // range check covers it (a partial last window may run past a row).
+    const int srow = lane >> 3, sdw = lane & 7;
+    auto sc_voff = [&](int base, int j, int win) {
+        return (base + 8 * (4 * j + wave) + srow) * KB + win * PF_SWB + sdw * 4;
+    };
 
-    auto issue_stage = [&](int kt) {
-        const uint32_t slot = lds0 + (uint32_t)((kt % PF_NS) * PF_SLOT);
-        const int soff_codes = kt * PF_ROWB, soff_scales = kt * 4;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) dma_b128(slot + (4 * wave + s) * 1024, a_voff[s], rsrc_a, soff_codes);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) dma_b128(slot + PF_TILE + (4 * wave + s) * 1024, w_voff[s], rsrc_w, soff_codes);
-        dma_b32(slot + 2 * PF_TILE + wave * 256, as_voff, rsrc_as, soff_scales);
-        dma_b32(slot + 2 * PF_TILE + PF_SCALE + wave * 256, ws_voff, rsrc_ws, soff_scales);
+    // Copy c (0..9) of virtual stage y: c = 0, 1 are the A and W pieces
+    // (y + 4) % 8 of scale window (y + 4) / 8 + 1; c = 2..9 are the code
+    // copies of stage y + PF_NS.  Stage y + PF_NS goes to the slot of stage y,
+    // whose fragments were read during stage y - 1.  A window's pieces are
+    // issued during the 8 stages that end four stages before its first stage
+    // is read, into the buffer of the window three back.
+    auto copy = [&](int y, int c) {
+        if (c < 2) {
+            const int win = ((y + 4) >> 3) + 1, j = (y + 4) & 7;
+            const int live = __builtin_amdgcn_readfirstlane(win * PF_SWS < nk ? 1 : 0);
+            int4_t r = c == 0 ? rsrc_as : rsrc_ws;
+            r[2] = live ? r[2] : 0;
+            const uint32_t dst = lds0 + PF_SC0 + (uint32_t)((win % PF_NWIN) * PF_WIN) + (4 * j + wave) * 256 +
+                                 c * PF_BM * PF_SWB;
+            dma_b32(dst, sc_voff(c == 0 ? m0 : n0, j, win), r, 0);
+        } else {
+            const int ks = y + PF_NS;
+            const int live = __builtin_amdgcn_readfirstlane(ks < nk ? 1 : 0);
+            const int s = (c - 2) & 3;
+            int4_t r = c < 6 ? rsrc_a : rsrc_w;
+            r[2] = live ? r[2] : 0;
+            const uint32_t dst = lds0 + (uint32_t)((ks % PF_NS) * PF_SLOT) + (c < 6 ? 0 : PF_TILE) + (4 * wave + s) * 1024;
+            dma_b128(dst, c < 6 ? a_voff[s] : w_voff[s], r, ks * PF_ROWB);
+        }
+    };
+
+    // LDS read q (0..23) of stage s: 16 code fragments, then 8 scale dwords
+    auto read_piece = [&](int s, int q, PfFrags& f) {
+        if (q < 16) {
+            const uint8_t* slot = smem + (s % PF_NS) * PF_SLOT;
+            const int kk = q >> 3, x = q & 7;
+            if (x < 4) {
+                const int row = wm * 128 + x * 32 + r32;
+                f.a[kk][x] = *reinterpret_cast<const int4_t*>(slot + row * PF_ROWB + (((2 * kk + g) ^ pf_swz(row)) * 16));
+            } else {
+                const int row = wn * 128 + (x - 4) * 32 + r32;
+                f.w[kk][x - 4] =
+                    *reinterpret_cast<const int4_t*>(slot + PF_TILE + row * PF_ROWB + (((2 * kk + g) ^ pf_swz(row)) * 16));
+            }
+        } else {
+            const uint8_t* win = smem + PF_SC0 + ((s / PF_SWS) % PF_NWIN) * PF_WIN + (s % PF_SWS) * 4;
+            const int x = q - 16;
+            if (x < 4) {
+                const int row = wm * 128 + x * 32 + r32;
+                f.sa[x] = (int)*reinterpret_cast<const uint32_t*>(win + row * PF_SWB);
+            } else {
+                const int row = wn * 128 + (x - 4) * 32 + r32;
+                f.sw[x - 4] = (int)*reinterpret_cast<const uint32_t*>(win + PF_BM * PF_SWB + row * PF_SWB);
+            }
+        }
     };
 
     float16_t acc[4][4];
@@ -147,63 +211,77 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    auto compute_stage = [&](int kt) {
-        const uint8_t* slot = smem + (kt % PF_NS) * PF_SLOT;
-        const uint8_t* a_t = slot;
-        const uint8_t* w_t = slot + PF_TILE;
-        // this lane's 4 scale dwords per operand (fragments i = 0..3), shifted so
-        // that byte 2*kk selects K block 2*kk + g
-        const int4_t sa4 = *reinterpret_cast<const int4_t*>(slot + 2 * PF_TILE + (wm * 128 + r32 * 4) * 4);
-        const int4_t sw4 = *reinterpret_cast<const int4_t*>(slot + 2 * PF_TILE + PF_SCALE + (wn * 128 + r32 * 4) * 4);
+    // matrix-core instruction q (0..31) of a stage: step kk = q / 16, fragment (i, j)
+    auto mfma = [&](int q, const PfFrags& f, const int* sa, const int* sw) {
+        const int kk = q >> 4, i = (q >> 2) & 3, j = q & 3;
+        const int8_t_ b8 = int8_t_{f.w[kk][j][0], f.w[kk][j][1], f.w[kk][j][2], f.w[kk][j][3], 0, 0, 0, 0};
+        const int8_t_ a8 = int8_t_{f.a[kk][i][0], f.a[kk][i][1], f.a[kk][i][2], f.a[kk][i][3], 0, 0, 0, 0};
+        if (kk == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 0, sw[j], 0, sa[i]);
+        else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 2, sw[j], 2, sa[i]);
+    };
+
+    // Stage s: computed from `cur`; stage s + 1 is read into `nxt`; virtual
+    // stage s issues its copies.
+    auto stage = [&](int s, const PfFrags& cur, PfFrags& nxt) {
+        // The copies of stage s + 1 were issued two stages ago; only the 10 of
+        // the previous stage may still be in flight.
+        wait_vmcnt<PF_COPIES>();
+        lds_barrier();
+        // byte 2 kk + g of a scale dword is this lane's block; after the shift
+        // it sits at byte 2 kk, which the instruction's op_sel picks
         int sa[4], sw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sa[i] = (int)((uint32_t)sa4[i] >> (8 * g));
-            sw[i] = (int)((uint32_t)sw4[i] >> (8 * g));
+            sa[i] = (int)((uint32_t)cur.sa[i] >> (8 * g));
+            sw[i] = (int)((uint32_t)cur.sw[i] >> (8 * g));
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            int4_t fa[4], fw[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * 128 + i * 32 + r32;
-                fa[i] = *reinterpret_cast<const int4_t*>(a_t + row * PF_ROWB + (((2 * kk + g) ^ pf_swz(row)) * 16));
+        for (int q = 0; q < 32; ++q) {
+            mfma(q, cur, sa, sw);
+            if (q < 24) {
+                __builtin_amdgcn_sched_barrier(0);
+                read_piece(s + 1, q, nxt);
+                __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = wn * 128 + j * 32 + r32;
-                fw[j] = *reinterpret_cast<const int4_t*>(w_t + row * PF_ROWB + (((2 * kk + g) ^ pf_swz(row)) * 16));
+            if ((q % 3) == 1 && q / 3 < PF_COPIES) {
+                __builtin_amdgcn_sched_barrier(0);
+                copy(s, q / 3);
+                __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int8_t_ b8 = int8_t_{fw[j][0], fw[j][1], fw[j][2], fw[j][3], 0, 0, 0, 0};
-                    const int8_t_ a8 = int8_t_{fa[i][0], fa[i][1], fa[i][2], fa[i][3], 0, 0, 0, 0};
-                    if (kk == 0)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 0, sw[j], 0, sa[i]);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 2, sw[j], 2, sa[i]);
-                }
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: three stages in flight
+    // Prologue: all of window 0, then virtual stages -4 .. -1 (window 1's
+    // pieces 0..3 and the codes of stages 0..2).
 #pragma unroll
-    for (int s = 0; s < PF_NS - 1; ++s)
-        if (s < nk) issue_stage(s);
-
-    for (int kt = 0; kt < nk; ++kt) {
-        // wait for this wave's copies of stage kt (later stages may stay in flight)
-        const int later = nk - 1 - kt;
-        if (later >= 2) wait_vmcnt<2 * PF_COPIES>();
-        else if (later == 1) wait_vmcnt<PF_COPIES>();
-        else wait_vmcnt<0>();
-        lds_barrier();  // stage kt is in LDS for every wave; slot of stage kt-1 is free
-        if (kt + PF_NS - 1 < nk) issue_stage(kt + PF_NS - 1);
-        compute_stage(kt);
+    for (int j = 0; j < PF_SWS; ++j) {
+        const uint32_t dst = lds0 + PF_SC0 + (4 * j + wave) * 256;
+        dma_b32(dst, sc_voff(m0, j, 0), rsrc_as, 0);
+        dma_b32(dst + PF_BM * PF_SWB, sc_voff(n0, j, 0), rsrc_ws, 0);
     }
-    lds_barrier();  // all waves are done reading the ring
+    copy(-4, 0);
+    copy(-4, 1);
+    for (int y = -3; y < 0; ++y)
+#pragma unroll
+        for (int c = 0; c < PF_COPIES; ++c) copy(y, c);
+    wait_vmcnt<2 * PF_COPIES>();  // window 0 and stage 0 have landed
+    lds_barrier();
+    PfFrags X, Y;
+#pragma unroll
+    for (int q = 0; q < 24; ++q) read_piece(0, q, X);
+
+    int s = 0;
+    for (; s + 1 < nk; s += 2) {
+        stage(s, X, Y);
+        stage(s + 1, Y, X);
+    }
+    if (s < nk) stage(s, X, Y);
+    wait_vmcnt<0>();   // the trailing zero-fill copies have landed
+    lds_barrier();     // every wave is done with the rings
 
     // Epilogue, one 32-row band (fragment row i) at a time through this
     // wave's private LDS region: write the band row-major, read it back as
@@ -245,12 +323,13 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
                     const int4_t iv = int4_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
                     __builtin_nontemporal_store(iv, reinterpret_cast<int4_t*>(yrow + (size_t)n * ESZ));
                 } else {
-                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                     for (int e = 0; e < 16 / ESZ; ++e) {
+                        const int wi = OUT_F32 ? e : e / 2;
+                        const uint32_t word = wi == 0 ? v.x : wi == 1 ? v.y : wi == 2 ? v.z : v.w;
                         if (n + e < p.N) {
-                            if (OUT_F32) reinterpret_cast<uint32_t*>(yrow)[n + e] = w[e];
-                            else reinterpret_cast<uint16_t*>(yrow)[n + e] = (uint16_t)(w[e / 2] >> (16 * (e % 2)));
+                            if (OUT_F32) reinterpret_cast<uint32_t*>(yrow)[n + e] = word;
+                            else reinterpret_cast<uint16_t*>(yrow)[n + e] = (uint16_t)(word >> (16 * (e % 2)));
                         }
                     }
                 }
