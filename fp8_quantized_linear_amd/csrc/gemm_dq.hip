@@ -305,9 +305,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
                     if (OUT_F32) {
                         reinterpret_cast<float*>(p.y)[(size_t)m * p.N + n] = v;
                     } else {
-                        uint32_t u = __float_as_uint(v);
-                        u += 0x7FFFu + ((u >> 16) & 1u);
-                        reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + n] = (uint16_t)(u >> 16);
+                        reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + n] = f32_to_bf16_rne(v);
                     }
                 }
             }

@@ -392,8 +392,8 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
                         *reinterpret_cast<float4_t*>(reinterpret_cast<float*>(p.y) + (size_t)m * p.N + n) =
                             float4_t{v0, v1, v2, v3};
                     } else {
-                        const uint32_t lo = (uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16);
-                        const uint32_t hi = (uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16);
+                        const uint32_t lo = bf16x2_rne(v0, v1);
+                        const uint32_t hi = bf16x2_rne(v2, v3);
                         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + (size_t)m * p.N + n) =
                             make_uint2(lo, hi);
                     }

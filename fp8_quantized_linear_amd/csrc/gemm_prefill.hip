@@ -302,10 +302,8 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
                     *reinterpret_cast<float4_t*>(dst) =
                         float4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                 } else {
-                    const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * q]) |
-                                        ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * q + 1]) << 16);
-                    const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * q + 2]) |
-                                        ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * q + 3]) << 16);
+                    const uint32_t lo = bf16x2_rne(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+                    const uint32_t hi = bf16x2_rne(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
                     *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
                 }
             }

@@ -205,12 +205,17 @@ __device__ __forceinline__ uint32_t e2m1_rne_ratio(double num, double den)
 }
 
 // fp32 -> bf16, round to nearest even (finite inputs).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+// fp32 -> bf16, round to nearest even, on the hardware converter
+// (v_cvt_pk_bf16_f32).  For every finite input it equals the bit rule
+// (u + 0x7fff + ((u >> 16) & 1)) >> 16 (checked exhaustively over all 2^32
+// patterns); non-finite inputs are outside the library's contract.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)bf16x2_rne(f, 0.0f); }
 
 // Tile ordering.  Workgroups are dispatched round-robin over the 8 XCDs
 // (workgroup i runs on XCD i % 8), and each XCD has its own L2.  So the
