@@ -447,7 +447,7 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream)
 typedef float float4_t_ __attribute__((ext_vector_type(4)));
 
 template <int MT, bool OUT_F32>
-__global__ __launch_bounds__(512) void mx_decode_kernel(GemmArgs p)
+__global__ __launch_bounds__(512) void mx_decode_generic_kernel(GemmArgs p)
 {
     constexpr int WAVES = 8, UNROLL = 4;
     __shared__ float red[WAVES][MT][64][4];
@@ -515,10 +515,290 @@ __global__ __launch_bounds__(512) void mx_decode_kernel(GemmArgs p)
     }
 }
 
+// Decode-shaped MXFP4 GEMM for K too large for mx_decode_kernel's LDS block
+// (M <= 32, K % 128 == 0).  Its cost is the number of vector-memory
+// instructions per CU as much as bytes.
+//  * One workgroup of 4 waves owns 32 rows of W (two groups of 16); wave w
+//    owns a contiguous quarter of K and walks it in chunks of CH stages of
+//    128, issuing every load of a chunk before its matrix-core work.
+//  * Operands follow the lane layout of v_mfma_scale_f32_16x16x128_f8f6f4
+//    (lane r + 16 g: row r, K elements [32 g, 32 g + 32) of the stage), so
+//    each 16-byte load is a fragment: one instruction reads 16 rows x 64
+//    contiguous bytes.  An A fragment (MT groups of 16 rows; rows past M
+//    read as zero through the buffer range check) serves both W groups.
+//  * The scales of the workgroup's W rows and of A are contiguous in memory;
+//    they are staged once into LDS with 16-byte loads (a few instructions per
+//    workgroup instead of one per stage) and read from there per stage.
+//  * The four K quarters are summed through LDS at the end.
+template <int MT, int CH, bool OUT_F32>
+__global__ __launch_bounds__(256) void mx_decode_direct_kernel(GemmArgs p)
+{
+    constexpr int WAVES = 4, RG = 2;   // waves, W row groups of 16
+    extern __shared__ __align__(16) uint8_t dsm[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the step offsets go in SGPRs
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16 * RG;
+    const int K = p.K, KB = K / 32, row_bytes = K / 2;
+    const int steps = K / 128;
+    const int s0 = wave * steps / WAVES, s1 = (wave + 1) * steps / WAVES;
+
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)p.w_q, (short)0, p.N * row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc((void*)p.w_s, (short)0, p.N * KB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_q, (short)0, p.M * row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_s, (short)0, p.M * KB, 0x00020000);
+
+    // LDS: W scales [16 RG rows][KB], A scales [16 MT rows][KB], then the reduction area
+    uint8_t* sw_lds = dsm;
+    uint8_t* sa_lds = dsm + 16 * RG * KB;
+    float4_t_* red = reinterpret_cast<float4_t_*>(dsm + 16 * (RG + MT) * KB);   // [WAVES][RG][MT][64]
+
+    // stage the scales: 16-byte pieces of the two contiguous byte ranges
+    {
+        const int wn = 16 * RG * KB / 16, an = 16 * MT * KB / 16;
+        for (int i = tid; i < wn + an; i += 256) {
+            const int4_t v = i < wn ? __builtin_amdgcn_raw_buffer_load_b128(rws, n0 * KB + i * 16, 0, 0)
+                                    : __builtin_amdgcn_raw_buffer_load_b128(ras, (i - wn) * 16, 0, 0);
+            *reinterpret_cast<int4_t*>(dsm + i * 16) = v;
+        }
+    }
+
+    int w_voff[RG], a_voff[MT];
+#pragma unroll
+    for (int h = 0; h < RG; ++h) w_voff[h] = (n0 + 16 * h + r) * row_bytes + g * 16;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) a_voff[t] = (16 * t + r) * row_bytes + g * 16;
+
+    float4_t_ acc[RG][MT];
+#pragma unroll
+    for (int h = 0; h < RG; ++h)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[h][t] = float4_t_{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();   // scales are in LDS
+
+    // `cnt` stages from stage sb (cnt == CH: straight-line code)
+    auto chunk = [&](int sb, int cnt) {
+        int4_t wf[CH][RG], af[CH][MT];
+#pragma unroll
+        for (int u = 0; u < CH; ++u)
+            if (u < cnt) {
+#pragma unroll
+                for (int h = 0; h < RG; ++h) wf[u][h] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff[h], (sb + u) * 64, 0);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) af[u][t] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_voff[t], (sb + u) * 64, 0);
+            }
+#pragma unroll
+        for (int u = 0; u < CH; ++u)
+            if (u < cnt) {
+                const int st = sb + u;
+                int wsb[RG], asb[MT];
+                // the dword of a row's scales for stage st holds blocks 4 st .. 4 st + 3; lane group g takes byte g
+#pragma unroll
+                for (int h = 0; h < RG; ++h)
+                    wsb[h] = (int)(*reinterpret_cast<const uint32_t*>(sw_lds + (16 * h + r) * KB + 4 * st) >> (8 * g));
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    asb[t] = (int)(*reinterpret_cast<const uint32_t*>(sa_lds + (16 * t + r) * KB + 4 * st) >> (8 * g));
+#pragma unroll
+                for (int h = 0; h < RG; ++h) {
+                    const int8_t_ b8 = int8_t_{wf[u][h][0], wf[u][h][1], wf[u][h][2], wf[u][h][3], 0, 0, 0, 0};
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        const int8_t_ a8 = int8_t_{af[u][t][0], af[u][t][1], af[u][t][2], af[u][t][3], 0, 0, 0, 0};
+                        acc[h][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[h][t], 4, 4, 0, asb[t], 0, wsb[h]);
+                    }
+                }
+            }
+    };
+    int sb = s0;
+    for (; sb + CH <= s1; sb += CH) chunk(sb, CH);
+    if (sb < s1) chunk(sb, s1 - sb);
+
+#pragma unroll
+    for (int h = 0; h < RG; ++h)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) red[((wave * RG + h) * MT + t) * 64 + lane] = acc[h][t];
+    __syncthreads();
+    // thread e < RG * MT * 64 finishes accumulator lane e % 64 of (row group h, A tile t):
+    // A rows 16 t + 4 (l / 16) + i, W row n0 + 16 h + l % 16
+    if (tid < RG * MT * 64) {
+        const int l = tid & 63, ht = tid >> 6, h = ht / MT, t = ht % MT;
+        float4_t_ v = red[(h * MT + t) * 64 + l];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+            const float4_t_ x = red[((w * RG + h) * MT + t) * 64 + l];
+            v = float4_t_{v[0] + x[0], v[1] + x[1], v[2] + x[2], v[3] + x[3]};
+        }
+        const int nn = n0 + 16 * h + (l & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 16 * t + 4 * (l >> 4) + i;
+            if (m < p.M && nn < p.N) {
+                if (OUT_F32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + nn] = v[i];
+                else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + nn] = f32_to_bf16_rne(v[i]);
+            }
+        }
+    }
+}
+
+template <int MT>
+static size_t decode_direct_lds_bytes(int K)
+{
+    return (size_t)16 * (2 + MT) * (K / 32) + (size_t)4 * 2 * MT * 64 * 16;
+}
+
+// Decode-shaped MXFP4 GEMM (M <= 32, K % 512 == 0, K up to 8192):
+// a stream over W.  One workgroup of 4 waves owns 16 rows of W.
+//  * W streams as whole rows: the 16 x K/2 byte block is contiguous, and each
+//    buffer-to-LDS copy moves 1 KiB of it (8 full cache lines; the pattern
+//    that streams fastest).  A copy lane places its 16-byte unit u of row r at
+//    unit u ^ (r & 15) of the LDS row (within aligned groups of 16 units), so
+//    the fragment reads below hit 16 distinct banks.
+//  * Scales of the W rows and of A (contiguous byte ranges) are copied into
+//    LDS the same way, 256 bytes per copy, so one wait covers everything.
+//  * After one barrier, wave w takes a contiguous quarter of K and runs
+//    v_mfma_scale_f32_16x16x128_f8f6f4 per stage (lane r + 16 g: row r, K
+//    elements [32 g, 32 g + 32) of the stage): W fragments from LDS, A
+//    fragments (MT groups of 16 rows; rows past M read as zero) loaded
+//    directly; they are the same for every workgroup and stay in the caches.
+//  * The four K quarters are summed through LDS (aliasing the W block).
+template <int MT, bool OUT_F32>
+__global__ __launch_bounds__(256) void mx_decode_kernel(GemmArgs p)
+{
+    constexpr int WAVES = 4;
+    extern __shared__ __align__(16) uint8_t dsm[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the step offsets go in SGPRs
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int K = p.K, KB = K / 32, row_bytes = K / 2;
+    const int steps = K / 128;
+    const int s0 = wave * steps / WAVES, s1 = (wave + 1) * steps / WAVES;
+    const int units = KB;                  // 16-byte units per W row
+    const int swz_units = units & ~15;     // units inside whole groups of 16 get swizzled
+
+    // LDS: W block [16][row_bytes] (later the reduction area, so at least its size), W scales [16][KB],
+    // A scales [16 MT][KB]
+    constexpr int RED_BYTES = WAVES * MT * 64 * 16;
+    uint8_t* w_lds = dsm;
+    uint8_t* sw_lds = dsm + (16 * row_bytes > RED_BYTES ? 16 * row_bytes : RED_BYTES);
+    uint8_t* sa_lds = sw_lds + 16 * KB;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dsm);
+
+    // W block copies: copy j moves block units [64 j, 64 j + 64)
+    {
+        const int4_t rsrc = make_rsrc(p.w_q, (uint32_t)p.N * row_bytes);
+        const int ncopy = 16 * units / 64;
+        for (int j = wave; j < ncopy; j += WAVES) {
+            const int q = 64 * j + lane, rr = q / units, pu = q - rr * units;
+            const int u = pu < swz_units ? pu ^ (rr & 15) : pu;
+            dma_b128(lds0 + (uint32_t)(64 * j * 16), (n0 + rr) * row_bytes + u * 16, rsrc, 0);
+        }
+    }
+    // scale copies, 256 bytes each: the W rows' scales (16 KB bytes, contiguous) and A's (16 MT KB bytes)
+    {
+        const int4_t rws = make_rsrc(p.w_s, (uint32_t)p.N * KB);
+        const int4_t ras = make_rsrc(p.a_s, (uint32_t)p.M * KB);
+        const uint32_t sbase = lds0 + (uint32_t)(sw_lds - dsm);
+        const int wn = 16 * KB / 256, an = 16 * MT * KB / 256;   // KB % 16 == 0 here
+        for (int j = wave; j < wn + an; j += WAVES) {
+            if (j < wn) dma_b32(sbase + j * 256, n0 * KB + j * 256 + lane * 4, rws, 0);
+            else dma_b32(sbase + j * 256, (j - wn) * 256 + lane * 4, ras, 0);
+        }
+    }
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_q, (short)0, p.M * row_bytes, 0x00020000);
+    // this wave's A fragments, issued before waiting on anything
+    constexpr int SMAX = 16;   // stages per wave held in registers (K <= 8192)
+    int4_t af[SMAX][MT];
+#pragma unroll
+    for (int u = 0; u < SMAX; ++u)
+        if (s0 + u < s1)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                af[u][t] = __builtin_amdgcn_raw_buffer_load_b128(ra, (16 * t + r) * row_bytes + g * 16, (s0 + u) * 64, 0);
+
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    float4_t_ acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = float4_t_{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < SMAX; ++u) {
+        const int st = s0 + u;
+        if (st < s1) {
+            const int un = 4 * st + g;
+            const int pu = un < swz_units ? un ^ r : un;
+            const int4_t wv = *reinterpret_cast<const int4_t*>(w_lds + r * row_bytes + pu * 16);
+            const int8_t_ b8 = int8_t_{wv[0], wv[1], wv[2], wv[3], 0, 0, 0, 0};
+            // the dword of a row's scales for stage st holds blocks 4 st .. 4 st + 3; lane group g takes byte g
+            const int wsb = (int)(*reinterpret_cast<const uint32_t*>(sw_lds + r * KB + 4 * st) >> (8 * g));
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const int asb = (int)(*reinterpret_cast<const uint32_t*>(sa_lds + (16 * t + r) * KB + 4 * st) >> (8 * g));
+                const int8_t_ a8 = int8_t_{af[u][t][0], af[u][t][1], af[u][t][2], af[u][t][3], 0, 0, 0, 0};
+                acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 4, 4, 0, asb, 0, wsb);
+            }
+        }
+    }
+    __syncthreads();   // every wave is done with the W block
+    float4_t_* red = reinterpret_cast<float4_t_*>(w_lds);   // [WAVES][MT][64]
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[(wave * MT + t) * 64 + lane] = acc[t];
+    __syncthreads();
+    // thread e < MT * 64 finishes accumulator lane e % 64 of A tile t:
+    // A rows 16 t + 4 (l / 16) + i, W row n0 + l % 16
+    if (tid < MT * 64) {
+        const int l = tid & 63, t = tid >> 6;
+        float4_t_ v = red[t * 64 + l];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+            const float4_t_ x = red[(w * MT + t) * 64 + l];
+            v = float4_t_{v[0] + x[0], v[1] + x[1], v[2] + x[2], v[3] + x[3]};
+        }
+        const int nn = n0 + (l & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 16 * t + 4 * (l >> 4) + i;
+            if (m < p.M && nn < p.N) {
+                if (OUT_F32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + nn] = v[i];
+                else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + nn] = f32_to_bf16_rne(v[i]);
+            }
+        }
+    }
+}
+
+template <int MT>
+static size_t decode_lds_bytes(int K)
+{
+    const size_t block = (size_t)16 * (K / 2), red = (size_t)4 * MT * 64 * 16;
+    return (block > red ? block : red) + (size_t)16 * (1 + MT) * (K / 32);
+}
+
+// which decode kernel runs for this shape: 2 = LDS block, 1 = direct loads, 0 = generic
+static int decode_kind(int64_t m, int64_t k)
+{
+    if (k % 128 != 0) return 0;
+    const bool mt1 = m <= 16;
+    if (k % 512 == 0 && k <= 8192 && (mt1 ? decode_lds_bytes<1>((int)k) : decode_lds_bytes<2>((int)k)) <= 65536)
+        return 2;
+    if ((mt1 ? decode_direct_lds_bytes<1>((int)k) : decode_direct_lds_bytes<2>((int)k)) <= 65536) return 1;
+    return 0;
+}
+
 template <int MT, bool OUT_F32>
 hipError_t launch_decode(const GemmArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((mx_decode_kernel<MT, OUT_F32>), dim3((a.N + 15) / 16), dim3(512), 0, stream, a);
+    const int kind = decode_kind(MT == 1 ? 16 : 32, a.K);
+    if (kind == 2)
+        hipLaunchKernelGGL((mx_decode_kernel<MT, OUT_F32>), dim3((a.N + 15) / 16), dim3(256), decode_lds_bytes<MT>(a.K),
+                           stream, a);
+    else if (kind == 1)
+        hipLaunchKernelGGL((mx_decode_direct_kernel<MT, MT == 1 ? 10 : 5, OUT_F32>), dim3((a.N + 31) / 32), dim3(256),
+                           decode_direct_lds_bytes<MT>(a.K), stream, a);
+    else
+        hipLaunchKernelGGL((mx_decode_generic_kernel<MT, OUT_F32>), dim3((a.N + 15) / 16), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -603,7 +883,13 @@ extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n,
 {
     switch (classify(a_bits, m, n, k, fused != 0)) {
     case SC_DECODE:
-        return "mx_decode_kernel<16 W rows per workgroup, 8-wave split-K, scaled mfma 16x16x128>";
+        switch (decode_kind(m, k)) {
+        case 2: return "mx_decode_kernel<16 W rows per workgroup, whole-row copies into swizzled LDS, 4 waves over K "
+                       "quarters, scaled mfma 16x16x128>";
+        case 1: return "mx_decode_direct_kernel<32 W rows per workgroup, 4 waves over K quarters, scales staged in LDS, "
+                       "scaled mfma 16x16x128>";
+        default: return "mx_decode_generic_kernel<16 W rows per workgroup, 8-wave split-K, scaled mfma 16x16x128>";
+        }
     case SC_LARGE:
         if (!fused && mxl_prefill_ok(m, n, k))
             return "mx_gemm_prefill_kernel<tile 256x256x128, 2x2 waves of 128x128, 3-slot code ring + "

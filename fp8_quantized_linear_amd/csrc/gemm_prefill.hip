@@ -71,37 +71,6 @@ struct PrefillArgs {
 // same logical chunk of 32 consecutive rows touch distinct banks.
 __device__ __forceinline__ int pf_swz(int row) { return (row >> 1) & 3; }
 
-__device__ __forceinline__ void dma_b128(uint32_t lds, int voff, const int4_t& rsrc, int soff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-}
-__device__ __forceinline__ void dma_b32(uint32_t lds, int voff, const int4_t& rsrc, int soff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
-// Raw buffer descriptor (stride 0) over `bytes` bytes at `base`, built as
-// four uniform dwords so it lives in SGPRs: base address (48 bits),
-// num_records, and the dword-format word that raw buffer loads use.
-__device__ __forceinline__ int4_t make_rsrc(const void* base, uint32_t bytes)
-{
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    int4_t v;
-    v[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    v[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-    v[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    v[3] = 0x00020000;
-    return v;
-}
-
 // one stage's operands in registers: code fragments per 64-wide step kk, and
 // the raw scale dwords (4 blocks of the stage) of this lane's fragment rows
 struct PfFrags {

@@ -217,6 +217,43 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi)
 }
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)bf16x2_rne(f, 0.0f); }
 
+// Buffer-to-LDS copies.  Each instruction writes its 64 lanes x width bytes
+// contiguously at the LDS address in M0, reading each lane's bytes from the
+// buffer at (voff + soff); lanes past the buffer's size read zero.  They are
+// issued from inline assembly, so the compiler does not count them: callers
+// wait with wait_vmcnt, whose count includes them, before a barrier that
+// publishes the data.
+__device__ __forceinline__ void dma_b128(uint32_t lds, int voff, const int4_t& rsrc, int soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void dma_b32(uint32_t lds, int voff, const int4_t& rsrc, int soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Raw buffer descriptor (stride 0) over `bytes` bytes at `base`, built as
+// four uniform dwords so it lives in SGPRs: base address (48 bits),
+// num_records, and the dword-format word that raw buffer loads use.
+__device__ __forceinline__ int4_t make_rsrc(const void* base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    int4_t v;
+    v[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    v[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    v[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    v[3] = 0x00020000;
+    return v;
+}
+
 // Tile ordering.  Workgroups are dispatched round-robin over the 8 XCDs
 // (workgroup i runs on XCD i % 8), and each XCD has its own L2.  So the
 // workgroup id is first remapped so that each XCD receives one contiguous
