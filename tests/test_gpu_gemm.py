@@ -128,6 +128,31 @@ def test_decode_shapes_full():
         assert torch.equal(y, yf)
 
 
+# Decode-shaped calls (M <= 32) pick one of three kernels by K: whole-row LDS
+# blocks (K % 512 == 0 while the block fits 64 KiB of LDS), K-chunked direct
+# loads (other K % 128 == 0)
+# and the generic split-K kernel.  Each is checked in full against the oracle
+# at ragged N and at the edges of its K range.
+DECODE_KINDS = [("mx_decode_kernel<", 512), ("mx_decode_kernel<", 6656), ("mx_decode_kernel<", 2560),
+                ("mx_decode_direct_kernel<", 384), ("mx_decode_direct_kernel<", 8192),
+                ("mx_decode_direct_kernel<", 16384),
+                ("mx_decode_generic_kernel<", 96), ("mx_decode_generic_kernel<", 4128)]
+
+
+@pytest.mark.parametrize("m", [1, 8, 17, 32])
+@pytest.mark.parametrize("kernel,k", DECODE_KINDS)
+def test_decode_kernel_kinds(kernel, k, m):
+    n = 300 if k <= 8192 else 70
+    say(f"decode kind {kernel} m={m} k={k} n={n}")
+    assert mxl.mx_gemm_plan("mxfp4", "mxfp4", m, n, k).split(" ", 1)[1].startswith(kernel)
+    a_bits = W.activations_entry_outliers(m, k, seed=3 + m)
+    w_bits = W.normal_bf16(n, k, 0.02, 4)
+    y_ref, s, _, _ = oracle_full(a_bits, w_bits, "mxfp4")
+    for out_f32 in (False, True):
+        y, _, _, _ = run_mx(a_bits, w_bits, "mxfp4", out_f32=out_f32)
+        check_gemm(y_host(y), y_ref, s, not out_f32, f"{kernel} {m}x{k}x{n} f32={out_f32}")
+
+
 def sampled_check(cfg, fmt, fused=True, count=4096):
     a_bits, w_bits = cfg.activations(), cfg.weights()
     say(f"sampled {cfg.name}: generated inputs")
