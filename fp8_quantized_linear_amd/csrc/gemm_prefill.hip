@@ -5,15 +5,16 @@
 // Operation: the W4A4 FP4 GEMM that serves the MXFP4 checkpoints
 // (Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Serving"), for prefill-sized M.
 //
-// Design (one 256x256 output tile per workgroup of 4 waves, each wave a
-// 128x128 sub-tile of 4x4 matrix-core fragments held in 256 AGPRs):
-//  * K advances in stages of 128 elements.  A stage's codes (16 KiB of A, 16
-//    KiB of W) live in one slot of a 3-slot LDS ring.  The E8M0 scales travel
-//    separately, in windows of 8 stages (32 bytes per row per operand, 16 KiB
-//    per window) held in a 3-window LDS ring: fetching 4 scale bytes per row
-//    per stage would cost one 64-row gather per 256 bytes, which measured as
-//    the dominant cost of the loop; a window fetch moves 32 contiguous bytes
-//    per row.
+// Design (one 256 x BN output tile per workgroup of 4 waves, 2 x 2 waves, each
+// wave a 128 x BN/2 sub-tile of 32x32 matrix-core fragments held in AGPRs;
+// BN = 256 for the bulk of the tiles, 128 for the tail, see below):
+//  * K advances in stages of 128 elements.  A stage's codes (16 KiB of A,
+//    BN * 64 bytes of W) live in one slot of a 3-slot LDS ring.  The E8M0
+//    scales travel separately, in windows of 8 stages (32 bytes per row per
+//    operand) held in a 3-window LDS ring: fetching 4 scale bytes per row per
+//    stage would cost one 64-row gather per 256 bytes, which measured as the
+//    dominant cost of the loop; a window fetch moves 32 contiguous bytes per
+//    row.
 //  * Everything is copied global -> LDS by the buffer-load-to-LDS path (each
 //    instruction writes 64 lanes x its width contiguously at the address in
 //    M0), so no registers are spent on staging.  The swizzled code layout is
@@ -22,70 +23,133 @@
 //    range check); copies past the last stage use a zero-sized buffer and
 //    fill a free slot with zeros, which keeps the loop free of branches and
 //    the outstanding-copy count the same every stage.
-//  * Each wave issues 10 copies per stage: 2 scale pieces (8 rows x 32 B each)
-//    of the window after next, then 8 code copies (16 rows x 64 B each) of
-//    the stage three ahead.  A wave waits for its own copies with an explicit
-//    vmcnt (the copies come from inline assembly the compiler does not
-//    track), then a workgroup barrier publishes them.
-//  * The fragments of stage s+1 (16 code reads, 8 scale reads per lane) are
-//    read from LDS while the 32 matrix-core instructions of stage s run, into
-//    a second register set, so no LDS latency is exposed; the loop is
-//    unrolled by two to alternate the sets without copies.  Reads, copies and
-//    matrix-core instructions are pinned in place with scheduling barriers.
+//  * Each wave issues the same number of copies every stage: one A and one W
+//    scale piece (8 rows x 32 B each) of the window after next, then 4 A and
+//    BN/64 W code copies (16 rows x 64 B each) of the stage three ahead.  With
+//    BN = 128 a window has only 16 W pieces, so two waves copy a piece from a
+//    zero-sized buffer into a dummy area to keep the count uniform.  A wave
+//    waits for its own copies with an explicit vmcnt (the copies come from
+//    inline assembly the compiler does not track), then a workgroup barrier
+//    publishes them.
+//  * The fragments of stage s+1 are read from LDS while the matrix-core
+//    instructions of stage s run, into a second register set, so no LDS
+//    latency is exposed; the loop is unrolled by two to alternate the sets
+//    without copies.  Reads, copies and matrix-core instructions are spread
+//    evenly and pinned in place with scheduling barriers.
 //  * W is the matrix core's first operand, A the second, so each lane's
 //    accumulator holds 4 consecutive output columns; the epilogue stages each
-//    32-row band of a wave's tile through LDS and writes whole 256-byte row
-//    segments to Y.
+//    32-row band of a wave's tile through LDS and writes whole row segments
+//    to Y.
 //  * Matrix-core layout (32x32x64, E2M1): lane l = r + 32 g holds row r of a
 //    fragment and K elements [32 g, 32 g + 32) of the 64-wide step; lane
 //    group g supplies the E8M0 scale of K block g.  Accumulator register i of
 //    lane l is C[(i/4)*8 + g*4 + i%4][r] with C = W_frag x A_frag^T.
-//  * Tile order: XCD-aware grouped order (tile_coords in mx_device.h).
+//  * Tile order: workgroup ids are first mapped XCD-aware (dispatch is
+//    round-robin over the 8 XCDs, each with its own L2: each XCD gets a
+//    contiguous range of the order), then walk groups of 4 tile columns down
+//    M (N fastest inside a group).
+//  * Tail: with C compute units, T tiles take ceil(T / C) rounds.  When the
+//    last round is at most half full (0 < T mod C <= C/2), the T mod C tiles
+//    at the end of the order are computed by a second launch as 256 x 128
+//    halves, so that round costs about half a tile instead of a full one.
+//    Every output element accumulates the same stages in the same order in
+//    both kernels, so the split does not change any result.
 // Requires K % 128 == 0 (whole stages); other shapes use the general tile
 // kernel.
 #include "mx_device.h"
 
 namespace mxl {
 
-constexpr int PF_BM = 256, PF_BN = 256, PF_BK = 128;
+constexpr int PF_BM = 256, PF_BK = 128;
 constexpr int PF_ROWB = PF_BK / 2;                 // E2M1 bytes of a row per stage
-constexpr int PF_TILE = PF_BM * PF_ROWB;           // 16 KiB per operand per stage
+constexpr int PF_TILE = PF_BM * PF_ROWB;           // 16 KiB of A codes per stage
 constexpr int PF_NS = 3;                           // code slots; copies run PF_NS stages ahead
-constexpr int PF_SLOT = 2 * PF_TILE;               // A codes, then W codes
 constexpr int PF_SWS = 8;                          // stages per scale window
 constexpr int PF_SWB = PF_SWS * 4;                 // scale bytes per row per window
-constexpr int PF_WIN = 2 * PF_BM * PF_SWB;         // A scales [256][32 B], then W scales
 constexpr int PF_NWIN = 3;
-constexpr int PF_SC0 = PF_NS * PF_SLOT;            // the scale windows follow the code ring
-constexpr int PF_LDS = PF_SC0 + PF_NWIN * PF_WIN;  // 147456 bytes
-constexpr int PF_COPIES = 10;                      // copies per wave per stage
+constexpr int PF_GROUP_N = 4;                      // tile columns per group of the tile order
+
+// LDS layout for tile width BN: code ring [NS][A 16 KiB | W BN*64], scale
+// windows [NWIN][A 256 x 32 B | W BN x 32 B], then a 512-byte dummy area
+template <int BN>
+struct PfLayout {
+    static constexpr int W_TILE = BN * PF_ROWB;
+    static constexpr int SLOT = PF_TILE + W_TILE;
+    static constexpr int WIN = (PF_BM + BN) * PF_SWB;
+    static constexpr int SC0 = PF_NS * SLOT;
+    static constexpr int DUMMY = SC0 + PF_NWIN * WIN;
+    static constexpr int LDS = DUMMY + 512;
+    static constexpr int WFR = BN / 64;            // W fragments per wave (a wave covers BN/2 W rows)
+    static constexpr int COPIES = 2 + 4 + WFR;     // copies per wave per stage
+    static constexpr int READS = 8 + 2 * WFR + 4 + WFR;  // LDS reads per lane per stage
+    static constexpr int MFMAS = 2 * 4 * WFR;      // matrix-core instructions per wave per stage
+    static constexpr int READ_SPAN = MFMAS * 3 / 4;  // reads go out during the first 3/4 of a stage,
+                                                     // leaving the rest to cover their latency
+};
 
 struct PrefillArgs {
     const uint8_t* a_q; const uint8_t* a_s;
     const uint8_t* w_q; const uint8_t* w_s;
     void* y;
     int M, N, K;
+    int tile_base;   // first tile (in the tile order) of this launch
+    int count;       // workgroups of this launch
 };
 
 // 16-byte chunk swizzle of the 64-byte LDS rows: the 32 lanes reading the
 // same logical chunk of 32 consecutive rows touch distinct banks.
 __device__ __forceinline__ int pf_swz(int row) { return (row >> 1) & 3; }
 
+// This workgroup's index in [0, count): workgroup b runs on XCD b % 8, and
+// each XCD receives one contiguous range.
+__device__ __forceinline__ int pf_xcd_order(int count)
+{
+    const int id = blockIdx.x;
+    const int xcd = id % NUM_XCD, j = id / NUM_XCD;
+    const int q = count / NUM_XCD, r = count % NUM_XCD;
+    return xcd * q + (xcd < r ? xcd : r) + j;
+}
+
+// Tile t of the grouped order over the 256 x 256 tile grid.
+__device__ __forceinline__ void pf_tile(int t, int M, int N, int& tm, int& tn)
+{
+    const int tiles_m = (M + PF_BM - 1) / PF_BM, tiles_n = (N + 255) / 256;
+    const int group_size = PF_GROUP_N * tiles_m;
+    const int first_n = (t / group_size) * PF_GROUP_N;
+    const int gn = (tiles_n - first_n) < PF_GROUP_N ? (tiles_n - first_n) : PF_GROUP_N;
+    const int in = t % group_size;
+    tm = in / gn;
+    tn = first_n + in % gn;
+}
+
 // one stage's operands in registers: code fragments per 64-wide step kk, and
 // the raw scale dwords (4 blocks of the stage) of this lane's fragment rows
+template <int WFR>
 struct PfFrags {
-    int4_t a[2][4], w[2][4];
-    int sa[4], sw[4];
+    int4_t a[2][4], w[2][WFR];
+    int sa[4], sw[WFR];
 };
 
-template <bool OUT_F32>
+template <bool OUT_F32, int BN>
 __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
 {
+    using L = PfLayout<BN>;
+    constexpr int WFR = L::WFR;
     extern __shared__ __align__(16) uint8_t smem[];
 
-    int tm, tn;
-    tile_coords<PF_BM, PF_BN, 4>(p.M, p.N, tm, tn);
-    const int m0 = tm * PF_BM, n0 = tn * PF_BN;
+    int m0, n0;
+    {
+        const int t = pf_xcd_order(p.count);
+        int tm, tn;
+        if (BN == 256) {
+            pf_tile(p.tile_base + t, p.M, p.N, tm, tn);
+            n0 = tn * 256;
+        } else {   // halves of the tail tiles; both halves of a tile on one XCD
+            pf_tile(p.tile_base + t / 2, p.M, p.N, tm, tn);
+            n0 = tn * 256 + (t % 2) * 128;
+        }
+        m0 = tm * PF_BM;
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: feeds M0
     const int wm = wave >> 1, wn = wave & 1;
@@ -99,90 +163,106 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     const int4_t rsrc_ws = make_rsrc(p.w_s, (uint32_t)p.N * KB);
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
-    // Code copies: wave w copies segments 4w .. 4w+3 (16 rows x 64 B = 1 KiB
-    // of LDS each) of each operand.  LDS position L of a segment is row
-    // 16*seg + L/4, physical chunk L%4, which holds logical chunk
-    // (L%4) ^ swz(row).
-    int a_voff[4], w_voff[4];
+    // Code copies: wave w copies A segments 4w .. 4w+3 and W segments
+    // WFR w .. WFR w + WFR - 1 (16 rows x 64 B = 1 KiB of LDS each).  LDS
+    // position L of a segment is row 16*seg + L/4, physical chunk L%4, which
+    // holds logical chunk (L%4) ^ swz(row).
+    int a_voff[4], w_voff[WFR];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int row = 16 * (4 * wave + s) + lane / 4;
-        const int c = (lane & 3) ^ pf_swz(row);
-        a_voff[s] = (m0 + row) * row_bytes + c * 16;
-        w_voff[s] = (n0 + row) * row_bytes + c * 16;
+        a_voff[s] = (m0 + row) * row_bytes + ((lane & 3) ^ pf_swz(row)) * 16;
     }
-    // Scale pieces: piece j (0..7) of a window is copy t = 4 j + wave of each
-    // operand, rows 8t .. 8t+7 of the tile, 32 bytes each ([row][32 B] in LDS).
-    // The window offset is part of the per-lane offset so that the buffer
-    // range check covers it (a partial last window may run past a row).
+#pragma unroll
+    for (int s = 0; s < WFR; ++s) {
+        const int row = 16 * (WFR * wave + s) + lane / 4;
+        w_voff[s] = (n0 + row) * row_bytes + ((lane & 3) ^ pf_swz(row)) * 16;
+    }
+    // Scale pieces: piece j (0..7) of a window is, for A, copy 4 j + wave
+    // (rows 8t .. 8t+7, [row][32 B] in LDS); for W it is copy WFR j + wave of
+    // BN/8, taken by the waves below WFR (the others copy a dummy).  The
+    // window offset is part of the per-lane offset so that the buffer range
+    // check covers it (a partial last window may run past a row).
     const int srow = lane >> 3, sdw = lane & 7;
-    auto sc_voff = [&](int base, int j, int win) {
-        return (base + 8 * (4 * j + wave) + srow) * KB + win * PF_SWB + sdw * 4;
-    };
+    const bool w_piece_real = wave < WFR;
 
-    // Copy c (0..9) of virtual stage y: c = 0, 1 are the A and W pieces
-    // (y + 4) % 8 of scale window (y + 4) / 8 + 1; c = 2..9 are the code
-    // copies of stage y + PF_NS.  Stage y + PF_NS goes to the slot of stage y,
-    // whose fragments were read during stage y - 1.  A window's pieces are
-    // issued during the 8 stages that end four stages before its first stage
-    // is read, into the buffer of the window three back.
+    // Copy c (0 .. COPIES-1) of virtual stage y: c = 0, 1 are the A and W
+    // pieces (y + 4) % 8 of scale window (y + 4) / 8 + 1; the rest are the code
+    // copies of stage y + PF_NS (A first, then W).  Stage y + PF_NS goes to the
+    // slot of stage y, whose fragments were read during stage y - 1.  A
+    // window's pieces are issued during the 8 stages that end four stages
+    // before its first stage is read, into the buffer of the window three back.
     auto copy = [&](int y, int c) {
         if (c < 2) {
             const int win = ((y + 4) >> 3) + 1, j = (y + 4) & 7;
             const int live = __builtin_amdgcn_readfirstlane(win * PF_SWS < nk ? 1 : 0);
-            int4_t r = c == 0 ? rsrc_as : rsrc_ws;
-            r[2] = live ? r[2] : 0;
-            const uint32_t dst = lds0 + PF_SC0 + (uint32_t)((win % PF_NWIN) * PF_WIN) + (4 * j + wave) * 256 +
-                                 c * PF_BM * PF_SWB;
-            dma_b32(dst, sc_voff(c == 0 ? m0 : n0, j, win), r, 0);
+            const uint32_t wbuf = lds0 + L::SC0 + (uint32_t)((win % PF_NWIN) * L::WIN);
+            if (c == 0) {
+                int4_t r = rsrc_as;
+                r[2] = live ? r[2] : 0;
+                const int t = 4 * j + wave;
+                dma_b32(wbuf + t * 256, (m0 + 8 * t + srow) * KB + win * PF_SWB + sdw * 4, r, 0);
+            } else {
+                int4_t r = rsrc_ws;
+                r[2] = (live && w_piece_real) ? r[2] : 0;
+                const int t = WFR * j + (w_piece_real ? wave : 0);
+                const uint32_t dst = w_piece_real ? wbuf + PF_BM * PF_SWB + t * 256 : lds0 + L::DUMMY + (wave & 1) * 256;
+                dma_b32(dst, (n0 + 8 * t + srow) * KB + win * PF_SWB + sdw * 4, r, 0);
+            }
         } else {
             const int ks = y + PF_NS;
             const int live = __builtin_amdgcn_readfirstlane(ks < nk ? 1 : 0);
-            const int s = (c - 2) & 3;
-            int4_t r = c < 6 ? rsrc_a : rsrc_w;
-            r[2] = live ? r[2] : 0;
-            const uint32_t dst = lds0 + (uint32_t)((ks % PF_NS) * PF_SLOT) + (c < 6 ? 0 : PF_TILE) + (4 * wave + s) * 1024;
-            dma_b128(dst, c < 6 ? a_voff[s] : w_voff[s], r, ks * PF_ROWB);
+            const uint32_t slot = lds0 + (uint32_t)((ks % PF_NS) * L::SLOT);
+            if (c < 6) {
+                const int s = c - 2;
+                int4_t r = rsrc_a;
+                r[2] = live ? r[2] : 0;
+                dma_b128(slot + (4 * wave + s) * 1024, a_voff[s], r, ks * PF_ROWB);
+            } else {
+                const int s = c - 6;
+                int4_t r = rsrc_w;
+                r[2] = live ? r[2] : 0;
+                dma_b128(slot + PF_TILE + (WFR * wave + s) * 1024, w_voff[s], r, ks * PF_ROWB);
+            }
         }
     };
 
-    // LDS read q (0..23) of stage s: 16 code fragments, then 8 scale dwords
-    auto read_piece = [&](int s, int q, PfFrags& f) {
-        if (q < 16) {
-            const uint8_t* slot = smem + (s % PF_NS) * PF_SLOT;
-            const int kk = q >> 3, x = q & 7;
-            if (x < 4) {
-                const int row = wm * 128 + x * 32 + r32;
-                f.a[kk][x] = *reinterpret_cast<const int4_t*>(slot + row * PF_ROWB + (((2 * kk + g) ^ pf_swz(row)) * 16));
-            } else {
-                const int row = wn * 128 + (x - 4) * 32 + r32;
-                f.w[kk][x - 4] =
-                    *reinterpret_cast<const int4_t*>(slot + PF_TILE + row * PF_ROWB + (((2 * kk + g) ^ pf_swz(row)) * 16));
-            }
+    // LDS read q (0 .. READS-1) of stage s: code fragments (A of both steps,
+    // then W of both steps), then the scale dwords (A, then W)
+    auto read_piece = [&](int s, int q, PfFrags<WFR>& f) {
+        const uint8_t* slot = smem + (s % PF_NS) * L::SLOT;
+        const uint8_t* win = smem + L::SC0 + ((s / PF_SWS) % PF_NWIN) * L::WIN + (s % PF_SWS) * 4;
+        if (q < 8) {
+            const int kk = q >> 2, x = q & 3;
+            const int row = wm * 128 + x * 32 + r32;
+            f.a[kk][x] = *reinterpret_cast<const int4_t*>(slot + row * PF_ROWB + (((2 * kk + g) ^ pf_swz(row)) * 16));
+        } else if (q < 8 + 2 * WFR) {
+            const int kk = (q - 8) / WFR, x = (q - 8) % WFR;
+            const int row = wn * (BN / 2) + x * 32 + r32;
+            f.w[kk][x] =
+                *reinterpret_cast<const int4_t*>(slot + PF_TILE + row * PF_ROWB + (((2 * kk + g) ^ pf_swz(row)) * 16));
+        } else if (q < 12 + 2 * WFR) {
+            const int x = q - 8 - 2 * WFR;
+            const int row = wm * 128 + x * 32 + r32;
+            f.sa[x] = (int)*reinterpret_cast<const uint32_t*>(win + row * PF_SWB);
         } else {
-            const uint8_t* win = smem + PF_SC0 + ((s / PF_SWS) % PF_NWIN) * PF_WIN + (s % PF_SWS) * 4;
-            const int x = q - 16;
-            if (x < 4) {
-                const int row = wm * 128 + x * 32 + r32;
-                f.sa[x] = (int)*reinterpret_cast<const uint32_t*>(win + row * PF_SWB);
-            } else {
-                const int row = wn * 128 + (x - 4) * 32 + r32;
-                f.sw[x - 4] = (int)*reinterpret_cast<const uint32_t*>(win + PF_BM * PF_SWB + row * PF_SWB);
-            }
+            const int x = q - 12 - 2 * WFR;
+            const int row = wn * (BN / 2) + x * 32 + r32;
+            f.sw[x] = (int)*reinterpret_cast<const uint32_t*>(win + PF_BM * PF_SWB + row * PF_SWB);
         }
     };
 
-    float16_t acc[4][4];
+    float16_t acc[4][WFR];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < WFR; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // matrix-core instruction q (0..31) of a stage: step kk = q / 16, fragment (i, j)
-    auto mfma = [&](int q, const PfFrags& f, const int* sa, const int* sw) {
-        const int kk = q >> 4, i = (q >> 2) & 3, j = q & 3;
+    // matrix-core instruction q of a stage: step kk = q / (4 WFR), fragment (i, j)
+    auto mfma = [&](int q, const PfFrags<WFR>& f, const int* sa, const int* sw) {
+        const int kk = q / (4 * WFR), i = (q / WFR) % 4, j = q % WFR;
         const int8_t_ b8 = int8_t_{f.w[kk][j][0], f.w[kk][j][1], f.w[kk][j][2], f.w[kk][j][3], 0, 0, 0, 0};
         const int8_t_ a8 = int8_t_{f.a[kk][i][0], f.a[kk][i][1], f.a[kk][i][2], f.a[kk][i][3], 0, 0, 0, 0};
         if (kk == 0)
@@ -192,32 +272,34 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     };
 
     // Stage s: computed from `cur`; stage s + 1 is read into `nxt`; virtual
-    // stage s issues its copies.
-    auto stage = [&](int s, const PfFrags& cur, PfFrags& nxt) {
-        // The copies of stage s + 1 were issued two stages ago; only the 10 of
-        // the previous stage may still be in flight.
-        wait_vmcnt<PF_COPIES>();
+    // stage s issues its copies.  Reads and copies are spread evenly over the
+    // matrix-core instructions.
+    auto stage = [&](int s, const PfFrags<WFR>& cur, PfFrags<WFR>& nxt) {
+        // The copies of stage s + 1 were issued two stages ago; only the
+        // previous stage's may still be in flight.
+        wait_vmcnt<L::COPIES>();
         lds_barrier();
         // byte 2 kk + g of a scale dword is this lane's block; after the shift
         // it sits at byte 2 kk, which the instruction's op_sel picks
-        int sa[4], sw[4];
+        int sa[4], sw[WFR];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa[i] = (int)((uint32_t)cur.sa[i] >> (8 * g));
-            sw[i] = (int)((uint32_t)cur.sw[i] >> (8 * g));
-        }
+        for (int i = 0; i < 4; ++i) sa[i] = (int)((uint32_t)cur.sa[i] >> (8 * g));
+#pragma unroll
+        for (int j = 0; j < WFR; ++j) sw[j] = (int)((uint32_t)cur.sw[j] >> (8 * g));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
+        for (int q = 0; q < L::MFMAS; ++q) {
             mfma(q, cur, sa, sw);
-            if (q < 24) {
+#pragma unroll
+            for (int x = q * L::READS / L::READ_SPAN; x < (q + 1) * L::READS / L::READ_SPAN && x < L::READS; ++x) {
                 __builtin_amdgcn_sched_barrier(0);
-                read_piece(s + 1, q, nxt);
+                read_piece(s + 1, x, nxt);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if ((q % 3) == 1 && q / 3 < PF_COPIES) {
+#pragma unroll
+            for (int c = q * L::COPIES / L::MFMAS; c < (q + 1) * L::COPIES / L::MFMAS; ++c) {
                 __builtin_amdgcn_sched_barrier(0);
-                copy(s, q / 3);
+                copy(s, c);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -228,20 +310,25 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     // pieces 0..3 and the codes of stages 0..2).
 #pragma unroll
     for (int j = 0; j < PF_SWS; ++j) {
-        const uint32_t dst = lds0 + PF_SC0 + (4 * j + wave) * 256;
-        dma_b32(dst, sc_voff(m0, j, 0), rsrc_as, 0);
-        dma_b32(dst + PF_BM * PF_SWB, sc_voff(n0, j, 0), rsrc_ws, 0);
+        const uint32_t wbuf = lds0 + L::SC0;
+        const int t = 4 * j + wave;
+        dma_b32(wbuf + t * 256, (m0 + 8 * t + srow) * KB + sdw * 4, rsrc_as, 0);
+        int4_t r = rsrc_ws;
+        r[2] = w_piece_real ? r[2] : 0;
+        const int tw = WFR * j + (w_piece_real ? wave : 0);
+        const uint32_t dst = w_piece_real ? wbuf + PF_BM * PF_SWB + tw * 256 : lds0 + L::DUMMY + (wave & 1) * 256;
+        dma_b32(dst, (n0 + 8 * tw + srow) * KB + sdw * 4, r, 0);
     }
     copy(-4, 0);
     copy(-4, 1);
     for (int y = -3; y < 0; ++y)
 #pragma unroll
-        for (int c = 0; c < PF_COPIES; ++c) copy(y, c);
-    wait_vmcnt<2 * PF_COPIES>();  // window 0 and stage 0 have landed
+        for (int c = 0; c < L::COPIES; ++c) copy(y, c);
+    wait_vmcnt<2 * L::COPIES>();  // window 0 and stage 0 have landed
     lds_barrier();
-    PfFrags X, Y;
+    PfFrags<WFR> X, Y;
 #pragma unroll
-    for (int q = 0; q < 24; ++q) read_piece(0, q, X);
+    for (int q = 0; q < L::READS; ++q) read_piece(0, q, X);
 
     int s = 0;
     for (; s + 1 < nk; s += 2) {
@@ -256,13 +343,14 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     // wave's private LDS region: write the band row-major, read it back as
     // whole row segments and store them with 16-byte stores.
     constexpr int ESZ = OUT_F32 ? 4 : 2;
-    constexpr int ROWB = 128 * ESZ + 16;                 // padded LDS row
+    constexpr int WCOLS = BN / 2;                        // output columns of a wave
+    constexpr int ROWB = WCOLS * ESZ + 16;               // padded LDS row
     uint8_t* region = smem + wave * (32 * ROWB);
     const bool vec_ok = (p.N % (16 / ESZ)) == 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < WFR; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int col = j * 32 + q * 8 + g * 4;
@@ -276,14 +364,14 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
                     *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
                 }
             }
-        constexpr int LPR = 128 * ESZ / 16;               // lanes per 16-byte-chunked row
+        constexpr int LPR = WCOLS * ESZ / 16;              // lanes per 16-byte-chunked row
         constexpr int RPI = 64 / LPR;                      // rows per read instruction
 #pragma unroll
         for (int t = 0; t < 32 / RPI; ++t) {
             const int row = t * RPI + lane / LPR, c16 = lane % LPR;
             const uint4 v = *reinterpret_cast<const uint4*>(region + row * ROWB + c16 * 16);
             const int m = m0 + wm * 128 + i * 32 + row;
-            const int n = n0 + wn * 128 + c16 * (16 / ESZ);
+            const int n = n0 + wn * WCOLS + c16 * (16 / ESZ);
             if (m < p.M) {
                 uint8_t* yrow = reinterpret_cast<uint8_t*>(p.y) + ((size_t)m * p.N) * ESZ;
                 if (vec_ok && n + 16 / ESZ <= p.N) {
@@ -305,19 +393,55 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     }
 }
 
-template <bool OUT_F32>
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
+template <bool OUT_F32, int BN>
+hipError_t launch_prefill_part(PrefillArgs a, int tile_base, int count, hipStream_t stream)
 {
-    auto kern = mx_gemm_prefill_kernel<OUT_F32>;
+    auto kern = mx_gemm_prefill_kernel<OUT_F32, BN>;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, PF_LDS);
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           PfLayout<BN>::LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int tiles = ((a.M + PF_BM - 1) / PF_BM) * ((a.N + PF_BN - 1) / PF_BN);
-    hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), PF_LDS, stream, a);
+    a.tile_base = tile_base;
+    a.count = count;
+    hipLaunchKernelGGL(kern, dim3(count), dim3(256), PfLayout<BN>::LDS, stream, a);
     return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+static int prefill_cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Tiles of the tail launch (0: none) for T tiles on C compute units.
+static int prefill_tail_tiles(int T, int C)
+{
+    const int rem = T % C;
+    return (rem > 0 && 2 * rem <= C) ? rem : 0;
+}
+
+template <bool OUT_F32>
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
+{
+    const int T = ((a.M + PF_BM - 1) / PF_BM) * ((a.N + 255) / 256);
+    const int tail = prefill_tail_tiles(T, prefill_cu_count());
+    if (T - tail > 0) {
+        const hipError_t e = launch_prefill_part<OUT_F32, 256>(a, 0, T - tail, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (tail > 0) return launch_prefill_part<OUT_F32, 128>(a, T - tail, 2 * tail, stream);
+    return hipSuccess;
 }
 
 } // namespace mxl
@@ -330,7 +454,7 @@ extern "C" int mxl_prefill_ok(int64_t m, int64_t n, int64_t k)
 {
     if (k % PF_BK != 0) return 0;
     const int64_t lim = ((int64_t)1 << 31) - (int64_t)PF_BM * (k / 2) - 1024;
-    return (m + PF_BM) * (k / 2) < lim && (n + PF_BN) * (k / 2) < lim ? 1 : 0;
+    return (m + PF_BM) * (k / 2) < lim && (n + 256) * (k / 2) < lim ? 1 : 0;
 }
 
 extern "C" hipError_t mxl_launch_mx_prefill(const void* aq, const void* as, const void* wq, const void* ws,
@@ -338,6 +462,6 @@ extern "C" hipError_t mxl_launch_mx_prefill(const void* aq, const void* as, cons
                                             hipStream_t stream)
 {
     PrefillArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
-                  static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k};
+                  static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, 0, 0};
     return out_f32 ? launch_prefill<true>(a, stream) : launch_prefill<false>(a, stream);
 }
