@@ -8,34 +8,39 @@
 // Design (one 256 x BN output tile per workgroup of 4 waves, 2 x 2 waves, each
 // wave a 128 x BN/2 sub-tile of 32x32 matrix-core fragments held in AGPRs;
 // BN = 256 for the bulk of the tiles, 128 for the tail, see below):
-//  * K advances in stages of 128 elements.  A stage's codes (16 KiB of A,
-//    BN * 64 bytes of W) live in one slot of a 3-slot LDS ring.  The E8M0
-//    scales travel separately, in windows of 8 stages (32 bytes per row per
-//    operand) held in a 3-window LDS ring: fetching 4 scale bytes per row per
-//    stage would cost one 64-row gather per 256 bytes, which measured as the
-//    dominant cost of the loop; a window fetch moves 32 contiguous bytes per
-//    row.
+//  * K advances in pairs of 256 elements, each computed as two sub-stages of
+//    128.  A pair's codes (32 KiB of A, BN * 128 bytes of W) live in one of
+//    two LDS slots, 128 bytes per row, so that every copy moves 8 rows x 128
+//    contiguous bytes (whole cache lines).  The E8M0 scales travel
+//    separately, in windows of 4 pairs (32 bytes per row per operand) held in
+//    two LDS buffers: fetching the 8 scale bytes of a row per pair would cost
+//    one 64-row gather per 512 bytes, which measured as the dominant cost of
+//    the loop; a window moves 32 contiguous bytes per row.  For BN = 256 the
+//    slots and windows fill the 160 KiB of LDS exactly.
 //  * Everything is copied global -> LDS by the buffer-load-to-LDS path (each
 //    instruction writes 64 lanes x its width contiguously at the address in
 //    M0), so no registers are spent on staging.  The swizzled code layout is
 //    obtained by choosing, per lane, which global 16-byte chunk lands at that
-//    lane's LDS position.  Rows past the end of A or W read as zero (buffer
-//    range check); copies past the last stage use a zero-sized buffer and
-//    fill a free slot with zeros, which keeps the loop free of branches and
-//    the outstanding-copy count the same every stage.
-//  * Each wave issues the same number of copies every stage: one A and one W
-//    scale piece (8 rows x 32 B each) of the window after next, then 4 A and
-//    BN/64 W code copies (16 rows x 64 B each) of the stage three ahead.  With
-//    BN = 128 a window has only 16 W pieces, so two waves copy a piece from a
-//    zero-sized buffer into a dummy area to keep the count uniform.  A wave
-//    waits for its own copies with an explicit vmcnt (the copies come from
-//    inline assembly the compiler does not track), then a workgroup barrier
-//    publishes them.
-//  * The fragments of stage s+1 are read from LDS while the matrix-core
-//    instructions of stage s run, into a second register set, so no LDS
-//    latency is exposed; the loop is unrolled by two to alternate the sets
-//    without copies.  Reads, copies and matrix-core instructions are spread
-//    evenly and pinned in place with scheduling barriers.
+//    lane's LDS position.  All offsets are per-lane, so the buffer range
+//    check turns anything past the end of A or W into zeros (rows past M or
+//    N, the half pair when K % 256 == 128); copies past the last pair use a
+//    zero-sized buffer and fill a free slot with zeros, which keeps the loop
+//    free of branches and the outstanding-copy count the same every pair.
+//  * During the second sub-stage of pair p every wave issues the same number
+//    of copies: 2 A and 2 W scale copies (8 rows x 32 B each) of a window,
+//    then 8 A and BN/32 W code copies of pair p + 2 into the slot of pair p,
+//    whose fragments were all read by then.  With BN = 128 a window piece
+//    has only 4 W copies, so two waves copy from a zero-sized buffer into a
+//    dummy area to keep the count uniform.  The copies come from inline
+//    assembly the compiler does not track: at the start of each second
+//    sub-stage every wave waits for all of its copies (vmcnt(0); they were
+//    issued two sub-stages earlier) and a workgroup barrier publishes them.
+//    That is the loop's only barrier.
+//  * The fragments of sub-stage s+1 are read from LDS while the
+//    matrix-core instructions of sub-stage s run, into a second register set,
+//    so no LDS latency is exposed; the loop is unrolled by two to alternate
+//    the sets without copies.  Reads, copies and matrix-core instructions are
+//    spread evenly and pinned in place with scheduling barriers.
 //  * W is the matrix core's first operand, A the second, so each lane's
 //    accumulator holds 4 consecutive output columns; the epilogue stages each
 //    32-row band of a wave's tile through LDS and writes whole row segments
@@ -52,39 +57,43 @@
 //    last round is at most half full (0 < T mod C <= C/2), the T mod C tiles
 //    at the end of the order are computed by a second launch as 256 x 128
 //    halves, so that round costs about half a tile instead of a full one.
-//    Every output element accumulates the same stages in the same order in
-//    both kernels, so the split does not change any result.
-// Requires K % 128 == 0 (whole stages); other shapes use the general tile
-// kernel.
+//    Every output element accumulates the same sub-stages in the same order
+//    in both kernels, so the split does not change any result.
+// Requires K % 128 == 0; other shapes use the general tile kernel.
 #include "mx_device.h"
 
 namespace mxl {
 
-constexpr int PF_BM = 256, PF_BK = 128;
-constexpr int PF_ROWB = PF_BK / 2;                 // E2M1 bytes of a row per stage
-constexpr int PF_TILE = PF_BM * PF_ROWB;           // 16 KiB of A codes per stage
-constexpr int PF_NS = 3;                           // code slots; copies run PF_NS stages ahead
-constexpr int PF_SWS = 8;                          // stages per scale window
-constexpr int PF_SWB = PF_SWS * 4;                 // scale bytes per row per window
-constexpr int PF_NWIN = 3;
+constexpr int PF_BM = 256, PF_BK = 128;            // tile rows of A; K per sub-stage
+constexpr int PF_PK = 256;                         // K per pair
+constexpr int PF_PROWB = PF_PK / 2;                // 128 code bytes of a row per pair
+constexpr int PF_ATILE = PF_BM * PF_PROWB;         // 32 KiB of A codes per pair
+constexpr int PF_NSL = 2;                          // pair slots
+constexpr int PF_WPAIRS = 4;                       // pairs per scale window
+constexpr int PF_SWB = PF_WPAIRS * 8;              // 32 scale bytes per row per window
+constexpr int PF_NWIN = 2;                         // scale window buffers
 constexpr int PF_GROUP_N = 4;                      // tile columns per group of the tile order
 
-// LDS layout for tile width BN: code ring [NS][A 16 KiB | W BN*64], scale
-// windows [NWIN][A 256 x 32 B | W BN x 32 B], then a 512-byte dummy area
+// LDS layout for tile width BN: pair slots [2][A 32 KiB | W BN*128], scale
+// windows [2][A 256 x 32 B | W BN x 32 B], then (BN = 128) a 512-byte dummy area
 template <int BN>
 struct PfLayout {
-    static constexpr int W_TILE = BN * PF_ROWB;
-    static constexpr int SLOT = PF_TILE + W_TILE;
+    static constexpr int W_TILE = BN * PF_PROWB;
+    static constexpr int SLOT = PF_ATILE + W_TILE;
     static constexpr int WIN = (PF_BM + BN) * PF_SWB;
-    static constexpr int SC0 = PF_NS * SLOT;
+    static constexpr int SC0 = PF_NSL * SLOT;
     static constexpr int DUMMY = SC0 + PF_NWIN * WIN;
-    static constexpr int LDS = DUMMY + 512;
+    static constexpr int LDS = DUMMY + (BN == 256 ? 0 : 512);   // 163840 bytes for BN = 256
     static constexpr int WFR = BN / 64;            // W fragments per wave (a wave covers BN/2 W rows)
-    static constexpr int COPIES = 2 + 4 + WFR;     // copies per wave per stage
-    static constexpr int READS = 8 + 2 * WFR + 4 + WFR;  // LDS reads per lane per stage
-    static constexpr int MFMAS = 2 * 4 * WFR;      // matrix-core instructions per wave per stage
-    static constexpr int READ_SPAN = MFMAS * 3 / 4;  // reads go out during the first 3/4 of a stage,
-                                                     // leaving the rest to cover their latency
+    static constexpr int ACOP = PF_ATILE / 1024 / 4;        // 8 A code copies per wave per pair
+    static constexpr int WCOP = BN * PF_PROWB / 1024 / 4;   // BN/32 W code copies per wave per pair
+    static constexpr int SCOP = 4;                 // scale copies per wave per pair (2 A, 2 W)
+    static constexpr int COPIES = SCOP + ACOP + WCOP;
+    static constexpr int READS = 8 + 2 * WFR + 4 + WFR;     // LDS reads per lane per sub-stage
+    static constexpr int MFMAS = 8 * WFR;          // matrix-core instructions per wave per sub-stage
+    static constexpr int READ_SPAN = MFMAS * 3 / 4;  // reads go out during the first 3/4 of a
+                                                     // sub-stage, leaving the rest to cover them
+    static_assert(LDS <= 163840, "LDS");
 };
 
 struct PrefillArgs {
@@ -96,9 +105,9 @@ struct PrefillArgs {
     int count;       // workgroups of this launch
 };
 
-// 16-byte chunk swizzle of the 64-byte LDS rows: the 32 lanes reading the
-// same logical chunk of 32 consecutive rows touch distinct banks.
-__device__ __forceinline__ int pf_swz(int row) { return (row >> 1) & 3; }
+// 16-byte chunk swizzle of the 128-byte LDS rows: the lanes reading the same
+// logical chunk of 16 consecutive rows touch distinct banks.
+__device__ __forceinline__ int pf_swz(int row) { return (row >> 1) & 7; }
 
 // This workgroup's index in [0, count): workgroup b runs on XCD b % 8, and
 // each XCD receives one contiguous range.
@@ -122,8 +131,8 @@ __device__ __forceinline__ void pf_tile(int t, int M, int N, int& tm, int& tn)
     tn = first_n + in % gn;
 }
 
-// one stage's operands in registers: code fragments per 64-wide step kk, and
-// the raw scale dwords (4 blocks of the stage) of this lane's fragment rows
+// one sub-stage's operands in registers: code fragments per 64-wide step kk,
+// and the raw scale dwords (4 blocks of the sub-stage) of this lane's rows
 template <int WFR>
 struct PfFrags {
     int4_t a[2][4], w[2][WFR];
@@ -155,7 +164,8 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     const int wm = wave >> 1, wn = wave & 1;
     const int r32 = lane & 31, g = lane >> 5;
     const int K = p.K, KB = K / 32, row_bytes = K / 2;
-    const int nk = K / PF_BK;
+    const int nk = K / PF_BK;          // sub-stages
+    const int np = (nk + 1) / 2;       // pairs (the last is half when K % 256 == 128)
 
     const int4_t rsrc_a = make_rsrc(p.a_q, (uint32_t)p.M * row_bytes);
     const int4_t rsrc_w = make_rsrc(p.w_q, (uint32_t)p.N * row_bytes);
@@ -163,84 +173,85 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     const int4_t rsrc_ws = make_rsrc(p.w_s, (uint32_t)p.N * KB);
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
-    // Code copies: wave w copies A segments 4w .. 4w+3 and W segments
-    // WFR w .. WFR w + WFR - 1 (16 rows x 64 B = 1 KiB of LDS each).  LDS
-    // position L of a segment is row 16*seg + L/4, physical chunk L%4, which
-    // holds logical chunk (L%4) ^ swz(row).
-    int a_voff[4], w_voff[WFR];
+    // Code copies, 8 rows x 128 B = 1 KiB of LDS each: wave w copies A rows
+    // [64 w, 64 w + 64) and W rows [8 WCOP w, 8 WCOP (w + 1)).  LDS position L
+    // of a copy is row 8*copy + L/8, physical chunk L%8, which holds logical
+    // chunk (L%8) ^ swz(row).
+    int a_voff[L::ACOP], w_voff[L::WCOP];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int row = 16 * (4 * wave + s) + lane / 4;
-        a_voff[s] = (m0 + row) * row_bytes + ((lane & 3) ^ pf_swz(row)) * 16;
+    for (int s = 0; s < L::ACOP; ++s) {
+        const int row = 8 * (L::ACOP * wave + s) + lane / 8;
+        a_voff[s] = (m0 + row) * row_bytes + ((lane & 7) ^ pf_swz(row)) * 16;
     }
 #pragma unroll
-    for (int s = 0; s < WFR; ++s) {
-        const int row = 16 * (WFR * wave + s) + lane / 4;
-        w_voff[s] = (n0 + row) * row_bytes + ((lane & 3) ^ pf_swz(row)) * 16;
+    for (int s = 0; s < L::WCOP; ++s) {
+        const int row = 8 * (L::WCOP * wave + s) + lane / 8;
+        w_voff[s] = (n0 + row) * row_bytes + ((lane & 7) ^ pf_swz(row)) * 16;
     }
-    // Scale pieces: piece j (0..7) of a window is, for A, copy 4 j + wave
-    // (rows 8t .. 8t+7, [row][32 B] in LDS); for W it is copy WFR j + wave of
-    // BN/8, taken by the waves below WFR (the others copy a dummy).  The
-    // window offset is part of the per-lane offset so that the buffer range
-    // check covers it (a partial last window may run past a row).
+    // Scale copies move 8 rows x 32 B ([row][32 B] in LDS); a window has 32
+    // for A and BN/8 for W, issued as 4 pieces.
     const int srow = lane >> 3, sdw = lane & 7;
-    const bool w_piece_real = wave < WFR;
+    constexpr int WSC = BN / 8;
 
-    // Copy c (0 .. COPIES-1) of virtual stage y: c = 0, 1 are the A and W
-    // pieces (y + 4) % 8 of scale window (y + 4) / 8 + 1; the rest are the code
-    // copies of stage y + PF_NS (A first, then W).  Stage y + PF_NS goes to the
-    // slot of stage y, whose fragments were read during stage y - 1.  A
-    // window's pieces are issued during the 8 stages that end four stages
-    // before its first stage is read, into the buffer of the window three back.
+    // Copy c (0 .. COPIES-1) issued in pair y: c < 4 are piece (y + 5) % 4 of
+    // scale window (y + 5) / 4 (A copies, then W copies); the rest are the
+    // code copies of pair y + 2 (A, then W).  Window w is issued during pairs
+    // 4w-5 .. 4w-2, after every read of window w-2 (same buffer), and has
+    // landed by the barrier that precedes its first read in pair 4w-1.
     auto copy = [&](int y, int c) {
-        if (c < 2) {
-            const int win = ((y + 4) >> 3) + 1, j = (y + 4) & 7;
-            const int live = __builtin_amdgcn_readfirstlane(win * PF_SWS < nk ? 1 : 0);
+        if (c < 4) {
+            const int win = (y + 5) >> 2, j = (y + 5) & 3;
+            const int live = __builtin_amdgcn_readfirstlane(win * PF_WPAIRS < np ? 1 : 0);
             const uint32_t wbuf = lds0 + L::SC0 + (uint32_t)((win % PF_NWIN) * L::WIN);
-            if (c == 0) {
+            if (c < 2) {
                 int4_t r = rsrc_as;
                 r[2] = live ? r[2] : 0;
-                const int t = 4 * j + wave;
+                const int t = 8 * j + 2 * wave + c;
                 dma_b32(wbuf + t * 256, (m0 + 8 * t + srow) * KB + win * PF_SWB + sdw * 4, r, 0);
             } else {
+                const int slot_in_piece = 2 * wave + (c - 2);
+                const bool real = slot_in_piece < WSC / 4;
+                const int t = (WSC / 4) * j + (real ? slot_in_piece : 0);
                 int4_t r = rsrc_ws;
-                r[2] = (live && w_piece_real) ? r[2] : 0;
-                const int t = WFR * j + (w_piece_real ? wave : 0);
-                const uint32_t dst = w_piece_real ? wbuf + PF_BM * PF_SWB + t * 256 : lds0 + L::DUMMY + (wave & 1) * 256;
+                r[2] = (live && real) ? r[2] : 0;
+                const uint32_t dst = real ? wbuf + PF_BM * PF_SWB + t * 256 : lds0 + L::DUMMY + (wave & 1) * 256;
                 dma_b32(dst, (n0 + 8 * t + srow) * KB + win * PF_SWB + sdw * 4, r, 0);
             }
         } else {
-            const int ks = y + PF_NS;
-            const int live = __builtin_amdgcn_readfirstlane(ks < nk ? 1 : 0);
-            const uint32_t slot = lds0 + (uint32_t)((ks % PF_NS) * L::SLOT);
-            if (c < 6) {
-                const int s = c - 2;
+            const int kp = y + 2;
+            const int live = __builtin_amdgcn_readfirstlane(kp < np ? 1 : 0);
+            const uint32_t slot = lds0 + (uint32_t)((kp % PF_NSL) * L::SLOT);
+            const int cc = c - 4;
+            if (cc < L::ACOP) {
                 int4_t r = rsrc_a;
                 r[2] = live ? r[2] : 0;
-                dma_b128(slot + (4 * wave + s) * 1024, a_voff[s], r, ks * PF_ROWB);
+                dma_b128(slot + (L::ACOP * wave + cc) * 1024, a_voff[cc] + kp * PF_PROWB, r, 0);
             } else {
-                const int s = c - 6;
+                const int s = cc - L::ACOP;
                 int4_t r = rsrc_w;
                 r[2] = live ? r[2] : 0;
-                dma_b128(slot + PF_TILE + (WFR * wave + s) * 1024, w_voff[s], r, ks * PF_ROWB);
+                dma_b128(slot + PF_ATILE + (L::WCOP * wave + s) * 1024, w_voff[s] + kp * PF_PROWB, r, 0);
             }
         }
     };
 
-    // LDS read q (0 .. READS-1) of stage s: code fragments (A of both steps,
-    // then W of both steps), then the scale dwords (A, then W)
+    // LDS read q (0 .. READS-1) of sub-stage s (pair s/2, half s%2): code
+    // fragments (A of both steps, then W of both steps), then the scale
+    // dwords (A, then W)
     auto read_piece = [&](int s, int q, PfFrags<WFR>& f) {
-        const uint8_t* slot = smem + (s % PF_NS) * L::SLOT;
-        const uint8_t* win = smem + L::SC0 + ((s / PF_SWS) % PF_NWIN) * L::WIN + (s % PF_SWS) * 4;
+        const int pr = s >> 1, h = s & 1;
+        const uint8_t* slot = smem + (pr % PF_NSL) * L::SLOT;
+        const uint8_t* win = smem + L::SC0 + ((pr / PF_WPAIRS) % PF_NWIN) * L::WIN + (pr % PF_WPAIRS) * 8 + h * 4;
         if (q < 8) {
             const int kk = q >> 2, x = q & 3;
             const int row = wm * 128 + x * 32 + r32;
-            f.a[kk][x] = *reinterpret_cast<const int4_t*>(slot + row * PF_ROWB + (((2 * kk + g) ^ pf_swz(row)) * 16));
+            f.a[kk][x] =
+                *reinterpret_cast<const int4_t*>(slot + row * PF_PROWB + (((4 * h + 2 * kk + g) ^ pf_swz(row)) * 16));
         } else if (q < 8 + 2 * WFR) {
             const int kk = (q - 8) / WFR, x = (q - 8) % WFR;
             const int row = wn * (BN / 2) + x * 32 + r32;
-            f.w[kk][x] =
-                *reinterpret_cast<const int4_t*>(slot + PF_TILE + row * PF_ROWB + (((2 * kk + g) ^ pf_swz(row)) * 16));
+            f.w[kk][x] = *reinterpret_cast<const int4_t*>(slot + PF_ATILE + row * PF_PROWB +
+                                                          (((4 * h + 2 * kk + g) ^ pf_swz(row)) * 16));
         } else if (q < 12 + 2 * WFR) {
             const int x = q - 8 - 2 * WFR;
             const int row = wm * 128 + x * 32 + r32;
@@ -260,7 +271,7 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // matrix-core instruction q of a stage: step kk = q / (4 WFR), fragment (i, j)
+    // matrix-core instruction q of a sub-stage: step kk = q / (4 WFR), fragment (i, j)
     auto mfma = [&](int q, const PfFrags<WFR>& f, const int* sa, const int* sw) {
         const int kk = q / (4 * WFR), i = (q / WFR) % 4, j = q % WFR;
         const int8_t_ b8 = int8_t_{f.w[kk][j][0], f.w[kk][j][1], f.w[kk][j][2], f.w[kk][j][3], 0, 0, 0, 0};
@@ -271,14 +282,14 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 2, sw[j], 2, sa[i]);
     };
 
-    // Stage s: computed from `cur`; stage s + 1 is read into `nxt`; virtual
-    // stage s issues its copies.  Reads and copies are spread evenly over the
-    // matrix-core instructions.
-    auto stage = [&](int s, const PfFrags<WFR>& cur, PfFrags<WFR>& nxt) {
-        // The copies of stage s + 1 were issued two stages ago; only the
-        // previous stage's may still be in flight.
-        wait_vmcnt<L::COPIES>();
-        lds_barrier();
+    // Sub-stage s: computed from `cur`; sub-stage s + 1 is read into `nxt`;
+    // the second sub-stage of a pair first waits for the pair after next's
+    // predecessor (all copies issued so far) and issues its own copies.
+    auto sub = [&](int s, const PfFrags<WFR>& cur, PfFrags<WFR>& nxt, bool second) {
+        if (second) {
+            wait_vmcnt<0>();
+            lds_barrier();
+        }
         // byte 2 kk + g of a scale dword is this lane's block; after the shift
         // it sits at byte 2 kk, which the instruction's op_sel picks
         int sa[4], sw[WFR];
@@ -296,48 +307,43 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
                 read_piece(s + 1, x, nxt);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (second) {
 #pragma unroll
-            for (int c = q * L::COPIES / L::MFMAS; c < (q + 1) * L::COPIES / L::MFMAS; ++c) {
-                __builtin_amdgcn_sched_barrier(0);
-                copy(s, c);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int c = q * L::COPIES / L::MFMAS; c < (q + 1) * L::COPIES / L::MFMAS; ++c) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    copy(s >> 1, c);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Prologue: all of window 0, then virtual stages -4 .. -1 (window 1's
-    // pieces 0..3 and the codes of stages 0..2).
+    // Prologue: the copy slots of virtual pairs -5 .. -1, with code copies
+    // only where they name pairs 0 and 1: windows 0 and (piece 0 of) 1, pairs
+    // 0 and 1.
+    for (int y = -5; y < 0; ++y) {
 #pragma unroll
-    for (int j = 0; j < PF_SWS; ++j) {
-        const uint32_t wbuf = lds0 + L::SC0;
-        const int t = 4 * j + wave;
-        dma_b32(wbuf + t * 256, (m0 + 8 * t + srow) * KB + sdw * 4, rsrc_as, 0);
-        int4_t r = rsrc_ws;
-        r[2] = w_piece_real ? r[2] : 0;
-        const int tw = WFR * j + (w_piece_real ? wave : 0);
-        const uint32_t dst = w_piece_real ? wbuf + PF_BM * PF_SWB + tw * 256 : lds0 + L::DUMMY + (wave & 1) * 256;
-        dma_b32(dst, (n0 + 8 * tw + srow) * KB + sdw * 4, r, 0);
+        for (int c = 0; c < 4; ++c) copy(y, c);
+        if (y >= -2) {
+#pragma unroll
+            for (int c = 4; c < L::COPIES; ++c) copy(y, c);
+        }
     }
-    copy(-4, 0);
-    copy(-4, 1);
-    for (int y = -3; y < 0; ++y)
-#pragma unroll
-        for (int c = 0; c < L::COPIES; ++c) copy(y, c);
-    wait_vmcnt<2 * L::COPIES>();  // window 0 and stage 0 have landed
+    wait_vmcnt<0>();
     lds_barrier();
     PfFrags<WFR> X, Y;
 #pragma unroll
     for (int q = 0; q < L::READS; ++q) read_piece(0, q, X);
 
-    int s = 0;
-    for (; s + 1 < nk; s += 2) {
-        stage(s, X, Y);
-        stage(s + 1, Y, X);
+    int pr = 0;
+    for (; 2 * pr + 1 < nk; ++pr) {
+        sub(2 * pr, X, Y, false);
+        sub(2 * pr + 1, Y, X, true);
     }
-    if (s < nk) stage(s, X, Y);
+    if (2 * pr < nk) sub(2 * pr, X, Y, false);   // the half pair when K % 256 == 128
     wait_vmcnt<0>();   // the trailing zero-fill copies have landed
-    lds_barrier();     // every wave is done with the rings
+    lds_barrier();     // every wave is done with the slots
 
     // Epilogue, one 32-row band (fragment row i) at a time through this
     // wave's private LDS region: write the band row-major, read it back as

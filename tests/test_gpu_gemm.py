@@ -190,6 +190,29 @@ def test_vocab_projection_sampled():
     sampled_check(W.MXFP4_VOCAB, "mxfp4", fused=False)
 
 
+# The prefill kernel on shapes that reach its edges: an odd number of 128-K
+# sub-stages (K % 256 == 128, a half pair at the end), ragged M and N, a main
+# launch with no tail, a tail-only launch, and a main launch plus a tail.
+# Sampled outputs against the oracle, bf16 and fp32 output.
+PREFILL_EDGE = [
+    ("odd sub-stages, main only", 2148, 1408, 4146),      # 9 x 17 = 153 tiles: no tail
+    ("tail only", 1024, 1152, 1100),                      # 4 x 5 = 20 tiles: all as halves
+    ("main + tail", 1300, 2560, 33000),                   # 6 x 129 = 774 tiles: 6 tail tiles
+]
+
+
+@pytest.mark.parametrize("what,m,k,n", PREFILL_EDGE)
+def test_prefill_kernel_edges(what, m, k, n):
+    assert mxl.mx_gemm_plan("mxfp4", "mxfp4", m, n, k).split(" ", 1)[1].startswith("mx_gemm_prefill_kernel<")
+    cfg = W.Gemm(f"prefill edge {what}", m, k, n)
+    y = sampled_check(cfg, "mxfp4", fused=False, count=3000)
+    a_bits, w_bits = cfg.activations(), cfg.weights()
+    _, _, (aq, as_), (wq, ws) = run_mx(a_bits, w_bits, "mxfp4", fused=False)
+    yf = mxl.mx_gemm(aq, as_, wq, ws, k, out_f32=True)
+    # the bf16 output is the RNE of the fp32 one, element by element
+    assert torch.equal(yf.to(torch.bfloat16), y)
+
+
 def test_deterministic():
     a_bits = W.activations_entry_outliers(300, 1024)
     w_bits = W.normal_bf16(700, 1024, 0.02, 1)
