@@ -189,8 +189,10 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
         w_voff[s] = (n0 + row) * row_bytes + ((lane & 7) ^ pf_swz(row)) * 16;
     }
     // Scale copies move 8 rows x 32 B ([row][32 B] in LDS); a window has 32
-    // for A and BN/8 for W, issued as 4 pieces.
+    // for A and BN/8 for W, issued as 4 pieces.  Per-lane part of their
+    // offsets (row srow of the copy, dword sdw of the row); the rest is uniform.
     const int srow = lane >> 3, sdw = lane & 7;
+    const int as_voff = (m0 + srow) * KB + sdw * 4, ws_voff = (n0 + srow) * KB + sdw * 4;
     constexpr int WSC = BN / 8;
 
     // Copy c (0 .. COPIES-1) issued in pair y: c < 4 are piece (y + 5) % 4 of
@@ -198,16 +200,17 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     // code copies of pair y + 2 (A, then W).  Window w is issued during pairs
     // 4w-5 .. 4w-2, after every read of window w-2 (same buffer), and has
     // landed by the barrier that precedes its first read in pair 4w-1.
+    // Everything but the per-lane offsets is uniform (scalar registers).
     auto copy = [&](int y, int c) {
         if (c < 4) {
             const int win = (y + 5) >> 2, j = (y + 5) & 3;
-            const int live = __builtin_amdgcn_readfirstlane(win * PF_WPAIRS < np ? 1 : 0);
-            const uint32_t wbuf = lds0 + L::SC0 + (uint32_t)((win % PF_NWIN) * L::WIN);
+            const bool live = win * PF_WPAIRS < np;
+            const uint32_t wbuf = lds0 + L::SC0 + (uint32_t)((win & (PF_NWIN - 1)) * L::WIN);
             if (c < 2) {
                 int4_t r = rsrc_as;
                 r[2] = live ? r[2] : 0;
                 const int t = 8 * j + 2 * wave + c;
-                dma_b32(wbuf + t * 256, (m0 + 8 * t + srow) * KB + win * PF_SWB + sdw * 4, r, 0);
+                dma_b32(wbuf + t * 256, as_voff + (8 * t * KB + win * PF_SWB), r, 0);
             } else {
                 const int slot_in_piece = 2 * wave + (c - 2);
                 const bool real = slot_in_piece < WSC / 4;
@@ -215,12 +218,12 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
                 int4_t r = rsrc_ws;
                 r[2] = (live && real) ? r[2] : 0;
                 const uint32_t dst = real ? wbuf + PF_BM * PF_SWB + t * 256 : lds0 + L::DUMMY + (wave & 1) * 256;
-                dma_b32(dst, (n0 + 8 * t + srow) * KB + win * PF_SWB + sdw * 4, r, 0);
+                dma_b32(dst, ws_voff + (8 * t * KB + win * PF_SWB), r, 0);
             }
         } else {
             const int kp = y + 2;
-            const int live = __builtin_amdgcn_readfirstlane(kp < np ? 1 : 0);
-            const uint32_t slot = lds0 + (uint32_t)((kp % PF_NSL) * L::SLOT);
+            const bool live = kp < np;
+            const uint32_t slot = lds0 + (uint32_t)((kp & (PF_NSL - 1)) * L::SLOT);
             const int cc = c - 4;
             if (cc < L::ACOP) {
                 int4_t r = rsrc_a;
@@ -240,8 +243,8 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     // dwords (A, then W)
     auto read_piece = [&](int s, int q, PfFrags<WFR>& f) {
         const int pr = s >> 1, h = s & 1;
-        const uint8_t* slot = smem + (pr % PF_NSL) * L::SLOT;
-        const uint8_t* win = smem + L::SC0 + ((pr / PF_WPAIRS) % PF_NWIN) * L::WIN + (pr % PF_WPAIRS) * 8 + h * 4;
+        const uint8_t* slot = smem + (pr & (PF_NSL - 1)) * L::SLOT;
+        const uint8_t* win = smem + L::SC0 + ((pr / PF_WPAIRS) & (PF_NWIN - 1)) * L::WIN + (pr % PF_WPAIRS) * 8 + h * 4;
         if (q < 8) {
             const int kk = q >> 2, x = q & 3;
             const int row = wm * 128 + x * 32 + r32;
