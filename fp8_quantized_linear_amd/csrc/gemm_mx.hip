@@ -892,8 +892,8 @@ extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n,
         }
     case SC_LARGE:
         if (!fused && mxl_prefill_ok(m, n, k))
-            return "mx_gemm_prefill_kernel<tile 256x256x128, 2x2 waves of 128x128, 3-slot code ring + "
-                   "8-stage scale windows fed by buffer-to-LDS copies, stage-ahead fragments, scaled mfma 32x32x64; "
+            return "mx_gemm_prefill_kernel<tile 256x256x128, 2x2 waves of 128x128, two 256-K pair slots + "
+                   "4-pair scale windows fed by buffer-to-LDS copies, stage-ahead fragments, scaled mfma 32x32x64; "
                    "a last round of tiles at most half full runs as 256x128 halves>";
         return "mx_gemm_kernel<tile 256x256x128, 2x2 waves of 128x128, scaled mfma 32x32x64>";
     default:

@@ -131,6 +131,16 @@ __device__ __forceinline__ void pf_tile(int t, int M, int N, int& tm, int& tn)
     tn = first_n + in % gn;
 }
 
+// LDS reads at a byte address of the workgroup's LDS
+__device__ __forceinline__ int4_t lds_read_b128(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) int4_t*>((size_t)addr);
+}
+__device__ __forceinline__ uint32_t lds_read_b32(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>((size_t)addr);
+}
+
 // one sub-stage's operands in registers: code fragments per 64-wide step kk,
 // and the raw scale dwords (4 blocks of the sub-stage) of this lane's rows
 template <int WFR>
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     // 4w-5 .. 4w-2, after every read of window w-2 (same buffer), and has
     // landed by the barrier that precedes its first read in pair 4w-1.
     // Everything but the per-lane offsets is uniform (scalar registers).
-    auto copy = [&](int y, int c) {
+    auto copy = [&](int y, int c) __attribute__((always_inline)) {
         if (c < 4) {
             const int win = (y + 5) >> 2, j = (y + 5) & 3;
             const bool live = win * PF_WPAIRS < np;
@@ -238,31 +248,42 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
         }
     };
 
+    // LDS read addresses.  Fragment rows of one lane differ by multiples of
+    // 32, so they share the chunk swizzle (r32 >> 1) & 7: a fragment's
+    // address is a per-(half, step) base, plus the slot's offset (uniform),
+    // plus 4096 bytes per 32 rows, which the read takes as an immediate.
+    const int swl = pf_swz(r32);
+    uint32_t abase[2][2], wbase[2][2];   // LDS byte addresses in slot 0
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int ch = ((4 * h + 2 * kk + g) ^ swl) * 16;
+            abase[h][kk] = lds0 + (wm * 128 + r32) * PF_PROWB + ch;
+            wbase[h][kk] = lds0 + PF_ATILE + (wn * (BN / 2) + r32) * PF_PROWB + ch;
+        }
+    const uint32_t sa_lane = lds0 + L::SC0 + (wm * 128 + r32) * PF_SWB;
+    const uint32_t sw_lane = lds0 + L::SC0 + PF_BM * PF_SWB + (wn * (BN / 2) + r32) * PF_SWB;
+
     // LDS read q (0 .. READS-1) of sub-stage s (pair s/2, half s%2): code
     // fragments (A of both steps, then W of both steps), then the scale
     // dwords (A, then W)
-    auto read_piece = [&](int s, int q, PfFrags<WFR>& f) {
+    auto read_piece = [&](int s, int q, PfFrags<WFR>& f) __attribute__((always_inline)) {
         const int pr = s >> 1, h = s & 1;
-        const uint8_t* slot = smem + (pr & (PF_NSL - 1)) * L::SLOT;
-        const uint8_t* win = smem + L::SC0 + ((pr / PF_WPAIRS) & (PF_NWIN - 1)) * L::WIN + (pr % PF_WPAIRS) * 8 + h * 4;
+        const uint32_t slot = (pr & (PF_NSL - 1)) * L::SLOT;
+        const uint32_t win = ((pr / PF_WPAIRS) & (PF_NWIN - 1)) * L::WIN + (pr % PF_WPAIRS) * 8 + h * 4;
         if (q < 8) {
             const int kk = q >> 2, x = q & 3;
-            const int row = wm * 128 + x * 32 + r32;
-            f.a[kk][x] =
-                *reinterpret_cast<const int4_t*>(slot + row * PF_PROWB + (((4 * h + 2 * kk + g) ^ pf_swz(row)) * 16));
+            f.a[kk][x] = lds_read_b128(abase[h][kk] + slot + x * 32 * PF_PROWB);
         } else if (q < 8 + 2 * WFR) {
             const int kk = (q - 8) / WFR, x = (q - 8) % WFR;
-            const int row = wn * (BN / 2) + x * 32 + r32;
-            f.w[kk][x] = *reinterpret_cast<const int4_t*>(slot + PF_ATILE + row * PF_PROWB +
-                                                          (((4 * h + 2 * kk + g) ^ pf_swz(row)) * 16));
+            f.w[kk][x] = lds_read_b128(wbase[h][kk] + slot + x * 32 * PF_PROWB);
         } else if (q < 12 + 2 * WFR) {
             const int x = q - 8 - 2 * WFR;
-            const int row = wm * 128 + x * 32 + r32;
-            f.sa[x] = (int)*reinterpret_cast<const uint32_t*>(win + row * PF_SWB);
+            f.sa[x] = (int)lds_read_b32(sa_lane + win + x * 32 * PF_SWB);
         } else {
             const int x = q - 12 - 2 * WFR;
-            const int row = wn * (BN / 2) + x * 32 + r32;
-            f.sw[x] = (int)*reinterpret_cast<const uint32_t*>(win + PF_BM * PF_SWB + row * PF_SWB);
+            f.sw[x] = (int)lds_read_b32(sw_lane + win + x * 32 * PF_SWB);
         }
     };
 
@@ -275,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // matrix-core instruction q of a sub-stage: step kk = q / (4 WFR), fragment (i, j)
-    auto mfma = [&](int q, const PfFrags<WFR>& f, const int* sa, const int* sw) {
+    auto mfma = [&](int q, const PfFrags<WFR>& f, const int* sa, const int* sw) __attribute__((always_inline)) {
         const int kk = q / (4 * WFR), i = (q / WFR) % 4, j = q % WFR;
         const int8_t_ b8 = int8_t_{f.w[kk][j][0], f.w[kk][j][1], f.w[kk][j][2], f.w[kk][j][3], 0, 0, 0, 0};
         const int8_t_ a8 = int8_t_{f.a[kk][i][0], f.a[kk][i][1], f.a[kk][i][2], f.a[kk][i][3], 0, 0, 0, 0};
@@ -286,9 +307,9 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     };
 
     // Sub-stage s: computed from `cur`; sub-stage s + 1 is read into `nxt`;
-    // the second sub-stage of a pair first waits for the pair after next's
-    // predecessor (all copies issued so far) and issues its own copies.
-    auto sub = [&](int s, const PfFrags<WFR>& cur, PfFrags<WFR>& nxt, bool second) {
+    // the second sub-stage of a pair first waits for all copies issued so
+    // far (the next pair) and then issues its own.
+    auto sub = [&](int s, const PfFrags<WFR>& cur, PfFrags<WFR>& nxt, bool second) __attribute__((always_inline)) {
         if (second) {
             wait_vmcnt<0>();
             lds_barrier();
