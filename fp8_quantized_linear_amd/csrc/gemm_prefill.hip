@@ -74,16 +74,20 @@ constexpr int PF_SWB = PF_WPAIRS * 8;              // 32 scale bytes per row per
 constexpr int PF_NWIN = 2;                         // scale window buffers
 constexpr int PF_GROUP_N = 4;                      // tile columns per group of the tile order
 
-// LDS layout for tile width BN: pair slots [2][A 32 KiB | W BN*128], scale
-// windows [2][A 256 x 32 B | W BN x 32 B], then (BN = 128) a 512-byte dummy area
+// LDS layout for tile width BN: A code slots [2][32 KiB], W code slots
+// [2][BN x 128 B], scale windows [2][A 256 x 32 B | W BN x 32 B], then (BN =
+// 128) 1 KiB that absorbs the scale copies of waves with none to make.  Both
+// slots of an operand lie within 64 KiB of its first, so a per-lane base
+// register reaches every fragment of either slot through the read's 16-bit
+// immediate offset.
 template <int BN>
 struct PfLayout {
     static constexpr int W_TILE = BN * PF_PROWB;
-    static constexpr int SLOT = PF_ATILE + W_TILE;
+    static constexpr int W0 = PF_NSL * PF_ATILE;   // W code slots
     static constexpr int WIN = (PF_BM + BN) * PF_SWB;
-    static constexpr int SC0 = PF_NSL * SLOT;
+    static constexpr int SC0 = W0 + PF_NSL * W_TILE;
     static constexpr int DUMMY = SC0 + PF_NWIN * WIN;
-    static constexpr int LDS = DUMMY + (BN == 256 ? 0 : 512);   // 163840 bytes for BN = 256
+    static constexpr int LDS = DUMMY + (BN == 256 ? 0 : 1024);   // 163840 bytes for BN = 256
     static constexpr int WFR = BN / 64;            // W fragments per wave (a wave covers BN/2 W rows)
     static constexpr int ACOP = PF_ATILE / 1024 / 4;        // 8 A code copies per wave per pair
     static constexpr int WCOP = BN * PF_PROWB / 1024 / 4;   // BN/32 W code copies per wave per pair
@@ -94,6 +98,9 @@ struct PfLayout {
     static constexpr int READ_SPAN = MFMAS * 3 / 4;  // reads go out during the first 3/4 of a
                                                      // sub-stage, leaving the rest to cover them
     static_assert(LDS <= 163840, "LDS");
+    static_assert((PF_NSL - 1) * PF_ATILE + 3 * 32 * PF_PROWB < 65536 &&
+                      (PF_NSL - 1) * W_TILE + (WFR - 1) * 32 * PF_PROWB < 65536,
+                  "fragment offsets fit the read's immediate");
 };
 
 struct PrefillArgs {
@@ -149,6 +156,16 @@ struct PfFrags {
     int sa[4], sw[WFR];
 };
 
+// The uniform part of the copies issued during one pair: buffer descriptors
+// (zero-sized once past the last pair or window), the K offset and LDS slot
+// of the code copies, and the LDS bases and buffer offsets of the
+// scale-window piece.
+struct PfPairCopies {
+    int4_t ra, rw, ras, rws;
+    int coff, asoff, wsoff;
+    uint32_t adst, wdst, asdst, wsdst;
+};
+
 template <bool OUT_F32, int BN>
 __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
 {
@@ -186,7 +203,7 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     // Code copies, 8 rows x 128 B = 1 KiB of LDS each: wave w copies A rows
     // [64 w, 64 w + 64) and W rows [8 WCOP w, 8 WCOP (w + 1)).  LDS position L
     // of a copy is row 8*copy + L/8, physical chunk L%8, which holds logical
-    // chunk (L%8) ^ swz(row).
+    // chunk (L%8) ^ swz(row).  Per-lane offsets of pair 0; pair kp adds kp*128.
     int a_voff[L::ACOP], w_voff[L::WCOP];
 #pragma unroll
     for (int s = 0; s < L::ACOP; ++s) {
@@ -198,92 +215,115 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
         const int row = 8 * (L::WCOP * wave + s) + lane / 8;
         w_voff[s] = (n0 + row) * row_bytes + ((lane & 7) ^ pf_swz(row)) * 16;
     }
-    // Scale copies move 8 rows x 32 B ([row][32 B] in LDS); a window has 32
-    // for A and BN/8 for W, issued as 4 pieces.  Per-lane part of their
-    // offsets (row srow of the copy, dword sdw of the row); the rest is uniform.
-    const int srow = lane >> 3, sdw = lane & 7;
-    const int as_voff = (m0 + srow) * KB + sdw * 4, ws_voff = (n0 + srow) * KB + sdw * 4;
-    constexpr int WSC = BN / 8;
+    const uint32_t a_dst = lds0 + (uint32_t)(L::ACOP * wave * 1024);           // in A slot 0
+    const uint32_t w_dst = lds0 + L::W0 + (uint32_t)(L::WCOP * wave * 1024);   // in W slot 0
 
-    // Copy c (0 .. COPIES-1) issued in pair y: c < 4 are piece (y + 5) % 4 of
-    // scale window (y + 5) / 4 (A copies, then W copies); the rest are the
-    // code copies of pair y + 2 (A, then W).  Window w is issued during pairs
-    // 4w-5 .. 4w-2, after every read of window w-2 (same buffer), and has
-    // landed by the barrier that precedes its first read in pair 4w-1.
-    // Everything but the per-lane offsets is uniform (scalar registers).
-    auto copy = [&](int y, int c) __attribute__((always_inline)) {
-        if (c < 4) {
-            const int win = (y + 5) >> 2, j = (y + 5) & 3;
-            const bool live = win * PF_WPAIRS < np;
-            const uint32_t wbuf = lds0 + L::SC0 + (uint32_t)((win & (PF_NWIN - 1)) * L::WIN);
-            if (c < 2) {
-                int4_t r = rsrc_as;
-                r[2] = live ? r[2] : 0;
-                const int t = 8 * j + 2 * wave + c;
-                dma_b32(wbuf + t * 256, as_voff + (8 * t * KB + win * PF_SWB), r, 0);
-            } else {
-                const int slot_in_piece = 2 * wave + (c - 2);
-                const bool real = slot_in_piece < WSC / 4;
-                const int t = (WSC / 4) * j + (real ? slot_in_piece : 0);
-                int4_t r = rsrc_ws;
-                r[2] = (live && real) ? r[2] : 0;
-                const uint32_t dst = real ? wbuf + PF_BM * PF_SWB + t * 256 : lds0 + L::DUMMY + (wave & 1) * 256;
-                dma_b32(dst, ws_voff + (8 * t * KB + win * PF_SWB), r, 0);
-            }
-        } else {
-            const int kp = y + 2;
-            const bool live = kp < np;
-            const uint32_t slot = lds0 + (uint32_t)((kp & (PF_NSL - 1)) * L::SLOT);
+    // Scale copies move 8 rows x 32 B ([row][32 B] in LDS).  A window is
+    // issued as 4 pieces; piece j holds A copies t = 8 j + (0 .. 7) and W
+    // copies t = (WSC/4) j + (0 .. WSC/4 - 1), copy t covering rows
+    // [8 t, 8 t + 8) of the window.  Wave w makes copies 2 w and 2 w + 1 of
+    // each piece; with BN = 128 waves 2 and 3 have no W copy and fill the
+    // spare area from a zero-sized buffer instead.
+    constexpr int WSC = BN / 8;
+    const bool ws_real = 2 * wave + 1 < WSC / 4;
+    const int srow = lane >> 3, sdw = lane & 7;
+    int as_v[2], ws_v[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        as_v[c] = (m0 + 8 * (2 * wave + c) + srow) * KB + sdw * 4;
+        ws_v[c] = (n0 + 8 * (2 * wave + c) + srow) * KB + sdw * 4;
+    }
+
+    // Copies issued during pair y: piece (y + 5) % 4 of scale window
+    // (y + 5) / 4, and the codes of pair y + 2 (into the slot of pair y).
+    // Window w is issued during pairs 4w-5 .. 4w-2, after every read of
+    // window w-2 (same buffer), and has landed by the barrier that precedes
+    // its first read in pair 4w-1.
+    auto pair_copies = [&](int y) __attribute__((always_inline)) {
+        PfPairCopies cp;
+        const int kp = y + 2;
+        const bool livec = kp < np;
+        cp.ra = rsrc_a;
+        cp.ra[2] = livec ? cp.ra[2] : 0;
+        cp.rw = rsrc_w;
+        cp.rw[2] = livec ? cp.rw[2] : 0;
+        cp.coff = kp * PF_PROWB;
+        cp.adst = a_dst + (uint32_t)((kp & (PF_NSL - 1)) * PF_ATILE);
+        cp.wdst = w_dst + (uint32_t)((kp & (PF_NSL - 1)) * L::W_TILE);
+        const int win = (y + 5) >> 2, j = (y + 5) & 3;
+        const bool lives = win * PF_WPAIRS < np;
+        const uint32_t wbuf = lds0 + L::SC0 + (uint32_t)((win & (PF_NWIN - 1)) * L::WIN);
+        cp.ras = rsrc_as;
+        cp.ras[2] = lives ? cp.ras[2] : 0;
+        cp.rws = rsrc_ws;
+        cp.rws[2] = (lives && ws_real) ? cp.rws[2] : 0;
+        cp.asdst = wbuf + (uint32_t)((8 * j + 2 * wave) * 256);
+        cp.wsdst = ws_real ? wbuf + PF_BM * PF_SWB + (uint32_t)(((WSC / 4) * j + 2 * wave) * 256)
+                           : lds0 + L::DUMMY + (uint32_t)((wave & 1) * 512);
+        cp.asoff = 64 * j * KB + win * PF_SWB;
+        cp.wsoff = 8 * (WSC / 4) * j * KB + win * PF_SWB;
+        return cp;
+    };
+    // copy c (0 .. COPIES-1) of a pair: 2 A and 2 W scale copies, then the A
+    // and W code copies
+    auto copy = [&](int c, const PfPairCopies& cp) __attribute__((always_inline)) {
+        if (c < 2) {
+            dma_b32_at(cp.asdst, c * 256, as_v[c], cp.asoff, cp.ras);
+        } else if (c < 4) {
+            dma_b32_at(cp.wsdst, (c - 2) * 256, ws_v[c - 2], cp.wsoff, cp.rws);
+        } else if (c - 4 < L::ACOP) {
             const int cc = c - 4;
-            if (cc < L::ACOP) {
-                int4_t r = rsrc_a;
-                r[2] = live ? r[2] : 0;
-                dma_b128(slot + (L::ACOP * wave + cc) * 1024, a_voff[cc] + kp * PF_PROWB, r, 0);
-            } else {
-                const int s = cc - L::ACOP;
-                int4_t r = rsrc_w;
-                r[2] = live ? r[2] : 0;
-                dma_b128(slot + PF_ATILE + (L::WCOP * wave + s) * 1024, w_voff[s] + kp * PF_PROWB, r, 0);
-            }
+            dma_b128_at(cp.adst, cc * 1024, a_voff[cc], cp.coff, cp.ra);
+        } else {
+            const int s = c - 4 - L::ACOP;
+            dma_b128_at(cp.wdst, s * 1024, w_voff[s], cp.coff, cp.rw);
         }
     };
 
     // LDS read addresses.  Fragment rows of one lane differ by multiples of
     // 32, so they share the chunk swizzle (r32 >> 1) & 7: a fragment's
-    // address is a per-(half, step) base, plus the slot's offset (uniform),
-    // plus 4096 bytes per 32 rows, which the read takes as an immediate.
+    // address is a per-(half, step) base plus 4096 bytes per 32 rows, which
+    // the read takes as an immediate.  During pair pr the half-1 bases point
+    // into slot pr % 2 (read by its first sub-stage) and the half-0 bases
+    // into slot (pr + 1) % 2 (read by its second, for the next pair); after
+    // the pair both move to the other slot.
     const int swl = pf_swz(r32);
-    uint32_t abase[2][2], wbase[2][2];   // LDS byte addresses in slot 0
+    uint32_t abase[2][2], wbase[2][2];   // LDS byte addresses
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int ch = ((4 * h + 2 * kk + g) ^ swl) * 16;
             abase[h][kk] = lds0 + (wm * 128 + r32) * PF_PROWB + ch;
-            wbase[h][kk] = lds0 + PF_ATILE + (wn * (BN / 2) + r32) * PF_PROWB + ch;
+            wbase[h][kk] = lds0 + L::W0 + (wn * (BN / 2) + r32) * PF_PROWB + ch;
         }
     const uint32_t sa_lane = lds0 + L::SC0 + (wm * 128 + r32) * PF_SWB;
     const uint32_t sw_lane = lds0 + L::SC0 + PF_BM * PF_SWB + (wn * (BN / 2) + r32) * PF_SWB;
+    // scale-read bases of pair pr: one add per pair, kept opaque so that the
+    // per-read part stays an immediate
+    auto scale_base = [&](int pr, uint32_t& sa, uint32_t& sw) __attribute__((always_inline)) {
+        const uint32_t off = (uint32_t)(((pr / PF_WPAIRS) & (PF_NWIN - 1)) * L::WIN + (pr % PF_WPAIRS) * 8);
+        sa = sa_lane + off;
+        sw = sw_lane + off;
+        asm volatile("" : "+v"(sa), "+v"(sw));
+    };
 
-    // LDS read q (0 .. READS-1) of sub-stage s (pair s/2, half s%2): code
-    // fragments (A of both steps, then W of both steps), then the scale
-    // dwords (A, then W)
-    auto read_piece = [&](int s, int q, PfFrags<WFR>& f) __attribute__((always_inline)) {
-        const int pr = s >> 1, h = s & 1;
-        const uint32_t slot = (pr & (PF_NSL - 1)) * L::SLOT;
-        const uint32_t win = ((pr / PF_WPAIRS) & (PF_NWIN - 1)) * L::WIN + (pr % PF_WPAIRS) * 8 + h * 4;
+    // LDS read q (0 .. READS-1) of half h (code bases abase/wbase[h], scale
+    // bases sa/sw): code fragments (A of both steps, then W of both steps),
+    // then the scale dwords (A, then W)
+    auto read_piece = [&](int q, PfFrags<WFR>& f, int h, uint32_t sa, uint32_t sw) __attribute__((always_inline)) {
         if (q < 8) {
             const int kk = q >> 2, x = q & 3;
-            f.a[kk][x] = lds_read_b128(abase[h][kk] + slot + x * 32 * PF_PROWB);
+            f.a[kk][x] = lds_read_b128(abase[h][kk] + x * 32 * PF_PROWB);
         } else if (q < 8 + 2 * WFR) {
             const int kk = (q - 8) / WFR, x = (q - 8) % WFR;
-            f.w[kk][x] = lds_read_b128(wbase[h][kk] + slot + x * 32 * PF_PROWB);
+            f.w[kk][x] = lds_read_b128(wbase[h][kk] + x * 32 * PF_PROWB);
         } else if (q < 12 + 2 * WFR) {
             const int x = q - 8 - 2 * WFR;
-            f.sa[x] = (int)lds_read_b32(sa_lane + win + x * 32 * PF_SWB);
+            f.sa[x] = (int)lds_read_b32(sa + h * 4 + x * 32 * PF_SWB);
         } else {
             const int x = q - 12 - 2 * WFR;
-            f.sw[x] = (int)lds_read_b32(sw_lane + win + x * 32 * PF_SWB);
+            f.sw[x] = (int)lds_read_b32(sw + h * 4 + x * 32 * PF_SWB);
         }
     };
 
@@ -306,10 +346,13 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 2, sw[j], 2, sa[i]);
     };
 
-    // Sub-stage s: computed from `cur`; sub-stage s + 1 is read into `nxt`;
-    // the second sub-stage of a pair first waits for all copies issued so
-    // far (the next pair) and then issues its own.
-    auto sub = [&](int s, const PfFrags<WFR>& cur, PfFrags<WFR>& nxt, bool second) __attribute__((always_inline)) {
+    // One sub-stage: computed from `cur` while the next sub-stage (half nh,
+    // scale bases nsa/nsw) is read into `nxt`.  The second sub-stage of a
+    // pair first waits for all copies issued so far (the next pair) and then
+    // issues the pair's copies; the first computes their uniform part in its
+    // read-free tail.
+    auto sub = [&](const PfFrags<WFR>& cur, PfFrags<WFR>& nxt, bool second, int nh, uint32_t nsa, uint32_t nsw,
+                   int pr, PfPairCopies& cp) __attribute__((always_inline)) {
         if (second) {
             wait_vmcnt<0>();
             lds_barrier();
@@ -328,14 +371,19 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
 #pragma unroll
             for (int x = q * L::READS / L::READ_SPAN; x < (q + 1) * L::READS / L::READ_SPAN && x < L::READS; ++x) {
                 __builtin_amdgcn_sched_barrier(0);
-                read_piece(s + 1, x, nxt);
+                read_piece(x, nxt, nh, nsa, nsw);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (!second && q == L::READ_SPAN) {
+                __builtin_amdgcn_sched_barrier(0);
+                cp = pair_copies(pr);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (second) {
 #pragma unroll
                 for (int c = q * L::COPIES / L::MFMAS; c < (q + 1) * L::COPIES / L::MFMAS; ++c) {
                     __builtin_amdgcn_sched_barrier(0);
-                    copy(s >> 1, c);
+                    copy(c, cp);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -347,25 +395,52 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     // only where they name pairs 0 and 1: windows 0 and (piece 0 of) 1, pairs
     // 0 and 1.
     for (int y = -5; y < 0; ++y) {
+        const PfPairCopies cp = pair_copies(y);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) copy(y, c);
+        for (int c = 0; c < 4; ++c) copy(c, cp);
         if (y >= -2) {
 #pragma unroll
-            for (int c = 4; c < L::COPIES; ++c) copy(y, c);
+            for (int c = 4; c < L::COPIES; ++c) copy(c, cp);
         }
     }
     wait_vmcnt<0>();
     lds_barrier();
     PfFrags<WFR> X, Y;
+    uint32_t sa_c, sw_c;   // scale-read bases of the current pair
+    scale_base(0, sa_c, sw_c);
 #pragma unroll
-    for (int q = 0; q < L::READS; ++q) read_piece(0, q, X);
+    for (int q = 0; q < L::READS; ++q) read_piece(q, X, 0, sa_c, sw_c);   // half 0 of pair 0, slot 0
+    // the half-0 bases move to slot 1 for the second sub-stage of pair 0
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        abase[0][kk] += PF_ATILE;
+        wbase[0][kk] += L::W_TILE;
+    }
 
+    int da = PF_ATILE, dw = L::W_TILE;   // slot step of the half-1 bases (the half-0 bases step by minus it)
     int pr = 0;
     for (; 2 * pr + 1 < nk; ++pr) {
-        sub(2 * pr, X, Y, false);
-        sub(2 * pr + 1, Y, X, true);
+        uint32_t sa_n, sw_n;
+        scale_base(pr + 1, sa_n, sw_n);
+        PfPairCopies cp;
+        sub(X, Y, false, 1, sa_c, sw_c, pr, cp);
+        sub(Y, X, true, 0, sa_n, sw_n, pr, cp);
+        sa_c = sa_n;
+        sw_c = sw_n;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            abase[1][kk] += da;
+            abase[0][kk] -= da;
+            wbase[1][kk] += dw;
+            wbase[0][kk] -= dw;
+        }
+        da = -da;
+        dw = -dw;
     }
-    if (2 * pr < nk) sub(2 * pr, X, Y, false);   // the half pair when K % 256 == 128
+    if (2 * pr < nk) {   // the half pair when K % 256 == 128
+        PfPairCopies cp;
+        sub(X, Y, false, 1, sa_c, sw_c, pr, cp);
+    }
     wait_vmcnt<0>();   // the trailing zero-fill copies have landed
     lds_barrier();     // every wave is done with the slots
 

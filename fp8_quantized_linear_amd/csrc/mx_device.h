@@ -204,7 +204,6 @@ __device__ __forceinline__ uint32_t e2m1_rne_ratio(double num, double den)
     return c;
 }
 
-// fp32 -> bf16, round to nearest even (finite inputs).
 // fp32 -> bf16, round to nearest even, on the hardware converter
 // (v_cvt_pk_bf16_f32).  For every finite input it equals the bit rule
 // (u + 0x7fff + ((u >> 16) & 1)) >> 16 (checked exhaustively over all 2^32
@@ -222,16 +221,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)
 // buffer at (voff + soff); lanes past the buffer's size read zero.  They are
 // issued from inline assembly, so the compiler does not count them: callers
 // wait with wait_vmcnt, whose count includes them, before a barrier that
-// publishes the data.
+// publishes the data.  A write of M0 needs one instruction between it and
+// the load that takes its LDS address from M0 (s_nop 0 here, the offset add
+// in the _at forms).
 __device__ __forceinline__ void dma_b128(uint32_t lds, int voff, const int4_t& rsrc, int soff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 __device__ __forceinline__ void dma_b32(uint32_t lds, int voff, const int4_t& rsrc, int soff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                  :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+// The same copies to LDS address lds + imm from buffer offset voff + sadd
+// (sadd uniform), in three instructions.  imm must fold to a constant once
+// the caller is inlined and unrolled.
+__device__ __forceinline__ void dma_b128_at(uint32_t lds, int imm, int voff, int sadd, const int4_t& rsrc)
+{
+    int off;
+    asm volatile("s_add_u32 m0, %1, %5\n\tv_add_u32 %0, %2, %3\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
+                 : "=&v"(off) : "s"(lds), "s"(sadd), "v"(voff), "s"(rsrc), "i"(imm) : "memory", "scc");
+}
+__device__ __forceinline__ void dma_b32_at(uint32_t lds, int imm, int voff, int sadd, const int4_t& rsrc)
+{
+    int off;
+    asm volatile("s_add_u32 m0, %1, %5\n\tv_add_u32 %0, %2, %3\n\tbuffer_load_dword %0, %4, 0 offen lds"
+                 : "=&v"(off) : "s"(lds), "s"(sadd), "v"(voff), "s"(rsrc), "i"(imm) : "memory", "scc");
 }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
