@@ -403,7 +403,10 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
             for (int c = 4; c < L::COPIES; ++c) copy(c, cp);
         }
     }
-    wait_vmcnt<0>();
+    // sub-stage 0 needs window 0 and pair 0; the copies of virtual pair -1
+    // (pair 1, piece 0 of window 1) may still be in flight, and the first
+    // second sub-stage waits for them
+    wait_vmcnt<L::COPIES>();
     lds_barrier();
     PfFrags<WFR> X, Y;
     uint32_t sa_c, sw_c;   // scale-read bases of the current pair
@@ -444,53 +447,87 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     wait_vmcnt<0>();   // the trailing zero-fill copies have landed
     lds_barrier();     // every wave is done with the slots
 
-    // Epilogue, one 32-row band (fragment row i) at a time through this
-    // wave's private LDS region: write the band row-major, read it back as
-    // whole row segments and store them with 16-byte stores.
+    // Epilogue, one 32-row band (fragment row i) at a time through two
+    // band buffers in this wave's private LDS region: band i + 1 is written
+    // row-major while band i is read back as whole row segments and stored
+    // with 16-byte stores.  A wave's LDS operations execute in order, so the
+    // reads see the writes issued before them and the writes of band i + 2
+    // come after the reads of band i in the same buffer.
     constexpr int ESZ = OUT_F32 ? 4 : 2;
     constexpr int WCOLS = BN / 2;                        // output columns of a wave
     constexpr int ROWB = WCOLS * ESZ + 16;               // padded LDS row
-    uint8_t* region = smem + wave * (32 * ROWB);
-    const bool vec_ok = (p.N % (16 / ESZ)) == 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    constexpr int BAND = 32 * ROWB;
+    static_assert(8 * BAND <= L::LDS, "epilogue buffers");
+    uint8_t* region = smem + wave * (2 * BAND);
+    constexpr int LPR = WCOLS * ESZ / 16;                // lanes per 16-byte-chunked row
+    constexpr int RPI = 64 / LPR;                        // rows per read instruction
+    const int lrow = lane / LPR, c16 = lane % LPR;
+    // full tiles with rows of whole 16-byte chunks store without checks, at
+    // a uniform band base plus a 32-bit per-lane offset
+    const bool full = m0 + PF_BM <= p.M && n0 + BN <= p.N && (p.N % (16 / ESZ)) == 0;
+    uint8_t* ywave = reinterpret_cast<uint8_t*>(p.y) + ((size_t)(m0 + wm * 128) * p.N + n0 + wn * WCOLS) * ESZ;
+    const uint32_t lane_off = (uint32_t)(lrow * p.N * ESZ + c16 * 16);
+
+    auto write_band = [&](int i) __attribute__((always_inline)) {
+        uint8_t* buf = region + (i & 1) * BAND;
 #pragma unroll
         for (int j = 0; j < WFR; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int col = j * 32 + q * 8 + g * 4;
-                uint8_t* dst = region + r32 * ROWB + col * ESZ;
                 if (OUT_F32) {
+                    uint8_t* dst = buf + r32 * ROWB + (j * 32 + q * 8 + g * 4) * ESZ;
                     *reinterpret_cast<float4_t*>(dst) =
                         float4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                } else {
-                    const uint32_t lo = bf16x2_rne(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-                    const uint32_t hi = bf16x2_rne(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+                } else if (q % 2 == 0) {
+                    // bf16: register groups q and q + 1 hold columns 8q + 4g .. +3 and
+                    // 8(q+1) + 4g .. +3.  Swapping the upper lane half of group q
+                    // with the lower half of group q + 1 leaves lane (r, g) with the
+                    // 8 consecutive columns 8(q + g) .. +7 of row r: one 16-byte
+                    // write, which the padded rows keep free of bank conflicts.
+                    const uint32_t a0 = bf16x2_rne(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+                    const uint32_t a1 = bf16x2_rne(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    const uint32_t b0 = bf16x2_rne(acc[i][j][4 * q + 4], acc[i][j][4 * q + 5]);
+                    const uint32_t b1 = bf16x2_rne(acc[i][j][4 * q + 6], acc[i][j][4 * q + 7]);
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+                    uint8_t* dst = buf + r32 * ROWB + (j * 32 + (q + g) * 8) * ESZ;
+                    *reinterpret_cast<int4_t*>(dst) = int4_t{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
                 }
             }
-        constexpr int LPR = WCOLS * ESZ / 16;              // lanes per 16-byte-chunked row
-        constexpr int RPI = 64 / LPR;                      // rows per read instruction
+    };
+    write_band(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i + 1 < 4) write_band(i + 1);
+        const uint8_t* buf = region + (i & 1) * BAND;
+        int4_t v[32 / RPI];
+#pragma unroll
+        for (int t = 0; t < 32 / RPI; ++t) v[t] = *reinterpret_cast<const int4_t*>(buf + (t * RPI + lrow) * ROWB + c16 * 16);
+        if (full) {
+#pragma unroll
+            for (int t = 0; t < 32 / RPI; ++t) {
+                uint8_t* yb = ywave + (size_t)(i * 32 + t * RPI) * p.N * ESZ;
+                __builtin_nontemporal_store(v[t], reinterpret_cast<int4_t*>(yb + lane_off));
+            }
+            continue;
+        }
 #pragma unroll
         for (int t = 0; t < 32 / RPI; ++t) {
-            const int row = t * RPI + lane / LPR, c16 = lane % LPR;
-            const uint4 v = *reinterpret_cast<const uint4*>(region + row * ROWB + c16 * 16);
+            const int row = t * RPI + lrow;
             const int m = m0 + wm * 128 + i * 32 + row;
             const int n = n0 + wn * WCOLS + c16 * (16 / ESZ);
-            if (m < p.M) {
-                uint8_t* yrow = reinterpret_cast<uint8_t*>(p.y) + ((size_t)m * p.N) * ESZ;
-                if (vec_ok && n + 16 / ESZ <= p.N) {
-                    const int4_t iv = int4_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-                    __builtin_nontemporal_store(iv, reinterpret_cast<int4_t*>(yrow + (size_t)n * ESZ));
-                } else {
+            if (m >= p.M) continue;
+            uint8_t* yrow = reinterpret_cast<uint8_t*>(p.y) + ((size_t)m * p.N) * ESZ;
+            if ((p.N % (16 / ESZ)) == 0 && n + 16 / ESZ <= p.N) {
+                __builtin_nontemporal_store(v[t], reinterpret_cast<int4_t*>(yrow + (size_t)n * ESZ));
+            } else {
 #pragma unroll
-                    for (int e = 0; e < 16 / ESZ; ++e) {
-                        const int wi = OUT_F32 ? e : e / 2;
-                        const uint32_t word = wi == 0 ? v.x : wi == 1 ? v.y : wi == 2 ? v.z : v.w;
-                        if (n + e < p.N) {
-                            if (OUT_F32) reinterpret_cast<uint32_t*>(yrow)[n + e] = word;
-                            else reinterpret_cast<uint16_t*>(yrow)[n + e] = (uint16_t)(word >> (16 * (e % 2)));
-                        }
+                for (int e = 0; e < 16 / ESZ; ++e) {
+                    const int wi = OUT_F32 ? e : e / 2;
+                    const uint32_t word = (uint32_t)v[t][wi];
+                    if (n + e < p.N) {
+                        if (OUT_F32) reinterpret_cast<uint32_t*>(yrow)[n + e] = word;
+                        else reinterpret_cast<uint16_t*>(yrow)[n + e] = (uint16_t)(word >> (16 * (e % 2)));
                     }
                 }
             }
