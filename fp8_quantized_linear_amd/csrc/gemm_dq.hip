@@ -119,7 +119,15 @@ struct DqArgs {
 // FUSED_A (MXFP8 only): A arrives as bf16 [M, K]; each 8-element chunk is
 // quantized in registers (block-32 scale by A_RULE over a lane quad, E4M3
 // codes) and dequantized back exactly, as mx_quantize_act would have done.
-template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL>
+// ODD16 (NVFP4 with K % 32 == 16): rows are only 8-byte aligned and the
+// last chunk of a row holds a single block of 16 elements.  SCW (NVFP4 with
+// K % 64 == 0, MXFP8 with K % 128 == 0): scale bytes are fetched as the
+// aligned dword of the row that holds them (NVFP4: the stage's 4 scales,
+// MXFP8: the 2 stages' 2 + 2) and extracted when the chunk is dequantized;
+// the compiler waits for a byte load's zero extension right after the load,
+// a dword needs none.
+template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL,
+          bool ODD16 = false, bool SCW = false>
 __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
 {
     using T = DqTraits<KIND>;
@@ -144,59 +152,74 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
     const int row_bytes = KIND == DQ_NVFP4 ? K / 2 : K;
     const int nk = (K + DQ_BK - 1) / DQ_BK;
 
-    uint4 ra[A_PER_T], rw[W_PER_T];
-    uint32_t sa[A_PER_T], sw[W_PER_T];  // scale bytes of the chunk (NVFP4: two, MXFP8: one)
+    // two register sets of staged chunks: stage kt lives in set kt % 2.
+    // Loads are branch-free and nothing loaded is used before the chunk is
+    // dequantized, so a stage's loads stay in flight through the compute of
+    // the stage before: an out-of-range chunk or scale byte is loaded from
+    // the operand's first byte instead and dropped by its flag.
+    uint4 ra[2][A_PER_T], rw[2][W_PER_T];
+    uint32_t sa[2][A_PER_T][2], sw[2][W_PER_T][2];   // scale bytes of the chunk (MXFP8: one)
+    uint32_t fa[2][A_PER_T], fw[2][W_PER_T];         // flags: 1 chunk, 2 its second 8 bytes, 4 second scale
 
     auto load_one = [&](const uint8_t* q, const uint8_t* s, int rows_lim, int r0, int qi, int kt,
-                        uint4& v, uint32_t& sc) {
+                        uint4& v, uint32_t* sc, uint32_t& fl) __attribute__((always_inline)) {
         const int row = qi / T::CHUNKS, c = qi % T::CHUNKS;
         const int gr = r0 + row;
         const int kb = kt * T::SRC_ROW_BYTES + c * 16;
-        v = make_uint4(0, 0, 0, 0);
-        sc = KIND == DQ_NVFP4 ? 0u : 127u;
-        if (gr < rows_lim && kb < row_bytes) {
-            const uint8_t* src = q + (size_t)gr * row_bytes + kb;
-            if ((row_bytes & 15) == 0) {
-                v = *reinterpret_cast<const uint4*>(src);
-            } else {
-                // NVFP4 with k % 32 == 16: rows are 8-byte aligned and the last
-                // chunk of a row holds a single block of 16 elements
-                const uint2 lo = *reinterpret_cast<const uint2*>(src);
-                const uint2 hi = kb + 8 < row_bytes ? *reinterpret_cast<const uint2*>(src + 8) : make_uint2(0, 0);
-                v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            }
-            if (KIND == DQ_NVFP4) {
-                const int blk = kt * (DQ_BK / 16) + c * 2;
-                sc = (uint32_t)s[(size_t)gr * KS + blk];
-                if (blk + 1 < KS) sc |= (uint32_t)s[(size_t)gr * KS + blk + 1] << 8;
-            } else {
-                sc = (uint32_t)s[(size_t)gr * KS + (kt * DQ_BK + c * 16) / 32];
-            }
+        const bool ok = gr < rows_lim && kb < row_bytes;
+        const size_t rb = ok ? (size_t)gr * row_bytes + kb : 0;
+        if (!ODD16) {
+            v = *reinterpret_cast<const uint4*>(q + rb);
+            fl = ok ? 3u : 0u;
+        } else {
+            const bool ok_hi = ok && kb + 8 < row_bytes;
+            const uint2 lo = *reinterpret_cast<const uint2*>(q + rb);
+            const uint2 hi = *reinterpret_cast<const uint2*>(q + (ok_hi ? rb + 8 : 0));
+            v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            fl = (ok ? 1u : 0u) | (ok_hi ? 2u : 0u);
+        }
+        if (SCW) {
+            const size_t so = KIND == DQ_NVFP4 ? (size_t)gr * KS + kt * 4 : (size_t)gr * KS + (kt >> 1) * 4;
+            sc[0] = *reinterpret_cast<const uint32_t*>(s + (ok ? so : 0));
+            fl |= ok ? 4u : 0u;
+        } else if (KIND == DQ_NVFP4) {
+            const int blk = kt * (DQ_BK / 16) + c * 2;
+            const bool ok1 = ok && blk + 1 < KS;
+            sc[0] = s[ok ? (size_t)gr * KS + blk : 0];
+            sc[1] = s[ok1 ? (size_t)gr * KS + blk + 1 : 0];
+            fl |= ok1 ? 4u : 0u;
+        } else {
+            sc[0] = s[ok ? (size_t)gr * KS + (kt * DQ_BK + c * 16) / 32 : 0];
         }
     };
-    auto load_stage = [&](int kt) {
+    auto load_stage = [&](int kt, int set) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < A_PER_T; ++i) {
             const int qi = tid + i * NT;
             if (FUSED_A) {
                 const int row = qi / A_CPR, c = qi % A_CPR, gm = m0 + row;
                 const int kb = kt * DQ_BK * 2 + c * 16;
-                ra[i] = make_uint4(0, 0, 0, 0);
-                if (gm < p.M && kb < K * 2)
-                    ra[i] = *reinterpret_cast<const uint4*>(p.a_q + (size_t)gm * K * 2 + kb);
-            } else if (qi < A_CH) {
-                load_one(p.a_q, p.a_s, p.M, m0, qi, kt, ra[i], sa[i]);
+                const bool ok = gm < p.M && kb < K * 2;
+                ra[set][i] = *reinterpret_cast<const uint4*>(p.a_q + (ok ? (size_t)gm * K * 2 + kb : 0));
+                fa[set][i] = ok ? 3u : 0u;
+            } else if (A_CH % NT == 0 || qi < A_CH) {
+                load_one(p.a_q, p.a_s, p.M, m0, qi, kt, ra[set][i], sa[set][i], fa[set][i]);
             }
         }
 #pragma unroll
         for (int i = 0; i < W_PER_T; ++i) {
             const int qi = tid + i * NT;
-            if (qi < W_CH) load_one(p.w_q, p.w_s, p.N, n0, qi, kt, rw[i], sw[i]);
+            if (W_CH % NT == 0 || qi < W_CH) load_one(p.w_q, p.w_s, p.N, n0, qi, kt, rw[set][i], sw[set][i], fw[set][i]);
         }
     };
-    auto store_one = [&](uint8_t* tile, int qi, const uint4& v, uint32_t sc) {
+    auto store_one = [&](uint8_t* tile, int qi, uint4 v, const uint32_t* scb, uint32_t fl, int par)
+                         __attribute__((always_inline)) {
         const int row = qi / T::CHUNKS, c = qi % T::CHUNKS;
+        if (!(fl & 1u)) v = make_uint4(0, 0, 0, 0);
+        if (!(fl & 2u)) v.z = v.w = 0;
         if (KIND == DQ_NVFP4) {
+            const uint32_t sc = SCW ? (fl & 1u ? __builtin_amdgcn_ubfe(scb[0], 16 * c, 16) : 0u)
+                                    : (fl & 1u ? scb[0] : 0u) | (fl & 4u ? scb[1] << 8 : 0u);
             const _Float16 s0 = e4m3_to_f16(sc & 0xFFu), s1 = e4m3_to_f16((sc >> 8) & 0xFFu);
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -206,14 +229,15 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
                 *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + chunk * 16) = d;
             }
         } else {
-            const int e = (int)sc - 127;
+            const uint32_t sb = SCW ? __builtin_amdgcn_ubfe(scb[0], 16 * par + 8 * (c >> 1), 8) : scb[0];
+            const int e = (fl & 1u ? (int)sb : 127) - 127;
             const uint4 d0 = dequant8_mxfp8(make_uint2(v.x, v.y), e);
             const uint4 d1 = dequant8_mxfp8(make_uint2(v.z, v.w), e);
             *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + (((2 * c) ^ dq_swz(row)) * 16)) = d0;
             *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + (((2 * c + 1) ^ dq_swz(row)) * 16)) = d1;
         }
     };
-    auto store_stage = [&](int buf) {
+    auto store_stage = [&](int buf, int set) __attribute__((always_inline)) {
         uint8_t* a_t = smem + buf * STAGE;
         uint8_t* w_t = a_t + A_TILE;
 #pragma unroll
@@ -222,18 +246,19 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
             if (FUSED_A) {
                 // 8 bf16 per lane; a lane quad holds one block of 32
                 const int row = qi / A_CPR, c = qi % A_CPR;
-                const uint32_t amax = quad_max_u32(amax_bits8(ra[i]));
+                const uint4 x = fa[set][i] ? ra[set][i] : make_uint4(0, 0, 0, 0);
+                const uint32_t amax = quad_max_u32(amax_bits8(x));
                 const int e = scale_exponent<ELEM_E4M3, A_RULE>(amax);
-                const uint4 d = dequant8_mxfp8(encode8_e4m3(ra[i], e), e);
+                const uint4 d = dequant8_mxfp8(encode8_e4m3(x, e), e);
                 *reinterpret_cast<uint4*>(a_t + row * DQ_ROW_BYTES + ((c ^ dq_swz(row)) * 16)) = d;
-            } else if (qi < A_CH) {
-                store_one(a_t, qi, ra[i], sa[i]);
+            } else if (A_CH % NT == 0 || qi < A_CH) {
+                store_one(a_t, qi, ra[set][i], sa[set][i], fa[set][i], set);
             }
         }
 #pragma unroll
         for (int i = 0; i < W_PER_T; ++i) {
             const int qi = tid + i * NT;
-            if (qi < W_CH) store_one(w_t, qi, rw[i], sw[i]);
+            if (W_CH % NT == 0 || qi < W_CH) store_one(w_t, qi, rw[set][i], sw[set][i], fw[set][i], set);
         }
     };
 
@@ -281,16 +306,29 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
         }
     };
 
-    load_stage(0);
-    store_stage(0);
+    // Stage kt is loaded into register set kt % 2 two stages ahead of its
+    // compute: loads of stage kt + 2 go out before the compute of stage kt,
+    // and stage kt + 1 (loaded one iteration earlier) is dequantized into
+    // LDS after it.  The loop is unrolled by two so that the sets are static,
+    // and both steps run unconditionally (stages past K load nothing and
+    // dequantize to zeros in the buffer no later stage reads), so the
+    // compiler's waits count exactly the loads of stage kt + 2 as newer.
+    load_stage(0, 0);
+    load_stage(1, 1);
+    store_stage(0, 0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        if (more) load_stage(kt + 1);
-        compute_stage(kt & 1);
-        if (more) store_stage((kt + 1) & 1);
+    auto iter = [&](int kt, int set) __attribute__((always_inline)) {
+        load_stage(kt + 2, set);
+        compute_stage(set);
+        store_stage(set ^ 1, set ^ 1);
         __syncthreads();
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        iter(kt, 0);
+        iter(kt + 1, 1);
     }
+    if (kt < nk) iter(kt, 0);
 
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -312,11 +350,12 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
         }
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL>
-hipError_t launch_dq(const DqArgs& a, hipStream_t stream)
+template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL,
+          bool ODD16 = false, bool SCW = false>
+hipError_t launch_dq_k(const DqArgs& a, hipStream_t stream)
 {
     constexpr int LDS = 2 * (BM + BN) * DQ_ROW_BYTES;
-    auto kern = dq_gemm_kernel<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE>;
+    auto kern = dq_gemm_kernel<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, ODD16, SCW>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
@@ -326,6 +365,18 @@ hipError_t launch_dq(const DqArgs& a, hipStream_t stream)
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     hipLaunchKernelGGL(kern, dim3(tiles), dim3(WM * WN * 64), LDS, stream, a);
     return hipGetLastError();
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL>
+hipError_t launch_dq(const DqArgs& a, hipStream_t stream)
+{
+    if constexpr (KIND == DQ_NVFP4) {
+        if (a.K % 32 != 0) return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, true, false>(a, stream);
+        if (a.K % 64 == 0) return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, true>(a, stream);
+    } else if (!FUSED_A) {
+        if (a.K % 128 == 0) return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, true>(a, stream);
+    }
+    return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, false>(a, stream);
 }
 
 } // namespace mxl

@@ -233,7 +233,9 @@ def nv_case(a_bits, w_bits, g_a, g_w, out_f32=False):
     return y, (aq, as_), (wq, ws)
 
 
-@pytest.mark.parametrize("m,k,n", [(16, 256, 256), (200, 400, 300), (1, 16, 1), (130, 5120, 96)])
+# K % 64 == 0 (scales fetched as row dwords), K % 64 == 32 (byte scales),
+# K % 32 == 16 (8-byte aligned rows, a last half chunk)
+@pytest.mark.parametrize("m,k,n", [(16, 256, 256), (200, 400, 300), (1, 16, 1), (130, 5120, 96), (64, 288, 100)])
 def test_nvfp4_full_small(m, k, n):
     a_bits = W.normal_bf16(m, k, 1.0, 0)
     w_bits = W.normal_bf16(n, k, 0.02, 1)
