@@ -235,6 +235,32 @@ def mx_gemm(a_elem, aq, a_s, w_elem, wq, w_s, m: int, n: int, k: int, nthreads=N
     return y, sa
 
 
+def bf16_to_f64(x_bf16: np.ndarray) -> np.ndarray:
+    """Exact values of bf16 bit patterns [rows, k]: a bf16 is the upper half
+    of an fp32."""
+    x = _u16(x_bf16)
+    return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def w4a16_gemm(a_bf16, wq, w_s, n: int, k: int, fmt: str = "mxfp4", g_w=None, nthreads=None):
+    """Weight-only quantized linear (W4A16): the bf16 activations as they are
+    times the dequantized packed weights, in fp64.  One packed artifact serves
+    W4A4 and W4A16 (Qwen3.5-27B-MXFP4-QAD-W4A4-LR1e-5-s1000, introduction),
+    and the NVFP4 weight-only checkpoint keeps its activations in bf16 with
+    weight bytes identical to the W4A4 sibling
+    (Qwen3.5-27B-NVFP4-RTN-weight-only, introduction).  MXFP4 weights
+    dequantize as e2m1 * 2^(s - 127), NVFP4 weights as e2m1 * s_e4m3 / g_w.
+    Returns (y, S) as gemm_dq does."""
+    a = bf16_to_f64(a_bf16)
+    if fmt == "nvfp4":
+        wd = nv_dequantize(wq, w_s, n, k, g_w, nthreads)
+    elif fmt == "mxfp4":
+        wd = mx_dequantize("e2m1", wq, w_s, n, k, nthreads)
+    else:
+        raise ValueError("W4A16 weights are mxfp4 or nvfp4")
+    return gemm_dq(a, wd, nthreads)
+
+
 # ---------------------------------------------------------------- compositions
 def mx_linear(a_bf16, w_bf16, a_elem="e2m1", w_elem="e2m1", a_rule="ceil", w_rule="even",
               nthreads=None):

@@ -459,3 +459,76 @@ def test_quantization_error_bound_end_to_end():
     d = oracle.mx_dequantize("e2m1", q, s, 8, 128)
     bound = np.repeat(2.0 ** (s.astype(np.float64) - 127), 32, axis=1)
     assert (np.abs(d - a.double().numpy()) <= bound).all()
+
+
+# ------------------------------------------------------------------ W4A16
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("fmt,k", [("mxfp4", 64), ("nvfp4", 48)])
+def test_w4a16_bruteforce_tiny(fmt, k):
+    # every term decoded on its own (torch for bf16 and E4M3, the OCP lattice
+    # file for E2M1) and summed in exact rationals
+    rng = np.random.default_rng(31)
+    m, n = 3, 2   # distinct sizes: a transposed operand cannot pass
+    ab = _bf16_bits(rng.standard_normal((m, k)) * 4)
+    wq = rng.integers(0, 256, (n, k // 2)).astype(np.uint8)
+    if fmt == "mxfp4":
+        ws = rng.integers(118, 136, (n, k // 32)).astype(np.uint8)
+        g = None
+    else:
+        ws = rng.integers(0x20, 0x60, (n, k // 16)).astype(np.uint8)
+        g = np.float32(3.0)
+    y, sa = oracle.w4a16_gemm(ab, wq, ws, n, k, fmt, g)
+    av = torch.from_numpy(ab.view(np.int16)).view(torch.bfloat16).double().numpy()
+    e4 = torch_e4m3_table()
+    for i in range(m):
+        for j in range(n):
+            acc, aabs = F(0), F(0)
+            for t in range(k):
+                code = (int(wq[j, t // 2]) >> (4 * (t % 2))) & 0xF
+                if fmt == "mxfp4":
+                    wv = F(LAT[code]) * F(2) ** (int(ws[j, t // 32]) - 127)
+                else:
+                    wv = F(LAT[code]) * F(float(e4[ws[j, t // 16]])) / F(float(g))
+                term = F(float(av[i, t])) * wv
+                acc += term
+                aabs += abs(term)
+            # fp64 dequantization (NVFP4 divides by g) and summation round
+            # at most a few ulps of the absolute sum
+            assert abs(F(y[i, j]) - acc) <= aabs * F(1, 2 ** 46) + F(1, 2 ** 1000)
+            assert abs(F(sa[i, j]) - aabs) <= aabs * F(1, 2 ** 46) + F(1, 2 ** 1000)
+
+
+def test_w4a16_equals_w4a4_on_representable_activations():
+    # activations that are already dequantized MXFP4 values (exact in bf16)
+    # give the W4A4 product of their codes
+    rng = np.random.default_rng(32)
+    m, n, k = 5, 7, 128
+    ab = _bf16_bits(rng.standard_normal((m, k)))
+    wb = _bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    aq, a_s = oracle.mx_quantize("e2m1", "ceil", ab)
+    wq, ws = oracle.mx_quantize("e2m1", "even", wb)
+    ad = oracle.mx_dequantize("e2m1", aq, a_s, m, k)
+    ad_bits = _bf16_bits(ad)
+    assert np.array_equal(oracle.bf16_to_f64(ad_bits), ad)   # exact in bf16
+    y16, s16 = oracle.w4a16_gemm(ad_bits, wq, ws, n, k, "mxfp4")
+    y4, s4 = oracle.mx_gemm("e2m1", aq, a_s, "e2m1", wq, ws, m, n, k)
+    np.testing.assert_allclose(y16, y4, rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(s16, s4, rtol=1e-13)
+
+
+def test_w4a16_nvfp4_closed_form():
+    # every weight element 1.0 (E2M1 code 2) with E4M3 scale 1.0 (0x38) and
+    # g_w = 4: each output is sum_k a / 4
+    rng = np.random.default_rng(33)
+    m, n, k = 4, 3, 80
+    ab = _bf16_bits(rng.standard_normal((m, k)))
+    wq = np.full((n, k // 2), 0x22, np.uint8)
+    ws = np.full((n, k // 16), 0x38, np.uint8)
+    y, sa = oracle.w4a16_gemm(ab, wq, ws, n, k, "nvfp4", np.float32(4.0))
+    av = oracle.bf16_to_f64(ab)
+    for j in range(n):
+        np.testing.assert_allclose(y[:, j], av.sum(axis=1) / 4, rtol=1e-14)
+        np.testing.assert_allclose(sa[:, j], np.abs(av).sum(axis=1) / 4, rtol=1e-14)
