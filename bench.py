@@ -293,7 +293,59 @@ def extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_d
                                     "kernel": mxl.mx_gemm_plan("mxfp4", "mxfp4", cfg.m, cfg.n, cfg.k)}
         log(f"decode m={cfg.m}: {med * 1e3:.2f} us {gbs:.0f} GB/s")
         del graph
-    del wcopies
+
+    # W4A16 (weight-only) decode on the same shapes: bf16 activations times
+    # the MXFP4 copies above, then times NVFP4 packings of the same weights
+    def graph_rows(call, name, nbytes, plan, m):
+        yd = call(10).clone()
+        ref = yd.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(3):
+                call(i, yd)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(11):
+                call(i, yd)
+        torch.cuda.synchronize()
+        times = []
+        for rep in range(25):
+            yd.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            if not torch.equal(yd, ref):
+                raise RuntimeError(f"{name}: graph replay {rep} differs from the eager result")
+            times.append(e0.elapsed_time(e1) / 11)
+        t = np.array(times[3:])
+        med, p10, p90 = float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+        gbs = nbytes / (med * 1e-3) / 1e9
+        rows[name] = {"us": round(med * 1e3, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
+                      "GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 3), "bytes": nbytes,
+                      "timing": "HIP graph of 11 back-to-back calls (one per weight copy), replayed",
+                      "kernel": plan}
+        log(f"{name}: {med * 1e3:.2f} us {gbs:.0f} GB/s")
+
+    w_bits_dev = to_dev(dec.weights())
+    g_w = mxl.mx_nv_global_scale(float(mxl.mx_tensor_amax(w_bits_dev).item()))
+    nq0, ns0 = mxl.mx_pack_weights(w_bits_dev, "nvfp4", global_scale=g_w)
+    del w_bits_dev
+    ncopies = [(nq0, ns0)] + [(nq0.clone(), ns0.clone()) for _ in range(10)]
+    alpha_nv = float(np.float32(1.0) / np.float32(g_w))
+    for cfg in [c for c in W.DECODE if c.m <= 16]:
+        a = to_dev(cfg.activations())
+        for fmt, copies, alpha in (("mxfp4", wcopies, 1.0), ("nvfp4", ncopies, alpha_nv)):
+            def call(i, y=None, fmt=fmt, copies=copies, alpha=alpha, a=a):
+                return mxl.mx_gemm_w4a16(a, copies[i][0], copies[i][1], fmt, alpha, y=y)
+            kb = cfg.k // (16 if fmt == "nvfp4" else 32)
+            nbytes = cfg.n * (cfg.k // 2 + kb) + cfg.m * cfg.k * 2 + cfg.m * cfg.n * 2
+            graph_rows(call, f"w4a16_{fmt}_decode_m{cfg.m}", nbytes,
+                       mxl.mx_gemm_w4a16_plan(fmt, cfg.m, cfg.n, cfg.k), cfg.m)
+    del wcopies, ncopies
 
     # NVFP4 W4A4
     nv = W.NVFP4

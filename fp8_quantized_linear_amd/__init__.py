@@ -54,6 +54,10 @@ def _load():
     L.mx_gemm_fused.argtypes = [i32, i32, P, i32, P, P, i64, i64, i64, P, u32, P, sz, P]
     L.nv_gemm.restype = i32
     L.nv_gemm.argtypes = [P, P, P, P, i64, i64, i64, f32, P, u32, P, sz, P]
+    L.mx_gemm_w4a16.restype = i32
+    L.mx_gemm_w4a16.argtypes = [i32, P, P, P, i64, i64, i64, f32, P, u32, P, sz, P]
+    L.mx_gemm_w4a16_plan.restype = i32
+    L.mx_gemm_w4a16_plan.argtypes = [i32, i64, i64, i64, ctypes.c_char_p, sz]
     L.mx_tensor_amax.restype, L.mx_tensor_amax.argtypes = i32, [P, i64, P, P]
     L.mx_nv_global_scale.restype, L.mx_nv_global_scale.argtypes = f32, [f32]
     L.mx_gemm_plan.restype = i32
@@ -192,6 +196,33 @@ def nv_gemm(a_q, a_s, w_q, w_s, k: int, alpha: float, out_f32: bool = False, y=N
                      MX_OUT_F32 if out_f32 else 0, None, 0, _stream(a_q))
     _check(st, "nv_gemm")
     return y
+
+
+def mx_gemm_w4a16(a: torch.Tensor, w_q, w_s, w_fmt: str = "mxfp4", alpha: float = 1.0,
+                  out_f32: bool = False, y=None):
+    """Weight-only quantized linear (W4A16): Y = alpha * A_bf16 dq(W)^T with
+    MXFP4 (E8M0 per 32) or NVFP4 (E4M3 per 16; alpha = 1 / g_w) weights."""
+    _need(a, torch.bfloat16, "a")
+    _need(w_q, torch.uint8, "w_q")
+    _need(w_s, torch.uint8, "w_s")
+    if w_fmt not in ("mxfp4", "nvfp4"):
+        raise ValueError("W4A16 weights are mxfp4 or nvfp4")
+    m, k = a.shape
+    n = w_q.shape[0]
+    if w_q.shape[1] != k // 2 or w_s.shape != (n, scales_per_row(w_fmt, k)):
+        raise ValueError("weight tensors do not match k")
+    y = _gemm_out(m, n, a.device, out_f32, y)
+    st = lib.mx_gemm_w4a16(_fmt(w_fmt), _ptr(a), _ptr(w_q), _ptr(w_s), m, n, k, float(alpha), _ptr(y),
+                           MX_OUT_F32 if out_f32 else 0, None, 0, _stream(a))
+    _check(st, "mx_gemm_w4a16")
+    return y
+
+
+def mx_gemm_w4a16_plan(w_fmt: str, m: int, n: int, k: int) -> str:
+    """Name of the kernel mx_gemm_w4a16 would launch for this shape."""
+    buf = ctypes.create_string_buffer(256)
+    _check(lib.mx_gemm_w4a16_plan(_fmt(w_fmt), m, n, k, buf, 256), "mx_gemm_w4a16_plan")
+    return buf.value.decode()
 
 
 def mx_tensor_amax(x: torch.Tensor) -> torch.Tensor:

@@ -33,6 +33,13 @@ hipError_t mxl_launch_mxfp8_exact_gemm(const void* aq, const void* as, const voi
 hipError_t mxl_launch_mxfp8_exact_gemm_fused(int a_rule, const void* a_bf16, const void* wq, const void* ws,
                                              int64_t m, int64_t n, int64_t k, void* y, int out_f32,
                                              hipStream_t stream);
+hipError_t mxl_launch_w4a16_gemm(int w_nv, const void* a_bf16, const void* wq, const void* ws, int64_t m,
+                                 int64_t n, int64_t k, float alpha, void* y, int out_f32, hipStream_t stream);
+hipError_t mxl_launch_w4a16_decode(int w_nv, const void* a_bf16, const void* wq, const void* ws, int64_t m,
+                                   int64_t n, int64_t k, float alpha, void* y, int out_f32, hipStream_t stream);
+int mxl_w4a16_decode_ok(int w_nv, int64_t m, int64_t k);
+const char* mxl_w4a16_gemm_config_name(void);
+const char* mxl_w4a16_decode_config_name(void);
 const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n, int64_t k, int fused);
 const char* mxl_nv_gemm_config_name(void);
 const char* mxl_mxfp8_exact_config_name(void);
@@ -109,6 +116,13 @@ mx_status check_gemm_shape(int64_t m, int64_t n, int64_t k, int block)
 }
 
 int bits_of(mx_format f) { return f == MX_FMT_MXFP8 ? 8 : 4; }
+
+// W4A16: the decode kernel takes M <= 16 with K % 512 == 0 when its W block
+// fits LDS and W's bytes stay within 32-bit buffer offsets
+bool w4a16_use_decode(bool nv, int64_t m, int64_t n, int64_t k)
+{
+    return mxl_w4a16_decode_ok(nv ? 1 : 0, m, k) && (n + 16) * (k / 2) < ((int64_t)1 << 31);
+}
 
 } // namespace
 
@@ -209,6 +223,41 @@ mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void*
     if ((st = check_device()) != MX_OK) return st;
     return from_hip(mxl_launch_nv_gemm(a_q, a_s, w_q, w_s, m, n, k, alpha, y, (flags & MX_OUT_F32) ? 1 : 0,
                                        static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_gemm_w4a16(mx_format w_fmt, const void* a_bf16, const void* w_q, const void* w_s, int64_t m,
+                        int64_t n, int64_t k, float alpha, void* y, unsigned flags, void* workspace,
+                        size_t ws_bytes, mx_stream_t stream)
+{
+    (void)workspace;
+    (void)ws_bytes;
+    if (!valid_fmt(w_fmt)) return MX_ERR_INVALID_ARG;
+    if (w_fmt == MX_FMT_MXFP8) return MX_ERR_UNSUPPORTED;
+    if (!a_bf16 || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
+    if (flags & ~MX_OUT_F32) return MX_ERR_INVALID_ARG;
+    if (!std::isfinite(alpha)) return MX_ERR_INVALID_ARG;
+    const bool nv = w_fmt == MX_FMT_NVFP4;
+    mx_status st = check_gemm_shape(m, n, k, nv ? 16 : 32);
+    if (st != MX_OK) return st;
+    if (!aligned16(a_bf16) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y)) return MX_ERR_ALIGN;
+    if ((st = check_device()) != MX_OK) return st;
+    const int f32 = (flags & MX_OUT_F32) ? 1 : 0;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (w4a16_use_decode(nv, m, n, k))
+        return from_hip(mxl_launch_w4a16_decode(nv ? 1 : 0, a_bf16, w_q, w_s, m, n, k, alpha, y, f32, hs));
+    return from_hip(mxl_launch_w4a16_gemm(nv ? 1 : 0, a_bf16, w_q, w_s, m, n, k, alpha, y, f32, hs));
+}
+
+mx_status mx_gemm_w4a16_plan(mx_format w_fmt, int64_t m, int64_t n, int64_t k, char* name, size_t len)
+{
+    if (!valid_fmt(w_fmt) || !name || len == 0) return MX_ERR_INVALID_ARG;
+    if (w_fmt == MX_FMT_MXFP8) return MX_ERR_UNSUPPORTED;
+    const bool nv = w_fmt == MX_FMT_NVFP4;
+    mx_status st = check_gemm_shape(m, n, k, nv ? 16 : 32);
+    if (st != MX_OK) return st;
+    std::snprintf(name, len, "w4a16 %s %s", nv ? "nvfp4" : "mxfp4",
+                  w4a16_use_decode(nv, m, n, k) ? mxl_w4a16_decode_config_name() : mxl_w4a16_gemm_config_name());
+    return MX_OK;
 }
 
 mx_status mx_tensor_amax(const void* x_bf16, int64_t count, float* amax_dev, mx_stream_t stream)

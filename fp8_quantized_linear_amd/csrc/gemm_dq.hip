@@ -5,11 +5,16 @@
 //   NVFP4: Y = alpha * sum_k (e2m1_a * s_a) * (e2m1_w * s_w), E4M3 scale per 16,
 //          alpha = 1 / (g_a * g_w)                                   -> f16
 //   MXFP8: Y = sum_k (e4m3_a * 2^ea) * (e4m3_w * 2^ew), E8M0 scale per 32 -> bf16
+//   W4A16: Y = alpha * sum_k a_bf16 * dq(w), w MXFP4 (e2m1 * 2^ew, alpha = 1)
+//          or NVFP4 (e2m1 * s_w, alpha = 1 / g_w)                    -> bf16
 //
 // Operations: the NVFP4 W4A4 path of Qwen3.5-27B-NVFP4-GPTQ and
 // Qwen3.5-27B-NVFP4-RTN-weight-only (introductions: FP4 elements, per-block
 // scales, per-tensor global scales), and the MXFP8 W8A8 attention projections
-// of Qwen3.8-27B-MXFP8Attn-MXFP4MLP-lmheadMXFP4 (introduction, section 2).
+// of Qwen3.8-27B-MXFP8Attn-MXFP4MLP-lmheadMXFP4 (introduction, section 2);
+// the weight-only mode that the same packed weights serve with bf16
+// activations (Qwen3.5-27B-MXFP4-QAD-W4A4-LR1e-5-s1000 and
+// Qwen3.5-27B-NVFP4-RTN-weight-only, introductions).
 //
 // Why these do not use the block-scaled FP4/FP8 matrix cores:
 //  - NVFP4 scales are E4M3 per 16 elements; the scaled instructions accept
@@ -30,7 +35,7 @@
 
 namespace mxl {
 
-enum : int { DQ_NVFP4 = 0, DQ_MXFP8 = 1 };
+enum : int { DQ_NVFP4 = 0, DQ_MXFP8 = 1, DQ_MXFP4 = 2 };   // format of W (and of A unless A is bf16)
 
 constexpr int DQ_BK = 64;                 // K elements per LDS stage
 constexpr int DQ_ROW_BYTES = DQ_BK * 2;   // 16-bit bytes per LDS row per stage (8 chunks)
@@ -40,9 +45,9 @@ __device__ __forceinline__ int dq_swz(int row) { return row & 7; }
 template <int KIND>
 struct DqTraits {
     // global bytes of one row per stage, 16-byte chunks per row per stage
-    static constexpr int SRC_ROW_BYTES = KIND == DQ_NVFP4 ? DQ_BK / 2 : DQ_BK;
+    static constexpr int SRC_ROW_BYTES = KIND == DQ_MXFP8 ? DQ_BK : DQ_BK / 2;
     static constexpr int CHUNKS = SRC_ROW_BYTES / 16;
-    static constexpr int ELEMS_PER_CHUNK = KIND == DQ_NVFP4 ? 32 : 16;
+    static constexpr int ELEMS_PER_CHUNK = KIND == DQ_MXFP8 ? 16 : 32;
     static constexpr int SCALE_BLOCK = KIND == DQ_NVFP4 ? 16 : 32;
 };
 
@@ -108,6 +113,48 @@ __device__ __forceinline__ uint4 dequant8_mxfp8(uint2 codes, int e)
     return out;
 }
 
+// 8 E2M1 codes (one dword) times 2^e, as 8 bf16 values (exact; the
+// conversion takes the power of two from its fp32 scale operand, so
+// e = -127 converts with 2^-126 and halves afterwards).
+__device__ __forceinline__ uint4 dequant8_mxfp4_bf16(uint32_t codes, int e)
+{
+    const float s = pow2f(e < -126 ? -126 : e);
+    bf16x2_t_ h[4];
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, s, 0);
+    h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, s, 1);
+    h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, s, 2);
+    h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, s, 3);
+    uint4 out;
+    __builtin_memcpy(&out, h, 16);
+    if (e < -126) {
+        out.x = bf16x2_halve(out.x);
+        out.y = bf16x2_halve(out.y);
+        out.z = bf16x2_halve(out.z);
+        out.w = bf16x2_halve(out.w);
+    }
+    return out;
+}
+
+// 8 E2M1 codes (one dword) times an E4M3 scale s (as fp32), as 8 bf16
+// values: e2m1 (2 significant bits) times s (4) is exact in bf16.
+__device__ __forceinline__ uint4 dequant8_nvfp4_bf16(uint32_t codes, float s)
+{
+    const float2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+    const float2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+    const float2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+    const float2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+    return make_uint4(bf16x2_rne(f0[0] * s, f0[1] * s), bf16x2_rne(f1[0] * s, f1[1] * s),
+                      bf16x2_rne(f2[0] * s, f2[1] * s), bf16x2_rne(f3[0] * s, f3[1] * s));
+}
+
+// E4M3 code -> fp32 (exact; NaN codes never occur in valid scales).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c)
+{
+    const uint32_t ef = (c >> 3) & 15u, m = c & 7u;
+    const float v = ef == 0 ? (float)m * 0x1p-9f : __uint_as_float(((ef + 120u) << 23) | (m << 20));
+    return (c & 0x80u) ? -v : v;
+}
+
 struct DqArgs {
     const uint8_t* a_q; const uint8_t* a_s;
     const uint8_t* w_q; const uint8_t* w_s;
@@ -119,6 +166,8 @@ struct DqArgs {
 // FUSED_A (MXFP8 only): A arrives as bf16 [M, K]; each 8-element chunk is
 // quantized in registers (block-32 scale by A_RULE over a lane quad, E4M3
 // codes) and dequantized back exactly, as mx_quantize_act would have done.
+// A_RAW (W4A16): A arrives as bf16 [M, K] and is staged as it is; W is
+// MXFP4 or NVFP4 and is dequantized to bf16.
 // ODD16 (NVFP4 with K % 32 == 16): rows are only 8-byte aligned and the
 // last chunk of a row holds a single block of 16 elements.  SCW (NVFP4 with
 // K % 64 == 0, MXFP8 with K % 128 == 0): scale bytes are fetched as the
@@ -127,18 +176,22 @@ struct DqArgs {
 // the compiler waits for a byte load's zero extension right after the load,
 // a dword needs none.
 template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL,
-          bool ODD16 = false, bool SCW = false>
+          bool ODD16 = false, bool SCW = false, bool A_RAW = false>
 __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
 {
     using T = DqTraits<KIND>;
     static_assert(!FUSED_A || KIND == DQ_MXFP8, "fused quantization is for MXFP8");
+    static_assert(!A_RAW || KIND != DQ_MXFP8, "W4A16 weights are MXFP4 or NVFP4");
+    static_assert(A_RAW || KIND != DQ_MXFP4, "MXFP4 x MXFP4 runs on the FP4 matrix cores");
+    constexpr bool A_BF16 = FUSED_A || A_RAW;       // A arrives as bf16
+    constexpr bool F16 = KIND == DQ_NVFP4 && !A_RAW;  // f16 matrix cores (NVFP4 W4A4), else bf16
     constexpr int NT = WM * WN * 64;
     constexpr int A_TILE = BM * DQ_ROW_BYTES, W_TILE = BN * DQ_ROW_BYTES;
     constexpr int STAGE = A_TILE + W_TILE;
     constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
-    constexpr int A_CPR = FUSED_A ? DQ_BK * 2 / 16 : T::CHUNKS;   // A chunks per row per stage
+    constexpr int A_CPR = A_BF16 ? DQ_BK * 2 / 16 : T::CHUNKS;   // A chunks per row per stage
     constexpr int A_CH = BM * A_CPR, W_CH = BN * T::CHUNKS;
-    static_assert(!FUSED_A || (A_CH % NT == 0 && NT % A_CPR == 0), "fused tile mapping");
+    static_assert(!A_BF16 || (A_CH % NT == 0 && NT % A_CPR == 0), "bf16 A tile mapping");
     constexpr int A_PER_T = (A_CH + NT - 1) / NT, W_PER_T = (W_CH + NT - 1) / NT;
 
     extern __shared__ __align__(16) uint8_t smem[];
@@ -149,7 +202,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int K = p.K, KS = K / T::SCALE_BLOCK;
-    const int row_bytes = KIND == DQ_NVFP4 ? K / 2 : K;
+    const int row_bytes = KIND == DQ_MXFP8 ? K : K / 2;   // W (and quantized A) bytes per row
     const int nk = (K + DQ_BK - 1) / DQ_BK;
 
     // two register sets of staged chunks: stage kt lives in set kt % 2.
@@ -189,14 +242,14 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
             sc[1] = s[ok1 ? (size_t)gr * KS + blk + 1 : 0];
             fl |= ok1 ? 4u : 0u;
         } else {
-            sc[0] = s[ok ? (size_t)gr * KS + (kt * DQ_BK + c * 16) / 32 : 0];
+            sc[0] = s[ok ? (size_t)gr * KS + (kt * DQ_BK + c * T::ELEMS_PER_CHUNK) / 32 : 0];
         }
     };
     auto load_stage = [&](int kt, int set) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < A_PER_T; ++i) {
             const int qi = tid + i * NT;
-            if (FUSED_A) {
+            if (A_BF16) {
                 const int row = qi / A_CPR, c = qi % A_CPR, gm = m0 + row;
                 const int kb = kt * DQ_BK * 2 + c * 16;
                 const bool ok = gm < p.M && kb < K * 2;
@@ -220,11 +273,31 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
         if (KIND == DQ_NVFP4) {
             const uint32_t sc = SCW ? (fl & 1u ? __builtin_amdgcn_ubfe(scb[0], 16 * c, 16) : 0u)
                                     : (fl & 1u ? scb[0] : 0u) | (fl & 4u ? scb[1] << 8 : 0u);
-            const _Float16 s0 = e4m3_to_f16(sc & 0xFFu), s1 = e4m3_to_f16((sc >> 8) & 0xFFu);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            if (F16) {
+                const _Float16 s0 = e4m3_to_f16(sc & 0xFFu), s1 = e4m3_to_f16((sc >> 8) & 0xFFu);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {   // 8 elements per dword -> one 16-B chunk of f16
+                    const uint4 d = dequant8_nvfp4(w[h], h < 2 ? s0 : s1);
+                    const int chunk = (c * 4 + h) ^ dq_swz(row);
+                    *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + chunk * 16) = d;
+                }
+            } else {
+                const float s0 = e4m3_to_f32(sc & 0xFFu), s1 = e4m3_to_f32((sc >> 8) & 0xFFu);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {   // 8 elements per dword -> one 16-B chunk of bf16
+                    const uint4 d = dequant8_nvfp4_bf16(w[h], h < 2 ? s0 : s1);
+                    const int chunk = (c * 4 + h) ^ dq_swz(row);
+                    *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + chunk * 16) = d;
+                }
+            }
+        } else if (KIND == DQ_MXFP4) {
+            const uint32_t sb = SCW ? __builtin_amdgcn_ubfe(scb[0], 16 * par + 8 * c, 8) : scb[0];
+            const int e = (fl & 1u ? (int)sb : 127) - 127;
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {   // 8 elements per dword -> one 16-B chunk of f16
-                const uint4 d = dequant8_nvfp4(w[h], h < 2 ? s0 : s1);
+            for (int h = 0; h < 4; ++h) {
+                const uint4 d = dequant8_mxfp4_bf16(w[h], e);
                 const int chunk = (c * 4 + h) ^ dq_swz(row);
                 *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + chunk * 16) = d;
             }
@@ -243,13 +316,16 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
 #pragma unroll
         for (int i = 0; i < A_PER_T; ++i) {
             const int qi = tid + i * NT;
-            if (FUSED_A) {
-                // 8 bf16 per lane; a lane quad holds one block of 32
+            if (A_BF16) {
+                // 8 bf16 per lane; (fused) a lane quad holds one block of 32
                 const int row = qi / A_CPR, c = qi % A_CPR;
                 const uint4 x = fa[set][i] ? ra[set][i] : make_uint4(0, 0, 0, 0);
-                const uint32_t amax = quad_max_u32(amax_bits8(x));
-                const int e = scale_exponent<ELEM_E4M3, A_RULE>(amax);
-                const uint4 d = dequant8_mxfp8(encode8_e4m3(x, e), e);
+                uint4 d = x;
+                if (FUSED_A) {
+                    const uint32_t amax = quad_max_u32(amax_bits8(x));
+                    const int e = scale_exponent<ELEM_E4M3, A_RULE>(amax);
+                    d = dequant8_mxfp8(encode8_e4m3(x, e), e);
+                }
                 *reinterpret_cast<uint4*>(a_t + row * DQ_ROW_BYTES + ((c ^ dq_swz(row)) * 16)) = d;
             } else if (A_CH % NT == 0 || qi < A_CH) {
                 store_one(a_t, qi, ra[set][i], sa[set][i], fa[set][i], set);
@@ -291,7 +367,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    if (KIND == DQ_NVFP4) {
+                    if (F16) {
                         half8_t a8, b8;
                         __builtin_memcpy(&a8, &fa[i], 16);
                         __builtin_memcpy(&b8, &fw[j], 16);
@@ -339,7 +415,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * WTM + i * 32 + (r / 4) * 8 + g * 4 + (r % 4);
                 if (m < p.M && n < p.N) {
-                    const float v = KIND == DQ_NVFP4 ? acc[i][j][r] * p.alpha : acc[i][j][r];
+                    const float v = (KIND == DQ_NVFP4 || A_RAW) ? acc[i][j][r] * p.alpha : acc[i][j][r];
                     if (OUT_F32) {
                         reinterpret_cast<float*>(p.y)[(size_t)m * p.N + n] = v;
                     } else {
@@ -351,11 +427,11 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
 }
 
 template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL,
-          bool ODD16 = false, bool SCW = false>
+          bool ODD16 = false, bool SCW = false, bool A_RAW = false>
 hipError_t launch_dq_k(const DqArgs& a, hipStream_t stream)
 {
     constexpr int LDS = 2 * (BM + BN) * DQ_ROW_BYTES;
-    auto kern = dq_gemm_kernel<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, ODD16, SCW>;
+    auto kern = dq_gemm_kernel<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, ODD16, SCW, A_RAW>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
@@ -367,16 +443,20 @@ hipError_t launch_dq_k(const DqArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL>
+template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL,
+          bool A_RAW = false>
 hipError_t launch_dq(const DqArgs& a, hipStream_t stream)
 {
     if constexpr (KIND == DQ_NVFP4) {
-        if (a.K % 32 != 0) return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, true, false>(a, stream);
-        if (a.K % 64 == 0) return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, true>(a, stream);
+        if (a.K % 32 != 0)
+            return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, true, false, A_RAW>(a, stream);
+        if (a.K % 64 == 0)
+            return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, true, A_RAW>(a, stream);
     } else if (!FUSED_A) {
-        if (a.K % 128 == 0) return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, true>(a, stream);
+        if (a.K % 128 == 0)
+            return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, true, A_RAW>(a, stream);
     }
-    return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, false>(a, stream);
+    return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, false, A_RAW>(a, stream);
 }
 
 } // namespace mxl
@@ -421,6 +501,28 @@ extern "C" hipError_t mxl_launch_mxfp8_exact_gemm_fused(int a_rule, const void* 
     if (a_rule == RULE_CEIL) return fused8<RULE_CEIL>(a, out_f32, stream);
     if (a_rule == RULE_FLOOR) return fused8<RULE_FLOOR>(a, out_f32, stream);
     return fused8<RULE_EVEN>(a, out_f32, stream);
+}
+
+// W4A16, any M: bf16 A staged as it is, MXFP4 (w_nv == 0) or NVFP4 (w_nv != 0)
+// weights dequantized exactly to bf16; alpha multiplies the result.
+extern "C" hipError_t mxl_launch_w4a16_gemm(int w_nv, const void* a_bf16, const void* wq, const void* ws,
+                                            int64_t m, int64_t n, int64_t k, float alpha, void* y,
+                                            int out_f32, hipStream_t stream)
+{
+    DqArgs a{static_cast<const uint8_t*>(a_bf16), nullptr, static_cast<const uint8_t*>(wq),
+             static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, alpha};
+    if (w_nv) {
+        if (out_f32) return launch_dq<DQ_NVFP4, 128, 128, 2, 2, true, false, RULE_CEIL, true>(a, stream);
+        return launch_dq<DQ_NVFP4, 128, 128, 2, 2, false, false, RULE_CEIL, true>(a, stream);
+    }
+    if (out_f32) return launch_dq<DQ_MXFP4, 128, 128, 2, 2, true, false, RULE_CEIL, true>(a, stream);
+    return launch_dq<DQ_MXFP4, 128, 128, 2, 2, false, false, RULE_CEIL, true>(a, stream);
+}
+
+extern "C" const char* mxl_w4a16_gemm_config_name(void)
+{
+    return "dq_gemm_kernel<bf16 A x (mxfp4|nvfp4 -> exact bf16) W, tile 128x128x64, 2x2 waves of 64x64, "
+           "bf16 mfma 32x32x16>";
 }
 
 extern "C" const char* mxl_nv_gemm_config_name(void)

@@ -164,6 +164,42 @@ mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void*
                   size_t ws_bytes, mx_stream_t stream);
 
 /*
+ * mx_gemm_w4a16 -- weight-only quantized linear (W4A16): bf16 activations,
+ * used as they are, times packed 4-bit weights.  One packed artifact serves
+ * both W4A4 and W4A16 (Qwen3.5-27B-MXFP4-QAD-W4A4-LR1e-5-s1000,
+ * introduction); the NVFP4 weight-only checkpoint keeps activations in bf16
+ * with weight bytes identical to the W4A4 sibling
+ * (Qwen3.5-27B-NVFP4-RTN-weight-only, introduction).
+ *
+ * a_bf16 [m, k] bf16; w_q [n, k/2] E2M1 (element 2j in the low nibble of
+ * byte j); w_s [n, k/32] E8M0 for w_fmt == MX_FMT_MXFP4 or [n, k/16] E4M3
+ * for MX_FMT_NVFP4.  y [m, n] bf16 (RNE of the fp32 result) or fp32 with
+ * MX_OUT_F32:
+ *   Y = alpha * sum_k a * dq(w),  dq(w) = e2m1 * 2^(s - 127)  (MXFP4)
+ *                                 dq(w) = e2m1 * s_e4m3       (NVFP4),
+ * alpha = 1 / g_w for NVFP4 weights (their global scale), normally 1 for
+ * MXFP4.  A weight element times its block scale is exact in bf16, so the
+ * contraction runs on bf16 matrix cores with fp32 accumulation: within
+ * 1e-4 * sum_k |a_k dq(w)_k| of the exact product (plus the bf16 output
+ * rounding); MXFP4 weight values below 2^-126 are flushed to zero.
+ * Requires k % 32 == 0 (MXFP4) or k % 16 == 0 (NVFP4); any m, n >= 1.
+ * Errors: MX_ERR_INVALID_ARG for null pointers, unknown flags, a
+ * non-finite alpha or a w_fmt other than MXFP4/NVFP4 (MXFP8:
+ * MX_ERR_UNSUPPORTED); MX_ERR_SHAPE, MX_ERR_ALIGN (16-byte alignment of
+ * every pointer) and MX_ERR_HIP as for mx_gemm.  workspace/ws_bytes are
+ * reserved and may be NULL/0.
+ */
+mx_status mx_gemm_w4a16(mx_format w_fmt, const void* a_bf16, const void* w_q, const void* w_s, int64_t m,
+                        int64_t n, int64_t k, float alpha, void* y, unsigned flags, void* workspace,
+                        size_t ws_bytes, mx_stream_t stream);
+
+/*
+ * mx_gemm_w4a16_plan -- writes into `name` (capacity `len`) the kernel that
+ * mx_gemm_w4a16 would launch for this shape.  Pure host logic.
+ */
+mx_status mx_gemm_w4a16_plan(mx_format w_fmt, int64_t m, int64_t n, int64_t k, char* name, size_t len);
+
+/*
  * mx_tensor_amax -- largest |x| of a bf16 tensor of `count` elements, written
  * as fp32 to *amax_dev (device memory).  The NVFP4 global scales come from it
  * (activations: the running maximum over calibration batches).

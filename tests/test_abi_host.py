@@ -33,6 +33,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("mx_pack_weights", "mx_quantize_act", "mx_gemm", "mx_gemm_fused", "nv_gemm",
+              "mx_gemm_w4a16", "mx_gemm_w4a16_plan",
               "mx_tensor_amax", "mx_nv_global_scale", "mx_gemm_plan", "mx_status_string",
               "mx_abi_version"):
         assert n in names
@@ -117,6 +118,22 @@ def test_fused_and_nv_validation():
     assert L.mx_tensor_amax(GOOD, 10, P(0x10002), None) == ALIGN
 
 
+def test_w4a16_validation():
+    w = L.mx_gemm_w4a16
+    def g(fmt=0, a=GOOD, wq=GOOD, ws=GOOD, m=4, n=4, k=64, alpha=1.0, y=GOOD, flags=0):
+        return w(fmt, a, wq, ws, m, n, k, alpha, y, flags, None, 0, None)
+    assert g(fmt=7) == INVALID
+    assert g(fmt=1) == UNSUPPORTED          # MXFP8 weights: no W4A16 mode
+    assert g(a=None) == INVALID
+    assert g(flags=0x80) == INVALID
+    assert g(alpha=float("nan")) == INVALID
+    assert g(k=48) == SHAPE                  # MXFP4 needs k % 32 == 0
+    assert g(fmt=2, k=40) == SHAPE           # NVFP4 needs k % 16 == 0
+    assert g(m=0) == SHAPE
+    assert g(wq=BAD_ALIGN) == ALIGN
+    assert g(fmt=2, k=48) in (OK, UNSUPPORTED, HIPERR)   # validation passes
+
+
 def test_plan_names_the_kernel():
     s = mxl.mx_gemm_plan("mxfp4", "mxfp4", 8192, 17408, 5120)
     assert "mfma" in s and "mxfp4" in s
@@ -125,6 +142,10 @@ def test_plan_names_the_kernel():
     assert mxl.mx_gemm_plan("mxfp8", "mxfp8", 16, 96, 5120)  # N = 96 is a valid plan
     with pytest.raises(mxl.MXError):
         mxl.mx_gemm_plan("mxfp4", "mxfp4", 16, 16, 40)
+    assert "w4a16_decode_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 1, 17408, 5120)
+    assert "w4a16_decode_kernel" in mxl.mx_gemm_w4a16_plan("nvfp4", 16, 17408, 5120)
+    assert "dq_gemm_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 17, 17408, 5120)
+    assert "dq_gemm_kernel" in mxl.mx_gemm_w4a16_plan("nvfp4", 1, 512, 400)
 
 
 def test_global_scale_helper_matches_oracle():
