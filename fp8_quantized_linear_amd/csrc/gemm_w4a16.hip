@@ -24,13 +24,15 @@
 //    global -> LDS by buffer-to-LDS copies (1 KiB and 256 B each); a copy
 //    lane places 16-byte unit u of row r at unit u ^ (r & 15) within aligned
 //    groups of 16, so that the step reads below hit distinct banks.
-//  * Wave w takes a contiguous quarter of K in steps of 32.  Lane
-//    l = r + 16 g supplies W row r and A row r (the MFMA's 16 x 32 operand
-//    layout: K elements [8 g, 8 g + 8) of the step): 4 bytes of codes and a
-//    scale byte from LDS, dequantized to 8 bf16 in registers; the 16 bytes
-//    of A come straight from global memory (A is at most 16 x K bf16,
-//    shared by every workgroup and cache-resident) through a ring of 8
-//    steps of loads in flight.  A rows past M read as zero.
+//  * Wave w takes a contiguous quarter of K in groups of 128 (4 steps of
+//    the 16x16x32 MFMA).  Lane l = r + 16 g supplies W row r and A row r; in
+//    each group it owns 32 consecutive K elements, one 16-byte code unit:
+//    one LDS read and one (MXFP4) or two (NVFP4) scale bytes per 4 MFMAs,
+//    dequantized to bf16 in registers 8 elements per step.  A and W assign
+//    the same K elements to each lane and step, so every step still sums 32
+//    distinct k.  The 64 bytes of A per group come straight from global
+//    memory (A is at most 16 x K bf16, shared by every workgroup and
+//    cache-resident), two groups of loads ahead.  A rows past M read as zero.
 //  * The four K quarters are summed through LDS (aliasing the W block).
 #include "mx_device.h"
 
@@ -116,7 +118,7 @@ static size_t w4a16_decode_lds_bytes(int K)
 template <bool NV, bool OUT_F32>
 __global__ __launch_bounds__(256) void w4a16_decode_kernel(W4a16Args p)
 {
-    constexpr int WAVES = 4, RING = 8;
+    constexpr int WAVES = 4;
     extern __shared__ __align__(16) uint8_t dsm[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -144,40 +146,58 @@ __global__ __launch_bounds__(256) void w4a16_decode_kernel(W4a16Args p)
         const int sn = 16 * KS / 256;   // K % 512 == 0: whole 256-byte copies
         for (int j = wave; j < sn; j += WAVES) dma_b32(sbase + j * 256, n0 * KS + j * 256 + lane * 4, rws, 0);
     }
-    // A rows past M read as zero through the range check
+    // A rows past M read as zero through the range check.  K is walked in
+    // groups of 128 (4 MFMA steps); in group q lane group g owns the 32 K
+    // elements [128 q + 32 g, 128 q + 32 g + 32), i.e. code unit 4 q + g of
+    // its W row, and feeds their 8-element quarters to the 4 steps (A and W
+    // use the same K assignment, so each step still sums 32 distinct k).
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.a, (short)0, p.M * K * 2, 0x00020000);
-    const int a_off = r * K * 2 + g * 16;   // this lane's A row and K offset within a step
-    bf16x8_w af[RING];
+    const int a_off = r * K * 2 + g * 64;   // this lane's A row and K offset within a group
+    const int q0 = s0 / 4, q1 = s1 / 4;     // this wave's groups (K % 512 == 0: whole groups)
+    constexpr int QR = 2;                   // groups of A loads in flight
+    bf16x8_w af[QR][4];
 #pragma unroll
-    for (int j = 0; j < RING; ++j)
-        af[j] = __builtin_bit_cast(bf16x8_w, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off, (s0 + j) * 64, 0));
-    wait_vmcnt<0>();   // the copies (and the first A steps) have landed
+    for (int x = 0; x < QR; ++x)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            af[x][j] = __builtin_bit_cast(bf16x8_w,
+                                          __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + j * 16, (q0 + x) * 256, 0));
+    wait_vmcnt<0>();   // the copies (and the first A groups) have landed
     __syncthreads();
 
     f32x4_w acc = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* wrow = w_lds + r * row_bytes + 4 * g;
+    const uint8_t* wrow = w_lds + r * row_bytes;
     const uint8_t* srow = ws_lds + r * KS;
-    // step st of ring slot j: the A loads of step st + RING go out as step st
+    // group q in ring slot x: the A loads of group q + QR go out as group q
     // is computed (past the wave's range they read data that is dropped)
-    auto step = [&](int st, int j) __attribute__((always_inline)) {
-        const uint32_t codes = *reinterpret_cast<const uint32_t*>(wrow + ((st ^ r) * 16));
-        float s = 1.0f;
+    auto group = [&](int q, int x) __attribute__((always_inline)) {
+        const int u = 4 * q + g;
+        const uint4 cw = *reinterpret_cast<const uint4*>(wrow + ((u ^ r) * 16));
+        float s_lo = 1.0f, s_hi = 1.0f;
         int e = 0;
-        if (NV) s = w4_e4m3_to_f32(srow[2 * st + (g >> 1)]);
-        else e = (int)srow[st] - 127;
-        const bf16x8_w b8 = w4_dequant8<NV>(codes, s, e);
-        const bf16x8_w a8 = af[j];
-        af[j] = __builtin_bit_cast(bf16x8_w, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off, (st + RING) * 64, 0));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
+        if (NV) {
+            const uint32_t sp = *reinterpret_cast<const uint16_t*>(srow + 2 * u);
+            s_lo = w4_e4m3_to_f32(sp & 0xFFu);
+            s_hi = w4_e4m3_to_f32(sp >> 8);
+        } else {
+            e = (int)srow[u] - 127;
+        }
+        const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8_w b8 = w4_dequant8<NV>(cws[j], j < 2 ? s_lo : s_hi, e);
+            const bf16x8_w a8 = af[x][j];
+            af[x][j] = __builtin_bit_cast(bf16x8_w,
+                                          __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + j * 16, (q + QR) * 256, 0));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
+        }
     };
-    int sb = s0;
-    for (; sb + RING <= s1; sb += RING) {
+    int q = q0;
+    for (; q + QR <= q1; q += QR) {
 #pragma unroll
-        for (int j = 0; j < RING; ++j) step(sb + j, j);
+        for (int x = 0; x < QR; ++x) group(q + x, x);
     }
-#pragma unroll
-    for (int j = 0; j < RING - 1; ++j)   // the wave's last steps (its range is a multiple of 4)
-        if (sb + j < s1) step(sb + j, j);
+    if (q < q1) group(q, 0);
     __syncthreads();   // every wave is done with the W block
     f32x4_w* red = reinterpret_cast<f32x4_w*>(w_lds);   // [WAVES][64]
     red[wave * 64 + lane] = acc;
@@ -237,5 +257,5 @@ extern "C" hipError_t mxl_launch_w4a16_decode(int w_nv, const void* a_bf16, cons
 extern "C" const char* mxl_w4a16_decode_config_name(void)
 {
     return "w4a16_decode_kernel<16 W rows per workgroup, whole-row copies into swizzled LDS, 4 waves over K "
-           "quarters, A through an 8-step load ring, bf16 mfma 16x16x32>";
+           "quarters in groups of 128, A two groups ahead, bf16 mfma 16x16x32>";
 }
