@@ -16,6 +16,10 @@ Every function states the passage it follows in the C source; in short:
   (Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode"), FLOOR (OCP);
 * NVFP4 global and block scales (Qwen3.5-27B-NVFP4-RTN-weight-only and
   Qwen3.5-27B-NVFP4-GPTQ, introductions);
+* fake quantization, the quantize -> dequantize round trip rounded to bf16
+  (Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode";
+  Qwen3.5-27B-MXFP4-QAD-W4A4-LR1e-5-s1000, "How this checkpoint was
+  produced", Training row);
 * the GEMM as a dot product of dequantized operands in fp64.
 """
 from __future__ import annotations
@@ -83,6 +87,9 @@ def lib():
         L.orc_gemm_dq.argtypes = [P, P, i64, i64, i64, P, P, i32]
         L.orc_gemm_dq_pairs.restype = i32
         L.orc_gemm_dq_pairs.argtypes = [P, P, i64, P, P, i64, P, P, i32]
+        L.orc_bf16_nearest_ratio.restype, L.orc_bf16_nearest_ratio.argtypes = u16, [d, d]
+        L.orc_fake_quant.restype = i32
+        L.orc_fake_quant.argtypes = [i32, i32, P, i64, i64, f32, P, i32]
         L.orc_mx_gemm.restype = i32
         L.orc_mx_gemm.argtypes = [i32, P, P, i32, P, P, i64, i64, i64, P, P, i32]
         _lib = L
@@ -259,6 +266,28 @@ def w4a16_gemm(a_bf16, wq, w_s, n: int, k: int, fmt: str = "mxfp4", g_w=None, nt
     else:
         raise ValueError("W4A16 weights are mxfp4 or nvfp4")
     return gemm_dq(a, wd, nthreads)
+
+
+FAKE_FMT = {"mxfp4": 0, "mxfp8": 1, "nvfp4": 2}
+
+
+def bf16_nearest_ratio(p: float, g: float) -> int:
+    """bf16 bits (sign clear) nearest to the exact ratio p / g, ties to even."""
+    return int(lib().orc_bf16_nearest_ratio(float(p), float(g)))
+
+
+def fake_quant(fmt: str, rule, x_bf16: np.ndarray, g=None, nthreads=None) -> np.ndarray:
+    """Quantize -> dequantize -> nearest bf16 (the training-time fake-quant
+    op).  MX formats use the block rule `rule`; NVFP4 uses the global scale
+    g.  Returns bf16 bit patterns [rows, k]."""
+    x = _u16(x_bf16)
+    rows, k = x.shape
+    out = np.empty((rows, k), np.uint16)
+    rc = lib().orc_fake_quant(FAKE_FMT[fmt], _rule(rule) if rule is not None else 0, _ptr(x), rows, k,
+                              float(np.float32(g if g is not None else 1.0)), _ptr(out), _nthreads(nthreads))
+    if rc != 0:
+        raise ValueError("bad format or k not a multiple of the block")
+    return out
 
 
 # ---------------------------------------------------------------- compositions

@@ -46,10 +46,14 @@
  *    block scale s = RNE_E4M3(block_amax * g / 6) in exact reals, element code
  *    = RNE_E2M1(x * g / s) in exact reals, s == 0 gives signed zeros;
  *  - Y = A * W^T with W stored [N, K] (nn.Linear orientation).
+ *  - fake quantization rounds the exact dequantized value once to bf16
+ *    (nearest, ties to even; infinity from the largest finite bf16 plus half
+ *    an ulp upward); a zero keeps its code's sign.
  */
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #include <omp.h>
 
@@ -460,4 +464,94 @@ int orc_mx_gemm(int a_elem, const uint8_t* aq, const uint8_t* as, int w_elem, co
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Fake quantization: the quantize -> dequantize round trip written back as  */
+/* bf16, the op that quantization-aware training runs in place of the        */
+/* serving quantizer ([MX-27B] "How this checkpoint was produced": weights   */
+/* and activations fake-quantized during training; [MX-9B] "Training mode": */
+/* the same CEIL rule as serving).  Each output is the bf16 nearest to the   */
+/* exact dequantized value, ties to the even pattern.                        */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 bits (sign clear) of the value nearest to the exact ratio p / g, for
+ * p >= 0 and g > 0 finite, ties to the even pattern; from the largest finite
+ * bf16 plus half an ulp upward the result is infinity.  The candidates are
+ * the patterns around the truncation of the double quotient, each compared
+ * by its distance |b * g - p| (b * g has at most 8 + 24 significant bits, so
+ * it is exact; near the quotient the difference is exact too). */
+uint16_t orc_bf16_nearest_ratio(double p, double g)
+{
+    const double top = orc_bf16_value(0x7F7F), half_ulp = ldexp(1.0, 127 - 8);
+    double q = p / g, bestd = -1.0;
+    float f = (float)q;
+    uint32_t fb;
+    int32_t u, c;
+    uint16_t best = 0;
+    if (p != p) return 0x7FC0;
+    if (p >= (top + half_ulp) * g) return 0x7F80;
+    memcpy(&fb, &f, 4);
+    u = (int32_t)(fb >> 16);
+    for (c = u - 2; c <= u + 2; c++) {
+        double d;
+        if (c < 0 || c > 0x7F7F) continue;
+        d = fabs(orc_bf16_value((uint16_t)c) * g - p);
+        if (bestd < 0.0 || d < bestd || (d == bestd && (c & 1) == 0)) {
+            best = (uint16_t)c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/*
+ * rows x k bf16 -> rows x k bf16 fake-quantized values.  fmt 0: MXFP4 (E2M1,
+ * E8M0 per 32 by `rule`); 1: MXFP8 (E4M3, E8M0 per 32 by `rule`); 2: NVFP4
+ * (E2M1, E4M3 per 16, global scale g; `rule` unused).  The codes and scales
+ * are those of orc_mx_quantize / orc_nv_quantize; MX values e * 2^(s - 127)
+ * and NVFP4 values e2m1 * s / g are rounded once to bf16.  A zero value keeps
+ * the sign of its code.  Returns -1 on a bad fmt or a k that is not a
+ * multiple of the block, -2 if scratch memory is unavailable.
+ */
+int orc_fake_quant(int fmt, int rule, const uint16_t* x, int64_t rows, int64_t k, float g, uint16_t* out,
+                   int nthreads)
+{
+    const int elem = fmt == 1 ? ORC_E4M3 : ORC_E2M1;
+    const int block = fmt == 2 ? 16 : 32;
+    const int64_t qbytes = elem == ORC_E2M1 ? rows * k / 2 : rows * k;
+    uint8_t *q, *sc;
+    int64_t i;
+    int rc;
+    if (fmt < 0 || fmt > 2 || k % block != 0 || rows < 0) return -1;
+    q = (uint8_t*)malloc((size_t)(qbytes > 0 ? qbytes : 1));
+    sc = (uint8_t*)malloc((size_t)(rows * k / block > 0 ? rows * k / block : 1));
+    if (!q || !sc) {
+        free(q);
+        free(sc);
+        return -2;
+    }
+    rc = fmt == 2 ? orc_nv_quantize(x, rows, k, g, q, sc, nthreads)
+                  : orc_mx_quantize(elem, rule, x, rows, k, q, sc, nthreads);
+    if (rc == 0) {
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+        for (i = 0; i < rows * k; i++) {
+            const int code = get_code(q, elem, i);
+            const int sign = elem == ORC_E2M1 ? (code >> 3) & 1 : (code >> 7) & 1;
+            double v;
+            uint16_t bits;
+            if (fmt == 2) {
+                v = fabs(orc_e2m1_value(code) * orc_e4m3_value(sc[i / 16]));   /* exact */
+                bits = v == 0.0 ? 0 : orc_bf16_nearest_ratio(v, (double)g);
+            } else {
+                v = fabs((elem == ORC_E2M1 ? orc_e2m1_value(code) : orc_e4m3_value(code)) *
+                         orc_e8m0_value(sc[i / 32]));                          /* exact */
+                bits = v == 0.0 ? 0 : orc_bf16_nearest_ratio(v, 1.0);
+            }
+            out[i] = (uint16_t)(bits | (sign << 15));
+        }
+    }
+    free(q);
+    free(sc);
+    return rc;
 }

@@ -75,3 +75,25 @@ def sample_pairs(m: int, n: int, count: int, seed: int = 0, tile: int = 128):
 def oracle_rows_mx(elem, rule, bits: np.ndarray, rows: np.ndarray):
     """Oracle quantization of selected rows (row-local, so a sample suffices)."""
     return oracle.mx_quantize(elem, rule, np.ascontiguousarray(bits[rows]))
+
+
+def double_rounding_trap_scales(count: int = 4, seed: int = 0) -> list[np.float32]:
+    """fp32 values g in [1, 2) for which rounding 1/g to fp32 and then to bf16
+    gives a different bf16 than rounding 1/g once: the fp32 reciprocal lands
+    exactly on a midpoint between two bf16 values, and the even one of the
+    two lies on the other side of 1/g.  m * g with the midpoint m (9
+    significant bits) and g (24) is exact in fp64, so 1 <=> m * g decides on
+    which side of the midpoint 1/g lies."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        mant = rng.integers(1, 1 << 23, 1 << 20, dtype=np.int64)
+        g = (1.0 + mant / float(1 << 23)).astype(np.float32)
+        r32 = (1.0 / g.astype(np.float64)).astype(np.float32)
+        bits = r32.view(np.uint32)
+        on_mid = (bits & 0xFFFF) == 0x8000
+        above = 1.0 > r32.astype(np.float64) * g.astype(np.float64)   # 1/g above the midpoint
+        lower_even = ((bits >> 16) & 1) == 0                           # tie would go down
+        pick = on_mid & (above == lower_even)
+        out.extend(g[pick][: count - len(out)])
+    return out

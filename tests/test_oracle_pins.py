@@ -532,3 +532,164 @@ def test_w4a16_nvfp4_closed_form():
     for j in range(n):
         np.testing.assert_allclose(y[:, j], av.sum(axis=1) / 4, rtol=1e-14)
         np.testing.assert_allclose(sa[:, j], np.abs(av).sum(axis=1) / 4, rtol=1e-14)
+
+
+# ------------------------------------------------------------------ fake quantization
+# Training-time fake quantization (Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000,
+# "Training mode"; Qwen3.5-27B-MXFP4-QAD-W4A4-LR1e-5-s1000, "How this
+# checkpoint was produced", Training row): the codes of the serving
+# quantizer, dequantized, rounded once to bf16.
+_BITS, _VALS = all_bf16_positive_finite()           # patterns 0x0001 .. 0x7F7F, ascending
+_TOP = F(float(_VALS[-1]))
+_HALF_ULP_TOP = F(2) ** (127 - 8)
+
+
+def _bf16_val(c: int) -> F:
+    return F(0) if c == 0 else F(float(_VALS[c - 1]))
+
+
+def brute_bf16_nearest(q: F) -> int:
+    """Nearest bf16 pattern to the rational q >= 0 by search over the sorted
+    table of every positive finite bf16; ties to the even pattern; from the
+    largest finite value plus half an ulp upward, infinity."""
+    if q >= _TOP + _HALF_ULP_TOP:
+        return 0x7F80
+    i = int(np.searchsorted(_VALS, float(q)))
+    cands = [0] + [int(_BITS[j]) for j in range(max(0, i - 2), min(len(_VALS), i + 2))]
+    return min(cands, key=lambda c: (abs(_bf16_val(c) - q), c & 1))
+
+
+def test_bf16_nearest_ratio_bruteforce():
+    rng = np.random.default_rng(17)
+    e4 = [float(v) for v in E4M3_POS[1:]]
+    for _ in range(3000):
+        p = float(rng.choice(POS[1:])) * float(rng.choice(e4))
+        g = float(np.float32(np.exp(rng.uniform(-60, 60))))
+        assert oracle.bf16_nearest_ratio(p, g) == brute_bf16_nearest(F(p) / F(g)), (p, g)
+    # exact midpoints between neighbouring patterns of both parities: ties to even
+    for c in (0x3F80, 0x3F81, 0x0001, 0x0002, 0x7F7E, 0x0080):
+        mid = (_bf16_val(c) + _bf16_val(c + 1)) / 2
+        for g in (1.0, 3.0, float(np.float32(0.1)), float(np.float32(1e-20))):
+            p = float(mid * F(g))
+            assert F(p) == mid * F(g)                       # 9 + 24 bits: exact in a double
+            assert oracle.bf16_nearest_ratio(p, g) == (c if c % 2 == 0 else c + 1), hex(c)
+    # overflow boundary: top + half ulp rounds to infinity, anything below to the top
+    edge = float(_TOP + _HALF_ULP_TOP)
+    assert oracle.bf16_nearest_ratio(edge, 1.0) == 0x7F80
+    assert oracle.bf16_nearest_ratio(np.nextafter(edge, 0.0), 1.0) == 0x7F7F
+    assert oracle.bf16_nearest_ratio(0.0, 5.0) == 0
+    assert oracle.bf16_nearest_ratio(2.0 ** -134, 1.0) == 0      # half the smallest subnormal: tie -> 0
+    assert oracle.bf16_nearest_ratio(3 * 2.0 ** -134, 1.0) == 2  # 1.5 subnormal steps: tie -> even 2
+
+
+def test_bf16_nearest_ratio_single_rounding():
+    """Where rounding to fp32 first lands on a bf16 midpoint, the result is
+    still the single rounding of the exact quotient."""
+    from helpers import double_rounding_trap_scales
+    for g in double_rounding_trap_scales(8):
+        q = F(1) / F(float(g))
+        want = brute_bf16_nearest(q)
+        assert oracle.bf16_nearest_ratio(1.0, float(g)) == want
+        twice = int(torch.tensor(float(np.float32(1.0 / float(g))), dtype=torch.float32)
+                    .to(torch.bfloat16).view(torch.int16)) & 0xFFFF
+        assert twice != want  # the trap is real: rounding twice goes the other way
+
+
+def _signed(bits: int, neg: bool) -> int:
+    return bits | (0x8000 if neg else 0)
+
+
+@pytest.mark.parametrize("elem,fmt", [("e2m1", "mxfp4"), ("e4m3", "mxfp8")])
+@pytest.mark.parametrize("rule", ["floor", "ceil", "even"])
+def test_fake_quant_mx_bruteforce(elem, fmt, rule):
+    rng = np.random.default_rng(77)
+    rows, k = 5, 96
+    x = rng.standard_normal((rows, k)).astype(np.float32)
+    x[1] *= 1e-38                                    # subnormal bf16 inputs, clamped scales
+    x[2, :32] = 0.0
+    x[2, 33] = -0.0
+    x[3, :32] = rng.standard_normal(32) * np.float32(1e38)   # codes near the top
+    x[3, 7] = 3.3e38   # CEIL: scale 2^126, code 4 -> 2^128, beyond bf16
+    x[4, :32] = np.float32(0.25) * rng.integers(-24, 25, 32)
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    vals = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = oracle.fake_quant(fmt, rule, xb)
+    grid = [F(p) for p in POS] if elem == "e2m1" else E4M3_POS
+    infs = 0
+    for r in range(rows):
+        for b in range(k // 32):
+            blk = [-0.0 if xb[r, b * 32 + i] == 0x8000 else vals[r, b * 32 + i] for i in range(32)]
+            sb, codes = brute_block(blk, elem, rule)
+            for i in range(32):
+                c = codes[i]
+                neg = bool(c & (8 if elem == "e2m1" else 128))
+                mag = grid[c & (7 if elem == "e2m1" else 127)] * F(2) ** (sb - 127)
+                want = _signed(brute_bf16_nearest(mag), neg)
+                infs += (want & 0x7FFF) == 0x7F80
+                assert int(got[r, b * 32 + i]) == want, (r, b, i, blk[i])
+    if rule == "ceil" and elem == "e2m1":
+        assert infs > 0  # the near-top block overflows bf16 under CEIL
+
+
+def test_fake_quant_nv_bruteforce():
+    from helpers import double_rounding_trap_scales
+    rng = np.random.default_rng(78)
+    rows, k = 4, 64
+    x = rng.standard_normal((rows, k)).astype(np.float32)
+    x[1] *= 1e-4
+    x[2, :16] = 0.0
+    x[3] *= 40
+    traps = double_rounding_trap_scales(4)
+    # blocks built so that s = 1 and one element codes to 1: its output is the
+    # single rounding of 1/g (a double-rounding trap for an fp32 path)
+    for j, gt in enumerate(traps[:2]):
+        x[0, 16 * j:16 * j + 16] = 0.0
+        x[0, 16 * j] = 6.0 / float(gt)
+        x[0, 16 * j + 1] = -1.0 / float(gt)
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    vals = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).double().numpy()
+    for g in (oracle.nv_global_scale(float(np.abs(vals).max())), np.float32(0.37), traps[0], traps[1]):
+        got = oracle.fake_quant("nvfp4", None, xb, g)
+        for r in range(rows):
+            for b in range(k // 16):
+                sc, codes = brute_nv_block(list(vals[r, b * 16:(b + 1) * 16]), g)
+                for i in range(16):
+                    v = F(POS[codes[i] & 7]) * E4M3_POS[sc] / F(float(g))
+                    want = _signed(brute_bf16_nearest(v), bool(codes[i] & 8))
+                    assert int(got[r, b * 16 + i]) == want, (g, r, b, i)
+
+
+def test_fake_quant_identity_on_lattice():
+    """Values already on a block's lattice come back unchanged."""
+    rng = np.random.default_rng(79)
+    # MXFP4 EVEN: a block whose amax is 6 * 2^e has scale 2^e (mantissa 1.5)
+    e = rng.integers(-20, 20, 4)
+    x = np.zeros((4, 32), np.float64)
+    for r in range(4):
+        x[r] = rng.choice(POS, 32) * rng.choice([-1, 1], 32) * 2.0 ** e[r]
+        x[r, 5] = 6.0 * 2.0 ** e[r]
+    xb = _bf16_bits(x)
+    assert np.array_equal(oracle.fake_quant("mxfp4", "even", xb), xb)
+    # NVFP4 with g = 1: block amax 6 * s with s on the E4M3 lattice
+    s = 1.25
+    y = rng.choice(POS, (2, 16)) * rng.choice([-1, 1], (2, 16)) * s
+    y[:, 0] = 6.0 * s
+    yb = _bf16_bits(y)
+    assert np.array_equal(oracle.fake_quant("nvfp4", None, yb, np.float32(1.0)), yb)
+
+
+def test_fake_quant_matches_dequantized_codes():
+    """Outputs agree with the fp64 dequantization of the serving quantizer's
+    codes wherever that value is a bf16 (always for MX, exactly-divisible
+    NVFP4 cases otherwise)."""
+    rng = np.random.default_rng(80)
+    x = torch.from_numpy(rng.standard_normal((6, 128)).astype(np.float32)).to(torch.bfloat16)
+    xb = x.view(torch.int16).numpy().view(np.uint16)
+    q, s = oracle.mx_quantize("e2m1", "ceil", xb)
+    d = oracle.mx_dequantize("e2m1", q, s, 6, 128)
+    want = torch.from_numpy(d).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.fake_quant("mxfp4", "ceil", xb)
+    # -0 codes dequantize to -0.0; numpy keeps the sign, so patterns compare directly
+    assert np.array_equal(got, want)
+    assert np.array_equal(torch.from_numpy(d).float().numpy(),
+                          torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy())
