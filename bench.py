@@ -245,6 +245,22 @@ def extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_d
                                      "bytes": nbytes}
         del copies
 
+    # fake quantization (training forward: quantize -> dequantize -> bf16),
+    # GB/s over bf16 in + bf16 out, inputs rotated through 4 copies
+    cfg = up
+    copies = [a_up] + [a_up.clone() for _ in range(3)]
+    yq = torch.empty_like(a_up)
+    g_fq = mxl.mx_nv_global_scale(float(mxl.mx_tensor_amax(a_up).item()))
+    for name, fmt, rule, g in (("mxfp4_ceil", "mxfp4", "ceil", 1.0), ("mxfp8_ceil", "mxfp8", "ceil", 1.0),
+                               ("nvfp4", "nvfp4", None, g_fq)):
+        med, _, _ = _median_ms(torch, lambda i: mxl.mx_fake_quant(copies[i % 4], fmt, rule, g, out=yq), 20)
+        nbytes = cfg.m * cfg.k * 4
+        rows[f"fake_quant_{name}"] = {"us": round(med * 1e3, 2), "GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
+                                      "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                                      "bytes": nbytes}
+        log(f"fake_quant {name}: {med * 1e3:.2f} us {nbytes / (med * 1e-3) / 1e9:.0f} GB/s")
+    del copies, yq
+
     # decode-shaped GEMMs, weights rotated through 11 copies (> 512 MB).  A
     # call takes a few microseconds, less than the host needs to submit one,
     # so the 11 calls are captured once in a HIP graph and the graph is

@@ -58,6 +58,8 @@ def _load():
     L.mx_gemm_w4a16.argtypes = [i32, P, P, P, i64, i64, i64, f32, P, u32, P, sz, P]
     L.mx_gemm_w4a16_plan.restype = i32
     L.mx_gemm_w4a16_plan.argtypes = [i32, i64, i64, i64, ctypes.c_char_p, sz]
+    L.mx_fake_quant.restype = i32
+    L.mx_fake_quant.argtypes = [i32, i32, P, i64, i64, f32, P, P]
     L.mx_tensor_amax.restype, L.mx_tensor_amax.argtypes = i32, [P, i64, P, P]
     L.mx_nv_global_scale.restype, L.mx_nv_global_scale.argtypes = f32, [f32]
     L.mx_gemm_plan.restype = i32
@@ -98,6 +100,8 @@ def _fmt(f):
 
 
 def _rule(r):
+    if r is None:  # NVFP4 takes no rule
+        return 0
     return RULES[r] if isinstance(r, str) else int(r)
 
 
@@ -223,6 +227,35 @@ def mx_gemm_w4a16_plan(w_fmt: str, m: int, n: int, k: int) -> str:
     buf = ctypes.create_string_buffer(256)
     _check(lib.mx_gemm_w4a16_plan(_fmt(w_fmt), m, n, k, buf, 256), "mx_gemm_w4a16_plan")
     return buf.value.decode()
+
+
+def mx_fake_quant(x: torch.Tensor, fmt: str = "mxfp4", rule: str = "ceil", global_scale: float = 1.0,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """Quantize -> dequantize -> bf16 with the serving quantizer's codes
+    (mx_fake_quant of the C ABI).  x [rows, k] bf16; returns [rows, k] bf16."""
+    _need(x, torch.bfloat16, "input")
+    if x.dim() != 2:
+        raise ValueError("input must be [rows, k]")
+    y = torch.empty_like(x) if out is None else out
+    _need(y, torch.bfloat16, "out")
+    if y.shape != x.shape:
+        raise ValueError("out must have the input's shape")
+    st = lib.mx_fake_quant(_fmt(fmt), _rule(rule), _ptr(x), x.shape[0], x.shape[1], float(global_scale),
+                           _ptr(y), _stream(x))
+    _check(st, "mx_fake_quant")
+    return y
+
+
+class FakeQuantSTE(torch.autograd.Function):
+    """mx_fake_quant forward with the straight-through gradient (identity)."""
+
+    @staticmethod
+    def forward(ctx, x, fmt="mxfp4", rule="ceil", global_scale=1.0):
+        return mx_fake_quant(x, fmt, rule, global_scale)
+
+    @staticmethod
+    def backward(ctx, grad):
+        return grad, None, None, None
 
 
 def mx_tensor_amax(x: torch.Tensor) -> torch.Tensor:

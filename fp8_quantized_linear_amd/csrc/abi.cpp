@@ -17,6 +17,9 @@ hipError_t mxl_launch_mx_quantize(int elem, int rule, const void* x, int64_t tot
                                   hipStream_t stream);
 hipError_t mxl_launch_nv_quantize(const void* x, int64_t total, float g, void* q, void* s,
                                   hipStream_t stream);
+hipError_t mxl_launch_mx_fake_quant(int elem, int rule, const void* x, int64_t total, void* y,
+                                   hipStream_t stream);
+hipError_t mxl_launch_nv_fake_quant(const void* x, int64_t total, float g, void* y, hipStream_t stream);
 hipError_t mxl_launch_amax(const void* x, int64_t count, float* out, hipStream_t stream);
 hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq, const void* as, const void* wq,
                               const void* ws, int64_t m, int64_t n, int64_t k, void* y, int out_f32,
@@ -258,6 +261,21 @@ mx_status mx_gemm_w4a16_plan(mx_format w_fmt, int64_t m, int64_t n, int64_t k, c
     std::snprintf(name, len, "w4a16 %s %s", nv ? "nvfp4" : "mxfp4",
                   w4a16_use_decode(nv, m, n, k) ? mxl_w4a16_decode_config_name() : mxl_w4a16_gemm_config_name());
     return MX_OK;
+}
+
+mx_status mx_fake_quant(mx_format fmt, mx_scale_rule rule, const void* x_bf16, int64_t rows, int64_t k,
+                        float global_scale, void* y_bf16, mx_stream_t stream)
+{
+    mx_status st = check_quant_args(fmt, rule, x_bf16, rows, k, global_scale, y_bf16, y_bf16);
+    if (st != MX_OK) return st;
+    const int64_t total = rows * k;
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(x_bf16), ya = reinterpret_cast<uintptr_t>(y_bf16);
+    const uintptr_t bytes = (uintptr_t)total * 2u;
+    if (xa < ya + bytes && ya < xa + bytes) return MX_ERR_INVALID_ARG;  // overlapping x and y
+    if ((st = check_device()) != MX_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (fmt == MX_FMT_NVFP4) return from_hip(mxl_launch_nv_fake_quant(x_bf16, total, global_scale, y_bf16, hs));
+    return from_hip(mxl_launch_mx_fake_quant(fmt == MX_FMT_MXFP4 ? 0 : 1, (int)rule, x_bf16, total, y_bf16, hs));
 }
 
 mx_status mx_tensor_amax(const void* x_bf16, int64_t count, float* amax_dev, mx_stream_t stream)

@@ -106,6 +106,131 @@ __global__ __launch_bounds__(QUANT_THREADS) void nv_quantize_kernel(const uint4*
     }
 }
 
+// ---------------------------------------------------------------- fake quantization
+// The quantize -> dequantize round trip written back as bf16, the op that
+// runs in the training forward in place of the serving quantizer
+// (Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode": the training
+// quantizer is bit-identical to the serving one).  The codes are produced by
+// the same encoders as the quantizer kernels above, then decoded; each output
+// is the bf16 nearest to the exact dequantized value, ties to even.
+
+// 8 decoded element values (scale 1, exact in fp32) of the codes of one
+// 8-element group.
+template <int ELEM>
+__device__ __forceinline__ void decode8(uint4 v, int e, float f[8])
+{
+    if (ELEM == ELEM_E2M1) {
+        const uint32_t c = encode8_e2m1(v, e);
+        const float2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+        const float2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+        const float2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+        const float2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+        f[0] = f0[0]; f[1] = f0[1]; f[2] = f1[0]; f[3] = f1[1];
+        f[4] = f2[0]; f[5] = f2[1]; f[6] = f3[0]; f[7] = f3[1];
+    } else {
+        const uint2 c = encode8_e4m3(v, e);
+        const float2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.x, 1.0f, false);
+        const float2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.x, 1.0f, true);
+        const float2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.y, 1.0f, false);
+        const float2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.y, 1.0f, true);
+        f[0] = f0[0]; f[1] = f0[1]; f[2] = f1[0]; f[3] = f1[1];
+        f[4] = f2[0]; f[5] = f2[1]; f[6] = f3[0]; f[7] = f3[1];
+    }
+}
+
+// MX: element value times 2^e is exact in fp32 (ldexp keeps subnormal
+// results and overflows to infinity), so one fp32 -> bf16 rounding gives the
+// nearest bf16.  Same work mapping as mx_quantize_kernel; each group of 8
+// goes out as one 16-byte store.
+template <int ELEM, int RULE>
+__global__ __launch_bounds__(QUANT_THREADS) void mx_fake_quant_kernel(const uint4* __restrict__ x,
+                                                                       int64_t total,
+                                                                       uint4* __restrict__ y)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_base = ((int64_t)blockIdx.x * (QUANT_THREADS / 64) + (threadIdx.x >> 6)) * ELEMS_PER_WAVE;
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t g = wave_base / 8 + 64 * j + lane;
+        v[j] = (g * 8 < total) ? x[g] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t g = wave_base / 8 + 64 * j + lane;
+        const int e = scale_exponent<ELEM, RULE>(quad_max_u32(amax_bits8(v[j])));
+        float f[8];
+        decode8<ELEM>(v[j], e, f);
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = bf16x2_rne(__builtin_amdgcn_ldexpf(f[2 * i], e), __builtin_amdgcn_ldexpf(f[2 * i + 1], e));
+        if (g * 8 < total) y[g] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// bf16 pattern (sign clear) nearest to p / g for p >= 0 and g > 0, ties to
+// even.  q = p / g in fp32 is within an ulp of the quotient, far closer than
+// the bf16 spacing, so the answer is the bf16 truncation lo of q or lo + 1;
+// the midpoint m between them (9 significant bits) decides, compared as
+// m * g <=> p through one fused multiply-add, whose single rounding keeps the
+// sign of the exact difference.  A zero difference is a tie.
+__device__ __forceinline__ uint32_t bf16_nearest_quotient(float p, float g)
+{
+    const float q = p / g;
+    const uint32_t lo = __float_as_uint(q) >> 16;
+    if (lo >= 0x7F80u) return 0x7F80u;
+    const float m = __uint_as_float((lo << 16) | 0x8000u);
+    const float r = __builtin_fmaf(m, g, -p);
+    return r > 0.0f ? lo : (r < 0.0f ? lo + 1 : lo + (lo & 1u));
+}
+
+// E2M1 magnitude of a 3-bit code: 0, 0.5 for codes 0, 1; (1 + m/2) * 2^(x-1)
+// for exponent field x = c >> 1 and mantissa bit m otherwise.
+__device__ __forceinline__ float e2m1_magnitude(uint32_t c)
+{
+    return c < 2 ? 0.5f * (float)c : __uint_as_float((((c >> 1) + 126u) << 23) | ((c & 1u) << 22));
+}
+
+// NVFP4: the dequantized value e2m1 * s / g (e2m1 * s is exact in fp32) is
+// rounded once to bf16 by bf16_nearest_quotient.  Same mapping as
+// nv_quantize_kernel.
+__global__ __launch_bounds__(QUANT_THREADS) void nv_fake_quant_kernel(const uint4* __restrict__ x,
+                                                                       int64_t total, float gscale,
+                                                                       uint4* __restrict__ y)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_base = ((int64_t)blockIdx.x * (QUANT_THREADS / 64) + (threadIdx.x >> 6)) * ELEMS_PER_WAVE;
+    const double g = (double)gscale;
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t gi = wave_base / 8 + 64 * j + lane;
+        v[j] = (gi * 8 < total) ? x[gi] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t gi = wave_base / 8 + 64 * j + lane;
+        const uint32_t amax = pair_max_u32(amax_bits8(v[j]));
+        const double ag = (double)bf16_bits_to_float(amax) * g;   // exact
+        const uint32_t sc = e4m3_rne_f64(ag / 6.0);
+        const double sv = e4m3_value_f64(sc);
+        const float sf = (float)sv;                               // exact
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t b = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+            const double xg = (double)bf16_bits_to_float(b & 0x7FFFu) * g; // exact
+            const uint32_t mag = sv == 0.0 ? 0u : e2m1_rne_ratio(xg, sv);
+            const float p = e2m1_magnitude(mag) * sf;                  // exact
+            const uint32_t h = (p == 0.0f ? 0u : bf16_nearest_quotient(p, gscale)) | (b & 0x8000u);
+            o[i / 2] |= h << (16 * (i % 2));
+        }
+        if (gi * 8 < total) y[gi] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
 // amax of a bf16 tensor into *out (fp32 bits; non-negative floats order like
 // unsigned integers, so an integer atomic max is a float max).
 __global__ void amax_init_kernel(uint32_t* out) { *out = 0u; }
@@ -178,5 +303,35 @@ extern "C" hipError_t mxl_launch_amax(const void* x, int64_t count, float* out, 
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(x), count, reinterpret_cast<uint32_t*>(out));
+    return hipGetLastError();
+}
+
+extern "C" hipError_t mxl_launch_mx_fake_quant(int elem, int rule, const void* x, int64_t total, void* y,
+                                               hipStream_t stream)
+{
+    const int64_t blocks = (total + ELEMS_PER_BLOCK - 1) / ELEMS_PER_BLOCK;
+    dim3 grid((unsigned)blocks), block(QUANT_THREADS);
+    const uint4* xv = static_cast<const uint4*>(x);
+    uint4* yv = static_cast<uint4*>(y);
+#define MXL_F(E, R) hipLaunchKernelGGL((mx_fake_quant_kernel<E, R>), grid, block, 0, stream, xv, total, yv)
+    if (elem == ELEM_E2M1) {
+        if (rule == RULE_FLOOR) MXL_F(ELEM_E2M1, RULE_FLOOR);
+        else if (rule == RULE_CEIL) MXL_F(ELEM_E2M1, RULE_CEIL);
+        else MXL_F(ELEM_E2M1, RULE_EVEN);
+    } else {
+        if (rule == RULE_FLOOR) MXL_F(ELEM_E4M3, RULE_FLOOR);
+        else if (rule == RULE_CEIL) MXL_F(ELEM_E4M3, RULE_CEIL);
+        else MXL_F(ELEM_E4M3, RULE_EVEN);
+    }
+#undef MXL_F
+    return hipGetLastError();
+}
+
+extern "C" hipError_t mxl_launch_nv_fake_quant(const void* x, int64_t total, float g, void* y,
+                                               hipStream_t stream)
+{
+    const int64_t blocks = (total + ELEMS_PER_BLOCK - 1) / ELEMS_PER_BLOCK;
+    hipLaunchKernelGGL(nv_fake_quant_kernel, dim3((unsigned)blocks), dim3(QUANT_THREADS), 0, stream,
+                       static_cast<const uint4*>(x), total, g, static_cast<uint4*>(y));
     return hipGetLastError();
 }

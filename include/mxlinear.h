@@ -90,7 +90,7 @@ typedef enum {
                           * the 1e-4 bound that the default path meets */
 
 /* ABI version of this header (bumped on any signature change). */
-#define MXLINEAR_ABI_VERSION 2
+#define MXLINEAR_ABI_VERSION 3
 int mx_abi_version(void);
 
 /* Static text for a status code; never NULL. */
@@ -198,6 +198,28 @@ mx_status mx_gemm_w4a16(mx_format w_fmt, const void* a_bf16, const void* w_q, co
  * mx_gemm_w4a16 would launch for this shape.  Pure host logic.
  */
 mx_status mx_gemm_w4a16_plan(mx_format w_fmt, int64_t m, int64_t n, int64_t k, char* name, size_t len);
+
+/*
+ * mx_fake_quant -- training-time fake quantization: the quantize ->
+ * dequantize round trip written back as bf16.  Quantization-aware
+ * distillation runs it in the student's forward on every quantized linear,
+ * weights with the EVEN rule and per-token activations with the CEIL rule
+ * (Qwen3.5-27B-MXFP4-QAD-W4A4-LR1e-5-s1000, "How this checkpoint was
+ * produced", Training row), and its activation quantizer is bit-identical to
+ * the serving one (Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode").
+ *
+ * x_bf16 [rows, k] bf16 in; y_bf16 [rows, k] bf16 out, which must not
+ * overlap x (MX_ERR_INVALID_ARG).  The codes and scales are exactly those
+ * that mx_quantize_act computes for the same fmt, rule and global_scale; each
+ * output is the bf16 nearest to the dequantized value, ties to even:
+ * code * 2^(e) for MXFP4/MXFP8 (exact in bf16 unless it passes the largest
+ * finite bf16, which gives infinity), code * s / g for NVFP4 (one rounding
+ * of the exact quotient).  A zero keeps the input's sign.  The straight-
+ * through gradient of the op is the identity and needs no call.
+ * Requirements and errors as mx_quantize_act.
+ */
+mx_status mx_fake_quant(mx_format fmt, mx_scale_rule rule, const void* x_bf16, int64_t rows, int64_t k,
+                        float global_scale, void* y_bf16, mx_stream_t stream);
 
 /*
  * mx_tensor_amax -- largest |x| of a bf16 tensor of `count` elements, written

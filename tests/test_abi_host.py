@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("mx_pack_weights", "mx_quantize_act", "mx_gemm", "mx_gemm_fused", "nv_gemm",
-              "mx_gemm_w4a16", "mx_gemm_w4a16_plan",
+              "mx_gemm_w4a16", "mx_gemm_w4a16_plan", "mx_fake_quant",
               "mx_tensor_amax", "mx_nv_global_scale", "mx_gemm_plan", "mx_status_string",
               "mx_abi_version"):
         assert n in names
@@ -132,6 +132,26 @@ def test_w4a16_validation():
     assert g(m=0) == SHAPE
     assert g(wq=BAD_ALIGN) == ALIGN
     assert g(fmt=2, k=48) in (OK, UNSUPPORTED, HIPERR)   # validation passes
+
+
+def test_fake_quant_validation():
+    f = L.mx_fake_quant
+    def g(fmt=0, rule=1, x=GOOD, rows=4, k=64, gs=1.0, y=P(0x20000)):
+        return f(fmt, rule, x, rows, k, gs, y, None)
+    assert g(fmt=7) == INVALID
+    assert g(rule=9) == INVALID
+    assert g(fmt=2, rule=9) in (OK, UNSUPPORTED, HIPERR)   # NVFP4 ignores the rule
+    assert g(x=None) == INVALID
+    assert g(y=None) == INVALID
+    assert g(fmt=2, gs=0.0) == INVALID
+    assert g(fmt=2, gs=float("inf")) == INVALID
+    assert g(y=P(0x10000 + 64 * 4 * 2 - 16)) == INVALID      # y overlaps the end of x
+    assert g(k=48) == SHAPE
+    assert g(fmt=2, k=40) == SHAPE
+    assert g(rows=0) == SHAPE
+    assert g(x=BAD_ALIGN) == ALIGN
+    assert g(y=P(0x20008)) == ALIGN
+    assert g(y=P(0x10000 + 64 * 4 * 2)) in (OK, UNSUPPORTED, HIPERR)  # adjacent, not overlapping
 
 
 def test_plan_names_the_kernel():
