@@ -178,30 +178,46 @@ __device__ __forceinline__ double e4m3_value_f64(uint32_t c)
 // RNE_E4M3 of a non-negative double v (saturating at 448): v >= 448 -> 0x7E;
 // below 2^-6 the subnormal step 2^-9 applies; otherwise the double is rounded
 // to 3 mantissa bits (ties to even) on its bit pattern.
+// All three forms are computed and one is selected, so the code has no branch.
 __device__ __forceinline__ uint32_t e4m3_rne_f64(double v)
 {
-    if (v >= 448.0) return 0x7Eu;
-    if (v < 0x1p-6) return (uint32_t)__builtin_rint(v * 512.0); // 0..8; 8 is 2^-6 (code 0x08)
+    const uint32_t sub = (uint32_t)__builtin_rint(__builtin_fmin(v, 0x1p-6) * 512.0); // 0..8; 8 is 2^-6
     uint64_t b = (uint64_t)__double_as_longlong(v);
     b += ((uint64_t)1 << 48) - 1 + ((b >> 49) & 1);              // RNE at mantissa bit 49
-    const uint32_t top = (uint32_t)(b >> 49);                    // exponent(11) | mantissa(3)
-    return top - ((1023u - 7u) << 3);
+    const uint32_t nrm = (uint32_t)(b >> 49) - ((1023u - 7u) << 3); // exponent(11) | mantissa(3), rebiased
+    return v >= 448.0 ? 0x7Eu : (v < 0x1p-6 ? sub : nrm);
 }
 
-// RNE_E2M1 of the exact real num/den (num >= 0, den > 0), by comparisons
-// num <=> t * den against the 7 rounding thresholds (exact in fp64 here:
-// num has at most 32 significant bits, t * den at most 7).
-__device__ __forceinline__ uint32_t e2m1_rne_ratio(double num, double den)
+// The 7 rounding thresholds of E2M1 (midpoints between neighbouring
+// magnitudes) times a block scale s: t * s is exact in fp32 (t has at most 3
+// significant bits, an E4M3 s at most 4).
+__device__ __forceinline__ void e2m1_thresholds(float s, float t[7])
 {
-    uint32_t c = 0;
-    c += num > 0.25 * den;
-    c += num >= 0.75 * den;
-    c += num > 1.25 * den;
-    c += num >= 1.75 * den;
-    c += num > 2.5 * den;
-    c += num >= 3.5 * den;
-    c += num > 5.0 * den;
-    return c;
+    t[0] = 0.25f * s; t[1] = 0.75f * s; t[2] = 1.25f * s; t[3] = 1.75f * s;
+    t[4] = 2.5f * s;  t[5] = 3.5f * s;  t[6] = 5.0f * s;
+}
+
+// RNE_E2M1 code (magnitude) of the exact real xa * g / s for xa >= 0, g > 0,
+// given the thresholds t of s > 0: the number of thresholds that xa * g
+// passes, where landing exactly on one goes to the even code, so the
+// thresholds below codes 1, 3, 5, 7 count only when passed strictly.  Each
+// comparison is the sign bit of one fma, the exact difference rounded once:
+// fma(-xa, g, t) < 0 for "xa * g > t" and fma(xa, g, -t) < 0 for
+// "xa * g < t"; an exact zero difference rounds to +0, so a tie is never
+// negative.  No difference rounds to zero from a nonzero value: near a
+// threshold xa * g >= 2^-11 and every bit of xa * g and t lies above 2^-42,
+// far from fp32's subnormal step.  An overflow of xa * g gives -inf / +inf,
+// which still compare correctly.
+__device__ __forceinline__ uint32_t e2m1_rne_fma(float xa, float g, const float t[7])
+{
+    const uint32_t above = (__float_as_uint(__builtin_fmaf(-xa, g, t[0])) >> 31) +
+                           (__float_as_uint(__builtin_fmaf(-xa, g, t[2])) >> 31) +
+                           (__float_as_uint(__builtin_fmaf(-xa, g, t[4])) >> 31) +
+                           (__float_as_uint(__builtin_fmaf(-xa, g, t[6])) >> 31);
+    const uint32_t below = (__float_as_uint(__builtin_fmaf(xa, g, -t[1])) >> 31) +
+                           (__float_as_uint(__builtin_fmaf(xa, g, -t[3])) >> 31) +
+                           (__float_as_uint(__builtin_fmaf(xa, g, -t[5])) >> 31);
+    return above + 3u - below;
 }
 
 // fp32 -> bf16, round to nearest even, on the hardware converter

@@ -64,11 +64,33 @@ __global__ __launch_bounds__(QUANT_THREADS) void mx_quantize_kernel(const uint4*
 }
 
 // NVFP4: a block of 16 is a lane pair.  The block scale and the element codes
-// are roundings of exact reals (amax * g / 6 and x * g / s): x * g is exact in
-// fp64 (8 + 24 significant bits), and the element thresholds are compared as
-// x * g <=> t * s, exact as well.  The scale's quotient by 6 is evaluated in
-// fp64; it can only meet an E4M3 rounding midpoint when the quotient is
-// exactly that midpoint, which fp64 then represents exactly.
+// are roundings of exact reals (amax * g / 6 and x * g / s).  amax * g is
+// exact in fp64 (8 + 24 significant bits); its quotient by 6 is evaluated in
+// fp64 and can only meet an E4M3 rounding midpoint when the quotient is
+// exactly that midpoint, which fp64 then represents exactly.  The element
+// thresholds are compared as x * g <=> t * s by the sign of one fma
+// (e2m1_rne_fma), which is exact.  Returns the 8 codes of the lane's group
+// (element i in nibble i) and the block's scale code and value.
+__device__ __forceinline__ uint32_t nv_encode8(uint4 v, float gscale, uint32_t& sc, float& sf)
+{
+    const uint32_t amax = pair_max_u32(amax_bits8(v));
+    const double ag = (double)bf16_bits_to_float(amax) * (double)gscale;   // exact
+    sc = e4m3_rne_f64(ag / 6.0);
+    sf = (float)e4m3_value_f64(sc);                                       // exact
+    float t[7];
+    e2m1_thresholds(sf, t);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t codes = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t b = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+        const uint32_t c = e2m1_rne_fma(bf16_bits_to_float(b & 0x7FFFu), gscale, t);
+        const uint32_t mag = sf == 0.0f ? 0u : c;   // s == 0: signed zeros
+        codes |= (mag | ((b >> 15) << 3)) << (4 * i);
+    }
+    return codes;
+}
+
 __global__ __launch_bounds__(QUANT_THREADS) void nv_quantize_kernel(const uint4* __restrict__ x,
                                                                      int64_t total, float gscale,
                                                                      uint8_t* __restrict__ q,
@@ -76,7 +98,6 @@ __global__ __launch_bounds__(QUANT_THREADS) void nv_quantize_kernel(const uint4*
 {
     const int lane = threadIdx.x & 63;
     const int64_t wave_base = ((int64_t)blockIdx.x * (QUANT_THREADS / 64) + (threadIdx.x >> 6)) * ELEMS_PER_WAVE;
-    const double g = (double)gscale;
     uint4 v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -86,19 +107,9 @@ __global__ __launch_bounds__(QUANT_THREADS) void nv_quantize_kernel(const uint4*
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t gi = wave_base / 8 + 64 * j + lane;
-        const uint32_t amax = pair_max_u32(amax_bits8(v[j]));
-        const double ag = (double)bf16_bits_to_float(amax) * g;   // exact
-        const uint32_t sc = e4m3_rne_f64(ag / 6.0);
-        const double sv = e4m3_value_f64(sc);
-        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-        uint32_t codes = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t b = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
-            const double xg = (double)bf16_bits_to_float(b & 0x7FFFu) * g; // exact
-            const uint32_t mag = sv == 0.0 ? 0u : e2m1_rne_ratio(xg, sv);
-            codes |= (mag | ((b >> 15) << 3)) << (4 * i);
-        }
+        uint32_t sc;
+        float sf;
+        const uint32_t codes = nv_encode8(v[j], gscale, sc, sf);
         if (gi * 8 < total) {
             reinterpret_cast<uint32_t*>(q)[gi] = codes;
             if ((lane & 1) == 0) s[gi >> 1] = (uint8_t)sc;
@@ -170,38 +181,36 @@ __global__ __launch_bounds__(QUANT_THREADS) void mx_fake_quant_kernel(const uint
 }
 
 // bf16 pattern (sign clear) nearest to p / g for p >= 0 and g > 0, ties to
-// even.  q = p / g in fp32 is within an ulp of the quotient, far closer than
-// the bf16 spacing, so the answer is the bf16 truncation lo of q or lo + 1;
-// the midpoint m between them (9 significant bits) decides, compared as
-// m * g <=> p through one fused multiply-add, whose single rounding keeps the
-// sign of the exact difference.  A zero difference is a tie.
-__device__ __forceinline__ uint32_t bf16_nearest_quotient(float p, float g)
+// even.  q = p * (1/g), with 1/g a normal fp32 (ginv; DIV divides instead,
+// for g beyond 2^126), is within 2 ulp of the quotient, far closer than the
+// bf16 spacing, so the answer is the bf16 truncation lo of q or lo + 1; the
+// midpoint m between them (9 significant bits) decides, compared as
+// m * g <=> p through one fused multiply-add: its result is negative exactly
+// when the quotient lies above m, and +0 exactly on a tie.  A quotient
+// beyond the fp32 range (q = inf, lo = 0x7F80) stays infinity.
+template <bool DIV>
+__device__ __forceinline__ uint32_t bf16_nearest_quotient(float p, float g, float ginv)
 {
-    const float q = p / g;
+    const float q = DIV ? p / g : p * ginv;
     const uint32_t lo = __float_as_uint(q) >> 16;
-    if (lo >= 0x7F80u) return 0x7F80u;
     const float m = __uint_as_float((lo << 16) | 0x8000u);
-    const float r = __builtin_fmaf(m, g, -p);
-    return r > 0.0f ? lo : (r < 0.0f ? lo + 1 : lo + (lo & 1u));
+    const uint32_t rb = __float_as_uint(__builtin_fmaf(m, g, -p));
+    const uint32_t up = (rb >> 31) + (rb == 0u ? (lo & 1u) : 0u);
+    const uint32_t r = lo + up;
+    return r < 0x7F80u ? r : 0x7F80u;
 }
 
-// E2M1 magnitude of a 3-bit code: 0, 0.5 for codes 0, 1; (1 + m/2) * 2^(x-1)
-// for exponent field x = c >> 1 and mantissa bit m otherwise.
-__device__ __forceinline__ float e2m1_magnitude(uint32_t c)
-{
-    return c < 2 ? 0.5f * (float)c : __uint_as_float((((c >> 1) + 126u) << 23) | ((c & 1u) << 22));
-}
-
-// NVFP4: the dequantized value e2m1 * s / g (e2m1 * s is exact in fp32) is
-// rounded once to bf16 by bf16_nearest_quotient.  Same mapping as
-// nv_quantize_kernel.
-__global__ __launch_bounds__(QUANT_THREADS) void nv_fake_quant_kernel(const uint4* __restrict__ x,
-                                                                       int64_t total, float gscale,
-                                                                       uint4* __restrict__ y)
+// NVFP4: the dequantized value e2m1 * s / g is rounded once to bf16 by
+// bf16_nearest_quotient; e2m1 * s comes from the codes through the hardware
+// decoder (scale 1) and one multiply, both exact.  Same mapping as
+// nv_quantize_kernel; the quotient's form is chosen once per launch.
+template <bool DIV>
+__device__ __forceinline__ void nv_fake_quant_body(const uint4* __restrict__ x, int64_t total, float gscale,
+                                                   uint4* __restrict__ y)
 {
     const int lane = threadIdx.x & 63;
     const int64_t wave_base = ((int64_t)blockIdx.x * (QUANT_THREADS / 64) + (threadIdx.x >> 6)) * ELEMS_PER_WAVE;
-    const double g = (double)gscale;
+    const float ginv = DIV ? 0.0f : 1.0f / gscale;
     uint4 v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -211,24 +220,36 @@ __global__ __launch_bounds__(QUANT_THREADS) void nv_fake_quant_kernel(const uint
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t gi = wave_base / 8 + 64 * j + lane;
-        const uint32_t amax = pair_max_u32(amax_bits8(v[j]));
-        const double ag = (double)bf16_bits_to_float(amax) * g;   // exact
-        const uint32_t sc = e4m3_rne_f64(ag / 6.0);
-        const double sv = e4m3_value_f64(sc);
-        const float sf = (float)sv;                               // exact
+        uint32_t sc;
+        float sf;
+        const uint32_t codes = nv_encode8(v[j], gscale, sc, sf);
+        float f[8];
+        {
+            const float2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+            const float2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+            const float2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+            const float2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+            f[0] = f0[0]; f[1] = f0[1]; f[2] = f1[0]; f[3] = f1[1];
+            f[4] = f2[0]; f[5] = f2[1]; f[6] = f3[0]; f[7] = f3[1];
+        }
         const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-        uint32_t o[4] = {0, 0, 0, 0};
+        uint32_t o[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t b = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
-            const double xg = (double)bf16_bits_to_float(b & 0x7FFFu) * g; // exact
-            const uint32_t mag = sv == 0.0 ? 0u : e2m1_rne_ratio(xg, sv);
-            const float p = e2m1_magnitude(mag) * sf;                  // exact
-            const uint32_t h = (p == 0.0f ? 0u : bf16_nearest_quotient(p, gscale)) | (b & 0x8000u);
-            o[i / 2] |= h << (16 * (i % 2));
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = bf16_nearest_quotient<DIV>(__builtin_fabsf(f[2 * i]) * sf, gscale, ginv);
+            const uint32_t hi = bf16_nearest_quotient<DIV>(__builtin_fabsf(f[2 * i + 1]) * sf, gscale, ginv);
+            o[i] = (lo | (hi << 16)) | (w[i] & 0x80008000u);   // the input's signs are the codes' signs
         }
         if (gi * 8 < total) y[gi] = make_uint4(o[0], o[1], o[2], o[3]);
     }
+}
+
+__global__ __launch_bounds__(QUANT_THREADS) void nv_fake_quant_kernel(const uint4* __restrict__ x,
+                                                                       int64_t total, float gscale,
+                                                                       uint4* __restrict__ y)
+{
+    if (gscale < 0x1p126f) nv_fake_quant_body<false>(x, total, gscale, y);
+    else nv_fake_quant_body<true>(x, total, gscale, y);
 }
 
 // amax of a bf16 tensor into *out (fp32 bits; non-negative floats order like
