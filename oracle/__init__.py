@@ -16,6 +16,7 @@ Every function states the passage it follows in the C source; in short:
   (Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode"), FLOOR (OCP);
 * NVFP4 global and block scales (Qwen3.5-27B-NVFP4-RTN-weight-only and
   Qwen3.5-27B-NVFP4-GPTQ, introductions);
+* the SwiGLU activation of the gated MLP (fused gate_up projection);
 * fake quantization, the quantize -> dequantize round trip rounded to bf16
   (Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode";
   Qwen3.5-27B-MXFP4-QAD-W4A4-LR1e-5-s1000, "How this checkpoint was
@@ -288,6 +289,27 @@ def fake_quant(fmt: str, rule, x_bf16: np.ndarray, g=None, nthreads=None) -> np.
     if rc != 0:
         raise ValueError("bad format or k not a multiple of the block")
     return out
+
+
+def swiglu(gate, up) -> np.ndarray:
+    """The gated MLP activation between the fused gate_up projection and the
+    down projection: h = silu(gate) * up = gate * up / (1 + e^-gate),
+    elementwise in fp64.  (The cards name vLLM's fused gate_up_proj,
+    Qwen3.8-27B-MXFP8Attn-MXFP4MLP-lmheadMXFP4 section 2; the Qwen MLP gates
+    with SiLU.)"""
+    g = np.asarray(gate, np.float64)
+    u = np.asarray(up, np.float64)
+    with np.errstate(over="ignore"):
+        return g * u / (1.0 + np.exp(-g))
+
+
+def mlp_swiglu(aq, a_s, wq, w_s, m: int, inter: int, k: int, nthreads=None):
+    """The gate_up projection of MXFP4 operands followed by SwiGLU, exactly:
+    W is [2 * inter, k] with the gate rows first, then the up rows.  Returns
+    (h, gate, up, S_gate, S_up) with S the absolute sums of the products."""
+    y, sa = mx_gemm("e2m1", aq, a_s, "e2m1", wq, w_s, m, 2 * inter, k, nthreads)
+    gate, up = y[:, :inter], y[:, inter:]
+    return swiglu(gate, up), gate, up, sa[:, :inter], sa[:, inter:]
 
 
 # ---------------------------------------------------------------- compositions

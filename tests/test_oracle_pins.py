@@ -693,3 +693,40 @@ def test_fake_quant_matches_dequantized_codes():
     assert np.array_equal(got, want)
     assert np.array_equal(torch.from_numpy(d).float().numpy(),
                           torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+# ------------------------------------------------------------------ SwiGLU
+def test_swiglu_matches_torch_silu():
+    rng = np.random.default_rng(90)
+    g = rng.standard_normal(4000) * 6
+    u = rng.standard_normal(4000) * 3
+    want = (torch.nn.functional.silu(torch.from_numpy(g)) * torch.from_numpy(u)).numpy()
+    np.testing.assert_allclose(oracle.swiglu(g, u), want, rtol=1e-14, atol=1e-300)
+
+
+def test_swiglu_special_values():
+    # sigmoid(1) = 1 / (1 + 1/e) = 0.7310585786300049 (tabulated value)
+    assert abs(oracle.swiglu(1.0, 1.0) - 0.7310585786300049) < 1e-15
+    assert oracle.swiglu(0.0, 5.0) == 0.0
+    g = np.array([40.0, 50.0, 100.0])
+    np.testing.assert_array_equal(oracle.swiglu(g, 3.0), 3.0 * g)       # e^-g below half an ulp
+    assert oracle.swiglu(-1000.0, 2.0) == 0.0                            # e^1000 overflows to inf
+    # silu(-x) = silu(x) - x
+    x = np.linspace(-9, 9, 37)
+    np.testing.assert_allclose(oracle.swiglu(-x, 1.0), oracle.swiglu(x, 1.0) - x, rtol=1e-13, atol=1e-14)
+
+
+def test_mlp_swiglu_composes_gate_and_up():
+    rng = np.random.default_rng(91)
+    m, inter, k = 5, 64, 96
+    a = _bf16_bits(rng.standard_normal((m, k)))
+    w = _bf16_bits(rng.standard_normal((2 * inter, k)) * 0.1)
+    aq, a_s = oracle.mx_quantize("e2m1", "ceil", a)
+    wq, w_s = oracle.mx_quantize("e2m1", "even", w)
+    h, gate, up, sg, su = oracle.mlp_swiglu(aq, a_s, wq, w_s, m, inter, k)
+    ad = oracle.mx_dequantize("e2m1", aq, a_s, m, k)
+    wd = oracle.mx_dequantize("e2m1", wq, w_s, 2 * inter, k)
+    np.testing.assert_allclose(gate, ad @ wd[:inter].T, rtol=1e-12, atol=1e-300)   # gate rows first
+    np.testing.assert_allclose(up, ad @ wd[inter:].T, rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(sg, np.abs(ad) @ np.abs(wd[:inter]).T, rtol=1e-12)
+    np.testing.assert_allclose(h, oracle.swiglu(gate, up), rtol=0)
