@@ -245,6 +245,36 @@ def extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_d
                                      "bytes": nbytes}
         del copies
 
+    # the gated MLP block: gate_up projection (8192 x 5120 x 34816) with the
+    # SwiGLU + CEIL MXFP4 epilogue fused, then the down projection; against
+    # the unfused chain (bf16 gate_up output, standalone SwiGLU quantization)
+    mlp = W.MLP_GATE_UP
+    inter = mlp.n // 2
+    w_gu = to_dev(mlp.weights())
+    wq_gu, ws_gu = mxl.mx_pack_weights(w_gu, "mxfp4", "even")
+    del w_gu
+    wq_il, ws_il = mxl.interleave_gate_up(wq_gu), mxl.interleave_gate_up(ws_gu)
+    aq_m, as_m = mxl.mx_quantize_act(a_up, "mxfp4", "ceil")
+    hq = torch.empty((mlp.m, inter // 2), dtype=torch.uint8, device=dev)
+    hs = torch.empty((mlp.m, inter // 32), dtype=torch.uint8, device=dev)
+    y_gu = torch.empty((mlp.m, mlp.n), dtype=torch.bfloat16, device=dev)
+    y_dn = torch.empty((down.m, down.n), dtype=torch.bfloat16, device=dev)
+    t_fused, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm_swiglu_quant(aq_m, as_m, wq_il, ws_il, mlp.k,
+                                                                         out=(hq, hs)), 10)
+    t_gemm, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm(aq_m, as_m, wq_gu, ws_gu, mlp.k, y=y_gu), 10)
+    t_act, _, _ = _median_ms(torch, lambda i: mxl.mx_swiglu_quant(y_gu, out=(hq, hs)), 10)
+    t_down, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm(hq, hs, wq_dn, ws_dn, down.k, y=y_dn), 10)
+    block_flops = mlp.flops + down.flops
+    rows["mlp_block"] = {
+        "gate_up_swiglu_fused_us": round(t_fused * 1e3, 1),
+        "gate_up_gemm_us": round(t_gemm * 1e3, 1), "swiglu_quant_us": round(t_act * 1e3, 1),
+        "down_us": round(t_down * 1e3, 1),
+        "fused_block_tflops": round(block_flops / ((t_fused + t_down) * 1e-3) / 1e12, 1),
+        "unfused_block_tflops": round(block_flops / ((t_gemm + t_act + t_down) * 1e-3) / 1e12, 1)}
+    log(f"mlp block: fused gate_up+swiglu {t_fused * 1e3:.1f} us vs gemm {t_gemm * 1e3:.1f} + act "
+        f"{t_act * 1e3:.1f} us; down {t_down * 1e3:.1f} us")
+    del wq_gu, ws_gu, wq_il, ws_il, y_gu, y_dn, hq, hs
+
     # fake quantization (training forward: quantize -> dequantize -> bf16),
     # GB/s over bf16 in + bf16 out, inputs rotated through 4 copies
     cfg = up

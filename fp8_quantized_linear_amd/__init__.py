@@ -58,6 +58,12 @@ def _load():
     L.mx_gemm_w4a16.argtypes = [i32, P, P, P, i64, i64, i64, f32, P, u32, P, sz, P]
     L.mx_gemm_w4a16_plan.restype = i32
     L.mx_gemm_w4a16_plan.argtypes = [i32, i64, i64, i64, ctypes.c_char_p, sz]
+    L.mx_gemm_swiglu_quant.restype = i32
+    L.mx_gemm_swiglu_quant.argtypes = [P, P, P, P, i64, i64, i64, P, P, P]
+    L.mx_gemm_swiglu_quant_plan.restype = i32
+    L.mx_gemm_swiglu_quant_plan.argtypes = [i64, i64, i64, ctypes.c_char_p, sz]
+    L.mx_swiglu_quant.restype = i32
+    L.mx_swiglu_quant.argtypes = [P, i64, i64, P, P, P]
     L.mx_fake_quant.restype = i32
     L.mx_fake_quant.argtypes = [i32, i32, P, i64, i64, f32, P, P]
     L.mx_tensor_amax.restype, L.mx_tensor_amax.argtypes = i32, [P, i64, P, P]
@@ -226,6 +232,65 @@ def mx_gemm_w4a16_plan(w_fmt: str, m: int, n: int, k: int) -> str:
     """Name of the kernel mx_gemm_w4a16 would launch for this shape."""
     buf = ctypes.create_string_buffer(256)
     _check(lib.mx_gemm_w4a16_plan(_fmt(w_fmt), m, n, k, buf, 256), "mx_gemm_w4a16_plan")
+    return buf.value.decode()
+
+
+def gate_up_interleave_index(inter: int, device=None) -> torch.Tensor:
+    """Row order that turns a [gate; up] weight ([2*inter, k], gate rows
+    first) into the layout mx_gemm_swiglu_quant reads: 32 gate rows, then
+    the 32 up rows of the same columns, and so on."""
+    if inter % 32 != 0:
+        raise ValueError("inter must be a multiple of 32")
+    c = torch.arange(inter // 32, device=device).repeat_interleave(64) * 32
+    r = torch.arange(64, device=device).repeat(inter // 32)
+    return torch.where(r < 32, c + r, inter + c + r - 32)
+
+
+def interleave_gate_up(w: torch.Tensor) -> torch.Tensor:
+    """Rows of a [gate; up] tensor (bf16 weights, or packed codes or scales,
+    since packing is row-local) in the order mx_gemm_swiglu_quant reads."""
+    return w.index_select(0, gate_up_interleave_index(w.shape[0] // 2, w.device)).contiguous()
+
+
+def mx_swiglu_quant(x: torch.Tensor, out=None):
+    """x [m, 2*inter] bf16 (gate columns, then up) -> MXFP4 codes [m, inter/2]
+    and CEIL scales [m, inter/32] of SwiGLU(gate, up)."""
+    _need(x, torch.bfloat16, "input")
+    if x.dim() != 2 or x.shape[1] % 2:
+        raise ValueError("input must be [m, 2*inter]")
+    m, inter = x.shape[0], x.shape[1] // 2
+    if out is None:
+        q = torch.empty((m, inter // 2), dtype=torch.uint8, device=x.device)
+        s = torch.empty((m, inter // 32), dtype=torch.uint8, device=x.device)
+    else:
+        q, s = out
+    _check(lib.mx_swiglu_quant(_ptr(x), m, inter, _ptr(q), _ptr(s), _stream(x)), "mx_swiglu_quant")
+    return q, s
+
+
+def mx_gemm_swiglu_quant(a_q, a_s, w_q, w_s, k: int, out=None):
+    """Fused gate_up GEMM + SwiGLU + CEIL MXFP4 quantization of h.  w_q/w_s
+    are the interleaved [2*inter, k] weights (interleave_gate_up)."""
+    for t, nm in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
+        _need(t, torch.uint8, nm)
+    m, inter = a_q.shape[0], w_q.shape[0] // 2
+    if a_q.shape[1] != k // 2 or w_q.shape != (2 * inter, k // 2):
+        raise ValueError("code tensors do not match k")
+    if a_s.shape != (m, k // 32) or w_s.shape != (2 * inter, k // 32):
+        raise ValueError("scale tensors do not match k")
+    if out is None:
+        q = torch.empty((m, inter // 2), dtype=torch.uint8, device=a_q.device)
+        s = torch.empty((m, inter // 32), dtype=torch.uint8, device=a_q.device)
+    else:
+        q, s = out
+    _check(lib.mx_gemm_swiglu_quant(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, inter, k, _ptr(q), _ptr(s),
+                                    _stream(a_q)), "mx_gemm_swiglu_quant")
+    return q, s
+
+
+def mx_gemm_swiglu_quant_plan(m: int, inter: int, k: int) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _check(lib.mx_gemm_swiglu_quant_plan(m, inter, k, buf, 512), "mx_gemm_swiglu_quant_plan")
     return buf.value.decode()
 
 

@@ -20,6 +20,12 @@ hipError_t mxl_launch_nv_quantize(const void* x, int64_t total, float g, void* q
 hipError_t mxl_launch_mx_fake_quant(int elem, int rule, const void* x, int64_t total, void* y,
                                    hipStream_t stream);
 hipError_t mxl_launch_nv_fake_quant(const void* x, int64_t total, float g, void* y, hipStream_t stream);
+hipError_t mxl_launch_swiglu_quant(const void* x, int64_t rows, int64_t inter, void* q, void* s,
+                                  hipStream_t stream);
+hipError_t mxl_launch_mx_prefill_swiglu(const void* aq, const void* as, const void* wq, const void* ws, int64_t m,
+                                        int64_t n, int64_t k, void* h_q, void* h_s, hipStream_t stream);
+int mxl_prefill_ok(int64_t m, int64_t n, int64_t k);
+const char* mxl_prefill_swiglu_config_name(void);
 hipError_t mxl_launch_amax(const void* x, int64_t count, float* out, hipStream_t stream);
 hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq, const void* as, const void* wq,
                               const void* ws, int64_t m, int64_t n, int64_t k, void* y, int out_f32,
@@ -276,6 +282,46 @@ mx_status mx_fake_quant(mx_format fmt, mx_scale_rule rule, const void* x_bf16, i
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (fmt == MX_FMT_NVFP4) return from_hip(mxl_launch_nv_fake_quant(x_bf16, total, global_scale, y_bf16, hs));
     return from_hip(mxl_launch_mx_fake_quant(fmt == MX_FMT_MXFP4 ? 0 : 1, (int)rule, x_bf16, total, y_bf16, hs));
+}
+
+mx_status mx_swiglu_quant(const void* x_bf16, int64_t m, int64_t inter, void* h_q, void* h_s, mx_stream_t stream)
+{
+    if (!x_bf16 || !h_q || !h_s) return MX_ERR_INVALID_ARG;
+    if (m < 1 || m > kMaxDim || inter < 32 || inter % 32 != 0 || inter > kMaxDim / 2) return MX_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(h_q) || !aligned16(h_s)) return MX_ERR_ALIGN;
+    mx_status st = check_device();
+    if (st != MX_OK) return st;
+    return from_hip(mxl_launch_swiglu_quant(x_bf16, m, inter, h_q, h_s, static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_gemm_swiglu_quant(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t m,
+                               int64_t inter, int64_t k, void* h_q, void* h_s, mx_stream_t stream)
+{
+    if (!a_q || !a_s || !w_q || !w_s || !h_q || !h_s) return MX_ERR_INVALID_ARG;
+    if (inter < 32 || inter % 32 != 0 || inter > kMaxDim / 2) return MX_ERR_SHAPE;
+    mx_status st = check_gemm_shape(m, 2 * inter, k, 32);
+    if (st != MX_OK) return st;
+    if (!mxl_prefill_ok(m, 2 * inter, k)) return MX_ERR_UNSUPPORTED;
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(h_q) ||
+        !aligned16(h_s))
+        return MX_ERR_ALIGN;
+    if ((st = check_device()) != MX_OK) return st;
+    if (log_enabled())
+        std::fprintf(stderr, "[mxlinear] mx_gemm_swiglu_quant m=%lld inter=%lld k=%lld -> %s\n", (long long)m,
+                     (long long)inter, (long long)k, mxl_prefill_swiglu_config_name());
+    return from_hip(mxl_launch_mx_prefill_swiglu(a_q, a_s, w_q, w_s, m, 2 * inter, k, h_q, h_s,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_gemm_swiglu_quant_plan(int64_t m, int64_t inter, int64_t k, char* name, size_t len)
+{
+    if (!name || len == 0) return MX_ERR_INVALID_ARG;
+    if (inter < 32 || inter % 32 != 0 || inter > kMaxDim / 2) return MX_ERR_SHAPE;
+    mx_status st = check_gemm_shape(m, 2 * inter, k, 32);
+    if (st != MX_OK) return st;
+    if (!mxl_prefill_ok(m, 2 * inter, k)) return MX_ERR_UNSUPPORTED;
+    std::snprintf(name, len, "mxfp4 %s", mxl_prefill_swiglu_config_name());
+    return MX_OK;
 }
 
 mx_status mx_tensor_amax(const void* x_bf16, int64_t count, float* amax_dev, mx_stream_t stream)

@@ -107,6 +107,7 @@ struct PrefillArgs {
     const uint8_t* a_q; const uint8_t* a_s;
     const uint8_t* w_q; const uint8_t* w_s;
     void* y;
+    uint8_t* h_q; uint8_t* h_s;   // SwiGLU epilogue: MXFP4 codes and scales of h
     int M, N, K;
     int tile_base;   // first tile (in the tile order) of this launch
     int count;       // workgroups of this launch
@@ -166,7 +167,11 @@ struct PfPairCopies {
     uint32_t adst, wdst, asdst, wsdst;
 };
 
-template <bool OUT_F32, int BN>
+// EPI selects the epilogue: PF_EPI_Y stores Y; PF_EPI_SWIGLU applies SwiGLU
+// to gate/up column pairs and stores h quantized to MXFP4 (CEIL rule).
+constexpr int PF_EPI_Y = 0, PF_EPI_SWIGLU = 1;
+
+template <bool OUT_F32, int BN, int EPI>
 __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
 {
     using L = PfLayout<BN>;
@@ -447,6 +452,58 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     wait_vmcnt<0>();   // the trailing zero-fill copies have landed
     lds_barrier();     // every wave is done with the slots
 
+    if constexpr (EPI == PF_EPI_SWIGLU) {
+        // W's rows alternate 32 gate rows and 32 up rows, so W fragment 2jj
+        // of a wave holds the gate and fragment 2jj + 1 the up values of the
+        // same 32 h columns, in the same registers of the same lanes.  Each
+        // value is rounded to bf16 as a stored Y would be, h = SwiGLU(gate,
+        // up) is rounded to bf16, and one fragment row of h (32 columns) is
+        // one MXFP4 block: lane (r, g) holds 16 of its values, the lane
+        // (r, 1 - g) the other 16.  h is [M, N/2]: codes [M, N/4] bytes,
+        // scales [M, N/64] bytes.
+        const int I = p.N / 2, hrow_b = I / 2, hblocks = I / 32;
+        const int hb0 = (n0 + wn * (BN / 2)) / 64;    // first h block of this wave
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = m0 + wm * 128 + i * 32 + r32;
+#pragma unroll
+            for (int jj = 0; jj < WFR / 2; ++jj) {
+                uint32_t hv[8];
+                uint32_t amax = 0;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const uint32_t gb = bf16x2_rne(acc[i][2 * jj][2 * t], acc[i][2 * jj][2 * t + 1]);
+                    const uint32_t ub = bf16x2_rne(acc[i][2 * jj + 1][2 * t], acc[i][2 * jj + 1][2 * t + 1]);
+                    const float h0 = swiglu_f32(__uint_as_float(gb << 16), __uint_as_float(ub << 16));
+                    const float h1 = swiglu_f32(__uint_as_float(gb & 0xFFFF0000u), __uint_as_float(ub & 0xFFFF0000u));
+                    hv[t] = bf16x2_rne(h0, h1);
+                    const uint32_t lo = hv[t] & 0x7FFFu, hi = (hv[t] >> 16) & 0x7FFFu;
+                    amax = amax > lo ? amax : lo;
+                    amax = amax > hi ? amax : hi;
+                }
+                const auto am = __builtin_amdgcn_permlane32_swap(amax, amax, false, false);
+                amax = am[0] > am[1] ? am[0] : am[1];
+                const int e = scale_exponent<ELEM_E2M1, RULE_CEIL>(amax);
+                // codes of register groups 0,1 and 2,3: group q covers columns
+                // 8q + 4g .. +3 of the block, 2 bytes
+                const uint32_t c01 = encode8_e2m1(make_uint4(hv[0], hv[1], hv[2], hv[3]), e);
+                const uint32_t c23 = encode8_e2m1(make_uint4(hv[4], hv[5], hv[6], hv[7]), e);
+                // lane g = 0 receives groups 0, 1 of both lane halves (bytes
+                // 0..7 of the block's 16), lane g = 1 groups 2, 3 (bytes 8..15)
+                const auto sw = __builtin_amdgcn_permlane32_swap(c01, c23, false, false);
+                const uint32_t d0 = (sw[0] & 0xFFFFu) | (sw[1] << 16);
+                const uint32_t d1 = (sw[0] >> 16) | (sw[1] & 0xFFFF0000u);
+                const int hb = hb0 + jj;
+                if (m < p.M && hb < hblocks) {
+                    uint8_t* dst = p.h_q + (size_t)m * hrow_b + hb * 16 + g * 8;
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(d0, d1);
+                    if (g == 0) p.h_s[(size_t)m * hblocks + hb] = (uint8_t)(e + 127);
+                }
+            }
+        }
+        return;
+    }
+
     // Epilogue, one 32-row band (fragment row i) at a time through two
     // band buffers in this wave's private LDS region: band i + 1 is written
     // row-major while band i is read back as whole row segments and stored
@@ -535,10 +592,10 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     }
 }
 
-template <bool OUT_F32, int BN>
+template <bool OUT_F32, int BN, int EPI>
 hipError_t launch_prefill_part(PrefillArgs a, int tile_base, int count, hipStream_t stream)
 {
-    auto kern = mx_gemm_prefill_kernel<OUT_F32, BN>;
+    auto kern = mx_gemm_prefill_kernel<OUT_F32, BN, EPI>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -573,16 +630,16 @@ static int prefill_tail_tiles(int T, int C)
     return (rem > 0 && 2 * rem <= C) ? rem : 0;
 }
 
-template <bool OUT_F32>
+template <bool OUT_F32, int EPI = PF_EPI_Y>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
 {
     const int T = ((a.M + PF_BM - 1) / PF_BM) * ((a.N + 255) / 256);
     const int tail = prefill_tail_tiles(T, prefill_cu_count());
     if (T - tail > 0) {
-        const hipError_t e = launch_prefill_part<OUT_F32, 256>(a, 0, T - tail, stream);
+        const hipError_t e = launch_prefill_part<OUT_F32, 256, EPI>(a, 0, T - tail, stream);
         if (e != hipSuccess) return e;
     }
-    if (tail > 0) return launch_prefill_part<OUT_F32, 128>(a, T - tail, 2 * tail, stream);
+    if (tail > 0) return launch_prefill_part<OUT_F32, 128, EPI>(a, T - tail, 2 * tail, stream);
     return hipSuccess;
 }
 
@@ -604,6 +661,26 @@ extern "C" hipError_t mxl_launch_mx_prefill(const void* aq, const void* as, cons
                                             hipStream_t stream)
 {
     PrefillArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
-                  static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, 0, 0};
+                  static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, nullptr, nullptr,
+                  (int)m, (int)n, (int)k, 0, 0};
     return out_f32 ? launch_prefill<true>(a, stream) : launch_prefill<false>(a, stream);
+}
+
+// The gate_up projection with the SwiGLU + MXFP4 epilogue: W is [n, k] with
+// rows alternating 32 gate and 32 up rows (n % 64 == 0); h_q [m, n/4] and
+// h_s [m, n/64].  Same shape limits as the plain kernel.
+extern "C" hipError_t mxl_launch_mx_prefill_swiglu(const void* aq, const void* as, const void* wq,
+                                                   const void* ws, int64_t m, int64_t n, int64_t k, void* h_q,
+                                                   void* h_s, hipStream_t stream)
+{
+    PrefillArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
+                  static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), nullptr,
+                  static_cast<uint8_t*>(h_q), static_cast<uint8_t*>(h_s), (int)m, (int)n, (int)k, 0, 0};
+    return launch_prefill<false, PF_EPI_SWIGLU>(a, stream);
+}
+
+extern "C" const char* mxl_prefill_swiglu_config_name(void)
+{
+    return "mx_gemm_prefill_kernel<swiglu epilogue> 256x256 tiles (4 waves of 128x128, 32x32x64 mxfp4 mfma), "
+           "gate/up rows interleaved by 32, h quantized to mxfp4 (ceil) in registers";
 }

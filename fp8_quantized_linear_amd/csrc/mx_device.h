@@ -232,6 +232,18 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi)
 }
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)bf16x2_rne(f, 0.0f); }
 
+// SwiGLU of bf16 gate and up values, silu(g) * u = g * u / (1 + e^-g),
+// evaluated in fp32 as (g * rcp(1 + exp2(-g * log2 e))) * u on the hardware
+// exp2 and reciprocal: a relative error of a few fp32 ulp, far below the
+// bf16 step of the result.  Every kernel that applies SwiGLU calls this
+// function, so fused and unfused paths agree bit for bit.  For g below about
+// -88 the exponential is +inf and the result a signed zero.
+__device__ __forceinline__ float swiglu_f32(float g, float u)
+{
+    const float t = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+    return g * __builtin_amdgcn_rcpf(1.0f + t) * u;
+}
+
 // Buffer-to-LDS copies.  Each instruction writes its 64 lanes x width bytes
 // contiguously at the LDS address in M0, reading each lane's bytes from the
 // buffer at (voff + soff); lanes past the buffer's size read zero.  They are

@@ -252,6 +252,54 @@ __global__ __launch_bounds__(QUANT_THREADS) void nv_fake_quant_kernel(const uint
     else nv_fake_quant_body<true>(x, total, gscale, y);
 }
 
+// ---------------------------------------------------------------- SwiGLU + quantization
+// The unfused step between the gate_up projection and the down projection:
+// x is [rows, 2 * inter] bf16 with gate columns [0, inter) and up columns
+// [inter, 2 * inter); h = bf16(swiglu_f32(gate, up)) is quantized to MXFP4
+// with CEIL-rule scales: codes [rows, inter/2], scales [rows, inter/32].
+// Work mapping as mx_quantize_kernel over the flat h array (inter % 32 == 0,
+// so a lane quad is one block of one row); each lane reads its 8 gate and 8
+// up values with one 16-byte load each.
+__global__ __launch_bounds__(QUANT_THREADS) void swiglu_quant_kernel(const uint4* __restrict__ x,
+                                                                      int64_t total, int inter,
+                                                                      uint8_t* __restrict__ q,
+                                                                      uint8_t* __restrict__ s)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_base = ((int64_t)blockIdx.x * (QUANT_THREADS / 64) + (threadIdx.x >> 6)) * ELEMS_PER_WAVE;
+    const int gpr = inter / 8;   // 8-element groups per row of h
+    uint4 gv[4], uv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t gi = wave_base / 8 + 64 * j + lane;
+        const int64_t row = gi / gpr, c = gi - row * gpr;
+        const int64_t src = row * (2 * (int64_t)gpr) + c;   // uint4 index of the gate group
+        const bool ok = gi * 8 < total;
+        gv[j] = ok ? x[src] : make_uint4(0, 0, 0, 0);
+        uv[j] = ok ? x[src + gpr] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t gi = wave_base / 8 + 64 * j + lane;
+        const uint32_t gw[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
+        const uint32_t uw[4] = {uv[j].x, uv[j].y, uv[j].z, uv[j].w};
+        uint32_t hw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float h0 = swiglu_f32(__uint_as_float(gw[i] << 16), __uint_as_float(uw[i] << 16));
+            const float h1 = swiglu_f32(__uint_as_float(gw[i] & 0xFFFF0000u), __uint_as_float(uw[i] & 0xFFFF0000u));
+            hw[i] = bf16x2_rne(h0, h1);
+        }
+        const uint4 h = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        const int e = scale_exponent<ELEM_E2M1, RULE_CEIL>(quad_max_u32(amax_bits8(h)));
+        const uint32_t codes = encode8_e2m1(h, e);
+        if (gi * 8 < total) {
+            reinterpret_cast<uint32_t*>(q)[gi] = codes;
+            if ((lane & 3) == 0) s[gi >> 2] = (uint8_t)(e + 127);
+        }
+    }
+}
+
 // amax of a bf16 tensor into *out (fp32 bits; non-negative floats order like
 // unsigned integers, so an integer atomic max is a float max).
 __global__ void amax_init_kernel(uint32_t* out) { *out = 0u; }
@@ -354,5 +402,16 @@ extern "C" hipError_t mxl_launch_nv_fake_quant(const void* x, int64_t total, flo
     const int64_t blocks = (total + ELEMS_PER_BLOCK - 1) / ELEMS_PER_BLOCK;
     hipLaunchKernelGGL(nv_fake_quant_kernel, dim3((unsigned)blocks), dim3(QUANT_THREADS), 0, stream,
                        static_cast<const uint4*>(x), total, g, static_cast<uint4*>(y));
+    return hipGetLastError();
+}
+
+extern "C" hipError_t mxl_launch_swiglu_quant(const void* x, int64_t rows, int64_t inter, void* q, void* s,
+                                              hipStream_t stream)
+{
+    const int64_t total = rows * inter;
+    const int64_t blocks = (total + ELEMS_PER_BLOCK - 1) / ELEMS_PER_BLOCK;
+    hipLaunchKernelGGL(swiglu_quant_kernel, dim3((unsigned)blocks), dim3(QUANT_THREADS), 0, stream,
+                       static_cast<const uint4*>(x), total, (int)inter, static_cast<uint8_t*>(q),
+                       static_cast<uint8_t*>(s));
     return hipGetLastError();
 }

@@ -90,7 +90,7 @@ typedef enum {
                           * the 1e-4 bound that the default path meets */
 
 /* ABI version of this header (bumped on any signature change). */
-#define MXLINEAR_ABI_VERSION 3
+#define MXLINEAR_ABI_VERSION 4
 int mx_abi_version(void);
 
 /* Static text for a status code; never NULL. */
@@ -198,6 +198,50 @@ mx_status mx_gemm_w4a16(mx_format w_fmt, const void* a_bf16, const void* w_q, co
  * mx_gemm_w4a16 would launch for this shape.  Pure host logic.
  */
 mx_status mx_gemm_w4a16_plan(mx_format w_fmt, int64_t m, int64_t n, int64_t k, char* name, size_t len);
+
+/*
+ * mx_gemm_swiglu_quant -- the gate_up projection of the gated MLP with the
+ * SwiGLU activation and the down projection's activation quantization fused
+ * into the GEMM's epilogue, so h never exists in bf16 in memory.  The MLP
+ * weights are MXFP4 and vLLM fuses gate_proj and up_proj into one
+ * gate_up_proj (Qwen3.8-27B-MXFP8Attn-MXFP4MLP-lmheadMXFP4, section 2); h is
+ * the down projection's input, quantized per token with the CEIL rule
+ * (Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode").
+ *
+ * a_q/a_s: [m, k] MXFP4 activations.  w_q/w_s: the [2*inter, k] MXFP4 gate_up
+ * weights with rows alternating 32 gate and 32 up rows: row 64c + r is gate
+ * row 32c + r and row 64c + 32 + r is up row 32c + r (a row permutation of
+ * the [gate; up] weight, applied before or after packing, since packing is
+ * row-local).  Outputs h_q [m, inter/2] codes and h_s [m, inter/32] E8M0
+ * scales, the layout of mx_quantize_act, ready for mx_gemm with the down
+ * projection's weights.
+ * Per element: gate and up are the fp32 accumulators rounded to bf16 (as a
+ * bf16 Y would hold them); h = bf16(gate * rcp(1 + exp2(-gate * log2 e)) * up)
+ * in fp32 on the hardware exp2 and reciprocal; then CEIL-rule MXFP4
+ * quantization of each 32-column block of h.  mx_swiglu_quant applies the
+ * same arithmetic to a stored [gate | up] Y, so the fused and unfused paths
+ * agree bit for bit whenever their GEMMs accumulate alike (both run the
+ * prefill kernel on these shapes).
+ * Requires inter % 32 == 0 and k % 32 == 0 (MX_ERR_SHAPE); the fused kernel
+ * needs k % 128 == 0 and operands below 2 GiB (else MX_ERR_UNSUPPORTED:
+ * use mx_gemm and mx_swiglu_quant).  16-byte aligned pointers.
+ */
+mx_status mx_gemm_swiglu_quant(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t m,
+                               int64_t inter, int64_t k, void* h_q, void* h_s, mx_stream_t stream);
+
+/* mx_gemm_swiglu_quant_plan -- names the kernel mx_gemm_swiglu_quant would
+ * launch for this shape, or returns its error.  Pure host logic. */
+mx_status mx_gemm_swiglu_quant_plan(int64_t m, int64_t inter, int64_t k, char* name, size_t len);
+
+/*
+ * mx_swiglu_quant -- the same SwiGLU + CEIL MXFP4 quantization as the fused
+ * epilogue above, from a stored bf16 gate_up output x_bf16 [m, 2*inter]
+ * whose columns [0, inter) are gate and [inter, 2*inter) up (the output of
+ * mx_gemm with the [gate; up] weight).  h_q [m, inter/2], h_s [m, inter/32].
+ * Requires inter % 32 == 0 and 16-byte aligned pointers.
+ */
+mx_status mx_swiglu_quant(const void* x_bf16, int64_t m, int64_t inter, void* h_q, void* h_s,
+                          mx_stream_t stream);
 
 /*
  * mx_fake_quant -- training-time fake quantization: the quantize ->

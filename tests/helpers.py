@@ -97,3 +97,57 @@ def double_rounding_trap_scales(count: int = 4, seed: int = 0) -> list[np.float3
         pick = on_mid & (above == lower_even)
         out.extend(g[pick][: count - len(out)])
     return out
+
+
+# ------------------------------------------------------------- quantized-output validity
+E2M1_VALS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def e2m1_values(q: np.ndarray) -> np.ndarray:
+    """Signed values of nibble-packed E2M1 codes [rows, k/2] -> [rows, k]."""
+    codes = np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[0], -1).astype(np.int64)
+    v = E2M1_VALS[codes & 7]
+    return np.where(codes & 8, -v, v)
+
+
+def _rne_bounds(x: np.ndarray):
+    """Lowest and highest signed E2M1 lattice values that round-to-nearest of
+    the real x can give, either way at an exact midpoint (saturating at 6)."""
+    a = np.abs(x)
+    strict = (a[..., None] > _E2M1_MIDS).sum(-1)      # midpoints passed
+    loose = (a[..., None] >= _E2M1_MIDS).sum(-1)      # ... or reached
+    lo = np.where(x < 0, -E2M1_VALS[loose], E2M1_VALS[strict])
+    hi = np.where(x < 0, -E2M1_VALS[strict], E2M1_VALS[loose])
+    return lo, hi
+
+
+def check_mxfp4_ceil_intervals(q: np.ndarray, s: np.ndarray, lo: np.ndarray, hi: np.ndarray, what: str):
+    """The codes q [rows, k/2] and E8M0 scales s [rows, k/32] must be the
+    CEIL-rule MXFP4 quantization of SOME values h with lo <= h <= hi
+    elementwise: each block's exponent lies between the CEIL exponents of
+    the smallest and the largest possible block maximum, and each code is a
+    rounding of some admissible value at that exponent.  Used where the
+    quantized values come from arithmetic the oracle can only bound."""
+    rows, k = lo.shape
+    nb = k // 32
+    mag_lo = np.where((lo <= 0) & (hi >= 0), 0.0, np.minimum(np.abs(lo), np.abs(hi)))
+    mag_hi = np.maximum(np.abs(lo), np.abs(hi))
+    amin = mag_lo.reshape(rows, nb, 32).max(-1)
+    amax = mag_hi.reshape(rows, nb, 32).max(-1)
+    e = s.astype(np.int64) - 127
+    bad = 0
+    for r in range(rows):
+        for b in range(nb):
+            e_lo = oracle.scale_exponent(float(amin[r, b]), "e2m1", "ceil")
+            e_hi = oracle.scale_exponent(float(amax[r, b]), "e2m1", "ceil")
+            bad += not (e_lo <= e[r, b] <= e_hi)
+    assert bad == 0, f"{what}: {bad} block scales outside their admissible range"
+    scale = np.ldexp(1.0, np.repeat(e, 32, axis=1))
+    vlo, _ = _rne_bounds(lo / scale)
+    _, vhi = _rne_bounds(hi / scale)
+    v = e2m1_values(q)
+    ok = (v >= vlo) & (v <= vhi)
+    if not ok.all():
+        i = np.argwhere(~ok)[:3].tolist()
+        raise AssertionError(f"{what}: {int((~ok).sum())} codes outside their admissible range; first at {i}")

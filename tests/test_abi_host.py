@@ -34,6 +34,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("mx_pack_weights", "mx_quantize_act", "mx_gemm", "mx_gemm_fused", "nv_gemm",
               "mx_gemm_w4a16", "mx_gemm_w4a16_plan", "mx_fake_quant",
+              "mx_gemm_swiglu_quant", "mx_gemm_swiglu_quant_plan", "mx_swiglu_quant",
               "mx_tensor_amax", "mx_nv_global_scale", "mx_gemm_plan", "mx_status_string",
               "mx_abi_version"):
         assert n in names
@@ -152,6 +153,36 @@ def test_fake_quant_validation():
     assert g(x=BAD_ALIGN) == ALIGN
     assert g(y=P(0x20008)) == ALIGN
     assert g(y=P(0x10000 + 64 * 4 * 2)) in (OK, UNSUPPORTED, HIPERR)  # adjacent, not overlapping
+
+
+def test_swiglu_validation():
+    f = L.mx_gemm_swiglu_quant
+    def g(aq=GOOD, a_s=GOOD, wq=GOOD, ws=GOOD, m=4, inter=64, k=256, hq=GOOD, hs=GOOD):
+        return f(aq, a_s, wq, ws, m, inter, k, hq, hs, None)
+    assert g(aq=None) == INVALID
+    assert g(hs=None) == INVALID
+    assert g(inter=48) == SHAPE
+    assert g(inter=0) == SHAPE
+    assert g(k=48) == SHAPE
+    assert g(m=0) == SHAPE
+    assert g(k=96) == UNSUPPORTED          # the fused kernel needs k % 128 == 0
+    assert g(hq=BAD_ALIGN) == ALIGN
+    assert g() in (OK, UNSUPPORTED, HIPERR)
+    s = L.mx_swiglu_quant
+    assert s(None, 4, 64, GOOD, GOOD, None) == INVALID
+    assert s(GOOD, 4, 40, GOOD, GOOD, None) == SHAPE
+    assert s(GOOD, 0, 64, GOOD, GOOD, None) == SHAPE
+    assert s(BAD_ALIGN, 4, 64, GOOD, GOOD, None) == ALIGN
+    assert "swiglu" in mxl.mx_gemm_swiglu_quant_plan(8192, 17408, 5120)
+    with pytest.raises(mxl.MXError):
+        mxl.mx_gemm_swiglu_quant_plan(16, 64, 96)
+
+
+def test_gate_up_interleave_index():
+    idx = mxl.gate_up_interleave_index(96).tolist()
+    assert sorted(idx) == list(range(192))
+    assert idx[:32] == list(range(0, 32)) and idx[32:64] == list(range(96, 128))
+    assert idx[64:96] == list(range(32, 64)) and idx[160:192] == list(range(160, 192))
 
 
 def test_plan_names_the_kernel():

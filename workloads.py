@@ -134,6 +134,9 @@ PREFILL_DOWN = Gemm("mxfp4_prefill_down_8192x17408x5120", 8192, 17408, 5120)
 NVFP4 = Gemm("nvfp4_4096x5120x5120", 4096, 5120, 5120, "nvfp4", "nvfp4", a_dist="normal")
 MXFP8_ATTN = Gemm("mxfp8_attn_4096x5120x6144", 4096, 5120, 6144, "mxfp8", "mxfp8")
 MXFP4_VOCAB = Gemm("mxfp4_vocab_4096x5120x151936", 4096, 5120, 151936)
+# the gated MLP's fused gate_up projection (gate rows, then up rows: 2 x
+# 17408) whose SwiGLU output feeds PREFILL_DOWN
+MLP_GATE_UP = Gemm("mxfp4_mlp_gate_up_8192x5120x34816", 8192, 5120, 34816)
 
 ALL = [SMALL, *DECODE, PREFILL_UP, PREFILL_DOWN, NVFP4, MXFP8_ATTN, MXFP4_VOCAB]
 
