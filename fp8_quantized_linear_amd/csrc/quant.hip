@@ -311,20 +311,36 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t nvec = count / 8;
     const uint4* xv = reinterpret_cast<const uint4*>(x);
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
-        uint32_t a = amax_bits8(xv[i]);
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // four independent 16-byte loads in flight per lane
+    for (; i + 3 * stride < nvec; i += 4 * stride) {
+        const uint4 v0 = xv[i], v1 = xv[i + stride], v2 = xv[i + 2 * stride], v3 = xv[i + 3 * stride];
+        const uint32_t a = max(max(amax_bits8(v0), amax_bits8(v1)), max(amax_bits8(v2), amax_bits8(v3)));
+        m = m > a ? m : a;
+    }
+    for (; i < nvec; i += stride) {
+        const uint32_t a = amax_bits8(xv[i]);
         m = m > a ? m : a;
     }
     for (int64_t i = nvec * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
         uint32_t a = x[i] & 0x7FFFu;
         m = m > a ? m : a;
     }
-    // wave reduction, then one atomic per wave
+    // wave reduction, then across the block's waves through LDS, then one
+    // atomic per block: atomics on a single address serialize, so their
+    // count (the grid is capped at 512 blocks) must stay small
     for (int off = 32; off > 0; off >>= 1) {
         uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
         m = m > o ? m : o;
     }
-    if ((threadIdx.x & 63) == 0) atomicMax(out, m << 16);
+    __shared__ uint32_t wmax[4];
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        m = wmax[0];
+        for (int w = 1; w < 4; ++w) m = m > wmax[w] ? m : wmax[w];
+        atomicMax(out, m << 16);
+    }
 }
 
 } // namespace mxl
@@ -369,7 +385,7 @@ extern "C" hipError_t mxl_launch_amax(const void* x, int64_t count, float* out, 
     hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, stream, reinterpret_cast<uint32_t*>(out));
     int64_t blocks = (count / 8 + 255) / 256;
     if (blocks < 1) blocks = 1;
-    if (blocks > 4096) blocks = 4096;
+    if (blocks > 512) blocks = 512;
     hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(x), count, reinterpret_cast<uint32_t*>(out));
     return hipGetLastError();
