@@ -438,6 +438,50 @@ def extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_d
     rows["mxfp4_vocab"] = {"us": round(med * 1e3, 1), "tflops": round(tfv, 1),
                            "frac_fp4_peak": round(tfv / PEAK_TFLOPS["fp4"], 3)}
     log(f"vocab: {med * 1e3:.1f} us {tfv:.0f} TFLOP/s")
+    del wqv, wsv, aqv, asv, yv
+
+    # small-N projections (the 96-wide fused in_proj_ba, MXFP8 and MXFP4) and
+    # a 512-token chunk: too few output tiles to fill the GPU, so the library
+    # splits K (workspace) -- timed with and without the split, per call from
+    # a HIP graph of 10 back-to-back calls
+    def graph_us(fn, reps=10):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(reps):
+                    fn()
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(15):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return float(np.median(ts[3:]))
+
+    for name, fmt, m, n in (("mxfp8_n96_m4096", "mxfp8", 4096, 96), ("mxfp8_n96_m1", "mxfp8", 1, 96),
+                            ("mxfp4_n96_m4096", "mxfp4", 4096, 96), ("mxfp4_n2048_m512", "mxfp4", 512, 2048)):
+        k = 5120
+        ws_ = to_dev(W.normal_bf16(n, k, 0.02, 1))
+        wq_, wsc_ = mxl.mx_pack_weights(ws_, fmt, "floor" if fmt == "mxfp8" else "even")
+        a_ = to_dev(W.activations_entry_outliers(m, k))
+        aq_, as_ = mxl.mx_quantize_act(a_, fmt, "ceil")
+        y_ = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        t_split = graph_us(lambda: mxl.mx_gemm(aq_, as_, wq_, wsc_, k, fmt, fmt, y=y_))
+        t_one = graph_us(lambda: mxl.mx_gemm(aq_, as_, wq_, wsc_, k, fmt, fmt, y=y_, split_k=False))
+        rows[f"small_{name}"] = {"us": round(t_split, 2), "unsplit_us": round(t_one, 2),
+                                 "tflops": round(2 * m * n * k / (t_split * 1e-6) / 1e12, 1),
+                                 "kernel": mxl.mx_gemm_plan(fmt, fmt, m, n, k),
+                                 "timing": "HIP graph of 10 back-to-back calls, replayed"}
+        log(f"small {name}: {t_split:.1f} us (unsplit {t_one:.1f} us)")
+        del ws_, wq_, wsc_, a_, aq_, as_, y_
     return rows
 
 

@@ -64,6 +64,10 @@ def _load():
     L.mx_gemm_swiglu_quant_plan.argtypes = [i64, i64, i64, ctypes.c_char_p, sz]
     L.mx_swiglu_quant.restype = i32
     L.mx_swiglu_quant.argtypes = [P, i64, i64, P, P, P]
+    L.mx_gemm_workspace_size.restype = i32
+    L.mx_gemm_workspace_size.argtypes = [i32, i32, i64, i64, i64, u32, ctypes.POINTER(sz)]
+    L.mx_gemm_w4a16_workspace_size.restype = i32
+    L.mx_gemm_w4a16_workspace_size.argtypes = [i32, i64, i64, i64, ctypes.POINTER(sz)]
     L.mx_fake_quant.restype = i32
     L.mx_fake_quant.argtypes = [i32, i32, P, i64, i64, f32, P, P]
     L.mx_tensor_amax.restype, L.mx_tensor_amax.argtypes = i32, [P, i64, P, P]
@@ -158,10 +162,28 @@ def _flags(out_f32, fp8_fast):
     return (MX_OUT_F32 if out_f32 else 0) | (MX_FP8_FAST if fp8_fast else 0)
 
 
+def _workspace(query, device, *args):
+    """Split-K scratch of the size the library asks for (None when 0), from
+    torch's caching allocator on the call's stream."""
+    n = ctypes.c_size_t(0)
+    _check(query(*args, ctypes.byref(n)), query.__name__)
+    if n.value == 0:
+        return None, 0
+    return torch.empty(n.value, dtype=torch.uint8, device=device), n.value
+
+
+def mx_gemm_workspace_size(a_fmt: str, w_fmt: str, m: int, n: int, k: int, fp8_fast: bool = False) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib.mx_gemm_workspace_size(_fmt(a_fmt), _fmt(w_fmt), m, n, k, _flags(False, fp8_fast), ctypes.byref(b)),
+           "mx_gemm_workspace_size")
+    return b.value
+
+
 def mx_gemm(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str = "mxfp4",
-            out_f32: bool = False, y=None, fp8_fast: bool = False):
+            out_f32: bool = False, y=None, fp8_fast: bool = False, split_k: bool = True):
     """Y[m, n] = A W^T on MX codes/scales (bf16 out, or fp32 with out_f32).
-    fp8_fast selects the FP8 matrix cores for MXFP8 (inexact accumulation)."""
+    fp8_fast selects the FP8 matrix cores for MXFP8 (inexact accumulation).
+    split_k passes the split-K workspace the library asks for on this shape."""
     for t, nm in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
         _need(t, torch.uint8, nm)
     m, n = a_q.shape[0], w_q.shape[0]
@@ -170,8 +192,10 @@ def mx_gemm(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str = "mxfp
     if a_s.shape != (m, k // 32) or w_s.shape != (n, k // 32):
         raise ValueError("scale tensors do not match k")
     y = _gemm_out(m, n, a_q.device, out_f32, y)
+    ws, wsb = _workspace(lib.mx_gemm_workspace_size, a_q.device, _fmt(a_fmt), _fmt(w_fmt), m, n, k,
+                         _flags(out_f32, fp8_fast)) if split_k else (None, 0)
     st = lib.mx_gemm(_fmt(a_fmt), _fmt(w_fmt), _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, n, k,
-                     _ptr(y), _flags(out_f32, fp8_fast), None, 0, _stream(a_q))
+                     _ptr(y), _flags(out_f32, fp8_fast), _ptr(ws), wsb, _stream(a_q))
     _check(st, "mx_gemm")
     return y
 
@@ -193,7 +217,7 @@ def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str =
     return y
 
 
-def nv_gemm(a_q, a_s, w_q, w_s, k: int, alpha: float, out_f32: bool = False, y=None):
+def nv_gemm(a_q, a_s, w_q, w_s, k: int, alpha: float, out_f32: bool = False, y=None, split_k: bool = True):
     """NVFP4 GEMM: Y = alpha * sum_k dq(A) dq(W) with E4M3 block-16 scales."""
     for t, nm in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
         _need(t, torch.uint8, nm)
@@ -202,14 +226,16 @@ def nv_gemm(a_q, a_s, w_q, w_s, k: int, alpha: float, out_f32: bool = False, y=N
             or w_s.shape != (n, k // 16):
         raise ValueError("NVFP4 tensors do not match k")
     y = _gemm_out(m, n, a_q.device, out_f32, y)
+    ws, wsb = _workspace(lib.mx_gemm_workspace_size, a_q.device, FORMATS["nvfp4"], FORMATS["nvfp4"], m, n, k,
+                         0) if split_k else (None, 0)
     st = lib.nv_gemm(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, n, k, float(alpha), _ptr(y),
-                     MX_OUT_F32 if out_f32 else 0, None, 0, _stream(a_q))
+                     MX_OUT_F32 if out_f32 else 0, _ptr(ws), wsb, _stream(a_q))
     _check(st, "nv_gemm")
     return y
 
 
 def mx_gemm_w4a16(a: torch.Tensor, w_q, w_s, w_fmt: str = "mxfp4", alpha: float = 1.0,
-                  out_f32: bool = False, y=None):
+                  out_f32: bool = False, y=None, split_k: bool = True):
     """Weight-only quantized linear (W4A16): Y = alpha * A_bf16 dq(W)^T with
     MXFP4 (E8M0 per 32) or NVFP4 (E4M3 per 16; alpha = 1 / g_w) weights."""
     _need(a, torch.bfloat16, "a")
@@ -222,8 +248,10 @@ def mx_gemm_w4a16(a: torch.Tensor, w_q, w_s, w_fmt: str = "mxfp4", alpha: float 
     if w_q.shape[1] != k // 2 or w_s.shape != (n, scales_per_row(w_fmt, k)):
         raise ValueError("weight tensors do not match k")
     y = _gemm_out(m, n, a.device, out_f32, y)
+    ws, wsb = _workspace(lib.mx_gemm_w4a16_workspace_size, a.device, _fmt(w_fmt), m, n, k) if split_k \
+        else (None, 0)
     st = lib.mx_gemm_w4a16(_fmt(w_fmt), _ptr(a), _ptr(w_q), _ptr(w_s), m, n, k, float(alpha), _ptr(y),
-                           MX_OUT_F32 if out_f32 else 0, None, 0, _stream(a))
+                           MX_OUT_F32 if out_f32 else 0, _ptr(ws), wsb, _stream(a))
     _check(st, "mx_gemm_w4a16")
     return y
 

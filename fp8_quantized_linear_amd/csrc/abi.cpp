@@ -29,21 +29,25 @@ const char* mxl_prefill_swiglu_config_name(void);
 hipError_t mxl_launch_amax(const void* x, int64_t count, float* out, hipStream_t stream);
 hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq, const void* as, const void* wq,
                               const void* ws, int64_t m, int64_t n, int64_t k, void* y, int out_f32,
-                              hipStream_t stream);
+                              void* work, size_t work_bytes, hipStream_t stream);
+size_t mxl_mx_gemm_workspace(int a_bits, int64_t m, int64_t n, int64_t k);
+size_t mxl_dq_workspace(int64_t m, int64_t n, int64_t k);
+int mxl_dq_splits(int64_t m, int64_t n, int64_t k);
 hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, int w_bits,
                                     const void* wq, const void* ws, int64_t m, int64_t n, int64_t k,
                                     void* y, int out_f32, hipStream_t stream);
 hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const void* wq, const void* ws, int64_t m,
-                              int64_t n, int64_t k, float alpha, void* y, int out_f32,
-                              hipStream_t stream);
+                              int64_t n, int64_t k, float alpha, void* y, int out_f32, void* work,
+                              size_t work_bytes, hipStream_t stream);
 hipError_t mxl_launch_mxfp8_exact_gemm(const void* aq, const void* as, const void* wq, const void* ws,
-                                       int64_t m, int64_t n, int64_t k, void* y, int out_f32,
-                                       hipStream_t stream);
+                                       int64_t m, int64_t n, int64_t k, void* y, int out_f32, void* work,
+                                       size_t work_bytes, hipStream_t stream);
 hipError_t mxl_launch_mxfp8_exact_gemm_fused(int a_rule, const void* a_bf16, const void* wq, const void* ws,
                                              int64_t m, int64_t n, int64_t k, void* y, int out_f32,
                                              hipStream_t stream);
 hipError_t mxl_launch_w4a16_gemm(int w_nv, const void* a_bf16, const void* wq, const void* ws, int64_t m,
-                                 int64_t n, int64_t k, float alpha, void* y, int out_f32, hipStream_t stream);
+                                 int64_t n, int64_t k, float alpha, void* y, int out_f32, void* work,
+                                 size_t work_bytes, hipStream_t stream);
 hipError_t mxl_launch_w4a16_decode(int w_nv, const void* a_bf16, const void* wq, const void* ws, int64_t m,
                                    int64_t n, int64_t k, float alpha, void* y, int out_f32, hipStream_t stream);
 int mxl_w4a16_decode_ok(int w_nv, int64_t m, int64_t k);
@@ -169,11 +173,10 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
                   const void* w_s, int64_t m, int64_t n, int64_t k, void* y, unsigned flags,
                   void* workspace, size_t ws_bytes, mx_stream_t stream)
 {
-    (void)workspace;
-    (void)ws_bytes;
     if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || a_fmt == MX_FMT_NVFP4 || w_fmt == MX_FMT_NVFP4)
         return MX_ERR_INVALID_ARG;
     if (!a_q || !a_s || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
+    if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
     if (flags & ~(MX_OUT_F32 | MX_FP8_FAST)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, 32);
     if (st != MX_OK) return st;
@@ -188,8 +191,10 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
                      (long long)k,
                      exact8 ? mxl_mxfp8_exact_config_name() : mxl_mx_gemm_config_name(bits_of(a_fmt), m, n, k, 0));
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (exact8) return from_hip(mxl_launch_mxfp8_exact_gemm(a_q, a_s, w_q, w_s, m, n, k, y, f32, hs));
-    return from_hip(mxl_launch_mx_gemm(bits_of(a_fmt), bits_of(w_fmt), a_q, a_s, w_q, w_s, m, n, k, y, f32, hs));
+    if (exact8)
+        return from_hip(mxl_launch_mxfp8_exact_gemm(a_q, a_s, w_q, w_s, m, n, k, y, f32, workspace, ws_bytes, hs));
+    return from_hip(mxl_launch_mx_gemm(bits_of(a_fmt), bits_of(w_fmt), a_q, a_s, w_q, w_s, m, n, k, y, f32,
+                                       workspace, ws_bytes, hs));
 }
 
 mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf16, mx_format w_fmt,
@@ -220,9 +225,8 @@ mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void*
                   int64_t k, float alpha, void* y, unsigned flags, void* workspace, size_t ws_bytes,
                   mx_stream_t stream)
 {
-    (void)workspace;
-    (void)ws_bytes;
     if (!a_q || !a_s || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
+    if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
     if (flags & ~MX_OUT_F32) return MX_ERR_INVALID_ARG;
     if (!std::isfinite(alpha)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, 16);
@@ -231,18 +235,17 @@ mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void*
         return MX_ERR_ALIGN;
     if ((st = check_device()) != MX_OK) return st;
     return from_hip(mxl_launch_nv_gemm(a_q, a_s, w_q, w_s, m, n, k, alpha, y, (flags & MX_OUT_F32) ? 1 : 0,
-                                       static_cast<hipStream_t>(stream)));
+                                       workspace, ws_bytes, static_cast<hipStream_t>(stream)));
 }
 
 mx_status mx_gemm_w4a16(mx_format w_fmt, const void* a_bf16, const void* w_q, const void* w_s, int64_t m,
                         int64_t n, int64_t k, float alpha, void* y, unsigned flags, void* workspace,
                         size_t ws_bytes, mx_stream_t stream)
 {
-    (void)workspace;
-    (void)ws_bytes;
     if (!valid_fmt(w_fmt)) return MX_ERR_INVALID_ARG;
     if (w_fmt == MX_FMT_MXFP8) return MX_ERR_UNSUPPORTED;
     if (!a_bf16 || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
+    if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
     if (flags & ~MX_OUT_F32) return MX_ERR_INVALID_ARG;
     if (!std::isfinite(alpha)) return MX_ERR_INVALID_ARG;
     const bool nv = w_fmt == MX_FMT_NVFP4;
@@ -254,7 +257,33 @@ mx_status mx_gemm_w4a16(mx_format w_fmt, const void* a_bf16, const void* w_q, co
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (w4a16_use_decode(nv, m, n, k))
         return from_hip(mxl_launch_w4a16_decode(nv ? 1 : 0, a_bf16, w_q, w_s, m, n, k, alpha, y, f32, hs));
-    return from_hip(mxl_launch_w4a16_gemm(nv ? 1 : 0, a_bf16, w_q, w_s, m, n, k, alpha, y, f32, hs));
+    return from_hip(mxl_launch_w4a16_gemm(nv ? 1 : 0, a_bf16, w_q, w_s, m, n, k, alpha, y, f32, workspace,
+                                          ws_bytes, hs));
+}
+
+mx_status mx_gemm_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k,
+                                 unsigned flags, size_t* bytes)
+{
+    if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || !bytes) return MX_ERR_INVALID_ARG;
+    const bool nv = a_fmt == MX_FMT_NVFP4;
+    if (nv != (w_fmt == MX_FMT_NVFP4)) return MX_ERR_INVALID_ARG;
+    mx_status st = check_gemm_shape(m, n, k, nv ? 16 : 32);
+    if (st != MX_OK) return st;
+    if (!nv && a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
+    const bool dq = nv || (a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST));
+    *bytes = dq ? mxl_dq_workspace(m, n, k) : mxl_mx_gemm_workspace(bits_of(a_fmt), m, n, k);
+    return MX_OK;
+}
+
+mx_status mx_gemm_w4a16_workspace_size(mx_format w_fmt, int64_t m, int64_t n, int64_t k, size_t* bytes)
+{
+    if (!valid_fmt(w_fmt) || !bytes) return MX_ERR_INVALID_ARG;
+    if (w_fmt == MX_FMT_MXFP8) return MX_ERR_UNSUPPORTED;
+    const bool nv = w_fmt == MX_FMT_NVFP4;
+    mx_status st = check_gemm_shape(m, n, k, nv ? 16 : 32);
+    if (st != MX_OK) return st;
+    *bytes = w4a16_use_decode(nv, m, n, k) ? 0 : mxl_dq_workspace(m, n, k);
+    return MX_OK;
 }
 
 mx_status mx_gemm_w4a16_plan(mx_format w_fmt, int64_t m, int64_t n, int64_t k, char* name, size_t len)
@@ -264,8 +293,11 @@ mx_status mx_gemm_w4a16_plan(mx_format w_fmt, int64_t m, int64_t n, int64_t k, c
     const bool nv = w_fmt == MX_FMT_NVFP4;
     mx_status st = check_gemm_shape(m, n, k, nv ? 16 : 32);
     if (st != MX_OK) return st;
-    std::snprintf(name, len, "w4a16 %s %s", nv ? "nvfp4" : "mxfp4",
-                  w4a16_use_decode(nv, m, n, k) ? mxl_w4a16_decode_config_name() : mxl_w4a16_gemm_config_name());
+    const bool dec = w4a16_use_decode(nv, m, n, k);
+    const int splits = dec ? 1 : mxl_dq_splits(m, n, k);
+    std::snprintf(name, len, "w4a16 %s %s%s", nv ? "nvfp4" : "mxfp4",
+                  dec ? mxl_w4a16_decode_config_name() : mxl_w4a16_gemm_config_name(),
+                  splits > 1 ? ", split-K with a workspace, else one split" : "");
     return MX_OK;
 }
 
@@ -380,7 +412,12 @@ mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, i
     const char* cfg = nv ? mxl_nv_gemm_config_name()
                          : (exact8 ? mxl_mxfp8_exact_config_name()
                                    : mxl_mx_gemm_config_name(bits_of(a_fmt), m, n, k, fused));
-    std::snprintf(name, len, "%s%s %s", fused && !nv ? "fused-quant " : "", fmt, cfg);
+    const int splits = (nv || exact8) && !fused ? mxl_dq_splits(m, n, k) : 1;
+    if (splits > 1)
+        std::snprintf(name, len, "%s%s %s, split-K %d with a workspace, else one split",
+                      fused && !nv ? "fused-quant " : "", fmt, cfg, splits);
+    else
+        std::snprintf(name, len, "%s%s %s", fused && !nv ? "fused-quant " : "", fmt, cfg);
     return MX_OK;
 }
 

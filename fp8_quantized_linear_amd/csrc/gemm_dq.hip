@@ -161,6 +161,12 @@ struct DqArgs {
     void* y;
     int M, N, K;
     float alpha;
+    // split-K as in the MX tile kernel: workgroup b computes stages
+    // [s * chunk, (s + 1) * chunk) (chunk even) of tile b % tiles, s = b /
+    // tiles, and with splits > 1 writes its fp32 partial (without alpha) to
+    // part + s * M * N
+    float* part;
+    int splits, chunk;
 };
 
 // FUSED_A (MXFP8 only): A arrives as bf16 [M, K]; each 8-element chunk is
@@ -197,13 +203,16 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
     extern __shared__ __align__(16) uint8_t smem[];
 
     const int tiles_n = (p.N + BN - 1) / BN;
-    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    const int tiles = ((p.M + BM - 1) / BM) * tiles_n;
+    const int split = blockIdx.x / tiles, bid = blockIdx.x - split * tiles;
+    const int tm = bid / tiles_n, tn = bid % tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int K = p.K, KS = K / T::SCALE_BLOCK;
     const int row_bytes = KIND == DQ_MXFP8 ? K : K / 2;   // W (and quantized A) bytes per row
-    const int nk = (K + DQ_BK - 1) / DQ_BK;
+    const int kt0 = split * p.chunk;                                // even: set parity = stage parity
+    const int nk = min(p.chunk, (K + DQ_BK - 1) / DQ_BK - kt0);     // stages of this split
 
     // two register sets of staged chunks: stage kt lives in set kt % 2.
     // Loads are branch-free and nothing loaded is used before the chunk is
@@ -389,12 +398,12 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
     // and both steps run unconditionally (stages past K load nothing and
     // dequantize to zeros in the buffer no later stage reads), so the
     // compiler's waits count exactly the loads of stage kt + 2 as newer.
-    load_stage(0, 0);
-    load_stage(1, 1);
+    load_stage(kt0, 0);
+    load_stage(kt0 + 1, 1);
     store_stage(0, 0);
     __syncthreads();
     auto iter = [&](int kt, int set) __attribute__((always_inline)) {
-        load_stage(kt + 2, set);
+        load_stage(kt0 + kt + 2, set);
         compute_stage(set);
         store_stage(set ^ 1, set ^ 1);
         __syncthreads();
@@ -405,6 +414,22 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
         iter(kt + 1, 1);
     }
     if (kt < nk) iter(kt, 0);
+
+    if (p.splits > 1) {   // fp32 partial of this split
+        float* part = p.part + (size_t)split * p.M * p.N;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + wn * WTN + j * 32 + r32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * WTM + i * 32 + (r / 4) * 8 + g * 4 + (r % 4);
+                    if (m < p.M && n < p.N) part[(size_t)m * p.N + n] = acc[i][j][r];
+                }
+            }
+        return;
+    }
 
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -439,7 +464,7 @@ hipError_t launch_dq_k(const DqArgs& a, hipStream_t stream)
         attr_set = true;
     }
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL(kern, dim3(tiles), dim3(WM * WN * 64), LDS, stream, a);
+    hipLaunchKernelGGL(kern, dim3(tiles * a.splits), dim3(WM * WN * 64), LDS, stream, a);
     return hipGetLastError();
 }
 
@@ -463,26 +488,77 @@ hipError_t launch_dq(const DqArgs& a, hipStream_t stream)
 
 using namespace mxl;
 
+extern "C" int mxl_choose_splits(int64_t tiles, int nk, int min_stages, int even, int* chunk);
+extern "C" hipError_t mxl_launch_splitk_reduce(const float* part, int splits, int64_t mn, float alpha, void* y,
+                                               int out_f32, hipStream_t stream);
+
+// Split-K plan of the 128 x 128 dequantizing kernel: at least 8 stages of 64
+// per split and an even stage count.
+static int dq_splits(int64_t m, int64_t n, int64_t k, int* chunk)
+{
+    const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    return mxl_choose_splits(tiles, (int)((k + DQ_BK - 1) / DQ_BK), 8, 1, chunk);
+}
+
+extern "C" size_t mxl_dq_workspace(int64_t m, int64_t n, int64_t k)
+{
+    int chunk;
+    const int s = dq_splits(m, n, k, &chunk);
+    return s > 1 ? (size_t)s * m * n * sizeof(float) : 0;
+}
+
+extern "C" int mxl_dq_splits(int64_t m, int64_t n, int64_t k)
+{
+    int chunk;
+    return dq_splits(m, n, k, &chunk);
+}
+
+// Runs `launch(args, out_f32)` either as one pass or, when a large enough
+// workspace is given and the tiles alone leave the machine idle, as split-K
+// partials plus the ordered reduction (which applies alpha).
+template <class F>
+static hipError_t dq_run(DqArgs a, int out_f32, void* work, size_t work_bytes, hipStream_t stream, F launch)
+{
+    a.part = nullptr;
+    a.splits = 1;
+    a.chunk = 1 << 30;
+    int chunk;
+    const int splits = dq_splits(a.M, a.N, a.K, &chunk);
+    if (work && splits > 1 && work_bytes >= (size_t)splits * a.M * a.N * sizeof(float)) {
+        a.part = static_cast<float*>(work);
+        a.splits = splits;
+        a.chunk = chunk;
+        const hipError_t e = launch(a, 1);
+        if (e != hipSuccess) return e;
+        return mxl_launch_splitk_reduce(a.part, splits, (int64_t)a.M * a.N, a.alpha, a.y, out_f32, stream);
+    }
+    return launch(a, out_f32);
+}
+
 extern "C" hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const void* wq, const void* ws,
                                          int64_t m, int64_t n, int64_t k, float alpha, void* y,
-                                         int out_f32, hipStream_t stream)
+                                         int out_f32, void* work, size_t work_bytes, hipStream_t stream)
 {
     DqArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
              static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
              (int)m, (int)n, (int)k, alpha};
-    if (out_f32) return launch_dq<DQ_NVFP4, 128, 128, 2, 2, true>(a, stream);
-    return launch_dq<DQ_NVFP4, 128, 128, 2, 2, false>(a, stream);
+    return dq_run(a, out_f32, work, work_bytes, stream, [&](const DqArgs& x, int f32) {
+        if (f32) return launch_dq<DQ_NVFP4, 128, 128, 2, 2, true>(x, stream);
+        return launch_dq<DQ_NVFP4, 128, 128, 2, 2, false>(x, stream);
+    });
 }
 
 extern "C" hipError_t mxl_launch_mxfp8_exact_gemm(const void* aq, const void* as, const void* wq,
                                                   const void* ws, int64_t m, int64_t n, int64_t k, void* y,
-                                                  int out_f32, hipStream_t stream)
+                                                  int out_f32, void* work, size_t work_bytes, hipStream_t stream)
 {
     DqArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
              static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
              (int)m, (int)n, (int)k, 1.0f};
-    if (out_f32) return launch_dq<DQ_MXFP8, 128, 128, 2, 2, true>(a, stream);
-    return launch_dq<DQ_MXFP8, 128, 128, 2, 2, false>(a, stream);
+    return dq_run(a, out_f32, work, work_bytes, stream, [&](const DqArgs& x, int f32) {
+        if (f32) return launch_dq<DQ_MXFP8, 128, 128, 2, 2, true>(x, stream);
+        return launch_dq<DQ_MXFP8, 128, 128, 2, 2, false>(x, stream);
+    });
 }
 
 template <int RULE>
@@ -497,7 +573,7 @@ extern "C" hipError_t mxl_launch_mxfp8_exact_gemm_fused(int a_rule, const void* 
                                                         void* y, int out_f32, hipStream_t stream)
 {
     DqArgs a{static_cast<const uint8_t*>(a_bf16), nullptr, static_cast<const uint8_t*>(wq),
-             static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, 1.0f};
+             static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, 1.0f, nullptr, 1, 1 << 30};
     if (a_rule == RULE_CEIL) return fused8<RULE_CEIL>(a, out_f32, stream);
     if (a_rule == RULE_FLOOR) return fused8<RULE_FLOOR>(a, out_f32, stream);
     return fused8<RULE_EVEN>(a, out_f32, stream);
@@ -507,16 +583,18 @@ extern "C" hipError_t mxl_launch_mxfp8_exact_gemm_fused(int a_rule, const void* 
 // weights dequantized exactly to bf16; alpha multiplies the result.
 extern "C" hipError_t mxl_launch_w4a16_gemm(int w_nv, const void* a_bf16, const void* wq, const void* ws,
                                             int64_t m, int64_t n, int64_t k, float alpha, void* y,
-                                            int out_f32, hipStream_t stream)
+                                            int out_f32, void* work, size_t work_bytes, hipStream_t stream)
 {
     DqArgs a{static_cast<const uint8_t*>(a_bf16), nullptr, static_cast<const uint8_t*>(wq),
              static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, alpha};
-    if (w_nv) {
-        if (out_f32) return launch_dq<DQ_NVFP4, 128, 128, 2, 2, true, false, RULE_CEIL, true>(a, stream);
-        return launch_dq<DQ_NVFP4, 128, 128, 2, 2, false, false, RULE_CEIL, true>(a, stream);
-    }
-    if (out_f32) return launch_dq<DQ_MXFP4, 128, 128, 2, 2, true, false, RULE_CEIL, true>(a, stream);
-    return launch_dq<DQ_MXFP4, 128, 128, 2, 2, false, false, RULE_CEIL, true>(a, stream);
+    return dq_run(a, out_f32, work, work_bytes, stream, [&](const DqArgs& x, int f32) {
+        if (w_nv) {
+            if (f32) return launch_dq<DQ_NVFP4, 128, 128, 2, 2, true, false, RULE_CEIL, true>(x, stream);
+            return launch_dq<DQ_NVFP4, 128, 128, 2, 2, false, false, RULE_CEIL, true>(x, stream);
+        }
+        if (f32) return launch_dq<DQ_MXFP4, 128, 128, 2, 2, true, false, RULE_CEIL, true>(x, stream);
+        return launch_dq<DQ_MXFP4, 128, 128, 2, 2, false, false, RULE_CEIL, true>(x, stream);
+    });
 }
 
 extern "C" const char* mxl_w4a16_gemm_config_name(void)

@@ -27,6 +27,7 @@
 // reading the same chunk of 32 consecutive rows hit distinct banks.
 #include "mx_device.h"
 
+#include <cstdio>
 #include <type_traits>
 
 namespace mxl {
@@ -110,6 +111,11 @@ struct GemmArgs {
     const uint8_t* w_s;    // [N, K/32]
     void* y;               // [M, N] bf16 or fp32
     int M, N, K;
+    // split-K: workgroup b computes K stages [s * chunk, (s + 1) * chunk) of
+    // tile b % tiles for s = b / tiles; with splits > 1 it writes its fp32
+    // partial tile to part + s * M * N and splitk_reduce_kernel sums them
+    float* part;
+    int splits, chunk;
 };
 
 
@@ -136,15 +142,18 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
 
     extern __shared__ __align__(16) uint8_t smem[];
 
+    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    const int split = blockIdx.x / tiles;
     int tm, tn;
-    tile_coords<BM, BN, 4>(p.M, p.N, tm, tn);
+    tile_coords<BM, BN, 4>(p.M, p.N, blockIdx.x - split * tiles, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int K = p.K, KB = K / 32;
     const int a_row_bytes = FUSED ? K * 2 : K * ABITS / 8;
     const int w_row_bytes = K * WBITS / 8;
-    const int nk = (K + BK - 1) / BK;
+    const int kt0 = split * p.chunk;                                  // this split's first stage
+    const int nk = min(p.chunk, (K + BK - 1) / BK - kt0);            // and its stage count
 
     constexpr int SA_PER_T = FUSED ? 1 : (BM + NT - 1) / NT;   // A scale rows per thread
     constexpr int SW_PER_T = (BN + NT - 1) / NT;                 // W scale rows per thread
@@ -189,7 +198,8 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
         }
         return v;
     };
-    auto load_stage = [&](int kt, Stage& st) {
+    auto load_stage = [&](int kl, Stage& st) {
+        const int kt = kt0 + kl;   // global stage index
         const bool a_in_k = SCALE_DWORD || kt * A_STAGE_BYTES + a_c * 16 < a_row_bytes;
         const bool w_in_k = SCALE_DWORD || kt * TW::ROW_BYTES + w_c * 16 < w_row_bytes;
 #pragma unroll
@@ -371,6 +381,34 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
         }
     }
 
+    // fp32 partial tile of this split (same layout as an fp32 Y); only the
+    // 128 x 128 unfused kernel is ever launched with splits
+    if constexpr (!FUSED && BM == 128) if (p.splits > 1) {
+        float* part = p.part + (size_t)split * p.M * p.N;
+        const bool vec = (p.N & 3) == 0;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + wm * WTM + i * 32 + r32;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // registers 4q .. 4q+3: 4 consecutive columns of row m
+                    const int n = n0 + wn * WTN + j * 32 + q * 8 + g * 4;
+                    if (m >= p.M) continue;
+                    if (vec && n + 3 < p.N) {
+                        *reinterpret_cast<float4_t*>(part + (size_t)m * p.N + n) =
+                            float4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            if (n + t < p.N) part[(size_t)m * p.N + n + t] = acc[i][j][4 * q + t];
+                    }
+                }
+        }
+        return;
+    }
+
     // epilogue: accumulator (i, j) register r holds Y[m][n] with
     //   m = tile row of fragment i + lane % 32,
     //   n = tile column of fragment j + (r / 4) * 8 + (lane / 32) * 4 + r % 4,
@@ -428,11 +466,66 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream)
         attr_set = true;
     }
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL(kern, dim3(tiles), dim3(WM * WN * 64), LDS, stream, a);
+    hipLaunchKernelGGL(kern, dim3(tiles * a.splits), dim3(WM * WN * 64), LDS, stream, a);
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- split-K
+// Y = alpha * sum over s of part[s] (fp32 partial products [M, N] each),
+// summed in split order, so the result does not depend on scheduling; 4
+// elements per lane (any M*N: the tail lanes take single elements).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
+                                                            int64_t mn, float alpha, void* __restrict__ y,
+                                                            int out_f32)
+{
+    const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i4 >= mn) return;
+    if (i4 + 4 <= mn && (mn & 3) == 0) {
+        float4_t acc = *reinterpret_cast<const float4_t*>(part + i4);
+        for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const float4_t*>(part + (size_t)s * mn + i4);
+        acc *= alpha;
+        if (out_f32) *reinterpret_cast<float4_t*>(reinterpret_cast<float*>(y) + i4) = acc;
+        else *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + i4) =
+                 make_uint2(bf16x2_rne(acc[0], acc[1]), bf16x2_rne(acc[2], acc[3]));
+        return;
+    }
+    for (int64_t i = i4; i < i4 + 4 && i < mn; ++i) {
+        float v = part[i];
+        for (int s = 1; s < splits; ++s) v += part[(size_t)s * mn + i];
+        v *= alpha;
+        if (out_f32) reinterpret_cast<float*>(y)[i] = v;
+        else reinterpret_cast<uint16_t*>(y)[i] = f32_to_bf16_rne(v);
+    }
+}
 
+// K splits for a launch of `tiles` tiles over nk stages: as many splits as
+// still fit one workgroup per compute unit (256), so that all of them run in
+// one round, every split at least min_stages long, and (even) a whole number
+// of stage pairs per split.  Returns the split count and sets the stages per
+// split.
+extern "C" int mxl_choose_splits(int64_t tiles, int nk, int min_stages, int even, int* chunk)
+{
+    int s = 1;
+    if (tiles <= 128) {
+        s = (int)(256 / tiles);
+        const int cap = nk / min_stages;
+        if (s > cap) s = cap;
+        if (s < 1) s = 1;
+    }
+    int c = (nk + s - 1) / s;
+    if (even && (c & 1)) ++c;
+    *chunk = c;
+    return (nk + c - 1) / c;
+}
+
+extern "C" hipError_t mxl_launch_splitk_reduce(const float* part, int splits, int64_t mn, float alpha, void* y,
+                                               int out_f32, hipStream_t stream)
+{
+    const int64_t blocks = (mn + 1023) / 1024;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, splits, mn, alpha,
+                       y, out_f32);
+    return hipGetLastError();
+}
 
 // ---------------------------------------------------------------- decode (M <= 32)
 // Weight streaming for a handful of tokens.  A workgroup owns 16 W rows and
@@ -826,7 +919,17 @@ static hipError_t dispatch_tile(const GemmArgs& a, ShapeClass sc, hipStream_t s)
 {
     if constexpr (AB == 4) if (sc == SC_LARGE)
         return launch_tile<AB, WB, 256, 256, 2, 2, FUSED, RULE, F32, FUSED ? 1 : 3, true>(a, s);
+    if constexpr (!FUSED) if (a.K % BK == 0)   // whole stages: dword scale loads, two stages in flight
+        return launch_tile<AB, WB, 128, 128, 2, 2, FUSED, RULE, F32, 3, true>(a, s);
     return launch_tile<AB, WB, 128, 128, 2, 2, FUSED, RULE, F32>(a, s);
+}
+
+// Split-K plan of the 128 x 128 tile kernel (the default class): splits and
+// stages per split; 1 split when the tiles already fill the machine.
+static int default_splits(int64_t m, int64_t n, int64_t k, int* chunk)
+{
+    const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    return mxl_choose_splits(tiles, (int)((k + BK - 1) / BK), 4, 0, chunk);
 }
 
 template <int AB, int WB, bool FUSED, int RULE>
@@ -841,13 +944,38 @@ extern "C" hipError_t mxl_launch_mx_prefill(const void* aq, const void* as, cons
                                             int64_t m, int64_t n, int64_t k, void* y, int out_f32,
                                             hipStream_t stream);
 
+// Workspace bytes mx_gemm can use for split-K on this shape (0: none).
+extern "C" size_t mxl_mx_gemm_workspace(int a_bits, int64_t m, int64_t n, int64_t k)
+{
+    if (classify(a_bits, m, n, k, false) != SC_DEFAULT) return 0;
+    int chunk;
+    const int s = default_splits(m, n, k, &chunk);
+    return s > 1 ? (size_t)s * m * n * sizeof(float) : 0;
+}
+
 extern "C" hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq, const void* as,
                                          const void* wq, const void* ws, int64_t m, int64_t n,
-                                         int64_t k, void* y, int out_f32, hipStream_t stream)
+                                         int64_t k, void* y, int out_f32, void* work, size_t work_bytes,
+                                         hipStream_t stream)
 {
     GemmArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
-               static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k};
+               static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k,
+               nullptr, 1, 1 << 30};
     const ShapeClass sc = classify(a_bits, m, n, k, false);
+    if (sc == SC_DEFAULT && work) {
+        int chunk;
+        const int splits = default_splits(m, n, k, &chunk);
+        if (splits > 1 && work_bytes >= (size_t)splits * m * n * sizeof(float)) {
+            a.part = static_cast<float*>(work);
+            a.splits = splits;
+            a.chunk = chunk;
+            hipError_t e = hipErrorInvalidValue;
+            if (a_bits == 4 && w_bits == 4) e = dispatch_out<4, 4, false, RULE_CEIL>(a, sc, true, stream);
+            else if (a_bits == 8 && w_bits == 8) e = dispatch_out<8, 8, false, RULE_CEIL>(a, sc, true, stream);
+            if (e != hipSuccess) return e;
+            return mxl_launch_splitk_reduce(a.part, splits, m * n, 1.0f, y, out_f32, stream);
+        }
+    }
     if (sc == SC_LARGE && mxl_prefill_ok(m, n, k))
         return mxl_launch_mx_prefill(aq, as, wq, ws, m, n, k, y, out_f32, stream);
     if (sc == SC_DECODE) {
@@ -864,7 +992,7 @@ extern "C" hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const voi
                                                int64_t k, void* y, int out_f32, hipStream_t stream)
 {
     GemmArgs a{static_cast<const uint8_t*>(a_bf16), nullptr, static_cast<const uint8_t*>(wq),
-               static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k};
+               static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, nullptr, 1, 1 << 30};
     const ShapeClass sc = classify(a_bits, m, n, k, true);
     if (a_bits == 4 && w_bits == 4) {
         if (a_rule == RULE_CEIL) return dispatch_out<4, 4, true, RULE_CEIL>(a, sc, out_f32, stream);
@@ -897,6 +1025,17 @@ extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n,
                    "a last round of tiles at most half full runs as 256x128 halves>";
         return "mx_gemm_kernel<tile 256x256x128, 2x2 waves of 128x128, scaled mfma 32x32x64>";
     default:
+        if (!fused) {
+            int chunk;
+            const int s = default_splits(m, n, k, &chunk);
+            if (s > 1) {
+                static thread_local char buf[192];
+                std::snprintf(buf, sizeof buf,
+                              "mx_gemm_kernel<tile 128x128x128, 2x2 waves of 64x64, scaled mfma 32x32x64>, "
+                              "split-K %d x %d stages with a workspace, else one split", s, chunk);
+                return buf;
+            }
+        }
         return "mx_gemm_kernel<tile 128x128x128, 2x2 waves of 64x64, scaled mfma 32x32x64>";
     }
 }

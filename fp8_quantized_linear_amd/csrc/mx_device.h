@@ -307,11 +307,10 @@ __device__ __forceinline__ int4_t make_rsrc(const void* base, uint32_t bytes)
 constexpr int NUM_XCD = 8;
 
 template <int BM, int BN, int GROUP_N>
-__device__ __forceinline__ void tile_coords(int M, int N, int& tm, int& tn)
+__device__ __forceinline__ void tile_coords(int M, int N, int id, int& tm, int& tn)
 {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int total = tiles_m * tiles_n;
-    const int id = blockIdx.x;
     const int xcd = id % NUM_XCD, j = id / NUM_XCD;
     const int q = total / NUM_XCD, r = total % NUM_XCD;
     const int t = xcd * q + (xcd < r ? xcd : r) + j;   // bijection onto [0, total)

@@ -65,7 +65,7 @@ typedef enum {
     MX_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, bad format/rule pair */
     MX_ERR_SHAPE = 2,       /* m, n or k < 1; k not a multiple of the block */
     MX_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
-    MX_ERR_WORKSPACE = 4,   /* reserved: workspace too small */
+    MX_ERR_WORKSPACE = 4,   /* reserved (a workspace smaller than needed runs unsplit) */
     MX_ERR_UNSUPPORTED = 5, /* current device is not gfx950 */
     MX_ERR_HIP = 6          /* a HIP runtime call or launch failed */
 } mx_status;
@@ -90,7 +90,7 @@ typedef enum {
                           * the 1e-4 bound that the default path meets */
 
 /* ABI version of this header (bumped on any signature change). */
-#define MXLINEAR_ABI_VERSION 4
+#define MXLINEAR_ABI_VERSION 5
 int mx_abi_version(void);
 
 /* Static text for a status code; never NULL. */
@@ -135,8 +135,16 @@ mx_status mx_pack_weights(mx_format fmt, mx_scale_rule rule, const void* w_bf16,
  * its power-of-two block scale) and runs on bf16 matrix cores; MX_FP8_FAST
  * selects the FP8 matrix cores instead.  Result: fp32 accumulation within
  * 1e-4 * sum_k |a_k w_k| of the exact product (plus the bf16 output rounding).
- * workspace/ws_bytes are reserved and may be NULL/0.  All pointers must be
- * 16-byte aligned.
+ * All pointers must be 16-byte aligned.
+ * workspace/ws_bytes: optional device scratch for split-K, owned by the
+ * caller (NULL/0 is valid).  When the output tiles alone cannot occupy the
+ * GPU (small m or n) and ws_bytes is at least mx_gemm_workspace_size's
+ * answer, K is split across workgroups: each writes an fp32 partial product
+ * into the workspace and a second kernel sums the partials in split order
+ * (deterministic) and rounds once.  Otherwise the call runs unsplit.  Both
+ * meet the tolerance above; they are not bitwise equal to each other (the
+ * fp32 summation order differs).  Calls sharing one workspace must not
+ * overlap in time.
  */
 mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void* a_s,
                   const void* w_q, const void* w_s, int64_t m, int64_t n, int64_t k, void* y,
@@ -145,7 +153,8 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
 /*
  * mx_gemm_fused -- mx_gemm with the activation quantization computed inside
  * the GEMM from bf16 A ([m, k]), with scale rule a_rule.  The result equals
- * mx_quantize_act followed by mx_gemm.
+ * mx_quantize_act followed by an unsplit mx_gemm.  workspace/ws_bytes are
+ * unused and may be NULL/0.
  */
 mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf16,
                         mx_format w_fmt, const void* w_q, const void* w_s, int64_t m, int64_t n,
@@ -157,7 +166,8 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf1
  * w_q [n, k/2], w_s [n, k/16].  Y = alpha * sum_k (e2m1_a * s_a) *
  * (e2m1_w * s_w), with alpha = 1 / (g_a * g_w) supplied by the caller.
  * Requires k % 16 == 0.  The block products are exact in f16, so the
- * contraction runs on f16 matrix cores with fp32 accumulation.
+ * contraction runs on f16 matrix cores with fp32 accumulation.  workspace:
+ * split-K scratch as for mx_gemm (alpha is applied after the partial sums).
  */
 mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t m,
                   int64_t n, int64_t k, float alpha, void* y, unsigned flags, void* workspace,
@@ -186,12 +196,24 @@ mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void*
  * Errors: MX_ERR_INVALID_ARG for null pointers, unknown flags, a
  * non-finite alpha or a w_fmt other than MXFP4/NVFP4 (MXFP8:
  * MX_ERR_UNSUPPORTED); MX_ERR_SHAPE, MX_ERR_ALIGN (16-byte alignment of
- * every pointer) and MX_ERR_HIP as for mx_gemm.  workspace/ws_bytes are
- * reserved and may be NULL/0.
+ * every pointer) and MX_ERR_HIP as for mx_gemm.  workspace: split-K scratch
+ * as for mx_gemm (see mx_gemm_w4a16_workspace_size), used by the general
+ * kernel only.
  */
 mx_status mx_gemm_w4a16(mx_format w_fmt, const void* a_bf16, const void* w_q, const void* w_s, int64_t m,
                         int64_t n, int64_t k, float alpha, void* y, unsigned flags, void* workspace,
                         size_t ws_bytes, mx_stream_t stream);
+
+/*
+ * mx_gemm_workspace_size / mx_gemm_w4a16_workspace_size -- *bytes = the
+ * workspace with which mx_gemm (a_fmt == w_fmt MXFP4/MXFP8, or NVFP4 for
+ * nv_gemm, with the given flags) or mx_gemm_w4a16 splits K on this shape;
+ * 0 when it never does.  Pure host logic; errors as the GEMM's own
+ * argument checks.
+ */
+mx_status mx_gemm_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k,
+                                 unsigned flags, size_t* bytes);
+mx_status mx_gemm_w4a16_workspace_size(mx_format w_fmt, int64_t m, int64_t n, int64_t k, size_t* bytes);
 
 /*
  * mx_gemm_w4a16_plan -- writes into `name` (capacity `len`) the kernel that

@@ -35,6 +35,7 @@ def test_header_declares_expected_entry_points():
     for n in ("mx_pack_weights", "mx_quantize_act", "mx_gemm", "mx_gemm_fused", "nv_gemm",
               "mx_gemm_w4a16", "mx_gemm_w4a16_plan", "mx_fake_quant",
               "mx_gemm_swiglu_quant", "mx_gemm_swiglu_quant_plan", "mx_swiglu_quant",
+              "mx_gemm_workspace_size", "mx_gemm_w4a16_workspace_size",
               "mx_tensor_amax", "mx_nv_global_scale", "mx_gemm_plan", "mx_status_string",
               "mx_abi_version"):
         assert n in names
@@ -176,6 +177,29 @@ def test_swiglu_validation():
     assert "swiglu" in mxl.mx_gemm_swiglu_quant_plan(8192, 17408, 5120)
     with pytest.raises(mxl.MXError):
         mxl.mx_gemm_swiglu_quant_plan(16, 64, 96)
+
+
+def test_workspace_sizes():
+    # few tiles and a long K: split-K with S fp32 partials of M x N
+    assert mxl.mx_gemm_workspace_size("mxfp8", "mxfp8", 64, 96, 5120) == 10 * 64 * 96 * 4
+    assert mxl.mx_gemm_workspace_size("mxfp4", "mxfp4", 512, 2048, 5120) == 4 * 512 * 2048 * 4
+    assert mxl.mx_gemm_workspace_size("nvfp4", "nvfp4", 96, 160, 4096) > 0
+    # tiles that fill the GPU, the decode kernel, the prefill kernel: none
+    assert mxl.mx_gemm_workspace_size("mxfp4", "mxfp4", 8192, 17408, 5120) == 0
+    assert mxl.mx_gemm_workspace_size("mxfp4", "mxfp4", 8, 17408, 5120) == 0
+    assert mxl.mx_gemm_workspace_size("mxfp8", "mxfp8", 4096, 6144, 5120) == 0
+    # short K: no split
+    assert mxl.mx_gemm_workspace_size("mxfp8", "mxfp8", 64, 96, 256) == 0
+    b = ctypes.c_size_t(7)
+    assert L.mx_gemm_workspace_size(0, 2, 4, 4, 64, 0, ctypes.byref(b)) == INVALID   # mixed NVFP4
+    assert L.mx_gemm_workspace_size(0, 0, 4, 4, 48, 0, ctypes.byref(b)) == SHAPE
+    assert L.mx_gemm_workspace_size(0, 0, 4, 4, 64, 0, None) == INVALID
+    assert L.mx_gemm_w4a16_workspace_size(1, 4, 4, 64, ctypes.byref(b)) == UNSUPPORTED
+    assert L.mx_gemm_w4a16_workspace_size(2, 8, 512, 5120, ctypes.byref(b)) == OK and b.value == 0  # decode
+    assert L.mx_gemm_w4a16_workspace_size(2, 96, 160, 4096, ctypes.byref(b)) == OK and b.value > 0
+    # a misaligned workspace is rejected before any HIP call
+    assert L.mx_gemm(0, 0, GOOD, GOOD, GOOD, GOOD, 4, 4, 64, GOOD, 0, BAD_ALIGN, 64, None) == ALIGN
+    assert "split-K" in mxl.mx_gemm_plan("mxfp8", "mxfp8", 64, 96, 5120)
 
 
 def test_gate_up_interleave_index():

@@ -38,7 +38,7 @@ def run_mx(a_bits, w_bits, fmt="mxfp4", out_f32=False, fused=False):
     k = a_bits.shape[1]
     wq, ws = mxl.mx_pack_weights(w, fmt=fmt, rule=W_RULE[fmt])
     aq, as_ = mxl.mx_quantize_act(a, fmt=fmt, rule="ceil")
-    y = mxl.mx_gemm(aq, as_, wq, ws, k, fmt, fmt, out_f32=out_f32)
+    y = mxl.mx_gemm(aq, as_, wq, ws, k, fmt, fmt, out_f32=out_f32, split_k=False)
     yf = mxl.mx_gemm_fused(a, wq, ws, fmt, "ceil", fmt, out_f32=out_f32) if fused else None
     torch.cuda.synchronize()
     return y, yf, (aq, as_), (wq, ws)
@@ -77,7 +77,12 @@ def test_gemm_full_small_shapes(fmt, m, k, n):
         check_gemm(y_host(y), y_ref, s, not out_f32, f"{fmt} {m}x{k}x{n} f32={out_f32}")
         # the fused prologue quantizes exactly like the standalone quantizer
         # and feeds the same matrix-core sequence: bitwise equal outputs
+        # (both unsplit)
         assert torch.equal(y, yf), "fused != standalone"
+        # the default call, which splits K where the tiles leave the GPU idle
+        ys = mxl.mx_gemm(aq, as_, wq, ws, k, fmt, fmt, out_f32=out_f32)
+        torch.cuda.synchronize()
+        check_gemm(y_host(ys), y_ref, s, not out_f32, f"{fmt} {m}x{k}x{n} f32={out_f32} split-K default")
 
 
 @pytest.mark.parametrize("m,k,n", [(129, 160, 257), (200, 416, 300), (33, 5120, 96)])
@@ -91,11 +96,13 @@ def test_mxfp8_fast_path_within_its_documented_bound(m, k, n):
     a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
     wq, ws = mxl.mx_pack_weights(w, fmt="mxfp8", rule="floor")
     aq, as_ = mxl.mx_quantize_act(a, fmt="mxfp8", rule="ceil")
-    y = mxl.mx_gemm(aq, as_, wq, ws, k, "mxfp8", "mxfp8", out_f32=True, fp8_fast=True)
+    y = mxl.mx_gemm(aq, as_, wq, ws, k, "mxfp8", "mxfp8", out_f32=True, fp8_fast=True, split_k=False)
+    ys = mxl.mx_gemm(aq, as_, wq, ws, k, "mxfp8", "mxfp8", out_f32=True, fp8_fast=True)
     yf = mxl.mx_gemm_fused(a, wq, ws, "mxfp8", "ceil", "mxfp8", out_f32=True, fp8_fast=True)
     torch.cuda.synchronize()
     # scale the error down by 5 so that check_gemm's 1e-4 bound reads as 5e-4
     rel = check_gemm(0.2 * (y_host(y) - y_ref) + y_ref, y_ref, s, False, f"fast fp8 {m}x{k}x{n}")
+    check_gemm(0.2 * (y_host(ys) - y_ref) + y_ref, y_ref, s, False, f"fast fp8 {m}x{k}x{n} split-K default")
     assert torch.equal(y, yf)
     say(f"fast fp8 {m}x{k}x{n}: max err/S = {rel * 5.0:.2e}")
 
@@ -269,3 +276,60 @@ def test_nvfp4_config_sampled():
                                     oracle.nv_dequantize(wq, ws, len(uc), cfg.k, g_w), ir, ic)
     yv = y[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()]
     check_gemm(y_host(yv), y_ref, s, True, cfg.name)
+
+
+# split-K: few output tiles and a long K, so the library splits K over
+# workgroups (mx_gemm_workspace_size > 0) and sums fp32 partials in order
+SPLIT_SHAPES = [(300, 2048, 200), (64, 5120, 96), (1, 4096, 48), (513, 1536, 130)]
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("m,k,n", SPLIT_SHAPES)
+def test_gemm_split_k(fmt, m, k, n):
+    if fmt == "mxfp4" and m <= 32:
+        pytest.skip("M <= 32 MXFP4 runs the decode kernel (no split)")
+    ws = mxl.mx_gemm_workspace_size(fmt, fmt, m, n, k)
+    plan = mxl.mx_gemm_plan(fmt, fmt, m, n, k)
+    say(f"split-K {fmt} m={m} k={k} n={n}: workspace {ws} B, plan {plan}")
+    assert ws > 0 and "split-K" in plan
+    a_bits = W.activations_entry_outliers(m, k)
+    w_bits = W.normal_bf16(n, k, 0.02, 1)
+    y_ref, s, _, _ = oracle_full(a_bits, w_bits, fmt)
+    a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
+    wq, wsc = mxl.mx_pack_weights(w, fmt=fmt, rule=W_RULE[fmt])
+    aq, as_ = mxl.mx_quantize_act(a, fmt=fmt, rule="ceil")
+    for out_f32 in (False, True):
+        ys = mxl.mx_gemm(aq, as_, wq, wsc, k, fmt, fmt, out_f32=out_f32)
+        y1 = mxl.mx_gemm(aq, as_, wq, wsc, k, fmt, fmt, out_f32=out_f32, split_k=False)
+        ys2 = mxl.mx_gemm(aq, as_, wq, wsc, k, fmt, fmt, out_f32=out_f32)
+        torch.cuda.synchronize()
+        check_gemm(y_host(ys), y_ref, s, not out_f32, f"split {fmt} {m}x{k}x{n} f32={out_f32}")
+        check_gemm(y_host(y1), y_ref, s, not out_f32, f"unsplit {fmt} {m}x{k}x{n} f32={out_f32}")
+        assert torch.equal(ys, ys2), "split-K is deterministic"
+
+
+def test_nvfp4_and_w4a16_split_k():
+    m, k, n = 96, 4096, 160
+    a_bits = W.normal_bf16(m, k, 1.0, 3)
+    w_bits = W.normal_bf16(n, k, 0.02, 4)
+    g_a = oracle.nv_global_scale(oracle.bf16_amax(a_bits))
+    g_w = oracle.nv_global_scale(oracle.bf16_amax(w_bits))
+    assert mxl.mx_gemm_workspace_size("nvfp4", "nvfp4", m, n, k) > 0
+    aq, as_ = mxl.mx_quantize_act(cuda_bf16(a_bits), "nvfp4", global_scale=float(g_a))
+    wq, ws = mxl.mx_pack_weights(cuda_bf16(w_bits), "nvfp4", global_scale=float(g_w))
+    alpha = float(np.float32(1.0) / (np.float32(g_a) * np.float32(g_w)))
+    y = mxl.nv_gemm(aq, as_, wq, ws, k, alpha, out_f32=True)
+    torch.cuda.synchronize()
+    raq, ras = oracle.nv_quantize(a_bits, g_a)
+    rwq, rws = oracle.nv_quantize(w_bits, g_w)
+    ad = oracle.nv_dequantize(raq, ras, m, k, g_a)
+    wd = oracle.nv_dequantize(rwq, rws, n, k, g_w)
+    y_ref, s = oracle.gemm_dq(ad, wd)
+    check_gemm(y_host(y), y_ref, s, False, "nvfp4 split-K")
+    # W4A16 general kernel (M > 16 runs it) with the same weights
+    say("w4a16 split-K: " + mxl.mx_gemm_w4a16_plan("nvfp4", m, n, k))
+    yw = mxl.mx_gemm_w4a16(cuda_bf16(a_bits), wq, ws, "nvfp4", alpha=float(np.float32(1.0) / np.float32(g_w)),
+                           out_f32=True)
+    torch.cuda.synchronize()
+    yw_ref = oracle.w4a16_gemm(a_bits, rwq, rws, n, k, "nvfp4", g_w=g_w)
+    check_gemm(y_host(yw), yw_ref[0], yw_ref[1], False, "w4a16 split-K")
