@@ -466,6 +466,21 @@ def extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_d
             ts.append(e0.elapsed_time(e1) * 1e3 / reps)
         return float(np.median(ts[3:]))
 
+    # c1, the small 16 x 256 x 256 configuration: launch-bound; one quantize +
+    # GEMM pair per call
+    c1 = W.SMALL
+    a1 = to_dev(c1.activations())
+    wq1, ws1 = mxl.mx_pack_weights(to_dev(c1.weights()), "mxfp4", "even")
+    aq1 = torch.empty((c1.m, c1.k // 2), dtype=torch.uint8, device=dev)
+    as1 = torch.empty((c1.m, c1.k // 32), dtype=torch.uint8, device=dev)
+    y1 = torch.empty((c1.m, c1.n), dtype=torch.bfloat16, device=dev)
+    t_q = graph_us(lambda: mxl.mx_quantize_act(a1, out=(aq1, as1)))
+    t_g = graph_us(lambda: mxl.mx_gemm(aq1, as1, wq1, ws1, c1.k, y=y1))
+    rows["small_c1_16x256x256"] = {"quantize_us": round(t_q, 2), "gemm_us": round(t_g, 2),
+                                   "kernel": mxl.mx_gemm_plan("mxfp4", "mxfp4", c1.m, c1.n, c1.k),
+                                   "timing": "HIP graph of 10 back-to-back calls, replayed"}
+    log(f"c1 16x256x256: quantize {t_q:.2f} us, gemm {t_g:.2f} us")
+
     for name, fmt, m, n in (("mxfp8_n96_m4096", "mxfp8", 4096, 96), ("mxfp8_n96_m1", "mxfp8", 1, 96),
                             ("mxfp4_n96_m4096", "mxfp4", 4096, 96), ("mxfp4_n2048_m512", "mxfp4", 512, 2048)):
         k = 5120

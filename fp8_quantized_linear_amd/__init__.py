@@ -26,6 +26,7 @@ FORMATS = {"mxfp4": 0, "mxfp8": 1, "nvfp4": 2}
 RULES = {"floor": 0, "ceil": 1, "even": 2}
 MX_OUT_F32 = 0x1
 MX_FP8_FAST = 0x2
+MX_DEBUG_DUMP_AQ = 0x4
 STATUS = {0: "MX_OK", 1: "MX_ERR_INVALID_ARG", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN",
           4: "MX_ERR_WORKSPACE", 5: "MX_ERR_UNSUPPORTED", 6: "MX_ERR_HIP"}
 
@@ -201,8 +202,11 @@ def mx_gemm(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str = "mxfp
 
 
 def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str = "ceil",
-                  w_fmt: str = "mxfp4", out_f32: bool = False, y=None, fp8_fast: bool = False):
-    """mx_gemm with the activation quantization done inside the GEMM from bf16 a[m, k]."""
+                  w_fmt: str = "mxfp4", out_f32: bool = False, y=None, fp8_fast: bool = False,
+                  dump_aq: bool = False):
+    """mx_gemm with the activation quantization done inside the GEMM from bf16 a[m, k].
+    dump_aq also returns the codes and scales the prologue computed:
+    (y, (a_q, a_s))."""
     _need(a, torch.bfloat16, "a")
     _need(w_q, torch.uint8, "w_q")
     _need(w_s, torch.uint8, "w_s")
@@ -211,9 +215,17 @@ def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str =
     if w_q.shape[1] != codes_per_row(w_fmt, k) or w_s.shape != (n, k // 32):
         raise ValueError("weight tensors do not match k")
     y = _gemm_out(m, n, a.device, out_f32, y)
+    flags = _flags(out_f32, fp8_fast)
+    ws, wsb, qb = None, 0, m * codes_per_row(a_fmt, k)
+    if dump_aq:
+        wsb = qb + m * (k // 32)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=a.device)
+        flags |= MX_DEBUG_DUMP_AQ
     st = lib.mx_gemm_fused(_fmt(a_fmt), _rule(a_rule), _ptr(a), _fmt(w_fmt), _ptr(w_q), _ptr(w_s),
-                           m, n, k, _ptr(y), _flags(out_f32, fp8_fast), None, 0, _stream(a))
+                           m, n, k, _ptr(y), flags, _ptr(ws), wsb, _stream(a))
     _check(st, "mx_gemm_fused")
+    if dump_aq:
+        return y, (ws[:qb].view(m, codes_per_row(a_fmt, k)), ws[qb:].view(m, k // 32))
     return y
 
 

@@ -35,7 +35,7 @@ size_t mxl_dq_workspace(int64_t m, int64_t n, int64_t k);
 int mxl_dq_splits(int64_t m, int64_t n, int64_t k);
 hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, int w_bits,
                                     const void* wq, const void* ws, int64_t m, int64_t n, int64_t k,
-                                    void* y, int out_f32, hipStream_t stream);
+                                    void* y, int out_f32, void* dump_q, void* dump_s, hipStream_t stream);
 hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const void* wq, const void* ws, int64_t m,
                               int64_t n, int64_t k, float alpha, void* y, int out_f32, void* work,
                               size_t work_bytes, hipStream_t stream);
@@ -43,8 +43,8 @@ hipError_t mxl_launch_mxfp8_exact_gemm(const void* aq, const void* as, const voi
                                        int64_t m, int64_t n, int64_t k, void* y, int out_f32, void* work,
                                        size_t work_bytes, hipStream_t stream);
 hipError_t mxl_launch_mxfp8_exact_gemm_fused(int a_rule, const void* a_bf16, const void* wq, const void* ws,
-                                             int64_t m, int64_t n, int64_t k, void* y, int out_f32,
-                                             hipStream_t stream);
+                                             int64_t m, int64_t n, int64_t k, void* y, int out_f32, void* dump_q,
+                                             void* dump_s, hipStream_t stream);
 hipError_t mxl_launch_w4a16_gemm(int w_nv, const void* a_bf16, const void* wq, const void* ws, int64_t m,
                                  int64_t n, int64_t k, float alpha, void* y, int out_f32, void* work,
                                  size_t work_bytes, hipStream_t stream);
@@ -201,24 +201,32 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf1
                         const void* w_q, const void* w_s, int64_t m, int64_t n, int64_t k, void* y,
                         unsigned flags, void* workspace, size_t ws_bytes, mx_stream_t stream)
 {
-    (void)workspace;
-    (void)ws_bytes;
     if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || a_fmt == MX_FMT_NVFP4 || w_fmt == MX_FMT_NVFP4 ||
         !valid_rule(a_rule))
         return MX_ERR_INVALID_ARG;
     if (!a_bf16 || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
-    if (flags & ~(MX_OUT_F32 | MX_FP8_FAST)) return MX_ERR_INVALID_ARG;
+    if (flags & ~(MX_OUT_F32 | MX_FP8_FAST | MX_DEBUG_DUMP_AQ)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, 32);
     if (st != MX_OK) return st;
     if (a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
     if (!aligned16(a_bf16) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y)) return MX_ERR_ALIGN;
+    // debug dump of the prologue's codes and scales into the workspace
+    void *dump_q = nullptr, *dump_s = nullptr;
+    if (flags & MX_DEBUG_DUMP_AQ) {
+        const size_t qb = (size_t)m * k * bits_of(a_fmt) / 8, sb = (size_t)m * (k / 32);
+        if (!workspace || ws_bytes < qb + sb) return MX_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return MX_ERR_ALIGN;
+        dump_q = workspace;
+        dump_s = static_cast<uint8_t*>(workspace) + qb;
+    }
     if ((st = check_device()) != MX_OK) return st;
     const int f32 = (flags & MX_OUT_F32) ? 1 : 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST))
-        return from_hip(mxl_launch_mxfp8_exact_gemm_fused((int)a_rule, a_bf16, w_q, w_s, m, n, k, y, f32, hs));
+        return from_hip(mxl_launch_mxfp8_exact_gemm_fused((int)a_rule, a_bf16, w_q, w_s, m, n, k, y, f32, dump_q,
+                                                          dump_s, hs));
     return from_hip(mxl_launch_mx_gemm_fused(bits_of(a_fmt), (int)a_rule, a_bf16, bits_of(w_fmt), w_q, w_s,
-                                             m, n, k, y, f32, hs));
+                                             m, n, k, y, f32, dump_q, dump_s, hs));
 }
 
 mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t m, int64_t n,

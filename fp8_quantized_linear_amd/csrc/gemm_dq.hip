@@ -167,6 +167,10 @@ struct DqArgs {
     // part + s * M * N
     float* part;
     int splits, chunk;
+    // FUSED_A only, optional: the prologue's E4M3 codes [M, K] and E8M0
+    // scales [M, K/32], written by the tiles of the first tile column
+    uint8_t* dump_q;
+    uint8_t* dump_s;
 };
 
 // FUSED_A (MXFP8 only): A arrives as bf16 [M, K]; each 8-element chunk is
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
             *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + (((2 * c + 1) ^ dq_swz(row)) * 16)) = d1;
         }
     };
-    auto store_stage = [&](int buf, int set) __attribute__((always_inline)) {
+    auto store_stage = [&](int buf, int set, int kg) __attribute__((always_inline)) {
         uint8_t* a_t = smem + buf * STAGE;
         uint8_t* w_t = a_t + A_TILE;
 #pragma unroll
@@ -333,7 +337,14 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
                 if (FUSED_A) {
                     const uint32_t amax = quad_max_u32(amax_bits8(x));
                     const int e = scale_exponent<ELEM_E4M3, A_RULE>(amax);
-                    d = dequant8_mxfp8(encode8_e4m3(x, e), e);
+                    const uint2 codes = encode8_e4m3(x, e);
+                    d = dequant8_mxfp8(codes, e);
+                    // debug dump of the prologue's codes (first tile column only)
+                    const int grow = m0 + row, kel = kg * DQ_BK + c * 8;
+                    if (p.dump_q != nullptr && tn == 0 && grow < p.M && kel < K) {
+                        *reinterpret_cast<uint2*>(p.dump_q + (size_t)grow * K + kel) = codes;
+                        if ((c & 3) == 0) p.dump_s[(size_t)grow * (K / 32) + kel / 32] = (uint8_t)(e + 127);
+                    }
                 }
                 *reinterpret_cast<uint4*>(a_t + row * DQ_ROW_BYTES + ((c ^ dq_swz(row)) * 16)) = d;
             } else if (A_CH % NT == 0 || qi < A_CH) {
@@ -400,12 +411,12 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
     // compiler's waits count exactly the loads of stage kt + 2 as newer.
     load_stage(kt0, 0);
     load_stage(kt0 + 1, 1);
-    store_stage(0, 0);
+    store_stage(0, 0, kt0);
     __syncthreads();
     auto iter = [&](int kt, int set) __attribute__((always_inline)) {
         load_stage(kt0 + kt + 2, set);
         compute_stage(set);
-        store_stage(set ^ 1, set ^ 1);
+        store_stage(set ^ 1, set ^ 1, kt0 + kt + 1);
         __syncthreads();
     };
     int kt = 0;
@@ -570,10 +581,12 @@ static hipError_t fused8(const DqArgs& a, int out_f32, hipStream_t stream)
 
 extern "C" hipError_t mxl_launch_mxfp8_exact_gemm_fused(int a_rule, const void* a_bf16, const void* wq,
                                                         const void* ws, int64_t m, int64_t n, int64_t k,
-                                                        void* y, int out_f32, hipStream_t stream)
+                                                        void* y, int out_f32, void* dump_q, void* dump_s,
+                                                        hipStream_t stream)
 {
     DqArgs a{static_cast<const uint8_t*>(a_bf16), nullptr, static_cast<const uint8_t*>(wq),
-             static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, 1.0f, nullptr, 1, 1 << 30};
+             static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, 1.0f, nullptr, 1, 1 << 30,
+             static_cast<uint8_t*>(dump_q), static_cast<uint8_t*>(dump_s)};
     if (a_rule == RULE_CEIL) return fused8<RULE_CEIL>(a, out_f32, stream);
     if (a_rule == RULE_FLOOR) return fused8<RULE_FLOOR>(a, out_f32, stream);
     return fused8<RULE_EVEN>(a, out_f32, stream);

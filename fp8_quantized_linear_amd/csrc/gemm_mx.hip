@@ -116,6 +116,10 @@ struct GemmArgs {
     // partial tile to part + s * M * N and splitk_reduce_kernel sums them
     float* part;
     int splits, chunk;
+    // fused kernel only, optional: the prologue's A codes [M, K*abits/8] and
+    // E8M0 scales [M, K/32], written by the tiles of the first tile column
+    uint8_t* dump_q;
+    uint8_t* dump_s;
 };
 
 
@@ -160,6 +164,7 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
     struct Stage {
         uint4 ra[A_PER_T], rw[W_PER_T];
         uint32_t rsa[SA_PER_T], rsw[SW_PER_T];
+        int kt;   // global stage index
     };
 
     // Buffer resources: 32-bit per-lane offsets, the stage offset in a scalar
@@ -200,6 +205,7 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
     };
     auto load_stage = [&](int kl, Stage& st) {
         const int kt = kt0 + kl;   // global stage index
+        st.kt = kt;
         const bool a_in_k = SCALE_DWORD || kt * A_STAGE_BYTES + a_c * 16 < a_row_bytes;
         const bool w_in_k = SCALE_DWORD || kt * TW::ROW_BYTES + w_c * 16 < w_row_bytes;
 #pragma unroll
@@ -250,15 +256,21 @@ __global__ __launch_bounds__(WM * WN * 64) void mx_gemm_kernel(GemmArgs p)
                 const int row = q / 16, c = q % 16, blk = c / 4, part = c % 4;
                 const uint32_t amax = quad_max_u32(amax_bits8(ra[i]));
                 const int e = scale_exponent<ABITS == 4 ? ELEM_E2M1 : ELEM_E4M3, A_RULE>(amax);
+                // debug dump of the prologue's codes (first tile column only)
+                const int grow = m0 + row, kel = sg.kt * BK + c * 8;
+                const bool dump = BM == 128 && p.dump_q != nullptr && tn == 0 && grow < p.M && kel < p.K;
                 if (ABITS == 4) {
                     const uint32_t codes = encode8_e2m1(ra[i], e);
                     const int chunk = blk ^ TA::swz(row);
                     *reinterpret_cast<uint32_t*>(a_t + row * TA::ROW_BYTES + chunk * 16 + part * 4) = codes;
+                    if (dump) *reinterpret_cast<uint32_t*>(p.dump_q + (size_t)grow * (p.K / 2) + kel / 2) = codes;
                 } else {
                     const uint2 codes = encode8_e4m3(ra[i], e);
                     const int chunk = (2 * blk + part / 2) ^ TA::swz(row);
                     *reinterpret_cast<uint2*>(a_t + row * TA::ROW_BYTES + chunk * 16 + (part % 2) * 8) = codes;
+                    if (dump) *reinterpret_cast<uint2*>(p.dump_q + (size_t)grow * p.K + kel) = codes;
                 }
+                if (dump && part == 0) p.dump_s[(size_t)grow * (p.K / 32) + kel / 32] = (uint8_t)(e + 127);
                 if (part == 0)
                     reinterpret_cast<uint8_t*>(sa16)[scale_entry<WTM>(row, blk % 2) * 2 + blk / 2] = (uint8_t)(e + 127);
             }
@@ -960,7 +972,7 @@ extern "C" hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq,
 {
     GemmArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
                static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k,
-               nullptr, 1, 1 << 30};
+               nullptr, 1, 1 << 30, nullptr, nullptr};
     const ShapeClass sc = classify(a_bits, m, n, k, false);
     if (sc == SC_DEFAULT && work) {
         int chunk;
@@ -989,11 +1001,15 @@ extern "C" hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq,
 
 extern "C" hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, int w_bits,
                                                const void* wq, const void* ws, int64_t m, int64_t n,
-                                               int64_t k, void* y, int out_f32, hipStream_t stream)
+                                               int64_t k, void* y, int out_f32, void* dump_q, void* dump_s,
+                                               hipStream_t stream)
 {
     GemmArgs a{static_cast<const uint8_t*>(a_bf16), nullptr, static_cast<const uint8_t*>(wq),
-               static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, nullptr, 1, 1 << 30};
-    const ShapeClass sc = classify(a_bits, m, n, k, true);
+               static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, nullptr, 1, 1 << 30,
+               static_cast<uint8_t*>(dump_q), static_cast<uint8_t*>(dump_s)};
+    // the dump is built into the 128 x 128 fused kernel only (the 256 x 256
+    // one has no registers to spare); both accumulate alike
+    const ShapeClass sc = dump_q ? SC_DEFAULT : classify(a_bits, m, n, k, true);
     if (a_bits == 4 && w_bits == 4) {
         if (a_rule == RULE_CEIL) return dispatch_out<4, 4, true, RULE_CEIL>(a, sc, out_f32, stream);
         if (a_rule == RULE_FLOOR) return dispatch_out<4, 4, true, RULE_FLOOR>(a, sc, out_f32, stream);

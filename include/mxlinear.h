@@ -88,9 +88,11 @@ typedef enum {
                           * throughput); their internal accumulation is inexact, with
                           * errors measured up to ~2e-4 * sum|a*b|, so this opts out of
                           * the 1e-4 bound that the default path meets */
+#define MX_DEBUG_DUMP_AQ 0x4u /* mx_gemm_fused only: also write the prologue's A codes and scales
+                                 to the workspace (see mx_gemm_fused) */
 
 /* ABI version of this header (bumped on any signature change). */
-#define MXLINEAR_ABI_VERSION 5
+#define MXLINEAR_ABI_VERSION 6
 int mx_abi_version(void);
 
 /* Static text for a status code; never NULL. */
@@ -154,7 +156,12 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
  * mx_gemm_fused -- mx_gemm with the activation quantization computed inside
  * the GEMM from bf16 A ([m, k]), with scale rule a_rule.  The result equals
  * mx_quantize_act followed by an unsplit mx_gemm.  workspace/ws_bytes are
- * unused and may be NULL/0.
+ * unused and may be NULL/0, unless flags has MX_DEBUG_DUMP_AQ: then the
+ * quantization the prologue computed is also written to the workspace, A
+ * codes [m, k * bits / 8] (bits 4 or 8) followed by E8M0 scales [m, k/32],
+ * the layout of mx_quantize_act, so it can be checked bit for bit.  The
+ * workspace must then hold both (MX_ERR_WORKSPACE otherwise) and be 16-byte
+ * aligned.
  */
 mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf16,
                         mx_format w_fmt, const void* w_q, const void* w_s, int64_t m, int64_t n,

@@ -202,6 +202,17 @@ def test_workspace_sizes():
     assert "split-K" in mxl.mx_gemm_plan("mxfp8", "mxfp8", 64, 96, 5120)
 
 
+def test_fused_dump_validation():
+    f = L.mx_gemm_fused
+    def g(flags=0x4, ws=P(0x40000), wsb=1 << 20, k=64):
+        return f(0, 1, GOOD, 0, GOOD, GOOD, 4, 4, k, GOOD, flags, ws, wsb, None)
+    assert g(flags=0x8) == INVALID
+    assert g(ws=None) == WORKSPACE
+    assert g(wsb=4 * 32 + 4 * 2 - 1) == WORKSPACE          # codes 4 x 32 B + scales 4 x 2 B
+    assert g(ws=BAD_ALIGN) == ALIGN
+    assert g(wsb=4 * 32 + 4 * 2) in (OK, UNSUPPORTED, HIPERR)
+
+
 def test_gate_up_interleave_index():
     idx = mxl.gate_up_interleave_index(96).tolist()
     assert sorted(idx) == list(range(192))

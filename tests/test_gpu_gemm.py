@@ -333,3 +333,23 @@ def test_nvfp4_and_w4a16_split_k():
     torch.cuda.synchronize()
     yw_ref = oracle.w4a16_gemm(a_bits, rwq, rws, n, k, "nvfp4", g_w=g_w)
     check_gemm(y_host(yw), yw_ref[0], yw_ref[1], False, "w4a16 split-K")
+
+
+# The fused prologue's own quantization, dumped by MX_DEBUG_DUMP_AQ, against
+# the oracle bit for bit: MXFP4 on the 128 x 128 and 256 x 256 fused kernels
+# (ragged M and N), MXFP8 on the exact (dequantizing) and the fast fused paths.
+@pytest.mark.parametrize("fmt,fast,m,k,n", [("mxfp4", False, 200, 416, 300), ("mxfp4", False, 1100, 1152, 1090),
+                                            ("mxfp8", False, 130, 544, 260), ("mxfp8", True, 130, 544, 260)])
+def test_fused_prologue_codes_dumped(fmt, fast, m, k, n):
+    say(f"fused dump {fmt} fast={fast} m={m} k={k} n={n}")
+    a_bits = W.fuzz_bf16(m, k, seed=17)
+    w_bits = W.normal_bf16(n, k, 0.02, 1)
+    a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
+    wq, ws = mxl.mx_pack_weights(w, fmt=fmt, rule=W_RULE[fmt])
+    y, (dq, ds) = mxl.mx_gemm_fused(a, wq, ws, fmt, "ceil", fmt, fp8_fast=fast, dump_aq=True)
+    y0 = mxl.mx_gemm_fused(a, wq, ws, fmt, "ceil", fmt, fp8_fast=fast)
+    torch.cuda.synchronize()
+    rq, rs = oracle.mx_quantize(ELEM[fmt], "ceil", a_bits)
+    assert np.array_equal(host(ds), rs), "prologue scales"
+    assert np.array_equal(host(dq), rq), "prologue codes"
+    assert torch.equal(y, y0), "the dump does not change the product"
