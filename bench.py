@@ -161,6 +161,16 @@ def main():
                 "per_launch_us": {"up": round(gemm_up_ms * 1e3, 2), "down": round(gemm_dn_ms * 1e3, 2)},
                 "algorithmic_flop_per_launch": up.flops}
 
+    # the graphics clock under this load (power-limited, below the 2.4 GHz of
+    # the spec peak), and the peak and fraction at that clock
+    clock = measure_gfxclk(lambda: (mxl.mx_gemm(aq_up, as_up, wq_up, ws_up, up.k, y=y_up),
+                                    mxl.mx_gemm(aq_dn, as_dn, wq_dn, ws_dn, down.k, y=y_dn)), torch)
+    if clock.get("gfxclk_mhz"):
+        peak_clk = PEAK_TFLOPS["fp4"] * clock["gfxclk_mhz"] / 2400.0
+        roofline["peak_at_measured_clock"] = round(peak_clk, 1)
+        roofline["frac_at_measured_clock"] = round(achieved / peak_clk, 4)
+    roofline["clock"] = clock
+
     rows = {"pack_weights_ms": round(pack_ms, 3)}
     if not args.quick:
         rows.update(extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_dn))
@@ -183,6 +193,46 @@ def main():
         "rows": rows,
     }
     print(json.dumps(out))
+
+
+def measure_gfxclk(step, torch, seconds: float = 2.5):
+    """Median graphics clock (MHz) reported by amdsmi (current_gfxclk, which
+    the driver refreshes about once a second) while `step` runs back to back
+    for `seconds`; samples from the first second are dropped."""
+    import threading
+    import time
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+        amdsmi.amdsmi_get_gpu_metrics_info(handle)
+    except Exception as e:   # no amdsmi or no access on this machine
+        return {"gfxclk_mhz": None, "error": repr(e)[:200]}
+    samples, stop = [], [False]
+    t0 = time.time()
+
+    def sampler():
+        while not stop[0]:
+            try:
+                mhz = amdsmi.amdsmi_get_gpu_metrics_info(handle).get("current_gfxclk")
+                if isinstance(mhz, (int, float)) and time.time() - t0 > 1.0:
+                    samples.append(float(mhz))
+            except Exception:
+                pass
+            time.sleep(0.01)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    while time.time() - t0 < seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    stop[0] = True
+    th.join()
+    if not samples:
+        return {"gfxclk_mhz": None, "error": "no samples"}
+    return {"gfxclk_mhz": float(np.median(samples)), "samples": len(samples),
+            "source": "amdsmi current_gfxclk during back-to-back headline GEMMs"}
 
 
 def traffic_from_profiles():
