@@ -26,8 +26,9 @@
 //    exponent spread, beyond the 1e-4 bound.  The f16/bf16 instructions stay at
 //    fp32 rounding level.  An E4M3 value times its power-of-two block scale is
 //    exact in bf16 (8-bit significand, fp32 exponent range) for every block
-//    whose scale exponent is at least -117; below that, dequantized values
-//    under 2^-126 are flushed (only blocks with amax below ~2^-110 have them).
+//    whose scale exponent is at least -117.  Below that (blocks with amax
+//    under ~2^-110), values under 2^-126 become bf16 subnormals rounded to
+//    nearest even, and in blocks with scale 2^-127 they are flushed to zero.
 //
 // 16-bit matrix-core layout (32x32x16): lane l = r + 32 g holds row/column r
 // and the 8 consecutive K elements [8g, 8g + 8) of the 16-wide step.

@@ -125,6 +125,42 @@ def test_integer_exact_tiny():
         assert np.array_equal(y_host(y), y_ref.astype(np.float32)), (m, k, n)
 
 
+# Exact MXFP8 dequantization inside the GEMM, read back through a selection
+# matrix: W row n holds the code of 1.0 (scale 2^0) at position n and zeros
+# elsewhere, so Y[m, n] = dequant(A)[m, n] with a single product.  A takes every
+# finite E4M3 code and scale exponents from -127 (the one the conversion cannot
+# take directly) upwards.  The conversion rounds each value to bf16: exact
+# down to 2^-126, and below that (blocks with scales under 2^-117) to bf16
+# subnormals, nearest even.  Blocks with scale 2^-127 keep exactly the values
+# of at least 2^-126 and flush the rest to zero.  K = 256 takes the scales as
+# aligned dwords (K % 128 == 0), K = 160 as bytes.
+@pytest.mark.parametrize("k", [256, 160])
+def test_mxfp8_exact_dequantization_by_selection(k):
+    say(f"mxfp8 selection k={k}")
+    rng = np.random.default_rng(31)
+    m = 96
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # finite E4M3
+    aq = codes[rng.integers(0, codes.size, (m, k))]
+    a_s = rng.choice(np.array([0, 0, 0, 1, 2, 5, 100, 127, 130], np.uint8), (m, k // 32))
+    a_s[0, :] = 0                                   # a whole row of 2^-127 blocks
+    wq = np.zeros((k, k), np.uint8)
+    wq[np.arange(k), np.arange(k)] = 0x38            # E4M3 1.0
+    ws = np.full((k, k // 32), 127, np.uint8)
+    ad = oracle.mx_dequantize("e4m3", aq, a_s, m, k)
+    rounded = (W._to_bf16_bits(ad.astype(np.float32)).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    tiny = np.repeat(a_s == 0, 32, axis=1)
+    expect = np.where(tiny, np.where(np.abs(ad) >= 2.0 ** -126, ad, 0.0), rounded)
+    assert np.count_nonzero(rounded != ad) > 0 and np.count_nonzero(tiny & (ad != 0) & (expect == 0)) > 0
+    dev = torch.device("cuda")
+    y = mxl.mx_gemm(torch.from_numpy(aq).to(dev), torch.from_numpy(a_s).to(dev), torch.from_numpy(wq).to(dev),
+                    torch.from_numpy(ws).to(dev), k, "mxfp8", "mxfp8", out_f32=True, split_k=False)
+    torch.cuda.synchronize()
+    yh = host(y).astype(np.float64)
+    bad = np.argwhere(yh != expect)
+    assert bad.size == 0, f"{bad.shape[0]} mismatches, first at {bad[0]}: {yh[tuple(bad[0])]} vs " \
+                          f"{expect[tuple(bad[0])]} (code {aq[tuple(bad[0])]:#x}, scale {a_s[bad[0][0], bad[0][1] // 32]})"
+
+
 def test_decode_shapes_full():
     for cfg in W.DECODE:
         say(f"decode {cfg.name}")
