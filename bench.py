@@ -252,7 +252,7 @@ def traffic_from_profiles():
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("mx_device.h", "gemm_mx.hip", "gemm_prefill.hip"):
+    for f in ("mx_device.h", "gemm_mx.hip", "gemm_prefill.hip", "gemm_prefill_tile.inc"):
         h.update(open(os.path.join(ROOT, "fp8_quantized_linear_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 

@@ -65,6 +65,8 @@ def _load():
     L.mx_gemm_swiglu_quant_plan.argtypes = [i64, i64, i64, ctypes.c_char_p, sz]
     L.mx_swiglu_quant.restype = i32
     L.mx_swiglu_quant.argtypes = [P, i64, i64, P, P, P]
+    L.mx_gemm_fused_workspace_size.restype = i32
+    L.mx_gemm_fused_workspace_size.argtypes = [i32, i32, i64, i64, i64, u32, ctypes.POINTER(sz)]
     L.mx_gemm_workspace_size.restype = i32
     L.mx_gemm_workspace_size.argtypes = [i32, i32, i64, i64, i64, u32, ctypes.POINTER(sz)]
     L.mx_gemm_w4a16_workspace_size.restype = i32
@@ -201,12 +203,21 @@ def mx_gemm(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str = "mxfp
     return y
 
 
+def mx_gemm_fused_workspace_size(a_fmt: str, w_fmt: str, m: int, n: int, k: int, fp8_fast: bool = False) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib.mx_gemm_fused_workspace_size(_fmt(a_fmt), _fmt(w_fmt), m, n, k, _flags(False, fp8_fast),
+                                            ctypes.byref(b)), "mx_gemm_fused_workspace_size")
+    return b.value
+
+
 def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str = "ceil",
                   w_fmt: str = "mxfp4", out_f32: bool = False, y=None, fp8_fast: bool = False,
-                  dump_aq: bool = False):
+                  dump_aq: bool = False, quantize_once: bool = True, workspace=None):
     """mx_gemm with the activation quantization done inside the GEMM from bf16 a[m, k].
     dump_aq also returns the codes and scales the prologue computed:
-    (y, (a_q, a_s))."""
+    (y, (a_q, a_s)).  quantize_once passes the workspace the library asks for
+    (large MXFP4 shapes: A is quantized once into it, in the same launch);
+    `workspace` (uint8, on a's device) is used instead when given."""
     _need(a, torch.bfloat16, "a")
     _need(w_q, torch.uint8, "w_q")
     _need(w_s, torch.uint8, "w_s")
@@ -221,6 +232,11 @@ def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str =
         wsb = qb + m * (k // 32)
         ws = torch.empty(wsb, dtype=torch.uint8, device=a.device)
         flags |= MX_DEBUG_DUMP_AQ
+    elif workspace is not None:
+        _need(workspace, torch.uint8, "workspace")
+        ws, wsb = workspace, workspace.numel()
+    elif quantize_once:
+        ws, wsb = _workspace(lib.mx_gemm_fused_workspace_size, a.device, _fmt(a_fmt), _fmt(w_fmt), m, n, k, flags)
     st = lib.mx_gemm_fused(_fmt(a_fmt), _rule(a_rule), _ptr(a), _fmt(w_fmt), _ptr(w_q), _ptr(w_s),
                            m, n, k, _ptr(y), flags, _ptr(ws), wsb, _stream(a))
     _check(st, "mx_gemm_fused")

@@ -35,7 +35,9 @@ size_t mxl_dq_workspace(int64_t m, int64_t n, int64_t k);
 int mxl_dq_splits(int64_t m, int64_t n, int64_t k);
 hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, int w_bits,
                                     const void* wq, const void* ws, int64_t m, int64_t n, int64_t k,
-                                    void* y, int out_f32, void* dump_q, void* dump_s, hipStream_t stream);
+                                    void* y, int out_f32, void* dump_q, void* dump_s, void* work,
+                                    size_t work_bytes, hipStream_t stream);
+size_t mxl_mx_gemm_fused_workspace(int a_bits, int64_t m, int64_t n, int64_t k);
 hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const void* wq, const void* ws, int64_t m,
                               int64_t n, int64_t k, float alpha, void* y, int out_f32, void* work,
                               size_t work_bytes, hipStream_t stream);
@@ -225,8 +227,23 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf1
     if (a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST))
         return from_hip(mxl_launch_mxfp8_exact_gemm_fused((int)a_rule, a_bf16, w_q, w_s, m, n, k, y, f32, dump_q,
                                                           dump_s, hs));
+    if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
     return from_hip(mxl_launch_mx_gemm_fused(bits_of(a_fmt), (int)a_rule, a_bf16, bits_of(w_fmt), w_q, w_s,
-                                             m, n, k, y, f32, dump_q, dump_s, hs));
+                                             m, n, k, y, f32, dump_q, dump_s, dump_q ? nullptr : workspace,
+                                             dump_q ? 0 : ws_bytes, hs));
+}
+
+mx_status mx_gemm_fused_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k,
+                                       unsigned flags, size_t* bytes)
+{
+    if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || a_fmt == MX_FMT_NVFP4 || w_fmt == MX_FMT_NVFP4 || !bytes)
+        return MX_ERR_INVALID_ARG;
+    if (flags & ~(MX_OUT_F32 | MX_FP8_FAST | MX_DEBUG_DUMP_AQ)) return MX_ERR_INVALID_ARG;
+    mx_status st = check_gemm_shape(m, n, k, 32);
+    if (st != MX_OK) return st;
+    if (a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
+    *bytes = (flags & MX_DEBUG_DUMP_AQ) ? 0 : mxl_mx_gemm_fused_workspace(bits_of(a_fmt), m, n, k);
+    return MX_OK;
 }
 
 mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t m, int64_t n,

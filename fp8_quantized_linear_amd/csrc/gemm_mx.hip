@@ -999,11 +999,35 @@ extern "C" hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq,
     return hipErrorInvalidValue;
 }
 
+extern "C" size_t mxl_prefill_fq_workspace(int64_t m, int64_t k);
+extern "C" hipError_t mxl_launch_mx_prefill_fq(int a_rule, const void* a_bf16, const void* wq, const void* ws,
+                                               int64_t m, int64_t n, int64_t k, void* y, int out_f32, void* work,
+                                               size_t work_bytes, hipStream_t stream);
+
+// Workspace bytes mx_gemm_fused can use on this shape: the quantize-once
+// launch for large MXFP4 shapes (0: none).
+extern "C" size_t mxl_mx_gemm_fused_workspace(int a_bits, int64_t m, int64_t n, int64_t k)
+{
+    if (a_bits == 4 && classify(4, m, n, k, true) == SC_LARGE && mxl_prefill_ok(m, n, k))
+        return mxl_prefill_fq_workspace(m, k);
+    return 0;
+}
+
 extern "C" hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, int w_bits,
                                                const void* wq, const void* ws, int64_t m, int64_t n,
                                                int64_t k, void* y, int out_f32, void* dump_q, void* dump_s,
-                                               hipStream_t stream)
+                                               void* work, size_t work_bytes, hipStream_t stream)
 {
+    // large MXFP4 shapes with a workspace: quantize A once, in the same launch
+    if (!dump_q && a_bits == 4 && w_bits == 4 && work) {
+        const size_t need = mxl_mx_gemm_fused_workspace(a_bits, m, n, k);
+        if (need > 0 && work_bytes >= need) {
+            const hipError_t e = mxl_launch_mx_prefill_fq(a_rule, a_bf16, wq, ws, m, n, k, y, out_f32, work,
+                                                          work_bytes, stream);
+            if (e == hipSuccess) return e;
+            (void)hipGetLastError();   // no cooperative launch here: the in-tile prologue below
+        }
+    }
     GemmArgs a{static_cast<const uint8_t*>(a_bf16), nullptr, static_cast<const uint8_t*>(wq),
                static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, nullptr, 1, 1 << 30,
                static_cast<uint8_t*>(dump_q), static_cast<uint8_t*>(dump_s)};

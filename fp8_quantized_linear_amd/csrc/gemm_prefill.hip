@@ -174,420 +174,151 @@ constexpr int PF_EPI_Y = 0, PF_EPI_SWIGLU = 1;
 template <bool OUT_F32, int BN, int EPI>
 __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
 {
-    using L = PfLayout<BN>;
-    constexpr int WFR = L::WFR;
     extern __shared__ __align__(16) uint8_t smem[];
+#define PF_TILE_T pf_xcd_order(p.count)
+#include "gemm_prefill_tile.inc"
+#undef PF_TILE_T
+}
 
-    int m0, n0;
-    {
-        const int t = pf_xcd_order(p.count);
-        int tm, tn;
-        if (BN == 256) {
-            pf_tile(p.tile_base + t, p.M, p.N, tm, tn);
-            n0 = tn * 256;
-        } else {   // halves of the tail tiles; both halves of a tile on one XCD
-            pf_tile(p.tile_base + t / 2, p.M, p.N, tm, tn);
-            n0 = tn * 256 + (t % 2) * 128;
-        }
-        m0 = tm * PF_BM;
-    }
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: feeds M0
-    const int wm = wave >> 1, wn = wave & 1;
-    const int r32 = lane & 31, g = lane >> 5;
-    const int K = p.K, KB = K / 32, row_bytes = K / 2;
-    const int nk = K / PF_BK;          // sub-stages
-    const int np = (nk + 1) / 2;       // pairs (the last is half when K % 256 == 128)
+// ---------------------------------------------------------------------------
+// Fused activation quantization for the large shapes, quantizing A once.
+// A prologue inside each tile (mx_gemm_kernel<FUSED>) redoes the quantization
+// of its A block for every tile column: 68 times for the 8192 x 5120 x 17408
+// projection.  Here one cooperative launch of resident workgroups (one per CU)
+// first quantizes all of A from bf16 into a workspace, exactly as
+// mx_quantize_act does (the same device functions, the same layout), meets at
+// a grid barrier, and then walks the output tiles of the prefill GEMM with
+// the same tile body (256 x 256 tiles in the same XCD-aware order, then the
+// 256 x 128 halves of a last round at most half full, as the non-persistent
+// launches do), reading the codes from the workspace.  The result is bitwise that of
+// mx_quantize_act followed by mx_gemm.
+//
+// Grid barrier: every wave waits for its stores (acknowledged by the L2);
+// thread 0 of each workgroup then releases (one write-back of its XCD's L2)
+// and counts itself, polls the count with device-scope atomic loads, and
+// acquires (one L2 invalidation) once all have arrived.  The launch is
+// cooperative, so every workgroup is resident and the count completes; the
+// poll still gives up after about half a second, sets an error word and ends
+// the workgroup, so that no mistake can hang the GPU.
+// ---------------------------------------------------------------------------
+constexpr int PF_FQ_GROUPS = 16;                 // 8-element groups per lane per step (all loaded first)
+constexpr int PF_FQ_WAVE_ELEMS = PF_FQ_GROUPS * 64 * 8;
+constexpr int PF_BARRIER_SPINS = 1 << 21;       // x s_sleep(4): about 0.5 s
 
-    const int4_t rsrc_a = make_rsrc(p.a_q, (uint32_t)p.M * row_bytes);
-    const int4_t rsrc_w = make_rsrc(p.w_q, (uint32_t)p.N * row_bytes);
-    const int4_t rsrc_as = make_rsrc(p.a_s, (uint32_t)p.M * KB);
-    const int4_t rsrc_ws = make_rsrc(p.w_s, (uint32_t)p.N * KB);
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+// Workgroup id -> position in the XCD-aware order of `count` tiles (the order
+// pf_xcd_order gives a non-persistent launch; id % 8 is still the XCD as long
+// as the grid is a multiple of 8).
+__device__ __forceinline__ int pf_xcd_order_of(int id, int count)
+{
+    const int xcd = id % NUM_XCD, j = id / NUM_XCD;
+    const int q = count / NUM_XCD, r = count % NUM_XCD;
+    return xcd * q + (xcd < r ? xcd : r) + j;
+}
 
-    // Code copies, 8 rows x 128 B = 1 KiB of LDS each: wave w copies A rows
-    // [64 w, 64 w + 64) and W rows [8 WCOP w, 8 WCOP (w + 1)).  LDS position L
-    // of a copy is row 8*copy + L/8, physical chunk L%8, which holds logical
-    // chunk (L%8) ^ swz(row).  Per-lane offsets of pair 0; pair kp adds kp*128.
-    int a_voff[L::ACOP], w_voff[L::WCOP];
-#pragma unroll
-    for (int s = 0; s < L::ACOP; ++s) {
-        const int row = 8 * (L::ACOP * wave + s) + lane / 8;
-        a_voff[s] = (m0 + row) * row_bytes + ((lane & 7) ^ pf_swz(row)) * 16;
-    }
-#pragma unroll
-    for (int s = 0; s < L::WCOP; ++s) {
-        const int row = 8 * (L::WCOP * wave + s) + lane / 8;
-        w_voff[s] = (n0 + row) * row_bytes + ((lane & 7) ^ pf_swz(row)) * 16;
-    }
-    const uint32_t a_dst = lds0 + (uint32_t)(L::ACOP * wave * 1024);           // in A slot 0
-    const uint32_t w_dst = lds0 + L::W0 + (uint32_t)(L::WCOP * wave * 1024);   // in W slot 0
-
-    // Scale copies move 8 rows x 32 B ([row][32 B] in LDS).  A window is
-    // issued as 4 pieces; piece j holds A copies t = 8 j + (0 .. 7) and W
-    // copies t = (WSC/4) j + (0 .. WSC/4 - 1), copy t covering rows
-    // [8 t, 8 t + 8) of the window.  Wave w makes copies 2 w and 2 w + 1 of
-    // each piece; with BN = 128 waves 2 and 3 have no W copy and fill the
-    // spare area from a zero-sized buffer instead.
-    constexpr int WSC = BN / 8;
-    const bool ws_real = 2 * wave + 1 < WSC / 4;
-    const int srow = lane >> 3, sdw = lane & 7;
-    int as_v[2], ws_v[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        as_v[c] = (m0 + 8 * (2 * wave + c) + srow) * KB + sdw * 4;
-        ws_v[c] = (n0 + 8 * (2 * wave + c) + srow) * KB + sdw * 4;
-    }
-
-    // Copies issued during pair y: piece (y + 5) % 4 of scale window
-    // (y + 5) / 4, and the codes of pair y + 2 (into the slot of pair y).
-    // Window w is issued during pairs 4w-5 .. 4w-2, after every read of
-    // window w-2 (same buffer), and has landed by the barrier that precedes
-    // its first read in pair 4w-1.
-    auto pair_copies = [&](int y) __attribute__((always_inline)) {
-        PfPairCopies cp;
-        const int kp = y + 2;
-        const bool livec = kp < np;
-        cp.ra = rsrc_a;
-        cp.ra[2] = livec ? cp.ra[2] : 0;
-        cp.rw = rsrc_w;
-        cp.rw[2] = livec ? cp.rw[2] : 0;
-        cp.coff = kp * PF_PROWB;
-        cp.adst = a_dst + (uint32_t)((kp & (PF_NSL - 1)) * PF_ATILE);
-        cp.wdst = w_dst + (uint32_t)((kp & (PF_NSL - 1)) * L::W_TILE);
-        const int win = (y + 5) >> 2, j = (y + 5) & 3;
-        const bool lives = win * PF_WPAIRS < np;
-        const uint32_t wbuf = lds0 + L::SC0 + (uint32_t)((win & (PF_NWIN - 1)) * L::WIN);
-        cp.ras = rsrc_as;
-        cp.ras[2] = lives ? cp.ras[2] : 0;
-        cp.rws = rsrc_ws;
-        cp.rws[2] = (lives && ws_real) ? cp.rws[2] : 0;
-        cp.asdst = wbuf + (uint32_t)((8 * j + 2 * wave) * 256);
-        cp.wsdst = ws_real ? wbuf + PF_BM * PF_SWB + (uint32_t)(((WSC / 4) * j + 2 * wave) * 256)
-                           : lds0 + L::DUMMY + (uint32_t)((wave & 1) * 512);
-        cp.asoff = 64 * j * KB + win * PF_SWB;
-        cp.wsoff = 8 * (WSC / 4) * j * KB + win * PF_SWB;
-        return cp;
+// mx_quantize_act (MXFP4, rule RULE) of `total` bf16 elements (a multiple of
+// 32), spread over the grid's waves: the per-group work of
+// mx_quantize_kernel (lane quads hold the blocks of 32).  With one workgroup
+// per CU only 4 waves per CU stream A, so each wave keeps the next step's 16
+// groups per lane in flight while it encodes the current ones (two register
+// sets, alternating).  Everything is branch-free, so that the compiler's
+// load counting lets the prefetch stay in flight: a quad past the end
+// re-reads the last block and stores the same codes and scale again, and
+// every lane of a quad stores the scale byte.
+template <int RULE>
+__device__ __forceinline__ void pf_quantize_a(const uint4* __restrict__ x, int64_t total, uint8_t* __restrict__ q,
+                                              uint8_t* __restrict__ s)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int64_t last_block = total / 32 - 1;
+    auto group = [&](int64_t w, int j) __attribute__((always_inline)) {
+        const int64_t g = w * (PF_FQ_WAVE_ELEMS / 8) + 64 * j + lane;
+        return (g >> 2) <= last_block ? g : 4 * last_block + (lane & 3);
     };
-    // copy c (0 .. COPIES-1) of a pair: 2 A and 2 W scale copies, then the A
-    // and W code copies
-    auto copy = [&](int c, const PfPairCopies& cp) __attribute__((always_inline)) {
-        if (c < 2) {
-            dma_b32_at(cp.asdst, c * 256, as_v[c], cp.asoff, cp.ras);
-        } else if (c < 4) {
-            dma_b32_at(cp.wsdst, (c - 2) * 256, ws_v[c - 2], cp.wsoff, cp.rws);
-        } else if (c - 4 < L::ACOP) {
-            const int cc = c - 4;
-            dma_b128_at(cp.adst, cc * 1024, a_voff[cc], cp.coff, cp.ra);
+    auto load = [&](uint4* v, int64_t w) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < PF_FQ_GROUPS; ++j) v[j] = x[group(w, j)];
+    };
+    auto encode = [&](const uint4* v, int64_t w) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < PF_FQ_GROUPS; ++j) {
+            const int64_t g = group(w, j);
+            const int e = scale_exponent<ELEM_E2M1, RULE>(quad_max_u32(amax_bits8(v[j])));
+            reinterpret_cast<uint32_t*>(q)[g] = encode8_e2m1(v[j], e);
+            s[g >> 2] = (uint8_t)(e + 127);
+        }
+    };
+    uint4 va[PF_FQ_GROUPS], vb[PF_FQ_GROUPS];
+    int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w * PF_FQ_WAVE_ELEMS >= total) return;
+    load(va, w);
+    while (true) {   // wave-uniform control flow; the prefetch past the end re-reads the last block
+        const int64_t w1 = w + nwaves;
+        load(vb, w1);
+        encode(va, w);
+        if (w1 * PF_FQ_WAVE_ELEMS >= total) break;
+        const int64_t w2 = w1 + nwaves;
+        load(va, w2);
+        encode(vb, w1);
+        if (w2 * PF_FQ_WAVE_ELEMS >= total) break;
+        w = w2;
+    }
+}
+
+// Returns false if the barrier gave up (then ctr[1] is set).
+__device__ __forceinline__ bool pf_grid_barrier(int* ctr, int n, uint8_t* smem)
+{
+    wait_vmcnt<0>();
+    __syncthreads();
+    int* ok = reinterpret_cast<int*>(smem);
+    if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        int v = 0;
+        for (int spin = 0; spin < PF_BARRIER_SPINS; ++spin) {
+            v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (v >= n) break;
+            __builtin_amdgcn_s_sleep(4);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (v < n) __hip_atomic_store(ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *ok = v >= n ? 1 : 0;
+    }
+    __syncthreads();
+    const bool r = *ok != 0;
+    __syncthreads();
+    return r;
+}
+
+// The tile body as a device function, for the persistent kernel below (the
+// non-persistent kernel includes it directly).
+template <bool OUT_F32, int BN, int EPI>
+__device__ __forceinline__ void pf_tile_dev(const PrefillArgs& p, int tile_t, uint8_t* smem)
+{
+#define PF_TILE_T tile_t
+#include "gemm_prefill_tile.inc"
+#undef PF_TILE_T
+}
+
+// p.a_q / p.a_s point at the workspace's codes and scales; p.tile_base is
+// the number of 256 x 256 tiles and p.count the number of 256 x 128 halves
+// after them (the last round's tiles when it is at most half full, as the
+// non-persistent launches split them); ctr[0] is zero at launch.
+template <bool OUT_F32, int RULE>
+__global__ __launch_bounds__(256, 1) void mx_gemm_prefill_fq_kernel(PrefillArgs p, const uint4* a_bf16, int* ctr)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    pf_quantize_a<RULE>(a_bf16, (int64_t)p.M * p.K, const_cast<uint8_t*>(p.a_q), const_cast<uint8_t*>(p.a_s));
+    if (!pf_grid_barrier(ctr, gridDim.x, smem)) return;
+    const int full = p.tile_base, items = full + p.count;
+    for (int vb = blockIdx.x; vb < items; vb += gridDim.x) {
+        __syncthreads();   // the previous tile is done with the LDS
+        if (vb < full) {
+            PrefillArgs q = p;
+            q.tile_base = 0;
+            q.count = full;
+            pf_tile_dev<OUT_F32, 256, PF_EPI_Y>(q, pf_xcd_order_of(vb, full), smem);
         } else {
-            const int s = c - 4 - L::ACOP;
-            dma_b128_at(cp.wdst, s * 1024, w_voff[s], cp.coff, cp.rw);
-        }
-    };
-
-    // LDS read addresses.  Fragment rows of one lane differ by multiples of
-    // 32, so they share the chunk swizzle (r32 >> 1) & 7: a fragment's
-    // address is a per-(half, step) base plus 4096 bytes per 32 rows, which
-    // the read takes as an immediate.  During pair pr the half-1 bases point
-    // into slot pr % 2 (read by its first sub-stage) and the half-0 bases
-    // into slot (pr + 1) % 2 (read by its second, for the next pair); after
-    // the pair both move to the other slot.
-    const int swl = pf_swz(r32);
-    uint32_t abase[2][2], wbase[2][2];   // LDS byte addresses
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int ch = ((4 * h + 2 * kk + g) ^ swl) * 16;
-            abase[h][kk] = lds0 + (wm * 128 + r32) * PF_PROWB + ch;
-            wbase[h][kk] = lds0 + L::W0 + (wn * (BN / 2) + r32) * PF_PROWB + ch;
-        }
-    const uint32_t sa_lane = lds0 + L::SC0 + (wm * 128 + r32) * PF_SWB;
-    const uint32_t sw_lane = lds0 + L::SC0 + PF_BM * PF_SWB + (wn * (BN / 2) + r32) * PF_SWB;
-    // scale-read bases of pair pr: one add per pair, kept opaque so that the
-    // per-read part stays an immediate
-    auto scale_base = [&](int pr, uint32_t& sa, uint32_t& sw) __attribute__((always_inline)) {
-        const uint32_t off = (uint32_t)(((pr / PF_WPAIRS) & (PF_NWIN - 1)) * L::WIN + (pr % PF_WPAIRS) * 8);
-        sa = sa_lane + off;
-        sw = sw_lane + off;
-        asm volatile("" : "+v"(sa), "+v"(sw));
-    };
-
-    // LDS read q (0 .. READS-1) of half h (code bases abase/wbase[h], scale
-    // bases sa/sw): code fragments (A of both steps, then W of both steps),
-    // then the scale dwords (A, then W)
-    auto read_piece = [&](int q, PfFrags<WFR>& f, int h, uint32_t sa, uint32_t sw) __attribute__((always_inline)) {
-        if (q < 8) {
-            const int kk = q >> 2, x = q & 3;
-            f.a[kk][x] = lds_read_b128(abase[h][kk] + x * 32 * PF_PROWB);
-        } else if (q < 8 + 2 * WFR) {
-            const int kk = (q - 8) / WFR, x = (q - 8) % WFR;
-            f.w[kk][x] = lds_read_b128(wbase[h][kk] + x * 32 * PF_PROWB);
-        } else if (q < 12 + 2 * WFR) {
-            const int x = q - 8 - 2 * WFR;
-            f.sa[x] = (int)lds_read_b32(sa + h * 4 + x * 32 * PF_SWB);
-        } else {
-            const int x = q - 12 - 2 * WFR;
-            f.sw[x] = (int)lds_read_b32(sw + h * 4 + x * 32 * PF_SWB);
-        }
-    };
-
-    float16_t acc[4][WFR];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < WFR; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // matrix-core instruction q of a sub-stage: step kk = q / (4 WFR), fragment (i, j)
-    auto mfma = [&](int q, const PfFrags<WFR>& f, const int* sa, const int* sw) __attribute__((always_inline)) {
-        const int kk = q / (4 * WFR), i = (q / WFR) % 4, j = q % WFR;
-        const int8_t_ b8 = int8_t_{f.w[kk][j][0], f.w[kk][j][1], f.w[kk][j][2], f.w[kk][j][3], 0, 0, 0, 0};
-        const int8_t_ a8 = int8_t_{f.a[kk][i][0], f.a[kk][i][1], f.a[kk][i][2], f.a[kk][i][3], 0, 0, 0, 0};
-        if (kk == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 0, sw[j], 0, sa[i]);
-        else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 2, sw[j], 2, sa[i]);
-    };
-
-    // One sub-stage: computed from `cur` while the next sub-stage (half nh,
-    // scale bases nsa/nsw) is read into `nxt`.  The second sub-stage of a
-    // pair first waits for all copies issued so far (the next pair) and then
-    // issues the pair's copies; the first computes their uniform part in its
-    // read-free tail.
-    auto sub = [&](const PfFrags<WFR>& cur, PfFrags<WFR>& nxt, bool second, int nh, uint32_t nsa, uint32_t nsw,
-                   int pr, PfPairCopies& cp) __attribute__((always_inline)) {
-        if (second) {
-            wait_vmcnt<0>();
-            lds_barrier();
-        }
-        // byte 2 kk + g of a scale dword is this lane's block; after the shift
-        // it sits at byte 2 kk, which the instruction's op_sel picks
-        int sa[4], sw[WFR];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sa[i] = (int)((uint32_t)cur.sa[i] >> (8 * g));
-#pragma unroll
-        for (int j = 0; j < WFR; ++j) sw[j] = (int)((uint32_t)cur.sw[j] >> (8 * g));
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < L::MFMAS; ++q) {
-            mfma(q, cur, sa, sw);
-#pragma unroll
-            for (int x = q * L::READS / L::READ_SPAN; x < (q + 1) * L::READS / L::READ_SPAN && x < L::READS; ++x) {
-                __builtin_amdgcn_sched_barrier(0);
-                read_piece(x, nxt, nh, nsa, nsw);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (!second && q == L::READ_SPAN) {
-                __builtin_amdgcn_sched_barrier(0);
-                cp = pair_copies(pr);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (second) {
-#pragma unroll
-                for (int c = q * L::COPIES / L::MFMAS; c < (q + 1) * L::COPIES / L::MFMAS; ++c) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    copy(c, cp);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // Prologue: the copy slots of virtual pairs -5 .. -1, with code copies
-    // only where they name pairs 0 and 1: windows 0 and (piece 0 of) 1, pairs
-    // 0 and 1.
-    for (int y = -5; y < 0; ++y) {
-        const PfPairCopies cp = pair_copies(y);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) copy(c, cp);
-        if (y >= -2) {
-#pragma unroll
-            for (int c = 4; c < L::COPIES; ++c) copy(c, cp);
-        }
-    }
-    // sub-stage 0 needs window 0 and pair 0; the copies of virtual pair -1
-    // (pair 1, piece 0 of window 1) may still be in flight, and the first
-    // second sub-stage waits for them
-    wait_vmcnt<L::COPIES>();
-    lds_barrier();
-    PfFrags<WFR> X, Y;
-    uint32_t sa_c, sw_c;   // scale-read bases of the current pair
-    scale_base(0, sa_c, sw_c);
-#pragma unroll
-    for (int q = 0; q < L::READS; ++q) read_piece(q, X, 0, sa_c, sw_c);   // half 0 of pair 0, slot 0
-    // the half-0 bases move to slot 1 for the second sub-stage of pair 0
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        abase[0][kk] += PF_ATILE;
-        wbase[0][kk] += L::W_TILE;
-    }
-
-    int da = PF_ATILE, dw = L::W_TILE;   // slot step of the half-1 bases (the half-0 bases step by minus it)
-    int pr = 0;
-    for (; 2 * pr + 1 < nk; ++pr) {
-        uint32_t sa_n, sw_n;
-        scale_base(pr + 1, sa_n, sw_n);
-        PfPairCopies cp;
-        sub(X, Y, false, 1, sa_c, sw_c, pr, cp);
-        sub(Y, X, true, 0, sa_n, sw_n, pr, cp);
-        sa_c = sa_n;
-        sw_c = sw_n;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            abase[1][kk] += da;
-            abase[0][kk] -= da;
-            wbase[1][kk] += dw;
-            wbase[0][kk] -= dw;
-        }
-        da = -da;
-        dw = -dw;
-    }
-    if (2 * pr < nk) {   // the half pair when K % 256 == 128
-        PfPairCopies cp;
-        sub(X, Y, false, 1, sa_c, sw_c, pr, cp);
-    }
-    wait_vmcnt<0>();   // the trailing zero-fill copies have landed
-    lds_barrier();     // every wave is done with the slots
-
-    if constexpr (EPI == PF_EPI_SWIGLU) {
-        // W's rows alternate 32 gate rows and 32 up rows, so W fragment 2jj
-        // of a wave holds the gate and fragment 2jj + 1 the up values of the
-        // same 32 h columns, in the same registers of the same lanes.  Each
-        // value is rounded to bf16 as a stored Y would be, h = SwiGLU(gate,
-        // up) is rounded to bf16, and one fragment row of h (32 columns) is
-        // one MXFP4 block: lane (r, g) holds 16 of its values, the lane
-        // (r, 1 - g) the other 16.  h is [M, N/2]: codes [M, N/4] bytes,
-        // scales [M, N/64] bytes.
-        const int I = p.N / 2, hrow_b = I / 2, hblocks = I / 32;
-        const int hb0 = (n0 + wn * (BN / 2)) / 64;    // first h block of this wave
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + wm * 128 + i * 32 + r32;
-#pragma unroll
-            for (int jj = 0; jj < WFR / 2; ++jj) {
-                uint32_t hv[8];
-                uint32_t amax = 0;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const uint32_t gb = bf16x2_rne(acc[i][2 * jj][2 * t], acc[i][2 * jj][2 * t + 1]);
-                    const uint32_t ub = bf16x2_rne(acc[i][2 * jj + 1][2 * t], acc[i][2 * jj + 1][2 * t + 1]);
-                    const float h0 = swiglu_f32(__uint_as_float(gb << 16), __uint_as_float(ub << 16));
-                    const float h1 = swiglu_f32(__uint_as_float(gb & 0xFFFF0000u), __uint_as_float(ub & 0xFFFF0000u));
-                    hv[t] = bf16x2_rne(h0, h1);
-                    const uint32_t lo = hv[t] & 0x7FFFu, hi = (hv[t] >> 16) & 0x7FFFu;
-                    amax = amax > lo ? amax : lo;
-                    amax = amax > hi ? amax : hi;
-                }
-                const auto am = __builtin_amdgcn_permlane32_swap(amax, amax, false, false);
-                amax = am[0] > am[1] ? am[0] : am[1];
-                const int e = scale_exponent<ELEM_E2M1, RULE_CEIL>(amax);
-                // codes of register groups 0,1 and 2,3: group q covers columns
-                // 8q + 4g .. +3 of the block, 2 bytes
-                const uint32_t c01 = encode8_e2m1(make_uint4(hv[0], hv[1], hv[2], hv[3]), e);
-                const uint32_t c23 = encode8_e2m1(make_uint4(hv[4], hv[5], hv[6], hv[7]), e);
-                // lane g = 0 receives groups 0, 1 of both lane halves (bytes
-                // 0..7 of the block's 16), lane g = 1 groups 2, 3 (bytes 8..15)
-                const auto sw = __builtin_amdgcn_permlane32_swap(c01, c23, false, false);
-                const uint32_t d0 = (sw[0] & 0xFFFFu) | (sw[1] << 16);
-                const uint32_t d1 = (sw[0] >> 16) | (sw[1] & 0xFFFF0000u);
-                const int hb = hb0 + jj;
-                if (m < p.M && hb < hblocks) {
-                    uint8_t* dst = p.h_q + (size_t)m * hrow_b + hb * 16 + g * 8;
-                    *reinterpret_cast<uint2*>(dst) = make_uint2(d0, d1);
-                    if (g == 0) p.h_s[(size_t)m * hblocks + hb] = (uint8_t)(e + 127);
-                }
-            }
-        }
-        return;
-    }
-
-    // Epilogue, one 32-row band (fragment row i) at a time through two
-    // band buffers in this wave's private LDS region: band i + 1 is written
-    // row-major while band i is read back as whole row segments and stored
-    // with 16-byte stores.  A wave's LDS operations execute in order, so the
-    // reads see the writes issued before them and the writes of band i + 2
-    // come after the reads of band i in the same buffer.
-    constexpr int ESZ = OUT_F32 ? 4 : 2;
-    constexpr int WCOLS = BN / 2;                        // output columns of a wave
-    constexpr int ROWB = WCOLS * ESZ + 16;               // padded LDS row
-    constexpr int BAND = 32 * ROWB;
-    static_assert(8 * BAND <= L::LDS, "epilogue buffers");
-    uint8_t* region = smem + wave * (2 * BAND);
-    constexpr int LPR = WCOLS * ESZ / 16;                // lanes per 16-byte-chunked row
-    constexpr int RPI = 64 / LPR;                        // rows per read instruction
-    const int lrow = lane / LPR, c16 = lane % LPR;
-    // full tiles with rows of whole 16-byte chunks store without checks, at
-    // a uniform band base plus a 32-bit per-lane offset
-    const bool full = m0 + PF_BM <= p.M && n0 + BN <= p.N && (p.N % (16 / ESZ)) == 0;
-    uint8_t* ywave = reinterpret_cast<uint8_t*>(p.y) + ((size_t)(m0 + wm * 128) * p.N + n0 + wn * WCOLS) * ESZ;
-    const uint32_t lane_off = (uint32_t)(lrow * p.N * ESZ + c16 * 16);
-
-    auto write_band = [&](int i) __attribute__((always_inline)) {
-        uint8_t* buf = region + (i & 1) * BAND;
-#pragma unroll
-        for (int j = 0; j < WFR; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (OUT_F32) {
-                    uint8_t* dst = buf + r32 * ROWB + (j * 32 + q * 8 + g * 4) * ESZ;
-                    *reinterpret_cast<float4_t*>(dst) =
-                        float4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                } else if (q % 2 == 0) {
-                    // bf16: register groups q and q + 1 hold columns 8q + 4g .. +3 and
-                    // 8(q+1) + 4g .. +3.  Swapping the upper lane half of group q
-                    // with the lower half of group q + 1 leaves lane (r, g) with the
-                    // 8 consecutive columns 8(q + g) .. +7 of row r: one 16-byte
-                    // write, which the padded rows keep free of bank conflicts.
-                    const uint32_t a0 = bf16x2_rne(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-                    const uint32_t a1 = bf16x2_rne(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                    const uint32_t b0 = bf16x2_rne(acc[i][j][4 * q + 4], acc[i][j][4 * q + 5]);
-                    const uint32_t b1 = bf16x2_rne(acc[i][j][4 * q + 6], acc[i][j][4 * q + 7]);
-                    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-                    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-                    uint8_t* dst = buf + r32 * ROWB + (j * 32 + (q + g) * 8) * ESZ;
-                    *reinterpret_cast<int4_t*>(dst) = int4_t{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
-                }
-            }
-    };
-    write_band(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (i + 1 < 4) write_band(i + 1);
-        const uint8_t* buf = region + (i & 1) * BAND;
-        int4_t v[32 / RPI];
-#pragma unroll
-        for (int t = 0; t < 32 / RPI; ++t) v[t] = *reinterpret_cast<const int4_t*>(buf + (t * RPI + lrow) * ROWB + c16 * 16);
-        if (full) {
-#pragma unroll
-            for (int t = 0; t < 32 / RPI; ++t) {
-                uint8_t* yb = ywave + (size_t)(i * 32 + t * RPI) * p.N * ESZ;
-                __builtin_nontemporal_store(v[t], reinterpret_cast<int4_t*>(yb + lane_off));
-            }
-            continue;
-        }
-#pragma unroll
-        for (int t = 0; t < 32 / RPI; ++t) {
-            const int row = t * RPI + lrow;
-            const int m = m0 + wm * 128 + i * 32 + row;
-            const int n = n0 + wn * WCOLS + c16 * (16 / ESZ);
-            if (m >= p.M) continue;
-            uint8_t* yrow = reinterpret_cast<uint8_t*>(p.y) + ((size_t)m * p.N) * ESZ;
-            if ((p.N % (16 / ESZ)) == 0 && n + 16 / ESZ <= p.N) {
-                __builtin_nontemporal_store(v[t], reinterpret_cast<int4_t*>(yrow + (size_t)n * ESZ));
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16 / ESZ; ++e) {
-                    const int wi = OUT_F32 ? e : e / 2;
-                    const uint32_t word = (uint32_t)v[t][wi];
-                    if (n + e < p.N) {
-                        if (OUT_F32) reinterpret_cast<uint32_t*>(yrow)[n + e] = word;
-                        else reinterpret_cast<uint16_t*>(yrow)[n + e] = (uint16_t)(word >> (16 * (e % 2)));
-                    }
-                }
-            }
+            pf_tile_dev<OUT_F32, 128, PF_EPI_Y>(p, pf_xcd_order_of(vb - full, p.count), smem);
         }
     }
 }
@@ -643,9 +374,100 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
     return hipSuccess;
 }
 
+// Clears the fused launch's barrier counter and error word.
+__global__ void pf_zero2_kernel(int* p)
+{
+    if (threadIdx.x < 2) p[threadIdx.x] = 0;
+}
+
+// Workspace layout of the quantize-once fused launch: A codes [m, k/2], E8M0
+// scales [m, k/32] (mx_quantize_act's layout), then two ints (barrier count,
+// error word) at a 256-byte boundary.
+static size_t prefill_fq_counter_offset(int64_t m, int64_t k)
+{
+    return ((size_t)m * (k / 2) + (size_t)m * (k / 32) + 255) & ~(size_t)255;
+}
+
+template <bool OUT_F32, int RULE>
+static hipError_t launch_prefill_fq(PrefillArgs a, const void* a_bf16, int* ctr, hipStream_t stream)
+{
+    auto kern = mx_gemm_prefill_fq_kernel<OUT_F32, RULE>;
+    static int per_cu = -1;
+    if (per_cu < 0) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           PfLayout<256>::LDS);
+        if (e != hipSuccess) return e;
+        int n = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)kern, 256, PfLayout<256>::LDS);
+        if (e != hipSuccess) return e;
+        per_cu = n;
+    }
+    const int cus = prefill_cu_count();
+    const int items = a.tile_base + a.count;
+    int grid = per_cu * cus;
+    if (grid > items) grid = items;
+    grid -= grid % NUM_XCD;     // keep workgroup id % 8 == XCD across the tile loop
+    if (grid < NUM_XCD) return hipErrorNotSupported;
+    hipLaunchKernelGGL(pf_zero2_kernel, dim3(1), dim3(64), 0, stream, ctr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const uint4* x = static_cast<const uint4*>(a_bf16);
+    void* args[] = {&a, &x, &ctr};
+    return hipLaunchCooperativeKernel((const void*)kern, dim3(grid), dim3(256), args, PfLayout<256>::LDS, stream);
+}
+
+static bool prefill_coop_supported()
+{
+    static int cached[64];
+    static bool init[64] = {false};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    if (!init[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) v = 0;
+        cached[dev] = v;
+        init[dev] = true;
+    }
+    return cached[dev] != 0;
+}
+
 } // namespace mxl
 
 using namespace mxl;
+
+// Workspace bytes of the quantize-once fused launch (mxl_prefill_ok shapes).
+extern "C" size_t mxl_prefill_fq_workspace(int64_t m, int64_t k)
+{
+    return prefill_fq_counter_offset(m, k) + 256;
+}
+
+// The quantize-once fused launch: A bf16 [m, k] quantized with rule a_rule
+// (MXFP4) into `work` (at least mxl_prefill_fq_workspace bytes, 16-byte
+// aligned), then Y = A W^T.  hipErrorNotSupported when the device cannot
+// launch cooperatively (the caller then uses the in-tile prologue).
+extern "C" hipError_t mxl_launch_mx_prefill_fq(int a_rule, const void* a_bf16, const void* wq, const void* ws,
+                                               int64_t m, int64_t n, int64_t k, void* y, int out_f32, void* work,
+                                               size_t work_bytes, hipStream_t stream)
+{
+    if (!prefill_coop_supported()) return hipErrorNotSupported;
+    if (!work || work_bytes < mxl_prefill_fq_workspace(m, k)) return hipErrorInvalidValue;
+    uint8_t* w8 = static_cast<uint8_t*>(work);
+    PrefillArgs a{w8, w8 + (size_t)m * (k / 2), static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
+                  y, nullptr, nullptr, (int)m, (int)n, (int)k, 0, 0};
+    const int T = (int)(((m + PF_BM - 1) / PF_BM) * ((n + 255) / 256));
+    const int tail = prefill_tail_tiles(T, prefill_cu_count());
+    a.tile_base = T - tail;   // 256 x 256 tiles
+    a.count = 2 * tail;       // then 256 x 128 halves of the tail tiles
+    int* ctr = reinterpret_cast<int*>(w8 + prefill_fq_counter_offset(m, k));
+    if (a_rule == RULE_CEIL)
+        return out_f32 ? launch_prefill_fq<true, RULE_CEIL>(a, a_bf16, ctr, stream)
+                       : launch_prefill_fq<false, RULE_CEIL>(a, a_bf16, ctr, stream);
+    if (a_rule == RULE_FLOOR)
+        return out_f32 ? launch_prefill_fq<true, RULE_FLOOR>(a, a_bf16, ctr, stream)
+                       : launch_prefill_fq<false, RULE_FLOOR>(a, a_bf16, ctr, stream);
+    return out_f32 ? launch_prefill_fq<true, RULE_EVEN>(a, a_bf16, ctr, stream)
+                   : launch_prefill_fq<false, RULE_EVEN>(a, a_bf16, ctr, stream);
+}
 
 // Shapes this kernel accepts: K % 128 == 0 and every operand below 2 GiB
 // (32-bit buffer offsets).  The caller checks them (mxl_prefill_ok).

@@ -92,7 +92,7 @@ typedef enum {
                                  to the workspace (see mx_gemm_fused) */
 
 /* ABI version of this header (bumped on any signature change). */
-#define MXLINEAR_ABI_VERSION 6
+#define MXLINEAR_ABI_VERSION 7
 int mx_abi_version(void);
 
 /* Static text for a status code; never NULL. */
@@ -155,18 +155,33 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
 /*
  * mx_gemm_fused -- mx_gemm with the activation quantization computed inside
  * the GEMM from bf16 A ([m, k]), with scale rule a_rule.  The result equals
- * mx_quantize_act followed by an unsplit mx_gemm.  workspace/ws_bytes are
- * unused and may be NULL/0, unless flags has MX_DEBUG_DUMP_AQ: then the
- * quantization the prologue computed is also written to the workspace, A
- * codes [m, k * bits / 8] (bits 4 or 8) followed by E8M0 scales [m, k/32],
- * the layout of mx_quantize_act, so it can be checked bit for bit.  The
- * workspace must then hold both (MX_ERR_WORKSPACE otherwise) and be 16-byte
- * aligned.
+ * mx_quantize_act followed by an unsplit mx_gemm.
+ * Workspace (optional, 16-byte aligned):
+ *  - without MX_DEBUG_DUMP_AQ, large MXFP4 shapes (m, n >= 1024, k % 128 ==
+ *    0) given at least mx_gemm_fused_workspace_size bytes run as one
+ *    cooperative launch that quantizes A once into the workspace (codes
+ *    [m, k/2], then scales [m, k/32], mx_quantize_act's layout), meets at a
+ *    grid barrier and computes the GEMM from it; the workspace then holds
+ *    A's codes and scales.  Other shapes, a smaller workspace or a device
+ *    without cooperative launch quantize inside each tile instead.  Calls
+ *    sharing a workspace must not overlap.
+ *  - with MX_DEBUG_DUMP_AQ the quantization the in-tile prologue computed is
+ *    also written to the workspace, A codes [m, k * bits / 8] (bits 4 or 8)
+ *    followed by E8M0 scales [m, k/32], so it can be checked bit for bit.
+ *    The workspace must then hold both (MX_ERR_WORKSPACE otherwise).
  */
 mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf16,
                         mx_format w_fmt, const void* w_q, const void* w_s, int64_t m, int64_t n,
                         int64_t k, void* y, unsigned flags, void* workspace, size_t ws_bytes,
                         mx_stream_t stream);
+
+/*
+ * mx_gemm_fused_workspace_size -- bytes of workspace mx_gemm_fused can use
+ * on this shape and flags (0: none; always 0 with MX_DEBUG_DUMP_AQ, whose
+ * workspace is the dump).  Same argument checks as mx_gemm_fused.
+ */
+mx_status mx_gemm_fused_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k,
+                                       unsigned flags, size_t* bytes);
 
 /*
  * nv_gemm -- NVFP4 x NVFP4 GEMM.  a_q [m, k/2] E2M1, a_s [m, k/16] E4M3,

@@ -35,7 +35,7 @@ def test_header_declares_expected_entry_points():
     for n in ("mx_pack_weights", "mx_quantize_act", "mx_gemm", "mx_gemm_fused", "nv_gemm",
               "mx_gemm_w4a16", "mx_gemm_w4a16_plan", "mx_fake_quant",
               "mx_gemm_swiglu_quant", "mx_gemm_swiglu_quant_plan", "mx_swiglu_quant",
-              "mx_gemm_workspace_size", "mx_gemm_w4a16_workspace_size",
+              "mx_gemm_workspace_size", "mx_gemm_w4a16_workspace_size", "mx_gemm_fused_workspace_size",
               "mx_tensor_amax", "mx_nv_global_scale", "mx_gemm_plan", "mx_status_string",
               "mx_abi_version"):
         assert n in names
@@ -186,6 +186,16 @@ def test_workspace_sizes():
     assert mxl.mx_gemm_workspace_size("nvfp4", "nvfp4", 96, 160, 4096) > 0
     # tiles that fill the GPU, the decode kernel, the prefill kernel: none
     assert mxl.mx_gemm_workspace_size("mxfp4", "mxfp4", 8192, 17408, 5120) == 0
+    # fused, quantize-once: A codes and scales of the 8192 x 5120 activations,
+    # then a 256-byte counter block at a 256-byte boundary
+    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 8192, 17408, 5120) == 8192 * 2560 + 8192 * 160 + 256
+    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1100, 1090, 1152) == \
+        ((1100 * 576 + 1100 * 36 + 255) // 256) * 256 + 256
+    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 512, 2048, 5120) == 0     # not a large shape
+    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 8192, 17408, 5120) == 0
+    b2 = ctypes.c_size_t(7)
+    assert L.mx_gemm_fused_workspace_size(0, 0, 8192, 17408, 5120, 0x4, ctypes.byref(b2)) == OK and b2.value == 0
+    assert L.mx_gemm_fused_workspace_size(0, 2, 64, 64, 64, 0, ctypes.byref(b2)) == INVALID
     assert mxl.mx_gemm_workspace_size("mxfp4", "mxfp4", 8, 17408, 5120) == 0
     assert mxl.mx_gemm_workspace_size("mxfp8", "mxfp8", 4096, 6144, 5120) == 0
     # short K: no split

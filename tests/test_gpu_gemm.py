@@ -256,6 +256,45 @@ def test_prefill_kernel_edges(what, m, k, n):
     assert torch.equal(yf.to(torch.bfloat16), y)
 
 
+# The quantize-once fused launch (large MXFP4 shapes with a workspace): one
+# cooperative launch quantizes all of A into the workspace, meets at a grid
+# barrier and runs the prefill tiles from it.  The workspace must then hold
+# exactly mx_quantize_act's codes and scales (which also shows that this path
+# ran), the barrier's error word must be clear, and Y must equal both the
+# standalone pair and the in-tile prologue bit for bit, for every rule.  The
+# first shape has fewer tiles than a grid of 8 workgroups per XCD round (24
+# workgroups over 25 tiles), the second several tiles per workgroup.
+FQ_SHAPES = [(1100, 1152, 1090), (1300, 2560, 33000)]
+
+
+@pytest.mark.parametrize("m,k,n", FQ_SHAPES)
+def test_fused_quantize_once(m, k, n):
+    wsz = mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", m, n, k)
+    say(f"fused quantize-once m={m} k={k} n={n}: workspace {wsz} B")
+    assert wsz > 0
+    a_bits = W.activations_entry_outliers(m, k)
+    w_bits = W.normal_bf16(n, k, 0.02, 1)
+    a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
+    wq, wsc = mxl.mx_pack_weights(w, fmt="mxfp4", rule="even")
+    qb, sb = m * k // 2, m * k // 32
+    cnt = (qb + sb + 255) // 256 * 256
+    for rule in ("ceil", "floor", "even"):
+        for out_f32 in (False, True):
+            ws = torch.full((wsz,), 0xA5, dtype=torch.uint8, device="cuda")
+            y = mxl.mx_gemm_fused(a, wq, wsc, "mxfp4", rule, "mxfp4", out_f32=out_f32, workspace=ws)
+            aq, as_ = mxl.mx_quantize_act(a, "mxfp4", rule)
+            y_ref = mxl.mx_gemm(aq, as_, wq, wsc, k, out_f32=out_f32, split_k=False)
+            y_tile = mxl.mx_gemm_fused(a, wq, wsc, "mxfp4", rule, "mxfp4", out_f32=out_f32, quantize_once=False)
+            torch.cuda.synchronize()
+            assert torch.equal(ws[:qb].view(m, k // 2), aq), f"{rule}: workspace codes"
+            assert torch.equal(ws[qb:qb + sb].view(m, k // 32), as_), f"{rule}: workspace scales"
+            assert int(ws[cnt + 4:cnt + 8].view(torch.int32).item()) == 0, "grid barrier error word"
+            assert torch.equal(y, y_ref), f"{rule} f32={out_f32}: quantize-once != standalone"
+            assert torch.equal(y, y_tile), f"{rule} f32={out_f32}: quantize-once != in-tile prologue"
+    rq, rs = oracle.mx_quantize("e2m1", "even", a_bits)
+    assert np.array_equal(host(ws[:qb].view(m, k // 2)), rq) and np.array_equal(host(ws[qb:qb + sb].view(m, k // 32)), rs)
+
+
 def test_deterministic():
     a_bits = W.activations_entry_outliers(300, 1024)
     w_bits = W.normal_bf16(700, 1024, 0.02, 1)
