@@ -1024,8 +1024,7 @@ extern "C" hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const voi
         if (need > 0 && work_bytes >= need) {
             const hipError_t e = mxl_launch_mx_prefill_fq(a_rule, a_bf16, wq, ws, m, n, k, y, out_f32, work,
                                                           work_bytes, stream);
-            if (e == hipSuccess) return e;
-            (void)hipGetLastError();   // no cooperative launch here: the in-tile prologue below
+            return e;
         }
     }
     GemmArgs a{static_cast<const uint8_t*>(a_bf16), nullptr, static_cast<const uint8_t*>(wq),

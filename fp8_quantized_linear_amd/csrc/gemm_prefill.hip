@@ -184,143 +184,127 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
 // Fused activation quantization for the large shapes, quantizing A once.
 // A prologue inside each tile (mx_gemm_kernel<FUSED>) redoes the quantization
 // of its A block for every tile column: 68 times for the 8192 x 5120 x 17408
-// projection.  Here one cooperative launch of resident workgroups (one per CU)
-// first quantizes all of A from bf16 into a workspace, exactly as
-// mx_quantize_act does (the same device functions, the same layout), meets at
-// a grid barrier, and then walks the output tiles of the prefill GEMM with
-// the same tile body (256 x 256 tiles in the same XCD-aware order, then the
-// 256 x 128 halves of a last round at most half full, as the non-persistent
-// launches do), reading the codes from the workspace.  The result is bitwise that of
-// mx_quantize_act followed by mx_gemm.
+// projection.  Here the workgroups quantize each 256-row block of A once,
+// into a workspace, exactly as mx_quantize_act does (the same device
+// functions, the same layout), and the tiles read the codes from there.
 //
-// Grid barrier: every wave waits for its stores (acknowledged by the L2);
-// thread 0 of each workgroup then releases (one write-back of its XCD's L2)
-// and counts itself, polls the count with device-scope atomic loads, and
-// acquires (one L2 invalidation) once all have arrived.  The launch is
-// cooperative, so every workgroup is resident and the count completes; the
-// poll still gives up after about half a second, sets an error word and ends
-// the workgroup, so that no mistake can hang the GPU.
+// Before its tile, a workgroup claims 16-row chunks of A (of any block) from
+// a pool counter and quantizes them until the pool is empty, then waits until
+// its own block's done counter shows every chunk of the block.  It only ever
+// waits for chunks that running workgroups have claimed and finish without
+// waiting, so the scheme needs no co-residency and runs as ordinary launches
+// (the same two as mx_gemm: 256 x 256 tiles, then the 256 x 128 halves of a
+// last round at most half full).  The first round of workgroups quantizes
+// all of A together; later ones find the pool empty and their block done.
+//
+// Visibility: a chunk's writer waits for its stores (acknowledged by the L2)
+// and, from one thread, releases (one write-back of its XCD's L2) before
+// counting the chunk done.  A reader polls the done counter with device-scope
+// atomic loads and needs no invalidation: the codes are read only after their
+// block is done, no L2 holds lines of the block from before (the launch
+// starts with the caches' acquire, the region is written only here, and
+// blocks start on cache-line boundaries: 256 rows of k/2 code bytes and of
+// k/32 scale bytes, k % 128 == 0).  Every poll is bounded (about 0.5 s, then an
+// error word and the tile is skipped), so that no mistake can hang the GPU.
 // ---------------------------------------------------------------------------
-constexpr int PF_FQ_GROUPS = 16;                 // 8-element groups per lane per step (all loaded first)
-constexpr int PF_FQ_WAVE_ELEMS = PF_FQ_GROUPS * 64 * 8;
-constexpr int PF_BARRIER_SPINS = 1 << 21;       // x s_sleep(4): about 0.5 s
+constexpr int PF_FQ_CHUNK_ROWS = 16;
+constexpr int PF_FQ_SPINS = 1 << 21;           // x s_sleep(4): about 0.5 s
 
-// Workgroup id -> position in the XCD-aware order of `count` tiles (the order
-// pf_xcd_order gives a non-persistent launch; id % 8 is still the XCD as long
-// as the grid is a multiple of 8).
-__device__ __forceinline__ int pf_xcd_order_of(int id, int count)
-{
-    const int xcd = id % NUM_XCD, j = id / NUM_XCD;
-    const int q = count / NUM_XCD, r = count % NUM_XCD;
-    return xcd * q + (xcd < r ? xcd : r) + j;
-}
-
-// mx_quantize_act (MXFP4, rule RULE) of `total` bf16 elements (a multiple of
-// 32), spread over the grid's waves: the per-group work of
-// mx_quantize_kernel (lane quads hold the blocks of 32).  With one workgroup
-// per CU only 4 waves per CU stream A, so each wave keeps the next step's 16
-// groups per lane in flight while it encodes the current ones (two register
-// sets, alternating).  Everything is branch-free, so that the compiler's
-// load counting lets the prefetch stay in flight: a quad past the end
-// re-reads the last block and stores the same codes and scale again, and
-// every lane of a quad stores the scale byte.
+// mx_quantize_act (MXFP4, rule RULE) of rows [r0, r1) of A (bf16, k per row):
+// the per-group work of mx_quantize_kernel; consecutive threads take
+// consecutive 8-element groups, so lane quads hold the blocks of 32.  Each
+// thread loads 16 groups before it encodes any (one workgroup per CU streams
+// the chunk; 32 measured the same), and a lane quad is always wholly inside
+// or wholly past r1 (k / 8 is a multiple of 16 groups).
 template <int RULE>
-__device__ __forceinline__ void pf_quantize_a(const uint4* __restrict__ x, int64_t total, uint8_t* __restrict__ q,
-                                              uint8_t* __restrict__ s)
+__device__ __forceinline__ void pf_quantize_rows(const uint4* __restrict__ x, int k, int r0, int r1,
+                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ s)
 {
+    constexpr int G = 16;
     const int lane = threadIdx.x & 63;
-    const int64_t nwaves = (int64_t)gridDim.x * 4;
-    const int64_t last_block = total / 32 - 1;
-    auto group = [&](int64_t w, int j) __attribute__((always_inline)) {
-        const int64_t g = w * (PF_FQ_WAVE_ELEMS / 8) + 64 * j + lane;
-        return (g >> 2) <= last_block ? g : 4 * last_block + (lane & 3);
-    };
-    auto load = [&](uint4* v, int64_t w) __attribute__((always_inline)) {
+    const int64_t g_end = (int64_t)r1 * (k / 8);
+    for (int64_t g0 = (int64_t)r0 * (k / 8) + threadIdx.x; g0 < g_end; g0 += G * 256) {
+        uint4 v[G];
 #pragma unroll
-        for (int j = 0; j < PF_FQ_GROUPS; ++j) v[j] = x[group(w, j)];
-    };
-    auto encode = [&](const uint4* v, int64_t w) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < PF_FQ_GROUPS; ++j) {
-            const int64_t g = group(w, j);
-            const int e = scale_exponent<ELEM_E2M1, RULE>(quad_max_u32(amax_bits8(v[j])));
-            reinterpret_cast<uint32_t*>(q)[g] = encode8_e2m1(v[j], e);
-            s[g >> 2] = (uint8_t)(e + 127);
+        for (int j = 0; j < G; ++j) {
+            const int64_t g = g0 + 256 * j;
+            v[j] = x[g < g_end ? g : g0];
         }
-    };
-    uint4 va[PF_FQ_GROUPS], vb[PF_FQ_GROUPS];
-    int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (w * PF_FQ_WAVE_ELEMS >= total) return;
-    load(va, w);
-    while (true) {   // wave-uniform control flow; the prefetch past the end re-reads the last block
-        const int64_t w1 = w + nwaves;
-        load(vb, w1);
-        encode(va, w);
-        if (w1 * PF_FQ_WAVE_ELEMS >= total) break;
-        const int64_t w2 = w1 + nwaves;
-        load(va, w2);
-        encode(vb, w1);
-        if (w2 * PF_FQ_WAVE_ELEMS >= total) break;
-        w = w2;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int64_t g = g0 + 256 * j;
+            const int e = scale_exponent<ELEM_E2M1, RULE>(quad_max_u32(amax_bits8(v[j])));
+            const uint32_t c = encode8_e2m1(v[j], e);
+            if (g < g_end) {
+                reinterpret_cast<uint32_t*>(q)[g] = c;
+                if ((lane & 3) == 0) s[g >> 2] = (uint8_t)(e + 127);
+            }
+        }
     }
 }
 
-// Returns false if the barrier gave up (then ctr[1] is set).
-__device__ __forceinline__ bool pf_grid_barrier(int* ctr, int n, uint8_t* smem)
+// Makes sure A block tm (rows [256 tm, 256 tm + 256) clipped to M) is
+// quantized into p.a_q / p.a_s.  Before that, the workgroup takes chunks from
+// the pool of all blocks' chunks (chunk c: block c / 16, rows 16 (c % 16) ..
+// of it) until the pool is empty, so the first round of workgroups quantizes
+// all of A together.  state: the pool counter, done counters [nb] (16 chunks
+// each, empty chunks past M included), the error word.  Returns false if the
+// poll gave up.
+template <int RULE>
+__device__ __forceinline__ bool pf_ensure_block(const PrefillArgs& p, const uint4* a_bf16, int* state, int nb,
+                                                int tm, uint8_t* smem)
 {
-    wait_vmcnt<0>();
+    constexpr int CPB = PF_BM / PF_FQ_CHUNK_ROWS;    // chunks per block
+    int* pool = state;
+    int* done = state + 1;
+    int* word = reinterpret_cast<int*>(smem);
+    while (true) {
+        __syncthreads();
+        if (threadIdx.x == 0) *word = __hip_atomic_fetch_add(pool, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int c = *word;
+        if (c >= nb * CPB) break;
+        const int b = c / CPB, r0 = b * PF_BM + (c % CPB) * PF_FQ_CHUNK_ROWS;
+        const int r1 = min(r0 + PF_FQ_CHUNK_ROWS, p.M);
+        if (r0 < r1)
+            pf_quantize_rows<RULE>(a_bf16, p.K, r0, r1, const_cast<uint8_t*>(p.a_q), const_cast<uint8_t*>(p.a_s));
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_fetch_add(done + b, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
-    int* ok = reinterpret_cast<int*>(smem);
     if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         int v = 0;
-        for (int spin = 0; spin < PF_BARRIER_SPINS; ++spin) {
-            v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (v >= n) break;
+        for (int spin = 0; spin < PF_FQ_SPINS; ++spin) {
+            v = __hip_atomic_load(done + tm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (v >= CPB) break;
             __builtin_amdgcn_s_sleep(4);
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        if (v < n) __hip_atomic_store(ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *ok = v >= n ? 1 : 0;
+        if (v < CPB) __hip_atomic_store(state + 1 + nb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *word = v >= CPB ? 1 : 0;
     }
     __syncthreads();
-    const bool r = *ok != 0;
-    __syncthreads();
-    return r;
+    const bool ok = *word != 0;
+    __syncthreads();   // the tile reuses this LDS word
+    return ok;
 }
 
-// The tile body as a device function, for the persistent kernel below (the
-// non-persistent kernel includes it directly).
-template <bool OUT_F32, int BN, int EPI>
-__device__ __forceinline__ void pf_tile_dev(const PrefillArgs& p, int tile_t, uint8_t* smem)
+// The prefill kernel with the quantize-once prologue: p.a_q / p.a_s point at
+// the workspace's codes and scales, a_bf16 is A; state as above, zeroed
+// before the first of the call's launches.
+template <bool OUT_F32, int BN, int RULE>
+__global__ __launch_bounds__(256, 1) void mx_gemm_prefill_fq_kernel(PrefillArgs p, const uint4* a_bf16, int* state,
+                                                                    int nb)
 {
+    constexpr int EPI = PF_EPI_Y;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tile_t = pf_xcd_order(p.count);
+    int tm, tn;
+    pf_tile(p.tile_base + (BN == 256 ? tile_t : tile_t / 2), p.M, p.N, tm, tn);
+    if (!pf_ensure_block<RULE>(p, a_bf16, state, nb, tm, smem)) return;
 #define PF_TILE_T tile_t
 #include "gemm_prefill_tile.inc"
 #undef PF_TILE_T
-}
-
-// p.a_q / p.a_s point at the workspace's codes and scales; p.tile_base is
-// the number of 256 x 256 tiles and p.count the number of 256 x 128 halves
-// after them (the last round's tiles when it is at most half full, as the
-// non-persistent launches split them); ctr[0] is zero at launch.
-template <bool OUT_F32, int RULE>
-__global__ __launch_bounds__(256, 1) void mx_gemm_prefill_fq_kernel(PrefillArgs p, const uint4* a_bf16, int* ctr)
-{
-    extern __shared__ __align__(16) uint8_t smem[];
-    pf_quantize_a<RULE>(a_bf16, (int64_t)p.M * p.K, const_cast<uint8_t*>(p.a_q), const_cast<uint8_t*>(p.a_s));
-    if (!pf_grid_barrier(ctr, gridDim.x, smem)) return;
-    const int full = p.tile_base, items = full + p.count;
-    for (int vb = blockIdx.x; vb < items; vb += gridDim.x) {
-        __syncthreads();   // the previous tile is done with the LDS
-        if (vb < full) {
-            PrefillArgs q = p;
-            q.tile_base = 0;
-            q.count = full;
-            pf_tile_dev<OUT_F32, 256, PF_EPI_Y>(q, pf_xcd_order_of(vb, full), smem);
-        } else {
-            pf_tile_dev<OUT_F32, 128, PF_EPI_Y>(p, pf_xcd_order_of(vb - full, p.count), smem);
-        }
-    }
 }
 
 template <bool OUT_F32, int BN, int EPI>
@@ -374,99 +358,89 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
     return hipSuccess;
 }
 
-// Clears the fused launch's barrier counter and error word.
-__global__ void pf_zero2_kernel(int* p)
+// Clears the quantize-once state (pool and done counters, error word).
+__global__ void pf_zero_kernel(int* p, int n)
 {
-    if (threadIdx.x < 2) p[threadIdx.x] = 0;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
 }
 
-// Workspace layout of the quantize-once fused launch: A codes [m, k/2], E8M0
-// scales [m, k/32] (mx_quantize_act's layout), then two ints (barrier count,
-// error word) at a 256-byte boundary.
-static size_t prefill_fq_counter_offset(int64_t m, int64_t k)
+// Workspace layout of the quantize-once launches: A codes [m, k/2], E8M0
+// scales [m, k/32] (mx_quantize_act's layout), then at a 256-byte boundary
+// the state: the chunk pool counter, a done counter per 256-row block, and an
+// error word.
+static size_t prefill_fq_state_offset(int64_t m, int64_t k)
 {
     return ((size_t)m * (k / 2) + (size_t)m * (k / 32) + 255) & ~(size_t)255;
 }
 
-template <bool OUT_F32, int RULE>
-static hipError_t launch_prefill_fq(PrefillArgs a, const void* a_bf16, int* ctr, hipStream_t stream)
+template <bool OUT_F32, int BN, int RULE>
+static hipError_t launch_prefill_fq_part(PrefillArgs a, int tile_base, int count, const uint4* x, int* state,
+                                         int nb, hipStream_t stream)
 {
-    auto kern = mx_gemm_prefill_fq_kernel<OUT_F32, RULE>;
-    static int per_cu = -1;
-    if (per_cu < 0) {
+    auto kern = mx_gemm_prefill_fq_kernel<OUT_F32, BN, RULE>;
+    static bool attr_set = false;
+    if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           PfLayout<256>::LDS);
+                                           PfLayout<BN>::LDS);
         if (e != hipSuccess) return e;
-        int n = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)kern, 256, PfLayout<256>::LDS);
-        if (e != hipSuccess) return e;
-        per_cu = n;
+        attr_set = true;
     }
-    const int cus = prefill_cu_count();
-    const int items = a.tile_base + a.count;
-    int grid = per_cu * cus;
-    if (grid > items) grid = items;
-    grid -= grid % NUM_XCD;     // keep workgroup id % 8 == XCD across the tile loop
-    if (grid < NUM_XCD) return hipErrorNotSupported;
-    hipLaunchKernelGGL(pf_zero2_kernel, dim3(1), dim3(64), 0, stream, ctr);
+    a.tile_base = tile_base;
+    a.count = count;
+    hipLaunchKernelGGL(kern, dim3(count), dim3(256), PfLayout<BN>::LDS, stream, a, x, state, nb);
+    return hipGetLastError();
+}
+
+template <bool OUT_F32, int RULE>
+static hipError_t launch_prefill_fq(PrefillArgs a, const void* a_bf16, int* state, hipStream_t stream)
+{
+    const int nb = (a.M + PF_BM - 1) / PF_BM;
+    hipLaunchKernelGGL(pf_zero_kernel, dim3((nb + 2 + 255) / 256), dim3(256), 0, stream, state, nb + 2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const uint4* x = static_cast<const uint4*>(a_bf16);
-    void* args[] = {&a, &x, &ctr};
-    return hipLaunchCooperativeKernel((const void*)kern, dim3(grid), dim3(256), args, PfLayout<256>::LDS, stream);
-}
-
-static bool prefill_coop_supported()
-{
-    static int cached[64];
-    static bool init[64] = {false};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-    if (!init[dev]) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) v = 0;
-        cached[dev] = v;
-        init[dev] = true;
+    const int T = ((a.M + PF_BM - 1) / PF_BM) * ((a.N + 255) / 256);
+    const int tail = prefill_tail_tiles(T, prefill_cu_count());
+    if (T - tail > 0) {
+        e = launch_prefill_fq_part<OUT_F32, 256, RULE>(a, 0, T - tail, x, state, nb, stream);
+        if (e != hipSuccess) return e;
     }
-    return cached[dev] != 0;
+    if (tail > 0) return launch_prefill_fq_part<OUT_F32, 128, RULE>(a, T - tail, 2 * tail, x, state, nb, stream);
+    return hipSuccess;
 }
 
 } // namespace mxl
 
 using namespace mxl;
 
-// Workspace bytes of the quantize-once fused launch (mxl_prefill_ok shapes).
+// Workspace bytes of the quantize-once fused launches (mxl_prefill_ok shapes).
 extern "C" size_t mxl_prefill_fq_workspace(int64_t m, int64_t k)
 {
-    return prefill_fq_counter_offset(m, k) + 256;
+    const int64_t nb = (m + PF_BM - 1) / PF_BM;
+    return prefill_fq_state_offset(m, k) + (((size_t)(nb + 2) * sizeof(int) + 255) & ~(size_t)255);
 }
 
-// The quantize-once fused launch: A bf16 [m, k] quantized with rule a_rule
+// The quantize-once fused GEMM: A bf16 [m, k] quantized with rule a_rule
 // (MXFP4) into `work` (at least mxl_prefill_fq_workspace bytes, 16-byte
-// aligned), then Y = A W^T.  hipErrorNotSupported when the device cannot
-// launch cooperatively (the caller then uses the in-tile prologue).
+// aligned; calls sharing it must not overlap), and Y = A W^T.
 extern "C" hipError_t mxl_launch_mx_prefill_fq(int a_rule, const void* a_bf16, const void* wq, const void* ws,
                                                int64_t m, int64_t n, int64_t k, void* y, int out_f32, void* work,
                                                size_t work_bytes, hipStream_t stream)
 {
-    if (!prefill_coop_supported()) return hipErrorNotSupported;
     if (!work || work_bytes < mxl_prefill_fq_workspace(m, k)) return hipErrorInvalidValue;
     uint8_t* w8 = static_cast<uint8_t*>(work);
     PrefillArgs a{w8, w8 + (size_t)m * (k / 2), static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
                   y, nullptr, nullptr, (int)m, (int)n, (int)k, 0, 0};
-    const int T = (int)(((m + PF_BM - 1) / PF_BM) * ((n + 255) / 256));
-    const int tail = prefill_tail_tiles(T, prefill_cu_count());
-    a.tile_base = T - tail;   // 256 x 256 tiles
-    a.count = 2 * tail;       // then 256 x 128 halves of the tail tiles
-    int* ctr = reinterpret_cast<int*>(w8 + prefill_fq_counter_offset(m, k));
+    int* state = reinterpret_cast<int*>(w8 + prefill_fq_state_offset(m, k));
     if (a_rule == RULE_CEIL)
-        return out_f32 ? launch_prefill_fq<true, RULE_CEIL>(a, a_bf16, ctr, stream)
-                       : launch_prefill_fq<false, RULE_CEIL>(a, a_bf16, ctr, stream);
+        return out_f32 ? launch_prefill_fq<true, RULE_CEIL>(a, a_bf16, state, stream)
+                       : launch_prefill_fq<false, RULE_CEIL>(a, a_bf16, state, stream);
     if (a_rule == RULE_FLOOR)
-        return out_f32 ? launch_prefill_fq<true, RULE_FLOOR>(a, a_bf16, ctr, stream)
-                       : launch_prefill_fq<false, RULE_FLOOR>(a, a_bf16, ctr, stream);
-    return out_f32 ? launch_prefill_fq<true, RULE_EVEN>(a, a_bf16, ctr, stream)
-                   : launch_prefill_fq<false, RULE_EVEN>(a, a_bf16, ctr, stream);
+        return out_f32 ? launch_prefill_fq<true, RULE_FLOOR>(a, a_bf16, state, stream)
+                       : launch_prefill_fq<false, RULE_FLOOR>(a, a_bf16, state, stream);
+    return out_f32 ? launch_prefill_fq<true, RULE_EVEN>(a, a_bf16, state, stream)
+                   : launch_prefill_fq<false, RULE_EVEN>(a, a_bf16, state, stream);
 }
 
 // Shapes this kernel accepts: K % 128 == 0 and every operand below 2 GiB

@@ -158,13 +158,13 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
  * mx_quantize_act followed by an unsplit mx_gemm.
  * Workspace (optional, 16-byte aligned):
  *  - without MX_DEBUG_DUMP_AQ, large MXFP4 shapes (m, n >= 1024, k % 128 ==
- *    0) given at least mx_gemm_fused_workspace_size bytes run as one
- *    cooperative launch that quantizes A once into the workspace (codes
- *    [m, k/2], then scales [m, k/32], mx_quantize_act's layout), meets at a
- *    grid barrier and computes the GEMM from it; the workspace then holds
- *    A's codes and scales.  Other shapes, a smaller workspace or a device
- *    without cooperative launch quantize inside each tile instead.  Calls
- *    sharing a workspace must not overlap.
+ *    0) given at least mx_gemm_fused_workspace_size bytes quantize each
+ *    256-row block of A once into the workspace (codes [m, k/2], then scales
+ *    [m, k/32], mx_quantize_act's layout; then block counters), inside the
+ *    GEMM's own launches: the first workgroups that need a block share its
+ *    quantization, the others read it.  The workspace then holds A's codes
+ *    and scales.  Other shapes, or a smaller workspace, quantize inside each
+ *    tile instead.  Calls sharing a workspace must not overlap.
  *  - with MX_DEBUG_DUMP_AQ the quantization the in-tile prologue computed is
  *    also written to the workspace, A codes [m, k * bits / 8] (bits 4 or 8)
  *    followed by E8M0 scales [m, k/32], so it can be checked bit for bit.

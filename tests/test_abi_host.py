@@ -187,7 +187,8 @@ def test_workspace_sizes():
     # tiles that fill the GPU, the decode kernel, the prefill kernel: none
     assert mxl.mx_gemm_workspace_size("mxfp4", "mxfp4", 8192, 17408, 5120) == 0
     # fused, quantize-once: A codes and scales of the 8192 x 5120 activations,
-    # then a 256-byte counter block at a 256-byte boundary
+    # then at a 256-byte boundary a chunk pool counter, a done counter per
+    # 256-row block and an error word, rounded up to 256 bytes
     assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 8192, 17408, 5120) == 8192 * 2560 + 8192 * 160 + 256
     assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1100, 1090, 1152) == \
         ((1100 * 576 + 1100 * 36 + 255) // 256) * 256 + 256

@@ -256,14 +256,15 @@ def test_prefill_kernel_edges(what, m, k, n):
     assert torch.equal(yf.to(torch.bfloat16), y)
 
 
-# The quantize-once fused launch (large MXFP4 shapes with a workspace): one
-# cooperative launch quantizes all of A into the workspace, meets at a grid
-# barrier and runs the prefill tiles from it.  The workspace must then hold
-# exactly mx_quantize_act's codes and scales (which also shows that this path
-# ran), the barrier's error word must be clear, and Y must equal both the
-# standalone pair and the in-tile prologue bit for bit, for every rule.  The
-# first shape has fewer tiles than a grid of 8 workgroups per XCD round (24
-# workgroups over 25 tiles), the second several tiles per workgroup.
+# The quantize-once fused path (large MXFP4 shapes with a workspace): the
+# GEMM's workgroups quantize A once into the workspace (claiming 16-row
+# chunks from a pool) and the tiles read the codes from there.  The workspace
+# must then hold exactly mx_quantize_act's codes and scales (which also shows
+# that this path ran), the pool and every block's done counter must show all
+# chunks, the error word must be clear, and Y must equal both the standalone
+# pair and the in-tile prologue bit for bit, for every rule.  The first shape
+# has a ragged last block (1100 rows: 76 rows) and only tail tiles (25 tiles
+# as 256 x 128 halves), the second a main launch plus a tail.
 FQ_SHAPES = [(1100, 1152, 1090), (1300, 2560, 33000)]
 
 
@@ -288,7 +289,11 @@ def test_fused_quantize_once(m, k, n):
             torch.cuda.synchronize()
             assert torch.equal(ws[:qb].view(m, k // 2), aq), f"{rule}: workspace codes"
             assert torch.equal(ws[qb:qb + sb].view(m, k // 32), as_), f"{rule}: workspace scales"
-            assert int(ws[cnt + 4:cnt + 8].view(torch.int32).item()) == 0, "grid barrier error word"
+            nb = (m + 255) // 256
+            st = ws[cnt:cnt + 4 * (nb + 2)].view(torch.int32).cpu().numpy()
+            assert st[0] >= 16 * nb, "chunk pool"
+            assert np.all(st[1:nb + 1] == 16), "done counters"
+            assert st[nb + 1] == 0, "error word"
             assert torch.equal(y, y_ref), f"{rule} f32={out_f32}: quantize-once != standalone"
             assert torch.equal(y, y_tile), f"{rule} f32={out_f32}: quantize-once != in-tile prologue"
     rq, rs = oracle.mx_quantize("e2m1", "even", a_bits)
