@@ -216,8 +216,9 @@ def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str =
     """mx_gemm with the activation quantization done inside the GEMM from bf16 a[m, k].
     dump_aq also returns the codes and scales the prologue computed:
     (y, (a_q, a_s)).  quantize_once passes the workspace the library asks for
-    (large MXFP4 shapes: A is quantized once into it, in the same launch);
-    `workspace` (uint8, on a's device) is used instead when given."""
+    (large MXFP4 shapes: the GEMM's workgroups quantize A once into it instead
+    of once per tile column); `workspace` (uint8, on a's device) is used
+    instead when given."""
     _need(a, torch.bfloat16, "a")
     _need(w_q, torch.uint8, "w_q")
     _need(w_s, torch.uint8, "w_s")
