@@ -287,7 +287,7 @@ def mx_gemm_w4a16(a: torch.Tensor, w_q, w_s, w_fmt: str = "mxfp4", alpha: float 
 
 def mx_gemm_w4a16_plan(w_fmt: str, m: int, n: int, k: int) -> str:
     """Name of the kernel mx_gemm_w4a16 would launch for this shape."""
-    buf = ctypes.create_string_buffer(256)
+    buf = ctypes.create_string_buffer(512)
     _check(lib.mx_gemm_w4a16_plan(_fmt(w_fmt), m, n, k, buf, 256), "mx_gemm_w4a16_plan")
     return buf.value.decode()
 
@@ -396,7 +396,7 @@ def mx_nv_global_scale(amax: float) -> float:
 def mx_gemm_plan(a_fmt: str, w_fmt: str, m: int, n: int, k: int, fused: bool = False,
                  fp8_fast: bool = False) -> str:
     """Name of the kernel/tile configuration the GEMM would launch for this shape."""
-    buf = ctypes.create_string_buffer(256)
+    buf = ctypes.create_string_buffer(512)
     _check(lib.mx_gemm_plan(_fmt(a_fmt), _fmt(w_fmt), m, n, k, int(fused), _flags(False, fp8_fast),
-                            buf, 256), "mx_gemm_plan")
+                            buf, 512), "mx_gemm_plan")
     return buf.value.decode()
