@@ -1063,7 +1063,7 @@ extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n,
                    "4-pair scale windows fed by buffer-to-LDS copies, stage-ahead fragments, scaled mfma 32x32x64; "
                    "a last round of tiles at most half full runs as 256x128 halves>";
         if (fused && a_bits == 4 && mxl_prefill_ok(m, n, k))
-            return "mx_gemm_prefill_fq_kernel<A quantized once into the workspace from a pool of 16-row chunks, "
+            return "mx_gemm_prefill_fq_kernel<A quantized once into the workspace from a pool of 32-row chunks, "
                    "then the prefill tiles> with a workspace, else mx_gemm_kernel<tile 256x256x128, 2x2 waves of "
                    "128x128, scaled mfma 32x32x64, A quantized in each tile>";
         return "mx_gemm_kernel<tile 256x256x128, 2x2 waves of 128x128, scaled mfma 32x32x64>";

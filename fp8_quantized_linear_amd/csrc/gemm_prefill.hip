@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
 // into a workspace, exactly as mx_quantize_act does (the same device
 // functions, the same layout), and the tiles read the codes from there.
 //
-// Before its tile, a workgroup claims 16-row chunks of A (of any block) from
+// Before its tile, a workgroup claims 32-row chunks of A (of any block) from
 // a pool counter and quantizes them until the pool is empty, then waits until
 // its own block's done counter shows every chunk of the block.  It only ever
 // waits for chunks that running workgroups have claimed and finish without
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
 // k/32 scale bytes, k % 128 == 0).  Every poll is bounded (about 0.5 s, then an
 // error word and the tile is skipped), so that no mistake can hang the GPU.
 // ---------------------------------------------------------------------------
-constexpr int PF_FQ_CHUNK_ROWS = 16;
+constexpr int PF_FQ_CHUNK_ROWS = 32;
 constexpr int PF_FQ_SPINS = 1 << 21;           // x s_sleep(4): about 0.5 s
 
 // mx_quantize_act (MXFP4, rule RULE) of rows [r0, r1) of A (bf16, k per row):
@@ -245,9 +245,9 @@ __device__ __forceinline__ void pf_quantize_rows(const uint4* __restrict__ x, in
 
 // Makes sure A block tm (rows [256 tm, 256 tm + 256) clipped to M) is
 // quantized into p.a_q / p.a_s.  Before that, the workgroup takes chunks from
-// the pool of all blocks' chunks (chunk c: block c / 16, rows 16 (c % 16) ..
+// the pool of all blocks' chunks (chunk c: block c / 8, rows 32 (c % 8) ..
 // of it) until the pool is empty, so the first round of workgroups quantizes
-// all of A together.  state: the pool counter, done counters [nb] (16 chunks
+// all of A together.  state: the pool counter, done counters [nb] (8 chunks
 // each, empty chunks past M included), the error word.  Returns false if the
 // poll gave up.
 template <int RULE>
