@@ -38,6 +38,10 @@ hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, 
                                     void* y, int out_f32, void* dump_q, void* dump_s, void* work,
                                     size_t work_bytes, hipStream_t stream);
 size_t mxl_mx_gemm_fused_workspace(int a_bits, int64_t m, int64_t n, int64_t k);
+size_t mxl_dq_pool_workspace(int64_t m, int64_t n, int64_t k);
+hipError_t mxl_launch_mxfp8_exact_gemm_pool(int a_rule, const void* a_bf16, const void* wq, const void* ws, int64_t m,
+                                            int64_t n, int64_t k, void* y, int out_f32, void* work, size_t work_bytes,
+                                            hipStream_t stream);
 hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const void* wq, const void* ws, int64_t m,
                               int64_t n, int64_t k, float alpha, void* y, int out_f32, void* work,
                               size_t work_bytes, hipStream_t stream);
@@ -224,10 +228,15 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf1
     if ((st = check_device()) != MX_OK) return st;
     const int f32 = (flags & MX_OUT_F32) ? 1 : 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST))
+    if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
+    if (a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST)) {
+        const size_t pool = mxl_dq_pool_workspace(m, n, k);
+        if (!dump_q && pool > 0 && workspace && ws_bytes >= pool)
+            return from_hip(mxl_launch_mxfp8_exact_gemm_pool((int)a_rule, a_bf16, w_q, w_s, m, n, k, y, f32,
+                                                             workspace, ws_bytes, hs));
         return from_hip(mxl_launch_mxfp8_exact_gemm_fused((int)a_rule, a_bf16, w_q, w_s, m, n, k, y, f32, dump_q,
                                                           dump_s, hs));
-    if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
+    }
     return from_hip(mxl_launch_mx_gemm_fused(bits_of(a_fmt), (int)a_rule, a_bf16, bits_of(w_fmt), w_q, w_s,
                                              m, n, k, y, f32, dump_q, dump_s, dump_q ? nullptr : workspace,
                                              dump_q ? 0 : ws_bytes, hs));
@@ -242,7 +251,12 @@ mx_status mx_gemm_fused_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t
     mx_status st = check_gemm_shape(m, n, k, 32);
     if (st != MX_OK) return st;
     if (a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
-    *bytes = (flags & MX_DEBUG_DUMP_AQ) ? 0 : mxl_mx_gemm_fused_workspace(bits_of(a_fmt), m, n, k);
+    if (flags & MX_DEBUG_DUMP_AQ)
+        *bytes = 0;
+    else if (a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST))
+        *bytes = mxl_dq_pool_workspace(m, n, k);
+    else
+        *bytes = mxl_mx_gemm_fused_workspace(bits_of(a_fmt), m, n, k);
     return MX_OK;
 }
 

@@ -172,7 +172,99 @@ struct DqArgs {
     // scales [M, K/32], written by the tiles of the first tile column
     uint8_t* dump_q;
     uint8_t* dump_s;
+    // POOL only: A as bf16 [M, K], quantized once (RULE of the pool) into
+    // a_q / a_s (a workspace) by the workgroups themselves; state: the chunk
+    // pool counter, a done counter per 128-row block, an error word
+    const uint4* a_bf16;
+    int* state;
+    int nb;
 };
+
+// ---------------------------------------------------------------------------
+// Quantize-once for the fused MXFP8 GEMM (POOL): before its tile, a
+// workgroup claims 32-row chunks of A (of any 128-row block) from the pool
+// counter and quantizes them into the workspace exactly as mx_quantize_act
+// does, until the pool is empty; then it waits until its own block's done
+// counter shows every chunk.  It only waits for chunks that running
+// workgroups have claimed and finish without waiting, so no co-residency is
+// needed.  A chunk's writer waits for its stores and releases (one L2
+// write-back) before counting it; readers poll with device-scope atomic loads
+// and need no invalidation: a block is read only after it is done, and no L2
+// holds its lines from before in this launch (blocks start on cache-line
+// boundaries: 128 rows of k code bytes and of k/32 scale bytes, k % 128 == 0).
+// Polls are bounded (about 0.5 s, then the error word; the tile is skipped).
+// ---------------------------------------------------------------------------
+constexpr int DQ_POOL_ROWS = 32;               // rows per chunk
+constexpr int DQ_POOL_SPINS = 1 << 21;
+
+// mx_quantize_act (MXFP8, rule RULE) of rows [r0, r1): consecutive threads
+// take consecutive 8-element groups (lane quads hold the blocks of 32), 16
+// groups per thread loaded before any is encoded.
+template <int RULE, int NT>
+__device__ __forceinline__ void dq_pool_quantize_rows(const uint4* __restrict__ x, int k, int r0, int r1,
+                                                      uint8_t* __restrict__ q, uint8_t* __restrict__ s)
+{
+    constexpr int G = 16;
+    const int lane = threadIdx.x & 63;
+    const int64_t g_end = (int64_t)r1 * (k / 8);
+    for (int64_t g0 = (int64_t)r0 * (k / 8) + threadIdx.x; g0 < g_end; g0 += G * NT) {
+        uint4 v[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int64_t g = g0 + NT * j;
+            v[j] = x[g < g_end ? g : g0];
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int64_t g = g0 + NT * j;
+            const int e = scale_exponent<ELEM_E4M3, RULE>(quad_max_u32(amax_bits8(v[j])));
+            const uint2 c = encode8_e4m3(v[j], e);
+            if (g < g_end) {
+                reinterpret_cast<uint2*>(q)[g] = c;
+                if ((lane & 3) == 0) s[g >> 2] = (uint8_t)(e + 127);
+            }
+        }
+    }
+}
+
+template <int RULE, int BM, int NT>
+__device__ __forceinline__ bool dq_pool_ensure(const DqArgs& p, int tm, uint8_t* smem)
+{
+    constexpr int CPB = BM / DQ_POOL_ROWS;
+    int* pool = p.state;
+    int* done = p.state + 1;
+    int* word = reinterpret_cast<int*>(smem);
+    while (true) {
+        __syncthreads();
+        if (threadIdx.x == 0) *word = __hip_atomic_fetch_add(pool, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int c = *word;
+        if (c >= p.nb * CPB) break;
+        const int b = c / CPB, r0 = b * BM + (c % CPB) * DQ_POOL_ROWS;
+        const int r1 = min(r0 + DQ_POOL_ROWS, p.M);
+        if (r0 < r1)
+            dq_pool_quantize_rows<RULE, NT>(p.a_bf16, p.K, r0, r1, const_cast<uint8_t*>(p.a_q),
+                                            const_cast<uint8_t*>(p.a_s));
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_fetch_add(done + b, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int v = 0;
+        for (int spin = 0; spin < DQ_POOL_SPINS; ++spin) {
+            v = __hip_atomic_load(done + tm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (v >= CPB) break;
+            __builtin_amdgcn_s_sleep(4);
+        }
+        if (v < CPB) __hip_atomic_store(p.state + 1 + p.nb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *word = v >= CPB ? 1 : 0;
+    }
+    __syncthreads();
+    const bool ok = *word != 0;
+    __syncthreads();   // the tile reuses this LDS word
+    return ok;
+}
 
 // FUSED_A (MXFP8 only): A arrives as bf16 [M, K]; each 8-element chunk is
 // quantized in registers (block-32 scale by A_RULE over a lane quad, E4M3
@@ -187,9 +279,10 @@ struct DqArgs {
 // the compiler waits for a byte load's zero extension right after the load,
 // a dword needs none.
 template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL,
-          bool ODD16 = false, bool SCW = false, bool A_RAW = false>
+          bool ODD16 = false, bool SCW = false, bool A_RAW = false, bool POOL = false>
 __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
 {
+    static_assert(!POOL || (KIND == DQ_MXFP8 && !FUSED_A && !A_RAW), "the pool quantizes MXFP8 A");
     using T = DqTraits<KIND>;
     static_assert(!FUSED_A || KIND == DQ_MXFP8, "fused quantization is for MXFP8");
     static_assert(!A_RAW || KIND != DQ_MXFP8, "W4A16 weights are MXFP4 or NVFP4");
@@ -218,6 +311,9 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
     const int row_bytes = KIND == DQ_MXFP8 ? K : K / 2;   // W (and quantized A) bytes per row
     const int kt0 = split * p.chunk;                                // even: set parity = stage parity
     const int nk = min(p.chunk, (K + DQ_BK - 1) / DQ_BK - kt0);     // stages of this split
+    if constexpr (POOL) {
+        if (!dq_pool_ensure<A_RULE, BM, NT>(p, tm, smem)) return;
+    }
 
     // two register sets of staged chunks: stage kt lives in set kt % 2.
     // Loads are branch-free and nothing loaded is used before the chunk is
@@ -464,11 +560,11 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
 }
 
 template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL,
-          bool ODD16 = false, bool SCW = false, bool A_RAW = false>
+          bool ODD16 = false, bool SCW = false, bool A_RAW = false, bool POOL = false>
 hipError_t launch_dq_k(const DqArgs& a, hipStream_t stream)
 {
     constexpr int LDS = 2 * (BM + BN) * DQ_ROW_BYTES;
-    auto kern = dq_gemm_kernel<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, ODD16, SCW, A_RAW>;
+    auto kern = dq_gemm_kernel<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, ODD16, SCW, A_RAW, POOL>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
@@ -609,6 +705,62 @@ extern "C" hipError_t mxl_launch_w4a16_gemm(int w_nv, const void* a_bf16, const 
         if (f32) return launch_dq<DQ_MXFP4, 128, 128, 2, 2, true, false, RULE_CEIL, true>(x, stream);
         return launch_dq<DQ_MXFP4, 128, 128, 2, 2, false, false, RULE_CEIL, true>(x, stream);
     });
+}
+
+// ---- the quantize-once fused MXFP8 GEMM (POOL) ----
+// Workspace: A codes [m, k], E8M0 scales [m, k/32] (mx_quantize_act's
+// layout), then at a 256-byte boundary the pool counter, a done counter per
+// 128-row block and an error word.
+static size_t dq_pool_state_offset(int64_t m, int64_t k)
+{
+    return ((size_t)m * k + (size_t)m * (k / 32) + 255) & ~(size_t)255;
+}
+
+// Used for k % 128 == 0 and n > 256 (with fewer tile columns the in-tile
+// prologue repeats little); 0 otherwise.
+extern "C" size_t mxl_dq_pool_workspace(int64_t m, int64_t n, int64_t k)
+{
+    if (k % 128 != 0 || n <= 256) return 0;
+    const int64_t nb = (m + 127) / 128;
+    return dq_pool_state_offset(m, k) + (((size_t)(nb + 2) * sizeof(int) + 255) & ~(size_t)255);
+}
+
+__global__ void dq_pool_zero_kernel(int* p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+template <int RULE>
+static hipError_t pool8(const DqArgs& a, int out_f32, hipStream_t stream)
+{
+    if (out_f32) return launch_dq_k<DQ_MXFP8, 128, 128, 2, 2, true, false, RULE, false, true, false, true>(a, stream);
+    return launch_dq_k<DQ_MXFP8, 128, 128, 2, 2, false, false, RULE, false, true, false, true>(a, stream);
+}
+
+// The fused MXFP8 GEMM with A quantized once into `work` (at least
+// mxl_dq_pool_workspace bytes, 16-byte aligned; calls sharing it must not
+// overlap) by the GEMM's own workgroups.  Y equals mx_quantize_act followed
+// by the unsplit mx_gemm.
+extern "C" hipError_t mxl_launch_mxfp8_exact_gemm_pool(int a_rule, const void* a_bf16, const void* wq,
+                                                       const void* ws, int64_t m, int64_t n, int64_t k, void* y,
+                                                       int out_f32, void* work, size_t work_bytes,
+                                                       hipStream_t stream)
+{
+    const size_t need = mxl_dq_pool_workspace(m, n, k);
+    if (need == 0 || !work || work_bytes < need) return hipErrorInvalidValue;
+    uint8_t* w8 = static_cast<uint8_t*>(work);
+    const int nb = (int)((m + 127) / 128);
+    int* state = reinterpret_cast<int*>(w8 + dq_pool_state_offset(m, k));
+    hipLaunchKernelGGL(dq_pool_zero_kernel, dim3((nb + 2 + 255) / 256), dim3(256), 0, stream, state, nb + 2);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    DqArgs a{w8, w8 + (size_t)m * k, static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
+             (int)m, (int)n, (int)k, 1.0f, nullptr, 1, 1 << 30, nullptr, nullptr,
+             static_cast<const uint4*>(a_bf16), state, nb};
+    if (a_rule == RULE_CEIL) return pool8<RULE_CEIL>(a, out_f32, stream);
+    if (a_rule == RULE_FLOOR) return pool8<RULE_FLOOR>(a, out_f32, stream);
+    return pool8<RULE_EVEN>(a, out_f32, stream);
 }
 
 extern "C" const char* mxl_w4a16_gemm_config_name(void)

@@ -163,8 +163,10 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
  *    [m, k/32], mx_quantize_act's layout; then block counters), inside the
  *    GEMM's own launches: the first workgroups that need a block share its
  *    quantization, the others read it.  The workspace then holds A's codes
- *    and scales.  Other shapes, or a smaller workspace, quantize inside each
- *    tile instead.  Calls sharing a workspace must not overlap.
+ *    and scales.  The exact MXFP8 path does the same with 128-row blocks
+ *    (k % 128 == 0, n > 256; codes [m, k], then scales [m, k/32]).  Other
+ *    shapes, MX_FP8_FAST, or a smaller workspace, quantize inside each tile
+ *    instead.  Calls sharing a workspace must not overlap.
  *  - with MX_DEBUG_DUMP_AQ the quantization the in-tile prologue computed is
  *    also written to the workspace, A codes [m, k * bits / 8] (bits 4 or 8)
  *    followed by E8M0 scales [m, k/32], so it can be checked bit for bit.

@@ -194,7 +194,11 @@ def test_workspace_sizes():
         ((1100 * 576 + 1100 * 36 + 255) // 256) * 256 + 256
     assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 512, 2048, 5120) == 0     # not a large shape
     assert "mx_gemm_prefill_fq_kernel<" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 8192, 17408, 5120, fused=True)
-    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 8192, 17408, 5120) == 0
+    # exact MXFP8: codes [m, k] and scales, then the pool counter, a done
+    # counter per 128-row block and an error word; none for the fast path
+    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 8192, 17408, 5120) == 8192 * 5120 + 8192 * 160 + 512
+    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 8192, 17408, 5120, fp8_fast=True) == 0
+    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 64, 96, 5120) == 0        # n <= 256
     b2 = ctypes.c_size_t(7)
     assert L.mx_gemm_fused_workspace_size(0, 0, 8192, 17408, 5120, 0x4, ctypes.byref(b2)) == OK and b2.value == 0
     assert L.mx_gemm_fused_workspace_size(0, 2, 64, 64, 64, 0, ctypes.byref(b2)) == INVALID

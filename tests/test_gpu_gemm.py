@@ -264,40 +264,44 @@ def test_prefill_kernel_edges(what, m, k, n):
 # chunks, the error word must be clear, and Y must equal both the standalone
 # pair and the in-tile prologue bit for bit, for every rule.  The first shape
 # has a ragged last block (1100 rows: 76 rows) and only tail tiles (25 tiles
-# as 256 x 128 halves), the second a main launch plus a tail.
-FQ_SHAPES = [(1100, 1152, 1090), (1300, 2560, 33000)]
+# as 256 x 128 halves), the second a main launch plus a tail.  The exact MXFP8
+# GEMM does the same with 128-row blocks (1100 rows: a ragged 76-row block).
+FQ_CASES = [("mxfp4", 1100, 1152, 1090), ("mxfp4", 1300, 2560, 33000), ("mxfp8", 1100, 1152, 1090),
+            ("mxfp8", 300, 2048, 700)]
 
 
-@pytest.mark.parametrize("m,k,n", FQ_SHAPES)
-def test_fused_quantize_once(m, k, n):
-    wsz = mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", m, n, k)
-    say(f"fused quantize-once m={m} k={k} n={n}: workspace {wsz} B")
+@pytest.mark.parametrize("fmt,m,k,n", FQ_CASES)
+def test_fused_quantize_once(fmt, m, k, n):
+    wsz = mxl.mx_gemm_fused_workspace_size(fmt, fmt, m, n, k)
+    say(f"fused quantize-once {fmt} m={m} k={k} n={n}: workspace {wsz} B")
     assert wsz > 0
     a_bits = W.activations_entry_outliers(m, k)
     w_bits = W.normal_bf16(n, k, 0.02, 1)
     a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
-    wq, wsc = mxl.mx_pack_weights(w, fmt="mxfp4", rule="even")
-    qb, sb = m * k // 2, m * k // 32
+    wq, wsc = mxl.mx_pack_weights(w, fmt=fmt, rule=W_RULE[fmt])
+    cpr = k // 2 if fmt == "mxfp4" else k           # code bytes per row
+    bm = 256 if fmt == "mxfp4" else 128             # rows per block
+    qb, sb = m * cpr, m * k // 32
     cnt = (qb + sb + 255) // 256 * 256
     for rule in ("ceil", "floor", "even"):
         for out_f32 in (False, True):
             ws = torch.full((wsz,), 0xA5, dtype=torch.uint8, device="cuda")
-            y = mxl.mx_gemm_fused(a, wq, wsc, "mxfp4", rule, "mxfp4", out_f32=out_f32, workspace=ws)
-            aq, as_ = mxl.mx_quantize_act(a, "mxfp4", rule)
-            y_ref = mxl.mx_gemm(aq, as_, wq, wsc, k, out_f32=out_f32, split_k=False)
-            y_tile = mxl.mx_gemm_fused(a, wq, wsc, "mxfp4", rule, "mxfp4", out_f32=out_f32, quantize_once=False)
+            y = mxl.mx_gemm_fused(a, wq, wsc, fmt, rule, fmt, out_f32=out_f32, workspace=ws)
+            aq, as_ = mxl.mx_quantize_act(a, fmt, rule)
+            y_ref = mxl.mx_gemm(aq, as_, wq, wsc, k, fmt, fmt, out_f32=out_f32, split_k=False)
+            y_tile = mxl.mx_gemm_fused(a, wq, wsc, fmt, rule, fmt, out_f32=out_f32, quantize_once=False)
             torch.cuda.synchronize()
-            assert torch.equal(ws[:qb].view(m, k // 2), aq), f"{rule}: workspace codes"
+            assert torch.equal(ws[:qb].view(m, cpr), aq), f"{rule}: workspace codes"
             assert torch.equal(ws[qb:qb + sb].view(m, k // 32), as_), f"{rule}: workspace scales"
-            nb = (m + 255) // 256
+            nb = (m + bm - 1) // bm
             st = ws[cnt:cnt + 4 * (nb + 2)].view(torch.int32).cpu().numpy()
-            assert st[0] >= (256 // 32) * nb, "chunk pool"
-            assert np.all(st[1:nb + 1] == 256 // 32), "done counters"
+            assert st[0] >= (bm // 32) * nb, "chunk pool"
+            assert np.all(st[1:nb + 1] == bm // 32), "done counters"
             assert st[nb + 1] == 0, "error word"
             assert torch.equal(y, y_ref), f"{rule} f32={out_f32}: quantize-once != standalone"
             assert torch.equal(y, y_tile), f"{rule} f32={out_f32}: quantize-once != in-tile prologue"
-    rq, rs = oracle.mx_quantize("e2m1", "even", a_bits)
-    assert np.array_equal(host(ws[:qb].view(m, k // 2)), rq) and np.array_equal(host(ws[qb:qb + sb].view(m, k // 32)), rs)
+    rq, rs = oracle.mx_quantize(ELEM[fmt], "even", a_bits)
+    assert np.array_equal(host(ws[:qb].view(m, cpr)), rq) and np.array_equal(host(ws[qb:qb + sb].view(m, k // 32)), rs)
 
 
 def test_deterministic():
