@@ -363,15 +363,14 @@ def test_nvfp4_config_sampled():
 
 
 # split-K: few output tiles and a long K, so the library splits K over
-# workgroups (mx_gemm_workspace_size > 0) and sums fp32 partials in order
+# workgroups (mx_gemm_workspace_size > 0) and sums fp32 partials in order.
+# (M <= 32 MXFP4 runs the decode kernel, which does not split.)
 SPLIT_SHAPES = [(300, 2048, 200), (64, 5120, 96), (1, 4096, 48), (513, 1536, 130)]
+SPLIT_CASES = [(f, m, k, n) for (m, k, n) in SPLIT_SHAPES for f in ("mxfp4", "mxfp8") if not (f == "mxfp4" and m <= 32)]
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
-@pytest.mark.parametrize("m,k,n", SPLIT_SHAPES)
+@pytest.mark.parametrize("fmt,m,k,n", SPLIT_CASES)
 def test_gemm_split_k(fmt, m, k, n):
-    if fmt == "mxfp4" and m <= 32:
-        pytest.skip("M <= 32 MXFP4 runs the decode kernel (no split)")
     ws = mxl.mx_gemm_workspace_size(fmt, fmt, m, n, k)
     plan = mxl.mx_gemm_plan(fmt, fmt, m, n, k)
     say(f"split-K {fmt} m={m} k={k} n={n}: workspace {ws} B, plan {plan}")
