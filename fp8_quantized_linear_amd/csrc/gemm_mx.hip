@@ -881,27 +881,34 @@ static size_t decode_lds_bytes(int K)
     return (block > red ? block : red) + (size_t)16 * (1 + MT) * (K / 32);
 }
 
-// which decode kernel runs for this shape: 2 = LDS block, 1 = direct loads, 0 = generic
-static int decode_kind(int64_t m, int64_t k)
+// which decode kernel runs with MT 16-row A fragments: 2 = LDS block,
+// 1 = direct loads (MT <= 2), 0 = generic
+template <int MT>
+static int decode_kind_mt(int64_t k)
 {
     if (k % 128 != 0) return 0;
-    const bool mt1 = m <= 16;
-    if (k % 512 == 0 && k <= 8192 && (mt1 ? decode_lds_bytes<1>((int)k) : decode_lds_bytes<2>((int)k)) <= 65536)
-        return 2;
-    if ((mt1 ? decode_direct_lds_bytes<1>((int)k) : decode_direct_lds_bytes<2>((int)k)) <= 65536) return 1;
+    if (k % 512 == 0 && k <= 8192 && decode_lds_bytes<MT>((int)k) <= 65536) return 2;
+    if (MT <= 2 && decode_direct_lds_bytes<MT <= 2 ? MT : 2>((int)k) <= 65536) return 1;
     return 0;
+}
+
+static int decode_kind(int64_t m, int64_t k)
+{
+    if (m <= 16) return decode_kind_mt<1>(k);
+    if (m <= 32) return decode_kind_mt<2>(k);
+    return decode_kind_mt<3>(k);
 }
 
 template <int MT, bool OUT_F32>
 hipError_t launch_decode(const GemmArgs& a, hipStream_t stream)
 {
-    const int kind = decode_kind(MT == 1 ? 16 : 32, a.K);
+    const int kind = decode_kind_mt<MT>(a.K);
     if (kind == 2)
         hipLaunchKernelGGL((mx_decode_kernel<MT, OUT_F32>), dim3((a.N + 15) / 16), dim3(256), decode_lds_bytes<MT>(a.K),
                            stream, a);
-    else if (kind == 1)
-        hipLaunchKernelGGL((mx_decode_direct_kernel<MT, MT == 1 ? 10 : 5, OUT_F32>), dim3((a.N + 31) / 32), dim3(256),
-                           decode_direct_lds_bytes<MT>(a.K), stream, a);
+    else if (kind == 1 && MT <= 2)
+        hipLaunchKernelGGL((mx_decode_direct_kernel<MT <= 2 ? MT : 2, MT == 1 ? 10 : 5, OUT_F32>), dim3((a.N + 31) / 32),
+                           dim3(256), decode_direct_lds_bytes<MT <= 2 ? MT : 2>(a.K), stream, a);
     else
         hipLaunchKernelGGL((mx_decode_generic_kernel<MT, OUT_F32>), dim3((a.N + 15) / 16), dim3(512), 0, stream, a);
     return hipGetLastError();
@@ -913,7 +920,7 @@ using namespace mxl;
 
 // ---------------------------------------------------------------- dispatch
 // Shape classes (MXFP4 and fast-path MXFP8):
-//   decode  : M <= 32 (MXFP4)                     -> mx_decode_kernel
+//   decode  : M <= 48 (MXFP4)                     -> mx_decode_kernel
 //   large   : MXFP4, M, N >= 1024, K % 128 == 0    -> 256x256 tiles, 2x2 waves of 128x128
 //             (the E4M3 fragments are twice as wide and would spill there)
 //   default : everything else                      -> 128x128 tiles, 2x2 waves of 64x64
@@ -921,7 +928,9 @@ enum ShapeClass { SC_DECODE, SC_LARGE, SC_DEFAULT };
 
 static ShapeClass classify(int a_bits, int64_t m, int64_t n, int64_t k, bool fused)
 {
-    if (!fused && a_bits == 4 && m <= 32) return SC_DECODE;
+    // up to three 16-row A fragments: with a fourth the LDS-block kernel
+    // needs 296 VGPRs (one wave per SIMD) and loses to the tile kernel
+    if (!fused && a_bits == 4 && m <= 48) return SC_DECODE;
     if (a_bits == 4 && m >= 1024 && n >= 1024 && k % 128 == 0) return SC_LARGE;
     return SC_DEFAULT;
 }
@@ -992,7 +1001,8 @@ extern "C" hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq,
         return mxl_launch_mx_prefill(aq, as, wq, ws, m, n, k, y, out_f32, stream);
     if (sc == SC_DECODE) {
         if (m <= 16) return out_f32 ? launch_decode<1, true>(a, stream) : launch_decode<1, false>(a, stream);
-        return out_f32 ? launch_decode<2, true>(a, stream) : launch_decode<2, false>(a, stream);
+        if (m <= 32) return out_f32 ? launch_decode<2, true>(a, stream) : launch_decode<2, false>(a, stream);
+        return out_f32 ? launch_decode<3, true>(a, stream) : launch_decode<3, false>(a, stream);
     }
     if (a_bits == 4 && w_bits == 4) return dispatch_out<4, 4, false, RULE_CEIL>(a, sc, out_f32, stream);
     if (a_bits == 8 && w_bits == 8) return dispatch_out<8, 8, false, RULE_CEIL>(a, sc, out_f32, stream);

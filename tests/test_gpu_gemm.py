@@ -171,7 +171,7 @@ def test_decode_shapes_full():
         assert torch.equal(y, yf)
 
 
-# Decode-shaped calls (M <= 32) pick one of three kernels by K: whole-row LDS
+# Decode-shaped calls (M <= 32 here) pick one of three kernels by K: whole-row LDS
 # blocks (K % 512 == 0 while the block fits 64 KiB of LDS), K-chunked direct
 # loads (other K % 128 == 0)
 # and the generic split-K kernel.  Each is checked in full against the oracle
@@ -194,6 +194,23 @@ def test_decode_kernel_kinds(kernel, k, m):
     for out_f32 in (False, True):
         y, _, _, _ = run_mx(a_bits, w_bits, "mxfp4", out_f32=out_f32)
         check_gemm(y_host(y), y_ref, s, not out_f32, f"{kernel} {m}x{k}x{n} f32={out_f32}")
+
+
+# M = 33 .. 48 runs the decode kernels with three 16-row A fragments (the
+# whole-row LDS block where it fits 64 KiB, else the generic kernel).
+@pytest.mark.parametrize("m", [33, 40, 48])
+@pytest.mark.parametrize("k", [512, 5120, 6656, 384, 4128])
+def test_decode_wide_m(m, k):
+    n = 300
+    plan = mxl.mx_gemm_plan("mxfp4", "mxfp4", m, n, k)
+    say(f"decode wide m={m} k={k} n={n}: {plan[:60]}")
+    assert plan.split(" ", 1)[1].startswith("mx_decode")
+    a_bits = W.activations_entry_outliers(m, k, seed=3 + m)
+    w_bits = W.normal_bf16(n, k, 0.02, 4)
+    y_ref, s, _, _ = oracle_full(a_bits, w_bits, "mxfp4")
+    for out_f32 in (False, True):
+        y, _, _, _ = run_mx(a_bits, w_bits, "mxfp4", out_f32=out_f32)
+        check_gemm(y_host(y), y_ref, s, not out_f32, f"decode wide {m}x{k}x{n} f32={out_f32}")
 
 
 def sampled_check(cfg, fmt, fused=True, count=4096):
@@ -364,9 +381,9 @@ def test_nvfp4_config_sampled():
 
 # split-K: few output tiles and a long K, so the library splits K over
 # workgroups (mx_gemm_workspace_size > 0) and sums fp32 partials in order.
-# (M <= 32 MXFP4 runs the decode kernel, which does not split.)
+# (M <= 48 MXFP4 runs the decode kernels, which do not split.)
 SPLIT_SHAPES = [(300, 2048, 200), (64, 5120, 96), (1, 4096, 48), (513, 1536, 130)]
-SPLIT_CASES = [(f, m, k, n) for (m, k, n) in SPLIT_SHAPES for f in ("mxfp4", "mxfp8") if not (f == "mxfp4" and m <= 32)]
+SPLIT_CASES = [(f, m, k, n) for (m, k, n) in SPLIT_SHAPES for f in ("mxfp4", "mxfp8") if not (f == "mxfp4" and m <= 48)]
 
 
 @pytest.mark.parametrize("fmt,m,k,n", SPLIT_CASES)
