@@ -33,12 +33,44 @@ def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
     return out
 
 
-def check_gemm(y_gpu: np.ndarray, y_ref: np.ndarray, s_abs: np.ndarray, bf16_out: bool, what: str):
+FP32_MIN_NORMAL = 2.0 ** -126
+
+
+def underflow_allowance(k: int) -> float:
+    """Absolute allowance for fp32 underflow in a K-long accumulation: each of
+    at most K/16 fp32 additions (one per 16-wide matrix-core step at the
+    narrowest) can lose a value below the smallest normal fp32 if the
+    hardware flushes it."""
+    return (k // 16 + 1) * FP32_MIN_NORMAL
+
+
+def flushed_terms(a_dq: np.ndarray, w_dq: np.ndarray) -> np.ndarray:
+    """F[m, n] = sum_k |a_k w_k| over the k where an operand value lies below
+    the smallest normal fp32 (2^-126): the terms that the dequantizing GEMMs
+    may round or flush.  Computed by the oracle as S minus the same sum over
+    the operands with those values zeroed (fp64 cancellation is ~1e-16 S)."""
+    _, s_all = oracle.gemm_dq(a_dq, w_dq)
+    a_n = np.where(np.abs(a_dq) >= FP32_MIN_NORMAL, a_dq, 0.0)
+    w_n = np.where(np.abs(w_dq) >= FP32_MIN_NORMAL, w_dq, 0.0)
+    _, s_norm = oracle.gemm_dq(a_n, w_n)
+    return np.maximum(s_all - s_norm, 0.0)
+
+
+def check_gemm(y_gpu: np.ndarray, y_ref: np.ndarray, s_abs: np.ndarray, bf16_out: bool, what: str,
+               flushed=None, underflow: float = 0.0):
+    """Asserts |y_gpu - y_ref| <= 1e-4 * S (+ half a bf16 ulp for bf16 Y).
+    Where operands reach below the fp32 normal range, the GEMM's contract
+    adds the sum of the affected terms (`flushed`, from flushed_terms) and an
+    accumulation underflow allowance (`underflow`, underflow_allowance(K));
+    both default to 0, the contract for operands in the normal range."""
     y_gpu = y_gpu.astype(np.float64)
     err = np.abs(y_gpu - y_ref)
     bound = 1e-4 * s_abs
     if bf16_out:
         bound = bound + half_ulp_bf16(np.maximum(np.abs(y_ref), np.abs(y_gpu)))
+    if flushed is not None:
+        bound = bound + flushed
+    bound = bound + underflow
     bad = ~(err <= bound)
     zero_s = s_abs == 0
     bad |= zero_s & (y_gpu != 0)
@@ -56,19 +88,29 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def sample_pairs(m: int, n: int, count: int, seed: int = 0, tile: int = 128):
-    """Random (row, col) pairs plus rows/cols at tile edges and the last ones."""
+def tile_edges(size: int, tiles=(128, 256)) -> list[int]:
+    """Every first and last index of every tile of each size in `tiles`
+    (the GEMM kernels tile by 128 and by 256), plus 0 and size - 1."""
+    out = {0, size - 1}
+    for t in tiles:
+        for e in range(t, size, t):
+            out.add(e - 1)
+            out.add(e)
+    return sorted(out)
+
+
+def sample_pairs(m: int, n: int, count: int, seed: int = 0, tiles=(128, 256)):
+    """Output positions to check against the oracle: `count` random (row,
+    col) pairs, plus every pair of a tile-edge row and a tile-edge column --
+    the first and last row and column of every 128- and 256-wide tile, and
+    the last row and column of the output."""
     rng = np.random.default_rng(seed)
     mi = list(rng.integers(0, m, count))
     ni = list(rng.integers(0, n, count))
-    edge_m = sorted({0, m - 1, *[min(m - 1, t) for t in range(tile - 1, m, tile)][:16],
-                     *[min(m - 1, t) for t in range(tile, m, tile)][:16]})
-    edge_n = sorted({0, n - 1, *[min(n - 1, t) for t in range(tile - 1, n, tile)][:16],
-                     *[min(n - 1, t) for t in range(tile, n, tile)][:16]})
-    for a in edge_m:
-        for b in edge_n[:8]:
-            mi.append(a)
-            ni.append(b)
+    em, en = tile_edges(m, tiles), tile_edges(n, tiles)
+    gm, gn = np.meshgrid(np.array(em, np.int64), np.array(en, np.int64), indexing="ij")
+    mi.extend(gm.ravel().tolist())
+    ni.extend(gn.ravel().tolist())
     return np.array(mi, np.int64), np.array(ni, np.int64)
 
 

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import check_gemm, cuda_bf16, host, sample_pairs
+from helpers import check_gemm, cuda_bf16, flushed_terms, host, sample_pairs, underflow_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -271,6 +271,149 @@ def test_prefill_kernel_edges(what, m, k, n):
     yf = mxl.mx_gemm(aq, as_, wq, ws, k, out_f32=True)
     # the bf16 output is the RNE of the fp32 one, element by element
     assert torch.equal(yf.to(torch.bfloat16), y)
+
+
+# Full-output parity of the headline prefill kernels: every element of Y
+# against the oracle, on shapes whose tile grid takes both launches (a main
+# launch of 256 x 256 tiles and a tail launch of 256 x 128 halves), for the
+# standalone GEMM and for the quantize-once fused path, bf16 and fp32 output.
+# The first shape has one 256-K pair per tile; the second has ragged M and N,
+# 4.5 pairs (two scale windows, a half pair at the end) and ragged last tiles.
+PREFILL_FULL = [("one pair, main + tail", 2048, 256, 10240),
+                ("ragged, 4.5 pairs, main + tail", 4300, 1152, 4000)]
+
+
+def prefill_launches(m: int, n: int):
+    """Tiles of the main and of the tail launch, as the library splits them
+    for this GPU's compute-unit count."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    t = ((m + 255) // 256) * ((n + 255) // 256)
+    rem = t % cus
+    tail = rem if rem and 2 * rem <= cus else 0
+    return t - tail, tail
+
+
+@pytest.mark.parametrize("what,m,k,n", PREFILL_FULL)
+def test_prefill_full_output(what, m, k, n):
+    main, tail = prefill_launches(m, n)
+    say(f"prefill full output {what}: {m}x{k}x{n}, {main} main tiles + {tail} tail tiles")
+    assert main > 0 and tail > 0
+    assert mxl.mx_gemm_plan("mxfp4", "mxfp4", m, n, k).split(" ", 1)[1].startswith("mx_gemm_prefill_kernel<")
+    assert "mx_gemm_prefill_fq_kernel" in mxl.mx_gemm_plan("mxfp4", "mxfp4", m, n, k, fused=True)
+    a_bits = W.activations_entry_outliers(m, k)
+    w_bits = W.normal_bf16(n, k, 0.02, 1)
+    y_ref, s, (raq, ras), (rwq, rws) = oracle_full(a_bits, w_bits, "mxfp4")
+    a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
+    wq, wsc = mxl.mx_pack_weights(w, "mxfp4", "even")
+    aq, as_ = mxl.mx_quantize_act(a, "mxfp4", "ceil")
+    wsz = mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", m, n, k)
+    assert wsz > 0
+    for out_f32 in (False, True):
+        y = mxl.mx_gemm(aq, as_, wq, wsc, k, out_f32=out_f32)
+        ws = torch.empty(wsz, dtype=torch.uint8, device="cuda")
+        yq = mxl.mx_gemm_fused(a, wq, wsc, "mxfp4", "ceil", "mxfp4", out_f32=out_f32, workspace=ws)
+        torch.cuda.synchronize()
+        if not out_f32:
+            assert np.array_equal(host(aq), raq) and np.array_equal(host(as_), ras)
+            assert np.array_equal(host(wq), rwq) and np.array_equal(host(wsc), rws)
+        rel = check_gemm(y_host(y), y_ref, s, not out_f32, f"prefill {what} f32={out_f32}")
+        check_gemm(y_host(yq), y_ref, s, not out_f32, f"quantize-once {what} f32={out_f32}")
+        assert torch.equal(y, yq), "quantize-once != standalone"
+        say(f"  f32={out_f32}: max err/S {rel:.2e}")
+
+
+# GEMM parity on adversarial operands: fuzz-corpus activations (blocks in
+# binades -135 .. 60, E2M1/E4M3 ties, rule thresholds, zero and -0 blocks,
+# mixed magnitudes) against fuzz-corpus weights (binades -20 .. 2), so that
+# tiny blocks meet large weights and scales reach 2^-127.  Ranges keep every
+# product and sum inside fp32.  The contract's bound for operands below the
+# fp32 normal range applies: 1e-4 * S, plus the terms with an operand value
+# below 2^-126 (helpers.flushed_terms) and an accumulation underflow
+# allowance of (K/16 + 1) * 2^-126.  Outputs that needed more than 1e-4 * S
+# are counted and printed.
+FUZZ_SHAPES = [(200, 416, 300), (1100, 1152, 1090)]     # the second runs the prefill kernel (MXFP4)
+
+
+def fuzz_operands(m, k, n):
+    a_bits = W.fuzz_bf16(m, k, seed=23, emax=60, mix=(-60, 60))
+    w_bits = W.fuzz_bf16(n, k, seed=29, emin=-20, emax=2, mix=(-20, 3))
+    return a_bits, w_bits
+
+
+def report_fuzz(what, y, y_ref, s, fl, bf16_out):
+    yv = y_host(y).astype(np.float64)
+    err = np.abs(yv - y_ref)
+    beyond = int((err > 1e-4 * s + (0 if not bf16_out else np.abs(y_ref) * 2.0 ** -8)).sum())
+    say(f"  {what}: {beyond} outputs beyond 1e-4*S; flushed-term allowance nonzero at "
+        f"{int((fl > 0).sum())} of {fl.size}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("m,k,n", FUZZ_SHAPES)
+def test_gemm_fuzz_operands(fmt, m, k, n):
+    say(f"fuzz gemm {fmt} {m}x{k}x{n}: {mxl.mx_gemm_plan(fmt, fmt, m, n, k)[:50]}")
+    a_bits, w_bits = fuzz_operands(m, k, n)
+    aq, as_ = oracle.mx_quantize(ELEM[fmt], "ceil", a_bits)
+    wq, ws = oracle.mx_quantize(ELEM[fmt], W_RULE[fmt], w_bits)
+    ad = oracle.mx_dequantize(ELEM[fmt], aq, as_, m, k)
+    wd = oracle.mx_dequantize(ELEM[fmt], wq, ws, n, k)
+    y_ref, s = oracle.gemm_dq(ad, wd)
+    fl = flushed_terms(ad, wd)
+    u = underflow_allowance(k)
+    for out_f32 in (False, True):
+        y, yf, (gaq, gas), (gwq, gws) = run_mx(a_bits, w_bits, fmt, out_f32=out_f32, fused=True)
+        assert np.array_equal(host(gaq), aq) and np.array_equal(host(gas), as_)
+        assert np.array_equal(host(gwq), wq) and np.array_equal(host(gws), ws)
+        check_gemm(y_host(y), y_ref, s, not out_f32, f"fuzz {fmt} {m}x{k}x{n} f32={out_f32}", fl, u)
+        assert torch.equal(y, yf), "fused != standalone"
+        report_fuzz(f"{fmt} f32={out_f32}", y, y_ref, s, fl, not out_f32)
+
+
+@pytest.mark.parametrize("m,k,n", [(8, 1024, 300), (130, 416, 200)])
+@pytest.mark.parametrize("w_fmt", ["mxfp4", "nvfp4"])
+def test_w4a16_fuzz_operands(w_fmt, m, k, n):
+    a_bits, w_bits = fuzz_operands(m, k, n)
+    say(f"fuzz w4a16 {w_fmt} {m}x{k}x{n}: {mxl.mx_gemm_w4a16_plan(w_fmt, m, n, k)[:40]}")
+    a = cuda_bf16(a_bits)
+    if w_fmt == "mxfp4":
+        wq, ws = oracle.mx_quantize("e2m1", "even", w_bits)
+        wd = oracle.mx_dequantize("e2m1", wq, ws, n, k)
+        g_w, alpha = None, 1.0
+    else:
+        g_w = oracle.nv_global_scale(oracle.bf16_amax(w_bits))
+        wq, ws = oracle.nv_quantize(w_bits, g_w)
+        wd = oracle.nv_dequantize(wq, ws, n, k, g_w)
+        alpha = float(np.float32(1.0) / np.float32(g_w))
+    ad = oracle.bf16_to_f64(a_bits)
+    y_ref, s = oracle.gemm_dq(ad, wd)
+    # the GEMM consumes the weights before the global scale: e2m1 * s_w
+    w_cons = wd if w_fmt == "mxfp4" else wd * float(g_w)
+    fl = flushed_terms(ad, w_cons) * (1.0 if w_fmt == "mxfp4" else 1.0 / float(g_w))
+    u = underflow_allowance(k)
+    dev = torch.device("cuda")
+    for out_f32 in (False, True):
+        y = mxl.mx_gemm_w4a16(a, torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev), w_fmt, alpha,
+                              out_f32=out_f32)
+        torch.cuda.synchronize()
+        check_gemm(y_host(y), y_ref, s, not out_f32, f"fuzz w4a16 {w_fmt} {m}x{k}x{n} f32={out_f32}", fl, u)
+        report_fuzz(f"w4a16 {w_fmt} f32={out_f32}", y, y_ref, s, fl, not out_f32)
+
+
+def test_nvfp4_fuzz_operands():
+    m, k, n = 200, 416, 300
+    a_bits, w_bits = fuzz_operands(m, k, n)
+    g_a = oracle.nv_global_scale(oracle.bf16_amax(a_bits))
+    g_w = oracle.nv_global_scale(oracle.bf16_amax(w_bits))
+    aq, as_ = oracle.nv_quantize(a_bits, g_a)
+    wq, ws = oracle.nv_quantize(w_bits, g_w)
+    y_ref, s = oracle.gemm_dq(oracle.nv_dequantize(aq, as_, m, k, g_a), oracle.nv_dequantize(wq, ws, n, k, g_w))
+    u = underflow_allowance(k)
+    for out_f32 in (False, True):
+        y, (gaq, gas), (gwq, gws) = nv_case(a_bits, w_bits, g_a, g_w, out_f32)
+        assert np.array_equal(host(gaq), aq) and np.array_equal(host(gas), as_)
+        assert np.array_equal(host(gwq), wq) and np.array_equal(host(gws), ws)
+        # e2m1 * s_e4m3 products are exact in f16: no operand leaves its range
+        check_gemm(y_host(y), y_ref, s, not out_f32, f"fuzz nvfp4 f32={out_f32}", None, u)
 
 
 # The quantize-once fused path (large MXFP4 shapes with a workspace): the

@@ -384,6 +384,53 @@ def test_nv_quantize_bruteforce():
                     assert ((int(q[r, j // 2]) >> (4 * (j % 2))) & 0xF) == codes[i], (g, r, b, i)
 
 
+def _torch_amax(bits: np.ndarray) -> float:
+    # torch decodes the bf16 patterns independently of the oracle
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return float(t.double().abs().max()) if bits.size else 0.0
+
+
+def test_bf16_amax_against_torch_decode():
+    # orc_bf16_amax feeds every NVFP4 global scale (the per-tensor amax of the
+    # weights, the running max of the activation batches).  Pinned against
+    # torch's bf16 decode on tensors built so that a dropped fabs, a signed
+    # compare, a skipped element or a subnormal flush each gives a wrong value:
+    # the extreme magnitude is negative, sits at the first or the last index,
+    # or is a subnormal among -0 and smaller subnormals.
+    rng = np.random.default_rng(41)
+    cases = []
+    x = rng.standard_normal(4099).astype(np.float32)
+    x[1234] = -37.5                                     # extreme value negative, mid-tensor
+    cases.append(x)
+    y = rng.standard_normal(513).astype(np.float32)
+    y[0] = -9.0e3                                       # first element
+    cases.append(y)
+    z = rng.standard_normal(777).astype(np.float32)
+    z[-1] = -6.5e4                                      # last element
+    cases.append(z)
+    cases.append(np.array([-3.0e38, 1.0, -0.0], np.float32))   # near the largest finite bf16
+    for xs in cases:
+        bits = torch.from_numpy(xs).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert oracle.bf16_amax(bits) == _torch_amax(bits)
+        assert oracle.bf16_amax(bits) > float(np.max(torch.from_numpy(bits.view(np.int16)).view(
+            torch.bfloat16).double().numpy())), "the extreme is negative: a signed max is smaller"
+    # subnormals only, with -0: the largest magnitude is the negative subnormal 0x807F
+    sub = np.array([0x8000, 0x0001, 0x807F, 0x0040, 0x8003, 0x0000], np.uint16)
+    assert oracle.bf16_amax(sub) == _torch_amax(sub) == 127 * 2.0 ** -133
+    # zeros of both signs: amax 0 (the NVFP4 global scale is then 1)
+    zeros = np.array([0x8000, 0x0000, 0x8000], np.uint16)
+    assert oracle.bf16_amax(zeros) == 0.0
+    assert oracle.nv_global_scale(oracle.bf16_amax(zeros)) == np.float32(1.0)
+    # every positive finite bf16 once, shuffled, negated: the maximum is the
+    # largest finite bf16 whatever the order
+    bits, vals = all_bf16_positive_finite()
+    perm = rng.permutation(bits.size)
+    neg = (bits[perm] | 0x8000).astype(np.uint16)
+    assert oracle.bf16_amax(neg) == vals.max() == _torch_amax(neg)
+    # one element
+    assert oracle.bf16_amax(np.array([0xC2F7], np.uint16)) == 123.5
+
+
 def test_nv_invariants():
     rng = np.random.default_rng(3)
     x = torch.from_numpy(rng.standard_normal((64, 256)).astype(np.float32)).to(torch.bfloat16)

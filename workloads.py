@@ -161,22 +161,26 @@ _AMAX_MANTISSAS = np.array([1.0, 1.0078125, 1.4921875, 1.5, 1.5078125, 1.7421875
                             1.9296875, 1.9375, 1.9453125, 1.9921875])
 
 
-def fuzz_bf16(rows: int, k: int, seed: int = 7) -> np.ndarray:
+def fuzz_bf16(rows: int, k: int, seed: int = 7, emin: int = -135, emax: int = 120,
+              mix: tuple[int, int] = (-60, 60)) -> np.ndarray:
     """Adversarial bf16 blocks (32 along k) for quantizer fuzzing.
 
-    Every block draws a binade E in [-135, 120] and one of six shapes:
+    Every block draws a binade E in [emin, emax] (default [-135, 120]) and
+    one of six shapes:
     random normals; E2M1 rounding ties (the block max is 2^(E+2), so every
     scale rule picks exponent E, and the other elements sit on lattice points,
     midpoints, or one bf16 step either side of them); E4M3 ties (max
     2^(E+8)); a block max with a mantissa at a rule threshold; all-zero or
-    negative-zero blocks; mixed huge and tiny values.  Values are built
-    exactly in bf16, so the final rounding changes nothing.
+    negative-zero blocks; mixed huge and tiny values (binades drawn from
+    `mix`).  Values are built exactly in bf16, so the final rounding changes
+    nothing.  GEMM tests narrow the ranges so that no product or sum leaves
+    the fp32 range.
     """
     rng = np.random.default_rng(seed)
     nblk = rows * k // 32
     out = np.zeros((nblk, 32), np.float64)
     kind = rng.integers(0, 6, nblk)
-    E = rng.integers(-135, 121, nblk)
+    E = rng.integers(emin, emax + 1, nblk)
     p2 = np.ldexp(1.0, E)[:, None]
     sign = np.where(rng.random((nblk, 32)) < 0.5, -1.0, 1.0)
     # 0: normals
@@ -198,8 +202,8 @@ def fuzz_bf16(rows: int, k: int, seed: int = 7) -> np.ndarray:
     z = np.where(rng.random((nblk, 32)) < 0.5, -0.0, 0.0)
     out[kind == 4] = z[kind == 4]
     # 5: mixed magnitudes
-    mix = rng.standard_normal((nblk, 32)) * np.ldexp(1.0, rng.integers(-60, 60, (nblk, 32)))
-    out[kind == 5] = mix[kind == 5]
+    mixed = rng.standard_normal((nblk, 32)) * np.ldexp(1.0, rng.integers(mix[0], mix[1], (nblk, 32)))
+    out[kind == 5] = mixed[kind == 5]
     # keep everything finite in bf16 and round to bf16 exactly once
     out = np.clip(out, -3.0e38, 3.0e38).astype(np.float32)
     bits = _to_bf16_bits(out.reshape(rows, k))
