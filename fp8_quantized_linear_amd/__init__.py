@@ -50,13 +50,13 @@ def _load():
     for f in (L.mx_quantize_act, L.mx_pack_weights):
         f.restype, f.argtypes = i32, [i32, i32, P, i64, i64, f32, P, P, P]
     L.mx_gemm.restype = i32
-    L.mx_gemm.argtypes = [i32, i32, P, P, P, P, i64, i64, i64, P, u32, P, sz, P]
+    L.mx_gemm.argtypes = [i32, i32, P, P, P, P, i64, i64, i64, P, P, sz, u32, P]
     L.mx_gemm_fused.restype = i32
-    L.mx_gemm_fused.argtypes = [i32, i32, P, i32, P, P, i64, i64, i64, P, u32, P, sz, P]
+    L.mx_gemm_fused.argtypes = [i32, i32, P, i32, P, P, i64, i64, i64, P, P, sz, u32, P]
     L.nv_gemm.restype = i32
-    L.nv_gemm.argtypes = [P, P, P, P, i64, i64, i64, f32, P, u32, P, sz, P]
+    L.nv_gemm.argtypes = [P, P, P, P, i64, i64, i64, f32, P, P, sz, u32, P]
     L.mx_gemm_w4a16.restype = i32
-    L.mx_gemm_w4a16.argtypes = [i32, P, P, P, i64, i64, i64, f32, P, u32, P, sz, P]
+    L.mx_gemm_w4a16.argtypes = [i32, P, P, P, i64, i64, i64, f32, P, P, sz, u32, P]
     L.mx_gemm_w4a16_plan.restype = i32
     L.mx_gemm_w4a16_plan.argtypes = [i32, i64, i64, i64, ctypes.c_char_p, sz]
     L.mx_gemm_swiglu_quant.restype = i32
@@ -185,8 +185,10 @@ def mx_gemm_workspace_size(a_fmt: str, w_fmt: str, m: int, n: int, k: int, fp8_f
 def mx_gemm(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str = "mxfp4",
             out_f32: bool = False, y=None, fp8_fast: bool = False, split_k: bool = True):
     """Y[m, n] = A W^T on MX codes/scales (bf16 out, or fp32 with out_f32).
-    fp8_fast selects the FP8 matrix cores for MXFP8 (inexact accumulation).
-    split_k passes the split-K workspace the library asks for on this shape."""
+    a_fmt and w_fmt may differ (mixed MXFP8 x MXFP4 pairs).  fp8_fast selects
+    the FP8 matrix cores for pairs with an MXFP8 operand (inexact
+    accumulation).  split_k passes the split-K workspace the library asks
+    for on this shape."""
     for t, nm in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
         _need(t, torch.uint8, nm)
     m, n = a_q.shape[0], w_q.shape[0]
@@ -198,7 +200,7 @@ def mx_gemm(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str = "mxfp
     ws, wsb = _workspace(lib.mx_gemm_workspace_size, a_q.device, _fmt(a_fmt), _fmt(w_fmt), m, n, k,
                          _flags(out_f32, fp8_fast)) if split_k else (None, 0)
     st = lib.mx_gemm(_fmt(a_fmt), _fmt(w_fmt), _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, n, k,
-                     _ptr(y), _flags(out_f32, fp8_fast), _ptr(ws), wsb, _stream(a_q))
+                     _ptr(y), _ptr(ws), wsb, _flags(out_f32, fp8_fast), _stream(a_q))
     _check(st, "mx_gemm")
     return y
 
@@ -216,9 +218,10 @@ def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str =
     """mx_gemm with the activation quantization done inside the GEMM from bf16 a[m, k].
     dump_aq also returns the codes and scales the prologue computed:
     (y, (a_q, a_s)).  quantize_once passes the workspace the library asks for
-    (large MXFP4 shapes: the GEMM's workgroups quantize A once into it instead
-    of once per tile column); `workspace` (uint8, on a's device) is used
-    instead when given."""
+    (large shapes: the GEMM's workgroups quantize A once into it instead of
+    once per tile column; mixed pairs: required); `workspace` (uint8, on a's
+    device, 256-byte aligned as torch allocates) is used instead when
+    given."""
     _need(a, torch.bfloat16, "a")
     _need(w_q, torch.uint8, "w_q")
     _need(w_s, torch.uint8, "w_s")
@@ -236,10 +239,10 @@ def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str =
     elif workspace is not None:
         _need(workspace, torch.uint8, "workspace")
         ws, wsb = workspace, workspace.numel()
-    elif quantize_once:
+    elif quantize_once or a_fmt != w_fmt:
         ws, wsb = _workspace(lib.mx_gemm_fused_workspace_size, a.device, _fmt(a_fmt), _fmt(w_fmt), m, n, k, flags)
-    st = lib.mx_gemm_fused(_fmt(a_fmt), _rule(a_rule), _ptr(a), _fmt(w_fmt), _ptr(w_q), _ptr(w_s),
-                           m, n, k, _ptr(y), flags, _ptr(ws), wsb, _stream(a))
+    st = lib.mx_gemm_fused(_fmt(a_fmt), _fmt(w_fmt), _ptr(a), _rule(a_rule), _ptr(w_q), _ptr(w_s),
+                           m, n, k, _ptr(y), _ptr(ws), wsb, flags, _stream(a))
     _check(st, "mx_gemm_fused")
     if dump_aq:
         return y, (ws[:qb].view(m, codes_per_row(a_fmt, k)), ws[qb:].view(m, k // 32))
@@ -258,7 +261,7 @@ def nv_gemm(a_q, a_s, w_q, w_s, k: int, alpha: float, out_f32: bool = False, y=N
     ws, wsb = _workspace(lib.mx_gemm_workspace_size, a_q.device, FORMATS["nvfp4"], FORMATS["nvfp4"], m, n, k,
                          0) if split_k else (None, 0)
     st = lib.nv_gemm(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, n, k, float(alpha), _ptr(y),
-                     MX_OUT_F32 if out_f32 else 0, _ptr(ws), wsb, _stream(a_q))
+                     _ptr(ws), wsb, MX_OUT_F32 if out_f32 else 0, _stream(a_q))
     _check(st, "nv_gemm")
     return y
 
@@ -280,7 +283,7 @@ def mx_gemm_w4a16(a: torch.Tensor, w_q, w_s, w_fmt: str = "mxfp4", alpha: float 
     ws, wsb = _workspace(lib.mx_gemm_w4a16_workspace_size, a.device, _fmt(w_fmt), m, n, k) if split_k \
         else (None, 0)
     st = lib.mx_gemm_w4a16(_fmt(w_fmt), _ptr(a), _ptr(w_q), _ptr(w_s), m, n, k, float(alpha), _ptr(y),
-                           MX_OUT_F32 if out_f32 else 0, _ptr(ws), wsb, _stream(a))
+                           _ptr(ws), wsb, MX_OUT_F32 if out_f32 else 0, _stream(a))
     _check(st, "mx_gemm_w4a16")
     return y
 
@@ -288,7 +291,7 @@ def mx_gemm_w4a16(a: torch.Tensor, w_q, w_s, w_fmt: str = "mxfp4", alpha: float 
 def mx_gemm_w4a16_plan(w_fmt: str, m: int, n: int, k: int) -> str:
     """Name of the kernel mx_gemm_w4a16 would launch for this shape."""
     buf = ctypes.create_string_buffer(512)
-    _check(lib.mx_gemm_w4a16_plan(_fmt(w_fmt), m, n, k, buf, 256), "mx_gemm_w4a16_plan")
+    _check(lib.mx_gemm_w4a16_plan(_fmt(w_fmt), m, n, k, buf, len(buf)), "mx_gemm_w4a16_plan")
     return buf.value.decode()
 
 
@@ -347,7 +350,7 @@ def mx_gemm_swiglu_quant(a_q, a_s, w_q, w_s, k: int, out=None):
 
 def mx_gemm_swiglu_quant_plan(m: int, inter: int, k: int) -> str:
     buf = ctypes.create_string_buffer(512)
-    _check(lib.mx_gemm_swiglu_quant_plan(m, inter, k, buf, 512), "mx_gemm_swiglu_quant_plan")
+    _check(lib.mx_gemm_swiglu_quant_plan(m, inter, k, buf, len(buf)), "mx_gemm_swiglu_quant_plan")
     return buf.value.decode()
 
 
@@ -398,5 +401,5 @@ def mx_gemm_plan(a_fmt: str, w_fmt: str, m: int, n: int, k: int, fused: bool = F
     """Name of the kernel/tile configuration the GEMM would launch for this shape."""
     buf = ctypes.create_string_buffer(512)
     _check(lib.mx_gemm_plan(_fmt(a_fmt), _fmt(w_fmt), m, n, k, int(fused), _flags(False, fp8_fast),
-                            buf, 512), "mx_gemm_plan")
+                            buf, len(buf)), "mx_gemm_plan")
     return buf.value.decode()

@@ -30,7 +30,12 @@ hipError_t mxl_launch_amax(const void* x, int64_t count, float* out, hipStream_t
 hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq, const void* as, const void* wq,
                               const void* ws, int64_t m, int64_t n, int64_t k, void* y, int out_f32,
                               void* work, size_t work_bytes, hipStream_t stream);
-size_t mxl_mx_gemm_workspace(int a_bits, int64_t m, int64_t n, int64_t k);
+size_t mxl_mx_gemm_workspace(int a_bits, int w_bits, int64_t m, int64_t n, int64_t k);
+int mxl_mx_gemm_fits(int a_bits, int w_bits, int64_t m, int64_t n, int64_t k, int fused_in_tile);
+hipError_t mxl_launch_mx_mixed_exact_gemm(int a_bits, const void* aq, const void* as, const void* wq,
+                                          const void* ws, int64_t m, int64_t n, int64_t k, void* y, int out_f32,
+                                          void* work, size_t work_bytes, hipStream_t stream);
+const char* mxl_mx_mixed_exact_config_name(void);
 size_t mxl_dq_workspace(int64_t m, int64_t n, int64_t k);
 int mxl_dq_splits(int64_t m, int64_t n, int64_t k);
 hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, int w_bits,
@@ -59,7 +64,7 @@ hipError_t mxl_launch_w4a16_decode(int w_nv, const void* a_bf16, const void* wq,
 int mxl_w4a16_decode_ok(int w_nv, int64_t m, int64_t k);
 const char* mxl_w4a16_gemm_config_name(void);
 const char* mxl_w4a16_decode_config_name(void);
-const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n, int64_t k, int fused);
+const char* mxl_mx_gemm_config_name(int a_bits, int w_bits, int64_t m, int64_t n, int64_t k, int fused);
 const char* mxl_nv_gemm_config_name(void);
 const char* mxl_mxfp8_exact_config_name(void);
 }
@@ -136,6 +141,35 @@ mx_status check_gemm_shape(int64_t m, int64_t n, int64_t k, int block)
 
 int bits_of(mx_format f) { return f == MX_FMT_MXFP8 ? 8 : 4; }
 
+// Kernel family of mx_gemm for an MX pair: the block-scaled matrix cores
+// (MXFP4 x MXFP4; pairs with an MXFP8 operand under MX_FP8_FAST), or exact
+// dequantization to bf16 (MXFP8 x MXFP8 and mixed pairs by default).
+enum MxPath { PATH_SCALED, PATH_EXACT8, PATH_MIXED_EXACT };
+
+MxPath mx_path(mx_format a, mx_format w, unsigned flags)
+{
+    if ((a == MX_FMT_MXFP4 && w == MX_FMT_MXFP4) || (flags & MX_FP8_FAST)) return PATH_SCALED;
+    return a == w ? PATH_EXACT8 : PATH_MIXED_EXACT;
+}
+
+// Split-K workspace mx_gemm uses for this pair and shape (0: none).
+size_t gemm_workspace_need(mx_format a, mx_format w, int64_t m, int64_t n, int64_t k, unsigned flags)
+{
+    return mx_path(a, w, flags) == PATH_SCALED ? mxl_mx_gemm_workspace(bits_of(a), bits_of(w), m, n, k)
+                                               : mxl_dq_workspace(m, n, k);
+}
+
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+// Workspace mx_gemm_fused uses: A's codes and scales (dump or mixed pair),
+// the quantize-once state (large same-format shapes), or none.
+size_t fused_workspace_need(mx_format a, mx_format w, int64_t m, int64_t n, int64_t k, unsigned flags)
+{
+    if (a != w || (flags & MX_DEBUG_DUMP_AQ)) return (size_t)m * k * bits_of(a) / 8 + (size_t)m * (k / 32);
+    if (a == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST)) return mxl_dq_pool_workspace(m, n, k);
+    return mxl_mx_gemm_fused_workspace(bits_of(a), m, n, k);
+}
+
 // W4A16: the decode kernel takes M <= 16 with K % 512 == 0 when its W block
 // fits LDS and W's bytes stay within 32-bit buffer offsets
 bool w4a16_use_decode(bool nv, int64_t m, int64_t n, int64_t k)
@@ -176,36 +210,43 @@ mx_status mx_pack_weights(mx_format fmt, mx_scale_rule rule, const void* w_bf16,
 }
 
 mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void* a_s, const void* w_q,
-                  const void* w_s, int64_t m, int64_t n, int64_t k, void* y, unsigned flags,
-                  void* workspace, size_t ws_bytes, mx_stream_t stream)
+                  const void* w_s, int64_t m, int64_t n, int64_t k, void* y, void* workspace, size_t ws_bytes,
+                  unsigned flags, mx_stream_t stream)
 {
     if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || a_fmt == MX_FMT_NVFP4 || w_fmt == MX_FMT_NVFP4)
         return MX_ERR_INVALID_ARG;
     if (!a_q || !a_s || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
-    if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
     if (flags & ~(MX_OUT_F32 | MX_FP8_FAST)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, 32);
     if (st != MX_OK) return st;
-    if (a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
-    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y))
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y) ||
+        (workspace && !aligned16(workspace)))
         return MX_ERR_ALIGN;
+    const size_t need = gemm_workspace_need(a_fmt, w_fmt, m, n, k, flags);
+    if (workspace && need > 0 && ws_bytes < need) return MX_ERR_WORKSPACE;
+    const MxPath path = mx_path(a_fmt, w_fmt, flags);
+    const int ab = bits_of(a_fmt), wb = bits_of(w_fmt);
+    if (path == PATH_SCALED && !mxl_mx_gemm_fits(ab, wb, m, n, k, 0)) return MX_ERR_UNSUPPORTED;
     if ((st = check_device()) != MX_OK) return st;
     const int f32 = (flags & MX_OUT_F32) ? 1 : 0;
-    const bool exact8 = a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST);
     if (log_enabled())
         std::fprintf(stderr, "[mxlinear] mx_gemm m=%lld n=%lld k=%lld -> %s\n", (long long)m, (long long)n,
                      (long long)k,
-                     exact8 ? mxl_mxfp8_exact_config_name() : mxl_mx_gemm_config_name(bits_of(a_fmt), m, n, k, 0));
+                     path == PATH_EXACT8 ? mxl_mxfp8_exact_config_name()
+                     : path == PATH_MIXED_EXACT ? mxl_mx_mixed_exact_config_name()
+                                                : mxl_mx_gemm_config_name(ab, wb, m, n, k, 0));
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (exact8)
+    if (path == PATH_EXACT8)
         return from_hip(mxl_launch_mxfp8_exact_gemm(a_q, a_s, w_q, w_s, m, n, k, y, f32, workspace, ws_bytes, hs));
-    return from_hip(mxl_launch_mx_gemm(bits_of(a_fmt), bits_of(w_fmt), a_q, a_s, w_q, w_s, m, n, k, y, f32,
-                                       workspace, ws_bytes, hs));
+    if (path == PATH_MIXED_EXACT)
+        return from_hip(mxl_launch_mx_mixed_exact_gemm(ab, a_q, a_s, w_q, w_s, m, n, k, y, f32, workspace,
+                                                       ws_bytes, hs));
+    return from_hip(mxl_launch_mx_gemm(ab, wb, a_q, a_s, w_q, w_s, m, n, k, y, f32, workspace, ws_bytes, hs));
 }
 
-mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf16, mx_format w_fmt,
+mx_status mx_gemm_fused(mx_format a_fmt, mx_format w_fmt, const void* a_bf16, mx_scale_rule a_rule,
                         const void* w_q, const void* w_s, int64_t m, int64_t n, int64_t k, void* y,
-                        unsigned flags, void* workspace, size_t ws_bytes, mx_stream_t stream)
+                        void* workspace, size_t ws_bytes, unsigned flags, mx_stream_t stream)
 {
     if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || a_fmt == MX_FMT_NVFP4 || w_fmt == MX_FMT_NVFP4 ||
         !valid_rule(a_rule))
@@ -214,32 +255,56 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf1
     if (flags & ~(MX_OUT_F32 | MX_FP8_FAST | MX_DEBUG_DUMP_AQ)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, 32);
     if (st != MX_OK) return st;
-    if (a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
-    if (!aligned16(a_bf16) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y)) return MX_ERR_ALIGN;
+    if (!aligned16(a_bf16) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y) ||
+        (workspace && !aligned16(workspace)))
+        return MX_ERR_ALIGN;
+    const int ab = bits_of(a_fmt), wb = bits_of(w_fmt);
+    const int f32 = (flags & MX_OUT_F32) ? 1 : 0;
+    const size_t need = fused_workspace_need(a_fmt, w_fmt, m, n, k, flags);
+    const size_t qb = (size_t)m * k * ab / 8;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+
+    if (a_fmt != w_fmt) {
+        // mixed pair: quantize A into the workspace, then the mixed GEMM reads it
+        if (!workspace || ws_bytes < need) return MX_ERR_WORKSPACE;
+        const MxPath path = mx_path(a_fmt, w_fmt, flags);
+        if (path == PATH_SCALED && !mxl_mx_gemm_fits(ab, wb, m, n, k, 0)) return MX_ERR_UNSUPPORTED;
+        if ((st = check_device()) != MX_OK) return st;
+        void* aq = workspace;
+        void* as = static_cast<uint8_t*>(workspace) + qb;
+        hipError_t e = mxl_launch_mx_quantize(a_fmt == MX_FMT_MXFP4 ? 0 : 1, (int)a_rule, a_bf16, m * k, aq, as, hs);
+        if (e != hipSuccess) return MX_ERR_HIP;
+        if (path == PATH_MIXED_EXACT)
+            return from_hip(mxl_launch_mx_mixed_exact_gemm(ab, aq, as, w_q, w_s, m, n, k, y, f32, nullptr, 0, hs));
+        return from_hip(mxl_launch_mx_gemm(ab, wb, aq, as, w_q, w_s, m, n, k, y, f32, nullptr, 0, hs));
+    }
+
     // debug dump of the prologue's codes and scales into the workspace
     void *dump_q = nullptr, *dump_s = nullptr;
+    bool use_ws = false;
     if (flags & MX_DEBUG_DUMP_AQ) {
-        const size_t qb = (size_t)m * k * bits_of(a_fmt) / 8, sb = (size_t)m * (k / 32);
-        if (!workspace || ws_bytes < qb + sb) return MX_ERR_WORKSPACE;
-        if (!aligned16(workspace)) return MX_ERR_ALIGN;
+        if (!workspace || ws_bytes < need) return MX_ERR_WORKSPACE;
         dump_q = workspace;
         dump_s = static_cast<uint8_t*>(workspace) + qb;
+    } else if (workspace && need > 0) {
+        if (ws_bytes < need) return MX_ERR_WORKSPACE;
+        if (!aligned256(workspace)) return MX_ERR_ALIGN;
+        use_ws = true;
     }
+    const bool exact8 = a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST);
+    // without the quantize-once workspace the in-tile prologue kernels run;
+    // the MX ones address operands with 32-bit offsets
+    if (!exact8 && !use_ws && !mxl_mx_gemm_fits(ab, wb, m, n, k, 1)) return MX_ERR_UNSUPPORTED;
     if ((st = check_device()) != MX_OK) return st;
-    const int f32 = (flags & MX_OUT_F32) ? 1 : 0;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
-    if (a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST)) {
-        const size_t pool = mxl_dq_pool_workspace(m, n, k);
-        if (!dump_q && pool > 0 && workspace && ws_bytes >= pool)
+    if (exact8) {
+        if (use_ws)
             return from_hip(mxl_launch_mxfp8_exact_gemm_pool((int)a_rule, a_bf16, w_q, w_s, m, n, k, y, f32,
                                                              workspace, ws_bytes, hs));
         return from_hip(mxl_launch_mxfp8_exact_gemm_fused((int)a_rule, a_bf16, w_q, w_s, m, n, k, y, f32, dump_q,
                                                           dump_s, hs));
     }
-    return from_hip(mxl_launch_mx_gemm_fused(bits_of(a_fmt), (int)a_rule, a_bf16, bits_of(w_fmt), w_q, w_s,
-                                             m, n, k, y, f32, dump_q, dump_s, dump_q ? nullptr : workspace,
-                                             dump_q ? 0 : ws_bytes, hs));
+    return from_hip(mxl_launch_mx_gemm_fused(ab, (int)a_rule, a_bf16, wb, w_q, w_s, m, n, k, y, f32, dump_q, dump_s,
+                                             use_ws ? workspace : nullptr, use_ws ? ws_bytes : 0, hs));
 }
 
 mx_status mx_gemm_fused_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k,
@@ -250,36 +315,32 @@ mx_status mx_gemm_fused_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t
     if (flags & ~(MX_OUT_F32 | MX_FP8_FAST | MX_DEBUG_DUMP_AQ)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, 32);
     if (st != MX_OK) return st;
-    if (a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
-    if (flags & MX_DEBUG_DUMP_AQ)
-        *bytes = 0;
-    else if (a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST))
-        *bytes = mxl_dq_pool_workspace(m, n, k);
-    else
-        *bytes = mxl_mx_gemm_fused_workspace(bits_of(a_fmt), m, n, k);
+    *bytes = fused_workspace_need(a_fmt, w_fmt, m, n, k, flags);
     return MX_OK;
 }
 
 mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t m, int64_t n,
-                  int64_t k, float alpha, void* y, unsigned flags, void* workspace, size_t ws_bytes,
+                  int64_t k, float alpha, void* y, void* workspace, size_t ws_bytes, unsigned flags,
                   mx_stream_t stream)
 {
     if (!a_q || !a_s || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
-    if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
     if (flags & ~MX_OUT_F32) return MX_ERR_INVALID_ARG;
     if (!std::isfinite(alpha)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, 16);
     if (st != MX_OK) return st;
-    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y))
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y) ||
+        (workspace && !aligned16(workspace)))
         return MX_ERR_ALIGN;
+    const size_t need = mxl_dq_workspace(m, n, k);
+    if (workspace && need > 0 && ws_bytes < need) return MX_ERR_WORKSPACE;
     if ((st = check_device()) != MX_OK) return st;
     return from_hip(mxl_launch_nv_gemm(a_q, a_s, w_q, w_s, m, n, k, alpha, y, (flags & MX_OUT_F32) ? 1 : 0,
                                        workspace, ws_bytes, static_cast<hipStream_t>(stream)));
 }
 
 mx_status mx_gemm_w4a16(mx_format w_fmt, const void* a_bf16, const void* w_q, const void* w_s, int64_t m,
-                        int64_t n, int64_t k, float alpha, void* y, unsigned flags, void* workspace,
-                        size_t ws_bytes, mx_stream_t stream)
+                        int64_t n, int64_t k, float alpha, void* y, void* workspace, size_t ws_bytes,
+                        unsigned flags, mx_stream_t stream)
 {
     if (!valid_fmt(w_fmt)) return MX_ERR_INVALID_ARG;
     if (w_fmt == MX_FMT_MXFP8) return MX_ERR_UNSUPPORTED;
@@ -291,6 +352,8 @@ mx_status mx_gemm_w4a16(mx_format w_fmt, const void* a_bf16, const void* w_q, co
     mx_status st = check_gemm_shape(m, n, k, nv ? 16 : 32);
     if (st != MX_OK) return st;
     if (!aligned16(a_bf16) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y)) return MX_ERR_ALIGN;
+    const size_t need = w4a16_use_decode(nv, m, n, k) ? 0 : mxl_dq_workspace(m, n, k);
+    if (workspace && need > 0 && ws_bytes < need) return MX_ERR_WORKSPACE;
     if ((st = check_device()) != MX_OK) return st;
     const int f32 = (flags & MX_OUT_F32) ? 1 : 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -308,9 +371,7 @@ mx_status mx_gemm_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t m, in
     if (nv != (w_fmt == MX_FMT_NVFP4)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, nv ? 16 : 32);
     if (st != MX_OK) return st;
-    if (!nv && a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
-    const bool dq = nv || (a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST));
-    *bytes = dq ? mxl_dq_workspace(m, n, k) : mxl_mx_gemm_workspace(bits_of(a_fmt), m, n, k);
+    *bytes = nv ? mxl_dq_workspace(m, n, k) : gemm_workspace_need(a_fmt, w_fmt, m, n, k, flags);
     return MX_OK;
 }
 
@@ -445,18 +506,23 @@ mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, i
     if (nv != (w_fmt == MX_FMT_NVFP4)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, nv ? 16 : 32);
     if (st != MX_OK) return st;
-    if (!nv && a_fmt != w_fmt) return MX_ERR_UNSUPPORTED;
-    const char* fmt = nv ? "nvfp4" : (a_fmt == MX_FMT_MXFP4 ? "mxfp4" : "mxfp8");
-    const bool exact8 = a_fmt == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST);
+    static const char* names[3] = {"mxfp4", "mxfp8", "nvfp4"};
+    char fmt[16];
+    if (a_fmt == w_fmt) std::snprintf(fmt, sizeof fmt, "%s", names[a_fmt]);
+    else std::snprintf(fmt, sizeof fmt, "%sx%s", names[a_fmt], names[w_fmt]);
+    const MxPath path = nv ? PATH_EXACT8 : mx_path(a_fmt, w_fmt, flags);
     const char* cfg = nv ? mxl_nv_gemm_config_name()
-                         : (exact8 ? mxl_mxfp8_exact_config_name()
-                                   : mxl_mx_gemm_config_name(bits_of(a_fmt), m, n, k, fused));
-    const int splits = (nv || exact8) && !fused ? mxl_dq_splits(m, n, k) : 1;
+                    : path == PATH_EXACT8 ? mxl_mxfp8_exact_config_name()
+                    : path == PATH_MIXED_EXACT ? mxl_mx_mixed_exact_config_name()
+                                               : mxl_mx_gemm_config_name(bits_of(a_fmt), bits_of(w_fmt), m, n, k,
+                                                                         fused && a_fmt == w_fmt);
+    const int splits = (nv || path != PATH_SCALED) && !fused ? mxl_dq_splits(m, n, k) : 1;
+    const char* pre = !fused || nv ? "" : a_fmt != w_fmt ? "fused-quant (mx_quantize_act into the workspace, then) "
+                                                         : "fused-quant ";
     if (splits > 1)
-        std::snprintf(name, len, "%s%s %s, split-K %d with a workspace, else one split",
-                      fused && !nv ? "fused-quant " : "", fmt, cfg, splits);
+        std::snprintf(name, len, "%s%s %s, split-K %d with a workspace, else one split", pre, fmt, cfg, splits);
     else
-        std::snprintf(name, len, "%s%s %s", fused && !nv ? "fused-quant " : "", fmt, cfg);
+        std::snprintf(name, len, "%s%s %s", pre, fmt, cfg);
     return MX_OK;
 }
 

@@ -7,6 +7,8 @@
 //   MXFP8: Y = sum_k (e4m3_a * 2^ea) * (e4m3_w * 2^ew), E8M0 scale per 32 -> bf16
 //   W4A16: Y = alpha * sum_k a_bf16 * dq(w), w MXFP4 (e2m1 * 2^ew, alpha = 1)
 //          or NVFP4 (e2m1 * s_w, alpha = 1 / g_w)                    -> bf16
+//   mixed MX pairs: A MXFP8 x W MXFP4 or A MXFP4 x W MXFP8, each operand
+//          dequantized by its own format                              -> bf16
 //
 // Operations: the NVFP4 W4A4 path of Qwen3.5-27B-NVFP4-GPTQ and
 // Qwen3.5-27B-NVFP4-RTN-weight-only (introductions: FP4 elements, per-block
@@ -34,9 +36,11 @@
 // and the 8 consecutive K elements [8g, 8g + 8) of the 16-wide step.
 #include "mx_device.h"
 
+#include <type_traits>
+
 namespace mxl {
 
-enum : int { DQ_NVFP4 = 0, DQ_MXFP8 = 1, DQ_MXFP4 = 2 };   // format of W (and of A unless A is bf16)
+enum : int { DQ_NVFP4 = 0, DQ_MXFP8 = 1, DQ_MXFP4 = 2 };   // format of W (and of A unless A is bf16 or KA says otherwise)
 
 constexpr int DQ_BK = 64;                 // K elements per LDS stage
 constexpr int DQ_ROW_BYTES = DQ_BK * 2;   // 16-bit bytes per LDS row per stage (8 chunks)
@@ -191,8 +195,10 @@ struct DqArgs {
 // write-back) before counting it; readers poll with device-scope atomic loads
 // and need no invalidation: a block is read only after it is done, and no L2
 // holds its lines from before in this launch (blocks start on cache-line
-// boundaries: 128 rows of k code bytes and of k/32 scale bytes, k % 128 == 0).
-// Polls are bounded (about 0.5 s, then the error word; the tile is skipped).
+// boundaries: the workspace is 256-byte aligned, the scale plane starts at a
+// 256-byte boundary, and a block is 128 rows of k code bytes and of k/32
+// scale bytes, k % 128 == 0).  Polls are bounded (about 0.5 s); a tile that
+// gives up sets the error word and fills its part of Y with NaN.
 // ---------------------------------------------------------------------------
 constexpr int DQ_POOL_ROWS = 32;               // rows per chunk
 constexpr int DQ_POOL_SPINS = 1 << 21;
@@ -271,6 +277,10 @@ __device__ __forceinline__ bool dq_pool_ensure(const DqArgs& p, int tm, uint8_t*
 // codes) and dequantized back exactly, as mx_quantize_act would have done.
 // A_RAW (W4A16): A arrives as bf16 [M, K] and is staged as it is; W is
 // MXFP4 or NVFP4 and is dequantized to bf16.
+// KA: the format of quantized A when it differs from W's (mixed MX pairs:
+// MXFP8 A with MXFP4 W, or MXFP4 A with MXFP8 W; both scale per 32, so the
+// scale layout and K tiling are shared and each operand is dequantized to
+// bf16 by its own format); -1 means the same format as W.
 // ODD16 (NVFP4 with K % 32 == 16): rows are only 8-byte aligned and the
 // last chunk of a row holds a single block of 16 elements.  SCW (NVFP4 with
 // K % 64 == 0, MXFP8 with K % 128 == 0): scale bytes are fetched as the
@@ -279,22 +289,28 @@ __device__ __forceinline__ bool dq_pool_ensure(const DqArgs& p, int tm, uint8_t*
 // the compiler waits for a byte load's zero extension right after the load,
 // a dword needs none.
 template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL,
-          bool ODD16 = false, bool SCW = false, bool A_RAW = false, bool POOL = false>
+          bool ODD16 = false, bool SCW = false, bool A_RAW = false, bool POOL = false, int KA = -1>
 __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
 {
-    static_assert(!POOL || (KIND == DQ_MXFP8 && !FUSED_A && !A_RAW), "the pool quantizes MXFP8 A");
-    using T = DqTraits<KIND>;
+    constexpr int KAQ = KA < 0 ? KIND : KA;   // format of quantized A
+    static_assert(!POOL || (KIND == DQ_MXFP8 && KAQ == KIND && !FUSED_A && !A_RAW), "the pool quantizes MXFP8 A");
+    using T = DqTraits<KIND>;                 // W
+    using TA = DqTraits<KAQ>;                 // quantized A
+    static_assert(KAQ == KIND || (KAQ != DQ_NVFP4 && KIND != DQ_NVFP4 && !FUSED_A && !A_RAW),
+                  "mixed pairs are MX formats with quantized A");
     static_assert(!FUSED_A || KIND == DQ_MXFP8, "fused quantization is for MXFP8");
     static_assert(!A_RAW || KIND != DQ_MXFP8, "W4A16 weights are MXFP4 or NVFP4");
-    static_assert(A_RAW || KIND != DQ_MXFP4, "MXFP4 x MXFP4 runs on the FP4 matrix cores");
+    static_assert(A_RAW || KIND != DQ_MXFP4 || KAQ != DQ_MXFP4, "MXFP4 x MXFP4 runs on the FP4 matrix cores");
     constexpr bool A_BF16 = FUSED_A || A_RAW;       // A arrives as bf16
     constexpr bool F16 = KIND == DQ_NVFP4 && !A_RAW;  // f16 matrix cores (NVFP4 W4A4), else bf16
     constexpr int NT = WM * WN * 64;
     constexpr int A_TILE = BM * DQ_ROW_BYTES, W_TILE = BN * DQ_ROW_BYTES;
     constexpr int STAGE = A_TILE + W_TILE;
     constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
-    constexpr int A_CPR = A_BF16 ? DQ_BK * 2 / 16 : T::CHUNKS;   // A chunks per row per stage
+    constexpr int A_CPR = A_BF16 ? DQ_BK * 2 / 16 : TA::CHUNKS;  // A chunks per row per stage
     constexpr int A_CH = BM * A_CPR, W_CH = BN * T::CHUNKS;
+    using KindW = std::integral_constant<int, KIND>;
+    using KindA = std::integral_constant<int, KAQ>;
     static_assert(!A_BF16 || (A_CH % NT == 0 && NT % A_CPR == 0), "bf16 A tile mapping");
     constexpr int A_PER_T = (A_CH + NT - 1) / NT, W_PER_T = (W_CH + NT - 1) / NT;
 
@@ -308,11 +324,14 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int K = p.K, KS = K / T::SCALE_BLOCK;
-    const int row_bytes = KIND == DQ_MXFP8 ? K : K / 2;   // W (and quantized A) bytes per row
+    auto row_bytes_of = [K](int kind) { return kind == DQ_MXFP8 ? K : K / 2; };   // code bytes per row
     const int kt0 = split * p.chunk;                                // even: set parity = stage parity
     const int nk = min(p.chunk, (K + DQ_BK - 1) / DQ_BK - kt0);     // stages of this split
     if constexpr (POOL) {
-        if (!dq_pool_ensure<A_RULE, BM, NT>(p, tm, smem)) return;
+        if (!dq_pool_ensure<A_RULE, BM, NT>(p, tm, smem)) {
+            fill_tile_nan(p.y, p.M, p.N, m0, n0, BM, BN, OUT_F32);
+            return;
+        }
     }
 
     // two register sets of staged chunks: stage kt lives in set kt % 2.
@@ -324,11 +343,14 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
     uint32_t sa[2][A_PER_T][2], sw[2][W_PER_T][2];   // scale bytes of the chunk (MXFP8: one)
     uint32_t fa[2][A_PER_T], fw[2][W_PER_T];         // flags: 1 chunk, 2 its second 8 bytes, 4 second scale
 
-    auto load_one = [&](const uint8_t* q, const uint8_t* s, int rows_lim, int r0, int qi, int kt,
+    auto load_one = [&](auto kind, const uint8_t* q, const uint8_t* s, int rows_lim, int r0, int qi, int kt,
                         uint4& v, uint32_t* sc, uint32_t& fl) __attribute__((always_inline)) {
-        const int row = qi / T::CHUNKS, c = qi % T::CHUNKS;
+        constexpr int KK = decltype(kind)::value;
+        using TK = DqTraits<KK>;
+        const int row_bytes = row_bytes_of(KK);
+        const int row = qi / TK::CHUNKS, c = qi % TK::CHUNKS;
         const int gr = r0 + row;
-        const int kb = kt * T::SRC_ROW_BYTES + c * 16;
+        const int kb = kt * TK::SRC_ROW_BYTES + c * 16;
         const bool ok = gr < rows_lim && kb < row_bytes;
         const size_t rb = ok ? (size_t)gr * row_bytes + kb : 0;
         if (!ODD16) {
@@ -342,17 +364,17 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
             fl = (ok ? 1u : 0u) | (ok_hi ? 2u : 0u);
         }
         if (SCW) {
-            const size_t so = KIND == DQ_NVFP4 ? (size_t)gr * KS + kt * 4 : (size_t)gr * KS + (kt >> 1) * 4;
+            const size_t so = KK == DQ_NVFP4 ? (size_t)gr * KS + kt * 4 : (size_t)gr * KS + (kt >> 1) * 4;
             sc[0] = *reinterpret_cast<const uint32_t*>(s + (ok ? so : 0));
             fl |= ok ? 4u : 0u;
-        } else if (KIND == DQ_NVFP4) {
+        } else if (KK == DQ_NVFP4) {
             const int blk = kt * (DQ_BK / 16) + c * 2;
             const bool ok1 = ok && blk + 1 < KS;
             sc[0] = s[ok ? (size_t)gr * KS + blk : 0];
             sc[1] = s[ok1 ? (size_t)gr * KS + blk + 1 : 0];
             fl |= ok1 ? 4u : 0u;
         } else {
-            sc[0] = s[ok ? (size_t)gr * KS + (kt * DQ_BK + c * T::ELEMS_PER_CHUNK) / 32 : 0];
+            sc[0] = s[ok ? (size_t)gr * KS + (kt * DQ_BK + c * TK::ELEMS_PER_CHUNK) / 32 : 0];
         }
     };
     auto load_stage = [&](int kt, int set) __attribute__((always_inline)) {
@@ -366,21 +388,24 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
                 ra[set][i] = *reinterpret_cast<const uint4*>(p.a_q + (ok ? (size_t)gm * K * 2 + kb : 0));
                 fa[set][i] = ok ? 3u : 0u;
             } else if (A_CH % NT == 0 || qi < A_CH) {
-                load_one(p.a_q, p.a_s, p.M, m0, qi, kt, ra[set][i], sa[set][i], fa[set][i]);
+                load_one(KindA{}, p.a_q, p.a_s, p.M, m0, qi, kt, ra[set][i], sa[set][i], fa[set][i]);
             }
         }
 #pragma unroll
         for (int i = 0; i < W_PER_T; ++i) {
             const int qi = tid + i * NT;
-            if (W_CH % NT == 0 || qi < W_CH) load_one(p.w_q, p.w_s, p.N, n0, qi, kt, rw[set][i], sw[set][i], fw[set][i]);
+            if (W_CH % NT == 0 || qi < W_CH)
+                load_one(KindW{}, p.w_q, p.w_s, p.N, n0, qi, kt, rw[set][i], sw[set][i], fw[set][i]);
         }
     };
-    auto store_one = [&](uint8_t* tile, int qi, uint4 v, const uint32_t* scb, uint32_t fl, int par)
+    auto store_one = [&](auto kind, uint8_t* tile, int qi, uint4 v, const uint32_t* scb, uint32_t fl, int par)
                          __attribute__((always_inline)) {
-        const int row = qi / T::CHUNKS, c = qi % T::CHUNKS;
+        constexpr int KK = decltype(kind)::value;
+        using TK = DqTraits<KK>;
+        const int row = qi / TK::CHUNKS, c = qi % TK::CHUNKS;
         if (!(fl & 1u)) v = make_uint4(0, 0, 0, 0);
         if (!(fl & 2u)) v.z = v.w = 0;
-        if (KIND == DQ_NVFP4) {
+        if (KK == DQ_NVFP4) {
             const uint32_t sc = SCW ? (fl & 1u ? __builtin_amdgcn_ubfe(scb[0], 16 * c, 16) : 0u)
                                     : (fl & 1u ? scb[0] : 0u) | (fl & 4u ? scb[1] << 8 : 0u);
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -401,7 +426,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
                     *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + chunk * 16) = d;
                 }
             }
-        } else if (KIND == DQ_MXFP4) {
+        } else if (KK == DQ_MXFP4) {
             const uint32_t sb = SCW ? __builtin_amdgcn_ubfe(scb[0], 16 * par + 8 * c, 8) : scb[0];
             const int e = (fl & 1u ? (int)sb : 127) - 127;
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -445,13 +470,13 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
                 }
                 *reinterpret_cast<uint4*>(a_t + row * DQ_ROW_BYTES + ((c ^ dq_swz(row)) * 16)) = d;
             } else if (A_CH % NT == 0 || qi < A_CH) {
-                store_one(a_t, qi, ra[set][i], sa[set][i], fa[set][i], set);
+                store_one(KindA{}, a_t, qi, ra[set][i], sa[set][i], fa[set][i], set);
             }
         }
 #pragma unroll
         for (int i = 0; i < W_PER_T; ++i) {
             const int qi = tid + i * NT;
-            if (W_CH % NT == 0 || qi < W_CH) store_one(w_t, qi, rw[set][i], sw[set][i], fw[set][i], set);
+            if (W_CH % NT == 0 || qi < W_CH) store_one(KindW{}, w_t, qi, rw[set][i], sw[set][i], fw[set][i], set);
         }
     };
 
@@ -560,11 +585,11 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
 }
 
 template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL,
-          bool ODD16 = false, bool SCW = false, bool A_RAW = false, bool POOL = false>
+          bool ODD16 = false, bool SCW = false, bool A_RAW = false, bool POOL = false, int KA = -1>
 hipError_t launch_dq_k(const DqArgs& a, hipStream_t stream)
 {
     constexpr int LDS = 2 * (BM + BN) * DQ_ROW_BYTES;
-    auto kern = dq_gemm_kernel<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, ODD16, SCW, A_RAW, POOL>;
+    auto kern = dq_gemm_kernel<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, ODD16, SCW, A_RAW, POOL, KA>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
@@ -577,7 +602,7 @@ hipError_t launch_dq_k(const DqArgs& a, hipStream_t stream)
 }
 
 template <int KIND, int BM, int BN, int WM, int WN, bool OUT_F32, bool FUSED_A = false, int A_RULE = RULE_CEIL,
-          bool A_RAW = false>
+          bool A_RAW = false, int KA = -1>
 hipError_t launch_dq(const DqArgs& a, hipStream_t stream)
 {
     if constexpr (KIND == DQ_NVFP4) {
@@ -587,9 +612,9 @@ hipError_t launch_dq(const DqArgs& a, hipStream_t stream)
             return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, true, A_RAW>(a, stream);
     } else if (!FUSED_A) {
         if (a.K % 128 == 0)
-            return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, true, A_RAW>(a, stream);
+            return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, true, A_RAW, false, KA>(a, stream);
     }
-    return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, false, A_RAW>(a, stream);
+    return launch_dq_k<KIND, BM, BN, WM, WN, OUT_F32, FUSED_A, A_RULE, false, false, A_RAW, false, KA>(a, stream);
 }
 
 } // namespace mxl
@@ -669,6 +694,31 @@ extern "C" hipError_t mxl_launch_mxfp8_exact_gemm(const void* aq, const void* as
     });
 }
 
+// Mixed MX pairs, exact: A codes of a_bits (8: E4M3, 4: E2M1), W codes of
+// the other width, each dequantized to bf16 by its own format.
+extern "C" hipError_t mxl_launch_mx_mixed_exact_gemm(int a_bits, const void* aq, const void* as, const void* wq,
+                                                     const void* ws, int64_t m, int64_t n, int64_t k, void* y,
+                                                     int out_f32, void* work, size_t work_bytes, hipStream_t stream)
+{
+    DqArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
+             static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
+             (int)m, (int)n, (int)k, 1.0f};
+    return dq_run(a, out_f32, work, work_bytes, stream, [&](const DqArgs& x, int f32) {
+        if (a_bits == 8) {   // A MXFP8, W MXFP4
+            if (f32) return launch_dq<DQ_MXFP4, 128, 128, 2, 2, true, false, RULE_CEIL, false, DQ_MXFP8>(x, stream);
+            return launch_dq<DQ_MXFP4, 128, 128, 2, 2, false, false, RULE_CEIL, false, DQ_MXFP8>(x, stream);
+        }
+        if (f32) return launch_dq<DQ_MXFP8, 128, 128, 2, 2, true, false, RULE_CEIL, false, DQ_MXFP4>(x, stream);
+        return launch_dq<DQ_MXFP8, 128, 128, 2, 2, false, false, RULE_CEIL, false, DQ_MXFP4>(x, stream);
+    });
+}
+
+extern "C" const char* mxl_mx_mixed_exact_config_name(void)
+{
+    return "dq_gemm_kernel<mxfp8 x mxfp4 -> exact bf16 per operand, tile 128x128x64, 2x2 waves of 64x64, "
+           "bf16 mfma 32x32x16>";
+}
+
 template <int RULE>
 static hipError_t fused8(const DqArgs& a, int out_f32, hipStream_t stream)
 {
@@ -708,12 +758,15 @@ extern "C" hipError_t mxl_launch_w4a16_gemm(int w_nv, const void* a_bf16, const 
 }
 
 // ---- the quantize-once fused MXFP8 GEMM (POOL) ----
-// Workspace: A codes [m, k], E8M0 scales [m, k/32] (mx_quantize_act's
-// layout), then at a 256-byte boundary the pool counter, a done counter per
-// 128-row block and an error word.
+// Workspace (256-byte aligned base): A codes [m, k] at 0, E8M0 scales
+// [m, k/32] (mx_quantize_act's layout) at the next 256-byte boundary, then at
+// the next one the pool counter, a done counter per 128-row block and an
+// error word.
+static size_t dq_align256(size_t v) { return (v + 255) & ~(size_t)255; }
+static size_t dq_pool_scale_offset(int64_t m, int64_t k) { return dq_align256((size_t)m * k); }
 static size_t dq_pool_state_offset(int64_t m, int64_t k)
 {
-    return ((size_t)m * k + (size_t)m * (k / 32) + 255) & ~(size_t)255;
+    return dq_align256(dq_pool_scale_offset(m, k) + (size_t)m * (k / 32));
 }
 
 // Used for k % 128 == 0 and n > 256 (with fewer tile columns the in-tile
@@ -739,7 +792,7 @@ static hipError_t pool8(const DqArgs& a, int out_f32, hipStream_t stream)
 }
 
 // The fused MXFP8 GEMM with A quantized once into `work` (at least
-// mxl_dq_pool_workspace bytes, 16-byte aligned; calls sharing it must not
+// mxl_dq_pool_workspace bytes, 256-byte aligned; calls sharing it must not
 // overlap) by the GEMM's own workgroups.  Y equals mx_quantize_act followed
 // by the unsplit mx_gemm.
 extern "C" hipError_t mxl_launch_mxfp8_exact_gemm_pool(int a_rule, const void* a_bf16, const void* wq,
@@ -748,14 +801,15 @@ extern "C" hipError_t mxl_launch_mxfp8_exact_gemm_pool(int a_rule, const void* a
                                                        hipStream_t stream)
 {
     const size_t need = mxl_dq_pool_workspace(m, n, k);
-    if (need == 0 || !work || work_bytes < need) return hipErrorInvalidValue;
+    if (need == 0 || !work || work_bytes < need || (reinterpret_cast<uintptr_t>(work) & 255))
+        return hipErrorInvalidValue;
     uint8_t* w8 = static_cast<uint8_t*>(work);
     const int nb = (int)((m + 127) / 128);
     int* state = reinterpret_cast<int*>(w8 + dq_pool_state_offset(m, k));
     hipLaunchKernelGGL(dq_pool_zero_kernel, dim3((nb + 2 + 255) / 256), dim3(256), 0, stream, state, nb + 2);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    DqArgs a{w8, w8 + (size_t)m * k, static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
+    DqArgs a{w8, w8 + dq_pool_scale_offset(m, k), static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
              (int)m, (int)n, (int)k, 1.0f, nullptr, 1, 1 << 30, nullptr, nullptr,
              static_cast<const uint4*>(a_bf16), state, nb};
     if (a_rule == RULE_CEIL) return pool8<RULE_CEIL>(a, out_f32, stream);

@@ -926,8 +926,9 @@ using namespace mxl;
 //   default : everything else                      -> 128x128 tiles, 2x2 waves of 64x64
 enum ShapeClass { SC_DECODE, SC_LARGE, SC_DEFAULT };
 
-static ShapeClass classify(int a_bits, int64_t m, int64_t n, int64_t k, bool fused)
+static ShapeClass classify(int a_bits, int w_bits, int64_t m, int64_t n, int64_t k, bool fused)
 {
+    if (a_bits != 4 || w_bits != 4) return SC_DEFAULT;   // MXFP8 and mixed pairs: the 128 x 128 tile kernel
     // up to three 16-row A fragments: with a fourth the LDS-block kernel
     // needs 296 VGPRs (one wave per SIMD) and loses to the tile kernel
     if (!fused && a_bits == 4 && m <= 48) return SC_DECODE;
@@ -938,7 +939,7 @@ static ShapeClass classify(int a_bits, int64_t m, int64_t n, int64_t k, bool fus
 template <int AB, int WB, bool FUSED, int RULE, bool F32>
 static hipError_t dispatch_tile(const GemmArgs& a, ShapeClass sc, hipStream_t s)
 {
-    if constexpr (AB == 4) if (sc == SC_LARGE)
+    if constexpr (AB == 4 && WB == 4) if (sc == SC_LARGE)
         return launch_tile<AB, WB, 256, 256, 2, 2, FUSED, RULE, F32, FUSED ? 1 : 3, true>(a, s);
     if constexpr (!FUSED) if (a.K % BK == 0)   // whole stages: dword scale loads, two stages in flight
         return launch_tile<AB, WB, 128, 128, 2, 2, FUSED, RULE, F32, 3, true>(a, s);
@@ -966,9 +967,9 @@ extern "C" hipError_t mxl_launch_mx_prefill(const void* aq, const void* as, cons
                                             hipStream_t stream);
 
 // Workspace bytes mx_gemm can use for split-K on this shape (0: none).
-extern "C" size_t mxl_mx_gemm_workspace(int a_bits, int64_t m, int64_t n, int64_t k)
+extern "C" size_t mxl_mx_gemm_workspace(int a_bits, int w_bits, int64_t m, int64_t n, int64_t k)
 {
-    if (classify(a_bits, m, n, k, false) != SC_DEFAULT) return 0;
+    if (classify(a_bits, w_bits, m, n, k, false) != SC_DEFAULT) return 0;
     int chunk;
     const int s = default_splits(m, n, k, &chunk);
     return s > 1 ? (size_t)s * m * n * sizeof(float) : 0;
@@ -982,7 +983,7 @@ extern "C" hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq,
     GemmArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
                static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k,
                nullptr, 1, 1 << 30, nullptr, nullptr};
-    const ShapeClass sc = classify(a_bits, m, n, k, false);
+    const ShapeClass sc = classify(a_bits, w_bits, m, n, k, false);
     if (sc == SC_DEFAULT && work) {
         int chunk;
         const int splits = default_splits(m, n, k, &chunk);
@@ -993,6 +994,8 @@ extern "C" hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq,
             hipError_t e = hipErrorInvalidValue;
             if (a_bits == 4 && w_bits == 4) e = dispatch_out<4, 4, false, RULE_CEIL>(a, sc, true, stream);
             else if (a_bits == 8 && w_bits == 8) e = dispatch_out<8, 8, false, RULE_CEIL>(a, sc, true, stream);
+            else if (a_bits == 8 && w_bits == 4) e = dispatch_out<8, 4, false, RULE_CEIL>(a, sc, true, stream);
+            else if (a_bits == 4 && w_bits == 8) e = dispatch_out<4, 8, false, RULE_CEIL>(a, sc, true, stream);
             if (e != hipSuccess) return e;
             return mxl_launch_splitk_reduce(a.part, splits, m * n, 1.0f, y, out_f32, stream);
         }
@@ -1006,7 +1009,23 @@ extern "C" hipError_t mxl_launch_mx_gemm(int a_bits, int w_bits, const void* aq,
     }
     if (a_bits == 4 && w_bits == 4) return dispatch_out<4, 4, false, RULE_CEIL>(a, sc, out_f32, stream);
     if (a_bits == 8 && w_bits == 8) return dispatch_out<8, 8, false, RULE_CEIL>(a, sc, out_f32, stream);
+    if (a_bits == 8 && w_bits == 4) return dispatch_out<8, 4, false, RULE_CEIL>(a, sc, out_f32, stream);
+    if (a_bits == 4 && w_bits == 8) return dispatch_out<4, 8, false, RULE_CEIL>(a, sc, out_f32, stream);
     return hipErrorInvalidValue;
+}
+
+// Whether the kernel that mx_gemm (fused_in_tile: mx_gemm_fused with the
+// in-tile prologue) selects for this shape can address its operands.  The
+// prefill kernel checks its own limits (mxl_prefill_ok); the tile and decode
+// kernels take 32-bit byte offsets and buffer sizes, so their operands (plus
+// one tile of overrun rows) must stay below 2 GiB.
+extern "C" int mxl_mx_gemm_fits(int a_bits, int w_bits, int64_t m, int64_t n, int64_t k, int fused_in_tile)
+{
+    const ShapeClass sc = classify(a_bits, w_bits, m, n, k, fused_in_tile != 0);
+    if (!fused_in_tile && sc == SC_LARGE && mxl_prefill_ok(m, n, k)) return 1;
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t a_row = fused_in_tile ? 2 * k : k * a_bits / 8, w_row = k * w_bits / 8;
+    return (m + 256) * a_row < lim && (n + 256) * w_row < lim ? 1 : 0;
 }
 
 extern "C" size_t mxl_prefill_fq_workspace(int64_t m, int64_t k);
@@ -1018,7 +1037,7 @@ extern "C" hipError_t mxl_launch_mx_prefill_fq(int a_rule, const void* a_bf16, c
 // launch for large MXFP4 shapes (0: none).
 extern "C" size_t mxl_mx_gemm_fused_workspace(int a_bits, int64_t m, int64_t n, int64_t k)
 {
-    if (a_bits == 4 && classify(4, m, n, k, true) == SC_LARGE && mxl_prefill_ok(m, n, k))
+    if (a_bits == 4 && classify(4, 4, m, n, k, true) == SC_LARGE && mxl_prefill_ok(m, n, k))
         return mxl_prefill_fq_workspace(m, k);
     return 0;
 }
@@ -1042,7 +1061,7 @@ extern "C" hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const voi
                static_cast<uint8_t*>(dump_q), static_cast<uint8_t*>(dump_s)};
     // the dump is built into the 128 x 128 fused kernel only (the 256 x 256
     // one has no registers to spare); both accumulate alike
-    const ShapeClass sc = dump_q ? SC_DEFAULT : classify(a_bits, m, n, k, true);
+    const ShapeClass sc = dump_q ? SC_DEFAULT : classify(a_bits, w_bits, m, n, k, true);
     if (a_bits == 4 && w_bits == 4) {
         if (a_rule == RULE_CEIL) return dispatch_out<4, 4, true, RULE_CEIL>(a, sc, out_f32, stream);
         if (a_rule == RULE_FLOOR) return dispatch_out<4, 4, true, RULE_FLOOR>(a, sc, out_f32, stream);
@@ -1056,9 +1075,9 @@ extern "C" hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const voi
     return hipErrorInvalidValue;
 }
 
-extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int64_t m, int64_t n, int64_t k, int fused)
+extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int w_bits, int64_t m, int64_t n, int64_t k, int fused)
 {
-    switch (classify(a_bits, m, n, k, fused != 0)) {
+    switch (classify(a_bits, w_bits, m, n, k, fused != 0)) {
     case SC_DECODE:
         switch (decode_kind(m, k)) {
         case 2: return "mx_decode_kernel<16 W rows per workgroup, whole-row copies into swizzled LDS, 4 waves over K "

@@ -203,9 +203,12 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
 // atomic loads and needs no invalidation: the codes are read only after their
 // block is done, no L2 holds lines of the block from before (the launch
 // starts with the caches' acquire, the region is written only here, and
-// blocks start on cache-line boundaries: 256 rows of k/2 code bytes and of
-// k/32 scale bytes, k % 128 == 0).  Every poll is bounded (about 0.5 s, then an
-// error word and the tile is skipped), so that no mistake can hang the GPU.
+// blocks start on cache-line boundaries: the workspace is 256-byte aligned,
+// the scale plane starts at the next 256-byte boundary after the codes, and a
+// block holds 256 rows of k/2 code bytes and of k/32 scale bytes, k % 128 ==
+// 0, so no cache line holds bytes of two blocks).  Every poll is bounded
+// (about 0.5 s); a tile that gives up sets the error word and fills its part
+// of Y with NaN, so that no mistake can hang the GPU or pass for a result.
 // ---------------------------------------------------------------------------
 constexpr int PF_FQ_CHUNK_ROWS = 32;
 constexpr int PF_FQ_SPINS = 1 << 21;           // x s_sleep(4): about 0.5 s
@@ -301,7 +304,11 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_fq_kernel(PrefillArgs 
     const int tile_t = pf_xcd_order(p.count);
     int tm, tn;
     pf_tile(p.tile_base + (BN == 256 ? tile_t : tile_t / 2), p.M, p.N, tm, tn);
-    if (!pf_ensure_block<RULE>(p, a_bf16, state, nb, tm, smem)) return;
+    if (!pf_ensure_block<RULE>(p, a_bf16, state, nb, tm, smem)) {
+        fill_tile_nan(p.y, p.M, p.N, tm * PF_BM, tn * 256 + (BN == 256 ? 0 : (tile_t % 2) * 128), PF_BM, BN,
+                      OUT_F32);
+        return;
+    }
 #define PF_TILE_T tile_t
 #include "gemm_prefill_tile.inc"
 #undef PF_TILE_T
@@ -365,13 +372,15 @@ __global__ void pf_zero_kernel(int* p, int n)
     if (i < n) p[i] = 0;
 }
 
-// Workspace layout of the quantize-once launches: A codes [m, k/2], E8M0
-// scales [m, k/32] (mx_quantize_act's layout), then at a 256-byte boundary
-// the state: the chunk pool counter, a done counter per 256-row block, and an
-// error word.
+// Workspace layout of the quantize-once launches (256-byte aligned base): A
+// codes [m, k/2] at 0, E8M0 scales [m, k/32] (mx_quantize_act's layout) at
+// the next 256-byte boundary, then at the next one the state: the chunk pool
+// counter, a done counter per 256-row block, and an error word.
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+static size_t prefill_fq_scale_offset(int64_t m, int64_t k) { return align256((size_t)m * (k / 2)); }
 static size_t prefill_fq_state_offset(int64_t m, int64_t k)
 {
-    return ((size_t)m * (k / 2) + (size_t)m * (k / 32) + 255) & ~(size_t)255;
+    return align256(prefill_fq_scale_offset(m, k) + (size_t)m * (k / 32));
 }
 
 template <bool OUT_F32, int BN, int RULE>
@@ -422,15 +431,17 @@ extern "C" size_t mxl_prefill_fq_workspace(int64_t m, int64_t k)
 }
 
 // The quantize-once fused GEMM: A bf16 [m, k] quantized with rule a_rule
-// (MXFP4) into `work` (at least mxl_prefill_fq_workspace bytes, 16-byte
+// (MXFP4) into `work` (at least mxl_prefill_fq_workspace bytes, 256-byte
 // aligned; calls sharing it must not overlap), and Y = A W^T.
 extern "C" hipError_t mxl_launch_mx_prefill_fq(int a_rule, const void* a_bf16, const void* wq, const void* ws,
                                                int64_t m, int64_t n, int64_t k, void* y, int out_f32, void* work,
                                                size_t work_bytes, hipStream_t stream)
 {
-    if (!work || work_bytes < mxl_prefill_fq_workspace(m, k)) return hipErrorInvalidValue;
+    if (!work || work_bytes < mxl_prefill_fq_workspace(m, k) || (reinterpret_cast<uintptr_t>(work) & 255))
+        return hipErrorInvalidValue;
     uint8_t* w8 = static_cast<uint8_t*>(work);
-    PrefillArgs a{w8, w8 + (size_t)m * (k / 2), static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
+    PrefillArgs a{w8, w8 + prefill_fq_scale_offset(m, k), static_cast<const uint8_t*>(wq),
+                  static_cast<const uint8_t*>(ws),
                   y, nullptr, nullptr, (int)m, (int)n, (int)k, 0, 0};
     int* state = reinterpret_cast<int*>(w8 + prefill_fq_state_offset(m, k));
     if (a_rule == RULE_CEIL)

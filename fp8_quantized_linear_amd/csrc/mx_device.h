@@ -298,6 +298,21 @@ __device__ __forceinline__ int4_t make_rsrc(const void* base, uint32_t bytes)
     return v;
 }
 
+// Fills the part of Y[M, N] (bf16, or fp32 when f32) covered by the tile
+// [m0, m0 + bm) x [n0, n0 + bn) with NaN, from all threads of the
+// workgroup.  A tile whose bounded wait for another workgroup gave up writes
+// this instead of its product, so the failure cannot pass for a result.
+__device__ __forceinline__ void fill_tile_nan(void* y, int M, int N, int m0, int n0, int bm, int bn, bool f32)
+{
+    for (int idx = threadIdx.x; idx < bm * bn; idx += blockDim.x) {
+        const int m = m0 + idx / bn, n = n0 + idx % bn;
+        if (m < M && n < N) {
+            if (f32) reinterpret_cast<uint32_t*>(y)[(size_t)m * N + n] = 0x7FC00000u;
+            else reinterpret_cast<uint16_t*>(y)[(size_t)m * N + n] = (uint16_t)0x7FC0u;
+        }
+    }
+}
+
 // Tile ordering.  Workgroups are dispatched round-robin over the 8 XCDs
 // (workgroup i runs on XCD i % 8), and each XCD has its own L2.  So the
 // workgroup id is first remapped so that each XCD receives one contiguous

@@ -45,6 +45,23 @@
  *    enqueued and a status code comes back.  Kernels never trap; non-finite
  *    inputs are outside the contract (unspecified output, no crash).
  *  - Functions are thread-safe.
+ *  - GEMM error bound and its domain.  Every GEMM meets, per output element,
+ *        |y - y_exact| <= 1e-4 * S + F + (K/16 + 1) * 2^-126
+ *    (plus half a bf16 ulp of the result when Y is bf16), where S =
+ *    sum_k |a_k w_k| over the dequantized operands and F is the part of S
+ *    contributed by terms with an operand value below 2^-126, the smallest
+ *    normal fp32.  For operands in the normal fp32 range (F = 0) and results
+ *    above 2^-126 * K this is the 1e-4 * S bound.  Below that range the
+ *    hardware may flush: the dequantizing kernels turn such operand values
+ *    into bf16 subnormals or zeros (MXFP8 blocks with scales below 2^-117,
+ *    MXFP4 weights in W4A16 with scale 2^-127, subnormal bf16 activations in
+ *    W4A16), and an fp32 accumulator may lose sums below 2^-126, at most once
+ *    per 16-wide step.
+ *  - Workspaces.  A GEMM that can use device scratch takes (workspace,
+ *    ws_bytes); NULL/0 is always valid and selects the variant that needs
+ *    none, except for mx_gemm_fused with a mixed pair.  A non-NULL workspace
+ *    smaller than the size query's answer for the same arguments returns
+ *    MX_ERR_WORKSPACE.  Calls sharing a workspace must not overlap in time.
  */
 #ifndef MXLINEAR_H
 #define MXLINEAR_H
@@ -64,9 +81,9 @@ typedef enum {
     MX_OK = 0,
     MX_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, bad format/rule pair */
     MX_ERR_SHAPE = 2,       /* m, n or k < 1; k not a multiple of the block */
-    MX_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
-    MX_ERR_WORKSPACE = 4,   /* reserved (a workspace smaller than needed runs unsplit) */
-    MX_ERR_UNSUPPORTED = 5, /* current device is not gfx950 */
+    MX_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned (256 for the quantize-once workspace) */
+    MX_ERR_WORKSPACE = 4,   /* a non-NULL workspace smaller than the call needs, or none where one is required */
+    MX_ERR_UNSUPPORTED = 5, /* device is not gfx950, or the selected kernel cannot address operands this large */
     MX_ERR_HIP = 6          /* a HIP runtime call or launch failed */
 } mx_status;
 
@@ -84,22 +101,29 @@ typedef enum {
 
 /* GEMM flags */
 #define MX_OUT_F32 0x1u  /* write Y as fp32 instead of bf16 */
-#define MX_FP8_FAST 0x2u /* MXFP8 only: contract on the FP8 matrix cores (about 2x the
-                          * throughput); their internal accumulation is inexact, with
-                          * errors measured up to ~2e-4 * sum|a*b|, so this opts out of
-                          * the 1e-4 bound that the default path meets */
+#define MX_FP8_FAST 0x2u /* pairs with an MXFP8 operand: contract on the block-scaled FP8
+                          * (or FP8 x FP4) matrix cores (about 2x the throughput); their
+                          * internal accumulation is inexact, with errors measured up to
+                          * ~2e-4 * sum|a*b|, so this opts out of the 1e-4 bound that the
+                          * default path meets (documented bound 5e-4 * sum|a*b|) */
 #define MX_DEBUG_DUMP_AQ 0x4u /* mx_gemm_fused only: also write the prologue's A codes and scales
                                  to the workspace (see mx_gemm_fused) */
 
 /* ABI version of this header (bumped on any signature change). */
-#define MXLINEAR_ABI_VERSION 7
+#define MXLINEAR_ABI_VERSION 8
 int mx_abi_version(void);
 
 /* Static text for a status code; never NULL. */
 const char* mx_status_string(mx_status status);
 
 /*
- * mx_quantize_act -- dynamic per-token activation quantization.
+ * mx_quantize_act -- dynamic per-token activation quantization: per token
+ * row, blocks of 32 along k to E2M1 with a CEIL-rule UE8M0 scale, computed
+ * at run time with no calibration state (Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-
+ * s3000, "Training mode"); MXFP8 activations are dynamic too
+ * (Qwen3.8-27B-MXFP8Attn-MXFP4MLP-lmheadMXFP4, section 2); NVFP4 uses the
+ * static per-tensor input global scale (Qwen3.5-27B-NVFP4-GPTQ,
+ * introduction).
  * a_bf16: [m, k] bf16.  Outputs a_q and a_s in the block layout above.
  *  fmt MXFP4 or MXFP8: one E8M0 scale per 32 along k, chosen by `rule`
  *    (CEIL is the activation rule); element = RNE(x * 2^-e), ties to the even
@@ -119,83 +143,109 @@ mx_status mx_quantize_act(mx_format fmt, mx_scale_rule rule, const void* a_bf16,
 
 /*
  * mx_pack_weights -- round-to-nearest weight packing, once per weight tensor
- * (the exporter step).  Same kernel and layouts as mx_quantize_act with the
- * [n, k] weight matrix; EVEN is the MXFP4 weight rule.
+ * (the exporter step): E2M1 in blocks of 32 with EVEN-rule E8M0 scales
+ * (Qwen3.5-27B-MXFP4-QAD-W4A4-LR1e-5-s1000, "How this checkpoint was
+ * produced"), each weight rounded to the lattice with no scale search
+ * (Qwen3.5-27B-NVFP4-RTN-weight-only, introduction).  Same kernel, layouts
+ * and errors as mx_quantize_act with the [n, k] weight matrix.
  */
 mx_status mx_pack_weights(mx_format fmt, mx_scale_rule rule, const void* w_bf16, int64_t n,
                           int64_t k, float global_scale, void* w_q, void* w_s,
                           mx_stream_t stream);
 
 /*
- * mx_gemm -- block-scaled GEMM on MX operands.
- * a_fmt == w_fmt in {MXFP4, MXFP8} (a mixed pair returns MX_ERR_UNSUPPORTED).
- * a_q/a_s are [m, k] codes and [m, k/32] scales, w_q/w_s are [n, k] codes and
- * [n, k/32] scales.  y is [m, n] bf16 (RNE of the fp32 accumulator) or fp32
- * with MX_OUT_F32.  Requires k % 32 == 0; any m, n >= 1 (no lower limit on n).
- * MXFP4 runs on the block-scaled FP4 matrix cores, whose block sums are exact.
- * MXFP8 by default dequantizes each operand exactly to bf16 (element times
- * its power-of-two block scale) and runs on bf16 matrix cores; MX_FP8_FAST
- * selects the FP8 matrix cores instead.  Result: fp32 accumulation within
- * 1e-4 * sum_k |a_k w_k| of the exact product (plus the bf16 output rounding).
- * All pointers must be 16-byte aligned.
- * workspace/ws_bytes: optional device scratch for split-K, owned by the
- * caller (NULL/0 is valid).  When the output tiles alone cannot occupy the
- * GPU (small m or n) and ws_bytes is at least mx_gemm_workspace_size's
- * answer, K is split across workgroups: each writes an fp32 partial product
- * into the workspace and a second kernel sums the partials in split order
- * (deterministic) and rounds once.  Otherwise the call runs unsplit.  Both
- * meet the tolerance above; they are not bitwise equal to each other (the
- * fp32 summation order differs).  Calls sharing one workspace must not
- * overlap in time.
+ * mx_gemm -- block-scaled GEMM on MX operands: the W4A4 FP4 GEMM that serves
+ * the MXFP4 checkpoints (Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Serving":
+ * block-32 E2M1 weights with E8M0 scales times activations quantized per
+ * token at run time), and the MXFP8 W8A8 projections of the mixed recipe
+ * (Qwen3.8-27B-MXFP8Attn-MXFP4MLP-lmheadMXFP4, introduction and section 2:
+ * E4M3 with E8M0 per group of 32 for attention, MXFP4 for the MLP and
+ * lm_head).
+ * a_fmt, w_fmt in {MXFP4, MXFP8}, equal or mixed.  a_q/a_s are [m, k] codes
+ * and [m, k/32] E8M0 scales, w_q/w_s are [n, k] codes and [n, k/32] scales
+ * (codes: E2M1 two per byte, E4M3 one per byte).  y is [m, n] bf16 (RNE of
+ * the fp32 accumulator) or fp32 with MX_OUT_F32.  Requires k % 32 == 0; any
+ * m, n >= 1 (no lower limit on n).  All pointers 16-byte aligned.
+ * Kernels:
+ *  - MXFP4 x MXFP4 runs on the block-scaled FP4 matrix cores, whose block
+ *    sums are exact.
+ *  - MXFP8 x MXFP8 and the mixed pairs by default dequantize each operand
+ *    exactly to bf16 (element times its power-of-two block scale) and run on
+ *    bf16 matrix cores.  MX_FP8_FAST selects the block-scaled FP8 (and
+ *    FP8 x FP4) matrix cores instead, whose internal accumulation is inexact
+ *    (bound 5e-4 * S instead of 1e-4 * S).
+ * Result: the GEMM error bound above (1e-4 * S on normal-range operands).
+ * workspace/ws_bytes: optional split-K scratch (mx_gemm_workspace_size).
+ * When the output tiles alone cannot occupy the GPU (small m or n) and a
+ * workspace is given, K is split across workgroups: each writes an fp32
+ * partial product into the workspace and a second kernel sums the partials
+ * in split order (deterministic) and rounds once.  Without one the call runs
+ * unsplit.  Both meet the bound; they are not bitwise equal to each other.
+ * Errors: MX_ERR_INVALID_ARG (NVFP4, null pointer, unknown flag),
+ * MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_WORKSPACE (workspace too small),
+ * MX_ERR_UNSUPPORTED (not gfx950; or the tile/decode kernels, which use
+ * 32-bit offsets, would see an operand of 2 GiB or more), MX_ERR_HIP.
  */
 mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void* a_s,
                   const void* w_q, const void* w_s, int64_t m, int64_t n, int64_t k, void* y,
-                  unsigned flags, void* workspace, size_t ws_bytes, mx_stream_t stream);
+                  void* workspace, size_t ws_bytes, unsigned flags, mx_stream_t stream);
 
 /*
- * mx_gemm_fused -- mx_gemm with the activation quantization computed inside
- * the GEMM from bf16 A ([m, k]), with scale rule a_rule.  The result equals
- * mx_quantize_act followed by an unsplit mx_gemm.
- * Workspace (optional, 16-byte aligned):
- *  - without MX_DEBUG_DUMP_AQ, large MXFP4 shapes (m, n >= 1024, k % 128 ==
- *    0) given at least mx_gemm_fused_workspace_size bytes quantize each
- *    256-row block of A once into the workspace (codes [m, k/2], then scales
- *    [m, k/32], mx_quantize_act's layout; then block counters), inside the
- *    GEMM's own launches: the first workgroups that need a block share its
- *    quantization, the others read it.  The workspace then holds A's codes
- *    and scales.  The exact MXFP8 path does the same with 128-row blocks
- *    (k % 128 == 0, n > 256; codes [m, k], then scales [m, k/32]).  Other
- *    shapes, MX_FP8_FAST, or a smaller workspace, quantize inside each tile
- *    instead.  Calls sharing a workspace must not overlap.
- *  - with MX_DEBUG_DUMP_AQ the quantization the in-tile prologue computed is
- *    also written to the workspace, A codes [m, k * bits / 8] (bits 4 or 8)
- *    followed by E8M0 scales [m, k/32], so it can be checked bit for bit.
- *    The workspace must then hold both (MX_ERR_WORKSPACE otherwise).
+ * mx_gemm_fused -- mx_gemm with the per-token activation quantization done
+ * inside the GEMM from bf16 A ([m, k]) with scale rule a_rule (CEIL is the
+ * activation rule: Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode").
+ * The result equals mx_quantize_act followed by an unsplit mx_gemm, bit for
+ * bit.  Workspace (mx_gemm_fused_workspace_size):
+ *  - same-format pairs without MX_DEBUG_DUMP_AQ: optional.  Large MXFP4
+ *    shapes (m, n >= 1024, k % 128 == 0) quantize each 256-row block of A
+ *    once into it, inside the GEMM's own launches; the exact MXFP8 path does
+ *    the same with 128-row blocks (k % 128 == 0, n > 256).  Layout from its
+ *    base, which must be 256-byte aligned (MX_ERR_ALIGN): A codes [m, k/2]
+ *    (MXFP4) or [m, k] (MXFP8); E8M0 scales [m, k/32] at the next 256-byte
+ *    boundary (both as mx_quantize_act writes them); at the next 256-byte
+ *    boundary the int32 state: a chunk pool counter, one done counter per
+ *    block and an error word.  The error word is nonzero after the call if
+ *    a tile's bounded wait for its block gave up; that tile's part of Y is
+ *    then NaN.  Without a workspace (or with MX_FP8_FAST) each tile
+ *    quantizes its own rows of A instead.
+ *  - mixed pairs: required (MX_ERR_WORKSPACE without it).  A is quantized
+ *    into it (codes [m, k * bits(a_fmt) / 8], then scales [m, k/32]) and
+ *    the mixed GEMM reads it there.
+ *  - with MX_DEBUG_DUMP_AQ (same-format pairs), the codes and scales that
+ *    the in-tile prologue computed are also written to the workspace, A
+ *    codes [m, k * bits / 8] followed by E8M0 scales [m, k/32], so they can
+ *    be checked bit for bit; the workspace must hold both.
+ * Errors as mx_gemm; MX_ERR_INVALID_ARG also for an unknown rule.
  */
-mx_status mx_gemm_fused(mx_format a_fmt, mx_scale_rule a_rule, const void* a_bf16,
-                        mx_format w_fmt, const void* w_q, const void* w_s, int64_t m, int64_t n,
-                        int64_t k, void* y, unsigned flags, void* workspace, size_t ws_bytes,
-                        mx_stream_t stream);
+mx_status mx_gemm_fused(mx_format a_fmt, mx_format w_fmt, const void* a_bf16, mx_scale_rule a_rule,
+                        const void* w_q, const void* w_s, int64_t m, int64_t n, int64_t k, void* y,
+                        void* workspace, size_t ws_bytes, unsigned flags, mx_stream_t stream);
 
 /*
- * mx_gemm_fused_workspace_size -- bytes of workspace mx_gemm_fused can use
- * on this shape and flags (0: none; always 0 with MX_DEBUG_DUMP_AQ, whose
- * workspace is the dump).  Same argument checks as mx_gemm_fused.
+ * mx_gemm_fused_workspace_size -- bytes of workspace mx_gemm_fused uses on
+ * this shape, pair and flags (0: none).  With MX_DEBUG_DUMP_AQ, or for a
+ * mixed pair, the codes and scales of A (the amount the call requires).
+ * Same argument checks as mx_gemm_fused.
  */
 mx_status mx_gemm_fused_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k,
                                        unsigned flags, size_t* bytes);
 
 /*
- * nv_gemm -- NVFP4 x NVFP4 GEMM.  a_q [m, k/2] E2M1, a_s [m, k/16] E4M3,
+ * nv_gemm -- NVFP4 x NVFP4 GEMM, the W4A4 path of the NVFP4 checkpoints
+ * (Qwen3.5-27B-NVFP4-GPTQ and Qwen3.5-27B-NVFP4-RTN-weight-only,
+ * introductions: E2M1 elements with block scales and per-tensor global
+ * scales for weights and inputs).  a_q [m, k/2] E2M1, a_s [m, k/16] E4M3,
  * w_q [n, k/2], w_s [n, k/16].  Y = alpha * sum_k (e2m1_a * s_a) *
  * (e2m1_w * s_w), with alpha = 1 / (g_a * g_w) supplied by the caller.
  * Requires k % 16 == 0.  The block products are exact in f16, so the
- * contraction runs on f16 matrix cores with fp32 accumulation.  workspace:
- * split-K scratch as for mx_gemm (alpha is applied after the partial sums).
+ * contraction runs on f16 matrix cores with fp32 accumulation: the GEMM
+ * error bound above with F = 0.  workspace: split-K scratch as for mx_gemm
+ * (alpha is applied after the partial sums).  Errors as mx_gemm, plus
+ * MX_ERR_INVALID_ARG for a non-finite alpha.
  */
 mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t m,
-                  int64_t n, int64_t k, float alpha, void* y, unsigned flags, void* workspace,
-                  size_t ws_bytes, mx_stream_t stream);
+                  int64_t n, int64_t k, float alpha, void* y, void* workspace, size_t ws_bytes,
+                  unsigned flags, mx_stream_t stream);
 
 /*
  * mx_gemm_w4a16 -- weight-only quantized linear (W4A16): bf16 activations,
@@ -213,9 +263,9 @@ mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void*
  *                                 dq(w) = e2m1 * s_e4m3       (NVFP4),
  * alpha = 1 / g_w for NVFP4 weights (their global scale), normally 1 for
  * MXFP4.  A weight element times its block scale is exact in bf16, so the
- * contraction runs on bf16 matrix cores with fp32 accumulation: within
- * 1e-4 * sum_k |a_k dq(w)_k| of the exact product (plus the bf16 output
- * rounding); MXFP4 weight values below 2^-126 are flushed to zero.
+ * contraction runs on bf16 matrix cores with fp32 accumulation: the GEMM
+ * error bound above (1e-4 * sum_k |a_k dq(w)_k| on normal-range operands;
+ * MXFP4 weight values and bf16 activations below 2^-126 may be flushed).
  * Requires k % 32 == 0 (MXFP4) or k % 16 == 0 (NVFP4); any m, n >= 1.
  * Errors: MX_ERR_INVALID_ARG for null pointers, unknown flags, a
  * non-finite alpha or a w_fmt other than MXFP4/NVFP4 (MXFP8:
@@ -225,14 +275,14 @@ mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void*
  * kernel only.
  */
 mx_status mx_gemm_w4a16(mx_format w_fmt, const void* a_bf16, const void* w_q, const void* w_s, int64_t m,
-                        int64_t n, int64_t k, float alpha, void* y, unsigned flags, void* workspace,
-                        size_t ws_bytes, mx_stream_t stream);
+                        int64_t n, int64_t k, float alpha, void* y, void* workspace, size_t ws_bytes,
+                        unsigned flags, mx_stream_t stream);
 
 /*
  * mx_gemm_workspace_size / mx_gemm_w4a16_workspace_size -- *bytes = the
- * workspace with which mx_gemm (a_fmt == w_fmt MXFP4/MXFP8, or NVFP4 for
- * nv_gemm, with the given flags) or mx_gemm_w4a16 splits K on this shape;
- * 0 when it never does.  Pure host logic; errors as the GEMM's own
+ * workspace with which mx_gemm (MX pairs, equal or mixed, with the given
+ * flags; NVFP4 with NVFP4 for nv_gemm) or mx_gemm_w4a16 splits K on this
+ * shape; 0 when it never does.  Pure host logic; errors as the GEMM's own
  * argument checks.
  */
 mx_status mx_gemm_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k,

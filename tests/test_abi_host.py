@@ -83,10 +83,10 @@ def test_quantize_validation(fn):
 
 def g(**kw):
     a = dict(a_fmt=0, w_fmt=0, aq=GOOD, as_=GOOD, wq=GOOD, ws=GOOD, m=16, n=16, k=64, y=GOOD,
-             flags=0)
+             flags=0, work=None, wsb=0)
     a.update(kw)
     return L.mx_gemm(a["a_fmt"], a["w_fmt"], a["aq"], a["as_"], a["wq"], a["ws"], a["m"], a["n"],
-                     a["k"], a["y"], a["flags"], None, 0, None)
+                     a["k"], a["y"], a["work"], a["wsb"], a["flags"], None)
 
 
 def test_gemm_validation():
@@ -99,22 +99,27 @@ def test_gemm_validation():
     assert g(n=0) == SHAPE
     assert g(k=48) == SHAPE
     assert g(k=1 << 31) == SHAPE
-    assert g(a_fmt=0, w_fmt=1) == UNSUPPORTED  # mixed element types
+    assert g(a_fmt=0, w_fmt=1) in (OK, UNSUPPORTED, HIPERR)   # mixed pairs pass validation
+    assert g(a_fmt=1, w_fmt=0, flags=0x2) in (OK, UNSUPPORTED, HIPERR)
     assert g(ws=BAD_ALIGN) == ALIGN
     assert g(n=96) in (OK, UNSUPPORTED, HIPERR)  # N < 128 is accepted (validation passes)
     assert g(n=1, m=1, k=32) in (OK, UNSUPPORTED, HIPERR)
 
 
 def test_fused_and_nv_validation():
-    f = L.mx_gemm_fused
-    assert f(0, 9, GOOD, 0, GOOD, GOOD, 4, 4, 64, GOOD, 0, None, 0, None) == INVALID
-    assert f(0, 1, None, 0, GOOD, GOOD, 4, 4, 64, GOOD, 0, None, 0, None) == INVALID
-    assert f(0, 1, GOOD, 0, GOOD, GOOD, 4, 4, 40, GOOD, 0, None, 0, None) == SHAPE
-    assert f(1, 1, GOOD, 0, GOOD, GOOD, 4, 4, 64, GOOD, 0, None, 0, None) == UNSUPPORTED
+    f = L.mx_gemm_fused   # (a_fmt, w_fmt, a_bf16, a_rule, w_q, w_s, m, n, k, y, workspace, ws_bytes, flags, stream)
+    assert f(0, 0, GOOD, 9, GOOD, GOOD, 4, 4, 64, GOOD, None, 0, 0, None) == INVALID
+    assert f(0, 0, None, 1, GOOD, GOOD, 4, 4, 64, GOOD, None, 0, 0, None) == INVALID
+    assert f(0, 0, GOOD, 1, GOOD, GOOD, 4, 4, 40, GOOD, None, 0, 0, None) == SHAPE
+    # mixed pairs quantize A into the workspace: required, codes + scales
+    assert f(1, 0, GOOD, 1, GOOD, GOOD, 4, 4, 64, GOOD, None, 0, 0, None) == WORKSPACE
+    assert f(1, 0, GOOD, 1, GOOD, GOOD, 4, 4, 64, GOOD, P(0x40000), 4 * 64 + 4 * 2 - 1, 0, None) == WORKSPACE
+    assert f(1, 0, GOOD, 1, GOOD, GOOD, 4, 4, 64, GOOD, P(0x40000), 4 * 64 + 4 * 2, 0, None) in (OK, UNSUPPORTED,
+                                                                                                HIPERR)
     nv = L.nv_gemm
-    assert nv(GOOD, GOOD, GOOD, GOOD, 4, 4, 40, 1.0, GOOD, 0, None, 0, None) == SHAPE
-    assert nv(GOOD, GOOD, GOOD, GOOD, 4, 4, 48, float("inf"), GOOD, 0, None, 0, None) == INVALID
-    assert nv(None, GOOD, GOOD, GOOD, 4, 4, 48, 1.0, GOOD, 0, None, 0, None) == INVALID
+    assert nv(GOOD, GOOD, GOOD, GOOD, 4, 4, 40, 1.0, GOOD, None, 0, 0, None) == SHAPE
+    assert nv(GOOD, GOOD, GOOD, GOOD, 4, 4, 48, float("inf"), GOOD, None, 0, 0, None) == INVALID
+    assert nv(None, GOOD, GOOD, GOOD, 4, 4, 48, 1.0, GOOD, None, 0, 0, None) == INVALID
     assert L.mx_tensor_amax(None, 10, GOOD, None) == INVALID
     assert L.mx_tensor_amax(GOOD, 0, GOOD, None) == SHAPE
     assert L.mx_tensor_amax(GOOD, 10, P(0x10002), None) == ALIGN
@@ -123,7 +128,7 @@ def test_fused_and_nv_validation():
 def test_w4a16_validation():
     w = L.mx_gemm_w4a16
     def g(fmt=0, a=GOOD, wq=GOOD, ws=GOOD, m=4, n=4, k=64, alpha=1.0, y=GOOD, flags=0):
-        return w(fmt, a, wq, ws, m, n, k, alpha, y, flags, None, 0, None)
+        return w(fmt, a, wq, ws, m, n, k, alpha, y, None, 0, flags, None)
     assert g(fmt=7) == INVALID
     assert g(fmt=1) == UNSUPPORTED          # MXFP8 weights: no W4A16 mode
     assert g(a=None) == INVALID
@@ -186,12 +191,22 @@ def test_workspace_sizes():
     assert mxl.mx_gemm_workspace_size("nvfp4", "nvfp4", 96, 160, 4096) > 0
     # tiles that fill the GPU, the decode kernel, the prefill kernel: none
     assert mxl.mx_gemm_workspace_size("mxfp4", "mxfp4", 8192, 17408, 5120) == 0
-    # fused, quantize-once: A codes and scales of the 8192 x 5120 activations,
-    # then at a 256-byte boundary a chunk pool counter, a done counter per
-    # 256-row block and an error word, rounded up to 256 bytes
+    # fused, quantize-once: A codes of the 8192 x 5120 activations, the
+    # scales at the next 256-byte boundary, then at the next one a chunk
+    # pool counter, a done counter per 256-row block and an error word,
+    # rounded up to 256 bytes
+    def up256(v):
+        return (v + 255) // 256 * 256
     assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 8192, 17408, 5120) == 8192 * 2560 + 8192 * 160 + 256
     assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1100, 1090, 1152) == \
-        ((1100 * 576 + 1100 * 36 + 255) // 256) * 256 + 256
+        up256(up256(1100 * 576) + 1100 * 36) + 256
+    # odd m and odd k/128: the scale plane no longer starts on a cache line
+    # after the codes, so it is moved to the next 256-byte boundary
+    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1025, 1090, 1152) == \
+        up256(up256(1025 * 576) + 1025 * 36) + 256
+    # mixed pairs: A's codes and scales
+    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp4", 100, 300, 512) == 100 * 512 + 100 * 16
+    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp8", 100, 300, 512) == 100 * 256 + 100 * 16
     assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 512, 2048, 5120) == 0     # not a large shape
     assert "mx_gemm_prefill_fq_kernel<" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 8192, 17408, 5120, fused=True)
     # exact MXFP8: codes [m, k] and scales, then the pool counter, a done
@@ -200,7 +215,8 @@ def test_workspace_sizes():
     assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 8192, 17408, 5120, fp8_fast=True) == 0
     assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 64, 96, 5120) == 0        # n <= 256
     b2 = ctypes.c_size_t(7)
-    assert L.mx_gemm_fused_workspace_size(0, 0, 8192, 17408, 5120, 0x4, ctypes.byref(b2)) == OK and b2.value == 0
+    assert L.mx_gemm_fused_workspace_size(0, 0, 8192, 17408, 5120, 0x4, ctypes.byref(b2)) == OK and \
+        b2.value == 8192 * 2560 + 8192 * 160                     # the dump
     assert L.mx_gemm_fused_workspace_size(0, 2, 64, 64, 64, 0, ctypes.byref(b2)) == INVALID
     assert mxl.mx_gemm_workspace_size("mxfp4", "mxfp4", 8, 17408, 5120) == 0
     assert mxl.mx_gemm_workspace_size("mxfp8", "mxfp8", 4096, 6144, 5120) == 0
@@ -213,15 +229,63 @@ def test_workspace_sizes():
     assert L.mx_gemm_w4a16_workspace_size(1, 4, 4, 64, ctypes.byref(b)) == UNSUPPORTED
     assert L.mx_gemm_w4a16_workspace_size(2, 8, 512, 5120, ctypes.byref(b)) == OK and b.value == 0  # decode
     assert L.mx_gemm_w4a16_workspace_size(2, 96, 160, 4096, ctypes.byref(b)) == OK and b.value > 0
+    # mixed pairs split like the exact MXFP8 kernel
+    assert mxl.mx_gemm_workspace_size("mxfp8", "mxfp4", 64, 96, 5120) == 10 * 64 * 96 * 4
     # a misaligned workspace is rejected before any HIP call
-    assert L.mx_gemm(0, 0, GOOD, GOOD, GOOD, GOOD, 4, 4, 64, GOOD, 0, BAD_ALIGN, 64, None) == ALIGN
+    assert L.mx_gemm(0, 0, GOOD, GOOD, GOOD, GOOD, 4, 4, 64, GOOD, BAD_ALIGN, 64, 0, None) == ALIGN
     assert "split-K" in mxl.mx_gemm_plan("mxfp8", "mxfp8", 64, 96, 5120)
+
+
+def test_workspace_too_small_is_an_error():
+    # a non-NULL workspace smaller than the size query's answer: MX_ERR_WORKSPACE
+    # (NULL always runs the variant that needs none)
+    need = mxl.mx_gemm_workspace_size("mxfp8", "mxfp8", 64, 96, 5120)
+    assert g(a_fmt=1, w_fmt=1, m=64, n=96, k=5120, work=P(0x40000), wsb=need - 1) == WORKSPACE
+    assert g(a_fmt=1, w_fmt=1, m=64, n=96, k=5120, work=P(0x40000), wsb=0) == WORKSPACE
+    assert g(a_fmt=1, w_fmt=1, m=64, n=96, k=5120, work=P(0x40000), wsb=need) in (OK, UNSUPPORTED, HIPERR)
+    assert g(a_fmt=1, w_fmt=1, m=64, n=96, k=5120) in (OK, UNSUPPORTED, HIPERR)
+    need4 = mxl.mx_gemm_workspace_size("mxfp4", "mxfp4", 512, 2048, 5120)
+    assert g(m=512, n=2048, k=5120, work=P(0x40000), wsb=need4 - 16) == WORKSPACE
+    # shapes that never split ignore the workspace
+    assert g(m=8192, n=17408, k=5120, work=P(0x40000), wsb=16) in (OK, UNSUPPORTED, HIPERR)
+    nvneed = mxl.mx_gemm_workspace_size("nvfp4", "nvfp4", 96, 160, 4096)
+    assert L.nv_gemm(GOOD, GOOD, GOOD, GOOD, 96, 160, 4096, 1.0, GOOD, P(0x40000), nvneed - 1, 0, None) == WORKSPACE
+    wneed = ctypes.c_size_t(0)
+    L.mx_gemm_w4a16_workspace_size(2, 96, 160, 4096, ctypes.byref(wneed))
+    assert L.mx_gemm_w4a16(2, GOOD, GOOD, GOOD, 96, 160, 4096, 1.0, GOOD, P(0x40000), wneed.value - 1, 0,
+                           None) == WORKSPACE
+    f = L.mx_gemm_fused
+    fneed = mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1100, 1090, 1152)
+    assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40000), fneed - 1, 0, None) == WORKSPACE
+    # the quantize-once workspace must be 256-byte aligned (its blocks own whole cache lines)
+    assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40010), fneed, 0, None) == ALIGN
+    assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40100), fneed, 0, None) in (OK, UNSUPPORTED,
+                                                                                               HIPERR)
+    pneed = mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 1100, 1090, 1152)
+    assert f(1, 1, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40080), pneed, 0, None) == ALIGN
+
+
+def test_operands_beyond_32bit_offsets_are_rejected():
+    # the tile and decode kernels address operands with 32-bit byte offsets:
+    # a call that would take them with an operand of 2 GiB or more is refused
+    # instead of computing with wrapped offsets
+    # MXFP8 fast path, W = 65536 x 32768 E4M3 codes = 2 GiB
+    assert g(a_fmt=1, w_fmt=1, m=64, n=65536, k=32768, flags=0x2) == UNSUPPORTED
+    # the same shape on the exact MXFP8 path (64-bit offsets) passes validation
+    assert g(a_fmt=1, w_fmt=1, m=64, n=65536, k=32768) in (OK, UNSUPPORTED, HIPERR)
+    # MXFP4 decode, W = 262144 x 16384 codes (2 GiB)
+    assert g(m=8, n=262144, k=32768) == UNSUPPORTED
+    # the fused in-tile kernel reads bf16 A: 32768 x 32768 x 2 B = 2 GiB
+    f = L.mx_gemm_fused
+    assert f(0, 0, GOOD, 1, GOOD, GOOD, 32768, 512, 32768, GOOD, None, 0, 0, None) == UNSUPPORTED
+    # shapes below the limit pass validation
+    assert g(m=8, n=17408, k=5120) in (OK, UNSUPPORTED, HIPERR)
 
 
 def test_fused_dump_validation():
     f = L.mx_gemm_fused
     def g(flags=0x4, ws=P(0x40000), wsb=1 << 20, k=64):
-        return f(0, 1, GOOD, 0, GOOD, GOOD, 4, 4, k, GOOD, flags, ws, wsb, None)
+        return f(0, 0, GOOD, 1, GOOD, GOOD, 4, 4, k, GOOD, ws, wsb, flags, None)
     assert g(flags=0x8) == INVALID
     assert g(ws=None) == WORKSPACE
     assert g(wsb=4 * 32 + 4 * 2 - 1) == WORKSPACE          # codes 4 x 32 B + scales 4 x 2 B
@@ -244,10 +308,25 @@ def test_plan_names_the_kernel():
     assert mxl.mx_gemm_plan("mxfp8", "mxfp8", 16, 96, 5120)  # N = 96 is a valid plan
     with pytest.raises(mxl.MXError):
         mxl.mx_gemm_plan("mxfp4", "mxfp4", 16, 16, 40)
+    assert "mxfp8xmxfp4 dq_gemm_kernel<mxfp8 x mxfp4" in mxl.mx_gemm_plan("mxfp8", "mxfp4", 4096, 5120, 5120)
+    assert "mxfp4xmxfp8 dq_gemm_kernel" in mxl.mx_gemm_plan("mxfp4", "mxfp8", 4096, 5120, 5120)
+    assert "mx_gemm_kernel<tile 128x128" in mxl.mx_gemm_plan("mxfp8", "mxfp4", 4096, 5120, 5120, fp8_fast=True)
+    assert "workspace" in mxl.mx_gemm_plan("mxfp8", "mxfp4", 4096, 5120, 5120, fused=True)
     assert "w4a16_decode_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 1, 17408, 5120)
     assert "w4a16_decode_kernel" in mxl.mx_gemm_w4a16_plan("nvfp4", 16, 17408, 5120)
     assert "dq_gemm_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 17, 17408, 5120)
     assert "dq_gemm_kernel" in mxl.mx_gemm_w4a16_plan("nvfp4", 1, 512, 400)
+
+
+def test_plan_names_fit_their_buffers():
+    # the binding passes its buffer's real length: a long plan name is cut
+    # by snprintf inside the buffer, never past it
+    for fmt in ("mxfp4", "nvfp4"):
+        assert len(mxl.mx_gemm_w4a16_plan(fmt, 96, 160, 4096)) < 512
+    small = ctypes.create_string_buffer(16)
+    assert L.mx_gemm_w4a16_plan(0, 96, 160, 4096, small, 16) == OK
+    assert len(small.value) == 15
+    assert L.mx_gemm_plan(0, 0, 8192, 17408, 5120, 0, 0, small, 16) == OK and len(small.value) == 15
 
 
 def test_global_scale_helper_matches_oracle():

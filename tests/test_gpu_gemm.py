@@ -424,10 +424,16 @@ def test_nvfp4_fuzz_operands():
 # chunks, the error word must be clear, and Y must equal both the standalone
 # pair and the in-tile prologue bit for bit, for every rule.  The first shape
 # has a ragged last block (1100 rows: 76 rows) and only tail tiles (25 tiles
-# as 256 x 128 halves), the second a main launch plus a tail.  The exact MXFP8
-# GEMM does the same with 128-row blocks (1100 rows: a ragged 76-row block).
-FQ_CASES = [("mxfp4", 1100, 1152, 1090), ("mxfp4", 1300, 2560, 33000), ("mxfp8", 1100, 1152, 1090),
-            ("mxfp8", 300, 2048, 700)]
+# as 256 x 128 halves), the second a main launch plus a tail, the third odd m
+# and odd k/128 (its code plane ends off a cache line, so the scale plane
+# starts at the next 256-byte boundary).  The exact MXFP8 GEMM does the same
+# with 128-row blocks (1100 rows: a ragged 76-row block).
+FQ_CASES = [("mxfp4", 1100, 1152, 1090), ("mxfp4", 1300, 2560, 33000), ("mxfp4", 1025, 1152, 1090),
+            ("mxfp8", 1100, 1152, 1090), ("mxfp8", 300, 2048, 700), ("mxfp8", 1025, 1152, 1090)]
+
+
+def up256(v: int) -> int:
+    return (v + 255) // 256 * 256
 
 
 @pytest.mark.parametrize("fmt,m,k,n", FQ_CASES)
@@ -442,7 +448,8 @@ def test_fused_quantize_once(fmt, m, k, n):
     cpr = k // 2 if fmt == "mxfp4" else k           # code bytes per row
     bm = 256 if fmt == "mxfp4" else 128             # rows per block
     qb, sb = m * cpr, m * k // 32
-    cnt = (qb + sb + 255) // 256 * 256
+    so = up256(qb)                                  # scale plane offset
+    cnt = up256(so + sb)                            # state offset
     for rule in ("ceil", "floor", "even"):
         for out_f32 in (False, True):
             ws = torch.full((wsz,), 0xA5, dtype=torch.uint8, device="cuda")
@@ -452,7 +459,7 @@ def test_fused_quantize_once(fmt, m, k, n):
             y_tile = mxl.mx_gemm_fused(a, wq, wsc, fmt, rule, fmt, out_f32=out_f32, quantize_once=False)
             torch.cuda.synchronize()
             assert torch.equal(ws[:qb].view(m, cpr), aq), f"{rule}: workspace codes"
-            assert torch.equal(ws[qb:qb + sb].view(m, k // 32), as_), f"{rule}: workspace scales"
+            assert torch.equal(ws[so:so + sb].view(m, k // 32), as_), f"{rule}: workspace scales"
             nb = (m + bm - 1) // bm
             st = ws[cnt:cnt + 4 * (nb + 2)].view(torch.int32).cpu().numpy()
             assert st[0] >= (bm // 32) * nb, "chunk pool"
@@ -461,7 +468,44 @@ def test_fused_quantize_once(fmt, m, k, n):
             assert torch.equal(y, y_ref), f"{rule} f32={out_f32}: quantize-once != standalone"
             assert torch.equal(y, y_tile), f"{rule} f32={out_f32}: quantize-once != in-tile prologue"
     rq, rs = oracle.mx_quantize(ELEM[fmt], "even", a_bits)
-    assert np.array_equal(host(ws[:qb].view(m, cpr)), rq) and np.array_equal(host(ws[qb:qb + sb].view(m, k // 32)), rs)
+    assert np.array_equal(host(ws[:qb].view(m, cpr)), rq) and np.array_equal(host(ws[so:so + sb].view(m, k // 32)), rs)
+
+
+# Mixed MX pairs (MXFP8 activations with MXFP4 weights and the reverse):
+# the default path dequantizes each operand exactly to bf16 (bound 1e-4 * S),
+# MX_FP8_FAST runs the block-scaled FP8 x FP4 matrix cores (documented bound
+# 5e-4 * S), and mx_gemm_fused quantizes A into its workspace and runs the
+# same GEMM (bitwise equal to mx_quantize_act + unsplit mx_gemm).  Full
+# outputs against the oracle, ragged shapes, both K tilings (K % 128 == 0
+# takes the scales as row dwords) and a split-K shape.
+MIXED_SHAPES = [(200, 416, 300), (129, 512, 257), (33, 5120, 96)]
+
+
+@pytest.mark.parametrize("a_fmt,w_fmt", [("mxfp8", "mxfp4"), ("mxfp4", "mxfp8")])
+@pytest.mark.parametrize("m,k,n", MIXED_SHAPES)
+def test_mixed_pairs(a_fmt, w_fmt, m, k, n):
+    say(f"mixed {a_fmt} x {w_fmt} {m}x{k}x{n}: {mxl.mx_gemm_plan(a_fmt, w_fmt, m, n, k)[:60]}")
+    a_bits = W.activations_entry_outliers(m, k)
+    w_bits = W.normal_bf16(n, k, 0.02, 1)
+    raq, ras = oracle.mx_quantize(ELEM[a_fmt], "ceil", a_bits)
+    rwq, rws = oracle.mx_quantize(ELEM[w_fmt], W_RULE[w_fmt], w_bits)
+    y_ref, s = oracle.gemm_dq(oracle.mx_dequantize(ELEM[a_fmt], raq, ras, m, k),
+                              oracle.mx_dequantize(ELEM[w_fmt], rwq, rws, n, k))
+    a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
+    aq, as_ = mxl.mx_quantize_act(a, a_fmt, "ceil")
+    wq, wsc = mxl.mx_pack_weights(w, w_fmt, W_RULE[w_fmt])
+    for out_f32 in (False, True):
+        y = mxl.mx_gemm(aq, as_, wq, wsc, k, a_fmt, w_fmt, out_f32=out_f32)
+        y1 = mxl.mx_gemm(aq, as_, wq, wsc, k, a_fmt, w_fmt, out_f32=out_f32, split_k=False)
+        yf = mxl.mx_gemm_fused(a, wq, wsc, a_fmt, "ceil", w_fmt, out_f32=out_f32)
+        yfast = mxl.mx_gemm(aq, as_, wq, wsc, k, a_fmt, w_fmt, out_f32=True, fp8_fast=True, split_k=False)
+        torch.cuda.synchronize()
+        check_gemm(y_host(y), y_ref, s, not out_f32, f"mixed {a_fmt}x{w_fmt} {m}x{k}x{n} f32={out_f32}")
+        check_gemm(y_host(y1), y_ref, s, not out_f32, f"mixed unsplit {a_fmt}x{w_fmt} f32={out_f32}")
+        assert torch.equal(yf, y1), "fused mixed != quantize + unsplit GEMM"
+        # the fast path against its documented 5e-4 bound (error scaled by 1/5)
+        rel = check_gemm(0.2 * (y_host(yfast) - y_ref) + y_ref, y_ref, s, False, f"mixed fast {a_fmt}x{w_fmt}")
+        say(f"  fast path max err/S = {rel * 5:.2e}")
 
 
 def test_deterministic():
