@@ -18,6 +18,23 @@ mxl = pytest.importorskip("fp8_quantized_linear_amd")
 L = mxl.lib
 
 OK, INVALID, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED, HIPERR = range(7)
+
+# The validation tests call the entry points with fake device pointers.
+# Calls whose arguments pass validation go on to the device check and, on a
+# machine with a GPU, would launch kernels on those pointers; so these tests
+# run only where no GPU is visible (counting devices initialises none).  On
+# a GPU machine only the pure host logic below them runs.
+import torch  # noqa: E402
+
+NO_GPU = torch.cuda.device_count() == 0
+fake_pointers = pytest.mark.skipif(not NO_GPU, reason="calls with fake device pointers run only without a GPU")
+
+
+def passes_validation(call) -> bool:
+    """True if call() gets past argument validation (reaching the device
+    check, which fails without a GPU)."""
+    assert NO_GPU
+    return call() in (OK, UNSUPPORTED, HIPERR)
 P = ctypes.c_void_p
 GOOD = P(0x10000)      # 16-byte aligned, never dereferenced by validation failures
 BAD_ALIGN = P(0x10008)
@@ -61,11 +78,12 @@ def q(fn, fmt=0, rule=1, x=GOOD, rows=4, k=64, g=1.0, qp=GOOD, sp=GOOD):
     return fn(fmt, rule, x, rows, k, g, qp, sp, None)
 
 
+@fake_pointers
 @pytest.mark.parametrize("fn", [L.mx_quantize_act, L.mx_pack_weights])
 def test_quantize_validation(fn):
     assert q(fn, fmt=7) == INVALID
     assert q(fn, rule=9) == INVALID
-    assert q(fn, fmt=2, rule=9, g=0.5) != INVALID  # NVFP4 ignores the rule
+    assert passes_validation(lambda: q(fn, fmt=2, rule=9, g=0.5))  # NVFP4 ignores the rule
     assert q(fn, x=None) == INVALID
     assert q(fn, qp=None) == INVALID
     assert q(fn, sp=None) == INVALID
@@ -78,7 +96,7 @@ def test_quantize_validation(fn):
     assert q(fn, x=BAD_ALIGN) == ALIGN
     # valid arguments reach the device check: without a GPU that is a HIP error
     st = q(fn)
-    assert st in (OK, UNSUPPORTED, HIPERR)
+    assert passes_validation(lambda: st)
 
 
 def g(**kw):
@@ -89,6 +107,7 @@ def g(**kw):
                      a["k"], a["y"], a["work"], a["wsb"], a["flags"], None)
 
 
+@fake_pointers
 def test_gemm_validation():
     assert g(a_fmt=2) == INVALID          # NVFP4 goes through nv_gemm
     assert g(w_fmt=5) == INVALID
@@ -99,13 +118,14 @@ def test_gemm_validation():
     assert g(n=0) == SHAPE
     assert g(k=48) == SHAPE
     assert g(k=1 << 31) == SHAPE
-    assert g(a_fmt=0, w_fmt=1) in (OK, UNSUPPORTED, HIPERR)   # mixed pairs pass validation
-    assert g(a_fmt=1, w_fmt=0, flags=0x2) in (OK, UNSUPPORTED, HIPERR)
+    assert passes_validation(lambda: g(a_fmt=0, w_fmt=1))   # mixed pairs pass validation
+    assert passes_validation(lambda: g(a_fmt=1, w_fmt=0, flags=0x2))
     assert g(ws=BAD_ALIGN) == ALIGN
-    assert g(n=96) in (OK, UNSUPPORTED, HIPERR)  # N < 128 is accepted (validation passes)
-    assert g(n=1, m=1, k=32) in (OK, UNSUPPORTED, HIPERR)
+    assert passes_validation(lambda: g(n=96))  # N < 128 is accepted (validation passes)
+    assert passes_validation(lambda: g(n=1, m=1, k=32))
 
 
+@fake_pointers
 def test_fused_and_nv_validation():
     f = L.mx_gemm_fused   # (a_fmt, w_fmt, a_bf16, a_rule, w_q, w_s, m, n, k, y, workspace, ws_bytes, flags, stream)
     assert f(0, 0, GOOD, 9, GOOD, GOOD, 4, 4, 64, GOOD, None, 0, 0, None) == INVALID
@@ -114,8 +134,8 @@ def test_fused_and_nv_validation():
     # mixed pairs quantize A into the workspace: required, codes + scales
     assert f(1, 0, GOOD, 1, GOOD, GOOD, 4, 4, 64, GOOD, None, 0, 0, None) == WORKSPACE
     assert f(1, 0, GOOD, 1, GOOD, GOOD, 4, 4, 64, GOOD, P(0x40000), 4 * 64 + 4 * 2 - 1, 0, None) == WORKSPACE
-    assert f(1, 0, GOOD, 1, GOOD, GOOD, 4, 4, 64, GOOD, P(0x40000), 4 * 64 + 4 * 2, 0, None) in (OK, UNSUPPORTED,
-                                                                                                HIPERR)
+    assert passes_validation(lambda: f(1, 0, GOOD, 1, GOOD, GOOD, 4, 4, 64, GOOD, P(0x40000), 4 * 64 + 4 * 2, 0,
+                                       None))
     nv = L.nv_gemm
     assert nv(GOOD, GOOD, GOOD, GOOD, 4, 4, 40, 1.0, GOOD, None, 0, 0, None) == SHAPE
     assert nv(GOOD, GOOD, GOOD, GOOD, 4, 4, 48, float("inf"), GOOD, None, 0, 0, None) == INVALID
@@ -125,6 +145,7 @@ def test_fused_and_nv_validation():
     assert L.mx_tensor_amax(GOOD, 10, P(0x10002), None) == ALIGN
 
 
+@fake_pointers
 def test_w4a16_validation():
     w = L.mx_gemm_w4a16
     def g(fmt=0, a=GOOD, wq=GOOD, ws=GOOD, m=4, n=4, k=64, alpha=1.0, y=GOOD, flags=0):
@@ -138,16 +159,17 @@ def test_w4a16_validation():
     assert g(fmt=2, k=40) == SHAPE           # NVFP4 needs k % 16 == 0
     assert g(m=0) == SHAPE
     assert g(wq=BAD_ALIGN) == ALIGN
-    assert g(fmt=2, k=48) in (OK, UNSUPPORTED, HIPERR)   # validation passes
+    assert passes_validation(lambda: g(fmt=2, k=48))   # validation passes
 
 
+@fake_pointers
 def test_fake_quant_validation():
     f = L.mx_fake_quant
     def g(fmt=0, rule=1, x=GOOD, rows=4, k=64, gs=1.0, y=P(0x20000)):
         return f(fmt, rule, x, rows, k, gs, y, None)
     assert g(fmt=7) == INVALID
     assert g(rule=9) == INVALID
-    assert g(fmt=2, rule=9) in (OK, UNSUPPORTED, HIPERR)   # NVFP4 ignores the rule
+    assert passes_validation(lambda: g(fmt=2, rule=9))   # NVFP4 ignores the rule
     assert g(x=None) == INVALID
     assert g(y=None) == INVALID
     assert g(fmt=2, gs=0.0) == INVALID
@@ -158,9 +180,10 @@ def test_fake_quant_validation():
     assert g(rows=0) == SHAPE
     assert g(x=BAD_ALIGN) == ALIGN
     assert g(y=P(0x20008)) == ALIGN
-    assert g(y=P(0x10000 + 64 * 4 * 2)) in (OK, UNSUPPORTED, HIPERR)  # adjacent, not overlapping
+    assert passes_validation(lambda: g(y=P(0x10000 + 64 * 4 * 2)))  # adjacent, not overlapping
 
 
+@fake_pointers
 def test_swiglu_validation():
     f = L.mx_gemm_swiglu_quant
     def g(aq=GOOD, a_s=GOOD, wq=GOOD, ws=GOOD, m=4, inter=64, k=256, hq=GOOD, hs=GOOD):
@@ -173,7 +196,7 @@ def test_swiglu_validation():
     assert g(m=0) == SHAPE
     assert g(k=96) == UNSUPPORTED          # the fused kernel needs k % 128 == 0
     assert g(hq=BAD_ALIGN) == ALIGN
-    assert g() in (OK, UNSUPPORTED, HIPERR)
+    assert passes_validation(lambda: g())
     s = L.mx_swiglu_quant
     assert s(None, 4, 64, GOOD, GOOD, None) == INVALID
     assert s(GOOD, 4, 40, GOOD, GOOD, None) == SHAPE
@@ -184,6 +207,7 @@ def test_swiglu_validation():
         mxl.mx_gemm_swiglu_quant_plan(16, 64, 96)
 
 
+@fake_pointers
 def test_workspace_sizes():
     # few tiles and a long K: split-K with S fp32 partials of M x N
     assert mxl.mx_gemm_workspace_size("mxfp8", "mxfp8", 64, 96, 5120) == 10 * 64 * 96 * 4
@@ -236,18 +260,19 @@ def test_workspace_sizes():
     assert "split-K" in mxl.mx_gemm_plan("mxfp8", "mxfp8", 64, 96, 5120)
 
 
+@fake_pointers
 def test_workspace_too_small_is_an_error():
     # a non-NULL workspace smaller than the size query's answer: MX_ERR_WORKSPACE
     # (NULL always runs the variant that needs none)
     need = mxl.mx_gemm_workspace_size("mxfp8", "mxfp8", 64, 96, 5120)
     assert g(a_fmt=1, w_fmt=1, m=64, n=96, k=5120, work=P(0x40000), wsb=need - 1) == WORKSPACE
     assert g(a_fmt=1, w_fmt=1, m=64, n=96, k=5120, work=P(0x40000), wsb=0) == WORKSPACE
-    assert g(a_fmt=1, w_fmt=1, m=64, n=96, k=5120, work=P(0x40000), wsb=need) in (OK, UNSUPPORTED, HIPERR)
-    assert g(a_fmt=1, w_fmt=1, m=64, n=96, k=5120) in (OK, UNSUPPORTED, HIPERR)
+    assert passes_validation(lambda: g(a_fmt=1, w_fmt=1, m=64, n=96, k=5120, work=P(0x40000), wsb=need))
+    assert passes_validation(lambda: g(a_fmt=1, w_fmt=1, m=64, n=96, k=5120))
     need4 = mxl.mx_gemm_workspace_size("mxfp4", "mxfp4", 512, 2048, 5120)
     assert g(m=512, n=2048, k=5120, work=P(0x40000), wsb=need4 - 16) == WORKSPACE
     # shapes that never split ignore the workspace
-    assert g(m=8192, n=17408, k=5120, work=P(0x40000), wsb=16) in (OK, UNSUPPORTED, HIPERR)
+    assert passes_validation(lambda: g(m=8192, n=17408, k=5120, work=P(0x40000), wsb=16))
     nvneed = mxl.mx_gemm_workspace_size("nvfp4", "nvfp4", 96, 160, 4096)
     assert L.nv_gemm(GOOD, GOOD, GOOD, GOOD, 96, 160, 4096, 1.0, GOOD, P(0x40000), nvneed - 1, 0, None) == WORKSPACE
     wneed = ctypes.c_size_t(0)
@@ -259,12 +284,13 @@ def test_workspace_too_small_is_an_error():
     assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40000), fneed - 1, 0, None) == WORKSPACE
     # the quantize-once workspace must be 256-byte aligned (its blocks own whole cache lines)
     assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40010), fneed, 0, None) == ALIGN
-    assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40100), fneed, 0, None) in (OK, UNSUPPORTED,
-                                                                                               HIPERR)
+    assert passes_validation(lambda: f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40100), fneed, 0,
+                                       None))
     pneed = mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 1100, 1090, 1152)
     assert f(1, 1, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40080), pneed, 0, None) == ALIGN
 
 
+@fake_pointers
 def test_operands_beyond_32bit_offsets_are_rejected():
     # the tile and decode kernels address operands with 32-bit byte offsets:
     # a call that would take them with an operand of 2 GiB or more is refused
@@ -272,16 +298,17 @@ def test_operands_beyond_32bit_offsets_are_rejected():
     # MXFP8 fast path, W = 65536 x 32768 E4M3 codes = 2 GiB
     assert g(a_fmt=1, w_fmt=1, m=64, n=65536, k=32768, flags=0x2) == UNSUPPORTED
     # the same shape on the exact MXFP8 path (64-bit offsets) passes validation
-    assert g(a_fmt=1, w_fmt=1, m=64, n=65536, k=32768) in (OK, UNSUPPORTED, HIPERR)
+    assert passes_validation(lambda: g(a_fmt=1, w_fmt=1, m=64, n=65536, k=32768))
     # MXFP4 decode, W = 262144 x 16384 codes (2 GiB)
     assert g(m=8, n=262144, k=32768) == UNSUPPORTED
     # the fused in-tile kernel reads bf16 A: 32768 x 32768 x 2 B = 2 GiB
     f = L.mx_gemm_fused
     assert f(0, 0, GOOD, 1, GOOD, GOOD, 32768, 512, 32768, GOOD, None, 0, 0, None) == UNSUPPORTED
     # shapes below the limit pass validation
-    assert g(m=8, n=17408, k=5120) in (OK, UNSUPPORTED, HIPERR)
+    assert passes_validation(lambda: g(m=8, n=17408, k=5120))
 
 
+@fake_pointers
 def test_fused_dump_validation():
     f = L.mx_gemm_fused
     def g(flags=0x4, ws=P(0x40000), wsb=1 << 20, k=64):
@@ -290,7 +317,7 @@ def test_fused_dump_validation():
     assert g(ws=None) == WORKSPACE
     assert g(wsb=4 * 32 + 4 * 2 - 1) == WORKSPACE          # codes 4 x 32 B + scales 4 x 2 B
     assert g(ws=BAD_ALIGN) == ALIGN
-    assert g(wsb=4 * 32 + 4 * 2) in (OK, UNSUPPORTED, HIPERR)
+    assert passes_validation(lambda: g(wsb=4 * 32 + 4 * 2))
 
 
 def test_gate_up_interleave_index():
