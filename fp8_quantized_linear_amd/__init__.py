@@ -51,6 +51,8 @@ def _load():
         f.restype, f.argtypes = i32, [i32, i32, P, i64, i64, f32, P, P, P]
     L.mx_gemm.restype = i32
     L.mx_gemm.argtypes = [i32, i32, P, P, P, P, i64, i64, i64, P, P, sz, u32, P]
+    L.mx_gemm_noalloc.restype = i32
+    L.mx_gemm_noalloc.argtypes = [i32, i32, P, P, P, P, i64, i64, i64, P, u32, P]
     L.mx_gemm_fused.restype = i32
     L.mx_gemm_fused.argtypes = [i32, i32, P, i32, P, P, i64, i64, i64, P, P, sz, u32, P]
     L.nv_gemm.restype = i32
@@ -202,6 +204,25 @@ def mx_gemm(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str = "mxfp
     st = lib.mx_gemm(_fmt(a_fmt), _fmt(w_fmt), _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, n, k,
                      _ptr(y), _ptr(ws), wsb, _flags(out_f32, fp8_fast), _stream(a_q))
     _check(st, "mx_gemm")
+    return y
+
+
+def mx_gemm_noalloc(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str = "mxfp4",
+                    out_f32: bool = False, y=None, fp8_fast: bool = False):
+    """mx_gemm without a workspace argument: split-K partials go to the
+    library's static device scratch (for callers that cannot allocate; calls
+    overlapping on one GPU race).  Pass `y` to allocate nothing here either."""
+    for t, nm in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
+        _need(t, torch.uint8, nm)
+    m, n = a_q.shape[0], w_q.shape[0]
+    if a_q.shape[1] != codes_per_row(a_fmt, k) or w_q.shape[1] != codes_per_row(w_fmt, k):
+        raise ValueError("code tensors do not match k")
+    if a_s.shape != (m, k // 32) or w_s.shape != (n, k // 32):
+        raise ValueError("scale tensors do not match k")
+    y = _gemm_out(m, n, a_q.device, out_f32, y)
+    st = lib.mx_gemm_noalloc(_fmt(a_fmt), _fmt(w_fmt), _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, n, k,
+                             _ptr(y), _flags(out_f32, fp8_fast), _stream(a_q))
+    _check(st, "mx_gemm_noalloc")
     return y
 
 

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "mxlinear.h"
 
@@ -107,6 +108,27 @@ mx_status check_device()
 }
 
 mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+// Split-K scratch of mx_gemm_noalloc: a file-scope device array that every
+// GPU the library runs on holds for the life of the process.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in):
+// the device address comes from hipGetSymbolAddress, once per device, with
+// that device current, and is kept per device.
+constexpr size_t kNoallocScratchBytes = (size_t)MX_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+std::once_flag g_scratch_once[64];
+void* g_scratch_ptr[64];
+
+// The current device's address of `scratch` (nullptr if the runtime refused).
+void* scratch_address(int dev)
+{
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) ptr = nullptr;
+        g_scratch_ptr[dev] = ptr;
+    });
+    return g_scratch_ptr[dev];
+}
 
 mx_status check_quant_args(mx_format fmt, mx_scale_rule rule, const void* x, int64_t rows, int64_t k,
                            float gscale, const void* q, const void* s)
@@ -242,6 +264,31 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
         return from_hip(mxl_launch_mx_mixed_exact_gemm(ab, a_q, a_s, w_q, w_s, m, n, k, y, f32, workspace,
                                                        ws_bytes, hs));
     return from_hip(mxl_launch_mx_gemm(ab, wb, a_q, a_s, w_q, w_s, m, n, k, y, f32, workspace, ws_bytes, hs));
+}
+
+mx_status mx_gemm_noalloc(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void* a_s, const void* w_q,
+                          const void* w_s, int64_t m, int64_t n, int64_t k, void* y, unsigned flags,
+                          mx_stream_t stream)
+{
+    if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || a_fmt == MX_FMT_NVFP4 || w_fmt == MX_FMT_NVFP4)
+        return MX_ERR_INVALID_ARG;
+    if (flags & ~(MX_OUT_F32 | MX_FP8_FAST)) return MX_ERR_INVALID_ARG;
+    mx_status st = check_gemm_shape(m, n, k, 32);
+    if (st != MX_OK) return st;
+    const size_t need = gemm_workspace_need(a_fmt, w_fmt, m, n, k, flags);
+    if (need > kNoallocScratchBytes) return MX_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        // the remaining argument checks run in mx_gemm; the scratch address
+        // needs the current device, so check it first
+        if (!a_q || !a_s || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
+        if ((st = check_device()) != MX_OK) return st;
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MX_ERR_HIP;
+        ws = scratch_address(dev);
+        if (!ws) return MX_ERR_HIP;
+    }
+    return mx_gemm(a_fmt, w_fmt, a_q, a_s, w_q, w_s, m, n, k, y, ws, ws ? kNoallocScratchBytes : 0, flags, stream);
 }
 
 mx_status mx_gemm_fused(mx_format a_fmt, mx_format w_fmt, const void* a_bf16, mx_scale_rule a_rule,

@@ -191,6 +191,26 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
                   void* workspace, size_t ws_bytes, unsigned flags, mx_stream_t stream);
 
 /*
+ * mx_gemm_noalloc -- mx_gemm for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace.  Where mx_gemm
+ * would split K, the fp32 partials go to a scratch array of
+ * MX_NOALLOC_SCRATCH_BYTES that the library holds in device memory on every
+ * GPU it runs on, for the life of the process; the call itself allocates
+ * nothing.  The result is bitwise equal to mx_gemm with a workspace.  Split-K
+ * runs only while the output tiles cannot fill the GPU (at most 256 tile-
+ * splits of 128 x 128 fp32), so every shape fits the scratch; a need beyond
+ * it would return MX_ERR_WORKSPACE.  All calls on one GPU share its scratch
+ * (nothing in it needs clearing between calls): calls that overlap in time
+ * on one GPU, on different streams, race and must be ordered by the caller.
+ * Errors as mx_gemm.
+ */
+#define MX_NOALLOC_SCRATCH_BYTES (16u << 20)
+mx_status mx_gemm_noalloc(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void* a_s,
+                          const void* w_q, const void* w_s, int64_t m, int64_t n, int64_t k, void* y,
+                          unsigned flags, mx_stream_t stream);
+
+/*
  * mx_gemm_fused -- mx_gemm with the per-token activation quantization done
  * inside the GEMM from bf16 A ([m, k]) with scale rule a_rule (CEIL is the
  * activation rule: Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode").
