@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--quick", action="store_true", help="headline only (skip the other rows)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time")
+    p.add_argument("--kernel-set", action="store_true",
+                   help="only run each main kernel a few times on its workload (for rocprofv3 counter passes) "
+                        "and exit")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain elementwise copy of known size (the reference point that "
                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes) and exit")
@@ -87,6 +90,10 @@ def main():
 
     import fp8_quantized_linear_amd as mxl
     import workloads as W
+
+    if args.kernel_set:
+        kernel_set(torch, mxl, W)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -193,6 +200,57 @@ def main():
         "rows": rows,
     }
     print(json.dumps(out))
+
+
+def kernel_set(torch, mxl, W, reps: int = 3):
+    """Each main kernel `reps` times on its workload, launch order fixed, for
+    per-kernel rocprofv3 counter passes (one kernel name per workload)."""
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def run(name, fn):
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        log(f"kernel-set: {name}")
+
+    up, down = W.PREFILL_UP, W.PREFILL_DOWN
+    for cfg in (up, down):
+        a, w = to_dev(cfg.activations()), to_dev(cfg.weights())
+        wq, ws = mxl.mx_pack_weights(w, "mxfp4", "even")
+        aq, as_ = mxl.mx_quantize_act(a, "mxfp4", "ceil")
+        y = torch.empty((cfg.m, cfg.n), dtype=torch.bfloat16, device=dev)
+        run(f"quantize {cfg.name}", lambda: mxl.mx_quantize_act(a, "mxfp4", "ceil", out=(aq, as_)))
+        run(f"gemm {cfg.name}", lambda: mxl.mx_gemm(aq, as_, wq, ws, cfg.k, y=y))
+        run(f"fused {cfg.name}", lambda: mxl.mx_gemm_fused(a, wq, ws, y=y))
+        del a, w, wq, ws, aq, as_, y
+    c8 = W.MXFP8_ATTN
+    a = to_dev(c8.activations())
+    wq, ws = mxl.mx_pack_weights(to_dev(c8.weights()), "mxfp8", "floor")
+    aq, as_ = mxl.mx_quantize_act(a, "mxfp8", "ceil")
+    y = torch.empty((c8.m, c8.n), dtype=torch.bfloat16, device=dev)
+    run(c8.name, lambda: mxl.mx_gemm(aq, as_, wq, ws, c8.k, "mxfp8", "mxfp8", y=y))
+    nv = W.NVFP4
+    a, w = to_dev(nv.activations()), to_dev(nv.weights())
+    g_a = mxl.mx_nv_global_scale(float(mxl.mx_tensor_amax(a).item()))
+    g_w = mxl.mx_nv_global_scale(float(mxl.mx_tensor_amax(w).item()))
+    aq, as_ = mxl.mx_quantize_act(a, "nvfp4", global_scale=g_a)
+    wq, ws = mxl.mx_pack_weights(w, "nvfp4", global_scale=g_w)
+    y = torch.empty((nv.m, nv.n), dtype=torch.bfloat16, device=dev)
+    run(f"quantize {nv.name}", lambda: mxl.mx_quantize_act(a, "nvfp4", global_scale=g_a, out=(aq, as_)))
+    run(nv.name, lambda: mxl.nv_gemm(aq, as_, wq, ws, nv.k, 1.0 / (g_a * g_w), y=y))
+    dec = W.DECODE[0]
+    wq, ws = mxl.mx_pack_weights(to_dev(dec.weights()), "mxfp4", "even")
+    for cfg in W.DECODE:
+        a = to_dev(cfg.activations())
+        aq, as_ = mxl.mx_quantize_act(a)
+        y = torch.empty((cfg.m, cfg.n), dtype=torch.bfloat16, device=dev)
+        run(cfg.name, lambda: mxl.mx_gemm(aq, as_, wq, ws, cfg.k, y=y))
+        if cfg.m <= 16:
+            run(f"w4a16 {cfg.name}", lambda: mxl.mx_gemm_w4a16(a, wq, ws, "mxfp4", y=y))
+    print(json.dumps({"kernel_set": "done", "reps": reps}))
 
 
 def measure_gfxclk(step, torch, seconds: float = 2.5):
