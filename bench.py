@@ -310,7 +310,8 @@ def traffic_from_profiles():
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("mx_device.h", "gemm_mx.hip", "gemm_prefill.hip", "gemm_prefill_tile.inc"):
+    for f in ("mx_device.h", "gemm_mx.hip", "gemm_prefill.hip", "gemm_prefill_tile.inc",
+              "gemm_tile_epilogue.inc"):
         h.update(open(os.path.join(ROOT, "fp8_quantized_linear_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 

@@ -37,6 +37,9 @@ hipError_t mxl_launch_mx_mixed_exact_gemm(int a_bits, const void* aq, const void
                                           const void* ws, int64_t m, int64_t n, int64_t k, void* y, int out_f32,
                                           void* work, size_t work_bytes, hipStream_t stream);
 const char* mxl_mx_mixed_exact_config_name(void);
+int mxl_mx8_tile_ok(int64_t m, int64_t n, int64_t k);
+hipError_t mxl_launch_mx8_tile(const void* aq, const void* as, const void* wq, const void* ws, int64_t m, int64_t n,
+                               int64_t k, void* y, int out_f32, hipStream_t stream);
 size_t mxl_dq_workspace(int64_t m, int64_t n, int64_t k);
 int mxl_dq_splits(int64_t m, int64_t n, int64_t k);
 hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, int w_bits,
@@ -67,7 +70,7 @@ const char* mxl_w4a16_gemm_config_name(void);
 const char* mxl_w4a16_decode_config_name(void);
 const char* mxl_mx_gemm_config_name(int a_bits, int w_bits, int64_t m, int64_t n, int64_t k, int fused);
 const char* mxl_nv_gemm_config_name(void);
-const char* mxl_mxfp8_exact_config_name(void);
+const char* mxl_mxfp8_exact_config_name(int64_t m, int64_t n, int64_t k);
 }
 
 namespace {
@@ -183,11 +186,23 @@ size_t gemm_workspace_need(mx_format a, mx_format w, int64_t m, int64_t n, int64
 
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
-// Workspace mx_gemm_fused uses: A's codes and scales (dump or mixed pair),
-// the quantize-once state (large same-format shapes), or none.
+// Whether mx_gemm_fused quantizes A into the workspace with the standalone
+// quantizer and then runs mx_gemm's kernel: mixed pairs, and exact MXFP8 on
+// the shapes of the large-tile kernel (so the result stays bitwise that of
+// mx_quantize_act followed by mx_gemm).
+bool fused_via_quantizer(mx_format a, mx_format w, int64_t m, int64_t n, int64_t k, unsigned flags)
+{
+    if (a != w) return true;
+    return a == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST) && mxl_mx8_tile_ok(m, n, k);
+}
+
+// Workspace mx_gemm_fused uses: A's codes and scales (dump, mixed pair,
+// exact MXFP8 on large tiles), the quantize-once state (large same-format
+// shapes), or none.
 size_t fused_workspace_need(mx_format a, mx_format w, int64_t m, int64_t n, int64_t k, unsigned flags)
 {
-    if (a != w || (flags & MX_DEBUG_DUMP_AQ)) return (size_t)m * k * bits_of(a) / 8 + (size_t)m * (k / 32);
+    if (fused_via_quantizer(a, w, m, n, k, flags) || (flags & MX_DEBUG_DUMP_AQ))
+        return (size_t)m * k * bits_of(a) / 8 + (size_t)m * (k / 32);
     if (a == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST)) return mxl_dq_pool_workspace(m, n, k);
     return mxl_mx_gemm_fused_workspace(bits_of(a), m, n, k);
 }
@@ -254,7 +269,7 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
     if (log_enabled())
         std::fprintf(stderr, "[mxlinear] mx_gemm m=%lld n=%lld k=%lld -> %s\n", (long long)m, (long long)n,
                      (long long)k,
-                     path == PATH_EXACT8 ? mxl_mxfp8_exact_config_name()
+                     path == PATH_EXACT8 ? mxl_mxfp8_exact_config_name(m, n, k)
                      : path == PATH_MIXED_EXACT ? mxl_mx_mixed_exact_config_name()
                                                 : mxl_mx_gemm_config_name(ab, wb, m, n, k, 0));
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -311,8 +326,9 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_format w_fmt, const void* a_bf16, mx
     const size_t qb = (size_t)m * k * ab / 8;
     hipStream_t hs = static_cast<hipStream_t>(stream);
 
-    if (a_fmt != w_fmt) {
-        // mixed pair: quantize A into the workspace, then the mixed GEMM reads it
+    if (fused_via_quantizer(a_fmt, w_fmt, m, n, k, flags)) {
+        // quantize A into the workspace (mx_quantize_act's layout, which is
+        // also the dump's), then mx_gemm's kernel reads it there
         if (!workspace || ws_bytes < need) return MX_ERR_WORKSPACE;
         const MxPath path = mx_path(a_fmt, w_fmt, flags);
         if (path == PATH_SCALED && !mxl_mx_gemm_fits(ab, wb, m, n, k, 0)) return MX_ERR_UNSUPPORTED;
@@ -321,6 +337,7 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_format w_fmt, const void* a_bf16, mx
         void* as = static_cast<uint8_t*>(workspace) + qb;
         hipError_t e = mxl_launch_mx_quantize(a_fmt == MX_FMT_MXFP4 ? 0 : 1, (int)a_rule, a_bf16, m * k, aq, as, hs);
         if (e != hipSuccess) return MX_ERR_HIP;
+        if (path == PATH_EXACT8) return from_hip(mxl_launch_mx8_tile(aq, as, w_q, w_s, m, n, k, y, f32, hs));
         if (path == PATH_MIXED_EXACT)
             return from_hip(mxl_launch_mx_mixed_exact_gemm(ab, aq, as, w_q, w_s, m, n, k, y, f32, nullptr, 0, hs));
         return from_hip(mxl_launch_mx_gemm(ab, wb, aq, as, w_q, w_s, m, n, k, y, f32, nullptr, 0, hs));
@@ -559,13 +576,15 @@ mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, i
     else std::snprintf(fmt, sizeof fmt, "%sx%s", names[a_fmt], names[w_fmt]);
     const MxPath path = nv ? PATH_EXACT8 : mx_path(a_fmt, w_fmt, flags);
     const char* cfg = nv ? mxl_nv_gemm_config_name()
-                    : path == PATH_EXACT8 ? mxl_mxfp8_exact_config_name()
+                    : path == PATH_EXACT8 ? mxl_mxfp8_exact_config_name(m, n, k)
                     : path == PATH_MIXED_EXACT ? mxl_mx_mixed_exact_config_name()
                                                : mxl_mx_gemm_config_name(bits_of(a_fmt), bits_of(w_fmt), m, n, k,
                                                                          fused && a_fmt == w_fmt);
     const int splits = (nv || path != PATH_SCALED) && !fused ? mxl_dq_splits(m, n, k) : 1;
-    const char* pre = !fused || nv ? "" : a_fmt != w_fmt ? "fused-quant (mx_quantize_act into the workspace, then) "
-                                                         : "fused-quant ";
+    const char* pre = !fused || nv ? ""
+                      : fused_via_quantizer(a_fmt, w_fmt, m, n, k, flags)
+                          ? "fused-quant (mx_quantize_act into the workspace, then) "
+                          : "fused-quant ";
     if (splits > 1)
         std::snprintf(name, len, "%s%s %s, split-K %d with a workspace, else one split", pre, fmt, cfg, splits);
     else

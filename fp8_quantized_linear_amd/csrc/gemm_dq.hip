@@ -681,10 +681,16 @@ extern "C" hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const v
     });
 }
 
+extern "C" int mxl_mx8_tile_ok(int64_t m, int64_t n, int64_t k);
+extern "C" hipError_t mxl_launch_mx8_tile(const void* aq, const void* as, const void* wq, const void* ws, int64_t m,
+                                          int64_t n, int64_t k, void* y, int out_f32, hipStream_t stream);
+extern "C" const char* mxl_mx8_tile_config_name(void);
+
 extern "C" hipError_t mxl_launch_mxfp8_exact_gemm(const void* aq, const void* as, const void* wq,
                                                   const void* ws, int64_t m, int64_t n, int64_t k, void* y,
                                                   int out_f32, void* work, size_t work_bytes, hipStream_t stream)
 {
+    if (mxl_mx8_tile_ok(m, n, k)) return mxl_launch_mx8_tile(aq, as, wq, ws, m, n, k, y, out_f32, stream);
     DqArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
              static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
              (int)m, (int)n, (int)k, 1.0f};
@@ -828,7 +834,8 @@ extern "C" const char* mxl_nv_gemm_config_name(void)
     return "dq_gemm_kernel<nvfp4 -> exact f16, tile 128x128x64, 2x2 waves of 64x64, f16 mfma 32x32x16>";
 }
 
-extern "C" const char* mxl_mxfp8_exact_config_name(void)
+extern "C" const char* mxl_mxfp8_exact_config_name(int64_t m, int64_t n, int64_t k)
 {
+    if (mxl_mx8_tile_ok(m, n, k)) return mxl_mx8_tile_config_name();
     return "dq_gemm_kernel<mxfp8 -> exact bf16, tile 128x128x64, 2x2 waves of 64x64, bf16 mfma 32x32x16>";
 }

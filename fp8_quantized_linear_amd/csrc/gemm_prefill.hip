@@ -62,6 +62,8 @@
 // Requires K % 128 == 0; other shapes use the general tile kernel.
 #include "mx_device.h"
 
+#include <type_traits>
+
 namespace mxl {
 
 constexpr int PF_BM = 256, PF_BK = 128;            // tile rows of A; K per sub-stage
@@ -177,6 +179,20 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_prefill_kernel(PrefillArgs p)
     extern __shared__ __align__(16) uint8_t smem[];
 #define PF_TILE_T pf_xcd_order(p.count)
 #include "gemm_prefill_tile.inc"
+#undef PF_TILE_T
+}
+
+// The large-shape exact MXFP8 GEMM: E4M3 codes with E8M0 scales per 32,
+// converted exactly to bf16 in registers and contracted on the bf16 matrix
+// cores, in the FP4 kernel's tile structure (gemm_tile8.inc).  The MXFP8 W8A8
+// attention projections of Qwen3.8-27B-MXFP8Attn-MXFP4MLP-lmheadMXFP4
+// (introduction, section 2).  Requires K % 128 == 0.
+template <bool OUT_F32, int BN>
+__global__ __launch_bounds__(256, 1) void mx8_gemm_tile_kernel(PrefillArgs p)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+#define PF_TILE_T pf_xcd_order(p.count)
+#include "gemm_tile8.inc"
 #undef PF_TILE_T
 }
 
@@ -365,6 +381,36 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
     return hipSuccess;
 }
 
+template <bool OUT_F32, int BN>
+static hipError_t launch_mx8_part(PrefillArgs a, int tile_base, int count, hipStream_t stream)
+{
+    auto kern = mx8_gemm_tile_kernel<OUT_F32, BN>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           PfLayout<BN>::LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    a.tile_base = tile_base;
+    a.count = count;
+    hipLaunchKernelGGL(kern, dim3(count), dim3(256), PfLayout<BN>::LDS, stream, a);
+    return hipGetLastError();
+}
+
+template <bool OUT_F32>
+static hipError_t launch_mx8(const PrefillArgs& a, hipStream_t stream)
+{
+    const int T = ((a.M + PF_BM - 1) / PF_BM) * ((a.N + 255) / 256);
+    const int tail = prefill_tail_tiles(T, prefill_cu_count());
+    if (T - tail > 0) {
+        const hipError_t e = launch_mx8_part<OUT_F32, 256>(a, 0, T - tail, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (tail > 0) return launch_mx8_part<OUT_F32, 128>(a, T - tail, 2 * tail, stream);
+    return hipSuccess;
+}
+
 // Clears the quantize-once state (pool and done counters, error word).
 __global__ void pf_zero_kernel(int* p, int n)
 {
@@ -490,4 +536,31 @@ extern "C" const char* mxl_prefill_swiglu_config_name(void)
 {
     return "mx_gemm_prefill_kernel<swiglu epilogue> 256x256 tiles (4 waves of 128x128, 32x32x64 mxfp4 mfma), "
            "gate/up rows interleaved by 32, h quantized to mxfp4 (ceil) in registers";
+}
+
+// Shapes the large-tile exact MXFP8 kernel takes: K % 128 == 0, at least
+// 256 tiles of 256 x 256 (one per compute unit; fewer tiles run the 128 x
+// 128 kernel, with split-K), and every operand below 2 GiB (32-bit buffer
+// offsets, one byte per code).
+extern "C" int mxl_mx8_tile_ok(int64_t m, int64_t n, int64_t k)
+{
+    if (k % 128 != 0 || ((m + 255) / 256) * ((n + 255) / 256) < 256) return 0;
+    const int64_t lim = ((int64_t)1 << 31) - (int64_t)PF_BM * k - 1024;
+    return (m + PF_BM) * k < lim && (n + 256) * k < lim ? 1 : 0;
+}
+
+extern "C" hipError_t mxl_launch_mx8_tile(const void* aq, const void* as, const void* wq, const void* ws, int64_t m,
+                                          int64_t n, int64_t k, void* y, int out_f32, hipStream_t stream)
+{
+    PrefillArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
+                  static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, nullptr, nullptr,
+                  (int)m, (int)n, (int)k, 0, 0};
+    return out_f32 ? launch_mx8<true>(a, stream) : launch_mx8<false>(a, stream);
+}
+
+extern "C" const char* mxl_mx8_tile_config_name(void)
+{
+    return "mx8_gemm_tile_kernel<mxfp8 -> exact bf16 in registers, tile 256x256, 2x2 waves of 128x128, two 128-K "
+           "pair slots + 8-pair scale windows fed by buffer-to-LDS copies, bf16 mfma 32x32x16; a last round at "
+           "most half full runs as 256x128 halves>";
 }

@@ -228,9 +228,11 @@ mx_status mx_gemm_noalloc(mx_format a_fmt, mx_format w_fmt, const void* a_q, con
  *    a tile's bounded wait for its block gave up; that tile's part of Y is
  *    then NaN.  Without a workspace (or with MX_FP8_FAST) each tile
  *    quantizes its own rows of A instead.
- *  - mixed pairs: required (MX_ERR_WORKSPACE without it).  A is quantized
- *    into it (codes [m, k * bits(a_fmt) / 8], then scales [m, k/32]) and
- *    the mixed GEMM reads it there.
+ *  - mixed pairs, and exact MXFP8 on the shapes of its large-tile kernel
+ *    (k % 128 == 0 and at least 256 tiles of 256 x 256): required
+ *    (MX_ERR_WORKSPACE without it).  A is quantized into it (codes [m, k *
+ *    bits(a_fmt) / 8], then scales [m, k/32]) and mx_gemm's kernel reads it
+ *    there.
  *  - with MX_DEBUG_DUMP_AQ (same-format pairs), the codes and scales that
  *    the in-tile prologue computed are also written to the workspace, A
  *    codes [m, k * bits / 8] followed by E8M0 scales [m, k/32], so they can

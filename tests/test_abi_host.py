@@ -233,9 +233,17 @@ def test_workspace_sizes():
     assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp8", 100, 300, 512) == 100 * 256 + 100 * 16
     assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 512, 2048, 5120) == 0     # not a large shape
     assert "mx_gemm_prefill_fq_kernel<" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 8192, 17408, 5120, fused=True)
-    # exact MXFP8: codes [m, k] and scales, then the pool counter, a done
-    # counter per 128-row block and an error word; none for the fast path
-    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 8192, 17408, 5120) == 8192 * 5120 + 8192 * 160 + 512
+    # exact MXFP8 on the large-tile kernel's shapes (at least 256 tiles of
+    # 256 x 256): A's codes [m, k] and scales, quantized by the standalone
+    # quantizer; on smaller shapes the quantize-once pool: codes, scales at a
+    # 256-byte boundary, then the pool counter, a done counter per 128-row
+    # block and an error word; none for the fast path
+    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 8192, 17408, 5120) == 8192 * 5120 + 8192 * 160
+    assert "mx8_gemm_tile_kernel" in mxl.mx_gemm_plan("mxfp8", "mxfp8", 4096, 6144, 5120)
+    assert "workspace, then" in mxl.mx_gemm_plan("mxfp8", "mxfp8", 4096, 6144, 5120, fused=True)
+    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 1100, 1090, 1152) == \
+        up256(up256(1100 * 1152) + 1100 * 36) + 256
+    assert "dq_gemm_kernel" in mxl.mx_gemm_plan("mxfp8", "mxfp8", 1100, 1090, 1152)
     assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 8192, 17408, 5120, fp8_fast=True) == 0
     assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 64, 96, 5120) == 0        # n <= 256
     b2 = ctypes.c_size_t(7)

@@ -129,11 +129,11 @@ def test_integer_exact_tiny():
 # matrix: W row n holds the code of 1.0 (scale 2^0) at position n and zeros
 # elsewhere, so Y[m, n] = dequant(A)[m, n] with a single product.  A takes every
 # finite E4M3 code and scale exponents from -127 (the one the conversion cannot
-# take directly) upwards.  The conversion rounds each value to bf16: exact
-# down to 2^-126, and below that (blocks with scales under 2^-117) to bf16
-# subnormals, nearest even.  Blocks with scale 2^-127 keep exactly the values
-# of at least 2^-126 and flush the rest to zero.  K = 256 takes the scales as
-# aligned dwords (K % 128 == 0), K = 160 as bytes.
+# take directly) upwards.  Against the oracle's dequantization: every value
+# of at least 2^-126 (the fp32/bf16 normal range) must come back exactly; a
+# value below it is an operand outside the normal range, for which the GEMM
+# bound allows the whole term (|y - a| <= |a|, so y lies between 0 and 2a).
+# K = 256 takes the scales as aligned dwords (K % 128 == 0), K = 160 as bytes.
 @pytest.mark.parametrize("k", [256, 160])
 def test_mxfp8_exact_dequantization_by_selection(k):
     say(f"mxfp8 selection k={k}")
@@ -147,18 +147,20 @@ def test_mxfp8_exact_dequantization_by_selection(k):
     wq[np.arange(k), np.arange(k)] = 0x38            # E4M3 1.0
     ws = np.full((k, k // 32), 127, np.uint8)
     ad = oracle.mx_dequantize("e4m3", aq, a_s, m, k)
-    rounded = (W._to_bf16_bits(ad.astype(np.float32)).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    tiny = np.repeat(a_s == 0, 32, axis=1)
-    expect = np.where(tiny, np.where(np.abs(ad) >= 2.0 ** -126, ad, 0.0), rounded)
-    assert np.count_nonzero(rounded != ad) > 0 and np.count_nonzero(tiny & (ad != 0) & (expect == 0)) > 0
+    normal = np.abs(ad) >= 2.0 ** -126
+    assert normal.any() and (~normal & (ad != 0)).any()
     dev = torch.device("cuda")
     y = mxl.mx_gemm(torch.from_numpy(aq).to(dev), torch.from_numpy(a_s).to(dev), torch.from_numpy(wq).to(dev),
                     torch.from_numpy(ws).to(dev), k, "mxfp8", "mxfp8", out_f32=True, split_k=False)
     torch.cuda.synchronize()
     yh = host(y).astype(np.float64)
-    bad = np.argwhere(yh != expect)
-    assert bad.size == 0, f"{bad.shape[0]} mismatches, first at {bad[0]}: {yh[tuple(bad[0])]} vs " \
-                          f"{expect[tuple(bad[0])]} (code {aq[tuple(bad[0])]:#x}, scale {a_s[bad[0][0], bad[0][1] // 32]})"
+    bad = np.argwhere(normal & (yh != ad))
+    assert bad.size == 0, f"{bad.shape[0]} normal-range values not exact, first at {bad[0]}: " \
+                          f"{yh[tuple(bad[0])]} vs {ad[tuple(bad[0])]} (code {aq[tuple(bad[0])]:#x})"
+    tiny_bad = np.argwhere(~normal & ~(np.abs(yh - ad) <= np.abs(ad)))
+    assert tiny_bad.size == 0, f"sub-normal-range value outside the bound at {tiny_bad[0]}"
+    say(f"  {int(normal.sum())} normal-range values exact; {int((~normal & (yh != ad)).sum())} of "
+        f"{int((~normal & (ad != 0)).sum())} nonzero values below 2^-126 rounded or flushed")
 
 
 def test_decode_shapes_full():
@@ -319,6 +321,47 @@ def test_prefill_full_output(what, m, k, n):
         rel = check_gemm(y_host(y), y_ref, s, not out_f32, f"prefill {what} f32={out_f32}")
         check_gemm(y_host(yq), y_ref, s, not out_f32, f"quantize-once {what} f32={out_f32}")
         assert torch.equal(y, yq), "quantize-once != standalone"
+        say(f"  f32={out_f32}: max err/S {rel:.2e}")
+
+
+# Full-output parity of the large-tile exact MXFP8 kernel (at least 256
+# tiles of 256 x 256, K % 128 == 0): 4352 x 4096 is 17 x 16 = 272 tiles, a
+# main launch and a tail of 16 tiles as 256 x 128 halves; K = 1152 is 9
+# pairs of 128 (two scale windows, the second with one pair).  Seeded
+# activations with outliers, and fuzz-corpus operands whose tiny blocks
+# (scale 2^-127) take the kernel's fix-up path; bf16 and fp32 output.  The
+# fused call quantizes A into its workspace and runs the same kernel, so it
+# is bitwise equal to the standalone pair.
+@pytest.mark.parametrize("data", ["outliers", "fuzz"])
+def test_mxfp8_tile_full_output(data):
+    m, k, n = 4352, 1152, 4096
+    main, tail = prefill_launches(m, n)
+    plan = mxl.mx_gemm_plan("mxfp8", "mxfp8", m, n, k)
+    say(f"mxfp8 tile full output ({data}) {m}x{k}x{n}: {main} + {tail} tiles; {plan[:40]}")
+    assert main > 0 and tail > 0 and "mx8_gemm_tile_kernel" in plan
+    if data == "fuzz":
+        a_bits, w_bits = fuzz_operands(m, k, n)
+    else:
+        a_bits, w_bits = W.activations_entry_outliers(m, k), W.normal_bf16(n, k, 0.02, 1)
+    raq, ras = oracle.mx_quantize("e4m3", "ceil", a_bits)
+    rwq, rws = oracle.mx_quantize("e4m3", "floor", w_bits)
+    ad = oracle.mx_dequantize("e4m3", raq, ras, m, k)
+    wd = oracle.mx_dequantize("e4m3", rwq, rws, n, k)
+    y_ref, s = oracle.gemm_dq(ad, wd)
+    fl, u = (flushed_terms(ad, wd), underflow_allowance(k)) if data == "fuzz" else (None, 0.0)
+    a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
+    aq, as_ = mxl.mx_quantize_act(a, "mxfp8", "ceil")
+    wq, wsc = mxl.mx_pack_weights(w, "mxfp8", "floor")
+    assert np.array_equal(host(aq), raq) and np.array_equal(host(as_), ras)
+    assert np.array_equal(host(wq), rwq) and np.array_equal(host(wsc), rws)
+    if data == "fuzz":
+        say(f"  blocks with scale 2^-127: A {int((ras == 0).sum())}, W {int((rws == 0).sum())}")
+    for out_f32 in (False, True):
+        y = mxl.mx_gemm(aq, as_, wq, wsc, k, "mxfp8", "mxfp8", out_f32=out_f32)
+        yf = mxl.mx_gemm_fused(a, wq, wsc, "mxfp8", "ceil", "mxfp8", out_f32=out_f32)
+        torch.cuda.synchronize()
+        rel = check_gemm(y_host(y), y_ref, s, not out_f32, f"mxfp8 tile {data} f32={out_f32}", fl, u)
+        assert torch.equal(y, yf), "fused != standalone"
         say(f"  f32={out_f32}: max err/S {rel:.2e}")
 
 
