@@ -30,7 +30,7 @@
 //    exact in bf16 (8-bit significand, fp32 exponent range) for every block
 //    whose scale exponent is at least -117.  Below that (blocks with amax
 //    under ~2^-110), values under 2^-126 become bf16 subnormals rounded to
-//    nearest even, and in blocks with scale 2^-127 they are flushed to zero.
+//    nearest even.
 //
 // 16-bit matrix-core layout (32x32x16): lane l = r + 32 g holds row/column r
 // and the 8 consecutive K elements [8g, 8g + 8) of the 16-wide step.
@@ -82,26 +82,12 @@ __device__ __forceinline__ uint4 dequant8_nvfp4(uint32_t codes, _Float16 s)
     return out;
 }
 
-// Halve bf16 pairs by exponent decrement; values that would leave the normal
-// range are flushed to signed zero.
-__device__ __forceinline__ uint32_t bf16x2_halve(uint32_t v)
-{
-    uint32_t out = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        uint32_t h = (v >> (16 * i)) & 0xFFFFu;
-        h = ((h >> 7) & 0xFFu) >= 2u ? h - 0x80u : (h & 0x8000u);
-        out |= h << (16 * i);
-    }
-    return out;
-}
-
-// 8 E4M3 codes (uint2) times 2^e, as 8 bf16 values: the conversion multiplies
-// by the power of two of its fp32 scale operand, which must be a normal fp32,
-// so e = -127 converts with 2^-126 and halves afterwards.
+// 8 E4M3 codes (uint2) times 2^e, as 8 bf16 values.  The conversion reads
+// the exponent field of its fp32 scale operand as an E8M0 scale, field 0
+// (e = -127) included, and rounds results below 2^-126 to nearest even.
 __device__ __forceinline__ uint4 dequant8_mxfp8(uint2 codes, int e)
 {
-    const float s = pow2f(e < -126 ? -126 : e);
+    const float s = pow2f(e);
     bf16x2_t_ h[4];
     h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, s, false);
     h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, s, true);
@@ -109,21 +95,14 @@ __device__ __forceinline__ uint4 dequant8_mxfp8(uint2 codes, int e)
     h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, s, true);
     uint4 out;
     __builtin_memcpy(&out, h, 16);
-    if (e < -126) {
-        out.x = bf16x2_halve(out.x);
-        out.y = bf16x2_halve(out.y);
-        out.z = bf16x2_halve(out.z);
-        out.w = bf16x2_halve(out.w);
-    }
     return out;
 }
 
-// 8 E2M1 codes (one dword) times 2^e, as 8 bf16 values (exact; the
-// conversion takes the power of two from its fp32 scale operand, so
-// e = -127 converts with 2^-126 and halves afterwards).
+// 8 E2M1 codes (one dword) times 2^e, as 8 bf16 values: exact for every
+// scale, 2^-127 included (e2m1 * 2^-127 is at least 2^-128, a bf16 subnormal).
 __device__ __forceinline__ uint4 dequant8_mxfp4_bf16(uint32_t codes, int e)
 {
-    const float s = pow2f(e < -126 ? -126 : e);
+    const float s = pow2f(e);
     bf16x2_t_ h[4];
     h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, s, 0);
     h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, s, 1);
@@ -131,12 +110,6 @@ __device__ __forceinline__ uint4 dequant8_mxfp4_bf16(uint32_t codes, int e)
     h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, s, 3);
     uint4 out;
     __builtin_memcpy(&out, h, 16);
-    if (e < -126) {
-        out.x = bf16x2_halve(out.x);
-        out.y = bf16x2_halve(out.y);
-        out.z = bf16x2_halve(out.z);
-        out.w = bf16x2_halve(out.w);
-    }
     return out;
 }
 

@@ -14,9 +14,8 @@
 // A weight element times its block scale is exact in bf16 (2 significant
 // bits times a power of two, or times 4 significant bits of E4M3), so the
 // contraction runs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16) with
-// fp32 accumulation, like the oracle's exact products.  MXFP4 values below
-// 2^-126 (blocks whose scale exponent is -127) are flushed, as in the MXFP8
-// dequantization.
+// fp32 accumulation, like the oracle's exact products.  MXFP4 blocks with
+// scale 2^-127 are exact too (as bf16 subnormals).
 //
 // Design (M <= 16, K % 512 == 0, the W block fits LDS): a stream over W.
 //  * One workgroup of 4 waves owns 16 rows of W.  Their contiguous
@@ -59,20 +58,6 @@ __device__ __forceinline__ float w4_e4m3_to_f32(uint32_t c)
     return (c & 0x80u) ? -v : v;
 }
 
-// bf16 pairs halved by exponent decrement; results below the normal range
-// flush to signed zero
-__device__ __forceinline__ uint32_t w4_bf16x2_halve(uint32_t v)
-{
-    uint32_t out = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        uint32_t h = (v >> (16 * i)) & 0xFFFFu;
-        h = ((h >> 7) & 0xFFu) >= 2u ? h - 0x80u : (h & 0x8000u);
-        out |= h << (16 * i);
-    }
-    return out;
-}
-
 // 8 E2M1 codes (a dword, element 2j in the low nibble of byte j) dequantized
 // to 8 bf16: NVFP4 with the E4M3 scale s, MXFP4 with the exponent e
 template <bool NV>
@@ -89,7 +74,9 @@ __device__ __forceinline__ bf16x8_w w4_dequant8(uint32_t codes, float s, int e)
         o[2] = bf16x2_rne(f2[0] * s, f2[1] * s);
         o[3] = bf16x2_rne(f3[0] * s, f3[1] * s);
     } else {
-        const float p = __uint_as_float((uint32_t)((e < -126 ? -126 : e) + 127) << 23);
+        // the conversion reads the scale operand's exponent field as E8M0,
+        // field 0 (2^-127) included
+        const float p = __uint_as_float((uint32_t)(e + 127) << 23);
         const bf16x2_w h0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, p, 0);
         const bf16x2_w h1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, p, 1);
         const bf16x2_w h2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, p, 2);
@@ -98,10 +85,6 @@ __device__ __forceinline__ bf16x8_w w4_dequant8(uint32_t codes, float s, int e)
         o[1] = __builtin_bit_cast(uint32_t, h1);
         o[2] = __builtin_bit_cast(uint32_t, h2);
         o[3] = __builtin_bit_cast(uint32_t, h3);
-        if (e < -126) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = w4_bf16x2_halve(o[j]);
-        }
     }
     bf16x8_w v;
     __builtin_memcpy(&v, o, 16);

@@ -315,20 +315,6 @@ __device__ __forceinline__ void fill_tile_nan(void* y, int M, int N, int m0, int
     }
 }
 
-// Halves two bf16 values by decrementing their exponents; a value that would
-// leave the normal range (exponent field below 2) becomes a signed zero.
-__device__ __forceinline__ uint32_t bf16x2_halve_flush(uint32_t v)
-{
-    uint32_t out = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        uint32_t h = (v >> (16 * i)) & 0xFFFFu;
-        h = ((h >> 7) & 0xFFu) >= 2u ? h - 0x80u : (h & 0x8000u);
-        out |= h << (16 * i);
-    }
-    return out;
-}
-
 // Calls f(std::integral_constant<int, i>) for i = B .. E-1 in order: a loop
 // whose index is a compile-time constant in every iteration however large the
 // body (unrolling by pragma stops at a size threshold, and inline-assembly

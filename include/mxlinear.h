@@ -51,12 +51,11 @@
  *    sum_k |a_k w_k| over the dequantized operands and F is the part of S
  *    contributed by terms with an operand value below 2^-126, the smallest
  *    normal fp32.  For operands in the normal fp32 range (F = 0) and results
- *    above 2^-126 * K this is the 1e-4 * S bound.  Below that range the
- *    hardware may flush: the dequantizing kernels turn such operand values
- *    into bf16 subnormals or zeros (MXFP8 blocks with scales below 2^-117,
- *    MXFP4 weights in W4A16 with scale 2^-127, subnormal bf16 activations in
- *    W4A16), and an fp32 accumulator may lose sums below 2^-126, at most once
- *    per 16-wide step.
+ *    above 2^-126 * K this is the 1e-4 * S bound.  Below that range values
+ *    are rounded: the dequantizing kernels hold operands in bf16, so MXFP8
+ *    values below 2^-126 (blocks with scales below 2^-117) become the
+ *    nearest bf16 subnormal (ties to even), and an fp32 accumulator may lose
+ *    sums below 2^-126, at most once per 16-wide step.
  *  - Workspaces.  A GEMM that can use device scratch takes (workspace,
  *    ws_bytes); NULL/0 is always valid and selects the variant that needs
  *    none, except for mx_gemm_fused with a mixed pair.  A non-NULL workspace

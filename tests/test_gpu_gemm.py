@@ -128,39 +128,47 @@ def test_integer_exact_tiny():
 # Exact MXFP8 dequantization inside the GEMM, read back through a selection
 # matrix: W row n holds the code of 1.0 (scale 2^0) at position n and zeros
 # elsewhere, so Y[m, n] = dequant(A)[m, n] with a single product.  A takes every
-# finite E4M3 code and scale exponents from -127 (the one the conversion cannot
-# take directly) upwards.  Against the oracle's dequantization: every value
-# of at least 2^-126 (the fp32/bf16 normal range) must come back exactly; a
-# value below it is an operand outside the normal range, for which the GEMM
-# bound allows the whole term (|y - a| <= |a|, so y lies between 0 and 2a).
-# K = 256 takes the scales as aligned dwords (K % 128 == 0), K = 160 as bytes.
-@pytest.mark.parametrize("k", [256, 160])
-def test_mxfp8_exact_dequantization_by_selection(k):
-    say(f"mxfp8 selection k={k}")
+# finite E4M3 code and scale exponents from -127 upwards.  The kernels hold
+# operands in bf16: every value must come back as the bf16 nearest to the
+# oracle's exact dequantized value (ties to even), which is the value itself
+# from 2^-126 up and a rounded bf16 subnormal below.  The rounding is torch's
+# fp32 -> bf16 conversion of the exact value (exact in fp32: 4 significant
+# bits, at least 2^-136).  K = 256 takes the 128 x 128 kernel's scales as
+# aligned dwords (K % 128 == 0), K = 160 as bytes; 4352 x 4096 x 4096 runs the
+# 256 x 256 tile kernel (256 tiles and 16 tail halves).
+@pytest.mark.parametrize("m,k", [(96, 256), (96, 160), (4352, 4096)])
+def test_mxfp8_exact_dequantization_by_selection(m, k):
+    plan = mxl.mx_gemm_plan("mxfp8", "mxfp8", m, k, k)
+    say(f"mxfp8 selection {m}x{k}x{k}: {plan[:60]}")
+    if m > 1024:
+        assert "mx8_gemm_tile_kernel" in plan
     rng = np.random.default_rng(31)
-    m = 96
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # finite E4M3
     aq = codes[rng.integers(0, codes.size, (m, k))]
-    a_s = rng.choice(np.array([0, 0, 0, 1, 2, 5, 100, 127, 130], np.uint8), (m, k // 32))
+    a_s = rng.choice(np.array([0, 0, 0, 1, 2, 5, 9, 100, 127, 130], np.uint8), (m, k // 32))
     a_s[0, :] = 0                                   # a whole row of 2^-127 blocks
     wq = np.zeros((k, k), np.uint8)
     wq[np.arange(k), np.arange(k)] = 0x38            # E4M3 1.0
     ws = np.full((k, k // 32), 127, np.uint8)
     ad = oracle.mx_dequantize("e4m3", aq, a_s, m, k)
+    ad32 = ad.astype(np.float32)
+    assert np.array_equal(ad32.astype(np.float64), ad)
+    want = torch.from_numpy(ad32).to(torch.bfloat16).float().numpy().astype(np.float64)
     normal = np.abs(ad) >= 2.0 ** -126
-    assert normal.any() and (~normal & (ad != 0)).any()
+    assert normal.any() and (~normal & (ad != 0)).any() and (~normal & (want != ad)).any()
     dev = torch.device("cuda")
     y = mxl.mx_gemm(torch.from_numpy(aq).to(dev), torch.from_numpy(a_s).to(dev), torch.from_numpy(wq).to(dev),
                     torch.from_numpy(ws).to(dev), k, "mxfp8", "mxfp8", out_f32=True, split_k=False)
     torch.cuda.synchronize()
     yh = host(y).astype(np.float64)
-    bad = np.argwhere(normal & (yh != ad))
-    assert bad.size == 0, f"{bad.shape[0]} normal-range values not exact, first at {bad[0]}: " \
-                          f"{yh[tuple(bad[0])]} vs {ad[tuple(bad[0])]} (code {aq[tuple(bad[0])]:#x})"
-    tiny_bad = np.argwhere(~normal & ~(np.abs(yh - ad) <= np.abs(ad)))
-    assert tiny_bad.size == 0, f"sub-normal-range value outside the bound at {tiny_bad[0]}"
-    say(f"  {int(normal.sum())} normal-range values exact; {int((~normal & (yh != ad)).sum())} of "
-        f"{int((~normal & (ad != 0)).sum())} nonzero values below 2^-126 rounded or flushed")
+    tiny = ~normal & (ad != 0)
+    say(f"  {int(normal.sum())} normal-range values, {int((normal & (yh == ad)).sum())} exact; "
+        f"{int(tiny.sum())} nonzero values below 2^-126: {int((tiny & (yh == want)).sum())} equal to the "
+        f"nearest bf16, {int((tiny & (yh == 0)).sum())} zero")
+    bad = np.argwhere(yh != want)
+    assert bad.size == 0, f"{bad.shape[0]} values differ from the nearest bf16, first at {bad[0]}: " \
+                          f"{yh[tuple(bad[0])]} vs {want[tuple(bad[0])]} (exact {ad[tuple(bad[0])]}, " \
+                          f"code {aq[tuple(bad[0])]:#x}, scale byte {a_s[bad[0][0], bad[0][1] // 32]})"
 
 
 def test_decode_shapes_full():
@@ -328,8 +336,8 @@ def test_prefill_full_output(what, m, k, n):
 # tiles of 256 x 256, K % 128 == 0): 4352 x 4096 is 17 x 16 = 272 tiles, a
 # main launch and a tail of 16 tiles as 256 x 128 halves; K = 1152 is 9
 # pairs of 128 (two scale windows, the second with one pair).  Seeded
-# activations with outliers, and fuzz-corpus operands whose tiny blocks
-# (scale 2^-127) take the kernel's fix-up path; bf16 and fp32 output.  The
+# activations with outliers, and fuzz-corpus operands with many tiny blocks
+# (scale 2^-127 included); bf16 and fp32 output.  The
 # fused call quantizes A into its workspace and runs the same kernel, so it
 # is bitwise equal to the standalone pair.
 @pytest.mark.parametrize("data", ["outliers", "fuzz"])
