@@ -224,7 +224,7 @@ def kernel_set(torch, mxl, W, reps: int = 3):
         y = torch.empty((cfg.m, cfg.n), dtype=torch.bfloat16, device=dev)
         run(f"quantize {cfg.name}", lambda: mxl.mx_quantize_act(a, "mxfp4", "ceil", out=(aq, as_)))
         run(f"gemm {cfg.name}", lambda: mxl.mx_gemm(aq, as_, wq, ws, cfg.k, y=y))
-        run(f"fused {cfg.name}", lambda: mxl.mx_gemm_fused(a, wq, ws, y=y))
+        run(f"fused in-GEMM {cfg.name}", lambda: mxl.mx_gemm_fused(a, wq, ws, y=y, in_gemm=True))
         del a, w, wq, ws, aq, as_, y
     c8 = W.MXFP8_ATTN
     a = to_dev(c8.activations())
@@ -338,9 +338,13 @@ def extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_d
     med, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm_fused(a_up, wq_up, ws_up, y=y), 10)
     y2 = torch.empty((down.m, down.n), dtype=torch.bfloat16, device=dev)
     med2, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm_fused(a_dn, wq_dn, ws_dn, y=y2), 10)
+    medg, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm_fused(a_up, wq_up, ws_up, y=y, in_gemm=True), 10)
+    medg2, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm_fused(a_dn, wq_dn, ws_dn, y=y2, in_gemm=True), 10)
     rows["fused_prefill"] = {"up_us": round(med * 1e3, 1), "down_us": round(med2 * 1e3, 1),
-                             "tflops": round((up.flops + down.flops) / ((med + med2) * 1e-3) / 1e12, 1)}
-    log(f"fused: up {med * 1e3:.1f} us down {med2 * 1e3:.1f} us")
+                             "tflops": round((up.flops + down.flops) / ((med + med2) * 1e-3) / 1e12, 1),
+                             "in_gemm_up_us": round(medg * 1e3, 1), "in_gemm_down_us": round(medg2 * 1e3, 1)}
+    log(f"fused: up {med * 1e3:.1f} us down {med2 * 1e3:.1f} us; quantizing inside the GEMM "
+        f"{medg * 1e3:.1f} / {medg2 * 1e3:.1f} us")
 
     # standalone quantizer GB/s (inputs rotated through 4 copies: > 256 MB)
     for name, cfg, a in (("up", up, a_up), ("down", down, a_dn)):

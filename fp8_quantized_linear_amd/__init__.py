@@ -27,6 +27,7 @@ RULES = {"floor": 0, "ceil": 1, "even": 2}
 MX_OUT_F32 = 0x1
 MX_FP8_FAST = 0x2
 MX_DEBUG_DUMP_AQ = 0x4
+MX_FUSED_IN_GEMM = 0x8
 STATUS = {0: "MX_OK", 1: "MX_ERR_INVALID_ARG", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN",
           4: "MX_ERR_WORKSPACE", 5: "MX_ERR_UNSUPPORTED", 6: "MX_ERR_HIP"}
 
@@ -226,23 +227,25 @@ def mx_gemm_noalloc(a_q, a_s, w_q, w_s, k: int, a_fmt: str = "mxfp4", w_fmt: str
     return y
 
 
-def mx_gemm_fused_workspace_size(a_fmt: str, w_fmt: str, m: int, n: int, k: int, fp8_fast: bool = False) -> int:
+def mx_gemm_fused_workspace_size(a_fmt: str, w_fmt: str, m: int, n: int, k: int, fp8_fast: bool = False,
+                                 in_gemm: bool = False) -> int:
     b = ctypes.c_size_t(0)
-    _check(lib.mx_gemm_fused_workspace_size(_fmt(a_fmt), _fmt(w_fmt), m, n, k, _flags(False, fp8_fast),
-                                            ctypes.byref(b)), "mx_gemm_fused_workspace_size")
+    flags = _flags(False, fp8_fast) | (MX_FUSED_IN_GEMM if in_gemm else 0)
+    _check(lib.mx_gemm_fused_workspace_size(_fmt(a_fmt), _fmt(w_fmt), m, n, k, flags, ctypes.byref(b)),
+           "mx_gemm_fused_workspace_size")
     return b.value
 
 
 def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str = "ceil",
                   w_fmt: str = "mxfp4", out_f32: bool = False, y=None, fp8_fast: bool = False,
-                  dump_aq: bool = False, quantize_once: bool = True, workspace=None):
+                  dump_aq: bool = False, quantize_once: bool = True, workspace=None, in_gemm: bool = False):
     """mx_gemm with the activation quantization done inside the GEMM from bf16 a[m, k].
     dump_aq also returns the codes and scales the prologue computed:
     (y, (a_q, a_s)).  quantize_once passes the workspace the library asks for
-    (large shapes: the GEMM's workgroups quantize A once into it instead of
-    once per tile column; mixed pairs: required); `workspace` (uint8, on a's
-    device, 256-byte aligned as torch allocates) is used instead when
-    given."""
+    (large shapes: A is quantized once into it, by the standalone quantizer
+    or, with in_gemm, by the GEMM's own workgroups, instead of once per tile
+    column; mixed pairs: required); `workspace` (uint8, on a's device,
+    256-byte aligned as torch allocates) is used instead when given."""
     _need(a, torch.bfloat16, "a")
     _need(w_q, torch.uint8, "w_q")
     _need(w_s, torch.uint8, "w_s")
@@ -251,7 +254,7 @@ def mx_gemm_fused(a: torch.Tensor, w_q, w_s, a_fmt: str = "mxfp4", a_rule: str =
     if w_q.shape[1] != codes_per_row(w_fmt, k) or w_s.shape != (n, k // 32):
         raise ValueError("weight tensors do not match k")
     y = _gemm_out(m, n, a.device, out_f32, y)
-    flags = _flags(out_f32, fp8_fast)
+    flags = _flags(out_f32, fp8_fast) | (MX_FUSED_IN_GEMM if in_gemm else 0)
     ws, wsb, qb = None, 0, m * codes_per_row(a_fmt, k)
     if dump_aq:
         wsb = qb + m * (k // 32)
@@ -418,9 +421,10 @@ def mx_nv_global_scale(amax: float) -> float:
 
 
 def mx_gemm_plan(a_fmt: str, w_fmt: str, m: int, n: int, k: int, fused: bool = False,
-                 fp8_fast: bool = False) -> str:
+                 fp8_fast: bool = False, in_gemm: bool = False) -> str:
     """Name of the kernel/tile configuration the GEMM would launch for this shape."""
     buf = ctypes.create_string_buffer(512)
-    _check(lib.mx_gemm_plan(_fmt(a_fmt), _fmt(w_fmt), m, n, k, int(fused), _flags(False, fp8_fast),
-                            buf, len(buf)), "mx_gemm_plan")
+    flags = _flags(False, fp8_fast) | (MX_FUSED_IN_GEMM if in_gemm else 0)
+    _check(lib.mx_gemm_plan(_fmt(a_fmt), _fmt(w_fmt), m, n, k, int(fused), flags, buf, len(buf)),
+           "mx_gemm_plan")
     return buf.value.decode()

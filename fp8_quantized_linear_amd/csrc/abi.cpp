@@ -186,25 +186,46 @@ size_t gemm_workspace_need(mx_format a, mx_format w, int64_t m, int64_t n, int64
 
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
-// Whether mx_gemm_fused quantizes A into the workspace with the standalone
-// quantizer and then runs mx_gemm's kernel: mixed pairs, and exact MXFP8 on
-// the shapes of the large-tile kernel (so the result stays bitwise that of
-// mx_quantize_act followed by mx_gemm).
-bool fused_via_quantizer(mx_format a, mx_format w, int64_t m, int64_t n, int64_t k, unsigned flags)
+// Workspace bytes of the quantize-once launches (A quantized inside the
+// GEMM's own workgroups), 0 where the shape has none: large MXFP4 shapes on
+// the prefill kernel, exact MXFP8 on the 128 x 128 kernel.
+size_t fused_pool_need(mx_format a, mx_format w, int64_t m, int64_t n, int64_t k, unsigned flags)
+{
+    if (a != w) return 0;
+    if (a == MX_FMT_MXFP8) return (flags & MX_FP8_FAST) ? 0 : mxl_dq_pool_workspace(m, n, k);
+    return mxl_mx_gemm_fused_workspace(bits_of(a), m, n, k);
+}
+
+// Whether mx_gemm_fused requires the quantizer path (A quantized into the
+// workspace by the standalone quantizer, then mx_gemm's kernel): mixed
+// pairs, and exact MXFP8 on the shapes of the large-tile kernel (so the
+// result stays bitwise that of mx_quantize_act followed by mx_gemm).
+bool fused_requires_quantizer(mx_format a, mx_format w, int64_t m, int64_t n, int64_t k, unsigned flags)
 {
     if (a != w) return true;
     return a == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST) && mxl_mx8_tile_ok(m, n, k);
 }
 
-// Workspace mx_gemm_fused uses: A's codes and scales (dump, mixed pair,
-// exact MXFP8 on large tiles), the quantize-once state (large same-format
-// shapes), or none.
+// Whether a call that brings a workspace takes the quantizer path: where it
+// is required, and on the quantize-once shapes unless MX_FUSED_IN_GEMM asks
+// for the one-launch variant (the separate full-occupancy quantizer launch
+// plus the GEMM measured faster: 414 / 437 us against 451 / 450 us on the
+// 8192 x 5120 x 17408 and 8192 x 17408 x 5120 MXFP4 projections).
+bool fused_via_quantizer(mx_format a, mx_format w, int64_t m, int64_t n, int64_t k, unsigned flags)
+{
+    if (flags & MX_DEBUG_DUMP_AQ) return false;
+    if (fused_requires_quantizer(a, w, m, n, k, flags)) return true;
+    return !(flags & MX_FUSED_IN_GEMM) && fused_pool_need(a, w, m, n, k, flags) > 0;
+}
+
+// Workspace mx_gemm_fused uses: A's codes and scales (dump, quantizer
+// path), the quantize-once codes, scales and state (MX_FUSED_IN_GEMM), or
+// none (the in-tile prologue).
 size_t fused_workspace_need(mx_format a, mx_format w, int64_t m, int64_t n, int64_t k, unsigned flags)
 {
     if (fused_via_quantizer(a, w, m, n, k, flags) || (flags & MX_DEBUG_DUMP_AQ))
         return (size_t)m * k * bits_of(a) / 8 + (size_t)m * (k / 32);
-    if (a == MX_FMT_MXFP8 && !(flags & MX_FP8_FAST)) return mxl_dq_pool_workspace(m, n, k);
-    return mxl_mx_gemm_fused_workspace(bits_of(a), m, n, k);
+    return fused_pool_need(a, w, m, n, k, flags);
 }
 
 // W4A16: the decode kernel takes M <= 16 with K % 512 == 0 when its W block
@@ -314,7 +335,7 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_format w_fmt, const void* a_bf16, mx
         !valid_rule(a_rule))
         return MX_ERR_INVALID_ARG;
     if (!a_bf16 || !w_q || !w_s || !y) return MX_ERR_INVALID_ARG;
-    if (flags & ~(MX_OUT_F32 | MX_FP8_FAST | MX_DEBUG_DUMP_AQ)) return MX_ERR_INVALID_ARG;
+    if (flags & ~(MX_OUT_F32 | MX_FP8_FAST | MX_DEBUG_DUMP_AQ | MX_FUSED_IN_GEMM)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, 32);
     if (st != MX_OK) return st;
     if (!aligned16(a_bf16) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y) ||
@@ -326,7 +347,8 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_format w_fmt, const void* a_bf16, mx
     const size_t qb = (size_t)m * k * ab / 8;
     hipStream_t hs = static_cast<hipStream_t>(stream);
 
-    if (fused_via_quantizer(a_fmt, w_fmt, m, n, k, flags)) {
+    if (fused_via_quantizer(a_fmt, w_fmt, m, n, k, flags) &&
+        (workspace || fused_requires_quantizer(a_fmt, w_fmt, m, n, k, flags))) {
         // quantize A into the workspace (mx_quantize_act's layout, which is
         // also the dump's), then mx_gemm's kernel reads it there
         if (!workspace || ws_bytes < need) return MX_ERR_WORKSPACE;
@@ -350,7 +372,7 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_format w_fmt, const void* a_bf16, mx
         if (!workspace || ws_bytes < need) return MX_ERR_WORKSPACE;
         dump_q = workspace;
         dump_s = static_cast<uint8_t*>(workspace) + qb;
-    } else if (workspace && need > 0) {
+    } else if (workspace && need > 0) {   // MX_FUSED_IN_GEMM on a quantize-once shape
         if (ws_bytes < need) return MX_ERR_WORKSPACE;
         if (!aligned256(workspace)) return MX_ERR_ALIGN;
         use_ws = true;
@@ -376,7 +398,7 @@ mx_status mx_gemm_fused_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t
 {
     if (!valid_fmt(a_fmt) || !valid_fmt(w_fmt) || a_fmt == MX_FMT_NVFP4 || w_fmt == MX_FMT_NVFP4 || !bytes)
         return MX_ERR_INVALID_ARG;
-    if (flags & ~(MX_OUT_F32 | MX_FP8_FAST | MX_DEBUG_DUMP_AQ)) return MX_ERR_INVALID_ARG;
+    if (flags & ~(MX_OUT_F32 | MX_FP8_FAST | MX_DEBUG_DUMP_AQ | MX_FUSED_IN_GEMM)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, 32);
     if (st != MX_OK) return st;
     *bytes = fused_workspace_need(a_fmt, w_fmt, m, n, k, flags);
@@ -575,16 +597,19 @@ mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, i
     if (a_fmt == w_fmt) std::snprintf(fmt, sizeof fmt, "%s", names[a_fmt]);
     else std::snprintf(fmt, sizeof fmt, "%sx%s", names[a_fmt], names[w_fmt]);
     const MxPath path = nv ? PATH_EXACT8 : mx_path(a_fmt, w_fmt, flags);
+    const bool via_q = fused && !nv && fused_via_quantizer(a_fmt, w_fmt, m, n, k, flags);
     const char* cfg = nv ? mxl_nv_gemm_config_name()
                     : path == PATH_EXACT8 ? mxl_mxfp8_exact_config_name(m, n, k)
                     : path == PATH_MIXED_EXACT ? mxl_mx_mixed_exact_config_name()
                                                : mxl_mx_gemm_config_name(bits_of(a_fmt), bits_of(w_fmt), m, n, k,
-                                                                         fused && a_fmt == w_fmt);
+                                                                         fused && a_fmt == w_fmt && !via_q);
     const int splits = (nv || path != PATH_SCALED) && !fused ? mxl_dq_splits(m, n, k) : 1;
     const char* pre = !fused || nv ? ""
-                      : fused_via_quantizer(a_fmt, w_fmt, m, n, k, flags)
+                      : !via_q ? "fused-quant "
+                      : fused_requires_quantizer(a_fmt, w_fmt, m, n, k, flags)
                           ? "fused-quant (mx_quantize_act into the workspace, then) "
-                          : "fused-quant ";
+                          : "fused-quant (with a workspace: mx_quantize_act into it, then; without: the in-tile "
+                            "prologue) ";
     if (splits > 1)
         std::snprintf(name, len, "%s%s %s, split-K %d with a workspace, else one split", pre, fmt, cfg, splits);
     else

@@ -107,6 +107,8 @@ typedef enum {
                           * default path meets (documented bound 5e-4 * sum|a*b|) */
 #define MX_DEBUG_DUMP_AQ 0x4u /* mx_gemm_fused only: also write the prologue's A codes and scales
                                  to the workspace (see mx_gemm_fused) */
+#define MX_FUSED_IN_GEMM 0x8u /* mx_gemm_fused only: on the quantize-once shapes, quantize A inside
+                                 the GEMM's own launches (see mx_gemm_fused) */
 
 /* ABI version of this header (bumped on any signature change). */
 #define MXLINEAR_ABI_VERSION 8
@@ -215,18 +217,23 @@ mx_status mx_gemm_noalloc(mx_format a_fmt, mx_format w_fmt, const void* a_q, con
  * activation rule: Qwen3.5-9B-MXFP4-QAD-W4A4-LR1e-5-s3000, "Training mode").
  * The result equals mx_quantize_act followed by an unsplit mx_gemm, bit for
  * bit.  Workspace (mx_gemm_fused_workspace_size):
- *  - same-format pairs without MX_DEBUG_DUMP_AQ: optional.  Large MXFP4
- *    shapes (m, n >= 1024, k % 128 == 0) quantize each 256-row block of A
- *    once into it, inside the GEMM's own launches; the exact MXFP8 path does
- *    the same with 128-row blocks (k % 128 == 0, n > 256).  Layout from its
- *    base, which must be 256-byte aligned (MX_ERR_ALIGN): A codes [m, k/2]
- *    (MXFP4) or [m, k] (MXFP8); E8M0 scales [m, k/32] at the next 256-byte
+ *  - same-format pairs on the quantize-once shapes (large MXFP4 shapes: m,
+ *    n >= 1024, k % 128 == 0; exact MXFP8 on its 128 x 128 kernel: k % 128
+ *    == 0, n > 256): optional.  With a workspace, A is quantized into it by
+ *    mx_quantize_act's kernel (codes [m, k * bits / 8], then scales [m,
+ *    k/32]) and mx_gemm's kernel reads it there: two launches, the same work
+ *    as the standalone pair.  With MX_FUSED_IN_GEMM instead, each 256-row
+ *    (MXFP4) or 128-row (MXFP8) block of A is quantized once into it inside
+ *    the GEMM's own launches.  That layout, from a 256-byte aligned base
+ *    (MX_ERR_ALIGN): A codes; E8M0 scales [m, k/32] at the next 256-byte
  *    boundary (both as mx_quantize_act writes them); at the next 256-byte
  *    boundary the int32 state: a chunk pool counter, one done counter per
  *    block and an error word.  The error word is nonzero after the call if
  *    a tile's bounded wait for its block gave up; that tile's part of Y is
  *    then NaN.  Without a workspace (or with MX_FP8_FAST) each tile
  *    quantizes its own rows of A instead.
+ *  - other same-format shapes without MX_DEBUG_DUMP_AQ: none used (each
+ *    tile quantizes its own rows of A; one launch).
  *  - mixed pairs, and exact MXFP8 on the shapes of its large-tile kernel
  *    (k % 128 == 0 and at least 256 tiles of 256 x 256): required
  *    (MX_ERR_WORKSPACE without it).  A is quantized into it (codes [m, k *
@@ -244,8 +251,8 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_format w_fmt, const void* a_bf16, mx
 
 /*
  * mx_gemm_fused_workspace_size -- bytes of workspace mx_gemm_fused uses on
- * this shape, pair and flags (0: none).  With MX_DEBUG_DUMP_AQ, or for a
- * mixed pair, the codes and scales of A (the amount the call requires).
+ * this shape, pair and flags (0: none): the codes and scales of A, or with
+ * MX_FUSED_IN_GEMM on a quantize-once shape that layout with its state.
  * Same argument checks as mx_gemm_fused.
  */
 mx_status mx_gemm_fused_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, int64_t k,

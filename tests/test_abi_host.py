@@ -215,24 +215,31 @@ def test_workspace_sizes():
     assert mxl.mx_gemm_workspace_size("nvfp4", "nvfp4", 96, 160, 4096) > 0
     # tiles that fill the GPU, the decode kernel, the prefill kernel: none
     assert mxl.mx_gemm_workspace_size("mxfp4", "mxfp4", 8192, 17408, 5120) == 0
-    # fused, quantize-once: A codes of the 8192 x 5120 activations, the
-    # scales at the next 256-byte boundary, then at the next one a chunk
-    # pool counter, a done counter per 256-row block and an error word,
-    # rounded up to 256 bytes
+    # fused on a quantize-once shape: by default A's codes and scales for the
+    # standalone quantizer; with MX_FUSED_IN_GEMM the codes, the scales at
+    # the next 256-byte boundary, then at the next one a chunk pool counter,
+    # a done counter per 256-row block and an error word, rounded up to 256
+    # bytes
     def up256(v):
         return (v + 255) // 256 * 256
-    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 8192, 17408, 5120) == 8192 * 2560 + 8192 * 160 + 256
-    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1100, 1090, 1152) == \
+    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 8192, 17408, 5120) == 8192 * 2560 + 8192 * 160
+    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 8192, 17408, 5120, in_gemm=True) == \
+        8192 * 2560 + 8192 * 160 + 256
+    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1100, 1090, 1152, in_gemm=True) == \
         up256(up256(1100 * 576) + 1100 * 36) + 256
     # odd m and odd k/128: the scale plane no longer starts on a cache line
     # after the codes, so it is moved to the next 256-byte boundary
-    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1025, 1090, 1152) == \
+    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1025, 1090, 1152, in_gemm=True) == \
         up256(up256(1025 * 576) + 1025 * 36) + 256
     # mixed pairs: A's codes and scales
     assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp4", 100, 300, 512) == 100 * 512 + 100 * 16
     assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp8", 100, 300, 512) == 100 * 256 + 100 * 16
     assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 512, 2048, 5120) == 0     # not a large shape
-    assert "mx_gemm_prefill_fq_kernel<" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 8192, 17408, 5120, fused=True)
+    assert mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 512, 2048, 5120, in_gemm=True) == 0
+    plan = mxl.mx_gemm_plan("mxfp4", "mxfp4", 8192, 17408, 5120, fused=True)
+    assert "mx_quantize_act into it" in plan and "mx_gemm_prefill_kernel<" in plan
+    assert "mx_gemm_prefill_fq_kernel<" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 8192, 17408, 5120, fused=True,
+                                                           in_gemm=True)
     # exact MXFP8 on the large-tile kernel's shapes (at least 256 tiles of
     # 256 x 256): A's codes [m, k] and scales, quantized by the standalone
     # quantizer; on smaller shapes the quantize-once pool: codes, scales at a
@@ -241,7 +248,8 @@ def test_workspace_sizes():
     assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 8192, 17408, 5120) == 8192 * 5120 + 8192 * 160
     assert "mx8_gemm_tile_kernel" in mxl.mx_gemm_plan("mxfp8", "mxfp8", 4096, 6144, 5120)
     assert "workspace, then" in mxl.mx_gemm_plan("mxfp8", "mxfp8", 4096, 6144, 5120, fused=True)
-    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 1100, 1090, 1152) == \
+    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 1100, 1090, 1152) == 1100 * 1152 + 1100 * 36
+    assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 1100, 1090, 1152, in_gemm=True) == \
         up256(up256(1100 * 1152) + 1100 * 36) + 256
     assert "dq_gemm_kernel" in mxl.mx_gemm_plan("mxfp8", "mxfp8", 1100, 1090, 1152)
     assert mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 8192, 17408, 5120, fp8_fast=True) == 0
@@ -288,14 +296,20 @@ def test_workspace_too_small_is_an_error():
     assert L.mx_gemm_w4a16(2, GOOD, GOOD, GOOD, 96, 160, 4096, 1.0, GOOD, P(0x40000), wneed.value - 1, 0,
                            None) == WORKSPACE
     f = L.mx_gemm_fused
-    fneed = mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1100, 1090, 1152)
-    assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40000), fneed - 1, 0, None) == WORKSPACE
-    # the quantize-once workspace must be 256-byte aligned (its blocks own whole cache lines)
-    assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40010), fneed, 0, None) == ALIGN
-    assert passes_validation(lambda: f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40100), fneed, 0,
+    IN_GEMM = mxl.MX_FUSED_IN_GEMM
+    qneed = mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1100, 1090, 1152)
+    assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40000), qneed - 1, 0, None) == WORKSPACE
+    assert passes_validation(lambda: f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40010), qneed, 0,
                                        None))
-    pneed = mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 1100, 1090, 1152)
-    assert f(1, 1, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40080), pneed, 0, None) == ALIGN
+    fneed = mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", 1100, 1090, 1152, in_gemm=True)
+    assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40000), fneed - 1, IN_GEMM, None) == WORKSPACE
+    # the quantize-once workspace must be 256-byte aligned (its blocks own whole cache lines)
+    assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40010), fneed, IN_GEMM, None) == ALIGN
+    assert passes_validation(lambda: f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40100), fneed,
+                                       IN_GEMM, None))
+    pneed = mxl.mx_gemm_fused_workspace_size("mxfp8", "mxfp8", 1100, 1090, 1152, in_gemm=True)
+    assert f(1, 1, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40080), pneed, IN_GEMM, None) == ALIGN
+    assert f(0, 0, GOOD, 1, GOOD, GOOD, 1100, 1090, 1152, GOOD, P(0x40100), fneed, 0x10, None) == INVALID
 
 
 @fake_pointers
@@ -321,7 +335,7 @@ def test_fused_dump_validation():
     f = L.mx_gemm_fused
     def g(flags=0x4, ws=P(0x40000), wsb=1 << 20, k=64):
         return f(0, 0, GOOD, 1, GOOD, GOOD, 4, 4, k, GOOD, ws, wsb, flags, None)
-    assert g(flags=0x8) == INVALID
+    assert g(flags=0x10) == INVALID
     assert g(ws=None) == WORKSPACE
     assert g(wsb=4 * 32 + 4 * 2 - 1) == WORKSPACE          # codes 4 x 32 B + scales 4 x 2 B
     assert g(ws=BAD_ALIGN) == ALIGN

@@ -309,19 +309,20 @@ def test_prefill_full_output(what, m, k, n):
     say(f"prefill full output {what}: {m}x{k}x{n}, {main} main tiles + {tail} tail tiles")
     assert main > 0 and tail > 0
     assert mxl.mx_gemm_plan("mxfp4", "mxfp4", m, n, k).split(" ", 1)[1].startswith("mx_gemm_prefill_kernel<")
-    assert "mx_gemm_prefill_fq_kernel" in mxl.mx_gemm_plan("mxfp4", "mxfp4", m, n, k, fused=True)
+    assert "mx_gemm_prefill_fq_kernel" in mxl.mx_gemm_plan("mxfp4", "mxfp4", m, n, k, fused=True, in_gemm=True)
     a_bits = W.activations_entry_outliers(m, k)
     w_bits = W.normal_bf16(n, k, 0.02, 1)
     y_ref, s, (raq, ras), (rwq, rws) = oracle_full(a_bits, w_bits, "mxfp4")
     a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
     wq, wsc = mxl.mx_pack_weights(w, "mxfp4", "even")
     aq, as_ = mxl.mx_quantize_act(a, "mxfp4", "ceil")
-    wsz = mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", m, n, k)
+    wsz = mxl.mx_gemm_fused_workspace_size("mxfp4", "mxfp4", m, n, k, in_gemm=True)
     assert wsz > 0
     for out_f32 in (False, True):
         y = mxl.mx_gemm(aq, as_, wq, wsc, k, out_f32=out_f32)
         ws = torch.empty(wsz, dtype=torch.uint8, device="cuda")
-        yq = mxl.mx_gemm_fused(a, wq, wsc, "mxfp4", "ceil", "mxfp4", out_f32=out_f32, workspace=ws)
+        yq = mxl.mx_gemm_fused(a, wq, wsc, "mxfp4", "ceil", "mxfp4", out_f32=out_f32, workspace=ws,
+                               in_gemm=True)
         torch.cuda.synchronize()
         if not out_f32:
             assert np.array_equal(host(aq), raq) and np.array_equal(host(as_), ras)
@@ -467,9 +468,14 @@ def test_nvfp4_fuzz_operands():
         check_gemm(y_host(y), y_ref, s, not out_f32, f"fuzz nvfp4 f32={out_f32}", None, u)
 
 
-# The quantize-once fused path (large MXFP4 shapes with a workspace): the
-# GEMM's workgroups quantize A once into the workspace (claiming 32-row
-# chunks from a pool) and the tiles read the codes from there.  The workspace
+# The quantize-once fused paths (large MXFP4 shapes and exact MXFP8 on the
+# 128 x 128 kernel, with a workspace).  By default A is quantized into the
+# workspace by the standalone quantizer and mx_gemm's kernel runs; with
+# MX_FUSED_IN_GEMM the GEMM's workgroups quantize A once into the workspace
+# (claiming 32-row chunks from a pool) and the tiles read the codes from
+# there.  Both must leave exactly mx_quantize_act's codes and scales in the
+# workspace and give Y bitwise equal to the standalone pair.  For the
+# in-GEMM variant:  The workspace
 # must then hold exactly mx_quantize_act's codes and scales (which also shows
 # that this path ran), the pool and every block's done counter must show all
 # chunks, the error word must be clear, and Y must equal both the standalone
@@ -489,9 +495,10 @@ def up256(v: int) -> int:
 
 @pytest.mark.parametrize("fmt,m,k,n", FQ_CASES)
 def test_fused_quantize_once(fmt, m, k, n):
-    wsz = mxl.mx_gemm_fused_workspace_size(fmt, fmt, m, n, k)
-    say(f"fused quantize-once {fmt} m={m} k={k} n={n}: workspace {wsz} B")
-    assert wsz > 0
+    wsz = mxl.mx_gemm_fused_workspace_size(fmt, fmt, m, n, k, in_gemm=True)
+    qsz = mxl.mx_gemm_fused_workspace_size(fmt, fmt, m, n, k)
+    say(f"fused quantize-once {fmt} m={m} k={k} n={n}: workspace {wsz} B in the GEMM, {qsz} B via the quantizer")
+    assert wsz > 0 and qsz == m * (k // 2 if fmt == "mxfp4" else k) + m * k // 32
     a_bits = W.activations_entry_outliers(m, k)
     w_bits = W.normal_bf16(n, k, 0.02, 1)
     a, w = cuda_bf16(a_bits), cuda_bf16(w_bits)
@@ -504,11 +511,16 @@ def test_fused_quantize_once(fmt, m, k, n):
     for rule in ("ceil", "floor", "even"):
         for out_f32 in (False, True):
             ws = torch.full((wsz,), 0xA5, dtype=torch.uint8, device="cuda")
-            y = mxl.mx_gemm_fused(a, wq, wsc, fmt, rule, fmt, out_f32=out_f32, workspace=ws)
+            y = mxl.mx_gemm_fused(a, wq, wsc, fmt, rule, fmt, out_f32=out_f32, workspace=ws, in_gemm=True)
+            wsq = torch.full((qsz,), 0x5A, dtype=torch.uint8, device="cuda")
+            yq = mxl.mx_gemm_fused(a, wq, wsc, fmt, rule, fmt, out_f32=out_f32, workspace=wsq)
             aq, as_ = mxl.mx_quantize_act(a, fmt, rule)
             y_ref = mxl.mx_gemm(aq, as_, wq, wsc, k, fmt, fmt, out_f32=out_f32, split_k=False)
             y_tile = mxl.mx_gemm_fused(a, wq, wsc, fmt, rule, fmt, out_f32=out_f32, quantize_once=False)
             torch.cuda.synchronize()
+            assert torch.equal(wsq[:qb].view(m, cpr), aq) and torch.equal(wsq[qb:].view(m, k // 32), as_), \
+                f"{rule}: quantizer-path workspace"
+            assert torch.equal(yq, y_ref), f"{rule} f32={out_f32}: quantizer path != standalone"
             assert torch.equal(ws[:qb].view(m, cpr), aq), f"{rule}: workspace codes"
             assert torch.equal(ws[so:so + sb].view(m, k // 32), as_), f"{rule}: workspace scales"
             nb = (m + bm - 1) // bm
