@@ -38,8 +38,6 @@ hipError_t mxl_launch_mx_mixed_exact_gemm(int a_bits, const void* aq, const void
                                           void* work, size_t work_bytes, hipStream_t stream);
 const char* mxl_mx_mixed_exact_config_name(void);
 int mxl_mx8_tile_ok(int64_t m, int64_t n, int64_t k);
-hipError_t mxl_launch_mx8_tile(const void* aq, const void* as, const void* wq, const void* ws, int64_t m, int64_t n,
-                               int64_t k, void* y, int out_f32, hipStream_t stream);
 size_t mxl_dq_workspace(int64_t m, int64_t n, int64_t k);
 int mxl_dq_splits(int64_t m, int64_t n, int64_t k);
 hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, int w_bits,
@@ -69,7 +67,7 @@ int mxl_w4a16_decode_ok(int w_nv, int64_t m, int64_t k);
 const char* mxl_w4a16_gemm_config_name(void);
 const char* mxl_w4a16_decode_config_name(void);
 const char* mxl_mx_gemm_config_name(int a_bits, int w_bits, int64_t m, int64_t n, int64_t k, int fused);
-const char* mxl_nv_gemm_config_name(void);
+const char* mxl_nv_gemm_config_name(int64_t m, int64_t n, int64_t k);
 const char* mxl_mxfp8_exact_config_name(int64_t m, int64_t n, int64_t k);
 }
 
@@ -359,7 +357,8 @@ mx_status mx_gemm_fused(mx_format a_fmt, mx_format w_fmt, const void* a_bf16, mx
         void* as = static_cast<uint8_t*>(workspace) + qb;
         hipError_t e = mxl_launch_mx_quantize(a_fmt == MX_FMT_MXFP4 ? 0 : 1, (int)a_rule, a_bf16, m * k, aq, as, hs);
         if (e != hipSuccess) return MX_ERR_HIP;
-        if (path == PATH_EXACT8) return from_hip(mxl_launch_mx8_tile(aq, as, w_q, w_s, m, n, k, y, f32, hs));
+        if (path == PATH_EXACT8)   // unsplit: the kernel mx_gemm picks without a workspace
+            return from_hip(mxl_launch_mxfp8_exact_gemm(aq, as, w_q, w_s, m, n, k, y, f32, nullptr, 0, hs));
         if (path == PATH_MIXED_EXACT)
             return from_hip(mxl_launch_mx_mixed_exact_gemm(ab, aq, as, w_q, w_s, m, n, k, y, f32, nullptr, 0, hs));
         return from_hip(mxl_launch_mx_gemm(ab, wb, aq, as, w_q, w_s, m, n, k, y, f32, nullptr, 0, hs));
@@ -598,7 +597,7 @@ mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, i
     else std::snprintf(fmt, sizeof fmt, "%sx%s", names[a_fmt], names[w_fmt]);
     const MxPath path = nv ? PATH_EXACT8 : mx_path(a_fmt, w_fmt, flags);
     const bool via_q = fused && !nv && fused_via_quantizer(a_fmt, w_fmt, m, n, k, flags);
-    const char* cfg = nv ? mxl_nv_gemm_config_name()
+    const char* cfg = nv ? mxl_nv_gemm_config_name(m, n, k)
                     : path == PATH_EXACT8 ? mxl_mxfp8_exact_config_name(m, n, k)
                     : path == PATH_MIXED_EXACT ? mxl_mx_mixed_exact_config_name()
                                                : mxl_mx_gemm_config_name(bits_of(a_fmt), bits_of(w_fmt), m, n, k,

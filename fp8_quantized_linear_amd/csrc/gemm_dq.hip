@@ -641,10 +641,19 @@ static hipError_t dq_run(DqArgs a, int out_f32, void* work, size_t work_bytes, h
     return launch(a, out_f32);
 }
 
+extern "C" int mxl_dq8w_ok(int fmt, int64_t m, int64_t n, int64_t k);
+extern "C" hipError_t mxl_launch_dq8w(int fmt, const void* aq, const void* as, const void* wq, const void* ws,
+                                      int64_t m, int64_t n, int64_t k, float alpha, void* y, int out_f32,
+                                      hipStream_t stream);
+extern "C" const char* mxl_dq8w_config_name(void);
+constexpr int DQ8W_FMT_NVFP4 = 2;
+
 extern "C" hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const void* wq, const void* ws,
                                          int64_t m, int64_t n, int64_t k, float alpha, void* y,
                                          int out_f32, void* work, size_t work_bytes, hipStream_t stream)
 {
+    if (mxl_dq8w_ok(DQ8W_FMT_NVFP4, m, n, k))
+        return mxl_launch_dq8w(DQ8W_FMT_NVFP4, aq, as, wq, ws, m, n, k, alpha, y, out_f32, stream);
     DqArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
              static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
              (int)m, (int)n, (int)k, alpha};
@@ -802,8 +811,9 @@ extern "C" const char* mxl_w4a16_gemm_config_name(void)
            "bf16 mfma 32x32x16>";
 }
 
-extern "C" const char* mxl_nv_gemm_config_name(void)
+extern "C" const char* mxl_nv_gemm_config_name(int64_t m, int64_t n, int64_t k)
 {
+    if (mxl_dq8w_ok(DQ8W_FMT_NVFP4, m, n, k)) return mxl_dq8w_config_name();
     return "dq_gemm_kernel<nvfp4 -> exact f16, tile 128x128x64, 2x2 waves of 64x64, f16 mfma 32x32x16>";
 }
 

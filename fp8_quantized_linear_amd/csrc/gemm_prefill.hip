@@ -113,6 +113,7 @@ struct PrefillArgs {
     int M, N, K;
     int tile_base;   // first tile (in the tile order) of this launch
     int count;       // workgroups of this launch
+    float alpha;     // NVFP4: Y = alpha * accumulator
 };
 
 // 16-byte chunk swizzle of the 128-byte LDS rows: the lanes reading the same
@@ -193,6 +194,26 @@ __global__ __launch_bounds__(256, 1) void mx8_gemm_tile_kernel(PrefillArgs p)
     extern __shared__ __align__(16) uint8_t smem[];
 #define PF_TILE_T pf_xcd_order(p.count)
 #include "gemm_tile8.inc"
+#undef PF_TILE_T
+}
+
+// The large-shape exact NVFP4 GEMM on 8 waves (two per SIMD), in the tile
+// structure of the kernels above (gemm_tile_dq8w.inc): the codes are
+// converted to f16 and multiplied by their E4M3 block scales in registers, 6
+// vector instructions per matrix-core instruction, more than one wave per
+// SIMD can issue beside the matrix cores.  Requires K % 256 == 0.  The body
+// also holds the MXFP8 variant; MXFP8 runs on the 4-wave kernel instead,
+// which converts each code twice per tile rather than up to four times and
+// measured as fast (226.9 against 232.9 us on 4096 x 6144 x 5120, bitwise
+// equal): the bf16 matrix cores run at a power-limited clock, and the extra
+// conversions cost as much as the extra issue slots gain.
+constexpr int DQ8W_MXFP8 = 1, DQ8W_NVFP4 = 2;
+template <int FMT, bool OUT_F32, int BN>
+__global__ __launch_bounds__(512, 1) void dq8w_gemm_tile_kernel(PrefillArgs p)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+#define PF_TILE_T pf_xcd_order(p.count)
+#include "gemm_tile_dq8w.inc"
 #undef PF_TILE_T
 }
 
@@ -411,6 +432,36 @@ static hipError_t launch_mx8(const PrefillArgs& a, hipStream_t stream)
     return hipSuccess;
 }
 
+template <int FMT, bool OUT_F32, int BN>
+static hipError_t launch_dq8w_part(PrefillArgs a, int tile_base, int count, hipStream_t stream)
+{
+    auto kern = dq8w_gemm_tile_kernel<FMT, OUT_F32, BN>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           PfLayout<BN>::LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    a.tile_base = tile_base;
+    a.count = count;
+    hipLaunchKernelGGL(kern, dim3(count), dim3(512), PfLayout<BN>::LDS, stream, a);
+    return hipGetLastError();
+}
+
+template <int FMT, bool OUT_F32>
+static hipError_t launch_dq8w(const PrefillArgs& a, hipStream_t stream)
+{
+    const int T = ((a.M + PF_BM - 1) / PF_BM) * ((a.N + 255) / 256);
+    const int tail = prefill_tail_tiles(T, prefill_cu_count());
+    if (T - tail > 0) {
+        const hipError_t e = launch_dq8w_part<FMT, OUT_F32, 256>(a, 0, T - tail, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (tail > 0) return launch_dq8w_part<FMT, OUT_F32, 128>(a, T - tail, 2 * tail, stream);
+    return hipSuccess;
+}
+
 // Clears the quantize-once state (pool and done counters, error word).
 __global__ void pf_zero_kernel(int* p, int n)
 {
@@ -563,4 +614,36 @@ extern "C" const char* mxl_mx8_tile_config_name(void)
     return "mx8_gemm_tile_kernel<mxfp8 -> exact bf16 in registers, tile 256x256, 2x2 waves of 128x128, two 128-K "
            "pair slots + 8-pair scale windows fed by buffer-to-LDS copies, bf16 mfma 32x32x16; a last round at "
            "most half full runs as 256x128 halves>";
+}
+
+// Whether the 8-wave exact GEMM takes this shape: fmt 2 NVFP4 (K % 256 ==
+// 0; fmt 1, MXFP8, is not launched); at least 256 tiles of 256 x 256 (fewer
+// leave compute units idle, and the 128 x 128 kernel with split-K serves
+// them); code bytes plus one tile of overrun rows within 32-bit buffer
+// offsets.
+extern "C" int mxl_dq8w_ok(int fmt, int64_t m, int64_t n, int64_t k)
+{
+    if (fmt != DQ8W_NVFP4) return 0;
+    if (k % (fmt == DQ8W_NVFP4 ? 256 : 128) != 0 || ((m + 255) / 256) * ((n + 255) / 256) < 256) return 0;
+    const int64_t rb = fmt == DQ8W_NVFP4 ? k / 2 : k;
+    const int64_t lim = ((int64_t)1 << 31) - (int64_t)PF_BM * rb - 1024;
+    return (m + PF_BM) * rb < lim && (n + 256) * rb < lim ? 1 : 0;
+}
+
+extern "C" hipError_t mxl_launch_dq8w(int fmt, const void* aq, const void* as, const void* wq, const void* ws,
+                                      int64_t m, int64_t n, int64_t k, float alpha, void* y, int out_f32,
+                                      hipStream_t stream)
+{
+    PrefillArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
+                  static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y, nullptr, nullptr,
+                  (int)m, (int)n, (int)k, 0, 0, alpha};
+    if (fmt != DQ8W_NVFP4) return hipErrorInvalidValue;
+    return out_f32 ? launch_dq8w<DQ8W_NVFP4, true>(a, stream) : launch_dq8w<DQ8W_NVFP4, false>(a, stream);
+}
+
+extern "C" const char* mxl_dq8w_config_name(void)
+{
+    return "dq8w_gemm_tile_kernel<nvfp4 -> exact f16 in registers, tile 256x256, 8 waves (2 per SIMD) as 2x4 of "
+           "128x64, two 256-K pair slots + 2-pair scale windows fed by buffer-to-LDS copies, f16 mfma 32x32x16; a "
+           "last round at most half full runs as 256x128 halves>";
 }

@@ -610,6 +610,39 @@ def test_nvfp4_full_small(m, k, n):
         check_gemm(y_host(y), y_ref, s, not out_f32, f"nvfp4 {m}x{k}x{n}")
 
 
+# Full-output parity of the 8-wave NVFP4 kernel (at least 256 tiles of 256 x
+# 256, K % 256 == 0): 4352 x 4096 is 17 x 16 = 272 tiles, a main launch and
+# a tail of 16 tiles as 256 x 128 halves; K = 1280 is 5 pairs of 256 (three
+# scale windows of 2 pairs, the last with one).  Normal activations as in
+# the NVFP4 workload, and fuzz-corpus operands whose E4M3 block scales reach
+# the subnormal ones; bf16 and fp32 output.
+@pytest.mark.parametrize("data", ["normal", "fuzz"])
+def test_nvfp4_tile_full_output(data):
+    m, k, n = 4352, 1280, 4096
+    plan = mxl.mx_gemm_plan("nvfp4", "nvfp4", m, n, k)
+    say(f"nvfp4 tile full output ({data}) {m}x{k}x{n}: {plan[:60]}")
+    assert "dq8w_gemm_tile_kernel" in plan
+    if data == "normal":
+        a_bits, w_bits = W.normal_bf16(m, k, 1.0, 0), W.normal_bf16(n, k, 0.02, 1)
+    else:
+        a_bits, w_bits = fuzz_operands(m, k, n)
+    g_a = oracle.nv_global_scale(oracle.bf16_amax(a_bits))
+    g_w = oracle.nv_global_scale(oracle.bf16_amax(w_bits))
+    aq, as_ = oracle.nv_quantize(a_bits, g_a)
+    wq, ws = oracle.nv_quantize(w_bits, g_w)
+    if data == "fuzz":
+        say(f"  E4M3 block scales below 2^-6 (subnormal): A {int(((as_ & 0x78) == 0).sum())}, "
+            f"W {int(((ws & 0x78) == 0).sum())}")
+    y_ref, s = oracle.gemm_dq(oracle.nv_dequantize(aq, as_, m, k, g_a), oracle.nv_dequantize(wq, ws, n, k, g_w))
+    u = underflow_allowance(k) if data == "fuzz" else 0.0
+    for out_f32 in (False, True):
+        y, (gaq, gas), (gwq, gws) = nv_case(a_bits, w_bits, g_a, g_w, out_f32)
+        assert np.array_equal(host(gaq), aq) and np.array_equal(host(gas), as_)
+        assert np.array_equal(host(gwq), wq) and np.array_equal(host(gws), ws)
+        rel = check_gemm(y_host(y), y_ref, s, not out_f32, f"nvfp4 tile {data} f32={out_f32}", None, u)
+        say(f"  f32={out_f32}: max err/S {rel:.2e}")
+
+
 def test_nvfp4_config_sampled():
     cfg = W.NVFP4
     run = max(oracle.bf16_amax(b) for b in cfg.calibration_batches())
