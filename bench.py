@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import platform
 import json
 import os
 import sys
@@ -107,8 +108,14 @@ def main():
     # ------------------------------------------------------------ headline inputs
     t0 = time.time()
     up, down = W.PREFILL_UP, W.PREFILL_DOWN
-    a_up, w_up = to_dev(up.activations()), to_dev(up.weights())
-    a_dn, w_dn = to_dev(down.activations()), to_dev(down.weights())
+    host_inputs = {"a_up": up.activations(), "w_up": up.weights(), "a_down": down.activations(),
+                   "w_down": down.weights()}
+    # SHA-256 of each bf16 input's bytes (row-major), so that another run can
+    # show it timed the same data
+    input_sha = {k: hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest() for k, v in host_inputs.items()}
+    a_up, w_up = to_dev(host_inputs["a_up"]), to_dev(host_inputs["w_up"])
+    a_dn, w_dn = to_dev(host_inputs["a_down"]), to_dev(host_inputs["w_down"])
+    del host_inputs
     log(f"inputs generated in {time.time() - t0:.1f}s")
 
     # offline weight packing (timed separately)
@@ -195,6 +202,8 @@ def main():
                                "per-token CEIL quantize + block-scaled FP4 GEMM, bf16 out",
                    "m": up.m, "k_up": up.k, "n_up": up.n, "k_down": down.k, "n_down": down.n,
                    "step_flop": step_flops},
+        "inputs_sha256": input_sha,
+        "host": host_info(torch),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "rows": rows,
@@ -611,6 +620,21 @@ def extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_d
         log(f"small {name}: {t_split:.1f} us (unsplit {t_one:.1f} us)")
         del ws_, wq_, wsc_, a_, aq_, as_, y_
     return rows
+
+
+def host_info(torch):
+    """CPU model and logical CPU count of the host, and the GPU's name."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model or platform.processor() or "unknown", "logical_cpus": os.cpu_count(),
+            "gpu": torch.cuda.get_device_name(0)}
 
 
 def cpu_baseline(cfg, target_s):

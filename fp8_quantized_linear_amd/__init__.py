@@ -20,7 +20,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmxlinear.so")
+# MXL_SANITIZED=1 loads the build whose host layer runs under ASan and UBSan
+# (build.build_sanitized); the process must preload clang's ASan runtime.
+LIB_PATH = os.path.join(_PKG, "libmxlinear_san.so" if os.environ.get("MXL_SANITIZED") == "1" else "libmxlinear.so")
 
 FORMATS = {"mxfp4": 0, "mxfp8": 1, "nvfp4": 2}
 RULES = {"floor": 0, "ceil": 1, "even": 2}

@@ -76,6 +76,10 @@ extern "C" {
  * HIP headers. */
 typedef void* mx_stream_t;
 
+/* Each enum carries two range markers so that its type holds every int:
+ * a caller may pass any int where an enum is expected, and the functions
+ * reject unknown values with MX_ERR_INVALID_ARG (or describe them, for
+ * mx_status_string) instead of reading an out-of-range enum value. */
 typedef enum {
     MX_OK = 0,
     MX_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, bad format/rule pair */
@@ -83,19 +87,22 @@ typedef enum {
     MX_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned (256 for the quantize-once workspace) */
     MX_ERR_WORKSPACE = 4,   /* a non-NULL workspace smaller than the call needs, or none where one is required */
     MX_ERR_UNSUPPORTED = 5, /* device is not gfx950, or the selected kernel cannot address operands this large */
-    MX_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+    MX_ERR_HIP = 6,         /* a HIP runtime call or launch failed */
+    MX_STATUS_RANGE_MIN_ = -2147483647 - 1, MX_STATUS_RANGE_MAX_ = 2147483647
 } mx_status;
 
 typedef enum {
     MX_FMT_MXFP4 = 0, /* E2M1 elements, E8M0 scale per 32 */
     MX_FMT_MXFP8 = 1, /* E4M3 elements, E8M0 scale per 32 */
-    MX_FMT_NVFP4 = 2  /* E2M1 elements, E4M3 scale per 16, fp32 global scale */
+    MX_FMT_NVFP4 = 2, /* E2M1 elements, E4M3 scale per 16, fp32 global scale */
+    MX_FMT_RANGE_MIN_ = -2147483647 - 1, MX_FMT_RANGE_MAX_ = 2147483647
 } mx_format;
 
 typedef enum {
     MX_RULE_FLOOR = 0, /* e = floor(log2 amax) - emax (OCP MX v1.0) */
     MX_RULE_CEIL = 1,  /* smallest e with amax <= max_elem * 2^e (activations) */
-    MX_RULE_EVEN = 2   /* amax rounded to the element's mantissa width, then FLOOR (weights) */
+    MX_RULE_EVEN = 2,  /* amax rounded to the element's mantissa width, then FLOOR (weights) */
+    MX_RULE_RANGE_MIN_ = -2147483647 - 1, MX_RULE_RANGE_MAX_ = 2147483647
 } mx_scale_rule;
 
 /* GEMM flags */

@@ -33,7 +33,12 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mx_oracle.c")
-_LIB = os.path.join(_HERE, "libmxoracle.so")
+# MXL_SANITIZED=1 selects the AddressSanitizer + UndefinedBehaviorSanitizer
+# build (build(sanitize=True)); the process must then preload clang's ASan
+# runtime, as tests/test_sanitized_host.py does.
+_SANITIZED = os.environ.get("MXL_SANITIZED") == "1"
+_LIB = os.path.join(_HERE, "libmxoracle_san.so" if _SANITIZED else "libmxoracle.so")
+_CLANG = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang")
 
 E2M1, E4M3 = 0, 1
 FLOOR, CEIL, EVEN = 0, 1, 2
@@ -43,14 +48,24 @@ RULES = {"floor": FLOOR, "ceil": CEIL, "even": EVEN}
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile mx_oracle.c with gcc (-O2, no fast-math, OpenMP)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-fopenmp", "-fPIC", "-shared",
-                               "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile mx_oracle.c with gcc (-O2, no fast-math, OpenMP).  With
+    sanitize, into libmxoracle_san.so with clang, AddressSanitizer and
+    UndefinedBehaviorSanitizer (any finding aborts), against the shared ASan
+    runtime."""
+    out = os.path.join(_HERE, "libmxoracle_san.so" if sanitize else "libmxoracle.so")
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        tmp = out + ".tmp"
+        if sanitize:
+            llvm_lib = os.path.join(os.path.dirname(os.path.dirname(_CLANG)), "lib")
+            cmd = [_CLANG, "-O1", "-g", "-std=c11", "-Wall", "-fopenmp", "-fPIC", "-shared",
+                   "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+                   "-shared-libsan", f"-Wl,-rpath,{llvm_lib}", "-o", tmp, _SRC, "-lm"]
+        else:
+            cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, out)
+    return out
 
 
 def _nthreads(n=None) -> int:
@@ -64,7 +79,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
+            build(force=True, sanitize=_SANITIZED)
         L = ctypes.CDLL(_LIB)
         d, i32, i64, u16, f32 = (ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_uint16,
                                  ctypes.c_float)
