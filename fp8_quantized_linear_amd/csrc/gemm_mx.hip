@@ -874,6 +874,200 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(GemmArgs p)
     }
 }
 
+// Decode-shaped MXFP4 GEMM streamed per wave (M <= 16 MT, MT <= 2, K =
+// 1024 QS / 2 with QS stages of 128 per wave, K <= 8192).  One workgroup of
+// 4 waves owns 16 rows of W and wave w a contiguous quarter of K.  Each wave
+// copies its own 16 x K/8-byte part of W into its own LDS region and
+// consumes it stage by stage as the copies land, so no wave waits for
+// another one (or for the whole block) before its matrix-core work; the
+// four partial sums meet once, at the end.
+//  * Copy (c, h) moves rows 8 h .. 8 h + 7 x bytes [128 c, 128 c + 128) of
+//    the wave's quarter: 8 full cache lines, 1 KiB.  The copies go out in c
+//    order, and stages 2 c and 2 c + 1 wait for copies (c, 0) and (c, 1)
+//    only, with an exact vmcnt.
+//  * Inside the 1 KiB of copy (c, h), row q of the group (8 h <= q < 8 h +
+//    8) holds its 16-byte chunk L at 128 (q % 8) + 16 (L ^ ((q >> 1) & 7)):
+//    the 16 rows of one lane group, reading the same chunk, cover all 64
+//    banks.  The swizzle is chosen by which chunk each copy lane fetches.
+//  * The A fragments of all the wave's stages (MT groups of 16 rows; rows
+//    past M read as zero through the buffer range check) and the scale
+//    dwords of its stages (a row's dword 4 s .. 4 s + 3 holds stage s's 4
+//    blocks) are loaded into registers before the copies are issued, so the
+//    copies' waits cover them as well.
+//  * Operands follow v_mfma_scale_f32_16x16x128_f8f6f4 (lane r + 16 g: row
+//    r, K elements [32 g, 32 g + 32) of the stage), as in mx_decode_kernel,
+//    and the partial sums are added in the same wave order.
+// s_waitcnt vmcnt(n) for an n that folds to a constant once loops are
+// unrolled (n <= 14 here)
+__device__ __forceinline__ void wait_vmcnt_n(int n)
+{
+    switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<0>(); break;
+    }
+}
+
+__device__ __forceinline__ uint32_t lds_read_u32(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>((size_t)addr);
+}
+
+__device__ __forceinline__ int4_t lds_read_v4(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) int4_t*>((size_t)addr);
+}
+
+template <int MT, int QS, bool OUT_F32>
+__global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
+{
+    constexpr int WAVES = 4, NC = QS / 2;
+    static_assert(QS % 2 == 0 && QS <= 16 && MT <= 2, "decode stream shape");
+    extern __shared__ __align__(16) uint8_t dsm[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the copy offsets go in SGPRs
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int K = QS * 512, KB = K / 32, row_bytes = K / 2;
+    const int QB = row_bytes / WAVES;     // W bytes per row per wave (64 QS)
+    const int st0 = wave * QS;            // this wave's first stage
+
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_q, (short)0, p.M * row_bytes, 0x00020000);
+    const int4_t rw = make_rsrc(p.w_q, (uint32_t)p.N * row_bytes);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dsm);
+    const uint32_t lds_w = lds0 + (uint32_t)(wave * 16 * QB);   // this wave's 2 NC blocks of 1 KiB
+
+    // The scale blocks of the workgroup's 16 W rows and of A's 16 MT rows
+    // (contiguous [rows][K/32] byte ranges) go to LDS first, 256 bytes per
+    // copy, spread over the waves; one barrier publishes them.
+    constexpr int SCOP = (1 + MT) * QS;   // 16 KB / 256 bytes per 16 rows
+    const uint32_t sw_lds = lds0 + (uint32_t)(16 * row_bytes), sa_lds = sw_lds + (uint32_t)(16 * KB);
+    {
+        const int4_t rws4 = make_rsrc(p.w_s, (uint32_t)p.N * KB);
+        const int4_t ras4 = make_rsrc(p.a_s, (uint32_t)p.M * KB);
+#pragma unroll
+        for (int j = 0; j < SCOP; ++j)
+            if (j % WAVES == wave) {
+                if (j < QS) dma_b32(sw_lds + j * 256, n0 * KB + j * 256 + lane * 4, rws4, 0);
+                else dma_b32(sw_lds + j * 256, (j - QS) * 256 + lane * 4, ras4, 0);
+            }
+    }
+    // A fragments of every stage of the wave
+    int4_t af[QS][MT];
+#pragma unroll
+    for (int u = 0; u < QS; ++u)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            af[u][t] = __builtin_amdgcn_raw_buffer_load_b128(ra, (16 * t + r) * row_bytes + g * 16, (st0 + u) * 64, 0);
+    // the wave's W copies, in stage order
+    int voffh[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = 8 * h + (lane >> 3);
+        voffh[h] = (n0 + q) * row_bytes + (((lane & 7) ^ ((q >> 1) & 7)) * 16);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) dma_b128(lds_w + (uint32_t)((2 * c + h) * 1024), voffh[h], rw, wave * QB + c * 128);
+
+    // the scale copies have landed once at most the A loads and W copies
+    // issued after them are outstanding
+    wait_vmcnt<QS * MT + QS>();
+    lds_barrier();
+
+    float4_t_ acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = float4_t_{0.f, 0.f, 0.f, 0.f};
+    const uint32_t rd = lds_w + (uint32_t)((r >> 3) * 1024 + (r & 7) * 128);
+    const int rsw = (r >> 1) & 7;
+    const uint32_t rsw_l = sw_lds + (uint32_t)(r * KB + 4 * st0), rsa_l = sa_lds + (uint32_t)(r * KB + 4 * st0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        // copies (c, 0) and (c, 1) have landed once at most the 2 (NC - 1 - c)
+        // copies issued after them are outstanding
+        wait_vmcnt_n(2 * (NC - 1 - c));
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int u = 2 * c + hf;
+            const int4_t wv = lds_read_v4(rd + (uint32_t)(2 * c * 1024 + (((4 * hf + g) ^ rsw) * 16)));
+            const int8_t_ b8 = int8_t_{wv[0], wv[1], wv[2], wv[3], 0, 0, 0, 0};
+            // a row's scale dword for stage s holds blocks 4 s .. 4 s + 3; lane group g takes byte g
+            const int wsb = (int)(lds_read_u32(rsw_l + 4 * u) >> (8 * g));
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const int asb = (int)(lds_read_u32(rsa_l + (uint32_t)(16 * t * KB + 4 * u)) >> (8 * g));
+                const int8_t_ a8 = int8_t_{af[u][t][0], af[u][t][1], af[u][t][2], af[u][t][3], 0, 0, 0, 0};
+                acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 4, 4, 0, asb, 0, wsb);
+            }
+        }
+    }
+    __syncthreads();   // every wave is done with its LDS region
+    float4_t_* red = reinterpret_cast<float4_t_*>(dsm);   // [WAVES][MT][64]
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[(wave * MT + t) * 64 + lane] = acc[t];
+    __syncthreads();
+    // thread e < MT * 64 finishes accumulator lane e % 64 of A tile t:
+    // A rows 16 t + 4 (l / 16) + i, W row n0 + l % 16
+    if (tid < MT * 64) {
+        const int l = tid & 63, t = tid >> 6;
+        float4_t_ v = red[t * 64 + l];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+            const float4_t_ x = red[(w * MT + t) * 64 + l];
+            v = float4_t_{v[0] + x[0], v[1] + x[1], v[2] + x[2], v[3] + x[3]};
+        }
+        const int nn = n0 + (l & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 16 * t + 4 * (l >> 4) + i;
+            if (m < p.M && nn < p.N) {
+                if (OUT_F32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + nn] = v[i];
+                else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + nn] = f32_to_bf16_rne(v[i]);
+            }
+        }
+    }
+}
+
+template <int MT>
+static size_t decode_stream_lds_bytes(int K) { return (size_t)16 * (K / 2) + (size_t)16 * (1 + MT) * (K / 32); }
+
+// whether mx_decode_stream_kernel serves M rows of A at this K (its LDS
+// within 64 KiB)
+static bool decode_stream_ok(int64_t m, int64_t k)
+{
+    if (m > 32 || k % 1024 != 0 || k < 1024 || k > 8192) return false;
+    return (m <= 16 ? decode_stream_lds_bytes<1>((int)k) : decode_stream_lds_bytes<2>((int)k)) <= 65536;
+}
+
+template <int MT, int QS, bool OUT_F32>
+static void launch_decode_stream_qs(const GemmArgs& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, OUT_F32>), dim3((a.N + 15) / 16), dim3(256),
+                       decode_stream_lds_bytes<MT>(a.K), stream, a);
+}
+
+template <int MT, bool OUT_F32>
+static void launch_decode_stream(const GemmArgs& a, hipStream_t stream)
+{
+    switch (a.K / 512) {
+    case 2: launch_decode_stream_qs<MT, 2, OUT_F32>(a, stream); break;
+    case 4: launch_decode_stream_qs<MT, 4, OUT_F32>(a, stream); break;
+    case 6: launch_decode_stream_qs<MT, 6, OUT_F32>(a, stream); break;
+    case 8: launch_decode_stream_qs<MT, 8, OUT_F32>(a, stream); break;
+    case 10: launch_decode_stream_qs<MT, 10, OUT_F32>(a, stream); break;
+    case 12: launch_decode_stream_qs<MT, 12, OUT_F32>(a, stream); break;
+    case 14: launch_decode_stream_qs<MT, 14, OUT_F32>(a, stream); break;
+    default: launch_decode_stream_qs<MT, 16, OUT_F32>(a, stream); break;
+    }
+}
+
 template <int MT>
 static size_t decode_lds_bytes(int K)
 {
@@ -902,6 +1096,12 @@ static int decode_kind(int64_t m, int64_t k)
 template <int MT, bool OUT_F32>
 hipError_t launch_decode(const GemmArgs& a, hipStream_t stream)
 {
+    if constexpr (MT <= 2) {
+        if (decode_stream_ok(a.M, a.K)) {
+            launch_decode_stream<MT, OUT_F32>(a, stream);
+            return hipGetLastError();
+        }
+    }
     const int kind = decode_kind_mt<MT>(a.K);
     if (kind == 2)
         hipLaunchKernelGGL((mx_decode_kernel<MT, OUT_F32>), dim3((a.N + 15) / 16), dim3(256), decode_lds_bytes<MT>(a.K),
@@ -1079,6 +1279,9 @@ extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int w_bits, int64_t m
 {
     switch (classify(a_bits, w_bits, m, n, k, fused != 0)) {
     case SC_DECODE:
+        if (decode_stream_ok(m, k))
+            return "mx_decode_stream_kernel<16 W rows per workgroup, each wave copies its own K quarter into LDS "
+                   "(8 rows x 128 B per copy) and computes each stage as its copies land, scaled mfma 16x16x128>";
         switch (decode_kind(m, k)) {
         case 2: return "mx_decode_kernel<16 W rows per workgroup, whole-row copies into swizzled LDS, 4 waves over K "
                        "quarters, scaled mfma 16x16x128>";

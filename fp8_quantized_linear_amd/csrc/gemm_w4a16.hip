@@ -91,6 +91,32 @@ __device__ __forceinline__ bf16x8_w w4_dequant8(uint32_t codes, float s, int e)
     return v;
 }
 
+// LDS reads at a byte address of the workgroup's LDS
+__device__ __forceinline__ uint32_t w4_lds_u32(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>((size_t)addr);
+}
+__device__ __forceinline__ int4_t w4_lds_v4(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) int4_t*>((size_t)addr);
+}
+// s_waitcnt vmcnt(n) for an n that folds to a constant once loops are
+// unrolled (even n <= 14)
+__device__ __forceinline__ void w4_wait_vmcnt_n(int n)
+{
+    switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<0>(); break;
+    }
+}
+
 template <bool NV>
 static size_t w4a16_decode_lds_bytes(int K)
 {
@@ -207,6 +233,166 @@ __global__ __launch_bounds__(256) void w4a16_decode_kernel(W4a16Args p)
     wait_vmcnt<0>();   // the trailing A loads have returned
 }
 
+// The same product streamed per wave, for M <= 2 rows of A, K % 1024 == 0
+// (QS = K / 512 stages of 128 per wave).  As in mx_decode_stream_kernel, wave
+// w owns a contiguous quarter of K: it copies its 16 x K/8 bytes of W codes
+// into its own LDS region (8 rows x 128 B per copy, copies in stage order),
+// and its quarter of each A row next to them, so that it can compute each
+// stage as soon as that stage's copies have landed, with an exact vmcnt and
+// no wait on the other waves.  The W scale block (16 rows) is copied once by
+// all waves together and published by one barrier before the first stage.
+//  * LDS: [4 W regions of 16 x K/8 bytes][A: M rows x K bf16][W scales 16 x KS].
+//  * Lane (r, g) of stage s (global stage st) holds W row r, K elements
+//    [128 st + 32 g, +32) (one 16-byte unit), dequantized 8 elements per
+//    MFMA step j, and A row min(r, M - 1), K [128 st + 32 g + 8 j, +8): the
+//    rows past M repeat a real row and only feed output rows that are never
+//    stored.  The K assignment, the step order and the wave order of the
+//    final sum are those of w4a16_decode_kernel, so the results are the same.
+template <bool NV, int QS, bool OUT_F32>
+__global__ __launch_bounds__(256) void w4a16_decode_stream_kernel(W4a16Args p)
+{
+    constexpr int WAVES = 4, NC = QS / 2;
+    constexpr int K = QS * 512, row_bytes = K / 2, KS = K / (NV ? 16 : 32), QB = row_bytes / WAVES;
+    extern __shared__ __align__(16) uint8_t dsm[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int st0 = wave * QS;
+    const int M = p.M;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dsm);
+    const uint32_t lds_w = lds0 + (uint32_t)(wave * 16 * QB);
+    const uint32_t a_lds = lds0 + (uint32_t)(16 * row_bytes);
+    const uint32_t s_lds = a_lds + (uint32_t)(M * K * 2);
+
+    // 1. the W scale block, 256 bytes per copy, spread over the waves
+    constexpr int SCOP = 16 * KS / 256;
+    {
+        const int4_t rws = make_rsrc(p.w_s, (uint32_t)p.N * KS);
+#pragma unroll
+        for (int j = 0; j < SCOP; ++j)
+            if (j % WAVES == wave) dma_b32(s_lds + j * 256, n0 * KS + j * 256 + lane * 4, rws, 0);
+    }
+    // 2. this wave's quarter of each A row (bf16: K/2 bytes), 256 bytes per copy
+    constexpr int ACOP = (K / 2) / 256;   // per A row: a quarter of K in bf16
+    {
+        const int4_t ra = make_rsrc(p.a, (uint32_t)M * K * 2);
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int j = 0; j < ACOP; ++j)
+                dma_b32(a_lds + (uint32_t)(m * K * 2 + wave * (K / 2) + j * 256), m * K * 2 + wave * (K / 2) + j * 256 + lane * 4,
+                        ra, 0);
+    }
+    // 3. this wave's W codes, in stage order
+    {
+        const int4_t rw = make_rsrc(p.w_q, (uint32_t)p.N * row_bytes);
+        int voffh[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int q = 8 * h + (lane >> 3);
+            voffh[h] = (n0 + q) * row_bytes + (((lane & 7) ^ ((q >> 1) & 7)) * 16);
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                dma_b128(lds_w + (uint32_t)((2 * c + h) * 1024), voffh[h], rw, wave * QB + c * 128);
+    }
+    // the scale and A copies have landed once at most the QS W copies are
+    // outstanding; the barrier publishes the scale block
+    wait_vmcnt<QS>();
+    lds_barrier();
+
+    f32x4_w acc = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t rd = lds_w + (uint32_t)((r >> 3) * 1024 + (r & 7) * 128);
+    const int rsw = (r >> 1) & 7;
+    const uint32_t arow = a_lds + (uint32_t)((r < M ? r : M - 1) * K * 2 + st0 * 256 + g * 64);
+    const uint32_t srow = s_lds + (uint32_t)(r * KS);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        w4_wait_vmcnt_n(2 * (NC - 1 - c));
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int u = 2 * c + hf, un = 4 * (st0 + u) + g;   // global 16-byte unit of the W row
+            const int4_t cw = w4_lds_v4(rd + (uint32_t)(2 * c * 1024 + (((4 * hf + g) ^ rsw) * 16)));
+            float s_lo = 1.0f, s_hi = 1.0f;
+            int e = 0;
+            if (NV) {
+                const uint32_t sp = w4_lds_u32(srow + (uint32_t)(2 * un) & ~3u) >> (8 * ((2 * un) & 3));
+                s_lo = w4_e4m3_to_f32(sp & 0xFFu);
+                s_hi = w4_e4m3_to_f32((sp >> 8) & 0xFFu);
+            } else {
+                e = (int)((w4_lds_u32(srow + (uint32_t)un & ~3u) >> (8 * (un & 3))) & 0xFFu) - 127;
+            }
+            const uint32_t cws[4] = {(uint32_t)cw[0], (uint32_t)cw[1], (uint32_t)cw[2], (uint32_t)cw[3]};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8_w b8 = w4_dequant8<NV>(cws[j], j < 2 ? s_lo : s_hi, e);
+                const bf16x8_w a8 = __builtin_bit_cast(bf16x8_w, w4_lds_v4(arow + (uint32_t)(u * 256 + j * 16)));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();   // every wave is done with its LDS regions
+    f32x4_w* red = reinterpret_cast<f32x4_w*>(dsm);   // [WAVES][64]
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (tid < 64) {
+        f32x4_w v = red[tid];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+            const f32x4_w x = red[w * 64 + tid];
+            v = f32x4_w{v[0] + x[0], v[1] + x[1], v[2] + x[2], v[3] + x[3]};
+        }
+        const int nn = n0 + (tid & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * (tid >> 4) + i;
+            if (m < p.M && nn < p.N) {
+                const float o = v[i] * p.alpha;
+                if (OUT_F32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + nn] = o;
+                else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + nn] = f32_to_bf16_rne(o);
+            }
+        }
+    }
+}
+
+template <bool NV>
+static size_t w4a16_stream_lds_bytes(int64_t m, int64_t k)
+{
+    return (size_t)(16 * (k / 2) + m * k * 2 + 16 * (k / (NV ? 16 : 32)));
+}
+
+// whether w4a16_decode_stream_kernel serves this shape
+static bool w4a16_stream_ok(int w_nv, int64_t m, int64_t k)
+{
+    if (m > 2 || k % 1024 != 0 || k < 1024 || k > 8192) return false;
+    return (w_nv ? w4a16_stream_lds_bytes<true>(m, k) : w4a16_stream_lds_bytes<false>(m, k)) <= 65536;
+}
+
+template <bool NV, int QS, bool OUT_F32>
+static void launch_w4a16_stream_qs(const W4a16Args& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((w4a16_decode_stream_kernel<NV, QS, OUT_F32>), dim3((a.N + 15) / 16), dim3(256),
+                       w4a16_stream_lds_bytes<NV>(a.M, a.K), stream, a);
+}
+
+template <bool NV, bool OUT_F32>
+static hipError_t launch_w4a16_stream(const W4a16Args& a, hipStream_t stream)
+{
+    switch (a.K / 512) {
+    case 2: launch_w4a16_stream_qs<NV, 2, OUT_F32>(a, stream); break;
+    case 4: launch_w4a16_stream_qs<NV, 4, OUT_F32>(a, stream); break;
+    case 6: launch_w4a16_stream_qs<NV, 6, OUT_F32>(a, stream); break;
+    case 8: launch_w4a16_stream_qs<NV, 8, OUT_F32>(a, stream); break;
+    case 10: launch_w4a16_stream_qs<NV, 10, OUT_F32>(a, stream); break;
+    case 12: launch_w4a16_stream_qs<NV, 12, OUT_F32>(a, stream); break;
+    case 14: launch_w4a16_stream_qs<NV, 14, OUT_F32>(a, stream); break;
+    default: launch_w4a16_stream_qs<NV, 16, OUT_F32>(a, stream); break;
+    }
+    return hipGetLastError();
+}
+
 template <bool NV, bool OUT_F32>
 static hipError_t launch_w4a16_decode(const W4a16Args& a, hipStream_t stream)
 {
@@ -233,12 +419,19 @@ extern "C" hipError_t mxl_launch_w4a16_decode(int w_nv, const void* a_bf16, cons
 {
     W4a16Args a{static_cast<const uint8_t*>(a_bf16), static_cast<const uint8_t*>(wq),
                 static_cast<const uint8_t*>(ws), y, (int)m, (int)n, (int)k, alpha};
+    if (w4a16_stream_ok(w_nv, m, k)) {
+        if (w_nv) return out_f32 ? launch_w4a16_stream<true, true>(a, stream) : launch_w4a16_stream<true, false>(a, stream);
+        return out_f32 ? launch_w4a16_stream<false, true>(a, stream) : launch_w4a16_stream<false, false>(a, stream);
+    }
     if (w_nv) return out_f32 ? launch_w4a16_decode<true, true>(a, stream) : launch_w4a16_decode<true, false>(a, stream);
     return out_f32 ? launch_w4a16_decode<false, true>(a, stream) : launch_w4a16_decode<false, false>(a, stream);
 }
 
-extern "C" const char* mxl_w4a16_decode_config_name(void)
+extern "C" const char* mxl_w4a16_decode_config_name(int w_nv, int64_t m, int64_t k)
 {
+    if (w4a16_stream_ok(w_nv, m, k))
+        return "w4a16_decode_stream_kernel<16 W rows per workgroup, each wave copies its own K quarter of W and A "
+               "into LDS and computes each stage as its copies land, bf16 mfma 16x16x32>";
     return "w4a16_decode_kernel<16 W rows per workgroup, whole-row copies into swizzled LDS, 4 waves over K "
            "quarters in groups of 128, A two groups ahead, bf16 mfma 16x16x32>";
 }

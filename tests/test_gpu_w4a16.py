@@ -51,6 +51,8 @@ def alpha_of(g):
 
 
 CASES = [
+    # per-wave streamed decode kernel: M <= 2, K % 1024 == 0, LDS within 64 KiB
+    (1, 1024, 300), (2, 5120, 100), (1, 6144, 33), (2, 3072, 17),
     # decode kernel: M <= 16, K % 512 == 0
     (1, 512, 16), (3, 1024, 100), (16, 512, 300), (8, 2048, 33),
     # general kernel
@@ -63,6 +65,10 @@ CASES = [
 def test_w4a16_full(fmt, m, k, n):
     plan = mxl.mx_gemm_w4a16_plan(fmt, m, n, k)
     say(f"w4a16 {fmt} m={m} k={k} n={n}: {plan}")
+    # the streamed kernel holds W codes, A and the W scale block in 64 KiB of LDS
+    lds = 16 * (k // 2) + m * k * 2 + 16 * (k // (16 if fmt == "nvfp4" else 32))
+    if m <= 2 and k % 1024 == 0 and lds <= 65536:
+        assert "w4a16_decode_stream_kernel<" in plan
     a_bits = W.activations_entry_outliers(m, k)
     w_bits = W.normal_bf16(n, k, 0.02, 1)
     wq, ws, rq, rs, g = pack(w_bits, fmt)
