@@ -317,10 +317,13 @@ def traffic_from_profiles():
     return rec.get("traffic_bytes_per_launch")
 
 
+# the sources of mx_gemm_prefill_kernel (the kernel the traffic record covers)
+PREFILL_SOURCES = ("mx_device.h", "gemm_prefill.hip", "gemm_prefill_tile.inc", "gemm_tile_epilogue.inc")
+
+
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("mx_device.h", "gemm_mx.hip", "gemm_prefill.hip", "gemm_prefill_tile.inc",
-              "gemm_tile_epilogue.inc"):
+    for f in PREFILL_SOURCES:
         h.update(open(os.path.join(ROOT, "fp8_quantized_linear_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
@@ -339,21 +342,53 @@ def _median_ms(torch, fn, iters, warmup=3):
     return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
 
+def _median_interleaved_ms(torch, fns, iters, warmup=2):
+    """Median event time of each call in fns, the calls alternating (fns[0],
+    fns[1], ..., fns[0], ...), so that all of them see the same clock: the
+    graphics clock of this chip drifts with power from call to call."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+           for _ in range(iters)]
+    for row in evs:
+        for f, (a, b) in zip(fns, row):
+            a.record()
+            f()
+            b.record()
+    torch.cuda.synchronize()
+    return [float(np.median([row[j][0].elapsed_time(row[j][1]) for row in evs])) for j in range(len(fns))]
+
+
 def extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_dn):
     rows = {}
     up, down = W.PREFILL_UP, W.PREFILL_DOWN
-    # fused quantization prologue vs standalone
-    y = torch.empty((up.m, up.n), dtype=torch.bfloat16, device=dev)
-    med, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm_fused(a_up, wq_up, ws_up, y=y), 10)
-    y2 = torch.empty((down.m, down.n), dtype=torch.bfloat16, device=dev)
-    med2, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm_fused(a_dn, wq_dn, ws_dn, y=y2), 10)
-    medg, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm_fused(a_up, wq_up, ws_up, y=y, in_gemm=True), 10)
-    medg2, _, _ = _median_ms(torch, lambda i: mxl.mx_gemm_fused(a_dn, wq_dn, ws_dn, y=y2, in_gemm=True), 10)
-    rows["fused_prefill"] = {"up_us": round(med * 1e3, 1), "down_us": round(med2 * 1e3, 1),
-                             "tflops": round((up.flops + down.flops) / ((med + med2) * 1e-3) / 1e12, 1),
-                             "in_gemm_up_us": round(medg * 1e3, 1), "in_gemm_down_us": round(medg2 * 1e3, 1)}
-    log(f"fused: up {med * 1e3:.1f} us down {med2 * 1e3:.1f} us; quantizing inside the GEMM "
-        f"{medg * 1e3:.1f} / {medg2 * 1e3:.1f} us")
+    # fused quantization prologue (the quantizer into the workspace, then the
+    # GEMM; and the one-launch form) against the standalone pair, interleaved
+    fused = {}
+    for name, cfg, a, wq, ws in (("up", up, a_up, wq_up, ws_up), ("down", down, a_dn, wq_dn, ws_dn)):
+        y = torch.empty((cfg.m, cfg.n), dtype=torch.bfloat16, device=dev)
+        aq = torch.empty((cfg.m, cfg.k // 2), dtype=torch.uint8, device=dev)
+        as_ = torch.empty((cfg.m, cfg.k // 32), dtype=torch.uint8, device=dev)
+
+        def pair(a=a, wq=wq, ws=ws, y=y, aq=aq, as_=as_, k=cfg.k):
+            mxl.mx_quantize_act(a, "mxfp4", "ceil", out=(aq, as_))
+            mxl.mx_gemm(aq, as_, wq, ws, k, y=y)
+        t_f, t_p, t_g = _median_interleaved_ms(
+            torch, [lambda: mxl.mx_gemm_fused(a, wq, ws, y=y), pair,
+                    lambda: mxl.mx_gemm_fused(a, wq, ws, y=y, in_gemm=True)], 10)
+        fused[name] = (t_f, t_p, t_g)
+        del y, aq, as_
+    (fu, pu, gu), (fd, pd, gd) = fused["up"], fused["down"]
+    rows["fused_prefill"] = {"up_us": round(fu * 1e3, 1), "down_us": round(fd * 1e3, 1),
+                             "tflops": round((up.flops + down.flops) / ((fu + fd) * 1e-3) / 1e12, 1),
+                             "pair_up_us": round(pu * 1e3, 1), "pair_down_us": round(pd * 1e3, 1),
+                             "in_gemm_up_us": round(gu * 1e3, 1), "in_gemm_down_us": round(gd * 1e3, 1),
+                             "timing": "median of 10 interleaved calls each: mx_gemm_fused (default), "
+                                       "mx_quantize_act + mx_gemm (pair), mx_gemm_fused one-launch form"}
+    log(f"fused: up {fu * 1e3:.1f} us (pair {pu * 1e3:.1f}, one launch {gu * 1e3:.1f}); "
+        f"down {fd * 1e3:.1f} us (pair {pd * 1e3:.1f}, one launch {gd * 1e3:.1f})")
 
     # standalone quantizer GB/s (inputs rotated through 4 copies: > 256 MB)
     for name, cfg, a in (("up", up, a_up), ("down", down, a_dn)):
