@@ -914,6 +914,14 @@ __device__ __forceinline__ void wait_vmcnt_n(int n)
     }
 }
 
+// buffer-to-LDS copy of 16 bytes per lane marked non-temporal: data read
+// once, streamed past the caches
+__device__ __forceinline__ void dma_b128_nt(uint32_t lds, int voff, const int4_t& rsrc, int soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_read_u32(uint32_t addr)
 {
     return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>((size_t)addr);
@@ -924,11 +932,11 @@ __device__ __forceinline__ int4_t lds_read_v4(uint32_t addr)
     return *reinterpret_cast<const __attribute__((address_space(3))) int4_t*>((size_t)addr);
 }
 
-template <int MT, int QS, bool OUT_F32>
+template <int MT, int QS, int RS, bool OUT_F32>
 __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
 {
-    constexpr int WAVES = 4, NC = QS / 2;
-    static_assert(QS % 2 == 0 && QS <= 16 && MT <= 2, "decode stream shape");
+    constexpr int WAVES = 4, NC = QS / 2, RSB = RS < NC ? RS : NC;
+    static_assert(QS % 2 == 0 && QS <= 16 && MT <= 2 && RSB >= 1, "decode stream shape");
     extern __shared__ __align__(16) uint8_t dsm[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the copy offsets go in SGPRs
@@ -941,13 +949,13 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_q, (short)0, p.M * row_bytes, 0x00020000);
     const int4_t rw = make_rsrc(p.w_q, (uint32_t)p.N * row_bytes);
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dsm);
-    const uint32_t lds_w = lds0 + (uint32_t)(wave * 16 * QB);   // this wave's 2 NC blocks of 1 KiB
+    const uint32_t lds_w = lds0 + (uint32_t)(wave * RSB * 2048);   // this wave's ring of RSB pair slots
 
     // The scale blocks of the workgroup's 16 W rows and of A's 16 MT rows
     // (contiguous [rows][K/32] byte ranges) go to LDS first, 256 bytes per
     // copy, spread over the waves; one barrier publishes them.
     constexpr int SCOP = (1 + MT) * QS;   // 16 KB / 256 bytes per 16 rows
-    const uint32_t sw_lds = lds0 + (uint32_t)(16 * row_bytes), sa_lds = sw_lds + (uint32_t)(16 * KB);
+    const uint32_t sw_lds = lds0 + (uint32_t)(WAVES * RSB * 2048), sa_lds = sw_lds + (uint32_t)(16 * KB);
     {
         const int4_t rws4 = make_rsrc(p.w_s, (uint32_t)p.N * KB);
         const int4_t ras4 = make_rsrc(p.a_s, (uint32_t)p.M * KB);
@@ -965,21 +973,26 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
 #pragma unroll
         for (int t = 0; t < MT; ++t)
             af[u][t] = __builtin_amdgcn_raw_buffer_load_b128(ra, (16 * t + r) * row_bytes + g * 16, (st0 + u) * 64, 0);
-    // the wave's W copies, in stage order
+    // the wave's W copies, in stage order: pair c (copies (c, 0) and (c, 1))
+    // goes to ring slot c % RSB; the first RSB pairs now, each later one
+    // once the pair before it in its slot has been computed
     int voffh[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int q = 8 * h + (lane >> 3);
         voffh[h] = (n0 + q) * row_bytes + (((lane & 7) ^ ((q >> 1) & 7)) * 16);
     }
+    auto copy_pair = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+        for (int h = 0; h < 2; ++h)
+            dma_b128_nt(lds_w + (uint32_t)(((c % RSB) * 2 + h) * 1024), voffh[h], rw, wave * QB + c * 128);
+    };
 #pragma unroll
-        for (int h = 0; h < 2; ++h) dma_b128(lds_w + (uint32_t)((2 * c + h) * 1024), voffh[h], rw, wave * QB + c * 128);
+    for (int c = 0; c < RSB; ++c) copy_pair(c);
 
     // the scale copies have landed once at most the A loads and W copies
     // issued after them are outstanding
-    wait_vmcnt<QS * MT + QS>();
+    wait_vmcnt<QS * MT + 2 * RSB>();
     lds_barrier();
 
     float4_t_ acc[MT];
@@ -990,13 +1003,17 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
     const uint32_t rsw_l = sw_lds + (uint32_t)(r * KB + 4 * st0), rsa_l = sa_lds + (uint32_t)(r * KB + 4 * st0);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        // copies (c, 0) and (c, 1) have landed once at most the 2 (NC - 1 - c)
-        // copies issued after them are outstanding
-        wait_vmcnt_n(2 * (NC - 1 - c));
+        // pairs 0 .. min(c - 1 + RSB, NC - 1) have been issued: pair c's
+        // copies have landed once at most the copies of the later ones are
+        // outstanding
+        {
+            const int last = c - 1 + RSB < NC - 1 ? c - 1 + RSB : NC - 1;
+            wait_vmcnt_n(2 * (last - c));
+        }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int u = 2 * c + hf;
-            const int4_t wv = lds_read_v4(rd + (uint32_t)(2 * c * 1024 + (((4 * hf + g) ^ rsw) * 16)));
+            const int4_t wv = lds_read_v4(rd + (uint32_t)((c % RSB) * 2048 + (((4 * hf + g) ^ rsw) * 16)));
             const int8_t_ b8 = int8_t_{wv[0], wv[1], wv[2], wv[3], 0, 0, 0, 0};
             // a row's scale dword for stage s holds blocks 4 s .. 4 s + 3; lane group g takes byte g
             const int wsb = (int)(lds_read_u32(rsw_l + 4 * u) >> (8 * g));
@@ -1006,6 +1023,11 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
                 const int8_t_ a8 = int8_t_{af[u][t][0], af[u][t][1], af[u][t][2], af[u][t][3], 0, 0, 0, 0};
                 acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 4, 4, 0, asb, 0, wsb);
             }
+        }
+        if (c + RSB < NC) {
+            // slot c % RSB is free once this pair's LDS reads have returned
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            copy_pair(c + RSB);
         }
     }
     __syncthreads();   // every wave is done with its LDS region
@@ -1035,22 +1057,39 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
     }
 }
 
-template <int MT>
-static size_t decode_stream_lds_bytes(int K) { return (size_t)16 * (K / 2) + (size_t)16 * (1 + MT) * (K / 32); }
+// The streamed decode kernel keeps either every stage pair of a wave's
+// quarter in flight (RS = K / 1024 slots) or a ring of 3 slots (2 KiB each
+// per wave), refilled as pairs are computed.  The ring lets five workgroups
+// share a CU where the whole quarters let three or four; it measured faster
+// from M = 16 up (more A fragment loads in flight) and slightly slower below,
+// and it is the only form whose LDS fits at K = 8192.
+static size_t decode_stream_lds_bytes(int mt, int k, bool ring)
+{
+    const int slots = ring ? 3 : k / 1024;
+    return (size_t)4 * slots * 2048 + (size_t)16 * (1 + mt) * (k / 32);
+}
 
-// whether mx_decode_stream_kernel serves M rows of A at this K (its LDS
-// within 64 KiB)
+static bool decode_stream_ring(int64_t m, int64_t k)
+{
+    return m > 8 || decode_stream_lds_bytes(m > 16 ? 2 : 1, (int)k, false) > 65536;
+}
+
+// whether mx_decode_stream_kernel serves M rows of A at this K
 static bool decode_stream_ok(int64_t m, int64_t k)
 {
-    if (m > 32 || k % 1024 != 0 || k < 1024 || k > 8192) return false;
-    return (m <= 16 ? decode_stream_lds_bytes<1>((int)k) : decode_stream_lds_bytes<2>((int)k)) <= 65536;
+    return m <= 32 && k % 1024 == 0 && k >= 1024 && k <= 8192;
 }
 
 template <int MT, int QS, bool OUT_F32>
 static void launch_decode_stream_qs(const GemmArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, OUT_F32>), dim3((a.N + 15) / 16), dim3(256),
-                       decode_stream_lds_bytes<MT>(a.K), stream, a);
+    const bool ring = decode_stream_ring(a.M, a.K);
+    if (ring)
+        hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, 3, OUT_F32>), dim3((a.N + 15) / 16), dim3(256),
+                           decode_stream_lds_bytes(MT, a.K, true), stream, a);
+    else
+        hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, QS / 2, OUT_F32>), dim3((a.N + 15) / 16), dim3(256),
+                           decode_stream_lds_bytes(MT, a.K, false), stream, a);
 }
 
 template <int MT, bool OUT_F32>
@@ -1280,8 +1319,13 @@ extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int w_bits, int64_t m
     switch (classify(a_bits, w_bits, m, n, k, fused != 0)) {
     case SC_DECODE:
         if (decode_stream_ok(m, k))
-            return "mx_decode_stream_kernel<16 W rows per workgroup, each wave copies its own K quarter into LDS "
-                   "(8 rows x 128 B per copy) and computes each stage as its copies land, scaled mfma 16x16x128>";
+            return decode_stream_ring(m, k)
+                       ? "mx_decode_stream_kernel<16 W rows per workgroup, each wave streams its own K quarter through a "
+                         "ring of 3 LDS pair slots (8 rows x 128 B non-temporal copies) and computes each stage as its "
+                         "copies land, scaled mfma 16x16x128>"
+                       : "mx_decode_stream_kernel<16 W rows per workgroup, each wave copies its whole K quarter into LDS "
+                         "(8 rows x 128 B non-temporal copies) and computes each stage as its copies land, scaled mfma "
+                         "16x16x128>";
         switch (decode_kind(m, k)) {
         case 2: return "mx_decode_kernel<16 W rows per workgroup, whole-row copies into swizzled LDS, 4 waves over K "
                        "quarters, scaled mfma 16x16x128>";

@@ -91,6 +91,14 @@ __device__ __forceinline__ bf16x8_w w4_dequant8(uint32_t codes, float s, int e)
     return v;
 }
 
+// buffer-to-LDS copy of 16 bytes per lane marked non-temporal: W codes are
+// read once, streamed past the caches
+__device__ __forceinline__ void w4_dma_b128_nt(uint32_t lds, int voff, const int4_t& rsrc, int soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
 // LDS reads at a byte address of the workgroup's LDS
 __device__ __forceinline__ uint32_t w4_lds_u32(uint32_t addr)
 {
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(256) void w4a16_decode_kernel(W4a16Args p)
 // The same product streamed per wave, for M <= 2 rows of A, K % 1024 == 0
 // (QS = K / 512 stages of 128 per wave).  As in mx_decode_stream_kernel, wave
 // w owns a contiguous quarter of K: it copies its 16 x K/8 bytes of W codes
-// into its own LDS region (8 rows x 128 B per copy, copies in stage order),
+// into its own LDS region (8 rows x 128 B non-temporal copies, in stage order),
 // and its quarter of each A row next to them, so that it can compute each
 // stage as soon as that stage's copies have landed, with an exact vmcnt and
 // no wait on the other waves.  The W scale block (16 rows) is copied once by
@@ -296,7 +304,7 @@ __global__ __launch_bounds__(256) void w4a16_decode_stream_kernel(W4a16Args p)
         for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                dma_b128(lds_w + (uint32_t)((2 * c + h) * 1024), voffh[h], rw, wave * QB + c * 128);
+                w4_dma_b128_nt(lds_w + (uint32_t)((2 * c + h) * 1024), voffh[h], rw, wave * QB + c * 128);
     }
     // the scale and A copies have landed once at most the QS W copies are
     // outstanding; the barrier publishes the scale block

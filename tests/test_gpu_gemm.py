@@ -182,15 +182,15 @@ def test_decode_shapes_full():
 
 
 # Decode-shaped calls (M <= 32 here) pick one of four kernels by K: per-wave
-# streamed K quarters (K % 1024 == 0 while W and the scales fit 64 KiB of
-# LDS: K <= 6144 for every M <= 32), whole-row LDS blocks (other
+# streamed K quarters (K % 1024 == 0, K <= 8192; whole quarters in LDS for
+# M <= 8 where they fit, else a ring of pair slots), whole-row LDS blocks (other
 # K % 512 == 0 while the block fits 64 KiB of LDS), K-chunked direct loads
 # (other K % 128 == 0) and the generic split-K kernel.  Each is checked in
 # full against the oracle at ragged N and at the edges of its K range.
 DECODE_KINDS = [("mx_decode_stream_kernel<", 1024), ("mx_decode_stream_kernel<", 5120),
-                ("mx_decode_stream_kernel<", 6144),
+                ("mx_decode_stream_kernel<", 6144), ("mx_decode_stream_kernel<", 8192),
                 ("mx_decode_kernel<", 512), ("mx_decode_kernel<", 6656), ("mx_decode_kernel<", 2560),
-                ("mx_decode_direct_kernel<", 384), ("mx_decode_direct_kernel<", 8192),
+                ("mx_decode_direct_kernel<", 384), ("mx_decode_direct_kernel<", 3200),
                 ("mx_decode_direct_kernel<", 16384),
                 ("mx_decode_generic_kernel<", 96), ("mx_decode_generic_kernel<", 4128)]
 
