@@ -932,16 +932,17 @@ __device__ __forceinline__ int4_t lds_read_v4(uint32_t addr)
     return *reinterpret_cast<const __attribute__((address_space(3))) int4_t*>((size_t)addr);
 }
 
-template <int MT, int QS, int RS, bool OUT_F32>
+template <int MT, int QS, int RS, int RG, bool OUT_F32>
 __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
 {
     constexpr int WAVES = 4, NC = QS / 2, RSB = RS < NC ? RS : NC;
-    static_assert(QS % 2 == 0 && QS <= 16 && MT <= 2 && RSB >= 1, "decode stream shape");
+    constexpr int SLOT = RG * 2048;       // a pair slot: RG groups of 16 rows x 128 B per wave
+    static_assert(QS % 2 == 0 && QS <= 16 && MT <= 2 && RSB >= 1 && (RG == 1 || RG == 2), "decode stream shape");
     extern __shared__ __align__(16) uint8_t dsm[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the copy offsets go in SGPRs
     const int r = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * 16 * RG;
     const int K = QS * 512, KB = K / 32, row_bytes = K / 2;
     const int QB = row_bytes / WAVES;     // W bytes per row per wave (64 QS)
     const int st0 = wave * QS;            // this wave's first stage
@@ -949,21 +950,21 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_q, (short)0, p.M * row_bytes, 0x00020000);
     const int4_t rw = make_rsrc(p.w_q, (uint32_t)p.N * row_bytes);
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dsm);
-    const uint32_t lds_w = lds0 + (uint32_t)(wave * RSB * 2048);   // this wave's ring of RSB pair slots
+    const uint32_t lds_w = lds0 + (uint32_t)(wave * RSB * SLOT);   // this wave's ring of RSB pair slots
 
-    // The scale blocks of the workgroup's 16 W rows and of A's 16 MT rows
+    // The scale blocks of the workgroup's 16 RG W rows and of A's 16 MT rows
     // (contiguous [rows][K/32] byte ranges) go to LDS first, 256 bytes per
     // copy, spread over the waves; one barrier publishes them.
-    constexpr int SCOP = (1 + MT) * QS;   // 16 KB / 256 bytes per 16 rows
-    const uint32_t sw_lds = lds0 + (uint32_t)(WAVES * RSB * 2048), sa_lds = sw_lds + (uint32_t)(16 * KB);
+    constexpr int SCOP = (RG + MT) * QS;   // 16 KB / 256 bytes per 16 rows
+    const uint32_t sw_lds = lds0 + (uint32_t)(WAVES * RSB * SLOT), sa_lds = sw_lds + (uint32_t)(16 * RG * KB);
     {
         const int4_t rws4 = make_rsrc(p.w_s, (uint32_t)p.N * KB);
         const int4_t ras4 = make_rsrc(p.a_s, (uint32_t)p.M * KB);
 #pragma unroll
         for (int j = 0; j < SCOP; ++j)
             if (j % WAVES == wave) {
-                if (j < QS) dma_b32(sw_lds + j * 256, n0 * KB + j * 256 + lane * 4, rws4, 0);
-                else dma_b32(sw_lds + j * 256, (j - QS) * 256 + lane * 4, ras4, 0);
+                if (j < RG * QS) dma_b32(sw_lds + j * 256, n0 * KB + j * 256 + lane * 4, rws4, 0);
+                else dma_b32(sw_lds + j * 256, (j - RG * QS) * 256 + lane * 4, ras4, 0);
             }
     }
     // A fragments of every stage of the wave
@@ -976,28 +977,31 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
     // the wave's W copies, in stage order: pair c (copies (c, 0) and (c, 1))
     // goes to ring slot c % RSB; the first RSB pairs now, each later one
     // once the pair before it in its slot has been computed
-    int voffh[2];
+    // (copy h of a pair: rows 8 h .. 8 h + 7 of the workgroup's 16 RG rows)
+    int voffh[2 * RG];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2 * RG; ++h) {
         const int q = 8 * h + (lane >> 3);
         voffh[h] = (n0 + q) * row_bytes + (((lane & 7) ^ ((q >> 1) & 7)) * 16);
     }
     auto copy_pair = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            dma_b128_nt(lds_w + (uint32_t)(((c % RSB) * 2 + h) * 1024), voffh[h], rw, wave * QB + c * 128);
+        for (int h = 0; h < 2 * RG; ++h)
+            dma_b128_nt(lds_w + (uint32_t)((c % RSB) * SLOT + h * 1024), voffh[h], rw, wave * QB + c * 128);
     };
 #pragma unroll
     for (int c = 0; c < RSB; ++c) copy_pair(c);
 
     // the scale copies have landed once at most the A loads and W copies
     // issued after them are outstanding
-    wait_vmcnt<QS * MT + 2 * RSB>();
+    wait_vmcnt<QS * MT + 2 * RG * RSB>();
     lds_barrier();
 
-    float4_t_ acc[MT];
+    float4_t_ acc[RG][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = float4_t_{0.f, 0.f, 0.f, 0.f};
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[rg][t] = float4_t_{0.f, 0.f, 0.f, 0.f};
     const uint32_t rd = lds_w + (uint32_t)((r >> 3) * 1024 + (r & 7) * 128);
     const int rsw = (r >> 1) & 7;
     const uint32_t rsw_l = sw_lds + (uint32_t)(r * KB + 4 * st0), rsa_l = sa_lds + (uint32_t)(r * KB + 4 * st0);
@@ -1008,20 +1012,23 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
         // outstanding
         {
             const int last = c - 1 + RSB < NC - 1 ? c - 1 + RSB : NC - 1;
-            wait_vmcnt_n(2 * (last - c));
+            wait_vmcnt_n(2 * RG * (last - c));
         }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int u = 2 * c + hf;
-            const int4_t wv = lds_read_v4(rd + (uint32_t)((c % RSB) * 2048 + (((4 * hf + g) ^ rsw) * 16)));
-            const int8_t_ b8 = int8_t_{wv[0], wv[1], wv[2], wv[3], 0, 0, 0, 0};
-            // a row's scale dword for stage s holds blocks 4 s .. 4 s + 3; lane group g takes byte g
-            const int wsb = (int)(lds_read_u32(rsw_l + 4 * u) >> (8 * g));
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const int asb = (int)(lds_read_u32(rsa_l + (uint32_t)(16 * t * KB + 4 * u)) >> (8 * g));
-                const int8_t_ a8 = int8_t_{af[u][t][0], af[u][t][1], af[u][t][2], af[u][t][3], 0, 0, 0, 0};
-                acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 4, 4, 0, asb, 0, wsb);
+            for (int rg = 0; rg < RG; ++rg) {
+                const int4_t wv = lds_read_v4(rd + (uint32_t)((c % RSB) * SLOT + rg * 2048 + (((4 * hf + g) ^ rsw) * 16)));
+                const int8_t_ b8 = int8_t_{wv[0], wv[1], wv[2], wv[3], 0, 0, 0, 0};
+                // a row's scale dword for stage s holds blocks 4 s .. 4 s + 3; lane group g takes byte g
+                const int wsb = (int)(lds_read_u32(rsw_l + (uint32_t)(16 * rg * KB + 4 * u)) >> (8 * g));
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    const int asb = (int)(lds_read_u32(rsa_l + (uint32_t)(16 * t * KB + 4 * u)) >> (8 * g));
+                    const int8_t_ a8 = int8_t_{af[u][t][0], af[u][t][1], af[u][t][2], af[u][t][3], 0, 0, 0, 0};
+                    acc[rg][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[rg][t], 4, 4, 0, asb, 0, wsb);
+                }
             }
         }
         if (c + RSB < NC) {
@@ -1031,21 +1038,23 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
         }
     }
     __syncthreads();   // every wave is done with its LDS region
-    float4_t_* red = reinterpret_cast<float4_t_*>(dsm);   // [WAVES][MT][64]
+    float4_t_* red = reinterpret_cast<float4_t_*>(dsm);   // [WAVES][RG][MT][64]
 #pragma unroll
-    for (int t = 0; t < MT; ++t) red[(wave * MT + t) * 64 + lane] = acc[t];
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) red[((wave * RG + rg) * MT + t) * 64 + lane] = acc[rg][t];
     __syncthreads();
-    // thread e < MT * 64 finishes accumulator lane e % 64 of A tile t:
-    // A rows 16 t + 4 (l / 16) + i, W row n0 + l % 16
-    if (tid < MT * 64) {
-        const int l = tid & 63, t = tid >> 6;
-        float4_t_ v = red[t * 64 + l];
+    // thread e < RG * MT * 64 finishes accumulator lane e % 64 of (W group rg,
+    // A tile t): A rows 16 t + 4 (l / 16) + i, W row n0 + 16 rg + l % 16
+    if (tid < RG * MT * 64) {
+        const int l = tid & 63, rt = tid >> 6, rg = rt / MT, t = rt % MT;
+        float4_t_ v = red[(rg * MT + t) * 64 + l];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) {
-            const float4_t_ x = red[(w * MT + t) * 64 + l];
+            const float4_t_ x = red[((w * RG + rg) * MT + t) * 64 + l];
             v = float4_t_{v[0] + x[0], v[1] + x[1], v[2] + x[2], v[3] + x[3]};
         }
-        const int nn = n0 + (l & 15);
+        const int nn = n0 + 16 * rg + (l & 15);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 16 * t + 4 * (l >> 4) + i;
@@ -1058,38 +1067,53 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
 }
 
 // The streamed decode kernel keeps either every stage pair of a wave's
-// quarter in flight (RS = K / 1024 slots) or a ring of 3 slots (2 KiB each
-// per wave), refilled as pairs are computed.  The ring lets five workgroups
-// share a CU where the whole quarters let three or four; it measured faster
-// from M = 16 up (more A fragment loads in flight) and slightly slower below,
-// and it is the only form whose LDS fits at K = 8192.
-static size_t decode_stream_lds_bytes(int mt, int k, bool ring)
+// quarter in flight (K / 1024 slots) or a ring of a few slots (2 KiB per 16
+// rows each per wave), refilled as pairs are computed.  The ring lets more
+// workgroups share a CU: it measured faster from M = 16 up (more A fragment
+// loads in flight) and slightly slower below, and it is the only form whose
+// LDS fits at K = 8192.  Above M = 16 a workgroup owns two 16-row groups of
+// W, so that each A fragment it loads from the L2 serves both.
+struct DecodeStreamCfg {
+    int rg;      // 16-row W groups per workgroup
+    int slots;   // ring slots (stage pairs) per wave; K / 1024 = every pair
+};
+
+static DecodeStreamCfg decode_stream_cfg(int64_t m, int64_t k)
 {
-    const int slots = ring ? 3 : k / 1024;
-    return (size_t)4 * slots * 2048 + (size_t)16 * (1 + mt) * (k / 32);
+    if (m > 16) return {2, 2};
+    const int all = (int)(k / 1024);
+    const size_t whole = (size_t)4 * all * 2048 + (size_t)16 * 2 * (k / 32);
+    if (m <= 8 && whole <= 65536) return {1, all};
+    return {1, 3};
 }
 
-static bool decode_stream_ring(int64_t m, int64_t k)
+static size_t decode_stream_lds_bytes(int mt, int k, DecodeStreamCfg c)
 {
-    return m > 8 || decode_stream_lds_bytes(m > 16 ? 2 : 1, (int)k, false) > 65536;
+    const int nc = k / 1024, slots = c.slots < nc ? c.slots : nc;
+    return (size_t)4 * slots * c.rg * 2048 + (size_t)16 * (c.rg + mt) * (k / 32);
 }
+
+static bool decode_stream_ring(int64_t m, int64_t k) { return decode_stream_cfg(m, k).slots < k / 1024; }
 
 // whether mx_decode_stream_kernel serves M rows of A at this K
 static bool decode_stream_ok(int64_t m, int64_t k)
 {
-    return m <= 32 && k % 1024 == 0 && k >= 1024 && k <= 8192;
+    return m <= 32 && k % 1024 == 0 && k >= 1024 && k <= 8192 &&
+           decode_stream_lds_bytes(m > 16 ? 2 : 1, (int)k, decode_stream_cfg(m, k)) <= 65536;
 }
 
 template <int MT, int QS, bool OUT_F32>
 static void launch_decode_stream_qs(const GemmArgs& a, hipStream_t stream)
 {
-    const bool ring = decode_stream_ring(a.M, a.K);
-    if (ring)
-        hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, 3, OUT_F32>), dim3((a.N + 15) / 16), dim3(256),
-                           decode_stream_lds_bytes(MT, a.K, true), stream, a);
+    const DecodeStreamCfg c = decode_stream_cfg(a.M, a.K);
+    const dim3 block(256);
+    const size_t lds = decode_stream_lds_bytes(MT, a.K, c);
+    if (MT == 2 && c.rg == 2)
+        hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, 2, 2, OUT_F32>), dim3((a.N + 31) / 32), block, lds, stream, a);
+    else if (c.slots == 3)
+        hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, 3, 1, OUT_F32>), dim3((a.N + 15) / 16), block, lds, stream, a);
     else
-        hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, QS / 2, OUT_F32>), dim3((a.N + 15) / 16), dim3(256),
-                           decode_stream_lds_bytes(MT, a.K, false), stream, a);
+        hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, QS / 2, 1, OUT_F32>), dim3((a.N + 15) / 16), block, lds, stream, a);
 }
 
 template <int MT, bool OUT_F32>
@@ -1319,7 +1343,10 @@ extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int w_bits, int64_t m
     switch (classify(a_bits, w_bits, m, n, k, fused != 0)) {
     case SC_DECODE:
         if (decode_stream_ok(m, k))
-            return decode_stream_ring(m, k)
+            return m > 16 ? "mx_decode_stream_kernel<32 W rows per workgroup (each A fragment serves both 16-row groups), "
+                            "each wave streams its own K quarter through a ring of 2 LDS pair slots (8 rows x 128 B "
+                            "non-temporal copies) and computes each stage as its copies land, scaled mfma 16x16x128>"
+                   : decode_stream_ring(m, k)
                        ? "mx_decode_stream_kernel<16 W rows per workgroup, each wave streams its own K quarter through a "
                          "ring of 3 LDS pair slots (8 rows x 128 B non-temporal copies) and computes each stage as its "
                          "copies land, scaled mfma 16x16x128>"
