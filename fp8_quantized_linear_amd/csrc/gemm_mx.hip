@@ -1044,10 +1044,10 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
 #pragma unroll
         for (int t = 0; t < MT; ++t) red[((wave * RG + rg) * MT + t) * 64 + lane] = acc[rg][t];
     __syncthreads();
-    // thread e < RG * MT * 64 finishes accumulator lane e % 64 of (W group rg,
+    // item e < RG * MT * 64 finishes accumulator lane e % 64 of (W group rg,
     // A tile t): A rows 16 t + 4 (l / 16) + i, W row n0 + 16 rg + l % 16
-    if (tid < RG * MT * 64) {
-        const int l = tid & 63, rt = tid >> 6, rg = rt / MT, t = rt % MT;
+    for (int e = tid; e < RG * MT * 64; e += 256) {
+        const int l = e & 63, rt = e >> 6, rg = rt / MT, t = rt % MT;
         float4_t_ v = red[(rg * MT + t) * 64 + l];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) {
