@@ -548,7 +548,33 @@ def extra_rows(torch, mxl, W, dev, to_dev, a_up, wq_up, ws_up, a_dn, wq_dn, ws_d
             nbytes = cfg.n * (cfg.k // 2 + kb) + cfg.m * cfg.k * 2 + cfg.m * cfg.n * 2
             graph_rows(call, f"w4a16_{fmt}_decode_m{cfg.m}", nbytes,
                        mxl.mx_gemm_w4a16_plan(fmt, cfg.m, cfg.n, cfg.k), cfg.m)
-    del wcopies, ncopies
+    del wcopies
+
+    # W4A4 NVFP4 (the NVFP4 copies above) and W8A8 MXFP8 (FLOOR packings of
+    # the same weights) decode on the same shapes
+    w_bits_dev = to_dev(dec.weights())
+    fq0, fs0 = mxl.mx_pack_weights(w_bits_dev, "mxfp8", "floor")
+    del w_bits_dev
+    fcopies = [(fq0, fs0)] + [(fq0.clone(), fs0.clone()) for _ in range(10)]
+    for cfg in [c for c in W.DECODE if c.m <= 16]:
+        a = to_dev(cfg.activations())
+        g_a = mxl.mx_nv_global_scale(float(mxl.mx_tensor_amax(a).item()))
+        naq, nas = mxl.mx_quantize_act(a, "nvfp4", global_scale=g_a)
+        alpha = float(np.float32(1.0) / (np.float32(g_a) * np.float32(g_w)))
+
+        def call_nv(i, y=None, naq=naq, nas=nas, alpha=alpha, k=cfg.k):
+            return mxl.nv_gemm(naq, nas, ncopies[i][0], ncopies[i][1], k, alpha, y=y)
+        nbytes = (cfg.m + cfg.n) * (cfg.k // 2 + cfg.k // 16) + cfg.m * cfg.n * 2
+        graph_rows(call_nv, f"nvfp4_decode_m{cfg.m}", nbytes,
+                   mxl.mx_gemm_plan("nvfp4", "nvfp4", cfg.m, cfg.n, cfg.k), cfg.m)
+        faq, fas = mxl.mx_quantize_act(a, "mxfp8", "ceil")
+
+        def call_f8(i, y=None, faq=faq, fas=fas, k=cfg.k):
+            return mxl.mx_gemm(faq, fas, fcopies[i][0], fcopies[i][1], k, "mxfp8", "mxfp8", y=y)
+        nbytes = (cfg.m + cfg.n) * (cfg.k + cfg.k // 32) + cfg.m * cfg.n * 2
+        graph_rows(call_f8, f"mxfp8_decode_m{cfg.m}", nbytes,
+                   mxl.mx_gemm_plan("mxfp8", "mxfp8", cfg.m, cfg.n, cfg.k), cfg.m)
+    del ncopies, fcopies
 
     # NVFP4 W4A4
     nv = W.NVFP4

@@ -598,6 +598,252 @@ extern "C" int mxl_choose_splits(int64_t tiles, int nk, int min_stages, int even
 extern "C" hipError_t mxl_launch_splitk_reduce(const float* part, int splits, int64_t mn, float alpha, void* y,
                                                int out_f32, hipStream_t stream);
 
+// ---------------------------------------------------------------- decode
+// Decode-shaped exact MXFP8 and NVFP4 GEMMs (M <= 16, K % 1024 == 0, K <=
+// 8192): a stream over W, built like the MXFP4 decode kernel
+// (mx_decode_stream_kernel): one workgroup of 4 waves owns 16 W rows, wave w
+// a contiguous quarter of K.  W is consumed in chunks of 128 code bytes per
+// row (one stage of 128 K for MXFP8, two for NVFP4):
+//  * Each wave copies its own chunks, rows 8 h .. 8 h + 7 x 128 bytes per
+//    copy (8 full cache lines, non-temporal: W is read once), through a ring
+//    of 3 chunk slots in its own LDS region, and computes each chunk once
+//    its two copies have landed (exact vmcnt); the slot is refilled when its
+//    LDS reads have returned.  Inside a copy, row q's 16-byte chunk L sits at
+//    L ^ ((q >> 1) & 7), so the 16 rows of a lane group cover all banks.
+//  * The scale blocks of the 16 W rows and of A's 16 rows go to LDS first
+//    (256-byte copies spread over the waves, one barrier), and the wave's A
+//    codes (rows past M read as zero) to registers, before the W copies.
+//  * Dequantization as in the tile kernels, in registers: MXFP8 codes to
+//    bf16 by v_cvt_scalef32_pk_bf16_fp8 with the E8M0 scale in the exponent
+//    field; NVFP4 codes to f16 (scale 1) times the E4M3 block scale as an
+//    f16 pair (exact).  Then v_mfma_f32_16x16x32_{bf16,f16}: lane (r, g)
+//    supplies row r and, in step j of a stage, elements [32 g + 8 j, +8) of
+//    it, for A and W alike, so each step sums 32 distinct K.
+//  * The four K quarters are summed through LDS; Y = alpha * sum.
+__device__ __forceinline__ void dq_dma_b128_nt(uint32_t lds, int voff, const int4_t& rsrc, int soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+__device__ __forceinline__ int4_t dq_lds_v4(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) int4_t*>((size_t)addr);
+}
+__device__ __forceinline__ uint32_t dq_lds_u32(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>((size_t)addr);
+}
+// s_waitcnt vmcnt(n) for an even n <= 6 that folds to a constant once loops
+// are unrolled
+__device__ __forceinline__ void dq_wait_vmcnt_n(int n)
+{
+    switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    default: wait_vmcnt<0>(); break;
+    }
+}
+
+constexpr int DQD_RS = 3;   // ring slots (chunks) per wave
+
+template <int KIND, int QC, bool OUT_F32>
+__global__ __launch_bounds__(256) void dq_decode_stream_kernel(DqArgs p)
+{
+    static_assert(KIND == DQ_MXFP8 || KIND == DQ_NVFP4, "decode formats");
+    constexpr bool NV = KIND == DQ_NVFP4;
+    constexpr int WAVES = 4, RSB = DQD_RS < QC ? DQD_RS : QC;
+    constexpr int K = NV ? QC * 1024 : QC * 512;          // QC chunks of 128 code bytes per wave
+    constexpr int ROWB = NV ? K / 2 : K;                  // code bytes per row
+    constexpr int KS = NV ? K / 16 : K / 32;              // scale bytes per row
+    constexpr int QB = ROWB / WAVES;                      // code bytes per row per wave (128 QC)
+    constexpr int SPC = NV ? 2 : 1;                       // stages (128 K) per chunk
+    constexpr int SCOP = 2 * 16 * KS / 256;               // scale copies: W block, then A block
+    extern __shared__ __align__(16) uint8_t dsm[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int st0 = wave * QC * SPC;                      // this wave's first stage
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dsm);
+    const uint32_t lds_w = lds0 + (uint32_t)(wave * RSB * 2048);
+    const uint32_t sw_lds = lds0 + (uint32_t)(WAVES * RSB * 2048), sa_lds = sw_lds + (uint32_t)(16 * KS);
+
+    // this wave's A codes, 32 bytes per lane and chunk: row r, K [32 g, +32)
+    // of each stage (MXFP8: 32 codes of the chunk's stage; NVFP4: 16 bytes of
+    // each of its two stages)
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_q, (short)0, p.M * ROWB, 0x00020000);
+    int4_t af[QC][2];
+#pragma unroll
+    for (int c = 0; c < QC; ++c)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int off = NV ? (st0 + SPC * c + i) * 64 + g * 16 : (st0 + c) * 128 + g * 32 + i * 16;
+            af[c][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, r * ROWB + off, 0, 0);
+        }
+    // scale blocks [16 rows][KS] of W and of A
+    {
+        const int4_t rws = make_rsrc(p.w_s, (uint32_t)p.N * KS);
+        const int4_t ras = make_rsrc(p.a_s, (uint32_t)p.M * KS);
+#pragma unroll
+        for (int j = 0; j < SCOP; ++j)
+            if (j % WAVES == wave) {
+                if (j < SCOP / 2) dma_b32(sw_lds + j * 256, n0 * KS + j * 256 + lane * 4, rws, 0);
+                else dma_b32(sw_lds + j * 256, (j - SCOP / 2) * 256 + lane * 4, ras, 0);
+            }
+    }
+    // W chunks: chunk c (copies h = 0, 1: rows 8 h .. 8 h + 7) into slot c % RSB
+    const int4_t rw = make_rsrc(p.w_q, (uint32_t)p.N * ROWB);
+    int voffh[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = 8 * h + (lane >> 3);
+        voffh[h] = (n0 + q) * ROWB + (((lane & 7) ^ ((q >> 1) & 7)) * 16);
+    }
+    auto copy_chunk = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            dq_dma_b128_nt(lds_w + (uint32_t)((c % RSB) * 2048 + h * 1024), voffh[h], rw, wave * QB + c * 128);
+    };
+#pragma unroll
+    for (int c = 0; c < RSB; ++c) copy_chunk(c);
+    // the scale copies (and the A loads before them) have landed once at
+    // most the W copies are outstanding; the barrier publishes the scales
+    wait_vmcnt<2 * RSB>();
+    lds_barrier();
+
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t rd = lds_w + (uint32_t)((r >> 3) * 1024 + (r & 7) * 128);
+    const int rsw = (r >> 1) & 7;
+    const uint32_t srw = sw_lds + (uint32_t)(r * KS), sra = sa_lds + (uint32_t)(r * KS);
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+        {
+            const int last = c - 1 + RSB < QC - 1 ? c - 1 + RSB : QC - 1;
+            dq_wait_vmcnt_n(2 * (last - c));
+        }
+        const uint32_t slot = rd + (uint32_t)((c % RSB) * 2048);
+#pragma unroll
+        for (int hf = 0; hf < SPC; ++hf) {
+            const int st = st0 + SPC * c + hf;   // global stage (128 K)
+            uint32_t wd[8], ad[8];
+            if (NV) {
+                // 32 codes of block pair (2 g, 2 g + 1) of 16: one 16-byte chunk
+                const int4_t w4 = dq_lds_v4(slot + (uint32_t)(((4 * hf + g) ^ rsw) * 16));
+                for (int i = 0; i < 4; ++i) { wd[i] = (uint32_t)w4[i]; ad[i] = (uint32_t)af[c][hf][i]; }
+            } else {
+                // 32 codes: logical chunks 2 g and 2 g + 1
+                const int4_t w0 = dq_lds_v4(slot + (uint32_t)(((2 * g) ^ rsw) * 16));
+                const int4_t w1 = dq_lds_v4(slot + (uint32_t)(((2 * g + 1) ^ rsw) * 16));
+                for (int i = 0; i < 4; ++i) {
+                    wd[i] = (uint32_t)w0[i]; wd[4 + i] = (uint32_t)w1[i];
+                    ad[i] = (uint32_t)af[c][0][i]; ad[4 + i] = (uint32_t)af[c][1][i];
+                }
+            }
+            if (NV) {
+                // E4M3 scales of blocks 8 st + 2 g, + 1 (two bytes of the row's dword)
+                const int sb = 8 * st + 2 * g;
+                const uint32_t wsp = dq_lds_u32(srw + (uint32_t)(sb & ~3)) >> (8 * (sb & 3));
+                const uint32_t asp = dq_lds_u32(sra + (uint32_t)(sb & ~3)) >> (8 * (sb & 3));
+                const _Float16 ws0 = e4m3_to_f16(wsp & 0xFFu), ws1 = e4m3_to_f16((wsp >> 8) & 0xFFu);
+                const _Float16 as0 = e4m3_to_f16(asp & 0xFFu), as1 = e4m3_to_f16((asp >> 8) & 0xFFu);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint4 bw = dequant8_nvfp4(wd[j], j < 2 ? ws0 : ws1);
+                    const uint4 ba = dequant8_nvfp4(ad[j], j < 2 ? as0 : as1);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ba),
+                                                                 __builtin_bit_cast(half8_t, bw), acc, 0, 0, 0);
+                }
+            } else {
+                // E8M0 scale of block 4 st + g
+                const int sb = 4 * st + g;
+                const int ew = (int)((dq_lds_u32(srw + (uint32_t)(sb & ~3)) >> (8 * (sb & 3))) & 0xFFu) - 127;
+                const int ea = (int)((dq_lds_u32(sra + (uint32_t)(sb & ~3)) >> (8 * (sb & 3))) & 0xFFu) - 127;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint4 bw = dequant8_mxfp8(make_uint2(wd[2 * j], wd[2 * j + 1]), ew);
+                    const uint4 ba = dequant8_mxfp8(make_uint2(ad[2 * j], ad[2 * j + 1]), ea);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ba),
+                                                                  __builtin_bit_cast(bf16x8_t, bw), acc, 0, 0, 0);
+                }
+            }
+        }
+        if (c + RSB < QC) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the slot's LDS reads have returned
+            copy_chunk(c + RSB);
+        }
+    }
+    __syncthreads();   // every wave is done with its LDS region
+    float4_t* red = reinterpret_cast<float4_t*>(dsm);   // [WAVES][64]
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    // lane l of the first wave finishes output rows 4 (l / 16) + i, column n0 + l % 16
+    if (tid < 64) {
+        float4_t v = red[tid];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+            const float4_t x = red[w * 64 + tid];
+            v = float4_t{v[0] + x[0], v[1] + x[1], v[2] + x[2], v[3] + x[3]};
+        }
+        const int nn = n0 + (tid & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * (tid >> 4) + i;
+            if (m < p.M && nn < p.N) {
+                const float o = v[i] * p.alpha;
+                if (OUT_F32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + nn] = o;
+                else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + nn] = f32_to_bf16_rne(o);
+            }
+        }
+    }
+}
+
+static size_t dq_decode_lds_bytes(int kind, int64_t k)
+{
+    const int64_t ks = kind == DQ_NVFP4 ? k / 16 : k / 32;
+    const int64_t qc = kind == DQ_NVFP4 ? k / 1024 : k / 512;
+    const int64_t rs = qc < DQD_RS ? qc : DQD_RS;
+    return (size_t)(4 * rs * 2048 + 2 * 16 * ks);
+}
+
+// whether dq_decode_stream_kernel serves this shape (kind: DQ_NVFP4 or DQ_MXFP8)
+static bool dq_decode_ok(int kind, int64_t m, int64_t k)
+{
+    return m <= 16 && k % 1024 == 0 && k >= 1024 && k <= 8192 && dq_decode_lds_bytes(kind, k) <= 65536;
+}
+
+template <int KIND, int QC, bool OUT_F32>
+static void launch_dq_decode_qc(const DqArgs& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((dq_decode_stream_kernel<KIND, QC, OUT_F32>), dim3((a.N + 15) / 16), dim3(256),
+                       dq_decode_lds_bytes(KIND, a.K), stream, a);
+}
+
+template <int KIND, bool OUT_F32>
+static hipError_t launch_dq_decode(const DqArgs& a, hipStream_t stream)
+{
+    const int qc = KIND == DQ_NVFP4 ? a.K / 1024 : a.K / 512;
+    switch (qc) {
+    case 1: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 1, OUT_F32>(a, stream); break;
+    case 2: launch_dq_decode_qc<KIND, 2, OUT_F32>(a, stream); break;
+    case 3: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 3, OUT_F32>(a, stream); break;
+    case 4: launch_dq_decode_qc<KIND, 4, OUT_F32>(a, stream); break;
+    case 5: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 5, OUT_F32>(a, stream); break;
+    case 6: launch_dq_decode_qc<KIND, 6, OUT_F32>(a, stream); break;
+    case 7: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 7, OUT_F32>(a, stream); break;
+    case 8: launch_dq_decode_qc<KIND, 8, OUT_F32>(a, stream); break;
+    case 10: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 10, OUT_F32>(a, stream); break;
+    case 12: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 12, OUT_F32>(a, stream); break;
+    case 14: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 14, OUT_F32>(a, stream); break;
+    case 16: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 16, OUT_F32>(a, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+extern "C" int mxl_dq_decode_ok(int nv, int64_t m, int64_t k) { return dq_decode_ok(nv ? DQ_NVFP4 : DQ_MXFP8, m, k) ? 1 : 0; }
+
 // Split-K plan of the 128 x 128 dequantizing kernel: at least 8 stages of 64
 // per split and an even stage count.
 static int dq_splits(int64_t m, int64_t n, int64_t k, int* chunk)
@@ -657,6 +903,8 @@ extern "C" hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const v
     DqArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
              static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
              (int)m, (int)n, (int)k, alpha};
+    if (dq_decode_ok(DQ_NVFP4, m, k))
+        return out_f32 ? launch_dq_decode<DQ_NVFP4, true>(a, stream) : launch_dq_decode<DQ_NVFP4, false>(a, stream);
     return dq_run(a, out_f32, work, work_bytes, stream, [&](const DqArgs& x, int f32) {
         if (f32) return launch_dq<DQ_NVFP4, 128, 128, 2, 2, true>(x, stream);
         return launch_dq<DQ_NVFP4, 128, 128, 2, 2, false>(x, stream);
@@ -676,6 +924,8 @@ extern "C" hipError_t mxl_launch_mxfp8_exact_gemm(const void* aq, const void* as
     DqArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
              static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
              (int)m, (int)n, (int)k, 1.0f};
+    if (dq_decode_ok(DQ_MXFP8, m, k))
+        return out_f32 ? launch_dq_decode<DQ_MXFP8, true>(a, stream) : launch_dq_decode<DQ_MXFP8, false>(a, stream);
     return dq_run(a, out_f32, work, work_bytes, stream, [&](const DqArgs& x, int f32) {
         if (f32) return launch_dq<DQ_MXFP8, 128, 128, 2, 2, true>(x, stream);
         return launch_dq<DQ_MXFP8, 128, 128, 2, 2, false>(x, stream);
@@ -814,11 +1064,18 @@ extern "C" const char* mxl_w4a16_gemm_config_name(void)
 extern "C" const char* mxl_nv_gemm_config_name(int64_t m, int64_t n, int64_t k)
 {
     if (mxl_dq8w_ok(DQ8W_FMT_NVFP4, m, n, k)) return mxl_dq8w_config_name();
+    if (dq_decode_ok(DQ_NVFP4, m, k))
+        return "dq_decode_stream_kernel<nvfp4 -> exact f16, 16 W rows per workgroup, each wave streams its own K quarter "
+               "through a ring of 3 LDS chunk slots (8 rows x 128 B non-temporal copies), f16 mfma 16x16x32>";
     return "dq_gemm_kernel<nvfp4 -> exact f16, tile 128x128x64, 2x2 waves of 64x64, f16 mfma 32x32x16>";
 }
 
 extern "C" const char* mxl_mxfp8_exact_config_name(int64_t m, int64_t n, int64_t k)
 {
     if (mxl_mx8_tile_ok(m, n, k)) return mxl_mx8_tile_config_name();
+    if (dq_decode_ok(DQ_MXFP8, m, k))
+        return "dq_decode_stream_kernel<mxfp8 -> exact bf16, 16 W rows per workgroup, each wave streams its own K "
+               "quarter through a ring of 3 LDS chunk slots (8 rows x 128 B non-temporal copies), bf16 mfma "
+               "16x16x32>";
     return "dq_gemm_kernel<mxfp8 -> exact bf16, tile 128x128x64, 2x2 waves of 64x64, bf16 mfma 32x32x16>";
 }

@@ -667,8 +667,9 @@ def test_nvfp4_config_sampled():
 
 # split-K: few output tiles and a long K, so the library splits K over
 # workgroups (mx_gemm_workspace_size > 0) and sums fp32 partials in order.
-# (M <= 48 MXFP4 runs the decode kernels, which do not split.)
-SPLIT_SHAPES = [(300, 2048, 200), (64, 5120, 96), (1, 4096, 48), (513, 1536, 130)]
+# (M <= 48 MXFP4 runs the decode kernels, which do not split; so does MXFP8
+# at M <= 16 when K is a multiple of 1024 up to 8192, hence K = 4608 at M = 1.)
+SPLIT_SHAPES = [(300, 2048, 200), (64, 5120, 96), (1, 4608, 48), (513, 1536, 130)]
 SPLIT_CASES = [(f, m, k, n) for (m, k, n) in SPLIT_SHAPES for f in ("mxfp4", "mxfp8") if not (f == "mxfp4" and m <= 48)]
 
 
@@ -739,3 +740,54 @@ def test_fused_prologue_codes_dumped(fmt, fast, m, k, n):
     assert np.array_equal(host(ds), rs), "prologue scales"
     assert np.array_equal(host(dq), rq), "prologue codes"
     assert torch.equal(y, y0), "the dump does not change the product"
+
+
+# The decode-shaped exact MXFP8 and NVFP4 GEMMs (dq_decode_stream_kernel: M <=
+# 16, K % 1024 == 0, K <= 8192) against the oracle in full: one chunk ring
+# slot (NVFP4 K = 1024), a ring shorter than the quarter (K = 5120), the
+# largest K; ragged N; normal operands and fuzz-corpus operands whose block
+# scales reach 2^-127 (MXFP8) or the subnormal E4M3 scales (NVFP4); bf16 and
+# fp32 output.
+DQ_DECODE_CASES = [(1, 1024, 300), (3, 5120, 200), (8, 5120, 17), (16, 8192, 130), (16, 2048, 1)]
+
+
+@pytest.mark.parametrize("data", ["normal", "fuzz"])
+@pytest.mark.parametrize("m,k,n", DQ_DECODE_CASES)
+def test_mxfp8_decode_kernel(m, k, n, data):
+    plan = mxl.mx_gemm_plan("mxfp8", "mxfp8", m, n, k)
+    say(f"mxfp8 decode {data} {m}x{k}x{n}: {plan[:60]}")
+    assert "dq_decode_stream_kernel<mxfp8" in plan
+    if data == "normal":
+        a_bits, w_bits = W.activations_entry_outliers(m, k, seed=5 + m), W.normal_bf16(n, k, 0.02, 6)
+    else:
+        a_bits, w_bits = fuzz_operands(m, k, n)
+    y_ref, s, (raq, ras), (rwq, rws) = oracle_full(a_bits, w_bits, "mxfp8")
+    fl = flushed_terms(oracle.mx_dequantize("e4m3", raq, ras, m, k), oracle.mx_dequantize("e4m3", rwq, rws, n, k))
+    for out_f32 in (False, True):
+        y, _, (aq, as_), (wq, ws) = run_mx(a_bits, w_bits, "mxfp8", out_f32=out_f32)
+        assert np.array_equal(host(aq), raq) and np.array_equal(host(wq), rwq)
+        check_gemm(y_host(y), y_ref, s, not out_f32, f"mxfp8 decode {data} {m}x{k}x{n} f32={out_f32}", fl,
+                   underflow_allowance(k) if data == "fuzz" else 0.0)
+
+
+@pytest.mark.parametrize("data", ["normal", "fuzz"])
+@pytest.mark.parametrize("m,k,n", DQ_DECODE_CASES)
+def test_nvfp4_decode_kernel(m, k, n, data):
+    plan = mxl.mx_gemm_plan("nvfp4", "nvfp4", m, n, k)
+    say(f"nvfp4 decode {data} {m}x{k}x{n}: {plan[:60]}")
+    assert "dq_decode_stream_kernel<nvfp4" in plan
+    if data == "normal":
+        a_bits, w_bits = W.normal_bf16(m, k, 1.0, 7), W.normal_bf16(n, k, 0.02, 8)
+    else:
+        a_bits, w_bits = fuzz_operands(m, k, n)
+    g_a = oracle.nv_global_scale(oracle.bf16_amax(a_bits))
+    g_w = oracle.nv_global_scale(oracle.bf16_amax(w_bits))
+    aq, as_ = oracle.nv_quantize(a_bits, g_a)
+    wq, ws = oracle.nv_quantize(w_bits, g_w)
+    y_ref, s = oracle.gemm_dq(oracle.nv_dequantize(aq, as_, m, k, g_a), oracle.nv_dequantize(wq, ws, n, k, g_w))
+    u = underflow_allowance(k) if data == "fuzz" else 0.0
+    for out_f32 in (False, True):
+        y, (gaq, gas), (gwq, gws) = nv_case(a_bits, w_bits, g_a, g_w, out_f32)
+        assert np.array_equal(host(gaq), aq) and np.array_equal(host(gas), as_)
+        assert np.array_equal(host(gwq), wq) and np.array_equal(host(gws), ws)
+        check_gemm(y_host(y), y_ref, s, not out_f32, f"nvfp4 decode {data} {m}x{k}x{n} f32={out_f32}", None, u)
