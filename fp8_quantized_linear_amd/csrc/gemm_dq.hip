@@ -59,21 +59,31 @@ struct DqTraits {
 typedef __bf16 bf16x2_t_ __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-// E4M3 code -> f16 (exact; NaN codes never occur in valid scales).
-__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t c)
+// The two E4M3 codes in bits 0-15 of v as an f16 pair, by the hardware
+// conversion at scale 1: exact, since every finite E4M3 value (subnormals
+// included) is an f16 normal.  NaN codes never occur in valid scales.
+__device__ __forceinline__ half2_t e4m3x2_to_f16x2(uint32_t v)
 {
-    const uint32_t ef = (c >> 3) & 15u, m = c & 7u;
-    float v = ef == 0 ? (float)m * 0x1p-9f : __uint_as_float(((ef + 120u) << 23) | (m << 20));
-    return (_Float16)((c & 0x80u) ? -v : v);
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+}
+// the same pair as fp32 values
+__device__ __forceinline__ float2_t e4m3x2_to_f32x2(uint32_t v)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 1.0f, false);
+}
+// {s[i], s[i]}
+__device__ __forceinline__ half2_t bcast_h2(half2_t s, int i)
+{
+    return i ? half2_t{s[1], s[1]} : half2_t{s[0], s[0]};
 }
 
 // 8 E2M1 codes (one dword, element 2j in the low nibble of byte j) times an
-// E4M3 scale, as 8 f16 values.
-__device__ __forceinline__ uint4 dequant8_nvfp4(uint32_t codes, _Float16 s)
+// E4M3 scale given as an f16 pair {s, s}, as 8 f16 values (exact products:
+// at most 6 significant bits, magnitudes in [2^-10, 2688]).
+__device__ __forceinline__ uint4 dequant8_nvfp4(uint32_t codes, half2_t s2)
 {
-    const half2_t s2 = {s, s};
     half2_t h[4];
-    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;  // exact products
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;
     h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s2;
     h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s2;
     h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s2;
@@ -123,14 +133,6 @@ __device__ __forceinline__ uint4 dequant8_nvfp4_bf16(uint32_t codes, float s)
     const float2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
     return make_uint4(bf16x2_rne(f0[0] * s, f0[1] * s), bf16x2_rne(f1[0] * s, f1[1] * s),
                       bf16x2_rne(f2[0] * s, f2[1] * s), bf16x2_rne(f3[0] * s, f3[1] * s));
-}
-
-// E4M3 code -> fp32 (exact; NaN codes never occur in valid scales).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c)
-{
-    const uint32_t ef = (c >> 3) & 15u, m = c & 7u;
-    const float v = ef == 0 ? (float)m * 0x1p-9f : __uint_as_float(((ef + 120u) << 23) | (m << 20));
-    return (c & 0x80u) ? -v : v;
 }
 
 struct DqArgs {
@@ -383,15 +385,16 @@ __global__ __launch_bounds__(WM * WN * 64) void dq_gemm_kernel(DqArgs p)
                                     : (fl & 1u ? scb[0] : 0u) | (fl & 4u ? scb[1] << 8 : 0u);
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
             if (F16) {
-                const _Float16 s0 = e4m3_to_f16(sc & 0xFFu), s1 = e4m3_to_f16((sc >> 8) & 0xFFu);
+                const half2_t sp = e4m3x2_to_f16x2(sc);
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {   // 8 elements per dword -> one 16-B chunk of f16
-                    const uint4 d = dequant8_nvfp4(w[h], h < 2 ? s0 : s1);
+                    const uint4 d = dequant8_nvfp4(w[h], bcast_h2(sp, h >> 1));
                     const int chunk = (c * 4 + h) ^ dq_swz(row);
                     *reinterpret_cast<uint4*>(tile + row * DQ_ROW_BYTES + chunk * 16) = d;
                 }
             } else {
-                const float s0 = e4m3_to_f32(sc & 0xFFu), s1 = e4m3_to_f32((sc >> 8) & 0xFFu);
+                const float2_t sp = e4m3x2_to_f32x2(sc);
+                const float s0 = sp[0], s1 = sp[1];
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {   // 8 elements per dword -> one 16-B chunk of bf16
                     const uint4 d = dequant8_nvfp4_bf16(w[h], h < 2 ? s0 : s1);
@@ -610,9 +613,10 @@ extern "C" hipError_t mxl_launch_splitk_reduce(const float* part, int splits, in
 //    its two copies have landed (exact vmcnt); the slot is refilled when its
 //    LDS reads have returned.  Inside a copy, row q's 16-byte chunk L sits at
 //    L ^ ((q >> 1) & 7), so the 16 rows of a lane group cover all banks.
-//  * The scale blocks of the 16 W rows and of A's 16 rows go to LDS first
-//    (256-byte copies spread over the waves, one barrier), and the wave's A
-//    codes (rows past M read as zero) to registers, before the W copies.
+//  * The wave's A codes (and, NVFP4, its A scales) go to registers first
+//    (rows past M read as zero), then the scale block of the 16 W rows (and,
+//    MXFP8, of A's 16 rows) to LDS (256-byte copies spread over the waves,
+//    one barrier), all before the W copies.
 //  * Dequantization as in the tile kernels, in registers: MXFP8 codes to
 //    bf16 by v_cvt_scalef32_pk_bf16_fp8 with the E8M0 scale in the exponent
 //    field; NVFP4 codes to f16 (scale 1) times the E4M3 block scale as an
@@ -659,7 +663,9 @@ __global__ __launch_bounds__(256) void dq_decode_stream_kernel(DqArgs p)
     constexpr int KS = NV ? K / 16 : K / 32;              // scale bytes per row
     constexpr int QB = ROWB / WAVES;                      // code bytes per row per wave (128 QC)
     constexpr int SPC = NV ? 2 : 1;                       // stages (128 K) per chunk
-    constexpr int SCOP = 2 * 16 * KS / 256;               // scale copies: W block, then A block
+    constexpr int NST = QC * SPC;                         // stages per wave
+    constexpr bool AS_REG = NV;                           // A scales in registers (else in LDS)
+    constexpr int SCOP = (AS_REG ? 1 : 2) * 16 * KS / 256; // scale block copies: W, then (MXFP8) A
     extern __shared__ __align__(16) uint8_t dsm[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -682,15 +688,25 @@ __global__ __launch_bounds__(256) void dq_decode_stream_kernel(DqArgs p)
             const int off = NV ? (st0 + SPC * c + i) * 64 + g * 16 : (st0 + c) * 128 + g * 32 + i * 16;
             af[c][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, r * ROWB + off, 0, 0);
         }
-    // scale blocks [16 rows][KS] of W and of A
+    // NVFP4: this wave's A scales, one dword per stage: row r, the dword
+    // that holds lane group g's bytes (blocks 8 st + 2 g, + 1, at byte
+    // 2 (g & 1)); rows past M read as zero
+    uint32_t asr[AS_REG ? NST : 1];
+    if (AS_REG) {
+        const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_s, (short)0, p.M * KS, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < NST; ++i)
+            asr[i] = __builtin_amdgcn_raw_buffer_load_b32(ras, r * KS + 8 * (st0 + i) + 4 * (g >> 1), 0, 0);
+    }
+    // the scale block [16 rows][KS] of W (MXFP8: then A's), spread over the waves
     {
         const int4_t rws = make_rsrc(p.w_s, (uint32_t)p.N * KS);
         const int4_t ras = make_rsrc(p.a_s, (uint32_t)p.M * KS);
 #pragma unroll
         for (int j = 0; j < SCOP; ++j)
             if (j % WAVES == wave) {
-                if (j < SCOP / 2) dma_b32(sw_lds + j * 256, n0 * KS + j * 256 + lane * 4, rws, 0);
-                else dma_b32(sw_lds + j * 256, (j - SCOP / 2) * 256 + lane * 4, ras, 0);
+                if (j < 16 * KS / 256) dma_b32(sw_lds + j * 256, n0 * KS + j * 256 + lane * 4, rws, 0);
+                else dma_b32(sw_lds + j * 256, (j - 16 * KS / 256) * 256 + lane * 4, ras, 0);
             }
     }
     // W chunks: chunk c (copies h = 0, 1: rows 8 h .. 8 h + 7) into slot c % RSB
@@ -743,15 +759,13 @@ __global__ __launch_bounds__(256) void dq_decode_stream_kernel(DqArgs p)
             }
             if (NV) {
                 // E4M3 scales of blocks 8 st + 2 g, + 1 (two bytes of the row's dword)
-                const int sb = 8 * st + 2 * g;
-                const uint32_t wsp = dq_lds_u32(srw + (uint32_t)(sb & ~3)) >> (8 * (sb & 3));
-                const uint32_t asp = dq_lds_u32(sra + (uint32_t)(sb & ~3)) >> (8 * (sb & 3));
-                const _Float16 ws0 = e4m3_to_f16(wsp & 0xFFu), ws1 = e4m3_to_f16((wsp >> 8) & 0xFFu);
-                const _Float16 as0 = e4m3_to_f16(asp & 0xFFu), as1 = e4m3_to_f16((asp >> 8) & 0xFFu);
+                const uint32_t wsp = dq_lds_u32(srw + (uint32_t)(8 * st + 4 * (g >> 1))) >> (16 * (g & 1));
+                const half2_t wsc = e4m3x2_to_f16x2(wsp);
+                const half2_t asc = e4m3x2_to_f16x2(asr[SPC * c + hf] >> (16 * (g & 1)));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const uint4 bw = dequant8_nvfp4(wd[j], j < 2 ? ws0 : ws1);
-                    const uint4 ba = dequant8_nvfp4(ad[j], j < 2 ? as0 : as1);
+                    const uint4 bw = dequant8_nvfp4(wd[j], bcast_h2(wsc, j >> 1));
+                    const uint4 ba = dequant8_nvfp4(ad[j], bcast_h2(asc, j >> 1));
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ba),
                                                                  __builtin_bit_cast(half8_t, bw), acc, 0, 0, 0);
                 }
@@ -804,7 +818,7 @@ static size_t dq_decode_lds_bytes(int kind, int64_t k)
     const int64_t ks = kind == DQ_NVFP4 ? k / 16 : k / 32;
     const int64_t qc = kind == DQ_NVFP4 ? k / 1024 : k / 512;
     const int64_t rs = qc < DQD_RS ? qc : DQD_RS;
-    return (size_t)(4 * rs * 2048 + 2 * 16 * ks);
+    return (size_t)(4 * rs * 2048 + (kind == DQ_NVFP4 ? 1 : 2) * 16 * ks);
 }
 
 // whether dq_decode_stream_kernel serves this shape (kind: DQ_NVFP4 or DQ_MXFP8)
