@@ -259,6 +259,18 @@ def kernel_set(torch, mxl, W, reps: int = 3):
         run(cfg.name, lambda: mxl.mx_gemm(aq, as_, wq, ws, cfg.k, y=y))
         if cfg.m <= 16:
             run(f"w4a16 {cfg.name}", lambda: mxl.mx_gemm_w4a16(a, wq, ws, "mxfp4", y=y))
+    # NVFP4 W4A4 and W8A8 MXFP8 decode, M = 1
+    cfg = W.DECODE[0]
+    w, a = to_dev(cfg.weights()), to_dev(cfg.activations())
+    g_w = mxl.mx_nv_global_scale(float(mxl.mx_tensor_amax(w).item()))
+    g_a = mxl.mx_nv_global_scale(float(mxl.mx_tensor_amax(a).item()))
+    wq, ws = mxl.mx_pack_weights(w, "nvfp4", global_scale=g_w)
+    aq, as_ = mxl.mx_quantize_act(a, "nvfp4", global_scale=g_a)
+    y = torch.empty((cfg.m, cfg.n), dtype=torch.bfloat16, device=dev)
+    run(f"nvfp4 {cfg.name}", lambda: mxl.nv_gemm(aq, as_, wq, ws, cfg.k, 1.0 / (g_a * g_w), y=y))
+    wq, ws = mxl.mx_pack_weights(w, "mxfp8", "floor")
+    aq, as_ = mxl.mx_quantize_act(a, "mxfp8", "ceil")
+    run(f"mxfp8 {cfg.name}", lambda: mxl.mx_gemm(aq, as_, wq, ws, cfg.k, "mxfp8", "mxfp8", y=y))
     print(json.dumps({"kernel_set": "done", "reps": reps}))
 
 

@@ -510,20 +510,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
-// K splits for a launch of `tiles` tiles over nk stages: as many splits as
-// still fit one workgroup per compute unit (256), so that all of them run in
-// one round, every split at least min_stages long, and (even) a whole number
-// of stage pairs per split.  Returns the split count and sets the stages per
-// split.
-extern "C" int mxl_choose_splits(int64_t tiles, int nk, int min_stages, int even, int* chunk)
+// K splits for a launch of `tiles` tiles over nk stages: up to 128 tiles, as
+// many splits as still fit one workgroup per compute unit (256), so that all
+// of them run in one round; from 129 to two_max tiles (0: none), two splits,
+// one round at two workgroups per CU; every split at least min_stages long,
+// and (even) a whole number of stage pairs per split.  Returns the split
+// count and sets the stages per split.
+extern "C" int mxl_choose_splits(int64_t tiles, int nk, int min_stages, int even, int two_max, int* chunk)
 {
     int s = 1;
     if (tiles <= 128) {
         s = (int)(256 / tiles);
-        const int cap = nk / min_stages;
-        if (s > cap) s = cap;
-        if (s < 1) s = 1;
+    } else if (tiles <= two_max) {
+        s = 2;
     }
+    const int cap = nk / min_stages;
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
     int c = (nk + s - 1) / s;
     if (even && (c & 1)) ++c;
     *chunk = c;
@@ -1214,7 +1217,7 @@ static hipError_t dispatch_tile(const GemmArgs& a, ShapeClass sc, hipStream_t s)
 static int default_splits(int64_t m, int64_t n, int64_t k, int* chunk)
 {
     const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
-    return mxl_choose_splits(tiles, (int)((k + BK - 1) / BK), 4, 0, chunk);
+    return mxl_choose_splits(tiles, (int)((k + BK - 1) / BK), 4, 0, 0, chunk);
 }
 
 template <int AB, int WB, bool FUSED, int RULE>

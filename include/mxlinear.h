@@ -206,14 +206,16 @@ mx_status mx_gemm(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void*
  * MX_NOALLOC_SCRATCH_BYTES that the library holds in device memory on every
  * GPU it runs on, for the life of the process; the call itself allocates
  * nothing.  The result is bitwise equal to mx_gemm with a workspace.  Split-K
- * runs only while the output tiles cannot fill the GPU (at most 256 tile-
- * splits of 128 x 128 fp32), so every shape fits the scratch; a need beyond
- * it would return MX_ERR_WORKSPACE.  All calls on one GPU share its scratch
- * (nothing in it needs clearing between calls): calls that overlap in time
- * on one GPU, on different streams, race and must be ordered by the caller.
+ * runs only while the output tiles cannot fill the GPU twice over (at most
+ * 384 tile-splits of 128 x 128 fp32: one per CU up to 128 tiles, two per
+ * tile from 129 to 192 tiles of the dequantizing kernel), so every shape fits
+ * the scratch; a need beyond it would return MX_ERR_WORKSPACE.  All calls on
+ * one GPU share its scratch (nothing in it needs clearing between calls):
+ * calls that overlap in time on one GPU, on different streams, race and must
+ * be ordered by the caller.
  * Errors as mx_gemm.
  */
-#define MX_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define MX_NOALLOC_SCRATCH_BYTES (24u << 20)
 mx_status mx_gemm_noalloc(mx_format a_fmt, mx_format w_fmt, const void* a_q, const void* a_s,
                           const void* w_q, const void* w_s, int64_t m, int64_t n, int64_t k, void* y,
                           unsigned flags, mx_stream_t stream);

@@ -39,7 +39,7 @@ def test_noalloc_matches_mx_gemm(fmt, big, small):
     for (m, k, n) in (big, small):
         need = mxl.mx_gemm_workspace_size(fmt, fmt, m, n, k)
         print(f"noalloc {fmt} {m}x{k}x{n}: split-K partials {need} B of scratch", flush=True)
-        assert 0 < need <= (16 << 20)
+        assert 0 < need <= (24 << 20)
         a_bits = W.activations_entry_outliers(m, k)
         w_bits = W.normal_bf16(n, k, 0.02, 1)
         aq, as_ = mxl.mx_quantize_act(cuda_bf16(a_bits), fmt, "ceil")
