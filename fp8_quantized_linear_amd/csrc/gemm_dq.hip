@@ -624,10 +624,15 @@ extern "C" hipError_t mxl_launch_splitk_reduce(const float* part, int splits, in
 //    supplies row r and, in step j of a stage, elements [32 g + 8 j, +8) of
 //    it, for A and W alike, so each step sums 32 distinct K.
 //  * The four K quarters are summed through LDS; Y = alpha * sum.
-__device__ __forceinline__ void dq_dma_b128_nt(uint32_t lds, int voff, const int4_t& rsrc, int soff)
+template <bool NT>
+__device__ __forceinline__ void dq_dma_b128(uint32_t lds, int voff, const int4_t& rsrc, int soff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+    if (NT)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 __device__ __forceinline__ int4_t dq_lds_v4(uint32_t addr)
 {
@@ -652,7 +657,7 @@ __device__ __forceinline__ void dq_wait_vmcnt_n(int n)
 
 constexpr int DQD_RS = 3;   // ring slots (chunks) per wave
 
-template <int KIND, int QC, bool OUT_F32>
+template <int KIND, int QC, bool OUT_F32, bool NT>
 __global__ __launch_bounds__(256) void dq_decode_stream_kernel(DqArgs p)
 {
     static_assert(KIND == DQ_MXFP8 || KIND == DQ_NVFP4, "decode formats");
@@ -720,7 +725,7 @@ __global__ __launch_bounds__(256) void dq_decode_stream_kernel(DqArgs p)
     auto copy_chunk = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            dq_dma_b128_nt(lds_w + (uint32_t)((c % RSB) * 2048 + h * 1024), voffh[h], rw, wave * QB + c * 128);
+            dq_dma_b128<NT>(lds_w + (uint32_t)((c % RSB) * 2048 + h * 1024), voffh[h], rw, wave * QB + c * 128);
     };
 #pragma unroll
     for (int c = 0; c < RSB; ++c) copy_chunk(c);
@@ -821,39 +826,62 @@ static size_t dq_decode_lds_bytes(int kind, int64_t k)
     return (size_t)(4 * rs * 2048 + (kind == DQ_NVFP4 ? 1 : 2) * 16 * ks);
 }
 
-// whether dq_decode_stream_kernel serves this shape (kind: DQ_NVFP4 or DQ_MXFP8)
+// whether dq_decode_stream_kernel serves this shape (kind: DQ_NVFP4 or DQ_MXFP8):
+// one launch per 16 rows of A, at most two
 static bool dq_decode_ok(int kind, int64_t m, int64_t k)
 {
-    return m <= 16 && k % 1024 == 0 && k >= 1024 && k <= 8192 && dq_decode_lds_bytes(kind, k) <= 65536;
+    return m <= 32 && k % 1024 == 0 && k >= 1024 && k <= 8192 && dq_decode_lds_bytes(kind, k) <= 65536;
 }
 
 template <int KIND, int QC, bool OUT_F32>
-static void launch_dq_decode_qc(const DqArgs& a, hipStream_t stream)
+static void launch_dq_decode_qc(const DqArgs& a, bool nt, hipStream_t stream)
 {
-    hipLaunchKernelGGL((dq_decode_stream_kernel<KIND, QC, OUT_F32>), dim3((a.N + 15) / 16), dim3(256),
-                       dq_decode_lds_bytes(KIND, a.K), stream, a);
+    if (nt)
+        hipLaunchKernelGGL((dq_decode_stream_kernel<KIND, QC, OUT_F32, true>), dim3((a.N + 15) / 16), dim3(256),
+                           dq_decode_lds_bytes(KIND, a.K), stream, a);
+    else
+        hipLaunchKernelGGL((dq_decode_stream_kernel<KIND, QC, OUT_F32, false>), dim3((a.N + 15) / 16), dim3(256),
+                           dq_decode_lds_bytes(KIND, a.K), stream, a);
 }
 
 template <int KIND, bool OUT_F32>
-static hipError_t launch_dq_decode(const DqArgs& a, hipStream_t stream)
+static hipError_t launch_dq_decode_rows(const DqArgs& a, bool nt, hipStream_t stream)
 {
     const int qc = KIND == DQ_NVFP4 ? a.K / 1024 : a.K / 512;
     switch (qc) {
-    case 1: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 1, OUT_F32>(a, stream); break;
-    case 2: launch_dq_decode_qc<KIND, 2, OUT_F32>(a, stream); break;
-    case 3: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 3, OUT_F32>(a, stream); break;
-    case 4: launch_dq_decode_qc<KIND, 4, OUT_F32>(a, stream); break;
-    case 5: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 5, OUT_F32>(a, stream); break;
-    case 6: launch_dq_decode_qc<KIND, 6, OUT_F32>(a, stream); break;
-    case 7: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 7, OUT_F32>(a, stream); break;
-    case 8: launch_dq_decode_qc<KIND, 8, OUT_F32>(a, stream); break;
-    case 10: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 10, OUT_F32>(a, stream); break;
-    case 12: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 12, OUT_F32>(a, stream); break;
-    case 14: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 14, OUT_F32>(a, stream); break;
-    case 16: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 16, OUT_F32>(a, stream); break;
+    case 1: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 1, OUT_F32>(a, nt, stream); break;
+    case 2: launch_dq_decode_qc<KIND, 2, OUT_F32>(a, nt, stream); break;
+    case 3: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 3, OUT_F32>(a, nt, stream); break;
+    case 4: launch_dq_decode_qc<KIND, 4, OUT_F32>(a, nt, stream); break;
+    case 5: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 5, OUT_F32>(a, nt, stream); break;
+    case 6: launch_dq_decode_qc<KIND, 6, OUT_F32>(a, nt, stream); break;
+    case 7: if constexpr (KIND == DQ_NVFP4) launch_dq_decode_qc<KIND, 7, OUT_F32>(a, nt, stream); break;
+    case 8: launch_dq_decode_qc<KIND, 8, OUT_F32>(a, nt, stream); break;
+    case 10: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 10, OUT_F32>(a, nt, stream); break;
+    case 12: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 12, OUT_F32>(a, nt, stream); break;
+    case 14: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 14, OUT_F32>(a, nt, stream); break;
+    case 16: if constexpr (KIND == DQ_MXFP8) launch_dq_decode_qc<KIND, 16, OUT_F32>(a, nt, stream); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// Rows 16 j .. 16 j + 15 of A and Y per launch (W streamed once per launch).
+template <int KIND, bool OUT_F32>
+static hipError_t launch_dq_decode(const DqArgs& a0, hipStream_t stream)
+{
+    const size_t rowb = KIND == DQ_NVFP4 ? (size_t)a0.K / 2 : (size_t)a0.K;
+    const size_t ks = KIND == DQ_NVFP4 ? (size_t)a0.K / 16 : (size_t)a0.K / 32;
+    for (int r0 = 0; r0 < a0.M; r0 += 16) {
+        DqArgs a = a0;
+        a.a_q = a0.a_q + r0 * rowb;
+        a.a_s = a0.a_s + r0 * ks;
+        a.y = static_cast<uint8_t*>(a0.y) + (size_t)r0 * a0.N * (OUT_F32 ? 4 : 2);
+        a.M = a0.M - r0 < 16 ? a0.M - r0 : 16;
+        const hipError_t e = launch_dq_decode_rows<KIND, OUT_F32>(a, r0 + 16 >= a0.M, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 extern "C" int mxl_dq_decode_ok(int nv, int64_t m, int64_t k) { return dq_decode_ok(nv ? DQ_NVFP4 : DQ_MXFP8, m, k) ? 1 : 0; }
@@ -1082,7 +1110,8 @@ extern "C" const char* mxl_nv_gemm_config_name(int64_t m, int64_t n, int64_t k)
     if (mxl_dq8w_ok(DQ8W_FMT_NVFP4, m, n, k)) return mxl_dq8w_config_name();
     if (dq_decode_ok(DQ_NVFP4, m, k))
         return "dq_decode_stream_kernel<nvfp4 -> exact f16, 16 W rows per workgroup, each wave streams its own K quarter "
-               "through a ring of 3 LDS chunk slots (8 rows x 128 B non-temporal copies), f16 mfma 16x16x32>";
+               "through a ring of 3 LDS chunk slots (8 rows x 128 B non-temporal copies), f16 mfma 16x16x32>, one launch per "
+               "16 rows of A";
     return "dq_gemm_kernel<nvfp4 -> exact f16, tile 128x128x64, 2x2 waves of 64x64, f16 mfma 32x32x16>";
 }
 
@@ -1092,6 +1121,6 @@ extern "C" const char* mxl_mxfp8_exact_config_name(int64_t m, int64_t n, int64_t
     if (dq_decode_ok(DQ_MXFP8, m, k))
         return "dq_decode_stream_kernel<mxfp8 -> exact bf16, 16 W rows per workgroup, each wave streams its own K "
                "quarter through a ring of 3 LDS chunk slots (8 rows x 128 B non-temporal copies), bf16 mfma "
-               "16x16x32>";
+               "16x16x32>, one launch per 16 rows of A";
     return "dq_gemm_kernel<mxfp8 -> exact bf16, tile 128x128x64, 2x2 waves of 64x64, bf16 mfma 32x32x16>";
 }

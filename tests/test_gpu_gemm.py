@@ -745,12 +745,14 @@ def test_fused_prologue_codes_dumped(fmt, fast, m, k, n):
 
 
 # The decode-shaped exact MXFP8 and NVFP4 GEMMs (dq_decode_stream_kernel: M <=
-# 16, K % 1024 == 0, K <= 8192) against the oracle in full: one chunk ring
+# 32, one launch per 16 rows of A; K % 1024 == 0, K <= 8192) against the
+# oracle in full: one chunk ring
 # slot (NVFP4 K = 1024), a ring shorter than the quarter (K = 5120), the
 # largest K; ragged N; normal operands and fuzz-corpus operands whose block
 # scales reach 2^-127 (MXFP8) or the subnormal E4M3 scales (NVFP4); bf16 and
 # fp32 output.
-DQ_DECODE_CASES = [(1, 1024, 300), (3, 5120, 200), (8, 5120, 17), (16, 8192, 130), (16, 2048, 1)]
+DQ_DECODE_CASES = [(1, 1024, 300), (3, 5120, 200), (8, 5120, 17), (16, 8192, 130), (16, 2048, 1),
+                   (17, 5120, 130), (32, 2048, 300), (29, 8192, 33)]   # above 16 rows: two launches
 
 
 @pytest.mark.parametrize("data", ["normal", "fuzz"])
