@@ -82,28 +82,69 @@ __global__ __launch_bounds__(QUANT_THREADS) void mx_quantize_kernel(const uint4*
 }
 
 // NVFP4: a block of 16 is a lane pair.  The block scale and the element codes
-// are roundings of exact reals (amax * g / 6 and x * g / s).  amax * g is
-// exact in fp64 (8 + 24 significant bits); its quotient by 6 is evaluated in
-// fp64 and can only meet an E4M3 rounding midpoint when the quotient is
-// exactly that midpoint, which fp64 then represents exactly.  The element
-// thresholds are compared as x * g <=> t * s by the sign of one fma
-// (e2m1_rne_fma), which is exact.  Returns the 8 codes of the lane's group
-// (element i in nibble i) and the block's scale code and value.
+// are roundings of exact reals (amax * g / 6 and x * g / s), each decided by
+// a bracket where it can be, else exactly:
+//  * Bracket.  With r an approximation of the real value within 2^-21.5
+//    (relative), the hardware converters round r (1 - 2^-20) and r (1 +
+//    2^-20), which strictly bracket the real value.  Rounding is monotonic,
+//    so where the two codes agree they are the real value's code; a
+//    midpoint inside the bracket makes them differ.  Values below 2^-100
+//    lose the relative bound but lie far below the formats' first nonzero
+//    rounding midpoint, and round to zero either way.
+//  * Scale: r = amax * g * fl(1/6) in fp32 (three roundings), clamped to 448
+//    (the format's saturation), rounded to E4M3 by v_cvt_scalef32_pk_fp8_f32
+//    (round to nearest even, subnormals included).  Exactly otherwise: amax *
+//    g is exact in fp64 (8 + 24 significant bits); its quotient by 6 is
+//    evaluated in fp64 and can only meet an E4M3 rounding midpoint when the
+//    quotient is exactly that midpoint, which fp64 then represents exactly.
+//  * Elements: r = x * g * rcp(s) (v_rcp_f32, within 1 ulp; four roundings
+//    in all), rounded to E2M1 by v_cvt_scalef32_pk_fp4_f32 (round to nearest
+//    even, saturating at 6, sign kept), when s > 0, c = g * rcp(s) >= 2^-100
+//    and amax * c (1 + 2^-20) <= 2^30 (no overflow).  Exactly otherwise, and
+//    in every lane whose two codes differ: x * g <=> t * s for each
+//    threshold t by the sign of one fma (e2m1_rne_fma).
+// Returns the 8 codes of the lane's group (element i in nibble i) and the
+// block's scale code and value.
 __device__ __forceinline__ uint32_t nv_encode8(uint4 v, float gscale, uint32_t& sc, float& sf)
 {
     const uint32_t amax = pair_max_u32(amax_bits8(v));
-    const double ag = (double)bf16_bits_to_float(amax) * (double)gscale;   // exact
-    sc = e4m3_rne_f64(ag / 6.0);
-    sf = (float)e4m3_value_f64(sc);                                       // exact
+    const float af = bf16_bits_to_float(amax);
+    {
+        const float r = af * gscale * (1.0f / 6.0f);
+        short2_t pk = {0, 0};
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pk, __builtin_fminf(r * (1.0f - 0x1p-20f), 448.0f),
+                                                      __builtin_fminf(r * (1.0f + 0x1p-20f), 448.0f), 1.0f, false);
+        const uint32_t pw = __builtin_bit_cast(uint32_t, pk);
+        if ((pw & 0xFFu) == ((pw >> 8) & 0xFFu)) {
+            sc = pw & 0xFFu;
+        } else {
+            const double ag = (double)af * (double)gscale;   // exact
+            sc = e4m3_rne_f64(ag / 6.0);
+        }
+    }
+    sf = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sc, 1.0f, false)[0];   // exact
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const float c = gscale * __builtin_amdgcn_rcpf(sf);
+    const float c_lo = c * (1.0f - 0x1p-20f), c_hi = c * (1.0f + 0x1p-20f);
+    uint32_t lo = 0, hi = 0;
+#define MXL_NV_PAIR(J)                                                                               \
+    {                                                                                                \
+        const float x0 = __uint_as_float(w[J] << 16), x1 = __uint_as_float(w[J] & 0xFFFF0000u);     \
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x0 * c_lo, x1 * c_lo, 1.0f, J);            \
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x0 * c_hi, x1 * c_hi, 1.0f, J);            \
+    }
+    MXL_NV_PAIR(0) MXL_NV_PAIR(1) MXL_NV_PAIR(2) MXL_NV_PAIR(3)
+#undef MXL_NV_PAIR
+    const bool fast = sf > 0.0f && c >= 0x1p-100f && af * c_hi <= 0x1p30f;
+    if (fast && lo == hi) return lo;
     float t[7];
     e2m1_thresholds(sf, t);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t codes = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint32_t b = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
-        const uint32_t c = e2m1_rne_fma(bf16_bits_to_float(b & 0x7FFFu), gscale, t);
-        const uint32_t mag = sf == 0.0f ? 0u : c;   // s == 0: signed zeros
+        const uint32_t cd = e2m1_rne_fma(bf16_bits_to_float(b & 0x7FFFu), gscale, t);
+        const uint32_t mag = sf == 0.0f ? 0u : cd;   // s == 0: signed zeros
         codes |= (mag | ((b >> 15) << 3)) << (4 * i);
     }
     return codes;
@@ -218,10 +259,13 @@ __device__ __forceinline__ uint32_t bf16_nearest_quotient(float p, float g, floa
     return r < 0x7F80u ? r : 0x7F80u;
 }
 
-// NVFP4: the dequantized value e2m1 * s / g is rounded once to bf16 by
-// bf16_nearest_quotient; e2m1 * s comes from the codes through the hardware
-// decoder (scale 1) and one multiply, both exact.  Same mapping as
-// nv_quantize_kernel; the quotient's form is chosen once per launch.
+// NVFP4: the dequantized value p / g, p = e2m1 * s, is rounded once to
+// bf16; p comes from the codes through the hardware decoder (scale 1) and
+// one multiply, both exact.  Where p (1/g) (1 - 2^-21) and p (1/g) (1 +
+// 2^-21) are normal and round to the same bf16 (hardware RNE), that is the
+// rounding of p / g, by the bracket argument of nv_encode8; otherwise
+// bf16_nearest_quotient decides.  Same mapping as nv_quantize_kernel; the
+// quotient's form is chosen once per launch.
 template <bool DIV>
 __device__ __forceinline__ void nv_fake_quant_body(const uint4* __restrict__ x, int64_t total, float gscale,
                                                    uint4* __restrict__ y)
@@ -229,6 +273,7 @@ __device__ __forceinline__ void nv_fake_quant_body(const uint4* __restrict__ x, 
     const int lane = threadIdx.x & 63;
     const int64_t wave_base = ((int64_t)blockIdx.x * (QUANT_THREADS / 64) + (threadIdx.x >> 6)) * ELEMS_PER_WAVE;
     const float ginv = DIV ? 0.0f : 1.0f / gscale;
+    const float g_lo = ginv * (1.0f - 0x1p-21f), g_hi = ginv * (1.0f + 0x1p-21f);
     uint4 v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -251,12 +296,17 @@ __device__ __forceinline__ void nv_fake_quant_body(const uint4* __restrict__ x, 
             f[4] = f2[0]; f[5] = f2[1]; f[6] = f3[0]; f[7] = f3[1];
         }
         const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        // the bracket of nv_encode8 once more: bf16 RNE of p (1/g) (1 -+ 2^-21)
+        // where both are normal (the smallest nonzero p is s / 2) and agree
+        const bool qfast = !DIV && sf * 0.5f * g_lo >= 0x1p-125f;
         uint32_t o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = bf16_nearest_quotient<DIV>(__builtin_fabsf(f[2 * i]) * sf, gscale, ginv);
-            const uint32_t hi = bf16_nearest_quotient<DIV>(__builtin_fabsf(f[2 * i + 1]) * sf, gscale, ginv);
-            o[i] = (lo | (hi << 16)) | (w[i] & 0x80008000u);   // the input's signs are the codes' signs
+            const float p0 = __builtin_fabsf(f[2 * i]) * sf, p1 = __builtin_fabsf(f[2 * i + 1]) * sf;
+            uint32_t r = bf16x2_rne(p0 * g_lo, p1 * g_lo);
+            if (!(qfast && r == bf16x2_rne(p0 * g_hi, p1 * g_hi)))
+                r = bf16_nearest_quotient<DIV>(p0, gscale, ginv) | (bf16_nearest_quotient<DIV>(p1, gscale, ginv) << 16);
+            o[i] = r | (w[i] & 0x80008000u);   // the input's signs are the codes' signs
         }
         if (gi * 8 < total) st_nt(&y[gi], make_uint4(o[0], o[1], o[2], o[3]));
     }

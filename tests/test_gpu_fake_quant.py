@@ -101,6 +101,10 @@ def test_nvfp4_global_scales_and_traps():
     assert_bits(gpu_fake(ragged, "nvfp4", None, 7.0), oracle.fake_quant("nvfp4", None, ragged, 7.0), "ragged")
     e = edge_rows(1040)
     assert_bits(gpu_fake(e, "nvfp4", None, 0.5), oracle.fake_quant("nvfp4", None, e, 0.5), "edges")
+    for g in (1.0, 0.5, 64.0, 2.0 ** -30):
+        tb = W.nvfp4_tie_bf16(64, 1024, g, seed=13)
+        say(f"fake nvfp4 ties g={g}")
+        assert_bits(gpu_fake(tb, "nvfp4", None, g), oracle.fake_quant("nvfp4", None, tb, g), f"nvfp4 ties g={g}")
 
 
 def test_nvfp4_workload():

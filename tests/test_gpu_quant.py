@@ -128,6 +128,11 @@ def test_amax_and_nvfp4_quantization():
         assert_same(gpu_quant(fz, "nvfp4", "ceil", g=g), oracle.nv_quantize(fz, g), f"nvfp4 g={g}")
     ragged = W.normal_bf16(3, 48, 2.0, 6)
     assert_same(gpu_quant(ragged, "nvfp4", "ceil", g=7.0), oracle.nv_quantize(ragged, 7.0), "ragged")
+    # elements on the E2M1 midpoints of exact E4M3 block scales and one bf16
+    # step either side (the encoder's fallback decides these)
+    for g in (1.0, 0.5, 64.0, 2.0 ** -30):
+        tb = W.nvfp4_tie_bf16(64, 1024, g, seed=12)
+        assert_same(gpu_quant(tb, "nvfp4", "ceil", g=g), oracle.nv_quantize(tb, g), f"nvfp4 ties g={g}")
 
 
 def test_deterministic():

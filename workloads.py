@@ -161,6 +161,34 @@ _AMAX_MANTISSAS = np.array([1.0, 1.0078125, 1.4921875, 1.5, 1.5078125, 1.7421875
                             1.9296875, 1.9375, 1.9453125, 1.9921875])
 
 
+def nvfp4_tie_bf16(rows: int, k: int, g: float, seed: int = 11) -> np.ndarray:
+    """NVFP4 blocks (16 along k) on the E2M1 rounding midpoints of a known
+    E4M3 block scale, for a power-of-two global scale g.
+
+    Each block draws a positive E4M3 value s (subnormals included); its max
+    element is 6 s / g, so the block scale is s exactly, and the other 15 are
+    lattice points or midpoints of E2M1 times s / g, each with a random sign,
+    a third of them then moved one bf16 step up or down.  Every value is
+    exact in bf16.
+    """
+    assert k % 16 == 0 and g > 0 and np.frexp(g)[0] == 0.5, "k % 16 == 0, g a power of two"
+    rng = np.random.default_rng(seed)
+    nblk = rows * k // 16
+    mags = np.array([m * 2.0 ** -9 for m in range(1, 8)] +
+                    [(1 + m / 8) * 2.0 ** (ef - 7) for ef in range(1, 16) for m in range(8) if (ef, m) != (15, 7)])
+    s = mags[rng.integers(0, len(mags), nblk)][:, None] / g
+    sign = np.where(rng.random((nblk, 16)) < 0.5, -1.0, 1.0)
+    out = _E2M1_POINTS[rng.integers(0, len(_E2M1_POINTS), (nblk, 16))] * s * sign
+    out[:, 0] = 6.0 * s[:, 0] * sign[:, 0]
+    b = _to_bf16_bits(out.astype(np.float32)).reshape(nblk, 16).astype(np.int32)
+    bump = rng.random((nblk, 16)) < 1 / 3
+    bump[:, 0] = False
+    step = np.where(rng.random((nblk, 16)) < 0.5, 1, -1).astype(np.int32)
+    mag = b & 0x7FFF
+    b = np.where(bump & (mag != 0), (b & 0x8000) | np.clip(mag + step, 0, 0x7F7F), b)
+    return b.astype(np.uint16).reshape(rows, k)
+
+
 def fuzz_bf16(rows: int, k: int, seed: int = 7, emin: int = -135, emax: int = 120,
               mix: tuple[int, int] = (-60, 60)) -> np.ndarray:
     """Adversarial bf16 blocks (32 along k) for quantizer fuzzing.
