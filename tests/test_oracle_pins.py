@@ -384,6 +384,29 @@ def test_nv_quantize_bruteforce():
                     assert ((int(q[r, j // 2]) >> (4 * (j % 2))) & 0xF) == codes[i], (g, r, b, i)
 
 
+def test_nv_quantize_ties_bruteforce():
+    # blocks whose elements sit on the E2M1 rounding midpoints of an exact
+    # E4M3 block scale (and one bf16 step either side): the brute-force block
+    # rule decides every tie, and the inputs do hold ties
+    import workloads as W
+    mids = {F(1, 4), F(3, 4), F(5, 4), F(7, 4), F(5, 2), F(7, 2), F(5)}
+    for g in (1.0, 0.5, 64.0):
+        xb = W.nvfp4_tie_bf16(3, 64, g, seed=21)
+        vals = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).double().numpy()
+        q, s = oracle.nv_quantize(xb, np.float32(g))
+        ties = 0
+        for r in range(3):
+            for b in range(4):
+                blk = list(vals[r, b * 16:(b + 1) * 16])
+                sc, codes = brute_nv_block(blk, np.float32(g))
+                assert int(s[r, b]) == sc and E4M3_POS[sc] == abs(F(float(blk[0]))) * F(g) / 6, (g, r, b)
+                ties += sum(abs(F(float(v))) * F(g) / E4M3_POS[sc] in mids for v in blk)
+                for i in range(16):
+                    j = b * 16 + i
+                    assert ((int(q[r, j // 2]) >> (4 * (j % 2))) & 0xF) == codes[i], (g, r, b, i)
+        assert ties >= 40, (g, ties)
+
+
 def _torch_amax(bits: np.ndarray) -> float:
     # torch decodes the bf16 patterns independently of the oracle
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
