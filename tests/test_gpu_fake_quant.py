@@ -107,6 +107,18 @@ def test_nvfp4_global_scales_and_traps():
         assert_bits(gpu_fake(tb, "nvfp4", None, g), oracle.fake_quant("nvfp4", None, tb, g), f"nvfp4 ties g={g}")
 
 
+def test_nvfp4_fake_large_fuzz():
+    # the fake quantization's bracketed bf16 rounding over 4M adversarial
+    # elements and global scales across the range
+    fz = W.fuzz_bf16(1024, 4096, seed=33)
+    rng = np.random.default_rng(6)
+    gs = [1.0, 0.37, 3.7e-3, 2.5e4, 1e-20, 1e20] + [float(v) for v in np.exp(rng.uniform(-30, 30, 4))]
+    for g in gs:
+        g = float(np.float32(g))
+        say(f"fake nvfp4 fuzz 1024x4096 g={g:.4g}")
+        assert_bits(gpu_fake(fz, "nvfp4", None, g), oracle.fake_quant("nvfp4", None, fz, g), f"nvfp4 fuzz g={g}")
+
+
 def test_nvfp4_workload():
     cfg = W.NVFP4
     a_bits = cfg.activations()

@@ -135,6 +135,22 @@ def test_amax_and_nvfp4_quantization():
         assert_same(gpu_quant(tb, "nvfp4", "ceil", g=g), oracle.nv_quantize(tb, g), f"nvfp4 ties g={g}")
 
 
+def test_nvfp4_quantization_large_fuzz():
+    # 4M adversarial elements under global scales across the whole range,
+    # plus normal data under its own scale: every code and scale bit for bit
+    # (the encoder's fast roundings and its exact fallback alike)
+    fz = W.fuzz_bf16(1024, 4096, seed=31)
+    rng = np.random.default_rng(5)
+    gs = [1.0, 0.37, 3.7e-3, 2.5e4, 1e-20, 1e20] + [float(v) for v in np.exp(rng.uniform(-30, 30, 4))]
+    for g in gs:
+        g = float(np.float32(g))
+        say(f"nvfp4 quant fuzz 1024x4096 g={g:.4g}")
+        assert_same(gpu_quant(fz, "nvfp4", "ceil", g=g), oracle.nv_quantize(fz, g), f"nvfp4 fuzz g={g}")
+    nb = W.normal_bf16(1024, 4096, 1.0, 32)
+    g = float(oracle.nv_global_scale(oracle.bf16_amax(nb)))
+    assert_same(gpu_quant(nb, "nvfp4", "ceil", g=g), oracle.nv_quantize(nb, g), "nvfp4 normal")
+
+
 def test_deterministic():
     bits = W.fuzz_bf16(64, 2048, seed=3)
     a = gpu_quant(bits, "mxfp4", "ceil")
