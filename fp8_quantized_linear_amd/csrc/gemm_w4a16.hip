@@ -58,6 +58,15 @@ __device__ __forceinline__ float w4_e4m3_to_f32(uint32_t c)
     return (c & 0x80u) ? -v : v;
 }
 
+// The two E4M3 codes in bits 0-15 of c as fp32 values, by the hardware
+// conversion at scale 1 (exact).  The stream kernel uses it (NVFP4 M = 1:
+// 16.2 -> 14.9 us at K = 5120, N = 17408); in the whole-row kernel the bit
+// form above measured 1.5% faster.
+__device__ __forceinline__ float2_t w4_e4m3x2_to_f32(uint32_t c)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, false);
+}
+
 // 8 E2M1 codes (a dword, element 2j in the low nibble of byte j) dequantized
 // to 8 bf16: NVFP4 with the E4M3 scale s, MXFP4 with the exponent e
 template <bool NV>
@@ -326,9 +335,9 @@ __global__ __launch_bounds__(256) void w4a16_decode_stream_kernel(W4a16Args p)
             float s_lo = 1.0f, s_hi = 1.0f;
             int e = 0;
             if (NV) {
-                const uint32_t sp = w4_lds_u32(srow + (uint32_t)(2 * un) & ~3u) >> (8 * ((2 * un) & 3));
-                s_lo = w4_e4m3_to_f32(sp & 0xFFu);
-                s_hi = w4_e4m3_to_f32((sp >> 8) & 0xFFu);
+                const float2_t sp = w4_e4m3x2_to_f32(w4_lds_u32(srow + (uint32_t)(2 * un) & ~3u) >> (8 * ((2 * un) & 3)));
+                s_lo = sp[0];
+                s_hi = sp[1];
             } else {
                 e = (int)((w4_lds_u32(srow + (uint32_t)un & ~3u) >> (8 * (un & 3))) & 0xFFu) - 127;
             }
