@@ -602,13 +602,15 @@ extern "C" hipError_t mxl_launch_splitk_reduce(const float* part, int splits, in
                                                int out_f32, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode
-// Decode-shaped exact MXFP8 and NVFP4 GEMMs (M <= 16, K % 1024 == 0, K <=
-// 8192): a stream over W, built like the MXFP4 decode kernel
-// (mx_decode_stream_kernel): one workgroup of 4 waves owns 16 W rows, wave w
-// a contiguous quarter of K.  W is consumed in chunks of 128 code bytes per
-// row (one stage of 128 K for MXFP8, two for NVFP4):
+// Decode-shaped exact MXFP8 and NVFP4 GEMMs (16 rows of A per launch, at
+// most two launches; K % 1024 == 0, K <= 8192): a stream over W, built like
+// the MXFP4 decode kernel (mx_decode_stream_kernel): one workgroup of 4 waves
+// owns 16 W rows, wave w a contiguous quarter of K.  W is consumed in chunks
+// of 128 code bytes per row (one stage of 128 K for MXFP8, two for NVFP4):
 //  * Each wave copies its own chunks, rows 8 h .. 8 h + 7 x 128 bytes per
-//    copy (8 full cache lines, non-temporal: W is read once), through a ring
+//    copy (8 full cache lines; non-temporal (NT) in the last launch, which
+//    reads W for the last time, and with the default policy in a first of
+//    two, whose W the second partly finds in the last-level cache), through a ring
 //    of 3 chunk slots in its own LDS region, and computes each chunk once
 //    its two copies have landed (exact vmcnt); the slot is refilled when its
 //    LDS reads have returned.  Inside a copy, row q's 16-byte chunk L sits at
