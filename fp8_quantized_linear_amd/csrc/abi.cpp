@@ -40,7 +40,7 @@ const char* mxl_mx_mixed_exact_config_name(void);
 int mxl_mx8_tile_ok(int64_t m, int64_t n, int64_t k);
 size_t mxl_dq_workspace(int64_t m, int64_t n, int64_t k);
 int mxl_dq_splits(int64_t m, int64_t n, int64_t k);
-int mxl_dq_decode_ok(int nv, int64_t m, int64_t k);
+int mxl_dq_decode_ok(int nv, int64_t m, int64_t n, int64_t k);
 hipError_t mxl_launch_mx_gemm_fused(int a_bits, int a_rule, const void* a_bf16, int w_bits,
                                     const void* wq, const void* ws, int64_t m, int64_t n, int64_t k,
                                     void* y, int out_f32, void* dump_q, void* dump_s, void* work,
@@ -181,7 +181,7 @@ size_t gemm_workspace_need(mx_format a, mx_format w, int64_t m, int64_t n, int64
 {
     const MxPath path = mx_path(a, w, flags);
     if (path == PATH_SCALED) return mxl_mx_gemm_workspace(bits_of(a), bits_of(w), m, n, k);
-    if (path == PATH_EXACT8 && mxl_dq_decode_ok(0, m, k)) return 0;   // the decode kernel does not split
+    if (path == PATH_EXACT8 && mxl_dq_decode_ok(0, m, n, k)) return 0;   // the decode kernel does not split
     return mxl_dq_workspace(m, n, k);
 }
 
@@ -419,7 +419,7 @@ mx_status nv_gemm(const void* a_q, const void* a_s, const void* w_q, const void*
     if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y) ||
         (workspace && !aligned16(workspace)))
         return MX_ERR_ALIGN;
-    const size_t need = mxl_dq_decode_ok(1, m, k) ? 0 : mxl_dq_workspace(m, n, k);
+    const size_t need = mxl_dq_decode_ok(1, m, n, k) ? 0 : mxl_dq_workspace(m, n, k);
     if (workspace && need > 0 && ws_bytes < need) return MX_ERR_WORKSPACE;
     if ((st = check_device()) != MX_OK) return st;
     return from_hip(mxl_launch_nv_gemm(a_q, a_s, w_q, w_s, m, n, k, alpha, y, (flags & MX_OUT_F32) ? 1 : 0,
@@ -459,7 +459,7 @@ mx_status mx_gemm_workspace_size(mx_format a_fmt, mx_format w_fmt, int64_t m, in
     if (nv != (w_fmt == MX_FMT_NVFP4)) return MX_ERR_INVALID_ARG;
     mx_status st = check_gemm_shape(m, n, k, nv ? 16 : 32);
     if (st != MX_OK) return st;
-    *bytes = nv ? (mxl_dq_decode_ok(1, m, k) ? 0 : mxl_dq_workspace(m, n, k))
+    *bytes = nv ? (mxl_dq_decode_ok(1, m, n, k) ? 0 : mxl_dq_workspace(m, n, k))
                 : gemm_workspace_need(a_fmt, w_fmt, m, n, k, flags);
     return MX_OK;
 }
@@ -606,7 +606,7 @@ mx_status mx_gemm_plan(mx_format a_fmt, mx_format w_fmt, int64_t m, int64_t n, i
                     : path == PATH_MIXED_EXACT ? mxl_mx_mixed_exact_config_name()
                                                : mxl_mx_gemm_config_name(bits_of(a_fmt), bits_of(w_fmt), m, n, k,
                                                                          fused && a_fmt == w_fmt && !via_q);
-    const bool dq_decode = (nv || path == PATH_EXACT8) && mxl_dq_decode_ok(nv ? 1 : 0, m, k);
+    const bool dq_decode = (nv || path == PATH_EXACT8) && mxl_dq_decode_ok(nv ? 1 : 0, m, n, k);
     const int splits = (nv || path != PATH_SCALED) && !fused && !dq_decode ? mxl_dq_splits(m, n, k) : 1;
     const char* pre = !fused || nv ? ""
                       : !via_q ? "fused-quant "

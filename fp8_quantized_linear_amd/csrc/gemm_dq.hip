@@ -829,10 +829,13 @@ static size_t dq_decode_lds_bytes(int kind, int64_t k)
 }
 
 // whether dq_decode_stream_kernel serves this shape (kind: DQ_NVFP4 or DQ_MXFP8):
-// one launch per 16 rows of A, at most two
-static bool dq_decode_ok(int kind, int64_t m, int64_t k)
+// one launch per 16 rows of A, at most two; W's bytes within the 32-bit
+// buffer ranges and offsets the kernel uses
+static bool dq_decode_ok(int kind, int64_t m, int64_t n, int64_t k)
 {
-    return m <= 32 && k % 1024 == 0 && k >= 1024 && k <= 8192 && dq_decode_lds_bytes(kind, k) <= 65536;
+    const int64_t rowb = kind == DQ_NVFP4 ? k / 2 : k;
+    return m <= 32 && k % 1024 == 0 && k >= 1024 && k <= 8192 && dq_decode_lds_bytes(kind, k) <= 65536 &&
+           (n + 16) * rowb < ((int64_t)1 << 31);
 }
 
 template <int KIND, int QC, bool OUT_F32>
@@ -886,7 +889,21 @@ static hipError_t launch_dq_decode(const DqArgs& a0, hipStream_t stream)
     return hipSuccess;
 }
 
-extern "C" int mxl_dq_decode_ok(int nv, int64_t m, int64_t k) { return dq_decode_ok(nv ? DQ_NVFP4 : DQ_MXFP8, m, k) ? 1 : 0; }
+// The decode kernel goes before the tile kernels (a wide N with few rows of A
+// is a stream over W), except for MXFP8 above 16 rows: its two launches read
+// W twice, which at N = 151936, K = 5120 (778 MB, beyond the last-level
+// cache) took 337 us against 258 us for the tile kernel at M = 32, while at
+// M = 1 and 8 the decode kernel took 118 and 143 us against 276 and 271.
+// NVFP4 (389 MB) gains at every M up to 32: 76 / 90 / 230 us against 279.
+static bool dq8_decode_first(int64_t m, int64_t n, int64_t k)
+{
+    return m <= 16 && dq_decode_ok(DQ_MXFP8, m, n, k);
+}
+
+extern "C" int mxl_dq_decode_ok(int nv, int64_t m, int64_t n, int64_t k)
+{
+    return dq_decode_ok(nv ? DQ_NVFP4 : DQ_MXFP8, m, n, k) ? 1 : 0;
+}
 
 // Split-K plan of the 128 x 128 dequantizing kernel: at least 8 stages of 64
 // per split and an even stage count; two splits up to 192 tiles (M = 32 to
@@ -944,13 +961,13 @@ extern "C" hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const v
                                          int64_t m, int64_t n, int64_t k, float alpha, void* y,
                                          int out_f32, void* work, size_t work_bytes, hipStream_t stream)
 {
-    if (mxl_dq8w_ok(DQ8W_FMT_NVFP4, m, n, k))
-        return mxl_launch_dq8w(DQ8W_FMT_NVFP4, aq, as, wq, ws, m, n, k, alpha, y, out_f32, stream);
     DqArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
              static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
              (int)m, (int)n, (int)k, alpha};
-    if (dq_decode_ok(DQ_NVFP4, m, k))
+    if (dq_decode_ok(DQ_NVFP4, m, n, k))   // before the tile kernel: a wide N with few rows is a W stream
         return out_f32 ? launch_dq_decode<DQ_NVFP4, true>(a, stream) : launch_dq_decode<DQ_NVFP4, false>(a, stream);
+    if (mxl_dq8w_ok(DQ8W_FMT_NVFP4, m, n, k))
+        return mxl_launch_dq8w(DQ8W_FMT_NVFP4, aq, as, wq, ws, m, n, k, alpha, y, out_f32, stream);
     return dq_run(a, out_f32, work, work_bytes, stream, [&](const DqArgs& x, int f32) {
         if (f32) return launch_dq<DQ_NVFP4, 128, 128, 2, 2, true>(x, stream);
         return launch_dq<DQ_NVFP4, 128, 128, 2, 2, false>(x, stream);
@@ -966,11 +983,13 @@ extern "C" hipError_t mxl_launch_mxfp8_exact_gemm(const void* aq, const void* as
                                                   const void* ws, int64_t m, int64_t n, int64_t k, void* y,
                                                   int out_f32, void* work, size_t work_bytes, hipStream_t stream)
 {
-    if (mxl_mx8_tile_ok(m, n, k)) return mxl_launch_mx8_tile(aq, as, wq, ws, m, n, k, y, out_f32, stream);
     DqArgs a{static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
              static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws), y,
              (int)m, (int)n, (int)k, 1.0f};
-    if (dq_decode_ok(DQ_MXFP8, m, k))
+    if (dq8_decode_first(m, n, k))
+        return out_f32 ? launch_dq_decode<DQ_MXFP8, true>(a, stream) : launch_dq_decode<DQ_MXFP8, false>(a, stream);
+    if (mxl_mx8_tile_ok(m, n, k)) return mxl_launch_mx8_tile(aq, as, wq, ws, m, n, k, y, out_f32, stream);
+    if (dq_decode_ok(DQ_MXFP8, m, n, k))
         return out_f32 ? launch_dq_decode<DQ_MXFP8, true>(a, stream) : launch_dq_decode<DQ_MXFP8, false>(a, stream);
     return dq_run(a, out_f32, work, work_bytes, stream, [&](const DqArgs& x, int f32) {
         if (f32) return launch_dq<DQ_MXFP8, 128, 128, 2, 2, true>(x, stream);
@@ -1109,20 +1128,20 @@ extern "C" const char* mxl_w4a16_gemm_config_name(void)
 
 extern "C" const char* mxl_nv_gemm_config_name(int64_t m, int64_t n, int64_t k)
 {
-    if (mxl_dq8w_ok(DQ8W_FMT_NVFP4, m, n, k)) return mxl_dq8w_config_name();
-    if (dq_decode_ok(DQ_NVFP4, m, k))
+    if (dq_decode_ok(DQ_NVFP4, m, n, k))
         return "dq_decode_stream_kernel<nvfp4 -> exact f16, 16 W rows per workgroup, each wave streams its own K quarter "
-               "through a ring of 3 LDS chunk slots (8 rows x 128 B non-temporal copies), f16 mfma 16x16x32>, one launch per "
+               "through a ring of 3 LDS chunk slots (8 rows x 128 B copies), f16 mfma 16x16x32>, one launch per "
                "16 rows of A";
+    if (mxl_dq8w_ok(DQ8W_FMT_NVFP4, m, n, k)) return mxl_dq8w_config_name();
     return "dq_gemm_kernel<nvfp4 -> exact f16, tile 128x128x64, 2x2 waves of 64x64, f16 mfma 32x32x16>";
 }
 
 extern "C" const char* mxl_mxfp8_exact_config_name(int64_t m, int64_t n, int64_t k)
 {
-    if (mxl_mx8_tile_ok(m, n, k)) return mxl_mx8_tile_config_name();
-    if (dq_decode_ok(DQ_MXFP8, m, k))
+    if (dq8_decode_first(m, n, k) || (!mxl_mx8_tile_ok(m, n, k) && dq_decode_ok(DQ_MXFP8, m, n, k)))
         return "dq_decode_stream_kernel<mxfp8 -> exact bf16, 16 W rows per workgroup, each wave streams its own K "
-               "quarter through a ring of 3 LDS chunk slots (8 rows x 128 B non-temporal copies), bf16 mfma "
+               "quarter through a ring of 3 LDS chunk slots (8 rows x 128 B copies), bf16 mfma "
                "16x16x32>, one launch per 16 rows of A";
+    if (mxl_mx8_tile_ok(m, n, k)) return mxl_mx8_tile_config_name();
     return "dq_gemm_kernel<mxfp8 -> exact bf16, tile 128x128x64, 2x2 waves of 64x64, bf16 mfma 32x32x16>";
 }

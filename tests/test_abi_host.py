@@ -368,6 +368,14 @@ def test_plan_names_the_kernel():
     assert "mx_decode_kernel" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 8, 17408, 2560)
     assert "dq_gemm_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 17, 17408, 5120)
     assert "dq_gemm_kernel" in mxl.mx_gemm_w4a16_plan("nvfp4", 1, 512, 400)
+    # decode shapes with a vocabulary-sized N stream W before the tile kernels
+    # are considered (MXFP8 up to 16 rows, NVFP4 up to 32), and W beyond the
+    # decode kernel's 32-bit offsets goes to the tile kernels
+    for fmt, m in (("mxfp8", 1), ("mxfp8", 16), ("nvfp4", 1), ("nvfp4", 32)):
+        assert "dq_decode_stream_kernel" in mxl.mx_gemm_plan(fmt, fmt, m, 151936, 5120), (fmt, m)
+    assert "mx8_gemm_tile_kernel" in mxl.mx_gemm_plan("mxfp8", "mxfp8", 17, 151936, 5120)
+    assert "dq_decode_stream_kernel" not in mxl.mx_gemm_plan("mxfp8", "mxfp8", 1, 300000, 8192)
+    assert "dq_decode_stream_kernel" not in mxl.mx_gemm_plan("nvfp4", "nvfp4", 1, 600000, 8192)
 
 
 def test_plan_names_fit_their_buffers():

@@ -752,7 +752,8 @@ def test_fused_prologue_codes_dumped(fmt, fast, m, k, n):
 # scales reach 2^-127 (MXFP8) or the subnormal E4M3 scales (NVFP4); bf16 and
 # fp32 output.
 DQ_DECODE_CASES = [(1, 1024, 300), (3, 5120, 200), (8, 5120, 17), (16, 8192, 130), (16, 2048, 1),
-                   (17, 5120, 130), (32, 2048, 300), (29, 8192, 33)]   # above 16 rows: two launches
+                   (17, 5120, 130), (32, 2048, 300), (29, 8192, 33),   # above 16 rows: two launches
+                   (2, 1024, 65600)]   # wide enough for the tile kernels, which the decode kernel precedes
 
 
 @pytest.mark.parametrize("data", ["normal", "fuzz"])
