@@ -957,6 +957,15 @@ extern "C" hipError_t mxl_launch_dq8w(int fmt, const void* aq, const void* as, c
 extern "C" const char* mxl_dq8w_config_name(void);
 constexpr int DQ8W_FMT_NVFP4 = 2;
 
+// The 8-wave NVFP4 tile kernel above 128 rows of A: below that the 128 x 128
+// kernel is faster even where N alone fills the tile count (N = 151936, K =
+// 5120: M = 64 / 128 take 276 / 300 us there against 326 / 330 us in the
+// tile kernel; M = 256: 574 against 361).
+static bool nv_tile_ok(int64_t m, int64_t n, int64_t k)
+{
+    return m > 128 && mxl_dq8w_ok(DQ8W_FMT_NVFP4, m, n, k);
+}
+
 extern "C" hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const void* wq, const void* ws,
                                          int64_t m, int64_t n, int64_t k, float alpha, void* y,
                                          int out_f32, void* work, size_t work_bytes, hipStream_t stream)
@@ -966,7 +975,7 @@ extern "C" hipError_t mxl_launch_nv_gemm(const void* aq, const void* as, const v
              (int)m, (int)n, (int)k, alpha};
     if (dq_decode_ok(DQ_NVFP4, m, n, k))   // before the tile kernel: a wide N with few rows is a W stream
         return out_f32 ? launch_dq_decode<DQ_NVFP4, true>(a, stream) : launch_dq_decode<DQ_NVFP4, false>(a, stream);
-    if (mxl_dq8w_ok(DQ8W_FMT_NVFP4, m, n, k))
+    if (nv_tile_ok(m, n, k))
         return mxl_launch_dq8w(DQ8W_FMT_NVFP4, aq, as, wq, ws, m, n, k, alpha, y, out_f32, stream);
     return dq_run(a, out_f32, work, work_bytes, stream, [&](const DqArgs& x, int f32) {
         if (f32) return launch_dq<DQ_NVFP4, 128, 128, 2, 2, true>(x, stream);
@@ -1132,7 +1141,7 @@ extern "C" const char* mxl_nv_gemm_config_name(int64_t m, int64_t n, int64_t k)
         return "dq_decode_stream_kernel<nvfp4 -> exact f16, 16 W rows per workgroup, each wave streams its own K quarter "
                "through a ring of 3 LDS chunk slots (8 rows x 128 B copies), f16 mfma 16x16x32>, one launch per "
                "16 rows of A";
-    if (mxl_dq8w_ok(DQ8W_FMT_NVFP4, m, n, k)) return mxl_dq8w_config_name();
+    if (nv_tile_ok(m, n, k)) return mxl_dq8w_config_name();
     return "dq_gemm_kernel<nvfp4 -> exact f16, tile 128x128x64, 2x2 waves of 64x64, f16 mfma 32x32x16>";
 }
 
