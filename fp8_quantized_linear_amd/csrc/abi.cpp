@@ -233,7 +233,9 @@ size_t fused_workspace_need(mx_format a, mx_format w, int64_t m, int64_t n, int6
 // fits LDS and W's bytes stay within 32-bit buffer offsets
 bool w4a16_use_decode(bool nv, int64_t m, int64_t n, int64_t k)
 {
-    return mxl_w4a16_decode_ok(nv ? 1 : 0, m, k) && (n + 16) * (k / 2) < ((int64_t)1 << 31);
+    // the decode kernels form 32-bit W offsets up to the last row of their
+    // last workgroup (32 rows)
+    return mxl_w4a16_decode_ok(nv ? 1 : 0, m, k) && (n + 32) * (k / 2) < ((int64_t)1 << 31);
 }
 
 } // namespace

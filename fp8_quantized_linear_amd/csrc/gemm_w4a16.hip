@@ -374,6 +374,229 @@ __global__ __launch_bounds__(256) void w4a16_decode_stream_kernel(W4a16Args p)
     }
 }
 
+// The same product for M <= 16 rows of A (K % 1024 == 0, QS = K / 512
+// stages of 128 per wave) where A does not fit in LDS beside W (above two
+// rows, or NVFP4 scales at two rows and K = 5120).  The whole-row kernel
+// reads A's full K extent (M x 2K bytes of bf16) from the L2 for every 16
+// rows of W, twice the W bytes at M = 8.  Here a workgroup owns two 16-row
+// groups of W, so each A fragment serves both, and every wave streams its
+// own K quarter of the 32 rows through a ring of RS pair slots, as the W4A4
+// decode kernel does above 16 rows of A.
+//  * Copy (c, h), h = 0 .. 3, moves rows 8 h .. 8 h + 7 of the 32 x bytes
+//    [128 c, 128 c + 128) of the wave's quarter (8 cache lines, 1 KiB) into
+//    slot c % RS, with the chunk swizzle of w4a16_decode_stream_kernel.
+//  * A comes straight from global memory into a register ring of APR stage
+//    pairs (4 x 16 bytes per lane and stage); rows past M read as zero
+//    through the buffer range check.  The A loads of pair c + APR go out
+//    once pair c has been computed, followed by the W copies of pair c + RS,
+//    and the wait before pair c counts exactly the loads and copies issued
+//    after both of its own.
+//  * Lane (r, g) of stage s holds, for each group rg, W row 16 rg + r, K
+//    elements [128 st + 32 g, +32), and A row r, K [128 st + 32 g + 8 j,
+//    +8) for MFMA step j: the K assignment, step order and wave order of
+//    the whole-row kernel, so the results are bitwise the same.
+constexpr int w16_min(int a, int b) { return a < b ? a : b; }
+// VMEM operations a wave has issued (after its scale copies) before it
+// computes pair c: the prologue's A pairs (8 loads each) and W pairs (4
+// copies each), then per computed pair i the A loads of pair i + APR and the
+// W copies of pair i + RSB
+constexpr int w16_issued(int c, int nc, int apr, int rsb)
+{
+    int n = 8 * w16_min(apr, nc) + 4 * w16_min(rsb, nc);
+    for (int i = 0; i < c; ++i) n += (i + apr < nc ? 8 : 0) + (i + rsb < nc ? 4 : 0);
+    return n;
+}
+// operations issued after the later of pair c's A loads and W copies, at
+// the point where pair c is computed: the vmcnt that waits for both
+constexpr int w16_wait(int c, int nc, int apr, int rsb)
+{
+    const int end_a = c < apr ? 8 * (c + 1) : w16_issued(c - apr, nc, apr, rsb) + 8;
+    const int end_w = c < rsb ? 8 * w16_min(apr, nc) + 4 * (c + 1)
+                              : w16_issued(c - rsb, nc, apr, rsb) + (c - rsb + apr < nc ? 8 : 0) + 4;
+    return w16_issued(c, nc, apr, rsb) - (end_a > end_w ? end_a : end_w);
+}
+// s_waitcnt vmcnt(n) for an n that folds to a constant once loops are
+// unrolled (n <= 23)
+__device__ __forceinline__ void w16_wait_vmcnt(int n)
+{
+    switch (n) {
+    case 0: wait_vmcnt<0>(); break;   case 1: wait_vmcnt<1>(); break;   case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;   case 4: wait_vmcnt<4>(); break;   case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;   case 7: wait_vmcnt<7>(); break;   case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;   case 10: wait_vmcnt<10>(); break; case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break; case 13: wait_vmcnt<13>(); break; case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break; case 16: wait_vmcnt<16>(); break; case 17: wait_vmcnt<17>(); break;
+    case 18: wait_vmcnt<18>(); break; case 19: wait_vmcnt<19>(); break; case 20: wait_vmcnt<20>(); break;
+    case 21: wait_vmcnt<21>(); break; case 22: wait_vmcnt<22>(); break; case 23: wait_vmcnt<23>(); break;
+    default: wait_vmcnt<0>(); break;
+    }
+}
+
+template <bool NV, int QS, int RS, bool OUT_F32>
+__global__ __launch_bounds__(256) void w4a16_decode_stream2_kernel(W4a16Args p)
+{
+    constexpr int WAVES = 4, RG = 2, NC = QS / 2, RSB = w16_min(RS, NC), APR = w16_min(2, NC);
+    constexpr int SLOT = RG * 2048;   // a pair slot: 32 rows x 128 B per wave
+    constexpr int K = QS * 512, row_bytes = K / 2, KS = K / (NV ? 16 : 32), QB = row_bytes / WAVES;
+    static_assert(QS % 2 == 0 && QS <= 16, "stream2 shape");
+    extern __shared__ __align__(16) uint8_t dsm[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16 * RG;
+    const int st0 = wave * QS;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dsm);
+    const uint32_t lds_w = lds0 + (uint32_t)(wave * RSB * SLOT);   // this wave's ring
+    const uint32_t s_lds = lds0 + (uint32_t)(WAVES * RSB * SLOT);  // W scales [32][KS]
+
+    // 1. the W scale block of the 32 rows, 256 bytes per copy, spread over the waves
+    constexpr int SCOP = 16 * RG * KS / 256;
+    {
+        const int4_t rws = make_rsrc(p.w_s, (uint32_t)p.N * KS);
+#pragma unroll
+        for (int j = 0; j < SCOP; ++j)
+            if (j % WAVES == wave) dma_b32(s_lds + j * 256, n0 * KS + j * 256 + lane * 4, rws, 0);
+    }
+    // 2. A fragments of the first APR pairs
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.a, (short)0, p.M * K * 2, 0x00020000);
+    const int a_off = r * K * 2 + g * 64;
+    bf16x8_w af[APR][2][4];
+    auto load_a = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                af[c % APR][hf][j] = __builtin_bit_cast(
+                    bf16x8_w, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + j * 16, (st0 + 2 * c + hf) * 256, 0));
+    };
+#pragma unroll
+    for (int c = 0; c < APR; ++c) load_a(c);
+    // 3. the W copies of the first RSB pairs
+    const int4_t rw = make_rsrc(p.w_q, (uint32_t)p.N * row_bytes);
+    int voffh[2 * RG];
+#pragma unroll
+    for (int h = 0; h < 2 * RG; ++h) {
+        const int q = 8 * h + (lane >> 3);
+        voffh[h] = (n0 + q) * row_bytes + (((lane & 7) ^ ((q >> 1) & 7)) * 16);
+    }
+    auto copy_pair = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2 * RG; ++h)
+            w4_dma_b128_nt(lds_w + (uint32_t)((c % RSB) * SLOT + h * 1024), voffh[h], rw, wave * QB + c * 128);
+    };
+#pragma unroll
+    for (int c = 0; c < RSB; ++c) copy_pair(c);
+    // the scale copies have landed once at most the A loads and W copies
+    // issued after them are outstanding; the barrier publishes them
+    wait_vmcnt<8 * APR + 4 * RSB>();
+    lds_barrier();
+
+    f32x4_w acc[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) acc[rg] = f32x4_w{0.f, 0.f, 0.f, 0.f};
+    const uint32_t rd = lds_w + (uint32_t)((r >> 3) * 1024 + (r & 7) * 128);
+    const int rsw = (r >> 1) & 7;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        w16_wait_vmcnt(w16_wait(c, NC, APR, RSB));
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int un = 4 * (st0 + 2 * c + hf) + g;   // global 16-byte unit of the W row
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                const int4_t cw = w4_lds_v4(rd + (uint32_t)((c % RSB) * SLOT + rg * 2048 + (((4 * hf + g) ^ rsw) * 16)));
+                const uint32_t srow = s_lds + (uint32_t)((16 * rg + r) * KS);
+                float s_lo = 1.0f, s_hi = 1.0f;
+                int e = 0;
+                if (NV) {
+                    const float2_t sp = w4_e4m3x2_to_f32(w4_lds_u32(srow + (uint32_t)(2 * un) & ~3u) >> (8 * ((2 * un) & 3)));
+                    s_lo = sp[0];
+                    s_hi = sp[1];
+                } else {
+                    e = (int)((w4_lds_u32(srow + (uint32_t)un & ~3u) >> (8 * (un & 3))) & 0xFFu) - 127;
+                }
+                const uint32_t cws[4] = {(uint32_t)cw[0], (uint32_t)cw[1], (uint32_t)cw[2], (uint32_t)cw[3]};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8_w b8 = w4_dequant8<NV>(cws[j], j < 2 ? s_lo : s_hi, e);
+                    acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[c % APR][hf][j], b8, acc[rg], 0, 0, 0);
+                }
+            }
+        }
+        if (c + APR < NC) load_a(c + APR);
+        if (c + RSB < NC) {
+            // slot c % RSB is free once this pair's LDS reads have returned
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            copy_pair(c + RSB);
+        }
+    }
+    __syncthreads();   // every wave is done with its ring
+    f32x4_w* red = reinterpret_cast<f32x4_w*>(dsm);   // [WAVES][RG][64]
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) red[(wave * RG + rg) * 64 + lane] = acc[rg];
+    __syncthreads();
+    // thread e < 128 finishes accumulator lane e % 64 of group e / 64: A rows
+    // 4 (l / 16) + i, W row n0 + 16 rg + l % 16
+    if (tid < RG * 64) {
+        const int l = tid & 63, rg = tid >> 6;
+        f32x4_w v = red[rg * 64 + l];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+            const f32x4_w x = red[(w * RG + rg) * 64 + l];
+            v = f32x4_w{v[0] + x[0], v[1] + x[1], v[2] + x[2], v[3] + x[3]};
+        }
+        const int nn = n0 + 16 * rg + (l & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * (l >> 4) + i;
+            if (m < p.M && nn < p.N) {
+                const float o = v[i] * p.alpha;
+                if (OUT_F32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + nn] = o;
+                else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + nn] = f32_to_bf16_rne(o);
+            }
+        }
+    }
+}
+
+constexpr int W16_SLOTS = 2;   // ring slots (stage pairs) per wave
+
+template <bool NV>
+static size_t w4a16_stream2_lds_bytes(int64_t k)
+{
+    const int nc = (int)(k / 1024), slots = W16_SLOTS < nc ? W16_SLOTS : nc;
+    return (size_t)4 * slots * 4096 + (size_t)32 * (k / (NV ? 16 : 32));
+}
+
+// whether w4a16_decode_stream2_kernel serves this shape (the dispatch
+// prefers w4a16_decode_stream_kernel where that one fits)
+static bool w4a16_stream2_ok(int64_t m, int64_t k)
+{
+    return m >= 1 && m <= 16 && k % 1024 == 0 && k >= 1024 && k <= 8192;
+}
+
+template <bool NV, int QS, bool OUT_F32>
+static void launch_w4a16_stream2_qs(const W4a16Args& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((w4a16_decode_stream2_kernel<NV, QS, W16_SLOTS, OUT_F32>), dim3((a.N + 31) / 32), dim3(256),
+                       w4a16_stream2_lds_bytes<NV>(a.K), stream, a);
+}
+
+template <bool NV, bool OUT_F32>
+static hipError_t launch_w4a16_stream2(const W4a16Args& a, hipStream_t stream)
+{
+    switch (a.K / 512) {
+    case 2: launch_w4a16_stream2_qs<NV, 2, OUT_F32>(a, stream); break;
+    case 4: launch_w4a16_stream2_qs<NV, 4, OUT_F32>(a, stream); break;
+    case 6: launch_w4a16_stream2_qs<NV, 6, OUT_F32>(a, stream); break;
+    case 8: launch_w4a16_stream2_qs<NV, 8, OUT_F32>(a, stream); break;
+    case 10: launch_w4a16_stream2_qs<NV, 10, OUT_F32>(a, stream); break;
+    case 12: launch_w4a16_stream2_qs<NV, 12, OUT_F32>(a, stream); break;
+    case 14: launch_w4a16_stream2_qs<NV, 14, OUT_F32>(a, stream); break;
+    default: launch_w4a16_stream2_qs<NV, 16, OUT_F32>(a, stream); break;
+    }
+    return hipGetLastError();
+}
+
 template <bool NV>
 static size_t w4a16_stream_lds_bytes(int64_t m, int64_t k)
 {
@@ -422,11 +645,13 @@ static hipError_t launch_w4a16_decode(const W4a16Args& a, hipStream_t stream)
 
 using namespace mxl;
 
-// Shapes the decode kernel takes: M <= 16, K % 512 == 0, its LDS block
-// within 64 KiB (three workgroups per compute unit).
+// Shapes the decode kernels take: M <= 16, K % 512 == 0, and either one of
+// the streamed kernels (K % 1024 == 0, K <= 8192) or the whole-row kernel's
+// LDS block within 64 KiB (three workgroups per compute unit).
 extern "C" int mxl_w4a16_decode_ok(int w_nv, int64_t m, int64_t k)
 {
     if (m > 16 || k % 512 != 0 || k > 65536) return 0;
+    if (w4a16_stream_ok(w_nv, m, k) || w4a16_stream2_ok(m, k)) return 1;
     return (w_nv ? w4a16_decode_lds_bytes<true>((int)k) : w4a16_decode_lds_bytes<false>((int)k)) <= 65536 ? 1 : 0;
 }
 
@@ -440,6 +665,10 @@ extern "C" hipError_t mxl_launch_w4a16_decode(int w_nv, const void* a_bf16, cons
         if (w_nv) return out_f32 ? launch_w4a16_stream<true, true>(a, stream) : launch_w4a16_stream<true, false>(a, stream);
         return out_f32 ? launch_w4a16_stream<false, true>(a, stream) : launch_w4a16_stream<false, false>(a, stream);
     }
+    if (w4a16_stream2_ok(m, k)) {
+        if (w_nv) return out_f32 ? launch_w4a16_stream2<true, true>(a, stream) : launch_w4a16_stream2<true, false>(a, stream);
+        return out_f32 ? launch_w4a16_stream2<false, true>(a, stream) : launch_w4a16_stream2<false, false>(a, stream);
+    }
     if (w_nv) return out_f32 ? launch_w4a16_decode<true, true>(a, stream) : launch_w4a16_decode<true, false>(a, stream);
     return out_f32 ? launch_w4a16_decode<false, true>(a, stream) : launch_w4a16_decode<false, false>(a, stream);
 }
@@ -449,6 +678,10 @@ extern "C" const char* mxl_w4a16_decode_config_name(int w_nv, int64_t m, int64_t
     if (w4a16_stream_ok(w_nv, m, k))
         return "w4a16_decode_stream_kernel<16 W rows per workgroup, each wave copies its own K quarter of W and A "
                "into LDS and computes each stage as its copies land, bf16 mfma 16x16x32>";
+    if (w4a16_stream2_ok(m, k))
+        return "w4a16_decode_stream2_kernel<32 W rows per workgroup (each A fragment serves both 16-row groups), each "
+               "wave streams its own K quarter of W through a ring of 2 LDS pair slots, A from global memory one pair "
+               "ahead, bf16 mfma 16x16x32>";
     return "w4a16_decode_kernel<16 W rows per workgroup, whole-row copies into swizzled LDS, 4 waves over K "
            "quarters in groups of 128, A two groups ahead, bf16 mfma 16x16x32>";
 }

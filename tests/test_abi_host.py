@@ -363,7 +363,9 @@ def test_plan_names_the_kernel():
     assert "workspace" in mxl.mx_gemm_plan("mxfp8", "mxfp4", 4096, 5120, 5120, fused=True)
     assert "w4a16_decode_stream_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 1, 17408, 5120)
     assert "w4a16_decode_stream_kernel" in mxl.mx_gemm_w4a16_plan("nvfp4", 1, 17408, 5120)
-    assert "w4a16_decode_kernel" in mxl.mx_gemm_w4a16_plan("nvfp4", 16, 17408, 5120)
+    assert "w4a16_decode_stream2_kernel" in mxl.mx_gemm_w4a16_plan("nvfp4", 16, 17408, 5120)
+    assert "w4a16_decode_stream2_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 3, 17408, 8192)
+    assert "w4a16_decode_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 8, 17408, 2560)
     assert "mx_decode_stream_kernel" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 32, 17408, 5120)
     assert "mx_decode_kernel" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 8, 17408, 2560)
     assert "dq_gemm_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 17, 17408, 5120)

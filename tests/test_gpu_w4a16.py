@@ -53,8 +53,11 @@ def alpha_of(g):
 CASES = [
     # per-wave streamed decode kernel: M <= 2, K % 1024 == 0, LDS within 64 KiB
     (1, 1024, 300), (2, 5120, 100), (1, 6144, 33), (2, 3072, 17),
+    # two-group streamed decode kernel: M <= 16, K % 1024 == 0, K <= 8192,
+    # where the one above does not fit (M > 2; NVFP4 at (2, 5120) and (1, 6144))
+    (3, 1024, 100), (8, 2048, 33), (16, 5120, 200), (5, 8192, 70), (12, 3072, 31), (16, 1024, 32),
     # decode kernel: M <= 16, K % 512 == 0
-    (1, 512, 16), (3, 1024, 100), (16, 512, 300), (8, 2048, 33),
+    (1, 512, 16), (16, 512, 300), (9, 1536, 48),
     # general kernel
     (17, 512, 130), (130, 96, 257), (200, 416, 300), (64, 1056, 64),
 ]
@@ -69,6 +72,10 @@ def test_w4a16_full(fmt, m, k, n):
     lds = 16 * (k // 2) + m * k * 2 + 16 * (k // (16 if fmt == "nvfp4" else 32))
     if m <= 2 and k % 1024 == 0 and lds <= 65536:
         assert "w4a16_decode_stream_kernel<" in plan
+    elif m <= 16 and k % 1024 == 0 and k <= 8192:
+        assert "w4a16_decode_stream2_kernel<" in plan
+    elif m <= 16 and k % 512 == 0:
+        assert "w4a16_decode_kernel<" in plan
     a_bits = W.activations_entry_outliers(m, k)
     w_bits = W.normal_bf16(n, k, 0.02, 1)
     wq, ws, rq, rs, g = pack(w_bits, fmt)
