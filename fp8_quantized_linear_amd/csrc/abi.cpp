@@ -66,7 +66,7 @@ hipError_t mxl_launch_w4a16_decode(int w_nv, const void* a_bf16, const void* wq,
                                    int64_t n, int64_t k, float alpha, void* y, int out_f32, hipStream_t stream);
 int mxl_w4a16_decode_ok(int w_nv, int64_t m, int64_t k);
 const char* mxl_w4a16_gemm_config_name(void);
-const char* mxl_w4a16_decode_config_name(int w_nv, int64_t m, int64_t k);
+const char* mxl_w4a16_decode_config_name(int w_nv, int64_t m, int64_t n, int64_t k);
 const char* mxl_mx_gemm_config_name(int a_bits, int w_bits, int64_t m, int64_t n, int64_t k, int fused);
 const char* mxl_nv_gemm_config_name(int64_t m, int64_t n, int64_t k);
 const char* mxl_mxfp8_exact_config_name(int64_t m, int64_t n, int64_t k);
@@ -487,7 +487,7 @@ mx_status mx_gemm_w4a16_plan(mx_format w_fmt, int64_t m, int64_t n, int64_t k, c
     const bool dec = w4a16_use_decode(nv, m, n, k);
     const int splits = dec ? 1 : mxl_dq_splits(m, n, k);
     std::snprintf(name, len, "w4a16 %s %s%s", nv ? "nvfp4" : "mxfp4",
-                  dec ? mxl_w4a16_decode_config_name(nv ? 1 : 0, m, k) : mxl_w4a16_gemm_config_name(),
+                  dec ? mxl_w4a16_decode_config_name(nv ? 1 : 0, m, n, k) : mxl_w4a16_gemm_config_name(),
                   splits > 1 ? ", split-K with a workspace, else one split" : "");
     return MX_OK;
 }

@@ -935,23 +935,34 @@ __device__ __forceinline__ int4_t lds_read_v4(uint32_t addr)
     return *reinterpret_cast<const __attribute__((address_space(3))) int4_t*>((size_t)addr);
 }
 
-template <int MT, int QS, int RS, int RG, bool OUT_F32>
+template <int MT, int QS, int RS, int RG, bool OUT_F32, bool PART = false>
 __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
 {
     constexpr int WAVES = 4, NC = QS / 2, RSB = RS < NC ? RS : NC;
     constexpr int SLOT = RG * 2048;       // a pair slot: RG groups of 16 rows x 128 B per wave
-    static_assert(QS % 2 == 0 && QS <= 16 && MT <= 2 && RSB >= 1 && (RG == 1 || RG == 2), "decode stream shape");
+    static_assert(QS % 2 == 0 && QS <= 16 && MT <= 2 && RSB >= 1 && RG >= 1 && RG <= 5, "decode stream shape");
     extern __shared__ __align__(16) uint8_t dsm[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the copy offsets go in SGPRs
     const int r = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16 * RG;
+    // PART: the grid's workgroups split the ceil(N / 16) row groups evenly,
+    // workgroup b taking groups [b G / grid, (b + 1) G / grid), at most RG of
+    // them; rows past its last group read as zero and are not stored
+    int n0, n_lim;
+    if (PART) {
+        const int64_t G = (p.N + 15) / 16, b = blockIdx.x, nwg = gridDim.x;
+        n0 = (int)(16 * (b * G / nwg));
+        n_lim = (int)min((int64_t)p.N, 16 * ((b + 1) * G / nwg));
+    } else {
+        n0 = blockIdx.x * 16 * RG;
+        n_lim = p.N;
+    }
     const int K = QS * 512, KB = K / 32, row_bytes = K / 2;
     const int QB = row_bytes / WAVES;     // W bytes per row per wave (64 QS)
     const int st0 = wave * QS;            // this wave's first stage
 
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.a_q, (short)0, p.M * row_bytes, 0x00020000);
-    const int4_t rw = make_rsrc(p.w_q, (uint32_t)p.N * row_bytes);
+    const int4_t rw = make_rsrc(p.w_q, (uint32_t)n_lim * row_bytes);
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dsm);
     const uint32_t lds_w = lds0 + (uint32_t)(wave * RSB * SLOT);   // this wave's ring of RSB pair slots
 
@@ -961,7 +972,7 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
     constexpr int SCOP = (RG + MT) * QS;   // 16 KB / 256 bytes per 16 rows
     const uint32_t sw_lds = lds0 + (uint32_t)(WAVES * RSB * SLOT), sa_lds = sw_lds + (uint32_t)(16 * RG * KB);
     {
-        const int4_t rws4 = make_rsrc(p.w_s, (uint32_t)p.N * KB);
+        const int4_t rws4 = make_rsrc(p.w_s, (uint32_t)n_lim * KB);
         const int4_t ras4 = make_rsrc(p.a_s, (uint32_t)p.M * KB);
 #pragma unroll
         for (int j = 0; j < SCOP; ++j)
@@ -1061,7 +1072,7 @@ __global__ __launch_bounds__(256) void mx_decode_stream_kernel(GemmArgs p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 16 * t + 4 * (l >> 4) + i;
-            if (m < p.M && nn < p.N) {
+            if (m < p.M && nn < n_lim) {
                 if (OUT_F32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + nn] = v[i];
                 else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + nn] = f32_to_bf16_rne(v[i]);
             }
@@ -1105,11 +1116,42 @@ static bool decode_stream_ok(int64_t m, int64_t k)
            decode_stream_lds_bytes(m > 16 ? 2 : 1, (int)k, decode_stream_cfg(m, k)) <= 65536;
 }
 
+// Above 8 rows of A, when the 16-row groups of W number 4 to 5 per compute
+// unit (MI355X: 256), one workgroup per compute unit takes 4 or 5 of them
+// (the grid splits the groups evenly), so each CU loads the A fragments
+// once instead of once per one or two groups, and no CU holds one workgroup
+// more than others.  Its ring (2 pair slots of 5 groups per wave, 80 KiB)
+// and scale blocks take up to 108 KiB of LDS.  (N = 17408, K = 5120: M = 32
+// 17.83 -> 14.07 us, M = 16 13.87 -> 12.45 us; at M = 8 and below it measured
+// equal or slower.)
+constexpr int DEC_PART_WGS = 256, DEC_PART_RG = 5;
+
+static bool decode_part_ok(int64_t m, int64_t n)
+{
+    const int64_t groups = (n + 15) / 16;
+    return m > 8 && groups >= 4 * DEC_PART_WGS && groups <= DEC_PART_RG * DEC_PART_WGS;
+}
+
 template <int MT, int QS, bool OUT_F32>
-static void launch_decode_stream_qs(const GemmArgs& a, hipStream_t stream)
+static hipError_t launch_decode_stream_qs(const GemmArgs& a, hipStream_t stream)
 {
     const DecodeStreamCfg c = decode_stream_cfg(a.M, a.K);
     const dim3 block(256);
+    if constexpr (MT <= 2) {
+        if (decode_part_ok(a.M, a.N)) {
+            auto kern = mx_decode_stream_kernel<MT, QS, 2, DEC_PART_RG, OUT_F32, true>;
+            const size_t lds_p = decode_stream_lds_bytes(MT, QS * 512, DecodeStreamCfg{DEC_PART_RG, 2});
+            static bool attr_set = false;  // benign race: setting the same value twice is harmless
+            if (!attr_set) {
+                const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                         (int)lds_p);
+                if (e != hipSuccess) return e;
+                attr_set = true;
+            }
+            hipLaunchKernelGGL(kern, dim3(DEC_PART_WGS), block, lds_p, stream, a);
+            return hipGetLastError();
+        }
+    }
     const size_t lds = decode_stream_lds_bytes(MT, a.K, c);
     if (MT == 2 && c.rg == 2)
         hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, 2, 2, OUT_F32>), dim3((a.N + 31) / 32), block, lds, stream, a);
@@ -1117,20 +1159,21 @@ static void launch_decode_stream_qs(const GemmArgs& a, hipStream_t stream)
         hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, 3, 1, OUT_F32>), dim3((a.N + 15) / 16), block, lds, stream, a);
     else
         hipLaunchKernelGGL((mx_decode_stream_kernel<MT, QS, QS / 2, 1, OUT_F32>), dim3((a.N + 15) / 16), block, lds, stream, a);
+    return hipGetLastError();
 }
 
 template <int MT, bool OUT_F32>
-static void launch_decode_stream(const GemmArgs& a, hipStream_t stream)
+static hipError_t launch_decode_stream(const GemmArgs& a, hipStream_t stream)
 {
     switch (a.K / 512) {
-    case 2: launch_decode_stream_qs<MT, 2, OUT_F32>(a, stream); break;
-    case 4: launch_decode_stream_qs<MT, 4, OUT_F32>(a, stream); break;
-    case 6: launch_decode_stream_qs<MT, 6, OUT_F32>(a, stream); break;
-    case 8: launch_decode_stream_qs<MT, 8, OUT_F32>(a, stream); break;
-    case 10: launch_decode_stream_qs<MT, 10, OUT_F32>(a, stream); break;
-    case 12: launch_decode_stream_qs<MT, 12, OUT_F32>(a, stream); break;
-    case 14: launch_decode_stream_qs<MT, 14, OUT_F32>(a, stream); break;
-    default: launch_decode_stream_qs<MT, 16, OUT_F32>(a, stream); break;
+    case 2: return launch_decode_stream_qs<MT, 2, OUT_F32>(a, stream);
+    case 4: return launch_decode_stream_qs<MT, 4, OUT_F32>(a, stream);
+    case 6: return launch_decode_stream_qs<MT, 6, OUT_F32>(a, stream);
+    case 8: return launch_decode_stream_qs<MT, 8, OUT_F32>(a, stream);
+    case 10: return launch_decode_stream_qs<MT, 10, OUT_F32>(a, stream);
+    case 12: return launch_decode_stream_qs<MT, 12, OUT_F32>(a, stream);
+    case 14: return launch_decode_stream_qs<MT, 14, OUT_F32>(a, stream);
+    default: return launch_decode_stream_qs<MT, 16, OUT_F32>(a, stream);
     }
 }
 
@@ -1163,10 +1206,7 @@ template <int MT, bool OUT_F32>
 hipError_t launch_decode(const GemmArgs& a, hipStream_t stream)
 {
     if constexpr (MT <= 2) {
-        if (decode_stream_ok(a.M, a.K)) {
-            launch_decode_stream<MT, OUT_F32>(a, stream);
-            return hipGetLastError();
-        }
+        if (decode_stream_ok(a.M, a.K)) return launch_decode_stream<MT, OUT_F32>(a, stream);
     }
     const int kind = decode_kind_mt<MT>(a.K);
     if (kind == 2)
@@ -1345,6 +1385,10 @@ extern "C" const char* mxl_mx_gemm_config_name(int a_bits, int w_bits, int64_t m
 {
     switch (classify(a_bits, w_bits, m, n, k, fused != 0)) {
     case SC_DECODE:
+        if (decode_stream_ok(m, k) && decode_part_ok(m, n))
+            return "mx_decode_stream_kernel<one workgroup per compute unit over 4-5 16-row W groups (each A fragment "
+                   "serves all of them), each wave streams its own K quarter through a ring of 2 LDS pair slots (8 rows "
+                   "x 128 B non-temporal copies) and computes each stage as its copies land, scaled mfma 16x16x128>";
         if (decode_stream_ok(m, k))
             return m > 16 ? "mx_decode_stream_kernel<32 W rows per workgroup (each A fragment serves both 16-row groups), "
                             "each wave streams its own K quarter through a ring of 2 LDS pair slots (8 rows x 128 B "

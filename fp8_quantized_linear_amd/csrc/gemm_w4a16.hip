@@ -397,23 +397,23 @@ __global__ __launch_bounds__(256) void w4a16_decode_stream_kernel(W4a16Args p)
 //    the whole-row kernel, so the results are bitwise the same.
 constexpr int w16_min(int a, int b) { return a < b ? a : b; }
 // VMEM operations a wave has issued (after its scale copies) before it
-// computes pair c: the prologue's A pairs (8 loads each) and W pairs (4
+// computes pair c: the prologue's A pairs (8 loads each) and W pairs (cw
 // copies each), then per computed pair i the A loads of pair i + APR and the
 // W copies of pair i + RSB
-constexpr int w16_issued(int c, int nc, int apr, int rsb)
+constexpr int w16_issued(int c, int nc, int apr, int rsb, int cw)
 {
-    int n = 8 * w16_min(apr, nc) + 4 * w16_min(rsb, nc);
-    for (int i = 0; i < c; ++i) n += (i + apr < nc ? 8 : 0) + (i + rsb < nc ? 4 : 0);
+    int n = 8 * w16_min(apr, nc) + cw * w16_min(rsb, nc);
+    for (int i = 0; i < c; ++i) n += (i + apr < nc ? 8 : 0) + (i + rsb < nc ? cw : 0);
     return n;
 }
 // operations issued after the later of pair c's A loads and W copies, at
 // the point where pair c is computed: the vmcnt that waits for both
-constexpr int w16_wait(int c, int nc, int apr, int rsb)
+constexpr int w16_wait(int c, int nc, int apr, int rsb, int cw)
 {
-    const int end_a = c < apr ? 8 * (c + 1) : w16_issued(c - apr, nc, apr, rsb) + 8;
-    const int end_w = c < rsb ? 8 * w16_min(apr, nc) + 4 * (c + 1)
-                              : w16_issued(c - rsb, nc, apr, rsb) + (c - rsb + apr < nc ? 8 : 0) + 4;
-    return w16_issued(c, nc, apr, rsb) - (end_a > end_w ? end_a : end_w);
+    const int end_a = c < apr ? 8 * (c + 1) : w16_issued(c - apr, nc, apr, rsb, cw) + 8;
+    const int end_w = c < rsb ? 8 * w16_min(apr, nc) + cw * (c + 1)
+                              : w16_issued(c - rsb, nc, apr, rsb, cw) + (c - rsb + apr < nc ? 8 : 0) + cw;
+    return w16_issued(c, nc, apr, rsb, cw) - (end_a > end_w ? end_a : end_w);
 }
 // s_waitcnt vmcnt(n) for an n that folds to a constant once loops are
 // unrolled (n <= 23)
@@ -432,18 +432,30 @@ __device__ __forceinline__ void w16_wait_vmcnt(int n)
     }
 }
 
-template <bool NV, int QS, int RS, bool OUT_F32>
+template <bool NV, int QS, int RS, bool OUT_F32, int RG = 2, bool PART = false>
 __global__ __launch_bounds__(256) void w4a16_decode_stream2_kernel(W4a16Args p)
 {
-    constexpr int WAVES = 4, RG = 2, NC = QS / 2, RSB = w16_min(RS, NC), APR = w16_min(2, NC);
-    constexpr int SLOT = RG * 2048;   // a pair slot: 32 rows x 128 B per wave
+    constexpr int WAVES = 4, NC = QS / 2, RSB = w16_min(RS, NC), APR = w16_min(2, NC);
+    constexpr int SLOT = RG * 2048;   // a pair slot: 16 RG rows x 128 B per wave
+    static_assert(RG >= 1 && RG <= 5, "row groups per workgroup");
     constexpr int K = QS * 512, row_bytes = K / 2, KS = K / (NV ? 16 : 32), QB = row_bytes / WAVES;
     static_assert(QS % 2 == 0 && QS <= 16, "stream2 shape");
     extern __shared__ __align__(16) uint8_t dsm[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16 * RG;
+    // PART: the grid's workgroups split the ceil(N / 16) row groups evenly,
+    // workgroup b taking groups [b G / grid, (b + 1) G / grid), at most RG of
+    // them; rows past its last group read as zero and are not stored
+    int n0, n_lim;
+    if (PART) {
+        const int64_t G = (p.N + 15) / 16, b = blockIdx.x, nwg = gridDim.x;
+        n0 = (int)(16 * (b * G / nwg));
+        n_lim = (int)min((int64_t)p.N, 16 * ((b + 1) * G / nwg));
+    } else {
+        n0 = blockIdx.x * 16 * RG;
+        n_lim = p.N;
+    }
     const int st0 = wave * QS;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dsm);
     const uint32_t lds_w = lds0 + (uint32_t)(wave * RSB * SLOT);   // this wave's ring
@@ -452,7 +464,7 @@ __global__ __launch_bounds__(256) void w4a16_decode_stream2_kernel(W4a16Args p)
     // 1. the W scale block of the 32 rows, 256 bytes per copy, spread over the waves
     constexpr int SCOP = 16 * RG * KS / 256;
     {
-        const int4_t rws = make_rsrc(p.w_s, (uint32_t)p.N * KS);
+        const int4_t rws = make_rsrc(p.w_s, (uint32_t)n_lim * KS);
 #pragma unroll
         for (int j = 0; j < SCOP; ++j)
             if (j % WAVES == wave) dma_b32(s_lds + j * 256, n0 * KS + j * 256 + lane * 4, rws, 0);
@@ -472,7 +484,7 @@ __global__ __launch_bounds__(256) void w4a16_decode_stream2_kernel(W4a16Args p)
 #pragma unroll
     for (int c = 0; c < APR; ++c) load_a(c);
     // 3. the W copies of the first RSB pairs
-    const int4_t rw = make_rsrc(p.w_q, (uint32_t)p.N * row_bytes);
+    const int4_t rw = make_rsrc(p.w_q, (uint32_t)n_lim * row_bytes);
     int voffh[2 * RG];
 #pragma unroll
     for (int h = 0; h < 2 * RG; ++h) {
@@ -488,7 +500,7 @@ __global__ __launch_bounds__(256) void w4a16_decode_stream2_kernel(W4a16Args p)
     for (int c = 0; c < RSB; ++c) copy_pair(c);
     // the scale copies have landed once at most the A loads and W copies
     // issued after them are outstanding; the barrier publishes them
-    wait_vmcnt<8 * APR + 4 * RSB>();
+    wait_vmcnt<8 * APR + 2 * RG * RSB>();
     lds_barrier();
 
     f32x4_w acc[RG];
@@ -498,7 +510,7 @@ __global__ __launch_bounds__(256) void w4a16_decode_stream2_kernel(W4a16Args p)
     const int rsw = (r >> 1) & 7;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        w16_wait_vmcnt(w16_wait(c, NC, APR, RSB));
+        w16_wait_vmcnt(w16_wait(c, NC, APR, RSB, 2 * RG));
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int un = 4 * (st0 + 2 * c + hf) + g;   // global 16-byte unit of the W row
@@ -535,10 +547,10 @@ __global__ __launch_bounds__(256) void w4a16_decode_stream2_kernel(W4a16Args p)
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) red[(wave * RG + rg) * 64 + lane] = acc[rg];
     __syncthreads();
-    // thread e < 128 finishes accumulator lane e % 64 of group e / 64: A rows
+    // item e < 64 RG finishes accumulator lane e % 64 of group e / 64: A rows
     // 4 (l / 16) + i, W row n0 + 16 rg + l % 16
-    if (tid < RG * 64) {
-        const int l = tid & 63, rg = tid >> 6;
+    for (int e = tid; e < RG * 64; e += 256) {
+        const int l = e & 63, rg = e >> 6;
         f32x4_w v = red[rg * 64 + l];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) {
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(256) void w4a16_decode_stream2_kernel(W4a16Args p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * (l >> 4) + i;
-            if (m < p.M && nn < p.N) {
+            if (m < p.M && nn < n_lim) {
                 const float o = v[i] * p.alpha;
                 if (OUT_F32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + nn] = o;
                 else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + nn] = f32_to_bf16_rne(o);
@@ -574,27 +586,64 @@ static bool w4a16_stream2_ok(int64_t m, int64_t k)
     return m >= 1 && m <= 16 && k % 1024 == 0 && k >= 1024 && k <= 8192;
 }
 
-template <bool NV, int QS, bool OUT_F32>
-static void launch_w4a16_stream2_qs(const W4a16Args& a, hipStream_t stream)
+// When the 16-row groups of W number 4 to 5 per compute unit (MI355X: 256),
+// one workgroup per compute unit takes 4 or 5 of them (the grid splits the
+// groups evenly): each CU then loads A once, and none holds a workgroup more
+// than the others.  Ring and scale blocks take up to 106 KiB of LDS.  NVFP4
+// takes it from 8 rows of A: its dequantization is vector-bound, and below
+// that the three workgroups per CU of the 32-row grid issue it faster (N =
+// 17408, K = 5120: M = 2 / 4 / 8 / 16 at 16.46 / 17.02 / 18.90 / 24.23 us
+// with 32-row workgroups, 17.79 / 17.70 / 18.35 / 20.35 us partitioned;
+// MXFP4 at M = 3 / 8 / 16: 14.72 / 17.59 / 22.89 -> 13.25 / 13.97 / 15.36 us).
+constexpr int W16_PART_WGS = 256, W16_PART_RG = 5;
+
+static bool w4a16_part_ok(int nv, int64_t m, int64_t n)
 {
+    const int64_t groups = (n + 15) / 16;
+    return (!nv || m >= 8) && groups >= 4 * W16_PART_WGS && groups <= W16_PART_RG * W16_PART_WGS;
+}
+
+template <bool NV>
+static size_t w4a16_part_lds_bytes(int64_t k)
+{
+    const int nc = (int)(k / 1024), slots = W16_SLOTS < nc ? W16_SLOTS : nc;
+    return (size_t)4 * slots * W16_PART_RG * 2048 + (size_t)16 * W16_PART_RG * (k / (NV ? 16 : 32));
+}
+
+template <bool NV, int QS, bool OUT_F32>
+static hipError_t launch_w4a16_stream2_qs(const W4a16Args& a, hipStream_t stream)
+{
+    if (w4a16_part_ok(NV, a.M, a.N)) {
+        auto kern = w4a16_decode_stream2_kernel<NV, QS, W16_SLOTS, OUT_F32, W16_PART_RG, true>;
+        const size_t lds = w4a16_part_lds_bytes<NV>(QS * 512);
+        static bool attr_set = false;  // benign race: setting the same value twice is harmless
+        if (!attr_set) {
+            const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)lds);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        hipLaunchKernelGGL(kern, dim3(W16_PART_WGS), dim3(256), lds, stream, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((w4a16_decode_stream2_kernel<NV, QS, W16_SLOTS, OUT_F32>), dim3((a.N + 31) / 32), dim3(256),
                        w4a16_stream2_lds_bytes<NV>(a.K), stream, a);
+    return hipGetLastError();
 }
 
 template <bool NV, bool OUT_F32>
 static hipError_t launch_w4a16_stream2(const W4a16Args& a, hipStream_t stream)
 {
     switch (a.K / 512) {
-    case 2: launch_w4a16_stream2_qs<NV, 2, OUT_F32>(a, stream); break;
-    case 4: launch_w4a16_stream2_qs<NV, 4, OUT_F32>(a, stream); break;
-    case 6: launch_w4a16_stream2_qs<NV, 6, OUT_F32>(a, stream); break;
-    case 8: launch_w4a16_stream2_qs<NV, 8, OUT_F32>(a, stream); break;
-    case 10: launch_w4a16_stream2_qs<NV, 10, OUT_F32>(a, stream); break;
-    case 12: launch_w4a16_stream2_qs<NV, 12, OUT_F32>(a, stream); break;
-    case 14: launch_w4a16_stream2_qs<NV, 14, OUT_F32>(a, stream); break;
-    default: launch_w4a16_stream2_qs<NV, 16, OUT_F32>(a, stream); break;
+    case 2: return launch_w4a16_stream2_qs<NV, 2, OUT_F32>(a, stream);
+    case 4: return launch_w4a16_stream2_qs<NV, 4, OUT_F32>(a, stream);
+    case 6: return launch_w4a16_stream2_qs<NV, 6, OUT_F32>(a, stream);
+    case 8: return launch_w4a16_stream2_qs<NV, 8, OUT_F32>(a, stream);
+    case 10: return launch_w4a16_stream2_qs<NV, 10, OUT_F32>(a, stream);
+    case 12: return launch_w4a16_stream2_qs<NV, 12, OUT_F32>(a, stream);
+    case 14: return launch_w4a16_stream2_qs<NV, 14, OUT_F32>(a, stream);
+    default: return launch_w4a16_stream2_qs<NV, 16, OUT_F32>(a, stream);
     }
-    return hipGetLastError();
 }
 
 template <bool NV>
@@ -673,11 +722,15 @@ extern "C" hipError_t mxl_launch_w4a16_decode(int w_nv, const void* a_bf16, cons
     return out_f32 ? launch_w4a16_decode<false, true>(a, stream) : launch_w4a16_decode<false, false>(a, stream);
 }
 
-extern "C" const char* mxl_w4a16_decode_config_name(int w_nv, int64_t m, int64_t k)
+extern "C" const char* mxl_w4a16_decode_config_name(int w_nv, int64_t m, int64_t n, int64_t k)
 {
     if (w4a16_stream_ok(w_nv, m, k))
         return "w4a16_decode_stream_kernel<16 W rows per workgroup, each wave copies its own K quarter of W and A "
                "into LDS and computes each stage as its copies land, bf16 mfma 16x16x32>";
+    if (w4a16_stream2_ok(m, k) && w4a16_part_ok(w_nv, m, n))
+        return "w4a16_decode_stream2_kernel<one workgroup per compute unit over 4-5 16-row W groups (each A fragment "
+               "serves all of them), each wave streams its own K quarter of W through a ring of 2 LDS pair slots, A "
+               "from global memory one pair ahead, bf16 mfma 16x16x32>";
     if (w4a16_stream2_ok(m, k))
         return "w4a16_decode_stream2_kernel<32 W rows per workgroup (each A fragment serves both 16-row groups), each "
                "wave streams its own K quarter of W through a ring of 2 LDS pair slots, A from global memory one pair "

@@ -364,9 +364,18 @@ def test_plan_names_the_kernel():
     assert "w4a16_decode_stream_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 1, 17408, 5120)
     assert "w4a16_decode_stream_kernel" in mxl.mx_gemm_w4a16_plan("nvfp4", 1, 17408, 5120)
     assert "w4a16_decode_stream2_kernel" in mxl.mx_gemm_w4a16_plan("nvfp4", 16, 17408, 5120)
+    assert "one workgroup per compute unit" in mxl.mx_gemm_w4a16_plan("nvfp4", 16, 17408, 5120)
+    assert "32 W rows per workgroup" in mxl.mx_gemm_w4a16_plan("mxfp4", 8, 4096, 5120)
+    assert "32 W rows per workgroup" in mxl.mx_gemm_w4a16_plan("nvfp4", 4, 17408, 5120)
+    assert "one workgroup per compute unit" in mxl.mx_gemm_w4a16_plan("mxfp4", 4, 17408, 5120)
     assert "w4a16_decode_stream2_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 3, 17408, 8192)
     assert "w4a16_decode_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 8, 17408, 2560)
     assert "mx_decode_stream_kernel" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 32, 17408, 5120)
+    # 9-32 rows over 4-5 sixteen-row W groups per compute unit: one workgroup per CU
+    assert "one workgroup per compute unit" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 32, 17408, 5120)
+    assert "one workgroup per compute unit" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 9, 17408, 5120)
+    assert "one workgroup per compute unit" not in mxl.mx_gemm_plan("mxfp4", "mxfp4", 8, 17408, 5120)
+    assert "one workgroup per compute unit" not in mxl.mx_gemm_plan("mxfp4", "mxfp4", 32, 151936, 5120)
     assert "mx_decode_kernel" in mxl.mx_gemm_plan("mxfp4", "mxfp4", 8, 17408, 2560)
     assert "dq_gemm_kernel" in mxl.mx_gemm_w4a16_plan("mxfp4", 17, 17408, 5120)
     assert "dq_gemm_kernel" in mxl.mx_gemm_w4a16_plan("nvfp4", 1, 512, 400)

@@ -209,6 +209,25 @@ def test_decode_kernel_kinds(kernel, k, m):
         check_gemm(y_host(y), y_ref, s, not out_f32, f"{kernel} {m}x{k}x{n} f32={out_f32}")
 
 
+# M = 9 .. 32 with 4 to 5 sixteen-row W groups per compute unit: one
+# workgroup per CU over an even share of the groups (4 or 5 each; rows past a
+# workgroup's share read as zero and are not stored).  Full outputs against
+# the oracle at even shares (N = 16384, 20480) and ragged ones.
+@pytest.mark.parametrize("m", [9, 16, 17, 32])
+@pytest.mark.parametrize("n", [16384, 16400, 17408, 20470])
+def test_decode_partitioned(m, n):
+    k = 1024
+    plan = mxl.mx_gemm_plan("mxfp4", "mxfp4", m, n, k)
+    say(f"decode partitioned m={m} k={k} n={n}: {plan[:70]}")
+    assert "one workgroup per compute unit" in plan
+    a_bits = W.activations_entry_outliers(m, k, seed=5 + m)
+    w_bits = W.normal_bf16(n, k, 0.02, 6)
+    y_ref, s, _, _ = oracle_full(a_bits, w_bits, "mxfp4")
+    for out_f32 in (False, True):
+        y, _, _, _ = run_mx(a_bits, w_bits, "mxfp4", out_f32=out_f32)
+        check_gemm(y_host(y), y_ref, s, not out_f32, f"decode partitioned {m}x{k}x{n} f32={out_f32}")
+
+
 # M = 33 .. 48 runs the decode kernels with three 16-row A fragments (the
 # whole-row LDS block where it fits 64 KiB, else the generic kernel).
 @pytest.mark.parametrize("m", [33, 40, 48])

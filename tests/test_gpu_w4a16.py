@@ -88,6 +88,29 @@ def test_w4a16_full(fmt, m, k, n):
         check_gemm(yh, y_ref, s, not out_f32, f"w4a16 {fmt} {m}x{k}x{n} f32={out_f32}")
 
 
+# 4 to 5 sixteen-row W groups per compute unit (NVFP4 from 8 rows of A): one
+# workgroup per CU over an even share of them (4 or 5; rows past a share read
+# as zero and are not stored), at even (N = 16384) and ragged shares
+@pytest.mark.parametrize("fmt,m,n", [("mxfp4", 3, 16384), ("mxfp4", 8, 16400), ("mxfp4", 16, 17408),
+                                     ("mxfp4", 5, 20470), ("nvfp4", 8, 16384), ("nvfp4", 9, 16400),
+                                     ("nvfp4", 16, 17408), ("nvfp4", 12, 20470)])
+def test_w4a16_partitioned(fmt, m, n):
+    k = 1024
+    plan = mxl.mx_gemm_w4a16_plan(fmt, m, n, k)
+    say(f"w4a16 partitioned {fmt} m={m} k={k} n={n}: {plan[:70]}")
+    assert "one workgroup per compute unit" in plan
+    a_bits = W.activations_entry_outliers(m, k, seed=9 + m)
+    w_bits = W.normal_bf16(n, k, 0.02, 10)
+    wq, ws, rq, rs, g = pack(w_bits, fmt)
+    y_ref, s = oracle.w4a16_gemm(a_bits, rq, rs, n, k, fmt, g)
+    a = cuda_bf16(a_bits)
+    for out_f32 in (False, True):
+        y = mxl.mx_gemm_w4a16(a, wq, ws, fmt, alpha_of(g), out_f32=out_f32)
+        torch.cuda.synchronize()
+        yh = host(y.float()) if not out_f32 else host(y)
+        check_gemm(yh, y_ref, s, not out_f32, f"w4a16 partitioned {fmt} {m}x{k}x{n} f32={out_f32}")
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 def test_w4a16_nvfp4_odd_k_and_small_n(fmt):
     # NVFP4 with K % 32 == 16 and N = 1 (general kernel); MXFP4 with N = 1
