@@ -879,11 +879,13 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(GemmArgs p)
 
 // Decode-shaped MXFP4 GEMM streamed per wave (M <= 16 MT, MT <= 2, K =
 // 1024 QS / 2 with QS stages of 128 per wave, K <= 8192).  One workgroup of
-// 4 waves owns 16 rows of W and wave w a contiguous quarter of K.  Each wave
-// copies its own 16 x K/8-byte part of W into its own LDS region and
-// consumes it stage by stage as the copies land, so no wave waits for
-// another one (or for the whole block) before its matrix-core work; the
-// four partial sums meet once, at the end.
+// 4 waves owns RG groups of 16 W rows (RG consecutive groups, or with PART
+// an even share of them per compute unit) and wave w a contiguous quarter
+// of K.  Each wave copies its own 16 RG x K/8-byte part of W into its own
+// LDS region and consumes it stage by stage as the copies land, so no wave
+// waits for another one (or for the whole block) before its matrix-core
+// work; the four partial sums meet once, at the end.  Each A fragment a
+// wave loads serves all RG groups.
 //  * Copy (c, h) moves rows 8 h .. 8 h + 7 x bytes [128 c, 128 c + 128) of
 //    the wave's quarter: 8 full cache lines, 1 KiB.  The copies go out in c
 //    order, and stages 2 c and 2 c + 1 wait for copies (c, 0) and (c, 1)
